@@ -1,0 +1,69 @@
+"""The five MoE FFN workloads, as plain data.
+
+Names follow the StackedMoE page (hidden_dim, num_experts,
+num_experts_per_token, moe_dim, gate_up_format, has_bias), the
+GatedActivation page (fused_activation, alpha, limit) and the
+sink_gate_router_kernel page (n_shared_experts, route_scale, global_scale).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    cfg_id: int
+    name: str
+    T: int                      # tokens
+    H: int                      # hidden_dim
+    E: int                      # num_experts (routed)
+    k: int                      # num_experts_per_token
+    D: int                      # moe_dim
+    router: str = "softmax"     # "softmax" | "sigmoid_sink"
+    s: int = 0                  # n_shared_experts (sink lanes), sigmoid router only
+    gate_up_format: str = "concatenated"   # | "interleaved"
+    has_bias: bool = False
+    activation: str = "silu"    # "silu" | "swigluoai" | "gelu_tanh"
+    alpha: float = 0.0
+    limit: float = 0.0
+    operand_dtype: str = "bf16"  # "bf16" | "fp8"
+    route_scale: float = 1.0
+    global_scale: float = 1.0
+    logit_std: float = 2.0      # sigmoid router: logits are an input ~N(0, logit_std)
+    bias_range: float = 0.1     # sigmoid router: selection bias ~U(-r, r)
+    x_std: float = 1.0
+    w_std: float = 0.02
+
+    @property
+    def R(self) -> int:
+        """Routed rows T*k (the most rows the grouped GEMMs can see)."""
+        return self.T * self.k
+
+    @property
+    def ffn_flops(self) -> int:
+        """Algorithmic FLOPs of both grouped GEMMs: 2*R*H*2D + 2*R*D*H."""
+        return 6 * self.R * self.H * self.D
+
+
+CONFIGS = {
+    1: MoEConfig(1, "tiny", T=64, H=256, E=8, k=2, D=512),
+    2: MoEConfig(2, "mixtral", T=4096, H=4096, E=8, k=2, D=14336),
+    3: MoEConfig(3, "sink", T=8192, H=2048, E=128, k=6, D=768,
+                 router="sigmoid_sink", s=2, route_scale=2.5, global_scale=1.0),
+    4: MoEConfig(4, "gptoss", T=4096, H=2880, E=32, k=4, D=2880,
+                 gate_up_format="interleaved", has_bias=True,
+                 activation="swigluoai", alpha=1.702, limit=7.0),
+    5: MoEConfig(5, "fp8", T=16384, H=7168, E=256, k=8, D=2048,
+                 router="sigmoid_sink", s=0, operand_dtype="fp8",
+                 route_scale=1.0, global_scale=1.0),
+}
+
+
+def get_config(i: int) -> MoEConfig:
+    return CONFIGS[i]
+
+
+def scaled(cfg: MoEConfig, **changes) -> MoEConfig:
+    """A copy of a workload with some sizes changed (smaller parity cases)."""
+    return dataclasses.replace(cfg, **changes)
