@@ -522,3 +522,63 @@ def test_small_configs_run_end_to_end():
             assert np.allclose(tot, c2.route_scale * c2.global_scale, rtol=1e-12)
         else:
             assert np.allclose(r["weights"].sum(1), 1.0, rtol=1e-12)
+
+
+def test_topk_ties_in_wide_rows_brute_force():
+    """Many exactly equal keys in rows wider than numpy's small-sort cutoff:
+    the selection must still put equal keys in ascending index order."""
+    rng = np.random.default_rng(20)
+    E, k = 96, 8
+    z = rng.choice(np.array([-1.0, 0.0, 0.5, 2.0], np.float32), size=(60, E))
+    idx, _ = O.route_softmax_topk(z, k)
+    idx2, _, _ = O.route_sigmoid_sink(z, E, k, 0)
+    for t in range(60):
+        assert idx[t].tolist() == _py_topk(z[t], k)
+        assert idx2[t].tolist() == _py_topk(O.sigmoid_f32(z[t]), k)
+
+
+def test_combine_brute_force():
+    rng = np.random.default_rng(21)
+    T, k, H, R = 9, 3, 5, 20
+    O_rows = rng.standard_normal((R, H))
+    rs = rng.integers(-1, R, (T, k))
+    w = rng.random((T, k))
+    mask = np.arange(T) != 4
+    y = O.combine(O_rows, rs, w, mask)
+    for t in range(T):
+        for h in range(H):
+            want = 0.0 if not mask[t] else math.fsum(w[t, j] * O_rows[rs[t, j], h] for j in range(k) if rs[t, j] >= 0)
+            assert y[t, h] == pytest.approx(want, rel=1e-14, abs=1e-15)
+
+
+@pytest.mark.parametrize("fmt,act", [("concatenated", "silu"), ("interleaved", "swigluoai"), ("concatenated", "gelu_tanh")])
+def test_expert_mlp_bias_scales_brute_force(fmt, act):
+    """Plain-Python expert MLP with bias, expert scales, either gate_up
+    layout and each activation, against expert_mlp."""
+    rng = np.random.default_rng(22)
+    n, H, D = 3, 5, 4
+    x = rng.standard_normal((n, H))
+    wgu = rng.standard_normal((H, 2 * D)) * 0.5
+    wd = rng.standard_normal((D, H)) * 0.5
+    bgu = rng.standard_normal(2 * D) * 0.3
+    bd = rng.standard_normal(H) * 0.3
+    sgu, sd = 1.5, 0.75
+    alpha, limit = (1.702, 7.0) if act == "swigluoai" else (0.0, 0.0)
+    got = O.expert_mlp(x, wgu, wd, fmt=fmt, activation=act, alpha=alpha, limit=limit,
+                       b_gate_up=bgu, b_down=bd, gate_up_scale=sgu, down_scale=sd, act_format="none")
+    for r in range(n):
+        h = [sgu * math.fsum(x[r, i] * wgu[i, c] for i in range(H)) + bgu[c] for c in range(2 * D)]
+        a = []
+        for d in range(D):
+            gi, ui = (d, D + d) if fmt == "concatenated" else (2 * d, 2 * d + 1)
+            g, u = h[gi], h[ui]
+            if act == "silu":
+                a.append(g / (1 + math.exp(-g)) * u)
+            elif act == "swigluoai":
+                g, u = min(g, limit), max(min(u, limit), -limit)
+                a.append(g / (1 + math.exp(-alpha * g)) * (u + 1))
+            else:
+                a.append(0.5 * g * (1 + math.tanh(0.7978845608028654 * (g + 0.044715 * g ** 3))) * u)
+        for c in range(H):
+            want = sd * math.fsum(a[d] * wd[d, c] for d in range(D)) + bd[c]
+            assert got[r, c] == pytest.approx(want, rel=1e-12, abs=1e-14)
