@@ -1,0 +1,220 @@
+"""Throughput of the MoE FFN forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--cfg 2] [--no-cpu-baseline]
+
+One step is the whole layer on one batch: moe_route -> moe_build_indices ->
+moe_grouped_ffn (gate_up GEMM + fused activation, down GEMM) -> moe_combine,
+on seeded synthetic inputs already resident in HBM.  The default workload is
+the Mixtral-shape layer: T=4096 tokens, hidden 4096, 8 experts, top-2 softmax
+gate, moe_dim 14336, concatenated gate_up, SiLU, bf16 operands with fp32
+accumulation.
+
+Prints one JSON line: whole-layer tokens/s, the roofline of the dominant
+kernel (the grouped gate_up GEMM, timed with HIP events recorded around its
+launch on the stream it runs on), and the CPU oracle timed on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + achieved TFLOPS (% MFMA peak), Mixtral shape, T=4096"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_mixtral_traffic.json")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles through libamdhip64 (timing on any stream)."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(h)) == 0
+            self.ev[i] = h
+        self.n = n
+
+    def record(self, i: int, stream: int):
+        assert self.hip.hipEventRecord(ctypes.c_void_p(self.ev[i]), ctypes.c_void_p(stream)) == 0
+
+    def triple(self, i: int):
+        arr = (ctypes.c_void_p * 3)(self.ev[i], self.ev[i + 1], self.ev[i + 2])
+        return arr
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]),
+                                            ctypes.c_void_p(self.ev[b])) == 0
+        return float(ms.value)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
+
+
+def _src_hash() -> str:
+    p = os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc", "ffn_bf16.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def _traffic():
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter
+    summary, or None when it is missing or the kernel source changed since."""
+    try:
+        d = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != _src_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, n_tokens: int):
+    """The oracle as it stands, on a sample of the workload's tokens."""
+    import numpy as np
+    import synth
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    hin = synth.to_host(inp)
+    rng = np.random.default_rng(0)
+    tokens = np.sort(rng.choice(cfg.T, n_tokens, replace=False))
+    t0 = time.perf_counter()
+    r = O.route(hin, cfg)
+    y = O.layer(hin, cfg, indices=r["indices"], weights=r["weights"], tokens=tokens)
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(y))
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tokens} of {cfg.T} tokens (seeded), all experts they route to, routing of all "
+                      f"{cfg.T} tokens; {dt:.1f} s on the host, float64 numpy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cfg", type=int, default=2)
+    ap.add_argument("--cpu-sample", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mixture_experts_ffn_top_amd as moe
+    import synth
+
+    cfg = synth.get_config(args.cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating workload cfg {cfg.cfg_id} ({cfg.name})", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, dev)
+    layer = moe.MoELayer(cfg, inp)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    K, W = args.steps, args.warmup
+    # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end), 6 after combine
+    ev = HipEvents(7 * (K + W))
+
+    def step(i):
+        base = 7 * i
+        c = cfg
+        ev.record(base + 0, stream)
+        if c.router == "softmax":
+            idx, w, sw, _ = moe.route(router="softmax", k=c.k, E=c.E, x=inp["x"], w_gate=layer.w_gate,
+                                      route_scale=c.route_scale, global_scale=layer.global_scale)
+        else:
+            idx, w, sw, _ = moe.route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=layer.logits,
+                                      expert_bias=layer.expert_bias, route_scale=c.route_scale,
+                                      global_scale=layer.global_scale)
+        ev.record(base + 1, stream)
+        gather = layer.gather
+        ind = moe.build_indices(idx, c.E, weights=w, x=None if gather else inp["x"],
+                                xperm_dtype="fp8" if c.operand_dtype == "fp8" else "bf16")
+        ev.record(base + 2, stream)
+        O_ = moe.grouped_ffn(ind["offsets"], layer.R, layer.w, x_perm=ind.get("x_perm"),
+                             x_perm_scale=ind.get("x_perm_scale"), x=inp["x"] if gather else None,
+                             sorted_token=ind["sorted_token"] if gather else None,
+                             activation=c.activation, alpha=c.alpha, limit=c.limit,
+                             gate_up_format=c.gate_up_format, out_dtype=layer.out_dtype,
+                             act_workspace=layer.act_ws, out=layer.O, timing_events=ev.triple(base + 3))
+        moe.combine(O_, ind["row_of_slot"], c.T, c.k, weights=w, out=layer.y)
+        ev.record(base + 6, stream)
+
+    print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1000.0 / K
+
+    def mean_ms(a, b):
+        return sum(ev.elapsed_ms(7 * i + a, 7 * i + b) for i in range(W, W + K)) / K
+
+    t_route, t_idx = mean_ms(0, 1), mean_ms(1, 2)
+    t_gu, t_dn = mean_ms(3, 4), mean_ms(4, 5)
+    t_comb = mean_ms(5, 6)
+    t_layer_dev = mean_ms(0, 6)
+    ev.close()
+
+    R = cfg.T * cfg.k
+    gu_flops = 4.0 * R * cfg.H * cfg.D
+    dn_flops = 2.0 * R * cfg.D * cfg.H
+    peak = PEAK_FP8_TFLOPS if cfg.operand_dtype == "fp8" else PEAK_BF16_TFLOPS
+    gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
+    ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
+    x_bytes = 2 * cfg.T * cfg.H
+    comb_bytes = 4 * R * cfg.H + 8 * R + 2 * cfg.T * cfg.H
+    line = {
+        "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8" if cfg.operand_dtype == "fp8" else "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
+                               f"top-{cfg.k} {cfg.router} router moe_dim={cfg.D} {cfg.gate_up_format} "
+                               f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,
+                   "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(gu_tf, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / peak, 4), "traffic": _traffic(),
+                     "kernel": "grouped gate_up GEMM + fused activation",
+                     "flops_per_launch": gu_flops, "avg_launch_ms": round(t_gu, 4)},
+        "ffn_tflops": round(ffn_tf, 2), "ffn_mfma_frac": round(ffn_tf / peak, 4),
+        "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),
+                         "gate_up": round(t_gu, 4), "down": round(t_dn, 4), "combine": round(t_comb, 4),
+                         "layer_device": round(t_layer_dev, 4)},
+        "hbm_gbs": {"route": round(x_bytes / (t_route * 1e-3) / 1e9, 1),
+                    "combine": round(comb_bytes / (t_comb * 1e-3) / 1e9, 1)},
+        "weight_layout": "out_in (transposed stacked weights, laid out once at load)",
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,317 @@
+/*
+ * moe_mi355x.h -- C ABI of the MoE FFN forward pass for AMD MI355X (gfx950).
+ *
+ * The layer is split into four calls, run in this order on one HIP stream:
+ *
+ *   moe_route          per-token router: softmax top-k gate, or the fused
+ *                      sigmoid + selection-bias top-k with sink lanes
+ *   moe_build_indices  per-expert CSR of the token->expert assignments,
+ *                      token permutation (and optional row gather / fp8
+ *                      quantisation of the activations)
+ *   moe_grouped_ffn    grouped gate_up GEMM with the gated activation fused
+ *                      into its epilogue, then the grouped down GEMM
+ *   moe_combine        router-weighted sum of each token's expert rows
+ *
+ * Sources (web pages, cited by title and section):
+ *   [StackedMoE]  MAX Python API, max.nn.moe.StackedMoE: constructor
+ *                 parameters, "Weight tensor shapes", transposed-weight
+ *                 properties.
+ *   [GatedAct]    MAX Python API, max.nn.moe.GatedActivation: fused_activation,
+ *                 alpha, limit, kernel_parameters().
+ *   [SinkRouter]  MAX Mojo API, nn.moe sink_gate_router_kernel: description,
+ *                 Parameters and Args.
+ *   [NeMoExperts] NeMo AutoModel, nemo_automodel.components.moe.experts:
+ *                 GroupedExperts.forward, _permute_tokens_for_grouped_mm,
+ *                 _apply_bias, the activation functions.
+ *   [MegaFFN]     MAX Mojo API, builtin_kernels mega_ffn: per-leg expert
+ *                 scales, clamp constants.
+ *
+ * Conventions shared by every call:
+ *   - Every pointer named "device" is device memory owned by the caller; the
+ *     library never allocates, frees, retains a pointer after returning, or
+ *     synchronises.  Host scalars are passed by value inside the args struct.
+ *   - Tensors are dense row-major; only `logits` has a leading dimension.
+ *     bf16 tensors are uint16 bit patterns; fp8 tensors are OCP e4m3fn codes.
+ *   - Every launch is asynchronous on `stream` (a hipStream_t; NULL is the
+ *     default stream).
+ *   - Argument errors are detected on the host before anything is launched:
+ *     the call returns MOE_ERR_INVALID_ARGUMENT (or MOE_ERR_UNSUPPORTED for a
+ *     valid but unimplemented combination, MOE_ERR_WORKSPACE_TOO_SMALL for a
+ *     short workspace) and moe_last_error_message() says why.  MOE_ERR_HIP
+ *     means a launch failed.  Data-dependent cases are defined behaviour, not
+ *     errors: empty experts, expert ids outside the local slice (dropped),
+ *     masked tokens (zero output).
+ *   - Device pointers must be 16-byte aligned; row lengths in bytes must be
+ *     multiples of 16 (so hidden_dim and moe_dim are multiples of 8).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status_t;
+
+/* Router kinds. */
+enum { MOE_ROUTER_SOFTMAX_TOPK = 0, MOE_ROUTER_SIGMOID_SINK = 1 };
+/* [GatedAct] fused_activation. */
+enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLUOAI = 1, MOE_ACT_GELU_TANH = 2 };
+/* [StackedMoE] gate_up_format. */
+enum { MOE_GATE_UP_CONCATENATED = 0, MOE_GATE_UP_INTERLEAVED = 1 };
+/* Element types. */
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_BLOCK128 = 1, MOE_DTYPE_FP32 = 2 };
+/* Weight layouts: [StackedMoE] stacked [E, in_features, out_features]
+   ("Weight tensor shapes"), or its transposed view
+   [E, out_features, in_features] (gate_up_proj_transposed /
+   down_proj_transposed). */
+enum { MOE_WEIGHT_IN_OUT = 0, MOE_WEIGHT_OUT_IN = 1 };
+
+/* ------------------------------------------------------------------------
+ * moe_route -- [SinkRouter] description and Args; [StackedMoE] gate_cls,
+ * router_dtype, num_experts_per_token.
+ *
+ * SOFTMAX_TOPK: logits z = x . w_gate^T (bf16 inputs, fp32 accumulate, fp32
+ *   logits), or `logits` given directly.  Selects the k largest logits,
+ *   largest first, equal logits to the lower expert index.  With renormalize
+ *   != 0 the weights are the softmax over the k selected logits; otherwise the
+ *   full-softmax probabilities of the selected experts.  n_shared_experts
+ *   must be 0 and expert_bias NULL.
+ * SIGMOID_SINK: key_e = sigmoid(z_e) + expert_bias[e] (float32; sigmoid is
+ *   evaluated as 1/(1+exp(-z)) with exp rounded once to float32 and a
+ *   correctly rounded add and divide); the k largest keys are selected,
+ *   largest first, ties to the lower index.  The weights are the softmax over
+ *   log-sigmoid of [the selected raw logits | the s sink logits, columns
+ *   E..E+s-1].  k + s must be a power of two no greater than 64 (one
+ *   wavefront).  Input is `logits` only.
+ * Both: every weight (expert and sink) is multiplied by
+ *   route_scale * global_scale[0].
+ *
+ * Arguments (device unless marked host):
+ *   router_kind, num_tokens T >= 0, n_routed_experts E in [1, 1024],
+ *   n_experts_per_tok k in [1, min(E, 64)], n_shared_experts s >= 0   host
+ *   hidden_dim H                       host, softmax x-form only
+ *   x          bf16 [T, H]             softmax x-form (logits == NULL), E <= 128
+ *   w_gate     bf16 [E, H]             gate linear layer (out, in)
+ *   logits     fp32 [T, logits_ld], logits_ld >= E + s; routed experts then
+ *              sink lanes; a wider row's tail is not read
+ *   logits_out fp32 [T, E] or NULL     softmax x-form: the computed logits
+ *   expert_bias fp32 [E] or NULL (0)   sigmoid: selection only
+ *   global_scale fp32 [1] or NULL (1.0)
+ *   route_scale                        host float
+ *   renormalize                        host int, softmax only
+ *   expert_indices int32 [T, k]        out
+ *   expert_weights fp32 [T, k]         out
+ *   sink_weights   fp32 [T, s]         out, required when s > 0
+ * ---------------------------------------------------------------------- */
+typedef struct moe_route_args {
+  int32_t router_kind;
+  int32_t num_tokens;
+  int32_t n_routed_experts;
+  int32_t n_experts_per_tok;
+  int32_t n_shared_experts;
+  int32_t hidden_dim;
+  const void* x;
+  const void* w_gate;
+  const float* logits;
+  int64_t logits_ld;
+  float* logits_out;
+  const float* expert_bias;
+  const float* global_scale;
+  float route_scale;
+  int32_t renormalize;
+  int32_t* expert_indices;
+  float* expert_weights;
+  float* sink_weights;
+} moe_route_args_t;
+
+moe_status_t moe_route(const moe_route_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_build_indices -- [SinkRouter] moe_create_indices (bucketing needs every
+ * token's assignment, hence its own launches); [NeMoExperts]
+ * _permute_tokens_for_grouped_mm (sorted token ids, routing weights, counts,
+ * cumulative offsets; n_local_experts / experts_start_idx; token_mask).
+ *
+ * Assignment (t, j) has flat slot t*k + j.  It is kept when
+ * experts_start_idx <= expert_indices[t, j] < experts_start_idx +
+ * n_local_experts and token_mask[t] != 0 (or token_mask is NULL); other
+ * assignments are dropped.  Kept slots are bucketed by local expert; inside a
+ * bucket they keep ascending slot order.
+ *
+ *   num_tokens T, n_experts_per_tok k, experts_start_idx,
+ *   n_local_experts L in [1, 1024]                            host
+ *   expert_indices int32 [T, k]
+ *   expert_weights fp32 [T, k] or NULL
+ *   token_mask     uint8 [T] or NULL
+ *   expert_offsets int32 [L + 1]   out: exclusive prefix of bucket sizes;
+ *                                  expert_offsets[L] = kept rows
+ *   sorted_token   int32 [T*k]     out: token of CSR row p (p < kept)
+ *   row_of_slot    int32 [T*k]     out: CSR row of slot t*k+j, -1 if dropped
+ *   sorted_weight  fp32 [T*k] or NULL  out: expert_weights of CSR row p
+ *   x              bf16 [T, H] or NULL   optional row gather:
+ *   hidden_dim H                   host
+ *   xperm_dtype    host: MOE_DTYPE_BF16 (copy rows) or
+ *                  MOE_DTYPE_FP8_E4M3_BLOCK128 (per-token 1x128 e4m3 with
+ *                  scale amax/448, 1 when amax = 0; H % 128 == 0)
+ *   x_perm         [T*k, H] bf16 or uint8 out, rows p < kept written
+ *   x_perm_scale   fp32 [T*k, H/128] out (fp8 only)
+ *   workspace      device scratch of moe_build_indices_workspace_bytes()
+ * Rows p >= expert_offsets[L] of the outputs are left unwritten.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_index_args {
+  int32_t num_tokens;
+  int32_t n_experts_per_tok;
+  int32_t experts_start_idx;
+  int32_t n_local_experts;
+  const int32_t* expert_indices;
+  const float* expert_weights;
+  const uint8_t* token_mask;
+  int32_t* expert_offsets;
+  int32_t* sorted_token;
+  int32_t* row_of_slot;
+  float* sorted_weight;
+  const void* x;
+  int32_t hidden_dim;
+  int32_t xperm_dtype;
+  void* x_perm;
+  float* x_perm_scale;
+  void* workspace;
+  int64_t workspace_bytes;
+} moe_index_args_t;
+
+moe_status_t moe_build_indices(const moe_index_args_t* args, void* stream);
+int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_per_tok,
+                                          int32_t n_local_experts);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_ffn -- [StackedMoE] weight shapes, gate_up_format, has_bias,
+ * quant_config (FP8 block scaling); [GatedAct] fused_activation, alpha, limit;
+ * [NeMoExperts] _apply_bias; [MegaFFN] per-leg expert scales.
+ *
+ * For every local expert e and every CSR row p in
+ * [expert_offsets[e], expert_offsets[e+1]):
+ *   h      = gate_up_expert_scales[e] * (x_p . W_gu[e]) + b_gate_up[e]   (fp32)
+ *   gate, up = split(h): CONCATENATED [gate | up], INTERLEAVED gate = even
+ *            columns, up = odd columns (the bias follows the same order)
+ *   A[p]   = activation(gate, up)            stored bf16 (fp8 path: e4m3 with
+ *            a per-row 1x128 scale amax/448)
+ *   O[p]   = down_expert_scales[e] * (A[p] . W_d[e]) + b_down[e]
+ * activation (GatedAct): SILU silu(gate)*up, with limit > 0 gate=min(gate,limit)
+ *   and up=clamp(up,-limit,limit) first; SWIGLUOAI g*sigmoid(alpha*g)*(u+1)
+ *   with the same clamps (limit 0 = no clamp); GELU_TANH gelu(gate)*up,
+ *   tanh approximation.  alpha must be 0 unless SWIGLUOAI; limit must be 0
+ *   for GELU_TANH and >= 0 otherwise.
+ *
+ *   max_rows       host: rows allocated in x_perm / act / expert_out
+ *                  (>= expert_offsets[L]); the row count itself is read on
+ *                  the device, no host synchronisation
+ *   hidden_dim H, moe_dim D, n_local_experts L in [1, 1024]       host
+ *   expert_offsets int32 [L + 1]
+ *   operand_dtype  host: MOE_DTYPE_BF16 or MOE_DTYPE_FP8_E4M3_BLOCK128
+ *   x_perm         [max_rows, H] bf16 (or e4m3 codes) -- or NULL to gather
+ *                  rows straight from x through sorted_token (bf16 only)
+ *   x_perm_scale   fp32 [max_rows, H/128]            fp8 only
+ *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form
+ *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]
+ *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128]
+ *   b_gate_up      bf16 [L, 2D] or NULL
+ *   w_down         layout IN_OUT [L, D, H] or OUT_IN [L, H, D]
+ *   w_down_scale   fp32 [L, D/128, H/128] (IN_OUT) or [L, H/128, D/128]
+ *   b_down         bf16 [L, H] or NULL
+ *   gate_up_expert_scales, down_expert_scales  fp32 [L] or NULL (1.0)
+ *   act_workspace  device buffer for A, moe_ffn_workspace_bytes() long
+ *   out_dtype      host: MOE_DTYPE_FP32 or MOE_DTYPE_BF16
+ *   expert_out     O [max_rows, H]; rows p >= expert_offsets[L] unwritten
+ *   timing_events  NULL, or an array of 3 hipEvent_t created by the caller:
+ *                  recorded on `stream` before the gate_up GEMM, between the
+ *                  two GEMMs and after the down GEMM (per-kernel timing)
+ * The weight pointers already point at the first local expert.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_ffn_args {
+  int32_t max_rows;
+  int32_t hidden_dim;
+  int32_t moe_dim;
+  int32_t n_local_experts;
+  const int32_t* expert_offsets;
+  int32_t operand_dtype;
+  const void* x_perm;
+  const float* x_perm_scale;
+  const void* x;
+  const int32_t* sorted_token;
+  const void* w_gate_up;
+  int32_t w_gate_up_layout;
+  const float* w_gate_up_scale;
+  const void* b_gate_up;
+  int32_t gate_up_format;
+  const void* w_down;
+  int32_t w_down_layout;
+  const float* w_down_scale;
+  const void* b_down;
+  int32_t activation;
+  float alpha;
+  float limit;
+  const float* gate_up_expert_scales;
+  const float* down_expert_scales;
+  void* act_workspace;
+  int64_t act_workspace_bytes;
+  int32_t out_dtype;
+  void* expert_out;
+  void* const* timing_events;
+} moe_ffn_args_t;
+
+moe_status_t moe_grouped_ffn(const moe_ffn_args_t* args, void* stream);
+int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t operand_dtype);
+
+/* ------------------------------------------------------------------------
+ * moe_combine -- [NeMoExperts] GroupedExperts.forward returns [T, dim]; the
+ * down bias is weighted by the routing probability (_apply_bias), which this
+ * form gives since the bias is inside O.
+ *
+ *   y[t] = sum over j = 0..k-1 with row_of_slot[t, j] >= 0 of
+ *          expert_weights[t, j] * O[row_of_slot[t, j]]
+ * summed in fp32 in ascending j, rounded to bf16; masked tokens give zero
+ * rows.  Deterministic (a gather, no atomics).
+ *
+ *   num_tokens T, n_experts_per_tok k, hidden_dim H               host
+ *   expert_out     O [*, H], fp32 or bf16 (out_dtype, host)
+ *   row_of_slot    int32 [T, k]
+ *   expert_weights fp32 [T, k] or NULL (weight 1: router weight applied first)
+ *   token_mask     uint8 [T] or NULL
+ *   y              bf16 [T, H] out
+ * ---------------------------------------------------------------------- */
+typedef struct moe_combine_args {
+  int32_t num_tokens;
+  int32_t n_experts_per_tok;
+  int32_t hidden_dim;
+  const void* expert_out;
+  int32_t out_dtype;
+  const int32_t* row_of_slot;
+  const float* expert_weights;
+  const uint8_t* token_mask;
+  void* y;
+} moe_combine_args_t;
+
+moe_status_t moe_combine(const moe_combine_args_t* args, void* stream);
+
+/* Helpers. */
+const char* moe_status_string(moe_status_t status);
+/* Message of the last failed call on this host thread ("" if none). */
+const char* moe_last_error_message(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,345 @@
+"""MI355X (gfx950) MoE FFN forward pass: thin Python binding of libmoe_mi355x.so.
+
+The four steps of the layer run in the HIP library, called through its C ABI
+(include/moe_mi355x.h) with ctypes.  This module only checks tensor dtypes,
+shapes and devices, allocates outputs with torch (device memory) and passes
+raw pointers plus torch's current stream.  There is no fallback: the first
+call raises ImportError when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+ROUTER_SOFTMAX_TOPK, ROUTER_SIGMOID_SINK = 0, 1
+ACT = {"silu": 0, "swigluoai": 1, "gelu_tanh": 2}
+FMT = {"concatenated": 0, "interleaved": 1}
+DTYPE_BF16, DTYPE_FP8_E4M3_BLOCK128, DTYPE_FP32 = 0, 1, 2
+WEIGHT_IN_OUT, WEIGHT_OUT_IN = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+
+
+class RouteArgs(ctypes.Structure):
+    _fields_ = [("router_kind", _i32), ("num_tokens", _i32), ("n_routed_experts", _i32),
+                ("n_experts_per_tok", _i32), ("n_shared_experts", _i32), ("hidden_dim", _i32),
+                ("x", _vp), ("w_gate", _vp), ("logits", _vp), ("logits_ld", _i64),
+                ("logits_out", _vp), ("expert_bias", _vp), ("global_scale", _vp),
+                ("route_scale", _f32), ("renormalize", _i32), ("expert_indices", _vp),
+                ("expert_weights", _vp), ("sink_weights", _vp)]
+
+
+class IndexArgs(ctypes.Structure):
+    _fields_ = [("num_tokens", _i32), ("n_experts_per_tok", _i32), ("experts_start_idx", _i32),
+                ("n_local_experts", _i32), ("expert_indices", _vp), ("expert_weights", _vp),
+                ("token_mask", _vp), ("expert_offsets", _vp), ("sorted_token", _vp),
+                ("row_of_slot", _vp), ("sorted_weight", _vp), ("x", _vp), ("hidden_dim", _i32),
+                ("xperm_dtype", _i32), ("x_perm", _vp), ("x_perm_scale", _vp),
+                ("workspace", _vp), ("workspace_bytes", _i64)]
+
+
+class FfnArgs(ctypes.Structure):
+    _fields_ = [("max_rows", _i32), ("hidden_dim", _i32), ("moe_dim", _i32),
+                ("n_local_experts", _i32), ("expert_offsets", _vp), ("operand_dtype", _i32),
+                ("x_perm", _vp), ("x_perm_scale", _vp), ("x", _vp), ("sorted_token", _vp),
+                ("w_gate_up", _vp), ("w_gate_up_layout", _i32), ("w_gate_up_scale", _vp),
+                ("b_gate_up", _vp), ("gate_up_format", _i32), ("w_down", _vp),
+                ("w_down_layout", _i32), ("w_down_scale", _vp), ("b_down", _vp),
+                ("activation", _i32), ("alpha", _f32), ("limit", _f32),
+                ("gate_up_expert_scales", _vp), ("down_expert_scales", _vp),
+                ("act_workspace", _vp), ("act_workspace_bytes", _i64), ("out_dtype", _i32),
+                ("expert_out", _vp), ("timing_events", _vp)]
+
+
+class CombineArgs(ctypes.Structure):
+    _fields_ = [("num_tokens", _i32), ("n_experts_per_tok", _i32), ("hidden_dim", _i32),
+                ("expert_out", _vp), ("out_dtype", _i32), ("row_of_slot", _vp),
+                ("expert_weights", _vp), ("token_mask", _vp), ("y", _vp)]
+
+
+ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_combine",
+                "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
+                "moe_status_string", "moe_last_error_message", "moe_abi_version")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_ffn_top_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, argt in (("moe_route", RouteArgs), ("moe_build_indices", IndexArgs),
+                       ("moe_grouped_ffn", FfnArgs), ("moe_combine", CombineArgs)):
+        f = getattr(lib, name)
+        f.argtypes = [ctypes.POINTER(argt), _vp]
+        f.restype = _i32
+    lib.moe_build_indices_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    lib.moe_build_indices_workspace_bytes.restype = _i64
+    lib.moe_ffn_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    lib.moe_ffn_workspace_bytes.restype = _i64
+    lib.moe_status_string.argtypes = [_i32]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error_message.argtypes = []
+    lib.moe_last_error_message.restype = ctypes.c_char_p
+    lib.moe_abi_version.argtypes = []
+    lib.moe_abi_version.restype = _i32
+    return lib
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (loaded on first use; raises if it is not built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+class MoEError(ValueError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{lib().moe_status_string(status).decode()}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != MOE_OK:
+        raise MoEError(status, lib().moe_last_error_message().decode())
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dt(t, dtype, name):
+    if t is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+
+
+# ------------------------------------------------------------------ the four calls
+
+def route(*, router: str, k: int, E: int, s: int = 0, x=None, w_gate=None, logits=None,
+          expert_bias=None, route_scale: float = 1.0, global_scale=None, renormalize: bool = True,
+          return_logits: bool = False):
+    """moe_route.  Returns (indices int32 [T,k], weights fp32 [T,k],
+    sink_weights fp32 [T,s] or None, logits fp32 [T,E] or None)."""
+    src = logits if logits is not None else x
+    T = src.shape[0]
+    dev = src.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    sw = torch.empty((T, s), dtype=torch.float32, device=dev) if s > 0 else None
+    lo = torch.empty((T, E), dtype=torch.float32, device=dev) if (return_logits and logits is None) else None
+    _dt(x, torch.bfloat16, "x")
+    _dt(w_gate, torch.bfloat16, "w_gate")
+    _dt(logits, torch.float32, "logits")
+    _dt(expert_bias, torch.float32, "expert_bias")
+    _dt(global_scale, torch.float32, "global_scale")
+    a = RouteArgs(router_kind=ROUTER_SOFTMAX_TOPK if router == "softmax" else ROUTER_SIGMOID_SINK,
+                  num_tokens=T, n_routed_experts=E, n_experts_per_tok=k, n_shared_experts=s,
+                  hidden_dim=x.shape[1] if x is not None else 0,
+                  x=_ptr(x), w_gate=_ptr(w_gate), logits=_ptr(logits),
+                  logits_ld=logits.stride(0) if logits is not None else 0,
+                  logits_out=_ptr(lo), expert_bias=_ptr(expert_bias), global_scale=_ptr(global_scale),
+                  route_scale=route_scale, renormalize=int(renormalize),
+                  expert_indices=_ptr(idx), expert_weights=_ptr(w), sink_weights=_ptr(sw))
+    _check(lib().moe_route(ctypes.byref(a), _stream(dev)))
+    return idx, w, sw, lo
+
+
+def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None, token_mask=None,
+                  x=None, xperm_dtype: str = "bf16"):
+    """moe_build_indices.  Returns a dict of device tensors: offsets, sorted_token,
+    row_of_slot, sorted_weight (if weights), x_perm / x_perm_scale (if x)."""
+    T, k = indices.shape
+    dev = indices.device
+    _dt(indices, torch.int32, "indices")
+    _dt(weights, torch.float32, "weights")
+    _dt(token_mask, torch.uint8, "token_mask")
+    R = T * k
+    out = {"offsets": torch.empty(n_local + 1, dtype=torch.int32, device=dev),
+           "sorted_token": torch.empty(max(R, 1), dtype=torch.int32, device=dev),
+           "row_of_slot": torch.empty(max(R, 1), dtype=torch.int32, device=dev)}
+    if weights is not None:
+        out["sorted_weight"] = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
+    H = 0
+    fp8 = xperm_dtype == "fp8"
+    if x is not None:
+        _dt(x, torch.bfloat16, "x")
+        H = x.shape[1]
+        out["x_perm"] = torch.empty((max(R, 1), H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        if fp8:
+            out["x_perm_scale"] = torch.empty((max(R, 1), H // 128), dtype=torch.float32, device=dev)
+    wsb = lib().moe_build_indices_workspace_bytes(T, k, n_local)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    a = IndexArgs(num_tokens=T, n_experts_per_tok=k, experts_start_idx=expert_start,
+                  n_local_experts=n_local, expert_indices=_ptr(indices), expert_weights=_ptr(weights),
+                  token_mask=_ptr(token_mask), expert_offsets=_ptr(out["offsets"]),
+                  sorted_token=_ptr(out["sorted_token"]), row_of_slot=_ptr(out["row_of_slot"]),
+                  sorted_weight=_ptr(out.get("sorted_weight")), x=_ptr(x), hidden_dim=H,
+                  xperm_dtype=DTYPE_FP8_E4M3_BLOCK128 if fp8 else DTYPE_BF16,
+                  x_perm=_ptr(out.get("x_perm")), x_perm_scale=_ptr(out.get("x_perm_scale")),
+                  workspace=_ptr(ws), workspace_bytes=ws.numel())
+    _check(lib().moe_build_indices(ctypes.byref(a), _stream(dev)))
+    return out
+
+
+def ffn_workspace(max_rows: int, D: int, operand: str, device) -> torch.Tensor:
+    n = lib().moe_ffn_workspace_bytes(max_rows, D, DTYPE_FP8_E4M3_BLOCK128 if operand == "fp8" else DTYPE_BF16)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None, x_perm_scale=None,
+                x=None, sorted_token=None, activation="silu", alpha=0.0, limit=0.0,
+                gate_up_format="concatenated", gate_up_expert_scales=None, down_expert_scales=None,
+                out_dtype=torch.float32, act_workspace=None, out=None, timing_events=None):
+    """moe_grouped_ffn.  Returns O [max_rows, H] (rows past offsets[-1] unwritten).
+
+    timing_events: optional ctypes array of 3 hipEvent_t handles, recorded
+    before the gate_up GEMM, between the GEMMs and after the down GEMM."""
+    dev = offsets.device
+    L, H, D = weights.L, weights.H, weights.D
+    if act_workspace is None:
+        act_workspace = ffn_workspace(max_rows, D, weights.operand, dev)
+    if out is None:
+        out = torch.empty((max(max_rows, 1), H), dtype=out_dtype, device=dev)
+    _dt(offsets, torch.int32, "offsets")
+    a = FfnArgs(max_rows=max_rows, hidden_dim=H, moe_dim=D, n_local_experts=L,
+                expert_offsets=_ptr(offsets),
+                operand_dtype=DTYPE_FP8_E4M3_BLOCK128 if weights.operand == "fp8" else DTYPE_BF16,
+                x_perm=_ptr(x_perm), x_perm_scale=_ptr(x_perm_scale), x=_ptr(x),
+                sorted_token=_ptr(sorted_token),
+                w_gate_up=_ptr(weights.w_gate_up), w_gate_up_layout=weights.layout,
+                w_gate_up_scale=_ptr(weights.w_gate_up_scale), b_gate_up=_ptr(weights.b_gate_up),
+                gate_up_format=FMT[gate_up_format], w_down=_ptr(weights.w_down),
+                w_down_layout=weights.layout, w_down_scale=_ptr(weights.w_down_scale),
+                b_down=_ptr(weights.b_down), activation=ACT[activation], alpha=alpha, limit=limit,
+                gate_up_expert_scales=_ptr(gate_up_expert_scales),
+                down_expert_scales=_ptr(down_expert_scales),
+                act_workspace=_ptr(act_workspace), act_workspace_bytes=act_workspace.numel(),
+                out_dtype=DTYPE_BF16 if out_dtype == torch.bfloat16 else DTYPE_FP32,
+                expert_out=_ptr(out),
+                timing_events=ctypes.addressof(timing_events) if timing_events is not None else None)
+    _check(lib().moe_grouped_ffn(ctypes.byref(a), _stream(dev)))
+    return out
+
+
+def combine(expert_out, row_of_slot, T: int, k: int, *, weights=None, token_mask=None, out=None):
+    """moe_combine.  Returns y bf16 [T, H]."""
+    H = expert_out.shape[1]
+    dev = expert_out.device
+    y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    a = CombineArgs(num_tokens=T, n_experts_per_tok=k, hidden_dim=H, expert_out=_ptr(expert_out),
+                    out_dtype=DTYPE_BF16 if expert_out.dtype == torch.bfloat16 else DTYPE_FP32,
+                    row_of_slot=_ptr(row_of_slot), expert_weights=_ptr(weights),
+                    token_mask=_ptr(token_mask), y=_ptr(y))
+    _check(lib().moe_combine(ctypes.byref(a), _stream(dev)))
+    return y
+
+
+# ------------------------------------------------------------------ weights and the whole layer
+
+@dataclass
+class ExpertWeights:
+    """Stacked expert weights as the library consumes them.
+
+    layout WEIGHT_OUT_IN: w_gate_up [L, 2D, H], w_down [L, H, D] (the
+    transposed views of the stacked [L, H, 2D] / [L, D, H] weights).
+    """
+    w_gate_up: torch.Tensor
+    w_down: torch.Tensor
+    L: int
+    H: int
+    D: int
+    operand: str = "bf16"
+    layout: int = WEIGHT_OUT_IN
+    w_gate_up_scale: torch.Tensor | None = None
+    w_down_scale: torch.Tensor | None = None
+    b_gate_up: torch.Tensor | None = None
+    b_down: torch.Tensor | None = None
+
+    @staticmethod
+    def from_stacked(w_gate_up, w_down, *, b_gate_up=None, b_down=None, w_gate_up_scale=None,
+                     w_down_scale=None, operand="bf16", layout=WEIGHT_OUT_IN):
+        """Take stacked [L, H, 2D] / [L, D, H] weights and lay them out once,
+        at load time, in the layout the kernels read."""
+        L, H, D2 = w_gate_up.shape
+        D = D2 // 2
+        if layout == WEIGHT_OUT_IN:
+            w_gate_up = w_gate_up.transpose(1, 2).contiguous()
+            w_down = w_down.transpose(1, 2).contiguous()
+            if w_gate_up_scale is not None:
+                w_gate_up_scale = w_gate_up_scale.transpose(1, 2).contiguous()
+                w_down_scale = w_down_scale.transpose(1, 2).contiguous()
+        return ExpertWeights(w_gate_up, w_down, L, H, D, operand, layout, w_gate_up_scale,
+                             w_down_scale, b_gate_up, b_down)
+
+
+class MoELayer:
+    """The whole forward pass over pre-allocated buffers: route ->
+    build_indices -> grouped_ffn -> combine, all on torch's current stream."""
+
+    def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True):
+        self.cfg = cfg
+        dev = inputs["x"].device
+        self.device = dev
+        self.gather = gather and cfg.operand_dtype == "bf16"
+        self.w = ExpertWeights.from_stacked(
+            inputs["w_gate_up"], inputs["w_down"], b_gate_up=inputs.get("b_gate_up"),
+            b_down=inputs.get("b_down"), w_gate_up_scale=inputs.get("w_gate_up_scale"),
+            w_down_scale=inputs.get("w_down_scale"), operand=cfg.operand_dtype, layout=layout)
+        self.w_gate = inputs.get("w_gate")
+        self.logits = inputs.get("logits")
+        self.expert_bias = inputs.get("expert_bias")
+        self.global_scale = torch.tensor([cfg.global_scale], dtype=torch.float32, device=dev)
+        T, k = cfg.T, cfg.k
+        R = T * k
+        self.R = R
+        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev)
+        self.out_dtype = torch.bfloat16 if cfg.operand_dtype == "fp8" else torch.float32
+        self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
+        self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+
+    def forward(self, x, token_mask=None):
+        c = self.cfg
+        if c.router == "softmax":
+            idx, w, sw, _ = route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate,
+                                  route_scale=c.route_scale, global_scale=self.global_scale)
+        else:
+            idx, w, sw, _ = route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=self.logits,
+                                  expert_bias=self.expert_bias, route_scale=c.route_scale,
+                                  global_scale=self.global_scale)
+        ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,
+                            x=None if self.gather else x,
+                            xperm_dtype="fp8" if c.operand_dtype == "fp8" else "bf16")
+        O = grouped_ffn(ind["offsets"], self.R, self.w, x_perm=ind.get("x_perm"),
+                        x_perm_scale=ind.get("x_perm_scale"), x=x if self.gather else None,
+                        sorted_token=ind["sorted_token"] if self.gather else None,
+                        activation=c.activation, alpha=c.alpha, limit=c.limit,
+                        gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
+                        act_workspace=self.act_ws, out=self.O)
+        y = combine(O, ind["row_of_slot"], c.T, c.k, weights=w, token_mask=token_mask, out=self.y)
+        return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O}
+
+
+__all__ = ["lib", "route", "build_indices", "grouped_ffn", "combine", "ExpertWeights", "MoELayer",
+           "MoEError", "load_library", "ENTRY_POINTS", "LIB_PATH"]

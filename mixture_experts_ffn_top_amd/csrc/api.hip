@@ -1,0 +1,271 @@
+// C ABI of the MoE FFN library: host-side argument validation (before any
+// HIP call) and kernel dispatch.  See include/moe_mi355x.h for the contract.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t ok() {
+  g_err[0] = '\0';
+  return MOE_OK;
+}
+
+moe_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+#define REQUIRE(cond, ...)                                                                         \
+  do {                                                                                             \
+    if (!(cond)) return fail(MOE_ERR_INVALID_ARGUMENT, __VA_ARGS__);                               \
+  } while (0)
+
+int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error_message(void) { return g_err; }
+
+const char* moe_status_string(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT: return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+// ---------------------------------------------------------------- route
+moe_status_t moe_route(const moe_route_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_route: args is NULL");
+  const int T = a->num_tokens, E = a->n_routed_experts, k = a->n_experts_per_tok,
+            s = a->n_shared_experts;
+  REQUIRE(T >= 0, "moe_route: num_tokens must be >= 0 (got %d)", T);
+  REQUIRE(E >= 1 && E <= 1024, "moe_route: n_routed_experts must be in [1, 1024] (got %d)", E);
+  REQUIRE(k >= 1 && k <= E && k <= 64,
+          "moe_route: n_experts_per_tok must be in [1, min(n_routed_experts, 64)] (got %d)", k);
+  REQUIRE(s >= 0, "moe_route: n_shared_experts must be >= 0 (got %d)", s);
+  REQUIRE(std::isfinite(a->route_scale), "moe_route: route_scale must be finite");
+  REQUIRE(T == 0 || (a->expert_indices && a->expert_weights),
+          "moe_route: expert_indices and expert_weights are required");
+  hipStream_t st = (hipStream_t)stream;
+  if (a->router_kind == MOE_ROUTER_SOFTMAX_TOPK) {
+    REQUIRE(s == 0, "moe_route: the softmax gate has no sink lanes (n_shared_experts must be 0)");
+    REQUIRE(a->expert_bias == nullptr, "moe_route: expert_bias is only for the sigmoid router");
+    const bool xform = a->logits == nullptr;
+    if (xform) {
+      REQUIRE(a->x != nullptr && a->w_gate != nullptr,
+              "moe_route: softmax router needs logits, or x and w_gate");
+      REQUIRE(E <= 128, "moe_route: the fused gate GEMM supports n_routed_experts <= 128 (got %d)", E);
+      REQUIRE(a->hidden_dim >= 8 && a->hidden_dim % 8 == 0,
+              "moe_route: hidden_dim must be a positive multiple of 8 (got %d)", a->hidden_dim);
+      REQUIRE(aligned16(a->x) && aligned16(a->w_gate), "moe_route: x and w_gate must be 16-byte aligned");
+      return hip_status(moe::launch_router_softmax_x(
+                            (const uint16_t*)a->x, (const uint16_t*)a->w_gate, T, a->hidden_dim, E, k,
+                            a->route_scale, a->global_scale, a->renormalize, a->logits_out,
+                            a->expert_indices, a->expert_weights, st),
+                        "moe_route");
+    }
+    REQUIRE(a->x == nullptr, "moe_route: pass either logits or x/w_gate, not both");
+    REQUIRE(a->logits_ld >= E, "moe_route: logits_ld must be >= n_routed_experts");
+    return hip_status(moe::launch_router_softmax_logits(a->logits, a->logits_ld, T, E, k,
+                                                        a->route_scale, a->global_scale,
+                                                        a->renormalize, a->expert_indices,
+                                                        a->expert_weights, st),
+                      "moe_route");
+  }
+  if (a->router_kind == MOE_ROUTER_SIGMOID_SINK) {
+    REQUIRE(a->logits != nullptr && a->x == nullptr, "moe_route: the sigmoid router takes logits");
+    REQUIRE(is_pow2(k + s) && k + s <= 64,
+            "moe_route: n_experts_per_tok + n_shared_experts must be a power of two <= 64 (got %d)",
+            k + s);
+    REQUIRE(a->logits_ld >= (int64_t)E + s,
+            "moe_route: logits_ld must be >= n_routed_experts + n_shared_experts");
+    REQUIRE(s == 0 || T == 0 || a->sink_weights != nullptr,
+            "moe_route: sink_weights is required when n_shared_experts > 0");
+    return hip_status(moe::launch_router_sigmoid_sink(a->logits, a->logits_ld, a->expert_bias, T, E,
+                                                      k, s, a->route_scale, a->global_scale,
+                                                      a->expert_indices, a->expert_weights,
+                                                      a->sink_weights, st),
+                      "moe_route");
+  }
+  return fail(MOE_ERR_INVALID_ARGUMENT, "moe_route: unknown router_kind %d", a->router_kind);
+}
+
+// ---------------------------------------------------------------- build indices
+int64_t moe_build_indices_workspace_bytes(int32_t T, int32_t k, int32_t L) {
+  if (T < 0 || k < 1 || L < 1) return 0;
+  const int64_t nblk = moe::csr_num_blocks((int64_t)T * k);
+  return round_up(nblk * L * (int64_t)sizeof(int32_t), 256);
+}
+
+moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_build_indices: args is NULL");
+  const int T = a->num_tokens, k = a->n_experts_per_tok, L = a->n_local_experts;
+  REQUIRE(T >= 0, "moe_build_indices: num_tokens must be >= 0 (got %d)", T);
+  REQUIRE(k >= 1 && k <= 1024, "moe_build_indices: n_experts_per_tok must be in [1, 1024] (got %d)", k);
+  REQUIRE(L >= 1 && L <= 1024, "moe_build_indices: n_local_experts must be in [1, 1024] (got %d)", L);
+  REQUIRE((int64_t)T * k < (int64_t)1 << 31, "moe_build_indices: num_tokens * n_experts_per_tok must be < 2^31");
+  REQUIRE(a->expert_offsets != nullptr, "moe_build_indices: expert_offsets is required");
+  REQUIRE(T == 0 || (a->expert_indices && a->sorted_token && a->row_of_slot),
+          "moe_build_indices: expert_indices, sorted_token and row_of_slot are required");
+  const int64_t need = moe_build_indices_workspace_bytes(T, k, L);
+  if (a->workspace_bytes < need || (need > 0 && a->workspace == nullptr))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_build_indices: workspace needs %lld bytes (got %lld)",
+                (long long)need, (long long)a->workspace_bytes);
+  REQUIRE(aligned16(a->workspace), "moe_build_indices: workspace must be 16-byte aligned");
+  const bool permute = a->x != nullptr;
+  if (permute) {
+    const int H = a->hidden_dim;
+    REQUIRE(H >= 8 && H % 8 == 0, "moe_build_indices: hidden_dim must be a positive multiple of 8 (got %d)", H);
+    REQUIRE(a->x_perm != nullptr, "moe_build_indices: x_perm is required with x");
+    REQUIRE(aligned16(a->x) && aligned16(a->x_perm), "moe_build_indices: x and x_perm must be 16-byte aligned");
+    if (a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
+      REQUIRE(H % 128 == 0, "moe_build_indices: fp8 quantisation needs hidden_dim % 128 == 0 (got %d)", H);
+      REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for fp8");
+    } else {
+      REQUIRE(a->xperm_dtype == MOE_DTYPE_BF16, "moe_build_indices: xperm_dtype must be BF16 or FP8_E4M3_BLOCK128");
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_build_indices(a->expert_indices, a->expert_weights, a->token_mask, T, k,
+                                           a->experts_start_idx, L, a->expert_offsets,
+                                           a->sorted_token, a->row_of_slot, a->sorted_weight,
+                                           (int32_t*)a->workspace, st);
+  if (e != hipSuccess) return hip_status(e, "moe_build_indices");
+  if (permute) {
+    e = moe::launch_permute((const uint16_t*)a->x, a->sorted_token, a->expert_offsets + L,
+                            (int64_t)T * k, a->hidden_dim,
+                            a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128, a->x_perm,
+                            a->x_perm_scale, st);
+    if (e != hipSuccess) return hip_status(e, "moe_build_indices (permute)");
+  }
+  return ok();
+}
+
+// ---------------------------------------------------------------- grouped FFN
+int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t D, int32_t dtype) {
+  if (max_rows < 0 || D < 1) return 0;
+  if (dtype == MOE_DTYPE_FP8_E4M3_BLOCK128)
+    return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 127) / 128) * 4, 256);
+  return round_up((int64_t)max_rows * D * 2, 256);
+}
+
+moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_grouped_ffn: args is NULL");
+  const int R = a->max_rows, H = a->hidden_dim, D = a->moe_dim, L = a->n_local_experts;
+  REQUIRE(R >= 0, "moe_grouped_ffn: max_rows must be >= 0 (got %d)", R);
+  REQUIRE(H >= 8 && H % 8 == 0, "moe_grouped_ffn: hidden_dim must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(D >= 8 && D % 8 == 0, "moe_grouped_ffn: moe_dim must be a positive multiple of 8 (got %d)", D);
+  REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn: n_local_experts must be in [1, 1024] (got %d)", L);
+  REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn: expert_offsets is required");
+  REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI ||
+              a->activation == MOE_ACT_GELU_TANH,
+          "moe_grouped_ffn: unknown activation %d", a->activation);
+  REQUIRE(std::isfinite(a->alpha) && std::isfinite(a->limit), "moe_grouped_ffn: alpha and limit must be finite");
+  REQUIRE(a->activation == MOE_ACT_SWIGLUOAI || a->alpha == 0.0f,
+          "moe_grouped_ffn: alpha is the sigmoid scale of swigluoai and must be 0 for the other activations");
+  REQUIRE(a->activation != MOE_ACT_GELU_TANH || a->limit == 0.0f,
+          "moe_grouped_ffn: limit must be 0 for gelu_tanh");
+  REQUIRE(a->limit >= 0.0f, "moe_grouped_ffn: limit must be >= 0");
+  REQUIRE(a->gate_up_format == MOE_GATE_UP_CONCATENATED || a->gate_up_format == MOE_GATE_UP_INTERLEAVED,
+          "moe_grouped_ffn: unknown gate_up_format %d", a->gate_up_format);
+  REQUIRE(a->out_dtype == MOE_DTYPE_FP32 || a->out_dtype == MOE_DTYPE_BF16,
+          "moe_grouped_ffn: out_dtype must be FP32 or BF16");
+  REQUIRE(a->w_gate_up_layout == MOE_WEIGHT_IN_OUT || a->w_gate_up_layout == MOE_WEIGHT_OUT_IN,
+          "moe_grouped_ffn: unknown w_gate_up_layout");
+  REQUIRE(a->w_down_layout == MOE_WEIGHT_IN_OUT || a->w_down_layout == MOE_WEIGHT_OUT_IN,
+          "moe_grouped_ffn: unknown w_down_layout");
+  REQUIRE(a->w_gate_up && a->w_down, "moe_grouped_ffn: w_gate_up and w_down are required");
+  REQUIRE(R == 0 || a->expert_out != nullptr, "moe_grouped_ffn: expert_out is required");
+  const bool gather = a->x_perm == nullptr;
+  if (gather) {
+    REQUIRE(R == 0 || (a->x != nullptr && a->sorted_token != nullptr),
+            "moe_grouped_ffn: pass x_perm, or x and sorted_token to gather rows");
+  } else {
+    REQUIRE(a->x == nullptr, "moe_grouped_ffn: pass either x_perm or x/sorted_token, not both");
+  }
+  REQUIRE(aligned16(a->x_perm) && aligned16(a->x) && aligned16(a->w_gate_up) && aligned16(a->w_down) &&
+              aligned16(a->act_workspace) && aligned16(a->expert_out),
+          "moe_grouped_ffn: tensors must be 16-byte aligned");
+  const int64_t need = moe_ffn_workspace_bytes(R, D, a->operand_dtype);
+  if (a->act_workspace_bytes < need || (need > 0 && a->act_workspace == nullptr))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn: act_workspace needs %lld bytes (got %lld)",
+                (long long)need, (long long)a->act_workspace_bytes);
+  if (a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
+    REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: fp8 needs hidden_dim and moe_dim multiples of 128");
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path is not built yet");
+  }
+  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn: operand_dtype must be BF16 or FP8_E4M3_BLOCK128");
+  if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 weights must use the OUT_IN layout for now");
+  if (R == 0) return ok();
+  moe::FfnBf16Params p{};
+  p.offsets = a->expert_offsets;
+  p.L = L;
+  p.H = H;
+  p.D = D;
+  p.max_rows = R;
+  p.x_perm = (const uint16_t*)a->x_perm;
+  p.x = (const uint16_t*)a->x;
+  p.sorted_token = a->sorted_token;
+  p.w_gate_up = (const uint16_t*)a->w_gate_up;
+  p.b_gate_up = (const uint16_t*)a->b_gate_up;
+  p.w_down = (const uint16_t*)a->w_down;
+  p.b_down = (const uint16_t*)a->b_down;
+  p.gate_up_scales = a->gate_up_expert_scales;
+  p.down_scales = a->down_expert_scales;
+  p.fmt = a->gate_up_format;
+  p.act_kind = a->activation;
+  p.alpha = a->alpha;
+  p.limit = a->limit;
+  p.act = (uint16_t*)a->act_workspace;
+  p.out = a->expert_out;
+  p.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+  p.events = (hipEvent_t const*)a->timing_events;
+  return hip_status(moe::launch_ffn_bf16(p, (hipStream_t)stream), "moe_grouped_ffn");
+}
+
+// ---------------------------------------------------------------- combine
+moe_status_t moe_combine(const moe_combine_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_combine: args is NULL");
+  const int T = a->num_tokens, k = a->n_experts_per_tok, H = a->hidden_dim;
+  REQUIRE(T >= 0, "moe_combine: num_tokens must be >= 0 (got %d)", T);
+  REQUIRE(k >= 1 && k <= 1024, "moe_combine: n_experts_per_tok must be in [1, 1024] (got %d)", k);
+  REQUIRE(H >= 8 && H % 8 == 0, "moe_combine: hidden_dim must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(a->out_dtype == MOE_DTYPE_FP32 || a->out_dtype == MOE_DTYPE_BF16,
+          "moe_combine: out_dtype must be FP32 or BF16");
+  REQUIRE(T == 0 || (a->expert_out && a->row_of_slot && a->y),
+          "moe_combine: expert_out, row_of_slot and y are required");
+  REQUIRE(aligned16(a->expert_out) && aligned16(a->y), "moe_combine: expert_out and y must be 16-byte aligned");
+  return hip_status(moe::launch_combine(a->expert_out, a->out_dtype == MOE_DTYPE_BF16, a->row_of_slot,
+                                        a->expert_weights, a->token_mask, T, k, H, (uint16_t*)a->y,
+                                        (hipStream_t)stream),
+                    "moe_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Router-weighted combine: y[t] = sum_j w[t, j] * O[row_of_slot[t, j]],
+// fp32 sums in ascending j, bf16 out; one wave per token, 8 columns per lane
+// per step, 16-byte loads and stores.  A gather with a fixed order, so the
+// result is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+template <bool O_BF16>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O,
+                                                      const int32_t* __restrict__ row_of_slot,
+                                                      const float* __restrict__ w,
+                                                      const uint8_t* __restrict__ mask, int T,
+                                                      int k, int H, uint16_t* __restrict__ y) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const bool valid = mask ? (mask[t] != 0) : true;
+  for (int c = lane * 8; c < H; c += 512) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    if (valid) {
+      for (int j = 0; j < k; ++j) {
+        const int r = row_of_slot[(int64_t)t * k + j];
+        if (r < 0) continue;
+        const float wt = w ? w[(int64_t)t * k + j] : 1.0f;
+        if (O_BF16) {
+          const u32x4_t v = *(const u32x4_t*)((const uint16_t*)O + (int64_t)r * H + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wt * bf16_to_f32((uint16_t)(v[i] & 0xffffu));
+            acc[2 * i + 1] += wt * bf16_to_f32((uint16_t)(v[i] >> 16));
+          }
+        } else {
+          const f32x4_t* src = (const f32x4_t*)((const float*)O + (int64_t)r * H + c);
+          const f32x4_t a = src[0], b = src[1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] += wt * a[i];
+            acc[4 + i] += wt * b[i];
+          }
+        }
+      }
+    }
+    u32x4_t out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+    *(u32x4_t*)(y + (int64_t)t * H + c) = out;
+  }
+}
+
+hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
+                          const uint8_t* mask, int T, int k, int H, uint16_t* y, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((T + 3) / 4), block(256);
+  if (o_bf16)
+    combine_kernel<true><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y);
+  else
+    combine_kernel<false><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,138 @@
+// Shared device helpers for the gfx950 MoE kernels: number formats, wave64
+// reductions, activation math, MFMA vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_WAVE 64
+
+namespace moe {
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- e4m3fn
+// float -> OCP e4m3fn code, round to nearest even, saturating at +-448.
+__device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
+  uint32_t u = __float_as_uint(f);
+  uint32_t sign = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint8_t)(sign | 0x7fu);   // NaN
+  if (a >= 0x43e00000u) return (uint8_t)(sign | 0x7eu);  // >= 448 (and inf): saturate
+  float af = __uint_as_float(a);
+  int e = (int)(a >> 23) - 127;                            // unbiased exponent
+  if (e < -6) {
+    // subnormal range: value / 2^-9, rounded to nearest even integer in [0, 8]
+    float q = rintf(af * 512.0f);                          // exact scaling
+    return (uint8_t)(sign | (uint32_t)q);                  // q == 8 is the code of 2^-6
+  }
+  // normal: keep 3 mantissa bits, round to nearest even on the 20 dropped bits
+  uint32_t m = a & 0x7fffffu;
+  uint32_t rest = m & 0xfffffu;
+  uint32_t keep = m >> 20;
+  uint32_t half = 0x80000u;
+  if (rest > half || (rest == half && (keep & 1u))) keep += 1;
+  uint32_t ef = (uint32_t)(e + 7);
+  if (keep == 8) { keep = 0; ef += 1; }
+  (void)af;
+  return (uint8_t)(sign | (ef << 3) | keep);
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
+  uint32_t s = (c & 0x80u) << 24;
+  uint32_t ef = (c >> 3) & 0xfu;
+  uint32_t m = c & 7u;
+  float v;
+  if (ef == 0) v = (float)m * (1.0f / 512.0f);
+  else v = __uint_as_float(((ef + 120u) << 23) | (m << 20));
+  if (ef == 15 && m == 7) v = __uint_as_float(0x7fc00000u);
+  return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// ---------------------------------------------------------------- wave64 reductions
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, o, MOE_WAVE);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, MOE_WAVE);
+    uint64_t w = ((uint64_t)hi << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of a float key to uint32 (-0 is taken as +0), packed
+// with the expert index so that the u64 maximum is the largest key and, among
+// equal keys, the lowest index.
+__device__ __forceinline__ uint64_t pack_key(float key, int idx) {
+  uint32_t u = __float_as_uint(key);
+  if (u == 0x80000000u) u = 0;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
+}
+__device__ __forceinline__ int unpack_idx(uint64_t p) { return (int)(0xffffffffu - (uint32_t)p); }
+
+// The router's float32 sigmoid: exp(-z) rounded once to float32, then a
+// correctly rounded add and divide.
+__device__ __forceinline__ float sigmoid_key_f32(float z) {
+  float e = (float)exp(-(double)z);
+  return __fdiv_rn(1.0f, __fadd_rn(1.0f, e));
+}
+
+__device__ __forceinline__ float log_sigmoid_f32(float v) {
+  return fminf(v, 0.0f) - log1pf(expf(-fabsf(v)));
+}
+
+// ---------------------------------------------------------------- activations
+enum { ACT_SILU = 0, ACT_SWIGLUOAI = 1, ACT_GELU_TANH = 2 };
+
+__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+template <int ACT>
+__device__ __forceinline__ float gated_act(float g, float u, float alpha, float limit) {
+  if (ACT == ACT_SILU || ACT == ACT_SWIGLUOAI) {
+    if (limit > 0.0f) {
+      g = fminf(g, limit);
+      u = fminf(fmaxf(u, -limit), limit);
+    }
+  }
+  if (ACT == ACT_SILU) return g * sigmoid_f32(g) * u;
+  if (ACT == ACT_SWIGLUOAI) return g * sigmoid_f32(alpha * g) * (u + 1.0f);
+  // gelu_tanh
+  const float c = 0.7978845608028654f, a = 0.044715f;
+  float t = tanhf(c * (g + a * g * g * g));
+  return 0.5f * g * (1.0f + t) * u;
+}
+
+__device__ __forceinline__ int xcd_count() { return 8; }
+
+}  // namespace moe

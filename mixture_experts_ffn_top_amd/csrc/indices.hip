@@ -1,0 +1,218 @@
+// Bucketing of token->expert assignments into a per-expert CSR
+// (moe_create_indices on the sink_gate_router_kernel page: it needs every
+// token's assignment, so it runs after the router as its own launches), and
+// the row gather of the activations, optionally with the per-token 1x128
+// e4m3 quantisation of the fp8 layer.
+//
+//   csr_hist    per block of IDX_SLOTS flat slots: LDS histogram over local
+//               experts -> counts[e][block]
+//   csr_scan    one workgroup: exclusive scan over blocks per expert, then over
+//               experts -> expert_offsets and per-(expert, block) bases
+//   csr_scatter per block: stable rank of each slot among same-expert slots
+//               (wave ballots per distinct expert, LDS running counts) ->
+//               sorted_token, row_of_slot, sorted_weight
+//   permute     x_perm[p] = x[sorted_token[p]] (bf16 copy, or e4m3 + scales)
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+static constexpr int IDX_SLOTS = 4096;
+
+int64_t csr_num_blocks(int64_t R) { return (R + IDX_SLOTS - 1) / IDX_SLOTS; }
+
+__device__ __forceinline__ int local_expert(const int32_t* idx, const uint8_t* mask, int64_t sl,
+                                            int k, int start, int L) {
+  int e = idx[sl] - start;
+  bool ok = (unsigned)e < (unsigned)L;
+  if (ok && mask) ok = mask[sl / k] != 0;
+  return ok ? e : -1;
+}
+
+__global__ __launch_bounds__(256) void csr_hist_kernel(const int32_t* __restrict__ idx,
+                                                       const uint8_t* __restrict__ mask, int64_t R,
+                                                       int k, int start, int L, int nblk,
+                                                       int32_t* __restrict__ counts) {
+  extern __shared__ int32_t s_h[];
+  for (int e = threadIdx.x; e < L; e += 256) s_h[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * IDX_SLOTS;
+  for (int i = threadIdx.x; i < IDX_SLOTS; i += 256) {
+    const int64_t sl = base + i;
+    if (sl >= R) break;
+    const int e = local_expert(idx, mask, sl, k, start, L);
+    if (e >= 0) atomicAdd(&s_h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < L; e += 256) counts[(int64_t)e * nblk + blockIdx.x] = s_h[e];
+}
+
+// One workgroup of 1024 threads; L <= 1024.
+__global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ counts, int L,
+                                                        int nblk, int32_t* __restrict__ offsets) {
+  __shared__ int32_t s[1024];
+  const int t = threadIdx.x;
+  int32_t tot = 0;
+  if (t < L) {
+    int32_t* c = counts + (int64_t)t * nblk;
+    for (int b = 0; b < nblk; ++b) {
+      int32_t v = c[b];
+      c[b] = tot;
+      tot += v;
+    }
+  }
+  s[t] = tot;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int32_t v = (t >= o) ? s[t - o] : 0;
+    __syncthreads();
+    s[t] += v;
+    __syncthreads();
+  }
+  const int32_t excl = s[t] - tot;
+  if (t < L) {
+    offsets[t] = excl;
+    int32_t* c = counts + (int64_t)t * nblk;
+    for (int b = 0; b < nblk; ++b) c[b] += excl;
+  }
+  if (t == L - 1) offsets[L] = s[t];
+}
+
+__global__ __launch_bounds__(256) void csr_scatter_kernel(
+    const int32_t* __restrict__ idx, const float* __restrict__ w, const uint8_t* __restrict__ mask,
+    int64_t R, int k, int start, int L, int nblk, const int32_t* __restrict__ base,
+    int32_t* __restrict__ sorted_token, int32_t* __restrict__ row_of_slot,
+    float* __restrict__ sorted_weight) {
+  extern __shared__ int32_t sm[];
+  int32_t* running = sm;       // [L]   next CSR row of each expert in this block
+  int32_t* wcnt = sm + L;      // [4][L] this round's count per wave and expert
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < L; e += 256) {
+    running[e] = base[(int64_t)e * nblk + blockIdx.x];
+    wcnt[e] = wcnt[L + e] = wcnt[2 * L + e] = wcnt[3 * L + e] = 0;
+  }
+  __syncthreads();
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int64_t blk0 = (int64_t)blockIdx.x * IDX_SLOTS;
+  for (int round = 0; round < IDX_SLOTS / 256; ++round) {
+    const int64_t sl = blk0 + round * 256 + wave * 64 + lane;
+    if (blk0 + round * 256 >= R) break;  // uniform across the block
+    const int e = (sl < R) ? local_expert(idx, mask, sl, k, start, L) : -1;
+    uint64_t pending = __ballot(e >= 0);
+    int rank = 0;
+    while (pending) {
+      const int leader = __ffsll((unsigned long long)pending) - 1;
+      const int le = __shfl(e, leader, MOE_WAVE);
+      const uint64_t m = __ballot(e == le);
+      if (e == le) rank = __popcll(m & lt_mask);
+      if (lane == leader) wcnt[wave * L + le] = __popcll(m);
+      pending &= ~m;
+    }
+    __syncthreads();
+    if (e >= 0) {
+      int pos = running[e] + rank;
+      for (int w2 = 0; w2 < wave; ++w2) pos += wcnt[w2 * L + e];
+      sorted_token[pos] = (int32_t)(sl / k);
+      row_of_slot[sl] = pos;
+      if (sorted_weight) sorted_weight[pos] = w[sl];
+    } else if (sl < R) {
+      row_of_slot[sl] = -1;
+    }
+    __syncthreads();
+    if (e >= 0 && rank == 0) atomicAdd(&running[e], wcnt[wave * L + e]);
+    __syncthreads();
+    if (e >= 0 && rank == 0) wcnt[wave * L + e] = 0;
+  }
+}
+
+// x_perm[p] = x[sorted_token[p]] for p < offsets_end[0]; one wave per row.
+__global__ __launch_bounds__(256) void permute_bf16_kernel(const uint16_t* __restrict__ x,
+                                                           const int32_t* __restrict__ sorted_token,
+                                                           const int32_t* __restrict__ n_rows,
+                                                           int H, uint16_t* __restrict__ xp) {
+  const int lane = threadIdx.x & 63;
+  const int n = n_rows[0];
+  const int chunks = H / 8;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n; row += gridDim.x * 4) {
+    const u32x4_t* src = (const u32x4_t*)(x + (int64_t)sorted_token[row] * H);
+    u32x4_t* dst = (u32x4_t*)(xp + (int64_t)row * H);
+    for (int c = lane; c < chunks; c += 64) dst[c] = src[c];
+  }
+}
+
+// Per-row, per-128-column e4m3 quantisation fused into the gather: 16 lanes
+// own one 128-column group (8 elements each); a wave does 4 groups at a time.
+__global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __restrict__ x,
+                                                          const int32_t* __restrict__ sorted_token,
+                                                          const int32_t* __restrict__ n_rows, int H,
+                                                          uint8_t* __restrict__ xq,
+                                                          float* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int n = n_rows[0];
+  const int groups = H / 128;
+  const int sub = lane & 15, gq = lane >> 4;
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n; row += gridDim.x * 4) {
+    const uint16_t* src = x + (int64_t)sorted_token[row] * H;
+    for (int g0 = 0; g0 < groups; g0 += 4) {
+      const int g = g0 + gq;
+      const bool ok = g < groups;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (ok) v = *(const u32x4_t*)(src + g * 128 + sub * 8);
+      float f[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf16_to_f32((uint16_t)(v[i] & 0xffffu));
+        f[2 * i + 1] = bf16_to_f32((uint16_t)(v[i] >> 16));
+      }
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
+      const float s = (amax > 0.0f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(f[i], s)) << (8 * i);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(f[4 + i], s)) << (8 * i);
+      if (ok) {
+        uint2 q;
+        q.x = lo;
+        q.y = hi;
+        *(uint2*)(xq + (int64_t)row * H + g * 128 + sub * 8) = q;
+        if (sub == 0) xs[(int64_t)row * groups + g] = s;
+      }
+    }
+  }
+}
+
+hipError_t launch_build_indices(const int32_t* idx, const float* w, const uint8_t* mask, int T,
+                                int k, int start, int L, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* row_of_slot, float* sorted_weight, int32_t* ws,
+                                hipStream_t st) {
+  const int64_t R = (int64_t)T * k;
+  const int nblk = (int)csr_num_blocks(R);
+  if (nblk > 0) {
+    csr_hist_kernel<<<nblk, 256, L * sizeof(int32_t), st>>>(idx, mask, R, k, start, L, nblk, ws);
+  }
+  csr_scan_kernel<<<1, 1024, 0, st>>>(ws, L, nblk, offsets);
+  if (nblk > 0) {
+    csr_scatter_kernel<<<nblk, 256, 5 * L * sizeof(int32_t), st>>>(
+        idx, w, mask, R, k, start, L, nblk, ws, sorted_token, row_of_slot, sorted_weight);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const uint16_t* x, const int32_t* sorted_token, const int32_t* n_rows,
+                          int64_t max_rows, int H, int fp8, void* xp, float* xs, hipStream_t st) {
+  if (max_rows == 0) return hipSuccess;
+  int64_t blocks = (max_rows + 3) / 4;
+  if (blocks > 16384) blocks = 16384;
+  if (fp8)
+    permute_fp8_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, H, (uint8_t*)xp, xs);
+  else
+    permute_bf16_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, H, (uint16_t*)xp);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,52 @@
+// Internal launchers of the HIP kernels (host side).  The public C ABI in
+// include/moe_mi355x.h validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_router_softmax_logits(const float* logits, int64_t ld, int T, int E, int k,
+                                        float scale, const float* gs, int renorm, int32_t* idx,
+                                        float* w, hipStream_t st);
+hipError_t launch_router_softmax_x(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
+                                   int k, float scale, const float* gs, int renorm,
+                                   float* logits_out, int32_t* idx, float* w, hipStream_t st);
+hipError_t launch_router_sigmoid_sink(const float* logits, int64_t ld, const float* bias, int T,
+                                      int E, int k, int s, float scale, const float* gs,
+                                      int32_t* idx, float* w, float* sink_w, hipStream_t st);
+
+int64_t csr_num_blocks(int64_t R);
+hipError_t launch_build_indices(const int32_t* idx, const float* w, const uint8_t* mask, int T,
+                                int k, int start, int L, int32_t* offsets, int32_t* sorted_token,
+                                int32_t* row_of_slot, float* sorted_weight, int32_t* ws,
+                                hipStream_t st);
+hipError_t launch_permute(const uint16_t* x, const int32_t* sorted_token, const int32_t* n_rows,
+                          int64_t max_rows, int H, int fp8, void* xp, float* xs, hipStream_t st);
+
+struct FfnBf16Params {
+  const int32_t* offsets;
+  int L, H, D, max_rows;
+  const uint16_t* x_perm;        // or nullptr: gather from x through sorted_token
+  const uint16_t* x;
+  const int32_t* sorted_token;
+  const uint16_t* w_gate_up;     // OUT_IN [L, 2D, H]
+  const uint16_t* b_gate_up;
+  const uint16_t* w_down;        // OUT_IN [L, H, D]
+  const uint16_t* b_down;
+  const float* gate_up_scales;
+  const float* down_scales;
+  int fmt, act_kind;
+  float alpha, limit;
+  uint16_t* act;                 // [max_rows, D]
+  void* out;                     // [max_rows, H]
+  int out_bf16;
+  hipEvent_t const* events;      // optional: before gate_up, between, after down
+};
+hipError_t launch_ffn_bf16(const FfnBf16Params& p, hipStream_t st);
+
+hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
+                          const uint8_t* mask, int T, int k, int H, uint16_t* y, hipStream_t st);
+
+}  // namespace moe

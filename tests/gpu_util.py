@@ -1,0 +1,53 @@
+"""Helpers shared by the GPU parity tests (not a test module)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+
+def say(*a):
+    """Print and flush, so that a GPU run names its case before each step."""
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t) -> np.ndarray:
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.numpy()
+
+
+def rel_rms_err(got, want) -> tuple[float, float]:
+    """(max |got - want| / rms(want), rms(want))."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    rms = float(np.sqrt(np.mean(w * w)))
+    if rms == 0.0:
+        return float(np.max(np.abs(g - w))) if g.size else 0.0, 0.0
+    return float(np.max(np.abs(g - w)) / rms) if g.size else 0.0, rms
+
+
+def assert_rel(got, want, rtol, what=""):
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    den = np.maximum(np.abs(w), 1e-30)
+    err = float(np.max(np.abs(g - w) / den)) if g.size else 0.0
+    assert err <= rtol, f"{what}: max relative error {err:.3e} > {rtol:.1e}"
+    return err
+
+
+def bf16_floor(y_ref) -> float:
+    """Rounding floor: max |bf16(y) - y| / rms(y) of the oracle's own output."""
+    return rel_rms_err(O.bf16_round(y_ref), y_ref)[0]
+
+
+def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
+    if n >= T:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, n, replace=False))

@@ -1,0 +1,154 @@
+"""The C ABI library on the CPU (no GPU needed): it loads, exports every
+function include/moe_mi355x.h declares, and refuses invalid arguments on the
+host before any HIP call, with a message."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_top_amd as m
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+[\s\*]+(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = m.lib()
+    names = _declared_functions()
+    assert set(names) >= {"moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_combine"}
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared but not exported"
+    assert set(names) == set(m.ENTRY_POINTS)
+    assert lib.moe_abi_version() == 1
+
+
+def test_struct_layouts_match_header_sizes():
+    # pointer-size fields and natural alignment: these sizes follow from the header
+    assert ctypes.sizeof(m.RouteArgs) == 6 * 4 + 3 * 8 + 8 + 3 * 8 + 4 + 4 + 3 * 8
+    assert ctypes.sizeof(m.CombineArgs) == 3 * 4 + 4 + 8 + 4 + 4 + 8 * 4
+
+
+def _err(fn, args):
+    st = fn(ctypes.byref(args), None)
+    return st, m.lib().moe_last_error_message().decode()
+
+
+def _route(**kw):
+    base = dict(router_kind=0, num_tokens=4, n_routed_experts=8, n_experts_per_tok=2, n_shared_experts=0,
+                hidden_dim=64, x=16, w_gate=32, logits=None, logits_ld=0, route_scale=1.0, renormalize=1,
+                expert_indices=48, expert_weights=64)
+    base.update(kw)
+    return m.RouteArgs(**base)
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_experts_per_tok=9), "n_experts_per_tok"),
+    (dict(n_experts_per_tok=0), "n_experts_per_tok"),
+    (dict(n_routed_experts=0), "n_routed_experts"),
+    (dict(num_tokens=-1), "num_tokens"),
+    (dict(n_shared_experts=2), "sink"),
+    (dict(expert_bias=80), "expert_bias"),
+    (dict(hidden_dim=60), "hidden_dim"),
+    (dict(x=17), "aligned"),
+    (dict(n_routed_experts=200, n_experts_per_tok=2), "<= 128"),
+    (dict(x=None, w_gate=None, logits=96, logits_ld=4), "logits_ld"),
+    (dict(router_kind=1, x=None, w_gate=None, logits=96, logits_ld=8, n_experts_per_tok=3), "power of two"),
+    (dict(router_kind=1, x=None, w_gate=None, logits=96, logits_ld=8, n_experts_per_tok=2,
+          n_shared_experts=2), "logits_ld"),
+    (dict(router_kind=1, x=None, w_gate=None, logits=96, logits_ld=10, n_experts_per_tok=2,
+          n_shared_experts=2), "sink_weights"),
+    (dict(router_kind=1, x=None, w_gate=None, logits=96, logits_ld=200, n_routed_experts=128,
+          n_experts_per_tok=64, n_shared_experts=64), "power of two"),
+    (dict(router_kind=7), "router_kind"),
+    (dict(expert_indices=None), "required"),
+    (dict(route_scale=float("inf")), "route_scale"),
+])
+def test_route_validation(kw, frag):
+    st, msg = _err(m.lib().moe_route, _route(**kw))
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+def _ffn(**kw):
+    base = dict(max_rows=64, hidden_dim=256, moe_dim=512, n_local_experts=8, expert_offsets=16,
+                operand_dtype=0, x_perm=32, w_gate_up=48, w_gate_up_layout=1, gate_up_format=0, w_down=64,
+                w_down_layout=1, activation=0, alpha=0.0, limit=0.0, act_workspace=80,
+                act_workspace_bytes=1 << 20, out_dtype=2, expert_out=96)
+    base.update(kw)
+    return m.FfnArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(alpha=1.0), m.MOE_ERR_INVALID_ARGUMENT, "alpha"),
+    (dict(activation=2, limit=7.0), m.MOE_ERR_INVALID_ARGUMENT, "gelu_tanh"),
+    (dict(limit=-1.0), m.MOE_ERR_INVALID_ARGUMENT, "limit"),
+    (dict(activation=5), m.MOE_ERR_INVALID_ARGUMENT, "activation"),
+    (dict(hidden_dim=250), m.MOE_ERR_INVALID_ARGUMENT, "hidden_dim"),
+    (dict(moe_dim=0), m.MOE_ERR_INVALID_ARGUMENT, "moe_dim"),
+    (dict(n_local_experts=0), m.MOE_ERR_INVALID_ARGUMENT, "n_local_experts"),
+    (dict(n_local_experts=2000), m.MOE_ERR_INVALID_ARGUMENT, "n_local_experts"),
+    (dict(gate_up_format=3), m.MOE_ERR_INVALID_ARGUMENT, "gate_up_format"),
+    (dict(out_dtype=1), m.MOE_ERR_INVALID_ARGUMENT, "out_dtype"),
+    (dict(x_perm=None), m.MOE_ERR_INVALID_ARGUMENT, "gather"),
+    (dict(x=128, sorted_token=144), m.MOE_ERR_INVALID_ARGUMENT, "not both"),
+    (dict(w_down=None), m.MOE_ERR_INVALID_ARGUMENT, "w_down"),
+    (dict(expert_out=100), m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(act_workspace_bytes=100), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
+    (dict(operand_dtype=1, hidden_dim=200), m.MOE_ERR_INVALID_ARGUMENT, "128"),
+])
+def test_grouped_ffn_validation(kw, status, frag):
+    st, msg = _err(m.lib().moe_grouped_ffn, _ffn(**kw))
+    assert st == status and frag in msg, msg
+
+
+def _idx(**kw):
+    base = dict(num_tokens=16, n_experts_per_tok=2, experts_start_idx=0, n_local_experts=8, expert_indices=16,
+                expert_offsets=32, sorted_token=48, row_of_slot=64, workspace=80, workspace_bytes=1 << 16)
+    base.update(kw)
+    return m.IndexArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(n_local_experts=0), m.MOE_ERR_INVALID_ARGUMENT, "n_local_experts"),
+    (dict(n_experts_per_tok=0), m.MOE_ERR_INVALID_ARGUMENT, "n_experts_per_tok"),
+    (dict(num_tokens=-3), m.MOE_ERR_INVALID_ARGUMENT, "num_tokens"),
+    (dict(num_tokens=1 << 30, n_experts_per_tok=4), m.MOE_ERR_INVALID_ARGUMENT, "2^31"),
+    (dict(expert_offsets=None), m.MOE_ERR_INVALID_ARGUMENT, "expert_offsets"),
+    (dict(workspace_bytes=4), m.MOE_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+    (dict(x=96, hidden_dim=256), m.MOE_ERR_INVALID_ARGUMENT, "x_perm"),
+    (dict(x=96, hidden_dim=250, x_perm=112), m.MOE_ERR_INVALID_ARGUMENT, "hidden_dim"),
+    (dict(x=96, hidden_dim=200, x_perm=112, xperm_dtype=1, x_perm_scale=128), m.MOE_ERR_INVALID_ARGUMENT, "128"),
+    (dict(x=96, hidden_dim=256, x_perm=112, xperm_dtype=1), m.MOE_ERR_INVALID_ARGUMENT, "x_perm_scale"),
+])
+def test_build_indices_validation(kw, status, frag):
+    st, msg = _err(m.lib().moe_build_indices, _idx(**kw))
+    assert st == status and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(hidden_dim=100), "hidden_dim"),
+    (dict(n_experts_per_tok=0), "n_experts_per_tok"),
+    (dict(out_dtype=1), "out_dtype"),
+    (dict(y=None), "required"),
+    (dict(y=40), "aligned"),
+])
+def test_combine_validation(kw, frag):
+    base = dict(num_tokens=8, n_experts_per_tok=2, hidden_dim=256, expert_out=16, out_dtype=2, row_of_slot=32,
+                y=48)
+    base.update(kw)
+    st, msg = _err(m.lib().moe_combine, m.CombineArgs(**base))
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+def test_workspace_queries_and_status_strings():
+    lib = m.lib()
+    assert lib.moe_build_indices_workspace_bytes(16384, 8, 256) >= 256 * 32 * 4
+    assert lib.moe_ffn_workspace_bytes(8192, 14336, 0) == 8192 * 14336 * 2
+    assert lib.moe_ffn_workspace_bytes(100, 256, 1) >= 100 * 256 + 100 * 2 * 4
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"

@@ -1,0 +1,339 @@
+"""GPU parity: every step of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: indices, CSR offsets, permutations and fp8 codes bit-exact; router
+weights within 1e-5 relative; bf16 layer output within 2e-2 x RMS and fp8
+within 6e-2 x RMS of the oracle's float64 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as O
+from tests.gpu_util import assert_rel, bf16_floor, host, rel_rms_err, sample_tokens, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+W_RTOL = 1e-5
+BF16_TOL = 2e-2
+FP8_TOL = 6e-2
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mixture_experts_ffn_top_amd as m
+    m.lib()
+    return m
+
+
+def _gen(cfg):
+    say(f"[gen] cfg={cfg.cfg_id}:{cfg.name} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} D={cfg.D}")
+    return synth.make_inputs(cfg, DEV)
+
+
+# ---------------------------------------------------------------- routers
+
+@pytest.mark.parametrize("cid,T", [(1, 64), (2, 4096), (4, 4096), (1, 1), (4, 77)])
+def test_softmax_router_x_form(moe, cid, T):
+    cfg = synth.scaled(synth.get_config(cid), T=T)
+    inp = _gen(cfg)
+    say(f"[route softmax x] cfg={cid} T={T}")
+    idx, w, _, lo = moe.route(router="softmax", k=cfg.k, E=cfg.E, x=inp["x"], w_gate=inp["w_gate"],
+                              return_logits=True)
+    torch.cuda.synchronize()
+    ref_logits = O.gate_logits(host(inp["x"]), host(inp["w_gate"]))
+    err, rms = rel_rms_err(host(lo), ref_logits)
+    say(f"  logits max err / rms = {err:.2e}")
+    assert err <= 2e-5
+    # selection and weights on the GPU's own float32 logits
+    ridx, rw = O.route_softmax_topk(host(lo), cfg.k)
+    assert np.array_equal(host(idx), ridx)
+    assert_rel(host(w), rw, W_RTOL, "softmax weights")
+
+
+@pytest.mark.parametrize("renorm,scale", [(True, 1.0), (False, 2.5)])
+def test_softmax_router_logits_form_and_ties(moe, renorm, scale):
+    rng = np.random.default_rng(1)
+    T, E, k = 300, 40, 5
+    z = rng.choice(np.array([-1.0, 0.0, 0.25, 3.0], np.float32), size=(T, E))   # many exact ties
+    z[:100] = rng.standard_normal((100, E)).astype(np.float32)
+    zt = torch.from_numpy(z).to(DEV)
+    gs = torch.tensor([0.5], device=DEV)
+    idx, w, _, _ = moe.route(router="softmax", k=k, E=E, logits=zt, route_scale=scale,
+                             global_scale=gs, renormalize=renorm)
+    ridx, rw = O.route_softmax_topk(z, k, scale, 0.5, renormalize=renorm)
+    assert np.array_equal(host(idx), ridx)
+    assert_rel(host(w), rw, W_RTOL, "softmax weights")
+
+
+@pytest.mark.parametrize("cid,T", [(3, 8192), (5, 16384), (3, 1), (3, 333)])
+def test_sigmoid_sink_router(moe, cid, T):
+    cfg = synth.scaled(synth.get_config(cid), T=T)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(100 + cid)
+    logits = (torch.randn((T, cfg.E + cfg.s), generator=g, device=DEV) * cfg.logit_std).contiguous()
+    bias = (torch.rand((cfg.E,), generator=g, device=DEV) * 0.2 - 0.1)
+    gs = torch.tensor([cfg.global_scale], device=DEV)
+    say(f"[route sigmoid] cfg={cid} T={T}")
+    idx, w, sw, _ = moe.route(router="sigmoid", k=cfg.k, E=cfg.E, s=cfg.s, logits=logits,
+                              expert_bias=bias, route_scale=cfg.route_scale, global_scale=gs)
+    ridx, rw, rsw = O.route_sigmoid_sink(host(logits), cfg.E, cfg.k, cfg.s, host(bias),
+                                         cfg.route_scale, cfg.global_scale)
+    assert np.array_equal(host(idx), ridx)
+    assert_rel(host(w), rw, W_RTOL, "expert weights")
+    if cfg.s:
+        assert_rel(host(sw), rsw, W_RTOL, "sink weights")
+
+
+def test_sigmoid_router_extremes(moe):
+    """Underflowing and saturated sigmoids, exact ties, a bias that forces
+    selection, and a logits row wider than E+s."""
+    E, k, s = 64, 6, 2
+    rows = [np.full(E + s + 3, -300.0), np.full(E + s + 3, 50.0), np.zeros(E + s + 3)]
+    r = np.linspace(-250, -100, E + s + 3)
+    rows.append(r)
+    z = np.stack(rows).astype(np.float32)
+    bias = np.zeros(E, np.float32)
+    bias[17] = 5.0
+    zt = torch.from_numpy(z).to(DEV)
+    full = moe.route(router="sigmoid", k=k, E=E, s=s, logits=zt, expert_bias=torch.from_numpy(bias).to(DEV),
+                     route_scale=2.5)
+    ridx, rw, rsw = O.route_sigmoid_sink(z, E, k, s, bias, 2.5, 1.0)
+    assert np.array_equal(host(full[0]), ridx)
+    assert np.all(np.isfinite(host(full[1]))) and np.all(np.isfinite(host(full[2])))
+    assert_rel(host(full[1]), rw, W_RTOL, "expert weights")
+    assert_rel(host(full[2]), rsw, W_RTOL, "sink weights")
+
+
+# ---------------------------------------------------------------- CSR and permute
+
+def _routing(T, E, k, seed, mode="random"):
+    rng = np.random.default_rng(seed)
+    if mode == "random":
+        idx = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    elif mode == "one_expert":
+        idx = np.zeros((T, k), np.int64)
+        idx[:, 1:] = np.arange(1, k)[None, :]
+    elif mode == "half_empty":
+        idx = np.stack([rng.permutation(E // 2)[:k] * 2 for _ in range(T)])
+    return idx.astype(np.int32), rng.random((T, k)).astype(np.float32)
+
+
+@pytest.mark.parametrize("T,E,k,start,L,mode,masked", [
+    (8192, 128, 6, 0, 128, "random", False),
+    (16384, 256, 8, 0, 256, "random", True),
+    (16384, 256, 8, 32, 32, "random", False),
+    (4096, 8, 2, 0, 8, "one_expert", False),
+    (1000, 64, 4, 0, 64, "half_empty", True),
+    (1, 8, 2, 0, 8, "random", False),
+    (5000, 1024, 3, 0, 1024, "random", False),
+])
+def test_build_indices(moe, T, E, k, start, L, mode, masked):
+    idx, w = _routing(T, E, k, 7 + T, mode)
+    mask = (np.random.default_rng(3).random(T) > 0.25).astype(np.uint8) if masked else None
+    say(f"[csr] T={T} E={E} k={k} start={start} L={L} mode={mode} masked={masked}")
+    out = moe.build_indices(torch.from_numpy(idx).to(DEV), L, expert_start=start,
+                            weights=torch.from_numpy(w).to(DEV),
+                            token_mask=torch.from_numpy(mask).to(DEV) if mask is not None else None)
+    ref = O.build_indices(idx, L, start, mask, w)
+    off = host(out["offsets"])
+    assert np.array_equal(off, ref["offsets"])
+    n = int(off[-1])
+    assert np.array_equal(host(out["sorted_token"])[:n], ref["sorted_token"])
+    assert np.array_equal(host(out["row_of_slot"])[:T * k], ref["row_of_slot"])
+    assert np.array_equal(host(out["sorted_weight"])[:n], ref["sorted_weight"].astype(np.float32))
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_permute(moe, fp8):
+    T, E, k, H = 3000, 16, 3, 7168 if fp8 else 2880
+    idx, _ = _routing(T, E, k, 11)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    x = (torch.randn((T, H), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    x[5, :128] = 0                       # an all-zero group
+    say(f"[permute] fp8={fp8} T={T} H={H}")
+    out = moe.build_indices(torch.from_numpy(idx).to(DEV), E, x=x, xperm_dtype="fp8" if fp8 else "bf16")
+    ref = O.build_indices(idx, E)
+    n = int(host(out["offsets"])[-1])
+    xh = host(x)
+    if not fp8:
+        assert np.array_equal(host(out["x_perm"])[:n], O.permute_rows(xh, ref["sorted_token"]))
+    else:
+        codes, sc = O.quantize_rows_block128(xh)
+        assert np.array_equal(host(out["x_perm"])[:n], codes[ref["sorted_token"]])
+        assert np.array_equal(host(out["x_perm_scale"])[:n], sc[ref["sorted_token"]])
+
+
+# ---------------------------------------------------------------- grouped FFN + whole layer
+
+def _run_layer(moe, cfg, inp, *, gather=True, token_mask=None):
+    layer = moe.MoELayer(cfg, inp, gather=gather)
+    res = layer.forward(inp["x"], token_mask=token_mask)
+    torch.cuda.synchronize()
+    return layer, res
+
+
+def _check_layer(cfg, inp, res, tokens, tol, token_mask=None):
+    hin = synth.to_host(inp)
+    idx = host(res["indices"])
+    w = host(res["weights"]).astype(np.float64)
+    y_ref = O.layer(hin, cfg, indices=idx, weights=w, tokens=tokens, token_mask=token_mask)
+    y = host(res["y"])[tokens]
+    err, rms = rel_rms_err(y, y_ref)
+    say(f"  y max err / rms = {err:.3e} (bf16 floor {bf16_floor(y_ref):.3e}, rms {rms:.3e})")
+    assert np.all(np.isfinite(y))
+    assert err <= tol
+    return err
+
+
+def _check_routing(cfg, inp, res):
+    hin = synth.to_host(inp, keys=["logits", "expert_bias"])
+    if cfg.router == "sigmoid_sink":
+        ridx, rw, rsw = O.route_sigmoid_sink(hin["logits"], cfg.E, cfg.k, cfg.s, hin["expert_bias"],
+                                             cfg.route_scale, cfg.global_scale)
+        assert np.array_equal(host(res["indices"]), ridx)
+        assert_rel(host(res["weights"]), rw, W_RTOL, "expert weights")
+        if cfg.s:
+            assert_rel(host(res["sink_weights"]), rsw, W_RTOL, "sink weights")
+
+
+@pytest.mark.parametrize("cid,changes,nsample", [
+    (1, {}, 64),
+    (3, {"T": 1024}, 1024),
+    (4, {"T": 512}, 512),
+    (2, {"T": 256, "H": 1024, "D": 2048}, 256),
+])
+def test_layer_small(moe, cid, changes, nsample):
+    cfg = synth.scaled(synth.get_config(cid), **changes)
+    inp = _gen(cfg)
+    for gather in (True, False):
+        say(f"[layer] cfg={cid} {changes} gather={gather}")
+        _, res = _run_layer(moe, cfg, inp, gather=gather)
+        _check_routing(cfg, inp, res)
+        _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample), BF16_TOL)
+
+
+@pytest.mark.parametrize("cid,nsample", [(2, 96), (3, 384), (4, 256)])
+def test_layer_full_size(moe, cid, nsample):
+    cfg = synth.get_config(cid)
+    inp = _gen(cfg)
+    say(f"[layer full] cfg={cid}")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=cid), BF16_TOL)
+
+
+@pytest.mark.parametrize("act,alpha,limit,fmt,bias", [
+    ("silu", 0.0, 7.0, "concatenated", False),
+    ("gelu_tanh", 0.0, 0.0, "concatenated", True),
+    ("swigluoai", 1.702, 7.0, "interleaved", True),
+    ("swigluoai", 1.702, 7.0, "concatenated", False),
+    ("silu", 0.0, 0.0, "interleaved", True),
+])
+def test_activation_variants_clamp_stress(moe, act, alpha, limit, fmt, bias):
+    """x scaled x8 so that |gate|, |up| reach well past limit = 7."""
+    cfg = synth.scaled(synth.get_config(4), T=300, H=512, D=384, E=6, k=2, activation=act, alpha=alpha,
+                       limit=limit, gate_up_format=fmt, has_bias=bias, x_std=8.0, w_std=0.05)
+    inp = _gen(cfg)
+    say(f"[variant] {act} alpha={alpha} limit={limit} {fmt} bias={bias}")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+
+
+def test_expert_scales_and_local_slice(moe):
+    cfg = synth.scaled(synth.get_config(3), T=700, E=24, k=4, s=4, H=512, D=256)
+    inp = _gen(cfg)
+    hin = synth.to_host(inp)
+    idx, w, _, _ = moe.route(router="sigmoid", k=cfg.k, E=cfg.E, s=cfg.s, logits=inp["logits"],
+                             expert_bias=inp["expert_bias"], route_scale=cfg.route_scale)
+    start, L = 5, 11
+    ew = moe.ExpertWeights.from_stacked(inp["w_gate_up"][start:start + L].contiguous(),
+                                        inp["w_down"][start:start + L].contiguous())
+    g = torch.Generator(device=DEV)
+    g.manual_seed(9)
+    sgu_all = torch.rand((cfg.E,), generator=g, device=DEV) + 0.5
+    sd_all = torch.rand((cfg.E,), generator=g, device=DEV) + 0.5
+    mask = (torch.rand((cfg.T,), generator=g, device=DEV) > 0.3).to(torch.uint8)
+    ind = moe.build_indices(idx, L, expert_start=start, weights=w, token_mask=mask)
+    O_ = moe.grouped_ffn(ind["offsets"], cfg.T * cfg.k, ew, x=inp["x"], sorted_token=ind["sorted_token"],
+                         gate_up_expert_scales=sgu_all[start:start + L].contiguous(),
+                         down_expert_scales=sd_all[start:start + L].contiguous())
+    y = moe.combine(O_, ind["row_of_slot"], cfg.T, cfg.k, weights=w, token_mask=mask)
+    torch.cuda.synchronize()
+    y_ref = O.layer(hin, cfg, indices=host(idx), weights=host(w).astype(np.float64),
+                    token_mask=host(mask), expert_start=start, num_local=L,
+                    gate_up_expert_scales=host(sgu_all), down_expert_scales=host(sd_all))
+    valid = host(mask) != 0
+    # the output RMS is taken over the valid tokens: masked rows are zero by definition
+    err, _ = rel_rms_err(host(y)[valid], y_ref[valid])
+    say(f"  slice+scales y err/rms = {err:.3e} (bf16 floor {bf16_floor(y_ref[valid]):.3e})")
+    assert err <= BF16_TOL
+    assert np.all(host(y)[~valid] == 0)
+
+
+@pytest.mark.parametrize("mode", ["one_expert", "half_empty", "k_eq_E", "single_expert"])
+def test_layer_routing_edge_cases(moe, mode):
+    base = synth.scaled(synth.get_config(1), T=200, H=256, D=256)
+    if mode == "k_eq_E":
+        cfg = synth.scaled(base, E=4, k=4)
+    elif mode == "single_expert":
+        cfg = synth.scaled(base, E=1, k=1)
+    else:
+        cfg = synth.scaled(base, E=8, k=2)
+    inp = _gen(cfg)
+    T, E, k = cfg.T, cfg.E, cfg.k
+    if mode in ("one_expert", "half_empty"):
+        idx, w = _routing(T, E, k, 1, mode)
+    else:
+        idx = np.tile(np.arange(k, dtype=np.int32), (T, 1))
+        w = np.random.default_rng(2).random((T, k)).astype(np.float32)
+    it, wt = torch.from_numpy(idx).to(DEV), torch.from_numpy(w).to(DEV)
+    ew = moe.ExpertWeights.from_stacked(inp["w_gate_up"], inp["w_down"])
+    ind = moe.build_indices(it, E, weights=wt)
+    O_ = moe.grouped_ffn(ind["offsets"], T * k, ew, x=inp["x"], sorted_token=ind["sorted_token"])
+    y = moe.combine(O_, ind["row_of_slot"], T, k, weights=wt)
+    torch.cuda.synchronize()
+    y_ref = O.layer(synth.to_host(inp), cfg, indices=idx, weights=w.astype(np.float64))
+    err, _ = rel_rms_err(host(y), y_ref)
+    say(f"[edge] {mode}: y err/rms = {err:.3e}")
+    assert err <= BF16_TOL
+
+
+def test_grouped_ffn_rows_and_determinism(moe):
+    """Expert rows O against the oracle's per-expert MLP, and two runs
+    bit-identical (no atomics on floating point anywhere)."""
+    cfg = synth.scaled(synth.get_config(4), T=600, H=640, D=448, E=5, k=2)
+    inp = _gen(cfg)
+    layer, r1 = _run_layer(moe, cfg, inp)
+    O1 = r1["O"].clone()
+    y1 = r1["y"].clone()
+    r2 = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(O1, r2["O"]) and torch.equal(y1, r2["y"])
+    hin = synth.to_host(inp)
+    ind = r1["index"]
+    off = host(ind["offsets"])
+    st = host(ind["sorted_token"])
+    Oh = host(O1)
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        ref = O.expert_mlp(hin["x"][st[rows]], hin["w_gate_up"][e], hin["w_down"][e], fmt=cfg.gate_up_format,
+                           activation=cfg.activation, alpha=cfg.alpha, limit=cfg.limit,
+                           b_gate_up=hin["b_gate_up"][e], b_down=hin["b_down"][e])
+        err, _ = rel_rms_err(Oh[rows], ref)
+        assert err <= 1e-2, f"expert {e}: O err/rms {err:.3e}"
+
+
+def test_abi_errors_on_gpu_path(moe):
+    """Invalid arguments are refused before any launch, also from the binding."""
+    x = torch.zeros((4, 24), dtype=torch.bfloat16, device=DEV)
+    wg = torch.zeros((8, 24), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(moe.MoEError):
+        moe.route(router="softmax", k=9, E=8, x=x, w_gate=wg)
+    with pytest.raises(moe.MoEError):
+        moe.route(router="sigmoid", k=3, E=8, s=0, logits=torch.zeros((4, 8), device=DEV))
