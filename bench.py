@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--cfg", type=int, default=2)
     ap.add_argument("--cpu-sample", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -121,6 +123,18 @@ def main():
     import torch
     import mixture_experts_ffn_top_amd as moe
     import synth
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_launch": n, "bytes_written_per_launch": n,
+                          "launches": 3}), flush=True)
+        return
 
     cfg = synth.get_config(args.cfg)
     dev = torch.device("cuda:0")

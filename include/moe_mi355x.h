@@ -223,6 +223,8 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *                  rows straight from x through sorted_token (bf16 only)
  *   x_perm_scale   fp32 [max_rows, H/128]            fp8 only
  *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form
+ *                  (x_perm / x, the activation buffer and one expert's
+ *                  weights must each be under 4 GiB)
  *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]
  *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128]
  *   b_gate_up      bf16 [L, 2D] or NULL

@@ -221,6 +221,10 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path is not built yet");
   }
   REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn: operand_dtype must be BF16 or FP8_E4M3_BLOCK128");
+  // the GEMMs address rows with 32-bit byte offsets
+  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 32) && (int64_t)R * D * 2 < ((int64_t)1 << 32) &&
+              (int64_t)2 * D * H * 2 < ((int64_t)1 << 32),
+          "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
   if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 weights must use the OUT_IN layout for now");
   if (R == 0) return ok();

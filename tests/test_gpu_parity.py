@@ -205,6 +205,8 @@ def _check_routing(cfg, inp, res):
     (3, {"T": 1024}, 1024),
     (4, {"T": 512}, 512),
     (2, {"T": 256, "H": 1024, "D": 2048}, 256),
+    (1, {"T": 100, "H": 1000, "D": 200}, 100),       # K not a multiple of the 64-wide k tile
+    (4, {"T": 90, "H": 296, "D": 72, "E": 3, "k": 2}, 90),   # ragged N and K in both GEMMs
 ])
 def test_layer_small(moe, cid, changes, nsample):
     cfg = synth.scaled(synth.get_config(cid), **changes)
