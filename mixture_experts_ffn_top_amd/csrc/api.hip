@@ -218,7 +218,43 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
                 (long long)need, (long long)a->act_workspace_bytes);
   if (a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
     REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: fp8 needs hidden_dim and moe_dim multiples of 128");
-    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path is not built yet");
+    REQUIRE(a->x_perm != nullptr && a->x_perm_scale != nullptr,
+            "moe_grouped_ffn: fp8 takes x_perm and x_perm_scale (quantised by moe_build_indices)");
+    REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
+            "moe_grouped_ffn: fp8 weights need w_gate_up_scale and w_down_scale");
+    REQUIRE((int64_t)R * H < ((int64_t)1 << 32) && (int64_t)R * D < ((int64_t)1 << 32) &&
+                (int64_t)2 * D * H < ((int64_t)1 << 32),
+            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
+    if (a->gate_up_format != MOE_GATE_UP_CONCATENATED)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path takes the concatenated gate_up format");
+    if (a->b_gate_up != nullptr || a->b_down != nullptr)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path has no bias");
+    if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: fp8 weights must use the OUT_IN layout");
+    if (R == 0) return ok();
+    moe::FfnFp8Params q{};
+    q.offsets = a->expert_offsets;
+    q.L = L;
+    q.H = H;
+    q.D = D;
+    q.max_rows = R;
+    q.x_perm = (const uint8_t*)a->x_perm;
+    q.x_scale = a->x_perm_scale;
+    q.w_gate_up = (const uint8_t*)a->w_gate_up;
+    q.w_gate_up_scale = a->w_gate_up_scale;
+    q.w_down = (const uint8_t*)a->w_down;
+    q.w_down_scale = a->w_down_scale;
+    q.gate_up_scales = a->gate_up_expert_scales;
+    q.down_scales = a->down_expert_scales;
+    q.act_kind = a->activation;
+    q.alpha = a->alpha;
+    q.limit = a->limit;
+    q.act = (uint8_t*)a->act_workspace;
+    q.act_scale = (float*)((uint8_t*)a->act_workspace + round_up((int64_t)R * D, 256));
+    q.out = a->expert_out;
+    q.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+    q.events = (hipEvent_t const*)a->timing_events;
+    return hip_status(moe::launch_ffn_fp8(q, (hipStream_t)stream), "moe_grouped_ffn");
   }
   REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn: operand_dtype must be BF16 or FP8_E4M3_BLOCK128");
   // the GEMMs address rows with 32-bit byte offsets

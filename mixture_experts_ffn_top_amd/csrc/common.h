@@ -133,6 +133,12 @@ __device__ __forceinline__ float gated_act(float g, float u, float alpha, float 
   return 0.5f * g * (1.0f + t) * u;
 }
 
-__device__ __forceinline__ int xcd_count() { return 8; }
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]) that wait on one counter only.
+constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+constexpr int waitcnt_lgkm(int n) { return 0xf | (0x3 << 14) | (0x7 << 4) | ((n & 0xf) << 8); }
+
+typedef const __attribute__((address_space(1))) void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
 
 }  // namespace moe

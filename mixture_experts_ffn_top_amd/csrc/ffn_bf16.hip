@@ -8,12 +8,11 @@
 // Tiling: 256 x 256 workgroup tile, 8 waves in 2 x 4 (two per SIMD), each
 // wave a 128 x 64 sub-tile of 4 x 2 MFMA blocks (128 fp32 accumulators per
 // lane); while one wave of a SIMD waits at a barrier or on LDS the other
-// issues MFMAs.  Both
-// operands go straight from global memory into LDS (direct-to-LDS loads, no
-// register staging) in 32-wide k stages, four stages deep, so about three
-// stages of loads are in flight while one runs on the matrix cores; the MFMA
-// fragments of the next 16-wide k step are read from LDS while the current
-// step's MFMAs issue.
+// issues MFMAs.  Both operands go straight from global memory into LDS
+// (direct-to-LDS loads, no register staging) in 64-wide k stages, double
+// buffered: the loads of stage k+1 are in flight while stage k runs on the
+// matrix cores, and the MFMA fragments of the next 16-wide k step are read
+// from LDS while the current step's MFMAs issue.
 //
 // The per-expert row counts live only on the device.  Every workgroup reads
 // expert_offsets, builds the prefix of 256-row blocks per expert in LDS and
@@ -79,11 +78,6 @@ __device__ __forceinline__ int swz_f(int r) {
   if (CPR == 4) return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1);
   return (r ^ (r >> 3)) & 7;
 }
-// s_waitcnt immediate that waits for vmcnt <= n only (gfx9 encoding: vmcnt
-// bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at maximum).
-constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
-// ... and for lgkmcnt <= n only.
-constexpr int waitcnt_lgkm(int n) { return 0xf | (0x3 << 14) | (0x7 << 4) | ((n & 0xf) << 8); }
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_f(row)) << 3); }
 
@@ -177,8 +171,6 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     }
     b_off[i] = (uint32_t)(wrow * b_row_bytes);
   }
-  typedef const __attribute__((address_space(1))) void* gptr_t;
-  typedef __attribute__((address_space(3))) void* lptr_t;
   const int KT = (p.K + BK - 1) / BK;
   auto issue = [&](int kt) {
     const int buf = kt & (NSTAGE - 1);

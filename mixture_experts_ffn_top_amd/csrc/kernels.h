@@ -46,6 +46,27 @@ struct FfnBf16Params {
 };
 hipError_t launch_ffn_bf16(const FfnBf16Params& p, hipStream_t st);
 
+struct FfnFp8Params {
+  const int32_t* offsets;
+  int L, H, D, max_rows;
+  const uint8_t* x_perm;         // e4m3 codes [max_rows, H]
+  const float* x_scale;          // [max_rows, H/128]
+  const uint8_t* w_gate_up;      // OUT_IN [L, 2D, H]
+  const float* w_gate_up_scale;  // [L, 2D/128, H/128]
+  const uint8_t* w_down;         // OUT_IN [L, H, D]
+  const float* w_down_scale;     // [L, H/128, D/128]
+  const float* gate_up_scales;
+  const float* down_scales;
+  int act_kind;
+  float alpha, limit;
+  uint8_t* act;                  // e4m3 codes [max_rows, D]
+  float* act_scale;              // [max_rows, D/128]
+  void* out;                     // [max_rows, H] bf16 or fp32
+  int out_bf16;
+  hipEvent_t const* events;
+};
+hipError_t launch_ffn_fp8(const FfnFp8Params& p, hipStream_t st);
+
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, hipStream_t st);
 

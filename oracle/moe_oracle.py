@@ -86,15 +86,25 @@ def e4m3_encode(a) -> np.ndarray:
     return code
 
 
-def e4m3_decode(codes) -> np.ndarray:
-    """OCP float8 e4m3fn codes (uint8) -> float64 values."""
-    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+def _e4m3_value(c) -> np.ndarray:
+    c = np.asarray(c, dtype=np.int64)
     s = np.where(c & 0x80, -1.0, 1.0)
     f = (c >> 3) & 0xF
     m = c & 0x7
     val = np.where(f == 0, m * 2.0 ** -9, (8 + m) * np.ldexp(1.0, f - 10))
     val = np.where((f == 15) & (m == 7), np.nan, val)
     return s * val
+
+
+# value of every one of the 256 codes, from the format definition above
+_E4M3_TABLE = _e4m3_value(np.arange(256))
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """OCP float8 e4m3fn codes (uint8) -> float64 values: sign, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent field 0 is subnormal (m * 2^-9);
+    0x7F / 0xFF are NaN.  Looked up in the 256-entry table of those values."""
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
 
 
 def quantize_rows_block128(a):

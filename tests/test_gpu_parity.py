@@ -339,3 +339,75 @@ def test_abi_errors_on_gpu_path(moe):
         moe.route(router="softmax", k=9, E=8, x=x, w_gate=wg)
     with pytest.raises(moe.MoEError):
         moe.route(router="sigmoid", k=3, E=8, s=0, logits=torch.zeros((4, 8), device=DEV))
+
+
+# ---------------------------------------------------------------- fp8 block-scaled path
+
+def _check_fp8_act(cfg, inp, res, layer):
+    """The re-quantised activation against the oracle's re-quantisation of its
+    own activation.  The two activations differ by float32 rounding, so a code
+    may land one e4m3 step away where a value sits near a rounding boundary;
+    the dequantised values must agree to within one step of the row scale."""
+    hin = synth.to_host(inp)
+    ind = res["index"]
+    off = host(ind["offsets"])
+    st = host(ind["sorted_token"])
+    R, D = layer.R, cfg.D
+    n = int(off[-1])
+    ws = host(layer.act_ws)
+    codes_gpu = ws[: R * D].reshape(R, D)[:n]
+    so = ((R * D + 255) // 256) * 256
+    scale_gpu = ws[so: so + R * (D // 128) * 4].view(np.float32).reshape(R, D // 128)[:n]
+    xq = O.layer_inputs_x(hin, "fp8")
+    same = total = 0
+    worst = 0.0
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        wgu = O.dequant_weight_block128(hin["w_gate_up"][e], hin["w_gate_up_scale"][e])
+        h = xq[st[rows]] @ wgu
+        a = O.gated_activation(h[:, :D], h[:, D:], cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
+        codes_ref, sc_ref = O.quantize_rows_block128(a)
+        cg = codes_gpu[rows]
+        same += int(np.sum(cg == codes_ref))
+        total += cg.size
+        deq_g = O.dequant_rows_block128(cg, scale_gpu[rows])
+        deq_r = O.dequant_rows_block128(codes_ref, sc_ref)
+        # one e4m3 step at the value in the normal range; in the subnormal
+        # range (|q| < 2^-6, absolute steps of 2^-9) values this close to zero
+        # move by a few steps for float32-level differences of the activation,
+        # so there the bound is the smallest normal 2^-6 -- all in units of the
+        # (oracle) row scale
+        step = np.maximum(np.abs(O.e4m3_decode(codes_ref)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(sc_ref, 128, axis=1)
+        ratio = np.abs(deq_g - deq_r) / step
+        worst = max(worst, float(ratio.max()))
+    frac = same / max(total, 1)
+    say(f"  fp8 activation codes identical: {frac:.5f}; worst |gpu - oracle| = {worst:.3f} e4m3 steps")
+    # each side rounds to the nearest code (half a step each) and the two
+    # activations differ at float32 level: two steps bound the sum
+    assert frac >= 0.99
+    assert worst <= 2.0
+
+
+@pytest.mark.parametrize("changes,nsample", [
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512),
+    ({"T": 2048, "E": 16, "k": 4}, 256),              # full hidden / moe dims of the fp8 layer
+])
+def test_fp8_layer_small(moe, changes, nsample):
+    cfg = synth.scaled(synth.get_config(5), **changes)
+    inp = _gen(cfg)
+    say(f"[fp8 layer] {changes}")
+    layer, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_fp8_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=3), FP8_TOL)
+
+
+def test_fp8_layer_full_size(moe):
+    cfg = synth.get_config(5)
+    inp = _gen(cfg)
+    say("[fp8 layer full] T=16384 H=7168 E=256 k=8 D=2048")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=5), FP8_TOL)
