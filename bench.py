@@ -149,28 +149,9 @@ def main():
 
     def step(i):
         base = 7 * i
-        c = cfg
+        slots = {1: base + 1, 2: base + 2, 3: base + 6}
         ev.record(base + 0, stream)
-        if c.router == "softmax":
-            idx, w, sw, _ = moe.route(router="softmax", k=c.k, E=c.E, x=inp["x"], w_gate=layer.w_gate,
-                                      route_scale=c.route_scale, global_scale=layer.global_scale)
-        else:
-            idx, w, sw, _ = moe.route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=layer.logits,
-                                      expert_bias=layer.expert_bias, route_scale=c.route_scale,
-                                      global_scale=layer.global_scale)
-        ev.record(base + 1, stream)
-        gather = layer.gather
-        ind = moe.build_indices(idx, c.E, weights=w, x=None if gather else inp["x"],
-                                xperm_dtype="fp8" if c.operand_dtype == "fp8" else "bf16")
-        ev.record(base + 2, stream)
-        O_ = moe.grouped_ffn(ind["offsets"], layer.R, layer.w, x_perm=ind.get("x_perm"),
-                             x_perm_scale=ind.get("x_perm_scale"), x=inp["x"] if gather else None,
-                             sorted_token=ind["sorted_token"] if gather else None,
-                             activation=c.activation, alpha=c.alpha, limit=c.limit,
-                             gate_up_format=c.gate_up_format, out_dtype=layer.out_dtype,
-                             act_workspace=layer.act_ws, out=layer.O, timing_events=ev.triple(base + 3))
-        moe.combine(O_, ind["row_of_slot"], c.T, c.k, weights=w, out=layer.y)
-        ev.record(base + 6, stream)
+        layer.forward(inp["x"], mark=lambda j: ev.record(slots[j], stream), ffn_events=ev.triple(base + 3))
 
     print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
     for i in range(W):

@@ -69,8 +69,11 @@ enum { MOE_ROUTER_SOFTMAX_TOPK = 0, MOE_ROUTER_SIGMOID_SINK = 1 };
 enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLUOAI = 1, MOE_ACT_GELU_TANH = 2 };
 /* [StackedMoE] gate_up_format. */
 enum { MOE_GATE_UP_CONCATENATED = 0, MOE_GATE_UP_INTERLEAVED = 1 };
-/* Element types. */
-enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_BLOCK128 = 1, MOE_DTYPE_FP32 = 2 };
+/* Element types.  MOE_DTYPE_FP8_E4M3_TOKENS is a moe_build_indices form of
+   the fp8 operand: every token quantised once (1x128 blocks), not permuted;
+   moe_grouped_ffn then gathers the rows it needs through sorted_token. */
+enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_BLOCK128 = 1, MOE_DTYPE_FP32 = 2,
+       MOE_DTYPE_FP8_E4M3_TOKENS = 3 };
 /* Weight layouts: [StackedMoE] stacked [E, in_features, out_features]
    ("Weight tensor shapes"), or its transposed view
    [E, out_features, in_features] (gate_up_proj_transposed /
@@ -163,7 +166,10 @@ moe_status_t moe_route(const moe_route_args_t* args, void* stream);
  *   hidden_dim H                   host
  *   xperm_dtype    host: MOE_DTYPE_BF16 (copy rows) or
  *                  MOE_DTYPE_FP8_E4M3_BLOCK128 (per-token 1x128 e4m3 with
- *                  scale amax/448, 1 when amax = 0; H % 128 == 0)
+ *                  scale amax/448, 1 when amax = 0; H % 128 == 0), or
+ *                  MOE_DTYPE_FP8_E4M3_TOKENS (the same quantisation, one row
+ *                  per token in token order: x_perm [T, H], x_perm_scale
+ *                  [T, H/128]; the gather is left to moe_grouped_ffn)
  *   x_perm         [T*k, H] bf16 or uint8 out, rows p < kept written
  *   x_perm_scale   fp32 [T*k, H/128] out (fp8 only)
  *   workspace      device scratch of moe_build_indices_workspace_bytes()
@@ -222,7 +228,9 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *   x_perm         [max_rows, H] bf16 (or e4m3 codes) -- or NULL to gather
  *                  rows straight from x through sorted_token (bf16 only)
  *   x_perm_scale   fp32 [max_rows, H/128]            fp8 only
- *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form
+ *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form; for fp8
+ *                  x holds the per-token codes [T, H] and x_perm_scale the
+ *                  per-token scales [T, H/128] (MOE_DTYPE_FP8_E4M3_TOKENS)
  *                  (x_perm / x, the activation buffer and one expert's
  *                  weights must each be under 4 GiB)
  *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]

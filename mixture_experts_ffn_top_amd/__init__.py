@@ -21,7 +21,7 @@ MOE_OK, MOE_ERR_INVALID_ARGUMENT, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMA
 ROUTER_SOFTMAX_TOPK, ROUTER_SIGMOID_SINK = 0, 1
 ACT = {"silu": 0, "swigluoai": 1, "gelu_tanh": 2}
 FMT = {"concatenated": 0, "interleaved": 1}
-DTYPE_BF16, DTYPE_FP8_E4M3_BLOCK128, DTYPE_FP32 = 0, 1, 2
+DTYPE_BF16, DTYPE_FP8_E4M3_BLOCK128, DTYPE_FP32, DTYPE_FP8_E4M3_TOKENS = 0, 1, 2, 3
 WEIGHT_IN_OUT, WEIGHT_OUT_IN = 0, 1
 
 _vp = ctypes.c_void_p
@@ -182,13 +182,14 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
     if weights is not None:
         out["sorted_weight"] = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
     H = 0
-    fp8 = xperm_dtype == "fp8"
+    fp8 = xperm_dtype in ("fp8", "fp8_tokens")
+    rows = T if xperm_dtype == "fp8_tokens" else R
     if x is not None:
         _dt(x, torch.bfloat16, "x")
         H = x.shape[1]
-        out["x_perm"] = torch.empty((max(R, 1), H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
+        out["x_perm"] = torch.empty((max(rows, 1), H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
         if fp8:
-            out["x_perm_scale"] = torch.empty((max(R, 1), H // 128), dtype=torch.float32, device=dev)
+            out["x_perm_scale"] = torch.empty((max(rows, 1), H // 128), dtype=torch.float32, device=dev)
     wsb = lib().moe_build_indices_workspace_bytes(T, k, n_local)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     a = IndexArgs(num_tokens=T, n_experts_per_tok=k, experts_start_idx=expert_start,
@@ -196,7 +197,8 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
                   token_mask=_ptr(token_mask), expert_offsets=_ptr(out["offsets"]),
                   sorted_token=_ptr(out["sorted_token"]), row_of_slot=_ptr(out["row_of_slot"]),
                   sorted_weight=_ptr(out.get("sorted_weight")), x=_ptr(x), hidden_dim=H,
-                  xperm_dtype=DTYPE_FP8_E4M3_BLOCK128 if fp8 else DTYPE_BF16,
+                  xperm_dtype={"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128,
+                               "fp8_tokens": DTYPE_FP8_E4M3_TOKENS}[xperm_dtype],
                   x_perm=_ptr(out.get("x_perm")), x_perm_scale=_ptr(out.get("x_perm_scale")),
                   workspace=_ptr(ws), workspace_bytes=ws.numel())
     _check(lib().moe_build_indices(ctypes.byref(a), _stream(dev)))
@@ -302,7 +304,7 @@ class MoELayer:
         self.cfg = cfg
         dev = inputs["x"].device
         self.device = dev
-        self.gather = gather and cfg.operand_dtype == "bf16"
+        self.gather = gather
         self.w = ExpertWeights.from_stacked(
             inputs["w_gate_up"], inputs["w_down"], b_gate_up=inputs.get("b_gate_up"),
             b_down=inputs.get("b_down"), w_gate_up_scale=inputs.get("w_gate_up_scale"),
@@ -319,7 +321,11 @@ class MoELayer:
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
 
-    def forward(self, x, token_mask=None):
+    def forward(self, x, token_mask=None, mark=None, ffn_events=None):
+        """One layer pass.  mark(i), if given, is called on the host after
+        each of the routing (i=1) and bucketing (i=2) calls and after the
+        combine (i=3); ffn_events are hipEvent_t handles recorded inside the
+        grouped FFN call (before gate_up, between the GEMMs, after down)."""
         c = self.cfg
         if c.router == "softmax":
             idx, w, sw, _ = route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate,
@@ -328,16 +334,30 @@ class MoELayer:
             idx, w, sw, _ = route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=self.logits,
                                   expert_bias=self.expert_bias, route_scale=c.route_scale,
                                   global_scale=self.global_scale)
-        ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,
-                            x=None if self.gather else x,
-                            xperm_dtype="fp8" if c.operand_dtype == "fp8" else "bf16")
+        if mark:
+            mark(1)
+        fp8 = c.operand_dtype == "fp8"
+        if fp8:
+            # the fp8 operand: every token quantised once; gathered by the GEMM
+            # (gather=True) or quantised per permuted row here (gather=False)
+            ind = build_indices(idx, c.E, weights=w, token_mask=token_mask, x=x,
+                                xperm_dtype="fp8_tokens" if self.gather else "fp8")
+            xg = ind.pop("x_perm") if self.gather else None
+        else:
+            ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,
+                                x=None if self.gather else x)
+            xg = x if self.gather else None
+        if mark:
+            mark(2)
         O = grouped_ffn(ind["offsets"], self.R, self.w, x_perm=ind.get("x_perm"),
-                        x_perm_scale=ind.get("x_perm_scale"), x=x if self.gather else None,
+                        x_perm_scale=ind.get("x_perm_scale"), x=xg,
                         sorted_token=ind["sorted_token"] if self.gather else None,
                         activation=c.activation, alpha=c.alpha, limit=c.limit,
                         gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
-                        act_workspace=self.act_ws, out=self.O)
+                        act_workspace=self.act_ws, out=self.O, timing_events=ffn_events)
         y = combine(O, ind["row_of_slot"], c.T, c.k, weights=w, token_mask=token_mask, out=self.y)
+        if mark:
+            mark(3)
         return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O}
 
 

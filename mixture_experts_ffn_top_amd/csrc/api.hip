@@ -144,11 +144,12 @@ moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
     REQUIRE(H >= 8 && H % 8 == 0, "moe_build_indices: hidden_dim must be a positive multiple of 8 (got %d)", H);
     REQUIRE(a->x_perm != nullptr, "moe_build_indices: x_perm is required with x");
     REQUIRE(aligned16(a->x) && aligned16(a->x_perm), "moe_build_indices: x and x_perm must be 16-byte aligned");
-    if (a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
+    if (a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128 || a->xperm_dtype == MOE_DTYPE_FP8_E4M3_TOKENS) {
       REQUIRE(H % 128 == 0, "moe_build_indices: fp8 quantisation needs hidden_dim % 128 == 0 (got %d)", H);
       REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for fp8");
     } else {
-      REQUIRE(a->xperm_dtype == MOE_DTYPE_BF16, "moe_build_indices: xperm_dtype must be BF16 or FP8_E4M3_BLOCK128");
+      REQUIRE(a->xperm_dtype == MOE_DTYPE_BF16,
+              "moe_build_indices: xperm_dtype must be BF16, FP8_E4M3_BLOCK128 or FP8_E4M3_TOKENS");
     }
   }
   hipStream_t st = (hipStream_t)stream;
@@ -158,9 +159,10 @@ moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
                                            (int32_t*)a->workspace, st);
   if (e != hipSuccess) return hip_status(e, "moe_build_indices");
   if (permute) {
-    e = moe::launch_permute((const uint16_t*)a->x, a->sorted_token, a->expert_offsets + L,
-                            (int64_t)T * k, a->hidden_dim,
-                            a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128, a->x_perm,
+    const bool tokens = a->xperm_dtype == MOE_DTYPE_FP8_E4M3_TOKENS;
+    e = moe::launch_permute((const uint16_t*)a->x, tokens ? nullptr : a->sorted_token,
+                            a->expert_offsets + L, tokens ? (int64_t)T : (int64_t)T * k,
+                            a->hidden_dim, a->xperm_dtype != MOE_DTYPE_BF16, a->x_perm,
                             a->x_perm_scale, st);
     if (e != hipSuccess) return hip_status(e, "moe_build_indices (permute)");
   }
@@ -218,8 +220,8 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
                 (long long)need, (long long)a->act_workspace_bytes);
   if (a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
     REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: fp8 needs hidden_dim and moe_dim multiples of 128");
-    REQUIRE(a->x_perm != nullptr && a->x_perm_scale != nullptr,
-            "moe_grouped_ffn: fp8 takes x_perm and x_perm_scale (quantised by moe_build_indices)");
+    REQUIRE(a->x_perm_scale != nullptr && (a->x_perm != nullptr || a->x != nullptr),
+            "moe_grouped_ffn: fp8 takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn: fp8 weights need w_gate_up_scale and w_down_scale");
     REQUIRE((int64_t)R * H < ((int64_t)1 << 32) && (int64_t)R * D < ((int64_t)1 << 32) &&
@@ -238,8 +240,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.H = H;
     q.D = D;
     q.max_rows = R;
-    q.x_perm = (const uint8_t*)a->x_perm;
+    q.x_perm = (const uint8_t*)(a->x_perm ? a->x_perm : a->x);
     q.x_scale = a->x_perm_scale;
+    q.sorted_token = a->x_perm ? nullptr : a->sorted_token;
     q.w_gate_up = (const uint8_t*)a->w_gate_up;
     q.w_gate_up_scale = a->w_gate_up_scale;
     q.w_down = (const uint8_t*)a->w_down;

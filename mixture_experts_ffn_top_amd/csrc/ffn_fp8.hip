@@ -60,8 +60,9 @@ struct Fp8GemmArgs {
   const int32_t* offsets;
   int L;
   int K, N;                  // reduction length; output columns (gate_up D, down H)
-  const uint8_t* A;          // [rows, K] codes
+  const uint8_t* A;          // [rows, K] codes (or per token, gathered)
   const float* A_scale;      // [rows, K/128]
+  const int32_t* gather;     // row -> token, or nullptr
   const uint8_t* W;          // OUT_IN per expert [w_rows, K]
   int64_t w_estride;         // bytes per expert
   const float* W_scale;      // per expert [w_rows/128, K/128]
@@ -143,7 +144,8 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     const int trow = (wave * F_LPW_A + i) * 8 + lrow;
     a_chunk[i] = (lane & 7) ^ f8_swz_f(trow);
     const int r = min(row_beg + trow, row_end - 1);
-    a_off[i] = (uint32_t)((int64_t)r * p.K);
+    const int64_t ar = p.gather ? (int64_t)p.gather[r] : (int64_t)r;
+    a_off[i] = (uint32_t)(ar * p.K);
   }
 #pragma unroll
   for (int i = 0; i < F_LPW_B; ++i) {
@@ -161,8 +163,9 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   }
   (void)lchunk;
   // activation scales of 16 tile rows per wave (lanes 0..15)
-  const int xs_row = min(row_beg + wave * 16 + (lane & 15), row_end - 1);
-  const float* xs_src = p.A_scale + (int64_t)xs_row * KB;
+  const int xs_r = min(row_beg + wave * 16 + (lane & 15), row_end - 1);
+  const int64_t xs_row = p.gather ? (int64_t)p.gather[xs_r] : (int64_t)xs_r;
+  const float* xs_src = p.A_scale + xs_row * KB;
 
   auto stage_a = [&](int kt) { return smem + (kt % F_NSTAGE) * F_STAGE_BYTES; };
   auto stage_xs = [&](int kt) { return (float*)(smem + F_NSTAGE * F_STAGE_BYTES + (kt % F_XS_BUFS) * F_XS_BYTES); };
@@ -376,6 +379,7 @@ hipError_t launch_ffn_fp8(const FfnFp8Params& q, hipStream_t st) {
   g.N = q.D;
   g.A = q.x_perm;
   g.A_scale = q.x_scale;
+  g.gather = q.sorted_token;
   g.W = q.w_gate_up;
   g.w_estride = (int64_t)2 * q.D * q.H;
   g.W_scale = q.w_gate_up_scale;

@@ -5,7 +5,7 @@
 // e4m3 quantisation of the fp8 layer.
 //
 //   csr_hist    per block of IDX_SLOTS flat slots: LDS histogram over local
-//               experts -> counts[e][block]
+//               experts -> counts[block][e]
 //   csr_scan    one workgroup: exclusive scan over blocks per expert, then over
 //               experts -> expert_offsets and per-(expert, block) bases
 //   csr_scatter per block: stable rank of each slot among same-expert slots
@@ -17,7 +17,7 @@
 
 namespace moe {
 
-static constexpr int IDX_SLOTS = 4096;
+static constexpr int IDX_SLOTS = 512;   // flat slots per workgroup
 
 int64_t csr_num_blocks(int64_t R) { return (R + IDX_SLOTS - 1) / IDX_SLOTS; }
 
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void csr_hist_kernel(const int32_t* __restrict
     if (e >= 0) atomicAdd(&s_h[e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < L; e += 256) counts[(int64_t)e * nblk + blockIdx.x] = s_h[e];
+  for (int e = threadIdx.x; e < L; e += 256) counts[(int64_t)blockIdx.x * L + e] = s_h[e];
 }
 
 // One workgroup of 1024 threads; L <= 1024.
@@ -54,10 +54,11 @@ __global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ co
   const int t = threadIdx.x;
   int32_t tot = 0;
   if (t < L) {
-    int32_t* c = counts + (int64_t)t * nblk;
+    // counts are block-major ([block][expert]): consecutive threads read
+    // consecutive words at every step
     for (int b = 0; b < nblk; ++b) {
-      int32_t v = c[b];
-      c[b] = tot;
+      int32_t v = counts[(int64_t)b * L + t];
+      counts[(int64_t)b * L + t] = tot;
       tot += v;
     }
   }
@@ -72,8 +73,7 @@ __global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ co
   const int32_t excl = s[t] - tot;
   if (t < L) {
     offsets[t] = excl;
-    int32_t* c = counts + (int64_t)t * nblk;
-    for (int b = 0; b < nblk; ++b) c[b] += excl;
+    for (int b = 0; b < nblk; ++b) counts[(int64_t)b * L + t] += excl;
   }
   if (t == L - 1) offsets[L] = s[t];
 }
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(
   int32_t* wcnt = sm + L;      // [4][L] this round's count per wave and expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < L; e += 256) {
-    running[e] = base[(int64_t)e * nblk + blockIdx.x];
+    running[e] = base[(int64_t)blockIdx.x * L + e];
     wcnt[e] = wcnt[L + e] = wcnt[2 * L + e] = wcnt[3 * L + e] = 0;
   }
   __syncthreads();
@@ -142,17 +142,21 @@ __global__ __launch_bounds__(256) void permute_bf16_kernel(const uint16_t* __res
 
 // Per-row, per-128-column e4m3 quantisation fused into the gather: 16 lanes
 // own one 128-column group (8 elements each); a wave does 4 groups at a time.
+// With sorted_token == nullptr the rows are not permuted: row p of the
+// output is token p (n_fixed rows), the per-token form the fp8 GEMM gathers
+// from.
 __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ sorted_token,
-                                                          const int32_t* __restrict__ n_rows, int H,
+                                                          const int32_t* __restrict__ n_rows,
+                                                          int n_fixed, int H,
                                                           uint8_t* __restrict__ xq,
                                                           float* __restrict__ xs) {
   const int lane = threadIdx.x & 63;
-  const int n = n_rows[0];
+  const int n = sorted_token ? n_rows[0] : n_fixed;
   const int groups = H / 128;
   const int sub = lane & 15, gq = lane >> 4;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n; row += gridDim.x * 4) {
-    const uint16_t* src = x + (int64_t)sorted_token[row] * H;
+    const uint16_t* src = x + (int64_t)(sorted_token ? sorted_token[row] : row) * H;
     for (int g0 = 0; g0 < groups; g0 += 4) {
       const int g = g0 + gq;
       const bool ok = g < groups;
@@ -209,7 +213,8 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* sorted_token, const 
   int64_t blocks = (max_rows + 3) / 4;
   if (blocks > 16384) blocks = 16384;
   if (fp8)
-    permute_fp8_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, H, (uint8_t*)xp, xs);
+    permute_fp8_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, (int)max_rows, H,
+                                                    (uint8_t*)xp, xs);
   else
     permute_bf16_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, H, (uint16_t*)xp);
   return hipGetLastError();

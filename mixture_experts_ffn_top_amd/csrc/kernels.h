@@ -49,8 +49,9 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& p, hipStream_t st);
 struct FfnFp8Params {
   const int32_t* offsets;
   int L, H, D, max_rows;
-  const uint8_t* x_perm;         // e4m3 codes [max_rows, H]
-  const float* x_scale;          // [max_rows, H/128]
+  const uint8_t* x_perm;         // e4m3 codes [max_rows, H], or per token [T, H] with sorted_token
+  const float* x_scale;          // [max_rows, H/128] or [T, H/128]
+  const int32_t* sorted_token;   // nullptr: rows already permuted
   const uint8_t* w_gate_up;      // OUT_IN [L, 2D, H]
   const float* w_gate_up_scale;  // [L, 2D/128, H/128]
   const uint8_t* w_down;         // OUT_IN [L, H, D]

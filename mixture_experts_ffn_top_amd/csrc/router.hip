@@ -86,60 +86,65 @@ __global__ __launch_bounds__(256) void router_softmax_logits_kernel(
 }
 
 // ------------------------------------------------------------ softmax, gate GEMM fused
-// Each wave owns 16 tokens.  logits^T[e][t] = sum_h W[e][h] x[t][h] runs on
+// A workgroup owns 16 tokens; its 4 waves split the hidden dimension into
+// quarters.  logits^T[e][t] = sum_h W[e][h] x[t][h] runs on
 // v_mfma_f32_16x16x32_bf16 with W as the A operand (16 experts per tile) and
-// x as the B operand (16 tokens); lane group g = lane/16 walks its own
-// contiguous quarter of the hidden dimension, 8 elements per step, so every
-// lane issues 16-byte loads.  Logits go through LDS to the top-k.
+// x as the B operand (16 tokens); inside a wave, lane group g = lane/16 walks
+// its own contiguous part of the wave's quarter, 8 elements per step, so
+// every lane issues 16-byte loads.  The four partial sums meet in LDS, then
+// each wave runs the top-k of 4 tokens.
 template <int ETILES, int J>
 __global__ __launch_bounds__(256) void router_softmax_x_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int H, int E, int k,
     float scale, const float* __restrict__ global_scale, int renorm, float* __restrict__ logits_out,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   constexpr int EP = ETILES * 16;
-  __shared__ float s_logit[4][16][EP + 1];
+  __shared__ float s_part[4][16][EP + 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int t0 = (blockIdx.x * 4 + wave) * 16;
+  const int t0 = blockIdx.x * 16;
   const int col = lane & 15, grp = lane >> 4;
-  const int steps = (H + 31) / 32;
+  const int chunks = H / 8;                          // 8-element chunks of a row
+  const int per_wave = (chunks + 3) / 4;
+  const int c_beg = wave * per_wave;
+  const int c_end = min(chunks, c_beg + per_wave);
+  const int per_grp = (per_wave + 3) / 4;
   const int tok = t0 + col;
+  const bool tok_ok = tok < T;
   f32x4_t acc[ETILES];
 #pragma unroll
   for (int i = 0; i < ETILES; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  if (t0 < T) {
-    const bool tok_ok = tok < T;
-    for (int s = 0; s < steps; ++s) {
-      const int h = (grp * steps + s) * 8;
-      u32x4_t bv = {0u, 0u, 0u, 0u};
-      if (tok_ok && h < H) bv = *(const u32x4_t*)(x + (int64_t)tok * H + h);
-      bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
+  for (int s = 0; s < per_grp; ++s) {
+    const int c = c_beg + grp * per_grp + s;
+    const bool c_ok = c < c_end;
+    u32x4_t bv = {0u, 0u, 0u, 0u};
+    if (tok_ok && c_ok) bv = *(const u32x4_t*)(x + (int64_t)tok * H + c * 8);
+    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
 #pragma unroll
-      for (int et = 0; et < ETILES; ++et) {
-        const int e = et * 16 + col;
-        u32x4_t av = {0u, 0u, 0u, 0u};
-        if (e < E && h < H) av = *(const u32x4_t*)(wg + (int64_t)e * H + h);
-        bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
-      }
+    for (int et = 0; et < ETILES; ++et) {
+      const int e = et * 16 + col;
+      u32x4_t av = {0u, 0u, 0u, 0u};
+      if (e < E && c_ok) av = *(const u32x4_t*)(wg + (int64_t)e * H + c * 8);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
+      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
     }
-    // acc[et][i] = logit[token t0 + col][expert et*16 + 4*grp + i]
-#pragma unroll
-    for (int et = 0; et < ETILES; ++et)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_logit[wave][col][et * 16 + grp * 4 + i] = acc[et][i];
   }
+  // acc[et][i] = partial logit[token t0 + col][expert et*16 + 4*grp + i]
+#pragma unroll
+  for (int et = 0; et < ETILES; ++et)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_part[wave][col][et * 16 + grp * 4 + i] = acc[et][i];
   __syncthreads();
-  if (t0 >= T) return;
   const float gs = global_scale ? global_scale[0] : 1.0f;
-  const int ntok = min(16, T - t0);
-  for (int tt = 0; tt < ntok; ++tt) {
+  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
     const int t = t0 + tt;
+    if (t >= T) break;
     float key[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      int e = lane + MOE_WAVE * j;
-      key[j] = (e < E) ? s_logit[wave][tt][e] : 0.0f;
+      const int e = lane + MOE_WAVE * j;
+      // fixed summation order over the four quarters
+      key[j] = (e < E) ? ((s_part[0][tt][e] + s_part[1][tt][e]) + s_part[2][tt][e]) + s_part[3][tt][e] : 0.0f;
       if (logits_out && e < E) logits_out[(int64_t)t * E + e] = key[j];
     }
     int sidx;
@@ -231,7 +236,7 @@ hipError_t launch_router_softmax_x(const uint16_t* x, const uint16_t* wg, int T,
                                    int k, float scale, const float* gs, int renorm,
                                    float* logits_out, int32_t* idx, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  dim3 grid((T + 63) / 64), block(256);
+  dim3 grid((T + 15) / 16), block(256);
   const int et = (E + 15) / 16;
 #define LAUNCH(ET, JJ)                                                                             \
   router_softmax_x_kernel<ET, JJ><<<grid, block, 0, st>>>(x, wg, T, H, E, k, scale, gs, renorm,     \

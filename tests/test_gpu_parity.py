@@ -146,7 +146,7 @@ def test_build_indices(moe, T, E, k, start, L, mode, masked):
     assert np.array_equal(host(out["sorted_weight"])[:n], ref["sorted_weight"].astype(np.float32))
 
 
-@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("fp8", [False, True, "tokens"])
 def test_permute(moe, fp8):
     T, E, k, H = 3000, 16, 3, 7168 if fp8 else 2880
     idx, _ = _routing(T, E, k, 11)
@@ -155,12 +155,17 @@ def test_permute(moe, fp8):
     x = (torch.randn((T, H), generator=g, device=DEV) * 3).to(torch.bfloat16)
     x[5, :128] = 0                       # an all-zero group
     say(f"[permute] fp8={fp8} T={T} H={H}")
-    out = moe.build_indices(torch.from_numpy(idx).to(DEV), E, x=x, xperm_dtype="fp8" if fp8 else "bf16")
+    mode = {False: "bf16", True: "fp8", "tokens": "fp8_tokens"}[fp8]
+    out = moe.build_indices(torch.from_numpy(idx).to(DEV), E, x=x, xperm_dtype=mode)
     ref = O.build_indices(idx, E)
     n = int(host(out["offsets"])[-1])
     xh = host(x)
-    if not fp8:
+    if mode == "bf16":
         assert np.array_equal(host(out["x_perm"])[:n], O.permute_rows(xh, ref["sorted_token"]))
+    elif mode == "fp8_tokens":
+        codes, sc = O.quantize_rows_block128(xh)
+        assert np.array_equal(host(out["x_perm"])[:T], codes)
+        assert np.array_equal(host(out["x_perm_scale"])[:T], sc)
     else:
         codes, sc = O.quantize_rows_block128(xh)
         assert np.array_equal(host(out["x_perm"])[:n], codes[ref["sorted_token"]])
@@ -390,15 +395,16 @@ def _check_fp8_act(cfg, inp, res, layer):
     assert worst <= 2.0
 
 
-@pytest.mark.parametrize("changes,nsample", [
-    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512),
-    ({"T": 2048, "E": 16, "k": 4}, 256),              # full hidden / moe dims of the fp8 layer
+@pytest.mark.parametrize("changes,nsample,gather", [
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, True),
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, False),
+    ({"T": 2048, "E": 16, "k": 4}, 256, True),              # full hidden / moe dims of the fp8 layer
 ])
-def test_fp8_layer_small(moe, changes, nsample):
+def test_fp8_layer_small(moe, changes, nsample, gather):
     cfg = synth.scaled(synth.get_config(5), **changes)
     inp = _gen(cfg)
-    say(f"[fp8 layer] {changes}")
-    layer, res = _run_layer(moe, cfg, inp)
+    say(f"[fp8 layer] {changes} gather={gather}")
+    layer, res = _run_layer(moe, cfg, inp, gather=gather)
     _check_routing(cfg, inp, res)
     _check_fp8_act(cfg, inp, res, layer)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=3), FP8_TOL)
