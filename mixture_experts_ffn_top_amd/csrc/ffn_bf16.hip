@@ -27,6 +27,8 @@
 // are resolved while loading), arranged so that each wave's accumulator
 // block 0 holds 32 gate columns and block 1 the up columns of the same 32
 // outputs: the activation runs in registers.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,17 +38,21 @@ enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
 enum { FMT_CONCAT = 0, FMT_INTERLEAVED = 1 };
 
 static constexpr int BM = 256, BN = 256, BK = 64;
-static constexpr int NSTAGE = 2;                                 // LDS pipeline depth (power of two)
+static constexpr int NSTAGE_A = 2, NSTAGE_B = 3;                 // LDS buffers per operand
 static constexpr int WAVES_M = 2, WAVES_N = 4;                   // 8 waves, 2 per SIMD
 static constexpr int NTHREADS = 64 * WAVES_M * WAVES_N;
 static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;     // wave tile 128 x 64
 static constexpr int MI = WTM / 32, NI = WTN / 32;               // 32x32 MFMA blocks per wave
 static constexpr int CPR = BK / 8;                               // 16-byte chunks per tile row
 static constexpr int RPB = 1024 / (BK * 2);                      // tile rows per 1 KB load block
-static constexpr int LPW = (BM * BK * 2 / 1024) / (WAVES_M * WAVES_N);  // 1 KB loads per wave per operand
+static constexpr int LPW_A = (BM * BK * 2 / 1024) / (WAVES_M * WAVES_N);  // 1 KB loads per wave, A
+static constexpr int LPW_B = (BN * BK * 2 / 1024) / (WAVES_M * WAVES_N);  // 1 KB loads per wave, B
 static constexpr int KKS = BK / 16;                              // 16-wide k steps per stage
-static constexpr int TILE_ELEMS = BM * BK;                       // bf16 elements per operand stage
-static constexpr int LDS_BYTES_TILES = NSTAGE * 2 * TILE_ELEMS * 2;  // 4 stages x 2 operands
+static constexpr int A_ELEMS = BM * BK, B_ELEMS = BN * BK;       // bf16 elements per operand stage
+static constexpr int LDS_BYTES_TILES = (NSTAGE_A * A_ELEMS + NSTAGE_B * B_ELEMS) * 2;  // 160 KB
+
+// Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
+static constexpr int BUF_DWORD3 = 0x00020000;
 
 struct GemmArgs {
   const int32_t* offsets;
@@ -81,13 +87,24 @@ __device__ __forceinline__ int swz_f(int r) {
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_f(row)) << 3); }
 
+// Workgroup barrier that publishes this wave's LDS writes (ds_write and the
+// buffer loads into LDS it has already waited for) without draining the
+// loads still in flight: __syncthreads() would add a full vmcnt(0) wait for
+// the outstanding loads into LDS.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int MODE, int ACT, int FMT, bool GATHER, bool OUT_BF16>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16_kernel(const GemmArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* As = (uint16_t*)smem;
-  uint16_t* Bs = As + NSTAGE * TILE_ELEMS;
-  int32_t* s_mbp = (int32_t*)(smem + LDS_BYTES_TILES);
+  uint16_t* Bs = As + NSTAGE_A * A_ELEMS;
+  // the m-block prefix is only needed to map this workgroup to its tile; it
+  // shares LDS with the operand buffers, which are filled after that
+  int32_t* s_mbp = (int32_t*)smem;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -135,31 +152,45 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     if (s_mbp[mid] * NB <= tile) lo = mid;
     else hi = mid - 1;
   }
-  const int e = lo;
+  // uniform by construction; made scalar so that every address base below
+  // lives in SGPRs
+  const int e = __builtin_amdgcn_readfirstlane(lo);
   const int nmb = s_mbp[e + 1] - s_mbp[e];
-  const int local = tile - s_mbp[e] * NB;
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[e] * NB);
   const int nb = local / nmb, mb = local % nmb;
-  const int row_beg = p.offsets[e] + mb * BM;
-  const int row_end = p.offsets[e + 1];
+  const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * BM);
+  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  __syncthreads();  // every wave has read the prefix before the loads overwrite it
 
-  // ---- loader: direct global -> LDS (global_load_lds_dwordx4), no VGPR
-  // staging.  One instruction moves a 1 KB block of RPB tile rows x CPR
-  // chunks; lane l lands at row RPB*blk + l/CPR, physical chunk l%CPR, so it
-  // fetches the logical chunk (l%CPR) ^ f(row).  Wave w moves blocks
-  // LPW*w .. LPW*w+LPW-1 of both operands.
+  // ---- loader: buffer loads straight into LDS (buffer_load_dwordx4 ... lds),
+  // no VGPR staging.  One instruction moves a 1 KB block of RPB tile rows x
+  // CPR chunks; lane l lands at row RPB*blk + l/CPR, physical chunk l%CPR,
+  // so it fetches the logical chunk (l%CPR) ^ f(row).  Wave w moves blocks
+  // LPW*w .. LPW*w+LPW-1 of both operands.  The per-lane byte offset (row and
+  // swizzled chunk) is fixed for the tile; the k offset of a stage goes in
+  // the scalar offset and the LDS destination in M0, so a load costs no
+  // vector instruction.
   const int lrow = lane / CPR;
   const char* a_base = GATHER ? (const char*)p.X : (const char*)p.A;
   const char* b_base = (const char*)(p.W + (int64_t)e * p.w_estride);
-  const int64_t a_row_bytes = p.lda * 2, b_row_bytes = p.ldb * 2;
-  uint32_t a_off[LPW], b_off[LPW];  // byte offset of this lane's row
-  int lchunk[LPW];
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, BUF_DWORD3);
+  const uint32_t a_row_bytes = (uint32_t)p.lda * 2u, b_row_bytes = (uint32_t)p.ldb * 2u;
+  uint32_t a_off[LPW_A], b_off[LPW_B];  // byte offset of this lane's row
+  int a_chunk[LPW_A], b_chunk[LPW_B];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int trow = (wave * LPW + i) * RPB + lrow;  // tile row 0..255
-    lchunk[i] = (lane % CPR) ^ swz_f(trow);
+  for (int i = 0; i < LPW_A; ++i) {
+    const int trow = (wave * LPW_A + i) * RPB + lrow;  // tile row
+    a_chunk[i] = (lane % CPR) ^ swz_f(trow);
     const int r = min(row_beg + trow, row_end - 1);
-    const int64_t arow = GATHER ? (int64_t)p.sorted_token[r] : (int64_t)r;
-    a_off[i] = (uint32_t)(arow * a_row_bytes);
+    const uint32_t arow = GATHER ? (uint32_t)p.sorted_token[r] : (uint32_t)r;
+    a_off[i] = arow * a_row_bytes;
+  }
+#pragma unroll
+  for (int i = 0; i < LPW_B; ++i) {
+    const int trow = (wave * LPW_B + i) * RPB + lrow;  // tile row
+    b_chunk[i] = (lane % CPR) ^ swz_f(trow);
     int wrow;
     if (MODE == MODE_DOWN) {
       wrow = min(nb * BN + trow, p.N - 1);
@@ -169,32 +200,53 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       const int oc = min(nb * NBO + q * (WTN / 2) + j, p.N - 1);
       wrow = (FMT == FMT_CONCAT) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
     }
-    b_off[i] = (uint32_t)(wrow * b_row_bytes);
+    b_off[i] = (uint32_t)wrow * b_row_bytes;
   }
-  const int KT = (p.K + BK - 1) / BK;
-  auto issue = [&](int kt) {
-    const int buf = kt & (NSTAGE - 1);
-    uint16_t* as = As + buf * TILE_ELEMS + wave * LPW * 512;
-    uint16_t* bs = Bs + buf * TILE_ELEMS + wave * LPW * 512;
+  const int KTF = p.K / BK;              // full k stages
+  const int KT = (p.K + BK - 1) / BK;    // all k stages (the last may be ragged)
+  uint32_t a_voff[LPW_A], b_voff[LPW_B];
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      // the last stage of a ragged K is clamped to stay inside the row; its
-      // A chunks past K are zeroed in LDS before the stage is published
-      const uint32_t kb = (uint32_t)min(kt * BK + lchunk[i] * 8, p.K - 8) * 2u;
-      __builtin_amdgcn_global_load_lds((gptr_t)(a_base + a_off[i] + kb), (lptr_t)(as + i * 512), 16, 0, 0);
-    }
+  for (int i = 0; i < LPW_A; ++i) a_voff[i] = a_off[i] + (uint32_t)a_chunk[i] * 16u;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const uint32_t kb = (uint32_t)min(kt * BK + lchunk[i] * 8, p.K - 8) * 2u;
-      __builtin_amdgcn_global_load_lds((gptr_t)(b_base + b_off[i] + kb), (lptr_t)(bs + i * 512), 16, 0, 0);
+  for (int i = 0; i < LPW_B; ++i) b_voff[i] = b_off[i] + (uint32_t)b_chunk[i] * 16u;
+
+  // A (activation rows) is double buffered, B (weight rows) triple buffered.
+  // Stage kt's A goes to buffer kt % 2 and its B to buffer kt % 3.
+  auto issue_a = [&](int kt) {
+    lptr_t dst = (lptr_t)(As + (kt % NSTAGE_A) * A_ELEMS + wave_s * LPW_A * 512);
+    if (kt < KTF) {
+#pragma unroll
+      for (int i = 0; i < LPW_A; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)((char*)dst + i * 1024), 16, a_voff[i], kt * (BK * 2), 0, 0);
+    } else {
+      // the ragged last stage is clamped to stay inside each row; its A
+      // chunks past K are zeroed in LDS before the stage is published
+#pragma unroll
+      for (int i = 0; i < LPW_A; ++i) {
+        const uint32_t kb = (uint32_t)min(kt * BK + a_chunk[i] * 8, p.K - 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)((char*)dst + i * 1024), 16, a_off[i] + kb, 0, 0, 0);
+      }
     }
   };
-  // wait until this wave's loads of stage `kt` have landed: the loads of the
-  // stages issued after it (at most NSTAGE-2 of them, 2*LPW each) may still fly
-  auto wait_stage = [&](int kt) {
-    const int newer = min(KT - 1, kt + NSTAGE - 2) - kt;
-    if (NSTAGE > 3 && newer >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * LPW));
-    else if (NSTAGE > 2 && newer >= 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW));
+  auto issue_b = [&](int kt) {
+    lptr_t dst = (lptr_t)(Bs + (kt % NSTAGE_B) * B_ELEMS + wave_s * LPW_B * 512);
+    if (kt < KTF) {
+#pragma unroll
+      for (int i = 0; i < LPW_B; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16, b_voff[i], kt * (BK * 2), 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW_B; ++i) {
+        const uint32_t kb = (uint32_t)min(kt * BK + b_chunk[i] * 8, p.K - 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16, b_off[i] + kb, 0, 0, 0);
+      }
+    }
+  };
+  // Issue order: A0 B0 B1 A1 B2 | in iteration kt: A(kt+2) B(kt+3).  When
+  // stage kt+1 is needed (end of iteration kt) the only loads issued after
+  // A(kt+1) are B(kt+2), so vmcnt(LPW_B) means A(kt+1) and B(kt+1) landed.
+  auto wait_next = [&](int kt) {
+    if (kt + 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW_B));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   };
   // ragged K: after this wave's loads of stage kt landed, overwrite the A
@@ -202,11 +254,11 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // barrier that publishes the stage orders these writes
   auto zero_tail = [&](int kt) {
     if (kt * BK + BK > p.K) {
-      uint16_t* as = As + (kt & (NSTAGE - 1)) * TILE_ELEMS + wave * LPW * 512;
+      uint16_t* as = As + (kt % NSTAGE_A) * A_ELEMS + wave_s * LPW_A * 512;
       const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-      for (int i = 0; i < LPW; ++i)
-        if (kt * BK + lchunk[i] * 8 >= p.K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
+      for (int i = 0; i < LPW_A; ++i)
+        if (kt * BK + a_chunk[i] * 8 >= p.K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
     }
   };
 
@@ -220,8 +272,8 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
   auto read_frags = [&](int kt, int kk, bf16x8_t (&af)[MI], bf16x8_t (&bfr)[NI]) {
-    const uint16_t* as = As + (kt & (NSTAGE - 1)) * TILE_ELEMS;
-    const uint16_t* bs = Bs + (kt & (NSTAGE - 1)) * TILE_ELEMS;
+    const uint16_t* as = As + (kt % NSTAGE_A) * A_ELEMS;
+    const uint16_t* bs = Bs + (kt % NSTAGE_B) * B_ELEMS;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
       af[mi] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(as + swz(wm * WTM + mi * 32 + fr, kk * 2 + fk)));
@@ -238,43 +290,68 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   };
 
   // ---- main loop.  The KKS 16-wide k steps of stage kt run as
-  //   [fragments (kt,kk+1) | MFMAs (kt,kk)]   for kk < KKS-1, then
-  //   wait stage kt+1, barrier, issue stage kt+NSTAGE into kt's buffer,
-  //   [fragments (kt+1,0) | MFMAs (kt,KKS-1)]
-  // so every fragment read overlaps a block of MFMAs and the global loads of
-  // the next NSTAGE-1 stages are in flight; two waves per SIMD cover each
-  // other's barrier and dependency stalls.
-  for (int s = 0; s < NSTAGE && s < KT; ++s) issue(s);
-  wait_stage(0);
-  zero_tail(0);
-  __syncthreads();
+  //   [MFMAs (kt,kk) interleaved with the fragment reads of (kt,kk+1)]
+  // for kk < KKS-1, then
+  //   wait for stage kt+1, barrier, fragment reads (kt+1,0),
+  //   [MFMAs (kt,KKS-1) interleaved with the loads of A(kt+2), B(kt+3)]
+  // so that neither the LDS reads nor the load issue ever hold up the matrix
+  // pipe; two waves per SIMD cover each other's barrier and wait stalls.
+  // Iterations whose loads are all full stages run without branches.
   bf16x8_t fa[2][MI], fb[2][NI];
-  read_frags(0, 0, fa[0], fb[0]);
-  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-  for (int kt = 0; kt < KT; ++kt) {
+  auto iteration = [&](int kt, auto steady) {
+    constexpr bool STEADY = decltype(steady)::value;
 #pragma unroll
     for (int kk = 0; kk < KKS; ++kk) {
       const int c = kk & 1;
       if (kk + 1 < KKS) {
         read_frags(kt, kk + 1, fa[c ^ 1], fb[c ^ 1]);
+        mfmas(fa[c], fb[c]);
+#pragma unroll
+        for (int j = 0; j < MI * NI; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (j < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+        }
       } else {
-        if (kt + 1 < KT) {
-          wait_stage(kt + 1);
+        if (STEADY) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW_B));
+        } else if (kt + 1 < KT) {
+          wait_next(kt);
           zero_tail(kt + 1);
         }
-        __syncthreads();
-        if (kt + NSTAGE < KT) issue(kt + NSTAGE);
-        if (kt + 1 < KT) read_frags(kt + 1, 0, fa[c ^ 1], fb[c ^ 1]);
+        block_barrier();
+        if (STEADY || kt + 1 < KT) read_frags(kt + 1, 0, fa[c ^ 1], fb[c ^ 1]);
+        if (STEADY || kt + 2 < KT) issue_a(kt + 2);
+        if (STEADY || kt + 3 < KT) issue_b(kt + 3);
+        mfmas(fa[c], fb[c]);
+        __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);  // DS reads first
+#pragma unroll
+        for (int j = 0; j < MI * NI; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      mfmas(fa[c], fb[c]);
-      __builtin_amdgcn_sched_barrier(0);
-      // retire the reads that overlapped this MFMA block, so that the next
-      // step's reads never leave more LDS operations outstanding than the
-      // compiler tracks precisely
+      // retire this step's fragment reads before the next step's MFMAs
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     }
-  }
+  };
+
+  issue_a(0);
+  issue_b(0);
+  if (KT > 1) issue_b(1);
+  if (KT > 1) issue_a(1);
+  if (KT > 2) issue_b(2);
+  if (KT > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW_B + LPW_A));
+  else if (KT > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW_B + LPW_A));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  zero_tail(0);
+  block_barrier();
+  read_frags(0, 0, fa[0], fb[0]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+  const int k_steady = KTF - 3;  // iterations whose loads are all full stages
+  int kt = 0;
+  for (; kt < k_steady; ++kt) iteration(kt, std::true_type{});
+  for (; kt < KT; ++kt) iteration(kt, std::false_type{});
 
   // ---- epilogue.  acc[mi][ni][r] is C[row][col] with
   //   row = wm*WTM + mi*32 + 8*(r/4) + 4*fk + r%4,  col = wn*WTN + ni*32 + fr
@@ -330,7 +407,8 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 template <typename KernelT>
 static hipError_t launch_gemm(KernelT kern, const GemmArgs& a, int max_rows, int NBO,
                               hipStream_t st) {
-  const int lds = LDS_BYTES_TILES + (a.L + 1) * (int)sizeof(int32_t);
+  const int prefix = (a.L + 1) * (int)sizeof(int32_t);
+  const int lds = LDS_BYTES_TILES > prefix ? LDS_BYTES_TILES : prefix;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int64_t nonempty = (int64_t)max_rows < a.L ? max_rows : a.L;
