@@ -281,12 +281,19 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     for (int ni = 0; ni < NI; ++ni)
       bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(bs + swz(wn * WTN + ni * 32 + fr, kk * 2 + fk)));
   };
-  auto mfmas = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NI]) {
+  // 32-row blocks of this wave that hold rows of the expert: the last m-block
+  // of an expert is usually partly empty, and its empty blocks skip their
+  // MFMAs (nothing is stored for those rows)
+  const int wm_s = wave_s / WAVES_N;
+  const int live_mi = min(max((row_end - (row_beg + wm_s * WTM) + 31) / 32, 0), MI);
+  auto mfmas = [&](const bf16x8_t (&af)[MI], const bf16x8_t (&bfr)[NI], auto full) {
+    constexpr bool FULL = decltype(full)::value;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
+      if (FULL || mi < live_mi)
 #pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+        for (int ni = 0; ni < NI; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
   };
 
   // ---- main loop.  The KKS 16-wide k steps of stage kt run as
@@ -298,14 +305,14 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // pipe; two waves per SIMD cover each other's barrier and wait stalls.
   // Iterations whose loads are all full stages run without branches.
   bf16x8_t fa[2][MI], fb[2][NI];
-  auto iteration = [&](int kt, auto steady) {
+  auto iteration = [&](int kt, auto steady, auto full) {
     constexpr bool STEADY = decltype(steady)::value;
 #pragma unroll
     for (int kk = 0; kk < KKS; ++kk) {
       const int c = kk & 1;
       if (kk + 1 < KKS) {
         read_frags(kt, kk + 1, fa[c ^ 1], fb[c ^ 1]);
-        mfmas(fa[c], fb[c]);
+        mfmas(fa[c], fb[c], full);
 #pragma unroll
         for (int j = 0; j < MI * NI; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -322,7 +329,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
         if (STEADY || kt + 1 < KT) read_frags(kt + 1, 0, fa[c ^ 1], fb[c ^ 1]);
         if (STEADY || kt + 2 < KT) issue_a(kt + 2);
         if (STEADY || kt + 3 < KT) issue_b(kt + 3);
-        mfmas(fa[c], fb[c]);
+        mfmas(fa[c], fb[c], full);
         __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);  // DS reads first
 #pragma unroll
         for (int j = 0; j < MI * NI; ++j) {
@@ -350,8 +357,13 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
   const int k_steady = KTF - 3;  // iterations whose loads are all full stages
   int kt = 0;
-  for (; kt < k_steady; ++kt) iteration(kt, std::true_type{});
-  for (; kt < KT; ++kt) iteration(kt, std::false_type{});
+  if (live_mi == MI) {
+    for (; kt < k_steady; ++kt) iteration(kt, std::true_type{}, std::true_type{});
+    for (; kt < KT; ++kt) iteration(kt, std::false_type{}, std::true_type{});
+  } else {
+    for (; kt < k_steady; ++kt) iteration(kt, std::true_type{}, std::false_type{});
+    for (; kt < KT; ++kt) iteration(kt, std::false_type{}, std::false_type{});
+  }
 
   // ---- epilogue.  acc[mi][ni][r] is C[row][col] with
   //   row = wm*WTM + mi*32 + 8*(r/4) + 4*fk + r%4,  col = wn*WTN + ni*32 + fr
