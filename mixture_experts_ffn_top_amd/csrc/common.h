@@ -30,6 +30,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
 }
 
+// Two floats to packed bf16 with one v_cvt_pk_bf16_f32 (round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 // ---------------------------------------------------------------- e4m3fn
 // float -> OCP e4m3fn code, round to nearest even, saturating at +-448.
 __device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
@@ -115,7 +123,9 @@ __device__ __forceinline__ float log_sigmoid_f32(float v) {
 // ---------------------------------------------------------------- activations
 enum { ACT_SILU = 0, ACT_SWIGLUOAI = 1, ACT_GELU_TANH = 2 };
 
-__device__ __forceinline__ float sigmoid_f32(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each):
+// ample for an activation whose result is stored in 16 or 8 bits.
+__device__ __forceinline__ float sigmoid_f32(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 template <int ACT>
 __device__ __forceinline__ float gated_act(float g, float u, float alpha, float limit) {

@@ -293,7 +293,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       if (FULL || mi < live_mi)
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
   };
 
   // ---- main loop.  The KKS 16-wide k steps of stage kt run as
@@ -365,54 +365,89 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     for (; kt < KT; ++kt) iteration(kt, std::false_type{}, std::false_type{});
   }
 
-  // ---- epilogue.  acc[mi][ni][r] is C[row][col] with
-  //   row = wm*WTM + mi*32 + 8*(r/4) + 4*fk + r%4,  col = wn*WTN + ni*32 + fr
+  // ---- epilogue.  The weight fragment is the MFMA's first operand, so the
+  // accumulators hold the transposed block: acc[mi][ni][r] is C[row][col] with
+  //   row = wm*WTM + mi*32 + fr,  col = wn*WTN + ni*32 + 8*(r/4) + 4*fk + r%4
+  // and every lane owns four consecutive columns of one row per r/4, written
+  // with one 8-byte (bf16) or 16-byte (fp32) store.  Column counts and row
+  // pitches are multiples of 8, so these stores are aligned.
   const float sc = p.escale ? p.escale[e] : 1.0f;
   const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
   if (MODE == MODE_GATE_UP) {
     // blocks ni < NI/2 hold gate columns, ni + NI/2 the up columns of the same outputs
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll
-    for (int ni = 0; ni < NI / 2; ++ni) {
-      const int oc = nb * NBO + wn * (WTN / 2) + ni * 32 + fr;
-      if (oc >= p.N) continue;
-      float bg = 0.0f, bu = 0.0f;
-      if (bias_e) {
-        const int gi = (FMT == FMT_CONCAT) ? oc : 2 * oc;
-        const int ui = (FMT == FMT_CONCAT) ? p.N + oc : 2 * oc + 1;
-        bg = bf16_to_f32(bias_e[gi]);
-        bu = bf16_to_f32(bias_e[ui]);
-      }
+    for (int ni = 0; ni < NI / 2; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int q = 0; q < 4; ++q) {
+        const int oc = nb * NBO + wn * (WTN / 2) + ni * 32 + 8 * q + 4 * fk;  // first of 4 outputs
+        if (oc >= p.N) continue;  // N is a multiple of 8: all 4 are in range
+        float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e) {
+          if (FMT == FMT_CONCAT) {
+            const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
+            bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
+            bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
+            bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
+            bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
+          } else {
+            // interleaved: gate of output j at 2j, up at 2j+1
+            const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_beg + wm * WTM + mi * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-          if (row < row_end) {
-            const float g = acc[mi][ni][r] * sc + bg;
-            const float u = acc[mi][ni + NI / 2][r] * sc + bu;
-            out[(int64_t)row * p.ldo + oc] = f32_to_bf16(gated_act<ACT>(g, u, p.alpha, p.limit));
+            for (int c = 0; c < 4; ++c) {
+              bg[c] = bf16_to_f32(b4[c] & 0xffffu);
+              bu[c] = bf16_to_f32(b4[c] >> 16);
+            }
           }
         }
-    }
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const int row = row_beg + wm * WTM + mi * 32 + fr;
+          if (row >= row_end) continue;
+          float a[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float g = acc[mi][ni][4 * q + c] * sc + bg[c];
+            const float u = acc[mi][ni + NI / 2][4 * q + c] * sc + bu[c];
+            a[c] = gated_act<ACT>(g, u, p.alpha, p.limit);
+          }
+          uint2 v;
+          v.x = pack_bf16x2_rne(a[0], a[1]);
+          v.y = pack_bf16x2_rne(a[2], a[3]);
+          *(uint2*)(out + (int64_t)row * p.ldo + oc) = v;
+        }
+      }
   } else {
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) {
-      const int n = nb * BN + wn * WTN + ni * 32 + fr;
-      if (n >= p.N) continue;
-      const float bd = bias_e ? bf16_to_f32(bias_e[n]) : 0.0f;
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb * BN + wn * WTN + ni * 32 + 8 * q + 4 * fk;  // first of 4 columns
+        if (n >= p.N) continue;
+        float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e) {
+          const uint2 b2 = *(const uint2*)(bias_e + n);
+          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+        }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = row_beg + wm * WTM + mi * 32 + 8 * (r >> 2) + 4 * fk + (r & 3);
-          if (row < row_end) {
-            const float v = acc[mi][ni][r] * sc + bd;
-            if (OUT_BF16) ((uint16_t*)p.out)[(int64_t)row * p.ldo + n] = f32_to_bf16(v);
-            else ((float*)p.out)[(int64_t)row * p.ldo + n] = v;
+        for (int mi = 0; mi < MI; ++mi) {
+          const int row = row_beg + wm * WTM + mi * 32 + fr;
+          if (row >= row_end) continue;
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
+          if (OUT_BF16) {
+            uint2 w;
+            w.x = pack_bf16x2_rne(v[0], v[1]);
+            w.y = pack_bf16x2_rne(v[2], v[3]);
+            *(uint2*)((uint16_t*)p.out + (int64_t)row * p.ldo + n) = w;
+          } else {
+            const f32x4_t w = {v[0], v[1], v[2], v[3]};
+            *(f32x4_t*)((float*)p.out + (int64_t)row * p.ldo + n) = w;
           }
         }
-    }
+      }
   }
 }
 
