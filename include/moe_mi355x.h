@@ -240,7 +240,11 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *   w_down_scale   fp32 [L, D/128, H/128] (IN_OUT) or [L, H/128, D/128]
  *   b_down         bf16 [L, H] or NULL
  *   gate_up_expert_scales, down_expert_scales  fp32 [L] or NULL (1.0)
- *   act_workspace  device buffer for A, moe_ffn_workspace_bytes() long
+ *   act_workspace  device scratch of moe_ffn_workspace_bytes(): A, and for
+ *                  bf16 the down GEMM's split-K partial tiles and arrival
+ *                  counters (the gate_up launch clears the counters, so the
+ *                  buffer needs no initialisation; calls sharing one buffer
+ *                  must not overlap)
  *   out_dtype      host: MOE_DTYPE_FP32 or MOE_DTYPE_BF16
  *   expert_out     O [max_rows, H]; rows p >= expert_offsets[L] unwritten
  *   timing_events  NULL, or an array of 3 hipEvent_t created by the caller:

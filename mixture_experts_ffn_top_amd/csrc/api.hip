@@ -174,7 +174,9 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t D, int32_t dtype) {
   if (max_rows < 0 || D < 1) return 0;
   if (dtype == MOE_DTYPE_FP8_E4M3_BLOCK128)
     return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 127) / 128) * 4, 256);
-  return round_up((int64_t)max_rows * D * 2, 256);
+  // bf16: A, then the down GEMM's split-K counters and partial tiles
+  return round_up((int64_t)max_rows * D * 2, 256) + moe::SPLIT_COUNTERS * 4 +
+         (int64_t)moe::split_slots_for(max_rows) * moe::SPLIT_TILE_FLOATS * 4;
 }
 
 moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
@@ -287,6 +289,12 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   p.alpha = a->alpha;
   p.limit = a->limit;
   p.act = (uint16_t*)a->act_workspace;
+  {
+    uint8_t* split = (uint8_t*)a->act_workspace + round_up((int64_t)R * D * 2, 256);
+    p.split_slots = moe::split_slots_for(R);
+    p.split_counters = p.split_slots > 0 ? (int32_t*)split : nullptr;
+    p.split_partial = p.split_slots > 0 ? (float*)(split + moe::SPLIT_COUNTERS * 4) : nullptr;
+  }
   p.out = a->expert_out;
   p.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
   p.events = (hipEvent_t const*)a->timing_events;

@@ -71,6 +71,13 @@ struct GemmArgs {
   void* out;
   int64_t ldo;
   int64_t lda, ldb;    // row pitch (elements) of the A rows and of the weight rows
+  // split-K of the last, partly filled round of tiles (nullptr: off)
+  float* partial;      // split_slots tiles of BM x BN fp32 partial sums
+  int32_t* counters;   // one arrival counter per split tile, zero on entry
+  int split_slots;     // capacity of `partial` in tiles
+  int G;               // workgroups resident at once (one per CU)
+  int32_t* zero;       // counters this launch clears for the next one (or nullptr)
+  int n_zero;
 };
 
 // LDS layout of one operand stage: 256 rows x BK bf16, CPR 16-byte chunks
@@ -109,6 +116,8 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int L = p.L;
+  if (p.zero && blockIdx.x == 0)
+    for (int i = tid; i < p.n_zero; i += NTHREADS) p.zero[i] = 0;
 
   // ---- prefix of 256-row blocks per expert (wave 0), in LDS
   if (wave == 0) {
@@ -140,11 +149,43 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   constexpr int NBO = (MODE == MODE_GATE_UP) ? BN / 2 : BN;  // output columns per tile
   const int NB = (p.N + NBO - 1) / NBO;
   const int total = s_mbp[L] * NB;
-  const int per_xcd = (total + 7) >> 3;
+  // Tiles run in rounds of G (one workgroup per CU).  When the last round is
+  // at most half full, its `rem` tiles are split along K into S parts each
+  // so that it fills the chip; the last part to finish adds the S partial
+  // sums in a fixed order and runs the epilogue.
+  int rem = 0, S = 1;
+  if (p.partial && p.G > 0) {
+    const int r = total % p.G;
+    if (r > 0 && 2 * r <= p.G) {
+      S = min(min(4, p.G / r), p.split_slots / r);
+      S = min(S, (p.K + BK - 1) / BK / 4);  // at least 4 k stages per part
+      if (S >= 2) rem = r;
+      else S = 1;
+    }
+  }
+  const int full = total - rem;  // a multiple of G (and of 8) when splitting
+  int tile, part = 0;
   const int slot = blockIdx.x >> 3;
-  if (slot >= per_xcd) return;
-  const int tile = (blockIdx.x & 7) * per_xcd + slot;
-  if (tile >= total) return;
+  if (rem == 0) {
+    const int per_xcd = (total + 7) >> 3;
+    if (slot >= per_xcd) return;
+    tile = (blockIdx.x & 7) * per_xcd + slot;
+    if (tile >= total) return;
+  } else {
+    // each XCD runs its share of the whole tiles, then all the parts of its
+    // share of the split tiles (the parts of one tile meet in one L2)
+    const int full_x = full >> 3, parts_x = ((rem + 7) >> 3) * S;
+    if (slot >= full_x + parts_x) return;
+    if (slot < full_x) {
+      tile = (blockIdx.x & 7) * full_x + slot;
+    } else {
+      const int j = (blockIdx.x & 7) * parts_x + (slot - full_x);
+      if (j >= rem * S) return;
+      tile = full + j / S;
+      part = j % S;
+    }
+  }
+  const bool split = tile >= full && rem > 0;
 
   int lo = 0, hi = L - 1;
   while (lo < hi) {
@@ -203,7 +244,10 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     b_off[i] = (uint32_t)wrow * b_row_bytes;
   }
   const int KTF = p.K / BK;              // full k stages
-  const int KT = (p.K + BK - 1) / BK;    // all k stages (the last may be ragged)
+  const int KT_ALL = (p.K + BK - 1) / BK;  // all k stages (the last may be ragged)
+  // this workgroup's k stages [KB, KT): all of them, or one part of a split tile
+  const int KB = split ? part * KT_ALL / S : 0;
+  const int KT = split ? (part + 1) * KT_ALL / S : KT_ALL;
   uint32_t a_voff[LPW_A], b_voff[LPW_B];
 #pragma unroll
   for (int i = 0; i < LPW_A; ++i) a_voff[i] = a_off[i] + (uint32_t)a_chunk[i] * 16u;
@@ -343,20 +387,21 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     }
   };
 
-  issue_a(0);
-  issue_b(0);
-  if (KT > 1) issue_b(1);
-  if (KT > 1) issue_a(1);
-  if (KT > 2) issue_b(2);
-  if (KT > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW_B + LPW_A));
-  else if (KT > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW_B + LPW_A));
+  const int NK = KT - KB;  // stages of this workgroup (>= 1)
+  issue_a(KB);
+  issue_b(KB);
+  if (NK > 1) issue_b(KB + 1);
+  if (NK > 1) issue_a(KB + 1);
+  if (NK > 2) issue_b(KB + 2);
+  if (NK > 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LPW_B + LPW_A));
+  else if (NK > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(LPW_B + LPW_A));
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  zero_tail(0);
+  zero_tail(KB);
   block_barrier();
-  read_frags(0, 0, fa[0], fb[0]);
+  read_frags(KB, 0, fa[0], fb[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
-  const int k_steady = KTF - 3;  // iterations whose loads are all full stages
-  int kt = 0;
+  const int k_steady = min(KTF, KT) - 3;  // iterations whose loads are all full stages
+  int kt = KB;
   if (live_mi == MI) {
     for (; kt < k_steady; ++kt) iteration(kt, std::true_type{}, std::true_type{});
     for (; kt < KT; ++kt) iteration(kt, std::false_type{}, std::true_type{});
@@ -371,6 +416,45 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // and every lane owns four consecutive columns of one row per r/4, written
   // with one 8-byte (bf16) or 16-byte (fp32) store.  Column counts and row
   // pitches are multiples of 8, so these stores are aligned.
+  if (split) {
+    // publish this part's partial sums, then let the last part of the tile
+    // (in arrival order) add all parts in part order
+    float* mine = p.partial + ((int64_t)(tile - full) * S + part) * (BM * BN);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
+          *(f32x4_t*)(mine + ((((mi * NI + ni) * 4 + q) * NTHREADS) + tid) * 4) = v;
+        }
+    __threadfence();
+    __syncthreads();
+    int32_t* s_flag = (int32_t*)smem;
+    if (tid == 0) {
+      const int old = atomicAdd(&p.counters[tile - full], 1);
+      s_flag[0] = (old == S - 1);
+      if (old == S - 1) p.counters[tile - full] = 0;  // ready for the next launch
+    }
+    __syncthreads();
+    if (s_flag[0] == 0) return;
+    __threadfence();
+    const float* first = p.partial + (int64_t)(tile - full) * S * (BM * BN);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t idx = ((((mi * NI + ni) * 4 + q) * NTHREADS) + tid) * 4;
+          f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)(first + idx));
+          for (int t = 1; t < S; ++t) v += __builtin_nontemporal_load((const f32x4_t*)(first + (int64_t)t * (BM * BN) + idx));
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[mi][ni][4 * q + c] = v[c];
+        }
+  }
+
   const float sc = p.escale ? p.escale[e] : 1.0f;
   const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
   if (MODE == MODE_GATE_UP) {
@@ -462,7 +546,9 @@ static hipError_t launch_gemm(KernelT kern, const GemmArgs& a, int max_rows, int
   const int64_t mblocks = (max_rows + BM - 1) / BM + nonempty;
   const int64_t NB = (a.N + NBO - 1) / NBO;
   const int64_t max_tiles = mblocks * NB;
-  const int64_t grid = ((max_tiles + 7) / 8) * 8;
+  // with the split tail round each XCD runs at most G/8 + 4 more workgroups
+  const int64_t extra = a.partial ? a.G / 8 + 4 : 0;
+  const int64_t grid = ((max_tiles + 7) / 8 + extra) * 8;
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   kern<<<(unsigned)grid, NTHREADS, lds, st>>>(a);
@@ -472,6 +558,18 @@ static hipError_t launch_gemm(KernelT kern, const GemmArgs& a, int max_rows, int
 template <int ACT, int FMT, bool GATHER>
 static hipError_t gate_up_dispatch(const GemmArgs& a, int max_rows, hipStream_t st) {
   return launch_gemm(grouped_gemm_bf16_kernel<MODE_GATE_UP, ACT, FMT, GATHER, true>, a, max_rows, BN / 2, st);
+}
+
+// Compute units of the current device (one GEMM workgroup each), cached per device.
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cache[dev] = n;
+  return n;
 }
 
 hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
@@ -494,6 +592,8 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
   g.ldo = q.D;
   g.lda = q.H;
   g.ldb = q.H;
+  g.zero = q.split_counters;  // the down GEMM's arrival counters start at zero
+  g.n_zero = q.split_counters ? SPLIT_COUNTERS : 0;
   const bool gather = (q.x_perm == nullptr);
   hipError_t err;
   if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
@@ -528,6 +628,12 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
   d.ldo = q.H;
   d.lda = q.D;
   d.ldb = q.D;
+  if (q.split_partial && q.split_slots > 0) {
+    d.partial = q.split_partial;
+    d.counters = q.split_counters;
+    d.split_slots = q.split_slots < SPLIT_COUNTERS ? q.split_slots : SPLIT_COUNTERS;
+    d.G = cu_count();
+  }
   if (q.out_bf16)
     err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, true>, d, q.max_rows, BN, st);
   else

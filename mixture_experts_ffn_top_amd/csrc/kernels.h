@@ -43,7 +43,18 @@ struct FfnBf16Params {
   void* out;                     // [max_rows, H]
   int out_bf16;
   hipEvent_t const* events;      // optional: before gate_up, between, after down
+  // split-K tail round of the down GEMM (all three null/0: off)
+  int32_t* split_counters;       // SPLIT_COUNTERS ints
+  float* split_partial;          // split_slots x SPLIT_TILE_FLOATS floats
+  int split_slots;
 };
+constexpr int SPLIT_COUNTERS = 256;
+constexpr int64_t SPLIT_TILE_FLOATS = 256 * 256;
+// partial-tile slots the workspace provides for max_rows rows
+inline int split_slots_for(int64_t max_rows) {
+  const int64_t s = max_rows / 16;
+  return (int)(s < SPLIT_COUNTERS ? s : SPLIT_COUNTERS);
+}
 hipError_t launch_ffn_bf16(const FfnBf16Params& p, hipStream_t st);
 
 struct FfnFp8Params {

@@ -336,6 +336,53 @@ def test_grouped_ffn_rows_and_determinism(moe):
         assert err <= 1e-2, f"expert {e}: O err/rms {err:.3e}"
 
 
+@pytest.mark.parametrize("D", [4096, 4040])
+def test_down_split_k_tail_round(moe, D):
+    """A down GEMM whose tiles fill less than half of one round is split
+    along K (D = 4040 also gives the last part a ragged k stage): the expert
+    rows match the oracle's per-expert MLP, two runs are bit-identical, every
+    partial slot the split needs was written and the arrival counters are
+    back at zero afterwards."""
+    cfg = synth.scaled(synth.get_config(2), T=256, H=512, D=D, E=4, k=2)
+    inp = _gen(cfg)
+    R = cfg.T * cfg.k
+    layer = moe.MoELayer(cfg, inp)
+    act_bytes = (R * D * 2 + 255) // 256 * 256
+    counters = layer.act_ws[act_bytes:act_bytes + 256 * 4].view(torch.int32)
+    partial = layer.act_ws[act_bytes + 256 * 4:].view(torch.float32)
+    partial.fill_(float("nan"))
+    r1 = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    # the split the kernel derives from the tile count and the CU count
+    G = torch.cuda.get_device_properties(0).multi_processor_count
+    off = host(r1["index"]["offsets"])
+    tiles = sum((int(off[e + 1] - off[e]) + 255) // 256 for e in range(cfg.E)) * ((cfg.H + 255) // 256)
+    slots = min(256, R // 16)
+    rem = tiles % G
+    S = min(4, G // rem, slots // rem, ((D + 63) // 64) // 4) if 0 < rem and 2 * rem <= G else 1
+    say(f"[split] D={D} tiles={tiles} G={G} S={S}")
+    assert S >= 2, "the case is meant to exercise the split"
+    assert torch.all(counters == 0)
+    written = partial[: rem * S * 256 * 256].view(rem * S, -1)
+    assert not torch.isnan(written).any(dim=1).any(), "a split part left its partial slot unwritten"
+    O1 = r1["O"].clone()
+    r2 = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    assert torch.equal(O1, r2["O"])
+    hin = synth.to_host(inp)
+    st = host(r1["index"]["sorted_token"])
+    Oh = host(O1)
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        ref = O.expert_mlp(hin["x"][st[rows]], hin["w_gate_up"][e], hin["w_down"][e], fmt=cfg.gate_up_format,
+                           activation=cfg.activation, alpha=cfg.alpha, limit=cfg.limit)
+        err, _ = rel_rms_err(Oh[rows], ref)
+        say(f"  expert {e}: O err/rms {err:.3e}")
+        assert err <= 1e-2, f"expert {e}: O err/rms {err:.3e}"
+
+
 def test_abi_errors_on_gpu_path(moe):
     """Invalid arguments are refused before any launch, also from the binding."""
     x = torch.zeros((4, 24), dtype=torch.bfloat16, device=DEV)
