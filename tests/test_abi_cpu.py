@@ -148,7 +148,9 @@ def test_combine_validation(kw, frag):
 def test_workspace_queries_and_status_strings():
     lib = m.lib()
     assert lib.moe_build_indices_workspace_bytes(16384, 8, 256) >= 256 * 32 * 4
-    assert lib.moe_ffn_workspace_bytes(8192, 14336, 0) == 8192 * 14336 * 2
+    # bf16: A, then 256 split-K arrival counters and min(256, R/16) fp32 256x256 partial tiles
+    assert lib.moe_ffn_workspace_bytes(8192, 14336, 0) == 8192 * 14336 * 2 + 256 * 4 + 256 * 256 * 256 * 4
+    assert lib.moe_ffn_workspace_bytes(64, 512, 0) == 64 * 512 * 2 + 256 * 4 + 4 * 256 * 256 * 4
     assert lib.moe_ffn_workspace_bytes(100, 256, 1) >= 100 * 256 + 100 * 2 * 4
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
