@@ -56,6 +56,16 @@ constexpr int F_EPI_PITCH = 132;                          // floats per row of t
 __device__ __forceinline__ int f8_swz_f(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int f8_swz(int row, int chunk) { return row * F_BK + ((chunk ^ f8_swz_f(row)) << 4); }
 
+// Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
+constexpr int F8_BUF_DWORD3 = 0x00020000;
+
+// Workgroup barrier that publishes LDS (ds writes and the loads into LDS this
+// wave waited for) without __syncthreads()'s full wait for the loads into
+// LDS still in flight; the clobber keeps LDS accesses on their side of it.
+__device__ __forceinline__ void f8_block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 struct Fp8GemmArgs {
   const int32_t* offsets;
   int L;
@@ -124,12 +134,15 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     if (s_mbp[mid] * NB <= tile) lo = mid;
     else hi = mid - 1;
   }
-  const int e = lo;
+  // uniform by construction; made scalar so that the address bases live in SGPRs
+  const int e = __builtin_amdgcn_readfirstlane(lo);
   const int nmb = s_mbp[e + 1] - s_mbp[e];
-  const int local = tile - s_mbp[e] * NB;
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[e] * NB);
   const int nb = local / nmb, mb = local % nmb;
-  const int row_beg = p.offsets[e] + mb * F_BM;
-  const int row_end = p.offsets[e + 1];
+  const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * F_BM);
+  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wn_s = wave_s % F_WAVES_N;
   const int KT = p.K / F_BK;       // K is a multiple of 128
   const int KB = KT;               // scale blocks along K
 
@@ -167,20 +180,32 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   const int64_t xs_row = p.gather ? (int64_t)p.gather[xs_r] : (int64_t)xs_r;
   const float* xs_src = p.A_scale + xs_row * KB;
 
+  // Buffer loads straight into LDS: per-lane offsets fixed for the tile, the
+  // k offset of a stage in the scalar offset, the destination in M0.
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, F8_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, F8_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A_scale, (short)0, 0x7fffffff, F8_BUF_DWORD3);
+  uint32_t a_voff[F_LPW_A], b_voff[F_LPW_B];
+#pragma unroll
+  for (int i = 0; i < F_LPW_A; ++i) a_voff[i] = a_off[i] + (uint32_t)a_chunk[i] * 16u;
+#pragma unroll
+  for (int i = 0; i < F_LPW_B; ++i) b_voff[i] = b_off[i] + (uint32_t)b_chunk[i] * 16u;
+  const uint32_t xs_voff = (uint32_t)(xs_row * KB) * 4u;
+
   auto stage_a = [&](int kt) { return smem + (kt % F_NSTAGE) * F_STAGE_BYTES; };
   auto stage_xs = [&](int kt) { return (float*)(smem + F_NSTAGE * F_STAGE_BYTES + (kt % F_XS_BUFS) * F_XS_BYTES); };
   auto issue = [&](int kt) {
-    uint8_t* as = stage_a(kt) + wave * F_LPW_A * 1024;
-    uint8_t* bs = stage_a(kt) + F_A_BYTES + wave * F_LPW_B * 1024;
-    const uint32_t kb = (uint32_t)kt * F_BK;
+    uint8_t* as = stage_a(kt) + wave_s * F_LPW_A * 1024;
+    uint8_t* bs = stage_a(kt) + F_A_BYTES + wave_s * F_LPW_B * 1024;
+    const int kb = kt * F_BK;
 #pragma unroll
     for (int i = 0; i < F_LPW_A; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(p.A + a_off[i] + kb + a_chunk[i] * 16), (lptr_t)(as + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(as + i * 1024), 16, a_voff[i], kb, 0, 0);
 #pragma unroll
     for (int i = 0; i < F_LPW_B; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(Wexp + b_off[i] + kb + b_chunk[i] * 16), (lptr_t)(bs + i * 1024), 16, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(bs + i * 1024), 16, b_voff[i], kb, 0, 0);
     if (lane < 16)
-      __builtin_amdgcn_global_load_lds((gptr_t)(xs_src + kt), (lptr_t)(stage_xs(kt) + wave * 16), 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(stage_xs(kt) + wave_s * 16), 4, xs_voff, kt * 4, 0, 0);
   };
   auto wait_stage = [&](int kt) {
     const int newer = min(KT - 1, kt + F_NSTAGE - 2) - kt;
@@ -229,10 +254,13 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   int ws_blk[F_NI];
 #pragma unroll
   for (int ni = 0; ni < F_NI; ++ni) {
-    if (MODE == F8_DOWN) ws_blk[ni] = min((nb * F_BN + wn * F_WTN) / 128, p.N / 128 - 1);
+    if (MODE == F8_DOWN) ws_blk[ni] = min((nb * F_BN + wn_s * F_WTN) / 128, p.N / 128 - 1);
     else ws_blk[ni] = (ni == 0) ? nb : (p.N / 128 + nb);  // gate block, up block
   }
-  const float* wsc = p.W_scale + (int64_t)e * p.ws_estride;
+  // read through the scalar cache: uniform per wave, and a vector load here
+  // would make the wait for it drain the loads into LDS still in flight
+  typedef const __attribute__((address_space(4))) float* scalar_f32_ptr;
+  const scalar_f32_ptr wsc = (scalar_f32_ptr)(p.W_scale + (int64_t)e * p.ws_estride);
   auto rescale = [&](int kt) {
     const float* xs = stage_xs(kt);
     float sw[F_NI];
@@ -255,7 +283,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   // ---- main loop: stage kt = two 64-wide k steps and one scale block
   for (int s = 0; s < F_NSTAGE && s < KT; ++s) issue(s);
   wait_stage(0);
-  __syncthreads();
+  f8_block_barrier();
   i32x8_t fa[2][F_MI], fb[2][F_NI];
   read_frags(0, 0, fa[0], fb[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
@@ -266,7 +294,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     if (kt + 1 < KT) wait_stage(kt + 1);
-    __syncthreads();
+    f8_block_barrier();
     // stage kt's operands are all in registers: refill its buffer.  The
     // scales use F_XS_BUFS > F_NSTAGE buffers, so stage kt's scales survive
     // until the rescale below.
