@@ -180,8 +180,13 @@ def main():
     peak = PEAK_FP8_TFLOPS if cfg.operand_dtype == "fp8" else PEAK_BF16_TFLOPS
     gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
     ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
-    x_bytes = 2 * cfg.T * cfg.H
-    comb_bytes = 4 * R * cfg.H + 8 * R + 2 * cfg.T * cfg.H
+    # algorithmic HBM bytes of the two bandwidth kernels
+    if cfg.router == "softmax":   # reads x and W_gate, writes indices and weights
+        route_bytes = 2 * cfg.T * cfg.H + 2 * cfg.H * cfg.E + 8 * cfg.T * cfg.k
+    else:                         # reads the logits and the bias, writes indices and weights
+        route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
+    o_bytes = 2 if cfg.operand_dtype == "fp8" else 4   # expert rows O: bf16 or fp32
+    comb_bytes = o_bytes * R * cfg.H + 8 * R + 2 * cfg.T * cfg.H
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
@@ -199,7 +204,7 @@ def main():
         "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),
                          "gate_up": round(t_gu, 4), "down": round(t_dn, 4), "combine": round(t_comb, 4),
                          "layer_device": round(t_layer_dev, 4)},
-        "hbm_gbs": {"route": round(x_bytes / (t_route * 1e-3) / 1e9, 1),
+        "hbm_gbs": {"route": round(route_bytes / (t_route * 1e-3) / 1e9, 1),
                     "combine": round(comb_bytes / (t_comb * 1e-3) / 1e9, 1)},
         "weight_layout": "out_in (transposed stacked weights, laid out once at load)",
     }
