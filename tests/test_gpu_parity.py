@@ -457,6 +457,26 @@ def test_fp8_layer_small(moe, changes, nsample, gather):
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=3), FP8_TOL)
 
 
+def test_fp8_zero_scales(moe):
+    """Zero block scales (with nonzero codes under them) contribute nothing,
+    also in the first k block of a tile, and all-zero tokens (scale 1, zero
+    codes) pass through: the GEMMs keep their accumulator units across them."""
+    cfg = synth.scaled(synth.get_config(5), T=512, E=8, H=512, D=256)
+    inp = _gen(cfg)
+    gus, ds = inp["w_gate_up_scale"], inp["w_down_scale"]   # [E, H/128, 2D/128], [E, D/128, H/128]
+    gus[0, 0, :] = 0.0          # expert 0: the first k block of every gate_up column block
+    gus[1, 2, 0] = 0.0          # expert 1: one gate block in the middle of K
+    gus[2, :, 3] = 0.0          # expert 2: a whole up column block
+    ds[3, 1, :] = 0.0           # expert 3: a down k block
+    ds[4, :, 2] = 0.0           # expert 4: a whole down column block
+    inp["x"][5:9] = 0.0         # whole tokens at zero
+    inp["x"][20, 128:256] = 0.0  # one zero 128-group of a token
+    say("[fp8 zero scales]")
+    layer, res = _run_layer(moe, cfg, inp)
+    _check_fp8_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
+
+
 def test_fp8_layer_full_size(moe):
     cfg = synth.get_config(5)
     inp = _gen(cfg)
