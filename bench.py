@@ -65,8 +65,11 @@ class HipEvents:
 
 
 def _src_hash() -> str:
-    p = os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc", "ffn_bf16.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the sources that make the bf16 GEMM kernels."""
+    h = hashlib.sha256()
+    for f in ("ffn_bf16.hip", "common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_ffn_top_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def _traffic():
@@ -79,6 +82,94 @@ def _traffic():
     if d.get("kernel_source_sha256_16") != _src_hash():
         return None
     return d.get("bytes_per_launch")
+
+
+PROFILE_CMDS = """# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp):
+#   rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/trace -o bench -- \\
+#       python3 $REPO/bench.py --no-cpu-baseline > $REPO/gpurun_out/prof/trace.log
+#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'grouped_gemm|router|csr|combine|permute' -f csv \\
+#       -d $REPO/gpurun_out/prof/FETCH_SIZE -o bench -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline
+#   (the same with WRITE_SIZE into .../WRITE_SIZE)
+#   rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/prof/copy_FETCH_SIZE -o copy -- \\
+#       python3 $REPO/bench.py --copy-calibration        (and WRITE_SIZE into .../copy_WRITE_SIZE)
+#   python3 bench.py --summarize-profile gpurun_out/prof    (writes the files under profiles/)"""
+
+
+def _short(name: str) -> str:
+    name = name.strip('"')
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_profile(d: str):
+    """Turn the rocprofv3 outputs of PROFILE_CMDS into the committed summaries."""
+    import csv
+    prof = os.path.join(ROOT, "profiles")
+    # kernel statistics of the bench run
+    rows = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_stats.csv"))))
+    mine = [r for r in rows if "moe::" in r["Name"]]
+    line = None
+    for ln in open(os.path.join(d, "trace.log")):
+        if ln.startswith('{"metric"'):
+            line = json.loads(ln)
+    bd = line["breakdown_ms"] if line else {}
+    out = ["# rocprofv3 kernel statistics: Mixtral-shape MoE FFN layer (bench.py default workload)",
+           "# workload: T=4096 tokens, hidden 4096, 8 experts, top-2 softmax gate, moe_dim 14336,",
+           "#           concatenated gate_up, SiLU, bf16 operands, fp32 accumulate",
+           PROFILE_CMDS,
+           f"# calls = warmup + timed steps of bench.py.  Durations in microseconds; only this library's",
+           "# kernels are listed (the torch kernels that generate the synthetic inputs are omitted).",
+           f"# bench.py's own HIP-event timing in the same run: gate_up {bd.get('gate_up', 0) * 1e3:.1f} us, "
+           f"down {bd.get('down', 0) * 1e3:.1f} us per launch.", "",
+           f"{'kernel':58s}{'calls':>7s}{'avg_us':>10s}{'min_us':>10s}{'max_us':>10s}"]
+    for r in sorted(mine, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"{_short(r['Name']):58s}{int(r['Calls']):7d}{float(r['AverageNs']) / 1e3:10.1f}"
+                   f"{float(r['MinNs']) / 1e3:10.1f}{float(r['MaxNs']) / 1e3:10.1f}")
+    out += ["", "# gate_up = grouped_gemm_bf16_kernel<0,...> (SiLU, concatenated, gathered x, bf16 out)",
+            "# down    = grouped_gemm_bf16_kernel<1,...> (fp32 out)"]
+    open(os.path.join(prof, "mixtral_layer_kernel_stats.txt"), "w").write("\n".join(out) + "\n")
+
+    # HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated on a plain copy of known size
+    def counters(path):
+        per = {}
+        for r in csv.DictReader(open(path)):
+            per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return per
+    n_copy = 1 << 30
+    cf = counters(os.path.join(d, "copy_FETCH_SIZE", "copy_counter_collection.csv"))
+    cw = counters(os.path.join(d, "copy_WRITE_SIZE", "copy_counter_collection.csv"))
+    copy_f = [v for k, vs in cf.items() if "copyBuffer" in k for v in vs]
+    copy_w = [v for k, vs in cw.items() if "copyBuffer" in k for v in vs]
+    f_factor = n_copy / (sum(copy_f) / len(copy_f) * 1024)
+    w_factor = n_copy / (sum(copy_w) / len(copy_w) * 1024)
+    fe = counters(os.path.join(d, "FETCH_SIZE", "bench_counter_collection.csv"))
+    wr = counters(os.path.join(d, "WRITE_SIZE", "bench_counter_collection.csv"))
+    out = ["# HBM traffic per launch from rocprofv3 counters: Mixtral-shape MoE FFN layer (bench.py workload)",
+           PROFILE_CMDS,
+           f"# calibration, a plain 1 GiB device copy: FETCH_SIZE {sum(copy_f) / len(copy_f):.0f} KiB -> read factor "
+           f"{f_factor:.3f}; WRITE_SIZE {sum(copy_w) / len(copy_w):.0f} KiB -> write factor {w_factor:.3f}",
+           "# bytes = counter KiB x 1024 x factor, averaged over the launches of each kernel.", "",
+           f"{'kernel':58s}{'read_MB':>10s}{'write_MB':>10s}{'total_MB':>10s}"]
+    gu = None
+    for k in fe:
+        rd = sum(fe[k]) / len(fe[k]) * 1024 * f_factor
+        wb = sum(wr.get(k, [0.0])) / max(len(wr.get(k, [])), 1) * 1024 * w_factor
+        out.append(f"{k:58s}{rd / 1e6:10.1f}{wb / 1e6:10.1f}{(rd + wb) / 1e6:10.1f}")
+        if k.startswith("moe::grouped_gemm_bf16_kernel<0"):
+            gu = (rd, wb)
+    out += ["", "# algorithmic bytes per launch for comparison: gate_up reads the 8 experts' gate_up weights",
+            "# (1879.0 MB) and the rows of the 4096 tokens (33.6 MB, each read once) and writes A (235.0 MB);",
+            "# down reads the down weights (939.5 MB) and A (235.0 MB) and writes O fp32 (134.2 MB).",
+            "# Traffic above that is weight tiles fetched again by m-blocks that missed each other in L2,",
+            "# and activation rows re-read from the Infinity Cache."]
+    open(os.path.join(prof, "mixtral_layer_hbm_traffic.txt"), "w").write("\n".join(out) + "\n")
+    if gu:
+        json.dump({"kernel": "grouped gate_up GEMM (bf16, SiLU, concatenated, gathered x)",
+                   "workload": "Mixtral-shape layer, T=4096", "bytes_per_launch": round(gu[0] + gu[1]),
+                   "read_bytes": round(gu[0]), "write_bytes": round(gu[1]),
+                   "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+                   "kernel_source_sha256_16": _src_hash(), "source": "profiles/mixtral_layer_hbm_traffic.txt"},
+                  open(TRAFFIC_FILE, "w"), indent=1)
+    print(f"[bench] wrote the profile summaries under {prof}", file=sys.stderr)
 
 
 def cpu_baseline(cfg, inp, n_tokens: int):
@@ -114,7 +205,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
+    ap.add_argument("--summarize-profile", metavar="DIR",
+                    help="only write the profiles/ summaries from the rocprofv3 outputs in DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(args.summarize_profile)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
