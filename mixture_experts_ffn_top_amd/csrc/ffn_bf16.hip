@@ -9,10 +9,11 @@
 // wave a 128 x 64 sub-tile of 4 x 2 MFMA blocks (128 fp32 accumulators per
 // lane); while one wave of a SIMD waits at a barrier or on LDS the other
 // issues MFMAs.  Both operands go straight from global memory into LDS
-// (direct-to-LDS loads, no register staging) in 64-wide k stages, double
-// buffered: the loads of stage k+1 are in flight while stage k runs on the
-// matrix cores, and the MFMA fragments of the next 16-wide k step are read
-// from LDS while the current step's MFMAs issue.
+// (buffer loads with an LDS destination, no register staging) in 64-wide k
+// stages: the activation rows double buffered, the weight rows triple
+// buffered, so the loads of the next stages are in flight while a stage runs
+// on the matrix cores, and the MFMA fragments of the next 16-wide k step are
+// read from LDS while the current step's MFMAs issue.
 //
 // The per-expert row counts live only on the device.  Every workgroup reads
 // expert_offsets, builds the prefix of 256-row blocks per expert in LDS and
