@@ -382,14 +382,25 @@ def combine(expert_out, row_of_slot, expert_weights=None, token_mask=None) -> np
 # Whole layer
 # --------------------------------------------------------------------------
 
-def _expert_weights_f64(inp, e, operand):
+def _expert_weights_f64(inp, e, operand, suffix=""):
     if operand == "fp8":
-        wgu = dequant_weight_block128(inp["w_gate_up"][e], inp["w_gate_up_scale"][e])
-        wd = dequant_weight_block128(inp["w_down"][e], inp["w_down_scale"][e])
+        wgu = dequant_weight_block128(inp["w_gate_up" + suffix][e], inp["w_gate_up" + suffix + "_scale"][e])
+        wd = dequant_weight_block128(inp["w_down" + suffix][e], inp["w_down" + suffix + "_scale"][e])
     else:
-        wgu = np.asarray(inp["w_gate_up"][e], np.float64)
-        wd = np.asarray(inp["w_down"][e], np.float64)
+        wgu = np.asarray(inp["w_gate_up" + suffix][e], np.float64)
+        wd = np.asarray(inp["w_down" + suffix][e], np.float64)
     return wgu, wd
+
+
+def shared_weights(cfg, sink_weights, T):
+    """Per-token weight of each shared expert: the sink lanes' routing
+    weights for the sigmoid router (sink_gate_router_kernel page: the sink
+    lanes are gated shared experts), 1 for the softmax router's always-on
+    shared experts (StackedMoE page: has_shared_experts)."""
+    if cfg.router == "sigmoid_sink":
+        assert cfg.n_shared == cfg.s, "the sink lanes gate the shared experts one to one"
+        return np.asarray(sink_weights, np.float64).reshape(T, cfg.n_shared)
+    return np.ones((T, cfg.n_shared), np.float64)
 
 
 def layer_inputs_x(inp, operand):
@@ -419,19 +430,25 @@ def route(inp, cfg, logits=None):
 
 def layer(inp, cfg, *, indices=None, weights=None, tokens=None, token_mask=None,
           expert_start=0, num_local=None, gate_up_expert_scales=None,
-          down_expert_scales=None):
+          down_expert_scales=None, sink_weights=None):
     """MoE FFN forward for the tokens in `tokens` (all by default), float64.
 
     y[t] = sum_j w[t,j] * MLP_{e(t,j)}(x[t]) over the slots whose expert is
-    local and whose token is valid.  Routing is computed by `route` unless
-    indices/weights are passed in (to share a routing under test).  The
-    experts are visited one at a time: gather the tokens that chose it, run
-    its MLP, scatter-add the weighted rows -- the per-expert loop of
-    GroupedExperts._forward_loop on the nemo_automodel experts page.
+    local and whose token is valid, plus, when the configuration has shared
+    experts, sum_i sw[t,i] * MLP_shared_i(x[t]) with the weights of
+    `shared_weights` (the shared experts are the same gated MLP with
+    moe_dim = shared_dim).  Routing is computed by `route` unless
+    indices/weights (and sink_weights) are passed in, to share a routing
+    under test.  The experts are visited one at a time: gather the tokens
+    that chose it, run its MLP, scatter-add the weighted rows -- the
+    per-expert loop of GroupedExperts._forward_loop on the nemo_automodel
+    experts page.
     """
     if indices is None or weights is None:
         r = route(inp, cfg)
         indices, weights = r["indices"], r["weights"]
+        if sink_weights is None:
+            sink_weights = r["sink_weights"]
     indices = np.asarray(indices, np.int64)
     weights = np.asarray(weights, np.float64)
     T = indices.shape[0]
@@ -457,4 +474,16 @@ def layer(inp, cfg, *, indices=None, weights=None, tokens=None, token_mask=None,
                        gate_up_scale=sgu, down_scale=sd,
                        act_format="fp8" if operand == "fp8" else "bf16")
         np.add.at(y, sel_t, w_s[sel_t, sel_j][:, None] * o)
+    if getattr(cfg, "n_shared", 0):
+        if cfg.router == "sigmoid_sink" and sink_weights is None:
+            sink_weights = route(inp, cfg)["sink_weights"]
+        sw = shared_weights(cfg, sink_weights, T)[tokens]
+        for i in range(cfg.n_shared):
+            wgu, wd = _expert_weights_f64(inp, i, operand, "_shared")
+            bgu = inp["b_gate_up_shared"][i] if cfg.has_bias else None
+            bd = inp["b_down_shared"][i] if cfg.has_bias else None
+            o = expert_mlp(xs, wgu, wd, fmt=cfg.gate_up_format, activation=cfg.activation,
+                           alpha=cfg.alpha, limit=cfg.limit, b_gate_up=bgu, b_down=bd,
+                           act_format="fp8" if operand == "fp8" else "bf16")
+            y += np.where(valid[:, None], sw[:, i:i + 1] * o, 0.0)
     return y

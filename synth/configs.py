@@ -22,6 +22,9 @@ class MoEConfig:
     D: int                      # moe_dim
     router: str = "softmax"     # "softmax" | "sigmoid_sink"
     s: int = 0                  # n_shared_experts (sink lanes), sigmoid router only
+    n_shared: int = 0           # shared experts with an FFN (sigmoid router: gated by the sink lanes,
+                                # so n_shared == s; softmax router: always on, weight 1)
+    shared_dim: int = 0         # shared_experts_dim: moe_dim of the shared experts
     gate_up_format: str = "concatenated"   # | "interleaved"
     has_bias: bool = False
     activation: str = "silu"    # "silu" | "swigluoai" | "gelu_tanh"
@@ -50,7 +53,8 @@ CONFIGS = {
     1: MoEConfig(1, "tiny", T=64, H=256, E=8, k=2, D=512),
     2: MoEConfig(2, "mixtral", T=4096, H=4096, E=8, k=2, D=14336),
     3: MoEConfig(3, "sink", T=8192, H=2048, E=128, k=6, D=768,
-                 router="sigmoid_sink", s=2, route_scale=2.5, global_scale=1.0),
+                 router="sigmoid_sink", s=2, n_shared=2, shared_dim=768,
+                 route_scale=2.5, global_scale=1.0),
     4: MoEConfig(4, "gptoss", T=4096, H=2880, E=32, k=4, D=2880,
                  gate_up_format="interleaved", has_bias=True,
                  activation="swigluoai", alpha=1.702, limit=7.0),

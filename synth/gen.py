@@ -94,6 +94,31 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
     if cfg.has_bias:
         out["b_gate_up"] = _normal((E, 2 * D), cfg.w_std, d, c, 5, 0, salt).to(torch.bfloat16)
         out["b_down"] = _normal((E, H), cfg.w_std, d, c, 6, 0, salt).to(torch.bfloat16)
+    if cfg.n_shared:
+        # shared experts: the same gated MLP with moe_dim = shared_dim, in the
+        # layer's operand dtype (tensor ids 7..10, one stream per shared expert)
+        S, Ds = cfg.n_shared, cfg.shared_dim
+        if cfg.operand_dtype == "bf16":
+            sgu = torch.empty((S, H, 2 * Ds), device=d, dtype=torch.bfloat16)
+            sd = torch.empty((S, Ds, H), device=d, dtype=torch.bfloat16)
+            for i in range(S):
+                sgu[i] = _normal((H, 2 * Ds), cfg.w_std, d, c, 7, i, salt).to(torch.bfloat16)
+                sd[i] = _normal((Ds, H), cfg.w_std, d, c, 8, i, salt).to(torch.bfloat16)
+            out["w_gate_up_shared"], out["w_down_shared"] = sgu, sd
+        else:
+            assert Ds % 128 == 0
+            sgu = torch.empty((S, H, 2 * Ds), device=d, dtype=torch.uint8)
+            sgus = torch.empty((S, H // 128, 2 * Ds // 128), device=d, dtype=torch.float32)
+            sd = torch.empty((S, Ds, H), device=d, dtype=torch.uint8)
+            sds = torch.empty((S, Ds // 128, H // 128), device=d, dtype=torch.float32)
+            for i in range(S):
+                sgu[i], sgus[i] = _quant_fp8_blocks(_normal((H, 2 * Ds), cfg.w_std, d, c, 7, i, salt))
+                sd[i], sds[i] = _quant_fp8_blocks(_normal((Ds, H), cfg.w_std, d, c, 8, i, salt))
+            out["w_gate_up_shared"], out["w_gate_up_shared_scale"] = sgu, sgus
+            out["w_down_shared"], out["w_down_shared_scale"] = sd, sds
+        if cfg.has_bias:
+            out["b_gate_up_shared"] = _normal((S, 2 * Ds), cfg.w_std, d, c, 9, 0, salt).to(torch.bfloat16)
+            out["b_down_shared"] = _normal((S, H), cfg.w_std, d, c, 10, 0, salt).to(torch.bfloat16)
     return out
 
 

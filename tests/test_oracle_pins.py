@@ -582,3 +582,54 @@ def test_expert_mlp_bias_scales_brute_force(fmt, act):
         for c in range(H):
             want = sd * math.fsum(a[d] * wd[d, c] for d in range(D)) + bd[c]
             assert got[r, c] == pytest.approx(want, rel=1e-12, abs=1e-14)
+
+
+def _mlp_brute(xr, wgu, wd):
+    """silu gated MLP of one row in Python loops; A rounded to bf16 as stored."""
+    H, D2 = wgu.shape
+    D = D2 // 2
+    a = []
+    for d in range(D):
+        g = math.fsum(float(xr[h]) * float(wgu[h, d]) for h in range(H))
+        u = math.fsum(float(xr[h]) * float(wgu[h, D + d]) for h in range(H))
+        a.append(float(O.bf16_round(np.array([g / (1 + math.exp(-g)) * u]))[0]))
+    return [math.fsum(a[d] * float(wd[d, hh]) for d in range(D)) for hh in range(wd.shape[1])]
+
+
+@pytest.mark.parametrize("router", ["sigmoid_sink", "softmax"])
+def test_shared_experts_brute_force(router):
+    """Shared experts add sum_i sw[t,i] * MLP_i(x[t]) to the routed output:
+    sw = the sink-lane weights for the sigmoid router (sink_gate_router_kernel
+    page: sink lanes are gated shared experts), 1 for the softmax router's
+    always-on shared experts (StackedMoE page: has_shared_experts).  Checked
+    against Python loops, and masked tokens stay zero rows."""
+    rng = np.random.default_rng(31)
+    T, H, D, E, k, S, Ds = 5, 6, 3, 3, 1, 2, 4
+    x = O.bf16_round(rng.standard_normal((T, H)))
+    inp = {"x": x, "w_gate_up": O.bf16_round(rng.standard_normal((E, H, 2 * D)) * 0.3),
+           "w_down": O.bf16_round(rng.standard_normal((E, D, H)) * 0.3),
+           "w_gate_up_shared": O.bf16_round(rng.standard_normal((S, H, 2 * Ds)) * 0.3),
+           "w_down_shared": O.bf16_round(rng.standard_normal((S, Ds, H)) * 0.3)}
+    if router == "sigmoid_sink":
+        inp["logits"] = rng.standard_normal((T, E + S)).astype(np.float32) * 2
+        inp["expert_bias"] = np.zeros(E, np.float32)
+        cfg = _Cfg(T=T, H=H, E=E, k=k, D=D, router=router, s=S, n_shared=S, shared_dim=Ds, route_scale=2.5)
+        r = O.route(inp, cfg)
+        sw = r["sink_weights"]
+    else:
+        inp["w_gate"] = O.bf16_round(rng.standard_normal((E, H)))
+        cfg = _Cfg(T=T, H=H, E=E, k=k, D=D, n_shared=S, shared_dim=Ds)
+        r = O.route(inp, cfg)
+        sw = np.ones((T, S))
+    y = O.layer(inp, cfg, indices=r["indices"], weights=r["weights"], sink_weights=r["sink_weights"])
+    routed = O.layer(inp, _Cfg(**{**cfg.__dict__, "n_shared": 0}), indices=r["indices"], weights=r["weights"])
+    for t in range(T):
+        want = [0.0] * H
+        for i in range(S):
+            o = _mlp_brute(x[t], inp["w_gate_up_shared"][i], inp["w_down_shared"][i])
+            want = [want[h] + sw[t, i] * o[h] for h in range(H)]
+        assert np.allclose(y[t] - routed[t], want, rtol=1e-11, atol=1e-13)
+    mask = np.array([1, 0, 1, 1, 0], np.uint8)
+    ym = O.layer(inp, cfg, indices=r["indices"], weights=r["weights"], sink_weights=r["sink_weights"],
+                 token_mask=mask)
+    assert np.all(ym[mask == 0] == 0.0) and np.allclose(ym[mask == 1], y[mask == 1], rtol=0, atol=0)
