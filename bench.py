@@ -240,14 +240,18 @@ def main():
     layer = moe.MoELayer(cfg, inp)
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
-    # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end), 6 after combine
-    ev = HipEvents(7 * (K + W))
+    # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
+    # 6 after combine, 7..9 the shared experts' ffn (if any)
+    NE = 10
+    ev = HipEvents(NE * (K + W))
+    has_shared = getattr(cfg, "n_shared", 0) > 0
 
     def step(i):
-        base = 7 * i
+        base = NE * i
         slots = {1: base + 1, 2: base + 2, 3: base + 6}
         ev.record(base + 0, stream)
-        layer.forward(inp["x"], mark=lambda j: ev.record(slots[j], stream), ffn_events=ev.triple(base + 3))
+        layer.forward(inp["x"], mark=lambda j: ev.record(slots[j], stream), ffn_events=ev.triple(base + 3),
+                      shared_events=ev.triple(base + 7) if has_shared else None)
 
     print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
     for i in range(W):
@@ -262,11 +266,12 @@ def main():
     ms_step = dt * 1000.0 / K
 
     def mean_ms(a, b):
-        return sum(ev.elapsed_ms(7 * i + a, 7 * i + b) for i in range(W, W + K)) / K
+        return sum(ev.elapsed_ms(NE * i + a, NE * i + b) for i in range(W, W + K)) / K
 
     t_route, t_idx = mean_ms(0, 1), mean_ms(1, 2)
     t_gu, t_dn = mean_ms(3, 4), mean_ms(4, 5)
-    t_comb = mean_ms(5, 6)
+    t_shared = mean_ms(7, 9) if has_shared else 0.0
+    t_comb = (mean_ms(9, 6) if has_shared else mean_ms(5, 6))
     t_layer_dev = mean_ms(0, 6)
     ev.close()
 
@@ -282,7 +287,8 @@ def main():
     else:                         # reads the logits and the bias, writes indices and weights
         route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
     o_bytes = 2 if cfg.operand_dtype == "fp8" else 4   # expert rows O: bf16 or fp32
-    comb_bytes = o_bytes * R * cfg.H + 8 * R + 2 * cfg.T * cfg.H
+    n_sh = getattr(cfg, "n_shared", 0)
+    comb_bytes = o_bytes * (R + n_sh * cfg.T) * cfg.H + 8 * R + 4 * n_sh * cfg.T + 2 * cfg.T * cfg.H
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
@@ -298,8 +304,9 @@ def main():
                      "flops_per_launch": gu_flops, "avg_launch_ms": round(t_gu, 4)},
         "ffn_tflops": round(ffn_tf, 2), "ffn_mfma_frac": round(ffn_tf / peak, 4),
         "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),
-                         "gate_up": round(t_gu, 4), "down": round(t_dn, 4), "combine": round(t_comb, 4),
-                         "layer_device": round(t_layer_dev, 4)},
+                         "gate_up": round(t_gu, 4), "down": round(t_dn, 4),
+                         **({"shared_experts_ffn": round(t_shared, 4)} if has_shared else {}),
+                         "combine": round(t_comb, 4), "layer_device": round(t_layer_dev, 4)},
         "hbm_gbs": {"route": round(route_bytes / (t_route * 1e-3) / 1e9, 1),
                     "combine": round(comb_bytes / (t_comb * 1e-3) / 1e9, 1)},
         "weight_layout": "out_in (transposed stacked weights, laid out once at load)",

@@ -11,6 +11,7 @@
  *   moe_grouped_ffn    grouped gate_up GEMM with the gated activation fused
  *                      into its epilogue, then the grouped down GEMM
  *   moe_combine        router-weighted sum of each token's expert rows
+ *   moe_shared_indices buckets of the shared (sink-lane) experts: all tokens each
  *
  * Sources (web pages, cited by title and section):
  *   [StackedMoE]  MAX Python API, max.nn.moe.StackedMoE: constructor
@@ -53,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -297,12 +298,23 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t opera
  * summed in fp32 in ascending j, rounded to bf16; masked tokens give zero
  * rows.  Deterministic (a gather, no atomics).
  *
+ * With shared experts ([StackedMoE] has_shared_experts; [SinkRouter] the
+ * sink lanes are gated shared experts) the shared rows are added after the
+ * routed slots, in ascending i:
+ *   y[t] += sum over i = 0..n_shared-1 of shared_weights[t, i] * O_sh[i*T + t]
+ *
  *   num_tokens T, n_experts_per_tok k, hidden_dim H               host
  *   expert_out     O [*, H], fp32 or bf16 (out_dtype, host)
  *   row_of_slot    int32 [T, k]
  *   expert_weights fp32 [T, k] or NULL (weight 1: router weight applied first)
  *   token_mask     uint8 [T] or NULL
  *   y              bf16 [T, H] out
+ *   n_shared       host: shared experts, 0 for none
+ *   shared_out     O_sh [n_shared * T, H], same dtype as expert_out (row i*T + t:
+ *                  shared expert i on token t, as moe_grouped_ffn writes it
+ *                  with the buckets of moe_shared_indices)
+ *   shared_weights fp32 [T, n_shared] (the router's sink_weights) or NULL
+ *                  (weight 1: always-on shared experts)
  * ---------------------------------------------------------------------- */
 typedef struct moe_combine_args {
   int32_t num_tokens;
@@ -314,9 +326,28 @@ typedef struct moe_combine_args {
   const float* expert_weights;
   const uint8_t* token_mask;
   void* y;
+  int32_t n_shared;
+  const void* shared_out;
+  const float* shared_weights;
 } moe_combine_args_t;
 
 moe_status_t moe_combine(const moe_combine_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_shared_indices -- buckets for the shared experts ([StackedMoE]
+ * has_shared_experts, shared_experts_dim; [SinkRouter] the n_shared_experts
+ * sink lanes are gated shared experts): every token goes to every shared
+ * expert, so shared expert i is the bucket of rows [i*T, (i+1)*T) in token
+ * order.  With these, moe_grouped_ffn (in its gather form, x + sorted_token)
+ * runs the shared experts' MLPs, and moe_combine adds them.
+ *
+ *   num_tokens T, n_shared                                        host
+ *   expert_offsets int32 [n_shared + 1] out: i * T
+ *   sorted_token   int32 [n_shared * T] out: row i*T + t holds t
+ * Errors: T < 0, n_shared < 1 or n_shared * T >= 2^31 -> INVALID_ARGUMENT.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_shared_indices(int32_t num_tokens, int32_t n_shared, int32_t* expert_offsets,
+                                int32_t* sorted_token, void* stream);
 
 /* Helpers. */
 const char* moe_status_string(moe_status_t status);

@@ -64,10 +64,11 @@ class FfnArgs(ctypes.Structure):
 class CombineArgs(ctypes.Structure):
     _fields_ = [("num_tokens", _i32), ("n_experts_per_tok", _i32), ("hidden_dim", _i32),
                 ("expert_out", _vp), ("out_dtype", _i32), ("row_of_slot", _vp),
-                ("expert_weights", _vp), ("token_mask", _vp), ("y", _vp)]
+                ("expert_weights", _vp), ("token_mask", _vp), ("y", _vp), ("n_shared", _i32),
+                ("shared_out", _vp), ("shared_weights", _vp)]
 
 
-ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_combine",
+ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_combine", "moe_shared_indices",
                 "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
                 "moe_status_string", "moe_last_error_message", "moe_abi_version")
 
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_last_error_message.restype = ctypes.c_char_p
     lib.moe_abi_version.argtypes = []
     lib.moe_abi_version.restype = _i32
+    lib.moe_shared_indices.argtypes = [_i32, _i32, _vp, _vp, _vp]
+    lib.moe_shared_indices.restype = _i32
     return lib
 
 
@@ -245,17 +248,33 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
     return out
 
 
-def combine(expert_out, row_of_slot, T: int, k: int, *, weights=None, token_mask=None, out=None):
-    """moe_combine.  Returns y bf16 [T, H]."""
+def combine(expert_out, row_of_slot, T: int, k: int, *, weights=None, token_mask=None, out=None,
+            shared_out=None, shared_weights=None, n_shared: int = 0):
+    """moe_combine.  Returns y bf16 [T, H].  shared_out [n_shared*T, H] (rows
+    of the shared experts, bucketed by moe_shared_indices) is added with
+    shared_weights [T, n_shared] (the sink weights), or weight 1 if None."""
     H = expert_out.shape[1]
     dev = expert_out.device
     y = out if out is not None else torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    _dt(shared_weights, torch.float32, "shared_weights")
+    if shared_out is not None and shared_out.dtype != expert_out.dtype:
+        raise ValueError("shared_out must have the dtype of expert_out")
     a = CombineArgs(num_tokens=T, n_experts_per_tok=k, hidden_dim=H, expert_out=_ptr(expert_out),
                     out_dtype=DTYPE_BF16 if expert_out.dtype == torch.bfloat16 else DTYPE_FP32,
                     row_of_slot=_ptr(row_of_slot), expert_weights=_ptr(weights),
-                    token_mask=_ptr(token_mask), y=_ptr(y))
+                    token_mask=_ptr(token_mask), y=_ptr(y), n_shared=n_shared,
+                    shared_out=_ptr(shared_out), shared_weights=_ptr(shared_weights))
     _check(lib().moe_combine(ctypes.byref(a), _stream(dev)))
     return y
+
+
+def shared_indices(T: int, n_shared: int, device):
+    """moe_shared_indices.  Returns (offsets int32 [n_shared+1], sorted_token
+    int32 [n_shared*T]): the buckets of the shared experts, every token in each."""
+    off = torch.empty(n_shared + 1, dtype=torch.int32, device=device)
+    st = torch.empty(max(n_shared * T, 1), dtype=torch.int32, device=device)
+    _check(lib().moe_shared_indices(T, n_shared, _ptr(off), _ptr(st), _stream(device)))
+    return off, st
 
 
 # ------------------------------------------------------------------ weights and the whole layer
@@ -320,12 +339,29 @@ class MoELayer:
         self.out_dtype = torch.bfloat16 if cfg.operand_dtype == "fp8" else torch.float32
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
+        # shared experts: their own weights and buckets (every token in each)
+        self.n_shared = getattr(cfg, "n_shared", 0)
+        if self.n_shared:
+            if cfg.router == "sigmoid_sink" and self.n_shared != cfg.s:
+                raise ValueError("the sink lanes gate the shared experts one to one: n_shared must equal s")
+            if cfg.operand_dtype == "fp8" and not gather:
+                raise ValueError("fp8 shared experts read the per-token codes: use gather=True")
+            self.w_shared = ExpertWeights.from_stacked(
+                inputs["w_gate_up_shared"], inputs["w_down_shared"], b_gate_up=inputs.get("b_gate_up_shared"),
+                b_down=inputs.get("b_down_shared"), w_gate_up_scale=inputs.get("w_gate_up_shared_scale"),
+                w_down_scale=inputs.get("w_down_shared_scale"), operand=cfg.operand_dtype, layout=layout)
+            Rs = self.n_shared * T
+            self.R_shared = Rs
+            self.shared_offsets, self.shared_token = shared_indices(T, self.n_shared, dev)
+            self.act_ws_shared = ffn_workspace(Rs, cfg.shared_dim, cfg.operand_dtype, dev)
+            self.O_shared = torch.empty((max(Rs, 1), cfg.H), dtype=self.out_dtype, device=dev)
 
-    def forward(self, x, token_mask=None, mark=None, ffn_events=None):
+    def forward(self, x, token_mask=None, mark=None, ffn_events=None, shared_events=None):
         """One layer pass.  mark(i), if given, is called on the host after
         each of the routing (i=1) and bucketing (i=2) calls and after the
         combine (i=3); ffn_events are hipEvent_t handles recorded inside the
-        grouped FFN call (before gate_up, between the GEMMs, after down)."""
+        grouped FFN call (before gate_up, between the GEMMs, after down), and
+        shared_events the same for the shared experts' FFN call."""
         c = self.cfg
         if c.router == "softmax":
             idx, w, sw, _ = route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate,
@@ -355,11 +391,23 @@ class MoELayer:
                         activation=c.activation, alpha=c.alpha, limit=c.limit,
                         gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
                         act_workspace=self.act_ws, out=self.O, timing_events=ffn_events)
-        y = combine(O, ind["row_of_slot"], c.T, c.k, weights=w, token_mask=token_mask, out=self.y)
+        O_sh = None
+        if self.n_shared:
+            xs = xg if fp8 else x
+            O_sh = grouped_ffn(self.shared_offsets, self.R_shared, self.w_shared,
+                               x_perm_scale=ind.get("x_perm_scale") if fp8 else None, x=xs,
+                               sorted_token=self.shared_token, activation=c.activation, alpha=c.alpha,
+                               limit=c.limit, gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
+                               act_workspace=self.act_ws_shared, out=self.O_shared,
+                               timing_events=shared_events)
+        y = combine(O, ind["row_of_slot"], c.T, c.k, weights=w, token_mask=token_mask, out=self.y,
+                    shared_out=O_sh, shared_weights=sw if c.router == "sigmoid_sink" else None,
+                    n_shared=self.n_shared)
         if mark:
             mark(3)
-        return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O}
+        return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O,
+                "O_shared": O_sh}
 
 
-__all__ = ["lib", "route", "build_indices", "grouped_ffn", "combine", "ExpertWeights", "MoELayer",
+__all__ = ["lib", "route", "build_indices", "grouped_ffn", "combine", "shared_indices", "ExpertWeights", "MoELayer",
            "MoEError", "load_library", "ENTRY_POINTS", "LIB_PATH"]

@@ -313,10 +313,29 @@ moe_status_t moe_combine(const moe_combine_args_t* a, void* stream) {
   REQUIRE(T == 0 || (a->expert_out && a->row_of_slot && a->y),
           "moe_combine: expert_out, row_of_slot and y are required");
   REQUIRE(aligned16(a->expert_out) && aligned16(a->y), "moe_combine: expert_out and y must be 16-byte aligned");
+  REQUIRE(a->n_shared >= 0 && a->n_shared <= 1024, "moe_combine: n_shared must be in [0, 1024] (got %d)",
+          a->n_shared);
+  REQUIRE(a->n_shared == 0 || T == 0 || a->shared_out != nullptr,
+          "moe_combine: shared_out is required when n_shared > 0");
+  REQUIRE(a->n_shared == 0 || aligned16(a->shared_out), "moe_combine: shared_out must be 16-byte aligned");
   return hip_status(moe::launch_combine(a->expert_out, a->out_dtype == MOE_DTYPE_BF16, a->row_of_slot,
                                         a->expert_weights, a->token_mask, T, k, H, (uint16_t*)a->y,
+                                        a->n_shared, a->shared_out, a->shared_weights,
                                         (hipStream_t)stream),
                     "moe_combine");
+}
+
+// ---------------------------------------------------------------- shared-expert buckets
+moe_status_t moe_shared_indices(int32_t T, int32_t n_shared, int32_t* expert_offsets,
+                                int32_t* sorted_token, void* stream) {
+  REQUIRE(T >= 0, "moe_shared_indices: num_tokens must be >= 0 (got %d)", T);
+  REQUIRE(n_shared >= 1 && n_shared <= 1024, "moe_shared_indices: n_shared must be in [1, 1024] (got %d)",
+          n_shared);
+  REQUIRE((int64_t)T * n_shared < ((int64_t)1 << 31), "moe_shared_indices: n_shared * num_tokens must be < 2^31");
+  REQUIRE(expert_offsets != nullptr && (T == 0 || sorted_token != nullptr),
+          "moe_shared_indices: expert_offsets and sorted_token are required");
+  return hip_status(moe::launch_shared_indices(T, n_shared, expert_offsets, sorted_token, (hipStream_t)stream),
+                    "moe_shared_indices");
 }
 
 }  // extern "C"

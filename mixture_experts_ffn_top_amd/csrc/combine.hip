@@ -1,7 +1,8 @@
-// Router-weighted combine: y[t] = sum_j w[t, j] * O[row_of_slot[t, j]],
-// fp32 sums in ascending j, bf16 out; one wave per token, 8 columns per lane
-// per step, 16-byte loads and stores.  A gather with a fixed order, so the
-// result is deterministic.
+// Router-weighted combine: y[t] = sum_j w[t, j] * O[row_of_slot[t, j]]
+// + sum_i ws[t, i] * O_sh[i*T + t] (the shared experts, if any), fp32 sums in
+// ascending j then i, bf16 out; one wave per token, 8 columns per lane per
+// step, 16-byte loads and stores.  A gather with a fixed order, so the result
+// is deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -12,7 +13,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
                                                       const int32_t* __restrict__ row_of_slot,
                                                       const float* __restrict__ w,
                                                       const uint8_t* __restrict__ mask, int T,
-                                                      int k, int H, uint16_t* __restrict__ y) {
+                                                      int k, int H, uint16_t* __restrict__ y,
+                                                      int n_shared, const void* __restrict__ Osh,
+                                                      const float* __restrict__ wsh) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -21,28 +24,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+    auto add_row = [&](const void* base, int64_t r, float wt) {
+      if (O_BF16) {
+        const u32x4_t v = *(const u32x4_t*)((const uint16_t*)base + r * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += wt * bf16_to_f32((uint16_t)(v[i] & 0xffffu));
+          acc[2 * i + 1] += wt * bf16_to_f32((uint16_t)(v[i] >> 16));
+        }
+      } else {
+        const f32x4_t* src = (const f32x4_t*)((const float*)base + r * H + c);
+        const f32x4_t a = src[0], b = src[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i] += wt * a[i];
+          acc[4 + i] += wt * b[i];
+        }
+      }
+    };
     if (valid) {
       for (int j = 0; j < k; ++j) {
         const int r = row_of_slot[(int64_t)t * k + j];
         if (r < 0) continue;
-        const float wt = w ? w[(int64_t)t * k + j] : 1.0f;
-        if (O_BF16) {
-          const u32x4_t v = *(const u32x4_t*)((const uint16_t*)O + (int64_t)r * H + c);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += wt * bf16_to_f32((uint16_t)(v[i] & 0xffffu));
-            acc[2 * i + 1] += wt * bf16_to_f32((uint16_t)(v[i] >> 16));
-          }
-        } else {
-          const f32x4_t* src = (const f32x4_t*)((const float*)O + (int64_t)r * H + c);
-          const f32x4_t a = src[0], b = src[1];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] += wt * a[i];
-            acc[4 + i] += wt * b[i];
-          }
-        }
+        add_row(O, r, w ? w[(int64_t)t * k + j] : 1.0f);
       }
+      for (int i = 0; i < n_shared; ++i)
+        add_row(Osh, (int64_t)i * T + t, wsh ? wsh[(int64_t)t * n_shared + i] : 1.0f);
     }
     u32x4_t out;
 #pragma unroll
@@ -52,13 +59,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
 }
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
-                          const uint8_t* mask, int T, int k, int H, uint16_t* y, hipStream_t st) {
+                          const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,
+                          const void* O_shared, const float* w_shared, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 3) / 4), block(256);
   if (o_bf16)
-    combine_kernel<true><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y);
+    combine_kernel<true><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y, n_shared, O_shared, w_shared);
   else
-    combine_kernel<false><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y);
+    combine_kernel<false><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y, n_shared, O_shared, w_shared);
   return hipGetLastError();
 }
 

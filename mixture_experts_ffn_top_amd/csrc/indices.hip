@@ -190,6 +190,25 @@ __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __rest
   }
 }
 
+// Buckets of the shared experts: every token in each, in token order.
+__global__ __launch_bounds__(256) void shared_indices_kernel(int T, int n_shared, int32_t* __restrict__ offsets,
+                                                             int32_t* __restrict__ sorted_token) {
+  const int64_t n = (int64_t)T * n_shared;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < n; p += (int64_t)gridDim.x * 256)
+    sorted_token[p] = (int32_t)(p % T);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= n_shared; i += 256) offsets[i] = i * T;
+}
+
+hipError_t launch_shared_indices(int T, int n_shared, int32_t* offsets, int32_t* sorted_token,
+                                 hipStream_t st) {
+  int64_t blocks = ((int64_t)T * n_shared + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  shared_indices_kernel<<<(int)blocks, 256, 0, st>>>(T, n_shared, offsets, sorted_token);
+  return hipGetLastError();
+}
+
 hipError_t launch_build_indices(const int32_t* idx, const float* w, const uint8_t* mask, int T,
                                 int k, int start, int L, int32_t* offsets, int32_t* sorted_token,
                                 int32_t* row_of_slot, float* sorted_weight, int32_t* ws,

@@ -80,6 +80,9 @@ struct FfnFp8Params {
 hipError_t launch_ffn_fp8(const FfnFp8Params& p, hipStream_t st);
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
-                          const uint8_t* mask, int T, int k, int H, uint16_t* y, hipStream_t st);
+                          const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,
+                          const void* O_shared, const float* w_shared, hipStream_t st);
+hipError_t launch_shared_indices(int T, int n_shared, int32_t* offsets, int32_t* sorted_token,
+                                 hipStream_t st);
 
 }  // namespace moe

@@ -25,13 +25,44 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_struct_layouts_match_header_sizes():
     # pointer-size fields and natural alignment: these sizes follow from the header
     assert ctypes.sizeof(m.RouteArgs) == 6 * 4 + 3 * 8 + 8 + 3 * 8 + 4 + 4 + 3 * 8
-    assert ctypes.sizeof(m.CombineArgs) == 3 * 4 + 4 + 8 + 4 + 4 + 8 * 4
+    assert ctypes.sizeof(m.CombineArgs) == 3 * 4 + 4 + 8 + 4 + 4 + 8 * 4 + 4 + 4 + 2 * 8
+
+
+STRUCTS = {"RouteArgs": "moe_route_args_t", "IndexArgs": "moe_index_args_t",
+           "FfnArgs": "moe_ffn_args_t", "CombineArgs": "moe_combine_args_t"}
+
+
+def test_struct_layouts_match_the_c_compiler(tmp_path):
+    """Every binding struct has the size and field offsets that a C compiler
+    gives the header's struct (gcc on this host, same ABI as the library)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", f'#include "{HEADER}"', "int main(void) {"]
+    for py, c in STRUCTS.items():
+        lines.append(f'printf("{py} size %zu\\n", sizeof({c}));')
+        for name, _ in getattr(m, py)._fields_:
+            lines.append(f'printf("{py} {name} %zu\\n", offsetof({c}, {name}));')
+    lines += ["return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c11", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {(a, b): int(v) for a, b, v in (ln.split() for ln in out if ln)}
+    for py in STRUCTS:
+        cls = getattr(m, py)
+        assert got[(py, "size")] == ctypes.sizeof(cls), py
+        for name, _ in cls._fields_:
+            assert got[(py, name)] == getattr(cls, name).offset, f"{py}.{name}"
 
 
 def _err(fn, args):
@@ -143,6 +174,31 @@ def test_combine_validation(kw, frag):
     base.update(kw)
     st, msg = _err(m.lib().moe_combine, m.CombineArgs(**base))
     assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(n_shared=2), "shared_out"),
+    (dict(n_shared=-1), "n_shared"),
+    (dict(n_shared=1, shared_out=72), "aligned"),
+])
+def test_combine_shared_validation(kw, frag):
+    base = dict(num_tokens=8, n_experts_per_tok=2, hidden_dim=256, expert_out=16, out_dtype=2, row_of_slot=32,
+                y=48)
+    base.update(kw)
+    st, msg = _err(m.lib().moe_combine, m.CombineArgs(**base))
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+@pytest.mark.parametrize("T,n,off,st_,frag", [
+    (-1, 2, 16, 32, "num_tokens"),
+    (8, 0, 16, 32, "n_shared"),
+    (8, 2, None, 32, "required"),
+    (1 << 30, 4, 16, 32, "2^31"),
+])
+def test_shared_indices_validation(T, n, off, st_, frag):
+    lib = m.lib()
+    st = lib.moe_shared_indices(T, n, off, st_, None)
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in lib.moe_last_error_message().decode()
 
 
 def test_workspace_queries_and_status_strings():

@@ -185,7 +185,8 @@ def _check_layer(cfg, inp, res, tokens, tol, token_mask=None):
     hin = synth.to_host(inp)
     idx = host(res["indices"])
     w = host(res["weights"]).astype(np.float64)
-    y_ref = O.layer(hin, cfg, indices=idx, weights=w, tokens=tokens, token_mask=token_mask)
+    sw = host(res["sink_weights"]).astype(np.float64) if res.get("sink_weights") is not None else None
+    y_ref = O.layer(hin, cfg, indices=idx, weights=w, tokens=tokens, token_mask=token_mask, sink_weights=sw)
     y = host(res["y"])[tokens]
     err, rms = rel_rms_err(y, y_ref)
     say(f"  y max err / rms = {err:.3e} (bf16 floor {bf16_floor(y_ref):.3e}, rms {rms:.3e})")
@@ -251,7 +252,7 @@ def test_activation_variants_clamp_stress(moe, act, alpha, limit, fmt, bias):
 
 
 def test_expert_scales_and_local_slice(moe):
-    cfg = synth.scaled(synth.get_config(3), T=700, E=24, k=4, s=4, H=512, D=256)
+    cfg = synth.scaled(synth.get_config(3), T=700, E=24, k=4, s=4, H=512, D=256, n_shared=0)
     inp = _gen(cfg)
     hin = synth.to_host(inp)
     idx, w, _, _ = moe.route(router="sigmoid", k=cfg.k, E=cfg.E, s=cfg.s, logits=inp["logits"],
@@ -381,6 +382,36 @@ def test_down_split_k_tail_round(moe, D):
         err, _ = rel_rms_err(Oh[rows], ref)
         say(f"  expert {e}: O err/rms {err:.3e}")
         assert err <= 1e-2, f"expert {e}: O err/rms {err:.3e}"
+
+
+def test_shared_indices(moe):
+    for T, n in [(1, 1), (77, 2), (8192, 2), (300, 5)]:
+        off, st = moe.shared_indices(T, n, torch.device(DEV))
+        torch.cuda.synchronize()
+        assert np.array_equal(host(off), np.arange(n + 1) * T)
+        assert np.array_equal(host(st)[: n * T], np.tile(np.arange(T), n))
+
+
+@pytest.mark.parametrize("cid,changes,nsample", [
+    (1, {"T": 256, "n_shared": 1, "shared_dim": 256}, 256),                   # always-on, weight 1
+    (1, {"T": 200, "n_shared": 3, "shared_dim": 136}, 200),                   # several, ragged dims
+    (4, {"T": 300, "H": 512, "D": 384, "E": 6, "k": 2, "n_shared": 2, "shared_dim": 256}, 300),  # bias, interleaved
+    (3, {"T": 700, "E": 32, "D": 256, "shared_dim": 512}, 700),               # sink-gated, two lanes
+])
+def test_layer_with_shared_experts(moe, cid, changes, nsample):
+    cfg = synth.scaled(synth.get_config(cid), **changes)
+    inp = _gen(cfg)
+    say(f"[shared] cfg={cid} {changes}")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample), BF16_TOL)
+    # masked tokens give zero rows, shared experts included
+    mask = torch.ones(cfg.T, dtype=torch.uint8, device=DEV)
+    mask[::7] = 0
+    _, res_m = _run_layer(moe, cfg, inp, token_mask=mask)
+    ym = host(res_m["y"])
+    assert np.all(ym[host(mask) == 0] == 0)
+    _check_layer(cfg, inp, res_m, sample_tokens(cfg.T, nsample), BF16_TOL, token_mask=host(mask))
 
 
 def test_abi_errors_on_gpu_path(moe):
