@@ -104,7 +104,8 @@ enum { MOE_WEIGHT_IN_OUT = 0, MOE_WEIGHT_OUT_IN = 1 };
  * Arguments (device unless marked host):
  *   router_kind, num_tokens T >= 0, n_routed_experts E in [1, 1024],
  *   n_experts_per_tok k in [1, min(E, 64)], n_shared_experts s >= 0   host
- *   hidden_dim H                       host, softmax x-form only
+ *   hidden_dim H                       host, softmax x-form only: a multiple
+ *                                      of 8 in [8, 4194304]
  *   x          bf16 [T, H]             softmax x-form (logits == NULL), E <= 128
  *   w_gate     bf16 [E, H]             gate linear layer (out, in)
  *   logits     fp32 [T, logits_ld], logits_ld >= E + s; routed experts then

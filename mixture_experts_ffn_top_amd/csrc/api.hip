@@ -81,8 +81,8 @@ moe_status_t moe_route(const moe_route_args_t* a, void* stream) {
       REQUIRE(a->x != nullptr && a->w_gate != nullptr,
               "moe_route: softmax router needs logits, or x and w_gate");
       REQUIRE(E <= 128, "moe_route: the fused gate GEMM supports n_routed_experts <= 128 (got %d)", E);
-      REQUIRE(a->hidden_dim >= 8 && a->hidden_dim % 8 == 0,
-              "moe_route: hidden_dim must be a positive multiple of 8 (got %d)", a->hidden_dim);
+      REQUIRE(a->hidden_dim >= 8 && a->hidden_dim % 8 == 0 && a->hidden_dim <= (1 << 22),
+              "moe_route: hidden_dim must be a multiple of 8 in [8, 4194304] (got %d)", a->hidden_dim);
       REQUIRE(aligned16(a->x) && aligned16(a->w_gate), "moe_route: x and w_gate must be 16-byte aligned");
       return hip_status(moe::launch_router_softmax_x(
                             (const uint16_t*)a->x, (const uint16_t*)a->w_gate, T, a->hidden_dim, E, k,

@@ -65,6 +65,21 @@ __device__ __forceinline__ uint8_t f32_to_e4m3(float f) {
   return (uint8_t)(sign | (ef << 3) | keep);
 }
 
+// Four floats -> four e4m3fn codes (byte i from v[i]), the same codes as
+// f32_to_e4m3.  v_cvt_pk_fp8_f32 rounds to nearest even into OCP e4m3fn;
+// for inputs first clamped to +-448 its codes equal f32_to_e4m3's for every
+// non-NaN float (verified over all 2^32 bit patterns on gfx950).  A group
+// holding a NaN takes the software encoder, which keeps NaN -> 0x7f | sign.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  if (__builtin_expect((a != a) | (b != b) | (c != c) | (d != d), 0))
+    return (uint32_t)f32_to_e4m3(a) | ((uint32_t)f32_to_e4m3(b) << 8) |
+           ((uint32_t)f32_to_e4m3(c) << 16) | ((uint32_t)f32_to_e4m3(d) << 24);
+  auto cl = [](float v) { return fminf(fmaxf(v, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return (uint32_t)w;
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t ef = (c >> 3) & 0xfu;
@@ -77,25 +92,61 @@ __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
 }
 
 // ---------------------------------------------------------------- wave64 reductions
+// All-lanes reductions over a full wave (all 64 lanes active).  Inside each
+// row of 16 lanes they run on DPP moves (quad_perm xor 1, xor 2, then
+// row_half_mirror and row_mirror: after each step every lane holds the
+// reduction of its quad, half-row, row); the four row results are then read
+// with v_readlane and combined in a fixed order, so every lane gets the same
+// value and no LDS round trip is taken.
+static constexpr int DPP_QP_XOR1 = 0xB1;        // quad_perm [1,0,3,2]
+static constexpr int DPP_QP_XOR2 = 0x4E;        // quad_perm [2,3,0,1]
+static constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+static constexpr int DPP_ROW_MIRROR = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v, uint32_t identity) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ uint32_t row_lane(uint32_t v, int r) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 16 * r);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, MOE_WAVE));
-  return v;
+  const uint32_t ninf = 0xff800000u;
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_XOR1>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_XOR2>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v), ninf)));
+  const uint32_t u = __float_as_uint(v);
+  return fmaxf(fmaxf(__uint_as_float(row_lane(u, 0)), __uint_as_float(row_lane(u, 1))),
+               fmaxf(__uint_as_float(row_lane(u, 2)), __uint_as_float(row_lane(u, 3))));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MOE_WAVE);
-  return v;
+  v += __uint_as_float(dpp_u32<DPP_QP_XOR1>(__float_as_uint(v), 0u));
+  v += __uint_as_float(dpp_u32<DPP_QP_XOR2>(__float_as_uint(v), 0u));
+  v += __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v), 0u));
+  v += __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v), 0u));
+  const uint32_t u = __float_as_uint(v);
+  return (__uint_as_float(row_lane(u, 0)) + __uint_as_float(row_lane(u, 1))) +
+         (__uint_as_float(row_lane(u, 2)) + __uint_as_float(row_lane(u, 3)));
+}
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint64_t w = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32), 0u) << 32) | dpp_u32<CTRL>((uint32_t)v, 0u);
+  return w > v ? w : v;
 }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<DPP_QP_XOR1>(v);
+  v = dpp_max_u64<DPP_QP_XOR2>(v);
+  v = dpp_max_u64<DPP_ROW_HALF_MIRROR>(v);
+  v = dpp_max_u64<DPP_ROW_MIRROR>(v);
+  uint64_t r = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, o, MOE_WAVE);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), o, MOE_WAVE);
-    uint64_t w = ((uint64_t)hi << 32) | lo;
-    v = w > v ? w : v;
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t x = ((uint64_t)row_lane((uint32_t)(v >> 32), q) << 32) | row_lane((uint32_t)v, q);
+    r = x > r ? x : r;
   }
-  return v;
+  return r;
 }
 
 // Order-preserving map of a float key to uint32 (-0 is taken as +0), packed

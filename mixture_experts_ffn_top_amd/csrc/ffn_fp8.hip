@@ -352,9 +352,8 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fk;
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) w |= (uint32_t)f32_to_e4m3(__fdiv_rn(a[mi][4 * q + c], s)) << (8 * c);
+        const uint32_t w = e4m3x4(__fdiv_rn(a[mi][4 * q + 0], s), __fdiv_rn(a[mi][4 * q + 1], s),
+                                  __fdiv_rn(a[mi][4 * q + 2], s), __fdiv_rn(a[mi][4 * q + 3], s));
         *(uint32_t*)(out + (int64_t)row * p.N + oc) = w;
       }
       if (wn == 0 && fk == 0) p.out_scale[(int64_t)row * (p.N / 128) + nb] = s;

@@ -5,9 +5,10 @@
 // e4m3 quantisation of the fp8 layer.
 //
 //   csr_hist    per block of IDX_SLOTS flat slots: LDS histogram over local
-//               experts -> counts[block][e]
-//   csr_scan    one workgroup: exclusive scan over blocks per expert, then over
-//               experts -> expert_offsets and per-(expert, block) bases
+//               experts -> counts[e][block] (expert-major)
+//   csr_scan    one workgroup: one flat exclusive scan of counts in that
+//               order, which is at once the per-(expert, block) base and, at
+//               block 0, the expert offset
 //   csr_scatter per block: stable rank of each slot among same-expert slots
 //               (wave ballots per distinct expert, LDS running counts) ->
 //               sorted_token, row_of_slot, sorted_weight
@@ -44,38 +45,82 @@ __global__ __launch_bounds__(256) void csr_hist_kernel(const int32_t* __restrict
     if (e >= 0) atomicAdd(&s_h[e], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < L; e += 256) counts[(int64_t)blockIdx.x * L + e] = s_h[e];
+  for (int e = threadIdx.x; e < L; e += 256) counts[(int64_t)e * nblk + blockIdx.x] = s_h[e];
 }
 
-// One workgroup of 1024 threads; L <= 1024.
+// One workgroup of 1024 threads.  Exclusive scan, in place, of the
+// n = L * nblk counts in expert-major order: entry (e, b) becomes the first
+// CSR row of expert e's slots in block b, and entry (e, 0) is expert e's
+// offset.  Tiles of 16 words per thread (64 KB) are read coalesced, the next
+// tile's loads in flight while the current one is scanned.
+static constexpr int SCAN_PER = 16;
+static constexpr int SCAN_TILE = 1024 * SCAN_PER;
+
+__device__ __forceinline__ void scan_load(const int32_t* c, int64_t g0, int64_t n, int32_t (&v)[SCAN_PER]) {
+  if (g0 + SCAN_PER <= n) {
+#pragma unroll
+    for (int q = 0; q < SCAN_PER / 4; ++q) {
+      const int4 x = *(const int4*)(c + g0 + 4 * q);
+      v[4 * q] = x.x; v[4 * q + 1] = x.y; v[4 * q + 2] = x.z; v[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) v[i] = (g0 + i < n) ? c[g0 + i] : 0;
+  }
+}
+
 __global__ __launch_bounds__(1024) void csr_scan_kernel(int32_t* __restrict__ counts, int L,
                                                         int nblk, int32_t* __restrict__ offsets) {
-  __shared__ int32_t s[1024];
-  const int t = threadIdx.x;
-  int32_t tot = 0;
-  if (t < L) {
-    // counts are block-major ([block][expert]): consecutive threads read
-    // consecutive words at every step
-    for (int b = 0; b < nblk; ++b) {
-      int32_t v = counts[(int64_t)b * L + t];
-      counts[(int64_t)b * L + t] = tot;
-      tot += v;
+  __shared__ int32_t s_wave[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int64_t n = (int64_t)L * nblk;
+  int32_t carry = 0;
+  int32_t v[SCAN_PER], nv[SCAN_PER];
+  if (n > 0) scan_load(counts, (int64_t)t * SCAN_PER, n, v);
+  for (int64_t t0 = 0; t0 < n; t0 += SCAN_TILE) {
+    const int64_t g0 = t0 + (int64_t)t * SCAN_PER;
+    if (t0 + SCAN_TILE < n) scan_load(counts, g0 + SCAN_TILE, n, nv);
+    int32_t run = 0;
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) {
+      const int32_t x = v[i];
+      v[i] = run;
+      run += x;
     }
-  }
-  s[t] = tot;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int32_t v = (t >= o) ? s[t - o] : 0;
+    int32_t inc = run;                       // inclusive scan of the thread sums in the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t y = __shfl_up(inc, o, MOE_WAVE);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) s_wave[wave] = inc;
     __syncthreads();
-    s[t] += v;
-    __syncthreads();
+    int32_t wpre = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int32_t x = s_wave[w];
+      wpre += (w < wave) ? x : 0;
+      tot += x;
+    }
+    const int32_t base = carry + wpre + (inc - run);
+    if (g0 + SCAN_PER <= n) {
+#pragma unroll
+      for (int q = 0; q < SCAN_PER / 4; ++q)
+        *(int4*)(counts + g0 + 4 * q) =
+            make_int4(v[4 * q] + base, v[4 * q + 1] + base, v[4 * q + 2] + base, v[4 * q + 3] + base);
+    } else {
+#pragma unroll
+      for (int i = 0; i < SCAN_PER; ++i)
+        if (g0 + i < n) counts[g0 + i] = v[i] + base;
+    }
+    carry += tot;
+    __syncthreads();                         // s_wave is rewritten by the next tile
+#pragma unroll
+    for (int i = 0; i < SCAN_PER; ++i) v[i] = nv[i];
   }
-  const int32_t excl = s[t] - tot;
-  if (t < L) {
-    offsets[t] = excl;
-    for (int b = 0; b < nblk; ++b) counts[(int64_t)b * L + t] += excl;
-  }
-  if (t == L - 1) offsets[L] = s[t];
+  // the barrier above (a workgroup-scope fence) makes the scanned words visible
+  for (int e = t; e < L; e += 1024) offsets[e] = nblk > 0 ? counts[(int64_t)e * nblk] : 0;
+  if (t == 0) offsets[L] = carry;
 }
 
 __global__ __launch_bounds__(256) void csr_scatter_kernel(
@@ -88,7 +133,7 @@ __global__ __launch_bounds__(256) void csr_scatter_kernel(
   int32_t* wcnt = sm + L;      // [4][L] this round's count per wave and expert
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < L; e += 256) {
-    running[e] = base[(int64_t)blockIdx.x * L + e];
+    running[e] = base[(int64_t)e * nblk + blockIdx.x];
     wcnt[e] = wcnt[L + e] = wcnt[2 * L + e] = wcnt[3 * L + e] = 0;
   }
   __syncthreads();
@@ -140,11 +185,14 @@ __global__ __launch_bounds__(256) void permute_bf16_kernel(const uint16_t* __res
   }
 }
 
-// Per-row, per-128-column e4m3 quantisation fused into the gather: 16 lanes
-// own one 128-column group (8 elements each); a wave does 4 groups at a time.
-// With sorted_token == nullptr the rows are not permuted: row p of the
-// output is token p (n_fixed rows), the per-token form the fp8 GEMM gathers
-// from.
+// Per-row, per-128-column e4m3 quantisation fused into the gather: one wave
+// per row, 16 lanes own one 128-column group (8 elements each).  A wave
+// issues the loads of PQ_U passes (4 groups each, 1 KB per load) before any
+// arithmetic, so every lane has PQ_U 16-byte reads in flight.  With
+// sorted_token == nullptr the rows are not permuted: row p of the output is
+// token p (n_fixed rows), the per-token form the fp8 GEMM gathers from.
+static constexpr int PQ_U = 4;
+
 __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __restrict__ x,
                                                           const int32_t* __restrict__ sorted_token,
                                                           const int32_t* __restrict__ n_rows,
@@ -157,34 +205,37 @@ __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __rest
   const int sub = lane & 15, gq = lane >> 4;
   for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n; row += gridDim.x * 4) {
     const uint16_t* src = x + (int64_t)(sorted_token ? sorted_token[row] : row) * H;
-    for (int g0 = 0; g0 < groups; g0 += 4) {
-      const int g = g0 + gq;
-      const bool ok = g < groups;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4_t*)(src + g * 128 + sub * 8);
-      float f[8];
+    uint8_t* dst = xq + (int64_t)row * H;
+    for (int g0 = 0; g0 < groups; g0 += 4 * PQ_U) {
+      u32x4_t v[PQ_U];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[2 * i] = bf16_to_f32((uint16_t)(v[i] & 0xffffu));
-        f[2 * i + 1] = bf16_to_f32((uint16_t)(v[i] >> 16));
+      for (int u = 0; u < PQ_U; ++u) {
+        const int g = g0 + 4 * u + gq;
+        v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (g < groups) v[u] = *(const u32x4_t*)(src + g * 128 + sub * 8);
       }
-      float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      for (int u = 0; u < PQ_U; ++u) {
+        const int g = g0 + 4 * u + gq;
+        float f[8];
 #pragma unroll
-      for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
-      const float s = (amax > 0.0f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
-      uint32_t lo = 0, hi = 0;
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_to_f32((uint16_t)(v[u][i] & 0xffffu));
+          f[2 * i + 1] = bf16_to_f32((uint16_t)(v[u][i] >> 16));
+        }
+        float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lo |= (uint32_t)f32_to_e4m3(__fdiv_rn(f[i], s)) << (8 * i);
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) hi |= (uint32_t)f32_to_e4m3(__fdiv_rn(f[4 + i], s)) << (8 * i);
-      if (ok) {
+        for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
+        const float s = (amax > 0.0f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
         uint2 q;
-        q.x = lo;
-        q.y = hi;
-        *(uint2*)(xq + (int64_t)row * H + g * 128 + sub * 8) = q;
-        if (sub == 0) xs[(int64_t)row * groups + g] = s;
+        q.x = e4m3x4(__fdiv_rn(f[0], s), __fdiv_rn(f[1], s), __fdiv_rn(f[2], s), __fdiv_rn(f[3], s));
+        q.y = e4m3x4(__fdiv_rn(f[4], s), __fdiv_rn(f[5], s), __fdiv_rn(f[6], s), __fdiv_rn(f[7], s));
+        if (g < groups) {
+          *(uint2*)(dst + g * 128 + sub * 8) = q;
+          if (sub == 0) xs[(int64_t)row * groups + g] = s;
+        }
       }
     }
   }

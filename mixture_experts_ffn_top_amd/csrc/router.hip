@@ -86,49 +86,119 @@ __global__ __launch_bounds__(256) void router_softmax_logits_kernel(
 }
 
 // ------------------------------------------------------------ softmax, gate GEMM fused
-// A workgroup owns 16 tokens; its 4 waves split the hidden dimension into
-// quarters.  logits^T[e][t] = sum_h W[e][h] x[t][h] runs on
+// A workgroup owns 16 tokens.  logits^T[e][t] = sum_h W[e][h] x[t][h] runs on
 // v_mfma_f32_16x16x32_bf16 with W as the A operand (16 experts per tile) and
-// x as the B operand (16 tokens); inside a wave, lane group g = lane/16 walks
-// its own contiguous part of the wave's quarter, 8 elements per step, so
-// every lane issues 16-byte loads.  The four partial sums meet in LDS, then
-// each wave runs the top-k of 4 tokens.
+// x as the B operand (16 tokens).  The hidden dimension is streamed in chunks
+// of RX_CC columns: the 16 token rows and the padded expert rows of a chunk
+// go straight from HBM/L2 into LDS with buffer loads (no VGPRs, one 1 KB
+// coalesced piece per instruction), RX_NS chunks deep, so that many loads
+// are in flight per CU; the kernel is bound by reading x once.  Inside a
+// chunk wave w takes the 32-column k steps w, w+4, ...; the four partial
+// sums meet in LDS, then each wave runs the top-k of 4 tokens.
+//
+// LDS row of a chunk: 32 pieces of 16 bytes.  Piece p of row r sits at slot
+// p ^ (r & 15): the 16 lanes of a fragment read (16 rows, one piece) then hit
+// 16 different 16-byte bank groups.
+static constexpr int RX_CC = 256;                 // columns per chunk
+static constexpr int RX_ROWB = RX_CC * 2;         // bytes of one row of a chunk
+static constexpr int RX_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
+
+template <int ETILES>
+struct RxShape {
+  static constexpr int EP = ETILES * 16;
+  static constexpr int STAGE = (16 + EP) * RX_ROWB;                  // bytes per chunk
+  static constexpr int NS = ETILES == 1 ? 8 : ETILES == 2 ? 5 : ETILES == 4 ? 3 : 2;
+  static constexpr int LPW = (16 + EP) * RX_ROWB / 1024 / 4;         // 1 KB loads per wave per chunk
+  static constexpr int PART = 4 * 16 * (EP + 1) * 4;                 // partial-sum exchange
+  static constexpr int LDS = NS * STAGE > PART ? NS * STAGE : PART;
+};
+
+// This wave's LPW loads of chunk c into the stage at `st`: 1 KB block
+// g = wave * LPW + l, x rows for g < 8, expert rows after.
+template <int LPW>
+__device__ __forceinline__ void rx_issue(char* st, int c, int wave, const uint32_t (&voff)[LPW],
+                                         __amdgpu_buffer_rsrc_t x_rsrc, __amdgpu_buffer_rsrc_t w_rsrc) {
+#pragma unroll
+  for (int l = 0; l < LPW; ++l) {
+    const int g = wave * LPW + l;
+    if (g < 8)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * RX_ROWB, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * RX_ROWB, 0, 0);
+  }
+}
+
 template <int ETILES, int J>
 __global__ __launch_bounds__(256) void router_softmax_x_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int H, int E, int k,
     float scale, const float* __restrict__ global_scale, int renorm, float* __restrict__ logits_out,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  constexpr int EP = ETILES * 16;
-  __shared__ float s_part[4][16][EP + 1];
+  constexpr int EP = RxShape<ETILES>::EP, NS = RxShape<ETILES>::NS, LPW = RxShape<ETILES>::LPW;
+  constexpr int STAGE = RxShape<ETILES>::STAGE;
+  __shared__ __attribute__((aligned(1024))) char smem[RxShape<ETILES>::LDS];
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
   const int col = lane & 15, grp = lane >> 4;
-  const int chunks = H / 8;                          // 8-element chunks of a row
-  const int per_wave = (chunks + 3) / 4;
-  const int c_beg = wave * per_wave;
-  const int c_end = min(chunks, c_beg + per_wave);
-  const int per_grp = (per_wave + 3) / 4;
-  const int tok = t0 + col;
-  const bool tok_ok = tok < T;
+  const int nrows = min(16, T - t0);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(x + (int64_t)t0 * H), (short)0, nrows * H * 2, RX_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t w_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, E * H * 2, RX_BUF_DWORD3);
+  // Load l of this wave moves 1 KB block g = wave * LPW + l of a chunk: two
+  // rows (x rows for g < 8, then expert rows), lane -> (row, slot).  Rows
+  // past the token or expert count read zeros (buffer bounds).
+  uint32_t voff[LPW];
+#pragma unroll
+  for (int l = 0; l < LPW; ++l) {
+    const int g = wave * LPW + l;
+    const int row = 2 * g + (lane >> 5);           // stage row: 0..15 x, then experts
+    const int piece = (lane & 31) ^ (row & 15);
+    const int r = g < 8 ? row : row - 16;
+    voff[l] = (uint32_t)r * (uint32_t)H * 2u + (uint32_t)piece * 16u;
+  }
+  const int nchunk = (H + RX_CC - 1) / RX_CC;
+
+#pragma unroll
+  for (int c = 0; c < NS - 1; ++c)
+    if (c < nchunk) rx_issue<LPW>(smem + (c % NS) * STAGE, c, wave, voff, x_rsrc, w_rsrc);
   f32x4_t acc[ETILES];
 #pragma unroll
   for (int i = 0; i < ETILES; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < per_grp; ++s) {
-    const int c = c_beg + grp * per_grp + s;
-    const bool c_ok = c < c_end;
-    u32x4_t bv = {0u, 0u, 0u, 0u};
-    if (tok_ok && c_ok) bv = *(const u32x4_t*)(x + (int64_t)tok * H + c * 8);
-    const bf16x8_t b = __builtin_bit_cast(bf16x8_t, bv);
+  for (int c = 0; c < nchunk; ++c) {
+    // chunk c landed (for this wave) once at most the loads of the chunks
+    // issued after it are outstanding; the barrier publishes every wave's
+    if (c + NS - 2 < nchunk) __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * LPW));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the buffer of chunk c-1 is free: every wave has passed the barrier
+    if (c + NS - 1 < nchunk)
+      rx_issue<LPW>(smem + ((c + NS - 1) % NS) * STAGE, c + NS - 1, wave, voff, x_rsrc, w_rsrc);
+    const char* st = smem + (c % NS) * STAGE;
+    const int cols_left = H - c * RX_CC;
 #pragma unroll
-    for (int et = 0; et < ETILES; ++et) {
-      const int e = et * 16 + col;
-      u32x4_t av = {0u, 0u, 0u, 0u};
-      if (e < E && c_ok) av = *(const u32x4_t*)(wg + (int64_t)e * H + c * 8);
-      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, av);
-      acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[et], 0, 0, 0);
+    for (int jj = 0; jj < RX_CC / 128; ++jj) {
+      const int p = 4 * (wave + 4 * jj) + grp;     // 32-column k step wave + 4*jj                    // piece of this lane's 8 columns
+      const int slot = (p ^ col) * 16;
+      u32x4_t bv = *(const u32x4_t*)(st + col * RX_ROWB + slot);
+      u32x4_t av[ETILES];
+#pragma unroll
+      for (int et = 0; et < ETILES; ++et)
+        av[et] = *(const u32x4_t*)(st + (16 + et * 16 + col) * RX_ROWB + slot);
+      if (p * 8 >= cols_left) {                     // past the end of the rows (last chunk)
+        bv = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int et = 0; et < ETILES; ++et) av[et] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int et = 0; et < ETILES; ++et)
+        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[et]),
+                                                          __builtin_bit_cast(bf16x8_t, bv), acc[et], 0, 0, 0);
     }
   }
+  // the exchange reuses the stage buffers once every wave is done with them
+  __syncthreads();
+  float (*s_part)[16][EP + 1] = (float (*)[16][EP + 1])smem;
   // acc[et][i] = partial logit[token t0 + col][expert et*16 + 4*grp + i]
 #pragma unroll
   for (int et = 0; et < ETILES; ++et)

@@ -86,6 +86,7 @@ def _route(**kw):
     (dict(n_shared_experts=2), "sink"),
     (dict(expert_bias=80), "expert_bias"),
     (dict(hidden_dim=60), "hidden_dim"),
+    (dict(hidden_dim=(1 << 22) + 8), "hidden_dim"),
     (dict(x=17), "aligned"),
     (dict(n_routed_experts=200, n_experts_per_tok=2), "<= 128"),
     (dict(x=None, w_gate=None, logits=96, logits_ld=4), "logits_ld"),

@@ -35,11 +35,17 @@ def _gen(cfg):
 
 # ---------------------------------------------------------------- routers
 
-@pytest.mark.parametrize("cid,T", [(1, 64), (2, 4096), (4, 4096), (1, 1), (4, 77)])
-def test_softmax_router_x_form(moe, cid, T):
-    cfg = synth.scaled(synth.get_config(cid), T=T)
+@pytest.mark.parametrize("cid,T,extra", [
+    (1, 64, {}), (2, 4096, {}), (4, 4096, {}), (1, 1, {}), (4, 77, {}),
+    # 33..64 and 65..128 experts (4 and 8 MFMA expert tiles), hidden sizes
+    # below one 256-column chunk and with a ragged last chunk
+    (1, 45, dict(E=64, k=6, H=1000)), (1, 33, dict(E=100, k=4, H=264)),
+    (1, 16, dict(E=128, k=8, H=8)), (1, 300, dict(E=40, k=3, H=776)),
+])
+def test_softmax_router_x_form(moe, cid, T, extra):
+    cfg = synth.scaled(synth.get_config(cid), T=T, **extra)
     inp = _gen(cfg)
-    say(f"[route softmax x] cfg={cid} T={T}")
+    say(f"[route softmax x] cfg={cid} T={T} {extra}")
     idx, w, _, lo = moe.route(router="softmax", k=cfg.k, E=cfg.E, x=inp["x"], w_gate=inp["w_gate"],
                               return_logits=True)
     torch.cuda.synchronize()
