@@ -135,6 +135,13 @@ __device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
   const uint64_t w = ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32), 0u) << 32) | dpp_u32<CTRL>((uint32_t)v, 0u);
   return w > v ? w : v;
 }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<DPP_QP_XOR1>(v, 0u));
+  v = max(v, dpp_u32<DPP_QP_XOR2>(v, 0u));
+  v = max(v, dpp_u32<DPP_ROW_HALF_MIRROR>(v, 0u));
+  v = max(v, dpp_u32<DPP_ROW_MIRROR>(v, 0u));
+  return max(max(row_lane(v, 0), row_lane(v, 1)), max(row_lane(v, 2), row_lane(v, 3)));
+}
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   v = dpp_max_u64<DPP_QP_XOR1>(v);
   v = dpp_max_u64<DPP_QP_XOR2>(v);
@@ -159,6 +166,12 @@ __device__ __forceinline__ uint64_t pack_key(float key, int idx) {
   return ((uint64_t)u << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
 }
 __device__ __forceinline__ int unpack_idx(uint64_t p) { return (int)(0xffffffffu - (uint32_t)p); }
+
+// The key half of pack_key alone (never 0 for a float), and its inverse.
+__device__ __forceinline__ uint32_t order_key(float key) { return (uint32_t)(pack_key(key, 0) >> 32); }
+__device__ __forceinline__ float order_key_inv(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
 
 // The router's float32 sigmoid: exp(-z) rounded once to float32, then a
 // correctly rounded add and divide.

@@ -12,31 +12,39 @@ namespace moe {
 
 // Selection over one token whose keys live in `key[j]` for expert
 // lane + 64*j.  Lane i < k returns the i-th selected expert and its key.
+// Each round takes the wave maximum of the order-preserving 32-bit key
+// images, then the lowest expert index holding it (first j whose ballot is
+// non-empty, lowest lane in it), and removes that entry; 0 marks removed
+// entries and experts past E (no float maps to 0).
 template <int J>
 __device__ __forceinline__ void wave_topk(const float (&key)[J], int E, int k, int lane,
                                           int& sel_idx, float& sel_key) {
-  uint64_t cand[J];
+  uint32_t cand[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    int e = lane + MOE_WAVE * j;
-    cand[j] = (e < E) ? pack_key(key[j], e) : 0ull;
+    const int e = lane + MOE_WAVE * j;
+    cand[j] = (e < E) ? order_key(key[j]) : 0u;
   }
   sel_idx = -1;
   sel_key = 0.0f;
   for (int it = 0; it < k; ++it) {
-    uint64_t best = 0;
+    uint32_t best = cand[0];
 #pragma unroll
-    for (int j = 0; j < J; ++j) best = cand[j] > best ? cand[j] : best;
-    uint64_t w = wave_max_u64(best);
+    for (int j = 1; j < J; ++j) best = cand[j] > best ? cand[j] : best;
+    const uint32_t m = wave_max_u32(best);
+    int win = -1;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const uint64_t b = __ballot(cand[j] == m);
+      if (win < 0 && b != 0) win = MOE_WAVE * j + (int)__builtin_ctzll(b);
+    }
     if (lane == it) {
-      sel_idx = unpack_idx(w);
-      uint32_t u = (uint32_t)(w >> 32);
-      u = (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u;
-      sel_key = __uint_as_float(u);
+      sel_idx = win;
+      sel_key = order_key_inv(m);
     }
 #pragma unroll
     for (int j = 0; j < J; ++j)
-      if (cand[j] == w) cand[j] = 0ull;
+      if (lane + MOE_WAVE * j == win) cand[j] = 0u;
   }
 }
 
