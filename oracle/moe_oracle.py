@@ -25,7 +25,8 @@ decides an integer: the router's selection key and the fp8 codes are computed
 in float32, the precision the pages fix for scores (scores_type) and for the
 activation ("in fp32"), with every float32 step correctly rounded so that the
 decision is reproducible.  Stored intermediates are rounded the way the layer
-stores them (bf16, or e4m3 with 1x128 scales) before they are used again.
+stores them (bf16, e4m3 with 1x128 scales, or MXFP8 for the MXFP4 layer)
+before they are used again.
 
 Parity of the whole layer has no worked example on the pages; each part is
 pinned separately by the CPU tests (closed forms, identities, brute force,
@@ -139,6 +140,92 @@ def dequant_weight_block128(codes, scales) -> np.ndarray:
     k, n = codes.shape
     v = e4m3_decode(codes).reshape(k // 128, 128, n // 128, 128)
     return (v * np.asarray(scales, np.float64)[:, None, :, None]).reshape(k, n)
+
+
+# --------------------------------------------------------------------------
+# MX block formats (StackedMoE page: optional MXFP4 weights, run W4A8 with
+# MXFP8 activations).  The pages name the formats only; their definition is
+# the OCP Microscaling (MX) v1.0 specification: 32 consecutive elements along
+# the reduction dimension share one E8M0 scale (an 8-bit power-of-two
+# exponent, bias 127, 0xFF = NaN); MXFP4 elements are E2M1 (1 sign, 2
+# exponent bits with bias 1, 1 mantissa bit, no inf/NaN), MXFP8 elements
+# are E4M3 (the OCP e4m3fn format above).
+# --------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E4M3_EMAX = 8            # largest e4m3 normal: 1.75 * 2^8
+
+
+def e8m0_decode(s) -> np.ndarray:
+    """E8M0 scale bytes -> float64 2^(s - 127); 255 is NaN."""
+    s = np.asarray(s, np.int64)
+    v = np.ldexp(1.0, s - 127)
+    return np.where(s == 255, np.nan, v)
+
+
+def _e2m1_value(c) -> np.ndarray:
+    c = np.asarray(c, np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.ldexp(1.0, e - 1))
+    return sign * mag
+
+
+_E2M1_TABLE = _e2m1_value(np.arange(16))
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 codes (0..15) -> float64: exponent field 0 is subnormal (m * 0.5),
+    otherwise (1 + m/2) * 2^(e-1); bit 3 is the sign."""
+    return _E2M1_TABLE[np.asarray(codes, np.int64) & 15]
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """uint8 [..., K/2] -> E2M1 codes [..., K]: element 2i is the low nibble
+    of byte i, element 2i+1 the high nibble."""
+    p = np.asarray(packed, np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+    out[..., 0::2] = p & 15
+    out[..., 1::2] = p >> 4
+    return out
+
+
+def mx_dequant_fp4(packed, scales) -> np.ndarray:
+    """MXFP4 rows: packed codes [N, K/2] and E8M0 scales [N, K/32] -> float64 [N, K]."""
+    v = e2m1_decode(unpack_fp4(packed))
+    n, k = v.shape
+    return (v.reshape(n, k // MX_BLOCK, MX_BLOCK) * e8m0_decode(scales)[:, :, None]).reshape(n, k)
+
+
+def mxfp8_quantize_rows(a):
+    """Per-row MXFP8 quantisation along the columns (blocks of 32).
+
+    For each block: amax = max |v| (float32); a block with amax = 0 gets the
+    unit scale (E8M0 127); otherwise the shared exponent is
+    X = floor(log2(amax)) - 8 (8 = emax of E4M3), kept >= -127, so that the
+    block's largest magnitude scales into [256, 512).  Elements are encoded
+    as e4m3(v * 2^-X) with round to nearest even, saturating at 448 (the
+    scaling by a power of two is exact in float32).  Returns (codes uint8
+    [N, C], E8M0 scales uint8 [N, C/32]).
+    """
+    a32 = np.asarray(a, dtype=np.float32)
+    n, c = a32.shape
+    assert c % MX_BLOCK == 0
+    g = a32.reshape(n, c // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(g).max(axis=2)
+    _, ex = np.frexp(amax.astype(np.float64))       # amax = f * 2^ex, f in [0.5, 1)
+    X = np.maximum(ex.astype(np.int64) - 1 - E4M3_EMAX, -127)
+    X = np.where(amax == 0, 0, X)
+    q = (g * np.ldexp(np.float32(1.0), -X)[:, :, None].astype(np.float32)).astype(np.float32)
+    codes = e4m3_encode(q).reshape(n, c)
+    return codes, (X + 127).astype(np.uint8)
+
+
+def mx_dequant_fp8(codes, scales) -> np.ndarray:
+    n, c = codes.shape
+    v = e4m3_decode(codes).reshape(n, c // MX_BLOCK, MX_BLOCK)
+    return (v * e8m0_decode(scales)[:, :, None]).reshape(n, c)
 
 
 # --------------------------------------------------------------------------
@@ -353,6 +440,9 @@ def expert_mlp(x_rows, w_gate_up, w_down, *, fmt="concatenated", activation="sil
     elif act_format == "fp8":
         codes, sc = quantize_rows_block128(a.astype(np.float32))
         a = dequant_rows_block128(codes, sc)
+    elif act_format == "mxfp8":
+        codes, sc = mxfp8_quantize_rows(a.astype(np.float32))
+        a = mx_dequant_fp8(codes, sc)
     elif act_format != "none":
         raise ValueError(act_format)
     o = float(down_scale) * (a @ np.asarray(w_down, np.float64))
@@ -383,6 +473,14 @@ def combine(expert_out, row_of_slot, expert_weights=None, token_mask=None) -> np
 # --------------------------------------------------------------------------
 
 def _expert_weights_f64(inp, e, operand, suffix=""):
+    """One expert's weights as float64 in the StackedMoE page's shapes,
+    W_gate_up [H, 2D] and W_down [D, H].  MXFP4 weights arrive as rows along
+    the reduction dimension (the MX blocks run along it): gate_up codes
+    [2D, H/2] with scales [2D, H/32], down codes [H, D/2] with [H, D/32]."""
+    if operand == "mxfp4":
+        wgu = mx_dequant_fp4(inp["w_gate_up" + suffix][e], inp["w_gate_up" + suffix + "_scale"][e]).T
+        wd = mx_dequant_fp4(inp["w_down" + suffix][e], inp["w_down" + suffix + "_scale"][e]).T
+        return wgu, wd
     if operand == "fp8":
         wgu = dequant_weight_block128(inp["w_gate_up" + suffix][e], inp["w_gate_up" + suffix + "_scale"][e])
         wd = dequant_weight_block128(inp["w_down" + suffix][e], inp["w_down" + suffix + "_scale"][e])
@@ -390,6 +488,10 @@ def _expert_weights_f64(inp, e, operand, suffix=""):
         wgu = np.asarray(inp["w_gate_up" + suffix][e], np.float64)
         wd = np.asarray(inp["w_down" + suffix][e], np.float64)
     return wgu, wd
+
+
+# how the layer stores the intermediate A, per operand type
+_ACT_FORMAT = {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp8"}
 
 
 def shared_weights(cfg, sink_weights, T):
@@ -410,6 +512,9 @@ def layer_inputs_x(inp, operand):
     if operand == "fp8":
         codes, sc = quantize_rows_block128(x)
         return dequant_rows_block128(codes, sc)
+    if operand == "mxfp4":
+        codes, sc = mxfp8_quantize_rows(x)
+        return mx_dequant_fp8(codes, sc)
     return x.astype(np.float64)
 
 
@@ -471,8 +576,7 @@ def layer(inp, cfg, *, indices=None, weights=None, tokens=None, token_mask=None,
         sd = 1.0 if down_expert_scales is None else down_expert_scales[e + expert_start]
         o = expert_mlp(xs[sel_t], wgu, wd, fmt=cfg.gate_up_format, activation=cfg.activation,
                        alpha=cfg.alpha, limit=cfg.limit, b_gate_up=bgu, b_down=bd,
-                       gate_up_scale=sgu, down_scale=sd,
-                       act_format="fp8" if operand == "fp8" else "bf16")
+                       gate_up_scale=sgu, down_scale=sd, act_format=_ACT_FORMAT[operand])
         np.add.at(y, sel_t, w_s[sel_t, sel_j][:, None] * o)
     if getattr(cfg, "n_shared", 0):
         if cfg.router == "sigmoid_sink" and sink_weights is None:
@@ -484,6 +588,6 @@ def layer(inp, cfg, *, indices=None, weights=None, tokens=None, token_mask=None,
             bd = inp["b_down_shared"][i] if cfg.has_bias else None
             o = expert_mlp(xs, wgu, wd, fmt=cfg.gate_up_format, activation=cfg.activation,
                            alpha=cfg.alpha, limit=cfg.limit, b_gate_up=bgu, b_down=bd,
-                           act_format="fp8" if operand == "fp8" else "bf16")
+                           act_format=_ACT_FORMAT[operand])
             y += np.where(valid[:, None], sw[:, i:i + 1] * o, 0.0)
     return y

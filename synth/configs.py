@@ -1,4 +1,4 @@
-"""The five MoE FFN workloads, as plain data.
+"""The MoE FFN workloads, as plain data.
 
 Names follow the StackedMoE page (hidden_dim, num_experts,
 num_experts_per_token, moe_dim, gate_up_format, has_bias), the
@@ -30,7 +30,7 @@ class MoEConfig:
     activation: str = "silu"    # "silu" | "swigluoai" | "gelu_tanh"
     alpha: float = 0.0
     limit: float = 0.0
-    operand_dtype: str = "bf16"  # "bf16" | "fp8"
+    operand_dtype: str = "bf16"  # "bf16" | "fp8" | "mxfp4" (MXFP4 weights, MXFP8 activations: W4A8)
     route_scale: float = 1.0
     global_scale: float = 1.0
     logit_std: float = 2.0      # sigmoid router: logits are an input ~N(0, logit_std)
@@ -60,6 +60,11 @@ CONFIGS = {
                  activation="swigluoai", alpha=1.702, limit=7.0),
     5: MoEConfig(5, "fp8", T=16384, H=7168, E=256, k=8, D=2048,
                  router="sigmoid_sink", s=0, operand_dtype="fp8",
+                 route_scale=1.0, global_scale=1.0),
+    # the fp8 layer's shape with MXFP4 experts run W4A8 (StackedMoE page:
+    # MXFP4 weights with MXFP8 activations)
+    6: MoEConfig(6, "mxfp4", T=16384, H=7168, E=256, k=8, D=2048,
+                 router="sigmoid_sink", s=0, operand_dtype="mxfp4",
                  route_scale=1.0, global_scale=1.0),
 }
 

@@ -18,6 +18,12 @@ layer receives them: float8_e4m3fn codes plus one fp32 scale per 128x128
 block (amax/448).  That quantisation is data preparation of the weights,
 done here with torch's own cast; it is not a step of the layer.
 
+For the MXFP4 workload the weights are drawn directly in their stored form:
+rows along the reduction dimension (gate_up [E, 2D, H/2], down [E, H, D/2]),
+two E2M1 codes per byte with every code equally likely, and one E8M0 scale
+byte per 32 codes, uniform in [118, 121] (tensor ids 11 and 12), which gives
+weights of about the bf16 workloads' spread.
+
 The same seed gives the same tensors on a given device type; a CPU run and a
 GPU run draw different numbers, which is why parity always copies the GPU's
 inputs to the host before calling the oracle.
@@ -60,6 +66,15 @@ def _quant_fp8_blocks(w: torch.Tensor):
     return codes, scale.contiguous()
 
 
+def _mxfp4(rows, K, device, cfg_id, tid, sid, expert, salt):
+    """Random MXFP4 rows: packed E2M1 codes [rows, K/2] and E8M0 scales [rows, K/32]."""
+    g = _gen(device, cfg_id, tid, expert, salt)
+    codes = torch.randint(0, 256, (rows, K // 2), generator=g, device=device, dtype=torch.uint8)
+    g = _gen(device, cfg_id, sid, expert, salt)
+    scales = torch.randint(118, 122, (rows, K // 32), generator=g, device=device, dtype=torch.uint8)
+    return codes, scales
+
+
 def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
     """Draw every input tensor of one workload on `device`."""
     d = torch.device(device)
@@ -80,6 +95,17 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
             wgu[e] = _normal((H, 2 * D), cfg.w_std, d, c, 3, e, salt).to(torch.bfloat16)
             wd[e] = _normal((D, H), cfg.w_std, d, c, 4, e, salt).to(torch.bfloat16)
         out["w_gate_up"], out["w_down"] = wgu, wd
+    elif cfg.operand_dtype == "mxfp4":
+        assert H % 32 == 0 and D % 32 == 0
+        wgu = torch.empty((E, 2 * D, H // 2), device=d, dtype=torch.uint8)
+        wgus = torch.empty((E, 2 * D, H // 32), device=d, dtype=torch.uint8)
+        wd = torch.empty((E, H, D // 2), device=d, dtype=torch.uint8)
+        wds = torch.empty((E, H, D // 32), device=d, dtype=torch.uint8)
+        for e in range(E):
+            wgu[e], wgus[e] = _mxfp4(2 * D, H, d, c, 3, 11, e, salt)
+            wd[e], wds[e] = _mxfp4(H, D, d, c, 4, 12, e, salt)
+        out["w_gate_up"], out["w_gate_up_scale"] = wgu, wgus
+        out["w_down"], out["w_down_scale"] = wd, wds
     else:
         assert H % 128 == 0 and D % 128 == 0
         wgu = torch.empty((E, H, 2 * D), device=d, dtype=torch.uint8)
@@ -95,6 +121,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
         out["b_gate_up"] = _normal((E, 2 * D), cfg.w_std, d, c, 5, 0, salt).to(torch.bfloat16)
         out["b_down"] = _normal((E, H), cfg.w_std, d, c, 6, 0, salt).to(torch.bfloat16)
     if cfg.n_shared:
+        assert cfg.operand_dtype != "mxfp4", "shared experts are bf16 or fp8"
         # shared experts: the same gated MLP with moe_dim = shared_dim, in the
         # layer's operand dtype (tensor ids 7..10, one stream per shared expert)
         S, Ds = cfg.n_shared, cfg.shared_dim

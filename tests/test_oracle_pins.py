@@ -510,7 +510,7 @@ def test_tokens_subset_and_mask_and_local_slice():
 
 def test_small_configs_run_end_to_end():
     import synth
-    for cid in (1, 3, 4):
+    for cid in (1, 3, 4, 6):
         cfg = synth.scaled(synth.get_config(cid), T=16)
         inp = synth.to_host(synth.make_inputs(synth.scaled(cfg, H=min(cfg.H, 256), D=min(cfg.D, 256), E=min(cfg.E, 16)), "cpu"))
         c2 = synth.scaled(cfg, H=min(cfg.H, 256), D=min(cfg.D, 256), E=min(cfg.E, 16))
@@ -633,3 +633,131 @@ def test_shared_experts_brute_force(router):
     ym = O.layer(inp, cfg, indices=r["indices"], weights=r["weights"], sink_weights=r["sink_weights"],
                  token_mask=mask)
     assert np.all(ym[mask == 0] == 0.0) and np.allclose(ym[mask == 1], y[mask == 1], rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------- MX formats
+# The pages name MXFP4 / MXFP8 (StackedMoE page: mxfp8_activations); the
+# element and scale formats are those of the OCP Microscaling v1.0 spec.
+
+def test_e8m0_decode_matches_torch():
+    s = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(s).view(torch.float8_e8m0fnu).double().numpy()
+    ours = O.e8m0_decode(s)
+    assert np.isnan(ours[255]) and np.isnan(ref[255])
+    assert np.array_equal(ours[:255], ref[:255])
+
+
+def test_e2m1_values_match_torch_e4m3_after_rebias():
+    """An E2M1 code (s, e, m) is the e4m3fn code with the exponent re-biased
+    from 1 to 7 and the mantissa bit widened to 3 bits; its one subnormal
+    (0.5) is the e4m3 normal 2^-1.  Decoded by torch's e4m3 cast."""
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e > 0:
+            code = (s << 7) | ((e - 1 + 7) << 3) | (m << 2)
+        else:
+            code = (s << 7) | ((6 << 3) if m else 0)
+        ref = torch.tensor([code], dtype=torch.uint8).view(torch.float8_e4m3fn).double().item()
+        got = float(O.e2m1_decode(np.array([c]))[0])
+        assert got == ref and math.copysign(1.0, got) == math.copysign(1.0, ref), (c, got, ref)
+
+
+def test_fp4_packing_is_low_nibble_first():
+    codes = np.arange(16, dtype=np.uint8)
+    packed = np.array([[0x10, 0x32, 0x54, 0x76, 0x98, 0xBA, 0xDC, 0xFE]], np.uint8)
+    assert np.array_equal(O.unpack_fp4(packed)[0], codes)
+
+
+def _brute_e4m3(v):
+    """Nearest finite e4m3fn value (torch decode of every code), ties to the
+    even code, saturating at +-448."""
+    allc = np.arange(256)
+    vals = torch.from_numpy(allc.astype(np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+    fin = [c for c in allc if not np.isnan(vals[c])]
+    if abs(v) >= 448.0:
+        return 0x7E | (0x80 if v < 0 else 0)
+    best = None
+    for c in fin:
+        d = abs(vals[c] - v)
+        key = (d, c & 1)
+        if best is None or key < best[0]:
+            best = (key, c)
+    c = best[1]
+    if vals[c] == 0.0:
+        return 0x80 if math.copysign(1.0, v) < 0 else 0x00
+    return c
+
+
+def test_mxfp8_quantisation_brute_force():
+    rng = np.random.default_rng(31)
+    rows = [rng.standard_normal(64) * 10.0 ** rng.integers(-6, 6),
+            np.zeros(64), np.r_[np.zeros(31), [-3e-38], rng.standard_normal(32) * 1e30],
+            np.r_[np.full(32, 448.0), np.full(32, -511.9)], np.r_[np.full(32, 1.0), np.full(32, 0.75)],
+            rng.standard_normal(64) * 1e-40]
+    a = O.bf16_round(np.stack(rows))
+    codes, scales = O.mxfp8_quantize_rows(a)
+    for r in range(a.shape[0]):
+        for b in range(2):
+            blk = a[r, 32 * b:32 * b + 32].astype(np.float64)
+            amax = np.abs(blk).max()
+            if amax == 0:
+                X = 0
+            else:
+                X = -127
+                while amax * 2.0 ** -X >= 512.0:       # smallest X (>= -127) with amax * 2^-X < 512
+                    X += 1
+            assert scales[r, b] == X + 127, (r, b, scales[r, b], X)
+            for j in range(32):
+                want = _brute_e4m3(blk[j] * 2.0 ** -X)
+                assert codes[r, 32 * b + j] == want, (r, b, j, blk[j], codes[r, 32 * b + j], want)
+
+
+def test_mx_dequant_fp4_brute_force():
+    rng = np.random.default_rng(32)
+    packed = rng.integers(0, 256, (3, 32), dtype=np.uint8)      # 3 rows, K = 64
+    scales = rng.integers(110, 140, (3, 2), dtype=np.uint8)
+    got = O.mx_dequant_fp4(packed, scales)
+    sv = torch.from_numpy(scales).view(torch.float8_e8m0fnu).double().numpy()
+    for n in range(3):
+        for k in range(64):
+            nib = (int(packed[n, k // 2]) >> (4 * (k % 2))) & 15
+            assert got[n, k] == float(O.e2m1_decode(np.array([nib]))[0]) * sv[n, k // 32]
+
+
+def test_mxfp4_layer_uses_dequantised_operands():
+    """The MXFP4 (W4A8) layer equals the plain MLP on dequantised MXFP4
+    weights (rows along the reduction dimension) and per-token MXFP8
+    activations, with A requantised to MXFP8 per row."""
+    rng = np.random.default_rng(33)
+    T, H, D, E, k = 5, 64, 32, 3, 2
+    x = O.bf16_round(rng.standard_normal((T, H)))
+    wgu = rng.integers(0, 256, (E, 2 * D, H // 2), dtype=np.uint8)
+    wgus = rng.integers(118, 123, (E, 2 * D, H // 32), dtype=np.uint8)
+    wd = rng.integers(0, 256, (E, H, D // 2), dtype=np.uint8)
+    wds = rng.integers(118, 123, (E, H, D // 32), dtype=np.uint8)
+    inp = {"x": x, "w_gate_up": wgu, "w_gate_up_scale": wgus, "w_down": wd, "w_down_scale": wds}
+    cfg = _Cfg(T=T, H=H, E=E, k=k, D=D, operand_dtype="mxfp4")
+    idx = np.array([[0, 1], [2, 0], [1, 2], [0, 2], [1, 0]], np.int32)
+    w = rng.random((T, k))
+    y = O.layer(inp, cfg, indices=idx, weights=w)
+
+    def deq(p, s):   # element by element, scales through torch
+        sv = torch.from_numpy(np.ascontiguousarray(s)).view(torch.float8_e8m0fnu).double().numpy()
+        out = np.zeros((p.shape[0], 2 * p.shape[1]))
+        for n in range(p.shape[0]):
+            for kk in range(out.shape[1]):
+                nib = (int(p[n, kk // 2]) >> (4 * (kk % 2))) & 15
+                out[n, kk] = O.e2m1_decode(np.array([nib]))[0] * sv[n, kk // 32]
+        return out
+    xc, xs = O.mxfp8_quantize_rows(x)
+    xq = O.e4m3_decode(xc) * np.repeat(torch.from_numpy(xs).view(torch.float8_e8m0fnu).double().numpy(), 32, axis=1)
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            e = idx[t, j]
+            h = xq[t:t + 1] @ deq(wgu[e], wgus[e]).T
+            a = O.gated_activation(h[:, :D], h[:, D:], "silu").astype(np.float32)
+            ac, asc = O.mxfp8_quantize_rows(a)
+            aq = O.e4m3_decode(ac) * np.repeat(torch.from_numpy(asc).view(torch.float8_e8m0fnu).double().numpy(), 32, axis=1)
+            acc += w[t, j] * (aq @ deq(wd[e], wds[e]).T)[0]
+        assert np.allclose(y[t], acc, rtol=1e-12, atol=1e-12)
