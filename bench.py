@@ -278,7 +278,8 @@ def main():
     R = cfg.T * cfg.k
     gu_flops = 4.0 * R * cfg.H * cfg.D
     dn_flops = 2.0 * R * cfg.D * cfg.H
-    peak = PEAK_FP8_TFLOPS if cfg.operand_dtype == "fp8" else PEAK_BF16_TFLOPS
+    # fp8 and the MXFP4 x MXFP8 product (which runs at the fp8 MFMA rate) take the fp8 peak
+    peak = PEAK_BF16_TFLOPS if cfg.operand_dtype == "bf16" else PEAK_FP8_TFLOPS
     gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
     ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
     # algorithmic HBM bytes of the two bandwidth kernels
@@ -286,14 +287,14 @@ def main():
         route_bytes = 2 * cfg.T * cfg.H + 2 * cfg.H * cfg.E + 8 * cfg.T * cfg.k
     else:                         # reads the logits and the bias, writes indices and weights
         route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
-    o_bytes = 2 if cfg.operand_dtype == "fp8" else 4   # expert rows O: bf16 or fp32
+    o_bytes = 4 if cfg.operand_dtype == "bf16" else 2   # expert rows O: fp32 or bf16
     n_sh = getattr(cfg, "n_shared", 0)
     comb_bytes = o_bytes * (R + n_sh * cfg.T) * cfg.H + 8 * R + 4 * n_sh * cfg.T + 2 * cfg.T * cfg.H
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if cfg.operand_dtype == "fp8" else "bf16", "data": "synthetic",
+        "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4_w4a8"}[cfg.operand_dtype], "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
                                f"top-{cfg.k} {cfg.router} router moe_dim={cfg.D} {cfg.gate_up_format} "
                                f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -72,9 +72,18 @@ enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLUOAI = 1, MOE_ACT_GELU_TANH = 2 };
 enum { MOE_GATE_UP_CONCATENATED = 0, MOE_GATE_UP_INTERLEAVED = 1 };
 /* Element types.  MOE_DTYPE_FP8_E4M3_TOKENS is a moe_build_indices form of
    the fp8 operand: every token quantised once (1x128 blocks), not permuted;
-   moe_grouped_ffn then gathers the rows it needs through sorted_token. */
+   moe_grouped_ffn then gathers the rows it needs through sorted_token.
+   MX block formats ([StackedMoE] mxfp8_activations: MXFP4 experts run W4A8;
+   formats of the OCP Microscaling specification): 32 consecutive elements
+   along the reduction dimension share one E8M0 scale byte (2^(s-127)).
+   MOE_DTYPE_MXFP4_W4A8 is a moe_grouped_ffn operand type: E2M1 weights
+   (two per byte, element 2i in the low nibble of byte i) times MXFP8
+   activations (e4m3 codes); MOE_DTYPE_MXFP8 / MOE_DTYPE_MXFP8_TOKENS are the
+   moe_build_indices forms of those activations (permuted rows, or one row
+   per token in token order). */
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_BLOCK128 = 1, MOE_DTYPE_FP32 = 2,
-       MOE_DTYPE_FP8_E4M3_TOKENS = 3 };
+       MOE_DTYPE_FP8_E4M3_TOKENS = 3, MOE_DTYPE_MXFP4_W4A8 = 4, MOE_DTYPE_MXFP8 = 5,
+       MOE_DTYPE_MXFP8_TOKENS = 6 };
 /* Weight layouts: [StackedMoE] stacked [E, in_features, out_features]
    ("Weight tensor shapes"), or its transposed view
    [E, out_features, in_features] (gate_up_proj_transposed /
@@ -171,9 +180,16 @@ moe_status_t moe_route(const moe_route_args_t* args, void* stream);
  *                  scale amax/448, 1 when amax = 0; H % 128 == 0), or
  *                  MOE_DTYPE_FP8_E4M3_TOKENS (the same quantisation, one row
  *                  per token in token order: x_perm [T, H], x_perm_scale
- *                  [T, H/128]; the gather is left to moe_grouped_ffn)
+ *                  [T, H/128]; the gather is left to moe_grouped_ffn), or
+ *                  MOE_DTYPE_MXFP8 / MOE_DTYPE_MXFP8_TOKENS (H % 32 == 0):
+ *                  per 32 columns, shared exponent X = floor(log2 amax) - 8
+ *                  (at least -127; 0 for an all-zero block), codes
+ *                  e4m3(v * 2^-X) rounded to nearest even and saturating at
+ *                  448, scale byte X + 127; permuted rows or one per token
  *   x_perm         [T*k, H] bf16 or uint8 out, rows p < kept written
- *   x_perm_scale   fp32 [T*k, H/128] out (fp8 only)
+ *                  ([T, H] for the _TOKENS forms)
+ *   x_perm_scale   out, fp8 and MX only: fp32 [rows, H/128] (fp8) or E8M0
+ *                  bytes [rows, H/32] (MX)
  *   workspace      device scratch of moe_build_indices_workspace_bytes()
  * Rows p >= expert_offsets[L] of the outputs are left unwritten.
  * ---------------------------------------------------------------------- */
@@ -193,7 +209,7 @@ typedef struct moe_index_args {
   int32_t hidden_dim;
   int32_t xperm_dtype;
   void* x_perm;
-  float* x_perm_scale;
+  void* x_perm_scale;
   void* workspace;
   int64_t workspace_bytes;
 } moe_index_args_t;
@@ -213,7 +229,8 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *   gate, up = split(h): CONCATENATED [gate | up], INTERLEAVED gate = even
  *            columns, up = odd columns (the bias follows the same order)
  *   A[p]   = activation(gate, up)            stored bf16 (fp8 path: e4m3 with
- *            a per-row 1x128 scale amax/448)
+ *            a per-row 1x128 scale amax/448; MX path: MXFP8, quantised as
+ *            moe_build_indices does)
  *   O[p]   = down_expert_scales[e] * (A[p] . W_d[e]) + b_down[e]
  * activation (GatedAct): SILU silu(gate)*up, with limit > 0 gate=min(gate,limit)
  *   and up=clamp(up,-limit,limit) first; SWIGLUOAI g*sigmoid(alpha*g)*(u+1)
@@ -226,20 +243,26 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *                  the device, no host synchronisation
  *   hidden_dim H, moe_dim D, n_local_experts L in [1, 1024]       host
  *   expert_offsets int32 [L + 1]
- *   operand_dtype  host: MOE_DTYPE_BF16 or MOE_DTYPE_FP8_E4M3_BLOCK128
+ *   operand_dtype  host: MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_BLOCK128 or
+ *                  MOE_DTYPE_MXFP4_W4A8 (H % 128 == 0 and D % 128 == 0;
+ *                  OUT_IN weights only, whose packed E2M1 rows run along K)
  *   x_perm         [max_rows, H] bf16 (or e4m3 codes) -- or NULL to gather
  *                  rows straight from x through sorted_token (bf16 only)
- *   x_perm_scale   fp32 [max_rows, H/128]            fp8 only
+ *   x_perm_scale   fp32 [max_rows, H/128] (fp8), E8M0 bytes [max_rows, H/32] (MX)
  *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form; for fp8
  *                  x holds the per-token codes [T, H] and x_perm_scale the
- *                  per-token scales [T, H/128] (MOE_DTYPE_FP8_E4M3_TOKENS)
+ *                  per-token scales [T, H/128] (MOE_DTYPE_FP8_E4M3_TOKENS);
+ *                  for MX the MOE_DTYPE_MXFP8_TOKENS codes and scales
  *                  (x_perm / x, the activation buffer and one expert's
  *                  weights must each be under 4 GiB)
  *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]
- *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128]
+ *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128];
+ *                  MX: packed E2M1 w_gate_up [L, 2D, H/2] with E8M0 scale
+ *                  bytes [L, 2D, H/32]
  *   b_gate_up      bf16 [L, 2D] or NULL
  *   w_down         layout IN_OUT [L, D, H] or OUT_IN [L, H, D]
- *   w_down_scale   fp32 [L, D/128, H/128] (IN_OUT) or [L, H/128, D/128]
+ *   w_down_scale   fp32 [L, D/128, H/128] (IN_OUT) or [L, H/128, D/128];
+ *                  MX: packed w_down [L, H, D/2] with scale bytes [L, H, D/32]
  *   b_down         bf16 [L, H] or NULL
  *   gate_up_expert_scales, down_expert_scales  fp32 [L] or NULL (1.0)
  *   act_workspace  device scratch of moe_ffn_workspace_bytes(): A, and for
@@ -262,17 +285,17 @@ typedef struct moe_ffn_args {
   const int32_t* expert_offsets;
   int32_t operand_dtype;
   const void* x_perm;
-  const float* x_perm_scale;
+  const void* x_perm_scale;
   const void* x;
   const int32_t* sorted_token;
   const void* w_gate_up;
   int32_t w_gate_up_layout;
-  const float* w_gate_up_scale;
+  const void* w_gate_up_scale;
   const void* b_gate_up;
   int32_t gate_up_format;
   const void* w_down;
   int32_t w_down_layout;
-  const float* w_down_scale;
+  const void* w_down_scale;
   const void* b_down;
   int32_t activation;
   float alpha;

@@ -22,6 +22,10 @@ ROUTER_SOFTMAX_TOPK, ROUTER_SIGMOID_SINK = 0, 1
 ACT = {"silu": 0, "swigluoai": 1, "gelu_tanh": 2}
 FMT = {"concatenated": 0, "interleaved": 1}
 DTYPE_BF16, DTYPE_FP8_E4M3_BLOCK128, DTYPE_FP32, DTYPE_FP8_E4M3_TOKENS = 0, 1, 2, 3
+DTYPE_MXFP4_W4A8, DTYPE_MXFP8, DTYPE_MXFP8_TOKENS = 4, 5, 6
+XPERM = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128, "fp8_tokens": DTYPE_FP8_E4M3_TOKENS,
+         "mxfp8": DTYPE_MXFP8, "mxfp8_tokens": DTYPE_MXFP8_TOKENS}
+OPERAND = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128, "mxfp4": DTYPE_MXFP4_W4A8}
 WEIGHT_IN_OUT, WEIGHT_OUT_IN = 0, 1
 
 _vp = ctypes.c_void_p
@@ -185,13 +189,18 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
     if weights is not None:
         out["sorted_weight"] = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
     H = 0
-    fp8 = xperm_dtype in ("fp8", "fp8_tokens")
-    rows = T if xperm_dtype == "fp8_tokens" else R
+    if xperm_dtype not in XPERM:
+        raise ValueError(f"xperm_dtype must be one of {sorted(XPERM)}")
+    quant = xperm_dtype != "bf16"
+    mx = xperm_dtype.startswith("mx")
+    rows = T if xperm_dtype.endswith("_tokens") else R
     if x is not None:
         _dt(x, torch.bfloat16, "x")
         H = x.shape[1]
-        out["x_perm"] = torch.empty((max(rows, 1), H), dtype=torch.uint8 if fp8 else torch.bfloat16, device=dev)
-        if fp8:
+        out["x_perm"] = torch.empty((max(rows, 1), H), dtype=torch.uint8 if quant else torch.bfloat16, device=dev)
+        if mx:
+            out["x_perm_scale"] = torch.empty((max(rows, 1), H // 32), dtype=torch.uint8, device=dev)
+        elif quant:
             out["x_perm_scale"] = torch.empty((max(rows, 1), H // 128), dtype=torch.float32, device=dev)
     wsb = lib().moe_build_indices_workspace_bytes(T, k, n_local)
     ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
@@ -200,8 +209,7 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
                   token_mask=_ptr(token_mask), expert_offsets=_ptr(out["offsets"]),
                   sorted_token=_ptr(out["sorted_token"]), row_of_slot=_ptr(out["row_of_slot"]),
                   sorted_weight=_ptr(out.get("sorted_weight")), x=_ptr(x), hidden_dim=H,
-                  xperm_dtype={"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128,
-                               "fp8_tokens": DTYPE_FP8_E4M3_TOKENS}[xperm_dtype],
+                  xperm_dtype=XPERM[xperm_dtype],
                   x_perm=_ptr(out.get("x_perm")), x_perm_scale=_ptr(out.get("x_perm_scale")),
                   workspace=_ptr(ws), workspace_bytes=ws.numel())
     _check(lib().moe_build_indices(ctypes.byref(a), _stream(dev)))
@@ -209,7 +217,7 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
 
 
 def ffn_workspace(max_rows: int, D: int, operand: str, device) -> torch.Tensor:
-    n = lib().moe_ffn_workspace_bytes(max_rows, D, DTYPE_FP8_E4M3_BLOCK128 if operand == "fp8" else DTYPE_BF16)
+    n = lib().moe_ffn_workspace_bytes(max_rows, D, OPERAND[operand])
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
@@ -230,7 +238,7 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
     _dt(offsets, torch.int32, "offsets")
     a = FfnArgs(max_rows=max_rows, hidden_dim=H, moe_dim=D, n_local_experts=L,
                 expert_offsets=_ptr(offsets),
-                operand_dtype=DTYPE_FP8_E4M3_BLOCK128 if weights.operand == "fp8" else DTYPE_BF16,
+                operand_dtype=OPERAND[weights.operand],
                 x_perm=_ptr(x_perm), x_perm_scale=_ptr(x_perm_scale), x=_ptr(x),
                 sorted_token=_ptr(sorted_token),
                 w_gate_up=_ptr(weights.w_gate_up), w_gate_up_layout=weights.layout,
@@ -285,6 +293,8 @@ class ExpertWeights:
 
     layout WEIGHT_OUT_IN: w_gate_up [L, 2D, H], w_down [L, H, D] (the
     transposed views of the stacked [L, H, 2D] / [L, D, H] weights).
+    operand "mxfp4": packed E2M1 w_gate_up [L, 2D, H/2], w_down [L, H, D/2]
+    with E8M0 scales [L, 2D, H/32] / [L, H, D/32] (rows along K, OUT_IN).
     """
     w_gate_up: torch.Tensor
     w_down: torch.Tensor
@@ -302,7 +312,18 @@ class ExpertWeights:
     def from_stacked(w_gate_up, w_down, *, b_gate_up=None, b_down=None, w_gate_up_scale=None,
                      w_down_scale=None, operand="bf16", layout=WEIGHT_OUT_IN):
         """Take stacked [L, H, 2D] / [L, D, H] weights and lay them out once,
-        at load time, in the layout the kernels read."""
+        at load time, in the layout the kernels read.  MXFP4 weights already
+        come as rows along K ([L, 2D, H/2] / [L, H, D/2]) and are kept."""
+        if operand == "mxfp4":
+            if layout != WEIGHT_OUT_IN:
+                raise ValueError("MXFP4 weights are rows along the reduction dimension (OUT_IN)")
+            for t, name in ((w_gate_up, "w_gate_up"), (w_down, "w_down"), (w_gate_up_scale, "w_gate_up_scale"),
+                            (w_down_scale, "w_down_scale")):
+                _dt(t, torch.uint8, name)
+            L, D2, Hh = w_gate_up.shape
+            return ExpertWeights(w_gate_up.contiguous(), w_down.contiguous(), L, 2 * Hh, D2 // 2, operand,
+                                 layout, w_gate_up_scale.contiguous(), w_down_scale.contiguous(),
+                                 b_gate_up, b_down)
         L, H, D2 = w_gate_up.shape
         D = D2 // 2
         if layout == WEIGHT_OUT_IN:
@@ -336,7 +357,7 @@ class MoELayer:
         R = T * k
         self.R = R
         self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev)
-        self.out_dtype = torch.bfloat16 if cfg.operand_dtype == "fp8" else torch.float32
+        self.out_dtype = torch.float32 if cfg.operand_dtype == "bf16" else torch.bfloat16
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
         # shared experts: their own weights and buckets (every token in each)
@@ -372,12 +393,13 @@ class MoELayer:
                                   global_scale=self.global_scale)
         if mark:
             mark(1)
-        fp8 = c.operand_dtype == "fp8"
+        fp8 = c.operand_dtype in ("fp8", "mxfp4")
         if fp8:
-            # the fp8 operand: every token quantised once; gathered by the GEMM
-            # (gather=True) or quantised per permuted row here (gather=False)
+            # the fp8 / MXFP8 operand: every token quantised once; gathered by
+            # the GEMM (gather=True) or quantised per permuted row here
+            q = "fp8" if c.operand_dtype == "fp8" else "mxfp8"
             ind = build_indices(idx, c.E, weights=w, token_mask=token_mask, x=x,
-                                xperm_dtype="fp8_tokens" if self.gather else "fp8")
+                                xperm_dtype=q + "_tokens" if self.gather else q)
             xg = ind.pop("x_perm") if self.gather else None
         else:
             ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,

@@ -147,9 +147,13 @@ moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
     if (a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128 || a->xperm_dtype == MOE_DTYPE_FP8_E4M3_TOKENS) {
       REQUIRE(H % 128 == 0, "moe_build_indices: fp8 quantisation needs hidden_dim % 128 == 0 (got %d)", H);
       REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for fp8");
+    } else if (a->xperm_dtype == MOE_DTYPE_MXFP8 || a->xperm_dtype == MOE_DTYPE_MXFP8_TOKENS) {
+      REQUIRE(H % 32 == 0, "moe_build_indices: MXFP8 quantisation needs hidden_dim % 32 == 0 (got %d)", H);
+      REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for MXFP8");
     } else {
       REQUIRE(a->xperm_dtype == MOE_DTYPE_BF16,
-              "moe_build_indices: xperm_dtype must be BF16, FP8_E4M3_BLOCK128 or FP8_E4M3_TOKENS");
+              "moe_build_indices: xperm_dtype must be BF16, FP8_E4M3_BLOCK128, FP8_E4M3_TOKENS, MXFP8 or "
+              "MXFP8_TOKENS");
     }
   }
   hipStream_t st = (hipStream_t)stream;
@@ -159,11 +163,12 @@ moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
                                            (int32_t*)a->workspace, st);
   if (e != hipSuccess) return hip_status(e, "moe_build_indices");
   if (permute) {
-    const bool tokens = a->xperm_dtype == MOE_DTYPE_FP8_E4M3_TOKENS;
+    const int dt = a->xperm_dtype;
+    const bool tokens = dt == MOE_DTYPE_FP8_E4M3_TOKENS || dt == MOE_DTYPE_MXFP8_TOKENS;
+    const int kind = dt == MOE_DTYPE_BF16 ? 0 : (dt == MOE_DTYPE_MXFP8 || dt == MOE_DTYPE_MXFP8_TOKENS) ? 2 : 1;
     e = moe::launch_permute((const uint16_t*)a->x, tokens ? nullptr : a->sorted_token,
                             a->expert_offsets + L, tokens ? (int64_t)T : (int64_t)T * k,
-                            a->hidden_dim, a->xperm_dtype != MOE_DTYPE_BF16, a->x_perm,
-                            a->x_perm_scale, st);
+                            a->hidden_dim, kind, a->x_perm, a->x_perm_scale, st);
     if (e != hipSuccess) return hip_status(e, "moe_build_indices (permute)");
   }
   return ok();
@@ -174,6 +179,8 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t D, int32_t dtype) {
   if (max_rows < 0 || D < 1) return 0;
   if (dtype == MOE_DTYPE_FP8_E4M3_BLOCK128)
     return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 127) / 128) * 4, 256);
+  if (dtype == MOE_DTYPE_MXFP4_W4A8)  // A codes, then one E8M0 byte per 32 columns
+    return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 31) / 32), 256);
   // bf16: A, then the down GEMM's split-K counters and partial tiles
   return round_up((int64_t)max_rows * D * 2, 256) + moe::SPLIT_COUNTERS * 4 +
          (int64_t)moe::split_slots_for(max_rows) * moe::SPLIT_TILE_FLOATS * 4;
@@ -187,6 +194,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   REQUIRE(D >= 8 && D % 8 == 0, "moe_grouped_ffn: moe_dim must be a positive multiple of 8 (got %d)", D);
   REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn: n_local_experts must be in [1, 1024] (got %d)", L);
   REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn: expert_offsets is required");
+  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16 || a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128 ||
+              a->operand_dtype == MOE_DTYPE_MXFP4_W4A8,
+          "moe_grouped_ffn: operand_dtype must be BF16, FP8_E4M3_BLOCK128 or MXFP4_W4A8");
   REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI ||
               a->activation == MOE_ACT_GELU_TANH,
           "moe_grouped_ffn: unknown activation %d", a->activation);
@@ -220,6 +230,47 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   if (a->act_workspace_bytes < need || (need > 0 && a->act_workspace == nullptr))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn: act_workspace needs %lld bytes (got %lld)",
                 (long long)need, (long long)a->act_workspace_bytes);
+  if (a->operand_dtype == MOE_DTYPE_MXFP4_W4A8) {
+    REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: MX needs hidden_dim and moe_dim multiples of 128");
+    REQUIRE(a->x_perm_scale != nullptr && (a->x_perm != nullptr || a->x != nullptr),
+            "moe_grouped_ffn: MX takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
+    REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
+            "moe_grouped_ffn: MXFP4 weights need w_gate_up_scale and w_down_scale");
+    REQUIRE((int64_t)R * H < ((int64_t)1 << 32) && (int64_t)R * D < ((int64_t)1 << 32) &&
+                (int64_t)D * H < ((int64_t)1 << 32),
+            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
+    REQUIRE(aligned16(a->b_gate_up) && aligned16(a->b_down), "moe_grouped_ffn: biases must be 16-byte aligned");
+    if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: MXFP4 weights must use the OUT_IN layout");
+    if (R == 0) return ok();
+    moe::FfnMxParams q{};
+    q.offsets = a->expert_offsets;
+    q.L = L;
+    q.H = H;
+    q.D = D;
+    q.max_rows = R;
+    q.fmt = a->gate_up_format;
+    q.x_perm = (const uint8_t*)(a->x_perm ? a->x_perm : a->x);
+    q.x_scale = (const uint8_t*)a->x_perm_scale;
+    q.sorted_token = a->x_perm ? nullptr : a->sorted_token;
+    q.w_gate_up = (const uint8_t*)a->w_gate_up;
+    q.w_gate_up_scale = (const uint8_t*)a->w_gate_up_scale;
+    q.w_down = (const uint8_t*)a->w_down;
+    q.w_down_scale = (const uint8_t*)a->w_down_scale;
+    q.b_gate_up = (const uint16_t*)a->b_gate_up;
+    q.b_down = (const uint16_t*)a->b_down;
+    q.gate_up_scales = a->gate_up_expert_scales;
+    q.down_scales = a->down_expert_scales;
+    q.act_kind = a->activation;
+    q.alpha = a->alpha;
+    q.limit = a->limit;
+    q.act = (uint8_t*)a->act_workspace;
+    q.act_scale = (uint8_t*)a->act_workspace + round_up((int64_t)R * D, 256);
+    q.out = a->expert_out;
+    q.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+    q.events = (hipEvent_t const*)a->timing_events;
+    return hip_status(moe::launch_ffn_mx(q, (hipStream_t)stream), "moe_grouped_ffn");
+  }
   if (a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {
     REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: fp8 needs hidden_dim and moe_dim multiples of 128");
     REQUIRE(a->x_perm_scale != nullptr && (a->x_perm != nullptr || a->x != nullptr),
@@ -243,12 +294,12 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.D = D;
     q.max_rows = R;
     q.x_perm = (const uint8_t*)(a->x_perm ? a->x_perm : a->x);
-    q.x_scale = a->x_perm_scale;
+    q.x_scale = (const float*)a->x_perm_scale;
     q.sorted_token = a->x_perm ? nullptr : a->sorted_token;
     q.w_gate_up = (const uint8_t*)a->w_gate_up;
-    q.w_gate_up_scale = a->w_gate_up_scale;
+    q.w_gate_up_scale = (const float*)a->w_gate_up_scale;
     q.w_down = (const uint8_t*)a->w_down;
-    q.w_down_scale = a->w_down_scale;
+    q.w_down_scale = (const float*)a->w_down_scale;
     q.gate_up_scales = a->gate_up_expert_scales;
     q.down_scales = a->down_expert_scales;
     q.act_kind = a->activation;
@@ -261,7 +312,6 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.events = (hipEvent_t const*)a->timing_events;
     return hip_status(moe::launch_ffn_fp8(q, (hipStream_t)stream), "moe_grouped_ffn");
   }
-  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn: operand_dtype must be BF16 or FP8_E4M3_BLOCK128");
   // the GEMMs address rows with 32-bit byte offsets
   REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 32) && (int64_t)R * D * 2 < ((int64_t)1 << 32) &&
               (int64_t)2 * D * H * 2 < ((int64_t)1 << 32),

@@ -1,0 +1,453 @@
+// Grouped MX block-scaled expert GEMMs on gfx950: MXFP4 (E2M1) weights times
+// MXFP8 (E4M3) activations, each with one E8M0 scale per 32 elements along K
+// (StackedMoE page: MXFP4 weights run W4A8 with MXFP8 activations; the
+// formats are those of the OCP Microscaling specification).  The scales go
+// straight into v_mfma_scale_f32_32x32x64_f8f6f4, which applies them per 32
+// K slots, so the main loop does no scale arithmetic at all.
+//
+// Operand layout of that MFMA with the e2m1 operand first and the e4m3
+// operand second (measured with one-wave probes on gfx950): lane l = 32h + r
+// holds row r.  Its 32 e2m1 codes all fall in the first 32 K slots (h = 0) or
+// the last 32 (h = 1); of its 32 e4m3 bytes, bytes 0-15 fall in the first 32
+// slots and bytes 16-31 in the last 32.  e2m1 code p of half 0 meets e4m3
+// byte p of half 0 (p < 16) or byte p-16 of half 1; e2m1 code p of half 1
+// meets e4m3 byte 16+p of half 0 (p < 16) or byte p of half 1.  The scale of
+// the first 32 slots is lane r's, of the last 32 lane 32+r's.  So for the
+// 64-wide k step kk, whose MX blocks are 2kk and 2kk+1:
+//   e2m1 lane h: k [64kk+32h, +32)            = 16-byte chunk 2kk+h of the row
+//   e4m3 lane h: k [64kk+16h, +16), [64kk+32+16h, +16) = chunks 4kk+h, 4kk+2+h
+//   both pass the scale byte of block 2kk+h.
+// (e2m1 element 2i is the low nibble of byte i, as the MFMA reads it.)
+//
+// gate_up:  h = s_gu[e] * C + b_gu[e]; A = act(gate, up), re-quantised to
+//           MXFP8 per row per 32 columns (shared exponent floor(log2 amax)-8,
+//           unit scale for an all-zero block) -> codes + E8M0 scales, the
+//           down GEMM's operand.
+// down:     O = s_d[e] * C + b_d[e]  (bf16 or fp32 out)
+//
+// Tiling: 256 x 256 workgroup tile, 8 waves in 2 x 4 (two per SIMD), each
+// wave 128 x 64 = 4 x 2 MFMA blocks.  k stages of 128 go global -> LDS by
+// buffer loads, triple buffered: 32 KB of e4m3 rows, 16 KB of packed e2m1
+// rows and the two operands' 4 scale bytes per row.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+enum { MX_GATE_UP = 0, MX_DOWN = 1 };
+
+constexpr int X_BM = 256, X_BN = 256, X_BK = 128;         // BK in elements
+constexpr int X_NSTAGE = 3;
+constexpr int X_WAVES_M = 2, X_WAVES_N = 4;
+constexpr int X_NT = 64 * X_WAVES_M * X_WAVES_N;           // 512 threads
+constexpr int X_WTM = X_BM / X_WAVES_M, X_WTN = X_BN / X_WAVES_N;  // 128 x 64
+constexpr int X_MI = X_WTM / 32, X_NI = X_WTN / 32;        // 4 x 2 MFMA blocks
+constexpr int X_A_ROW = X_BK;                              // bytes per e4m3 stage row
+constexpr int X_B_ROW = X_BK / 2;                          // bytes per packed e2m1 stage row
+constexpr int X_A_BYTES = X_BM * X_A_ROW;                  // 32 KB
+constexpr int X_B_BYTES = X_BN * X_B_ROW;                  // 16 KB
+constexpr int X_AS_OFF = X_A_BYTES + X_B_BYTES;            // 256 scale dwords of the A rows
+constexpr int X_BS_OFF = X_AS_OFF + X_BM * 4;              // 256 scale dwords of the B rows
+constexpr int X_STAGE_BYTES = X_BS_OFF + X_BN * 4;         // 50 KB
+constexpr int X_LPW_A = X_A_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 4
+constexpr int X_LPW_B = X_B_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 2
+constexpr int X_LOADS = X_LPW_A + X_LPW_B + 2;             // per wave per stage (+2: scale rows)
+constexpr int X_LDS_PIPE = X_NSTAGE * X_STAGE_BYTES;       // 150 KB
+
+constexpr int X_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
+
+// e4m3 rows: 128 bytes, 8 chunks; chunk c of row r at c ^ fa(r).
+__device__ __forceinline__ int mx_fa(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int mx_a_off(int row, int chunk) { return row * X_A_ROW + ((chunk ^ mx_fa(row)) << 4); }
+// e2m1 rows: 64 bytes, 4 chunks; chunk c of row r at c ^ fb(r), which puts the
+// rows r, r+4, r+8, r+12 that share banks on four different chunks (the
+// fragment reads of 32 consecutive rows are conflict-free).
+__device__ __forceinline__ int mx_fb(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
+__device__ __forceinline__ int mx_b_off(int row, int chunk) { return row * X_B_ROW + ((chunk ^ mx_fb(row)) << 4); }
+
+__device__ __forceinline__ void mx_block_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct MxGemmArgs {
+  const int32_t* offsets;
+  int L;
+  int K, N;                  // reduction length; output columns (gate_up D, down H)
+  int fmt;                   // gate_up format (gate_up only)
+  const uint8_t* A;          // e4m3 [rows, K] (or per token, gathered)
+  const uint8_t* A_scale;    // E8M0 [rows, K/32]
+  const int32_t* gather;     // row -> token, or nullptr
+  const uint8_t* W;          // packed e2m1, OUT_IN per expert [w_rows, K/2]
+  int64_t w_estride;         // bytes per expert
+  const uint8_t* W_scale;    // E8M0 per expert [w_rows, K/32]
+  int64_t ws_estride;        // bytes per expert
+  const uint16_t* bias;      // bf16 per expert, or nullptr
+  int64_t bias_estride;
+  const float* escale;
+  float alpha, limit;
+  void* out;                 // gate_up: e4m3 [rows, D]; down: bf16 / fp32 [rows, H]
+  uint8_t* out_scale;        // gate_up: E8M0 [rows, D/32]
+};
+
+// Shared exponent of an MXFP8 block with largest magnitude m (>= 0):
+// floor(log2 m) - 8, at least -127; 0 for m = 0.
+__device__ __forceinline__ int mx_shared_exp(float m) {
+  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
+  return m == 0.0f ? 0 : max(e - 127 - 8, -127);
+}
+// 2^-X for X in [-127, 120]: a normal float built from its exponent field.
+__device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
+
+template <int MODE, int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(X_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_mx_kernel(const MxGemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int32_t* s_mbp = (int32_t*)smem;  // m-block prefix, before the stage buffers are filled
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / X_WAVES_N, wn = wave % X_WAVES_N;
+  const int L = p.L;
+
+  // ---- prefix of 256-row blocks per expert (wave 0), in LDS
+  if (wave == 0) {
+    const int per = (L + 63) / 64;
+    const int e0 = lane * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < L) sum += (p.offsets[e + 1] - p.offsets[e] + X_BM - 1) / X_BM;
+    }
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, MOE_WAVE);
+      if (lane >= o) inc += v;
+    }
+    int run = inc - sum;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < L) {
+        s_mbp[e] = run;
+        run += (p.offsets[e + 1] - p.offsets[e] + X_BM - 1) / X_BM;
+      }
+    }
+    if (lane == 63) s_mbp[L] = inc;
+  }
+  __syncthreads();
+
+  constexpr int NBO = (MODE == MX_GATE_UP) ? X_BN / 2 : X_BN;  // output columns per tile
+  const int NB = (p.N + NBO - 1) / NBO;
+  const int total = s_mbp[L] * NB;
+  const int per_xcd = (total + 7) >> 3;
+  const int slot = blockIdx.x >> 3;
+  if (slot >= per_xcd) return;
+  const int tile = (blockIdx.x & 7) * per_xcd + slot;
+  if (tile >= total) return;
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_mbp[mid] * NB <= tile) lo = mid;
+    else hi = mid - 1;
+  }
+  const int e = __builtin_amdgcn_readfirstlane(lo);
+  const int nmb = s_mbp[e + 1] - s_mbp[e];
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[e] * NB);
+  const int nb = local / nmb, mb = local % nmb;
+  const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * X_BM);
+  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm_s = wave_s / X_WAVES_N;
+  const int KT = p.K / X_BK;        // K is a multiple of 128
+  const uint32_t srow = (uint32_t)p.K / 32u;  // scale bytes per row
+  __syncthreads();  // every wave has read the prefix before the loads overwrite it
+
+  // weight row of B tile row trow: wave column q owns 32 gate rows then the
+  // matching 32 up rows (gate_up), or 64 consecutive rows (down)
+  auto w_row = [&](int trow) {
+    if (MODE == MX_DOWN) return min(nb * X_BN + trow, p.N - 1);
+    const int q = trow / X_WTN, rr = trow % X_WTN, isup = rr / (X_WTN / 2), j = rr % (X_WTN / 2);
+    const int oc = min(nb * NBO + q * (X_WTN / 2) + j, p.N - 1);
+    return (FMT == 0) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
+  };
+
+  // ---- loader.  A: 1 KB = 8 rows x 8 chunks per instruction; B: 16 rows x
+  // 4 chunks.  Per-lane offsets fixed for the tile, the k offset of a stage in
+  // the scalar offset, the LDS destination in M0.  Rows past the expert's
+  // last row (or past N) repeat it; their results are never stored.
+  const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
+  const uint8_t* WSexp = p.W_scale + (int64_t)e * p.ws_estride;
+  uint32_t a_voff[X_LPW_A], b_voff[X_LPW_B];
+#pragma unroll
+  for (int i = 0; i < X_LPW_A; ++i) {
+    const int trow = (wave * X_LPW_A + i) * 8 + (lane >> 3);
+    const int r = min(row_beg + trow, row_end - 1);
+    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+    a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < X_LPW_B; ++i) {
+    const int trow = (wave * X_LPW_B + i) * 16 + (lane >> 2);
+    b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)p.K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+  }
+  // scale rows: lanes 0..31 of wave w fetch the 4 bytes of tile rows 32w + lane
+  const int sr = wave * 32 + (lane & 31);
+  const int a_sr = min(row_beg + sr, row_end - 1);
+  const uint32_t as_voff = (p.gather ? (uint32_t)p.gather[a_sr] : (uint32_t)a_sr) * srow;
+  const uint32_t bs_voff = (uint32_t)w_row(sr) * srow;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, X_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A_scale, (short)0, 0x7fffffff, X_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)WSexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
+
+  auto stage_base = [&](int kt) { return smem + (kt % X_NSTAGE) * X_STAGE_BYTES; };
+  auto issue = [&](int kt) {
+    uint8_t* st = stage_base(kt);
+#pragma unroll
+    for (int i = 0; i < X_LPW_A; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (wave_s * X_LPW_A + i) * 1024), 16, a_voff[i],
+                                               kt * X_A_ROW, 0, 0);
+#pragma unroll
+    for (int i = 0; i < X_LPW_B; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + X_A_BYTES + (wave_s * X_LPW_B + i) * 1024), 16,
+                                               b_voff[i], kt * X_B_ROW, 0, 0);
+    if (lane < 32) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(st + X_AS_OFF + wave_s * 128), 4, as_voff, kt * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + X_BS_OFF + wave_s * 128), 4, bs_voff, kt * 4, 0, 0);
+    }
+  };
+
+  const int fr = lane & 31, fh = lane >> 5;
+  f32x16_t acc[X_MI][X_NI];
+#pragma unroll
+  for (int mi = 0; mi < X_MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < X_NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+
+  // fragments of one 64-wide k step kk (see the layout note at the top)
+  auto frag_a = [&](const uint8_t* st, int row, int kk) {
+    const u32x4_t lo4 = *(const u32x4_t*)(st + mx_a_off(row, 4 * kk + fh));
+    const u32x4_t hi4 = *(const u32x4_t*)(st + mx_a_off(row, 4 * kk + 2 + fh));
+    return i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
+  };
+  auto frag_b = [&](const uint8_t* st, int row, int kk) {
+    const u32x4_t c4 = *(const u32x4_t*)(st + X_A_BYTES + mx_b_off(row, 2 * kk + fh));
+    return i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
+  };
+
+  const int live_mi = min(max((row_end - (row_beg + wm_s * X_WTM) + 31) / 32, 0), X_MI);
+
+  // ---- main loop: stage kt is waited for and published, stage kt+2 is
+  // issued into the buffer of stage kt-1 (free: every wave has passed the
+  // barrier after computing it), then the stage's 16 MFMAs per wave run
+  issue(0);
+  if (KT > 1) issue(1);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(X_LOADS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    mx_block_barrier();
+    if (kt + 2 < KT) issue(kt + 2);
+    const uint8_t* st = stage_base(kt);
+    const uint32_t* as_l = (const uint32_t*)(st + X_AS_OFF);
+    const uint32_t* bs_l = (const uint32_t*)(st + X_BS_OFF);
+    i32x8_t bq[X_NI][2];
+    int bsc[X_NI][2];
+#pragma unroll
+    for (int ni = 0; ni < X_NI; ++ni) {
+      const int row = wn * X_WTN + ni * 32 + fr;
+      const uint32_t s4 = bs_l[row];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bq[ni][kk] = frag_b(st, row, kk);
+        bsc[ni][kk] = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < X_MI; ++mi) {
+      if (mi < live_mi) {
+        const int row = wm * X_WTM + mi * 32 + fr;
+        const uint32_t s4 = as_l[row];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const i32x8_t aq = frag_a(st, row, kk);
+          const int asc = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
+#pragma unroll
+          for (int ni = 0; ni < X_NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[ni][kk], aq, acc[mi][ni], 4, 0, 0,
+                                                                          bsc[ni][kk], 0, asc);
+        }
+      }
+    }
+  }
+
+  // ---- epilogue.  acc[mi][ni][4q + c] is C[row][col] with
+  //   row = wm*128 + mi*32 + fr,  col = wn*64 + ni*32 + 8q + 4fh + c
+  const float sc = p.escale ? p.escale[e] : 1.0f;
+  const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
+  if (MODE == MX_GATE_UP) {
+    // block 0 holds the gate columns, block 1 the up columns of the wave's 32
+    // outputs, which are one MX block of each row: the 16 values of a lane and
+    // the 16 of lane xor 32
+    uint8_t* out = (uint8_t*)p.out;
+    float bg[4][4], bu[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fh;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bg[q][c] = 0.0f;
+        bu[q][c] = 0.0f;
+      }
+      if (bias_e) {
+        if (FMT == 0) {
+          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
+          bg[q][0] = bf16_to_f32(g2.x & 0xffffu); bg[q][1] = bf16_to_f32(g2.x >> 16);
+          bg[q][2] = bf16_to_f32(g2.y & 0xffffu); bg[q][3] = bf16_to_f32(g2.y >> 16);
+          bu[q][0] = bf16_to_f32(u2.x & 0xffffu); bu[q][1] = bf16_to_f32(u2.x >> 16);
+          bu[q][2] = bf16_to_f32(u2.y & 0xffffu); bu[q][3] = bf16_to_f32(u2.y >> 16);
+        } else {
+          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bg[q][c] = bf16_to_f32(b4[c] & 0xffffu);
+            bu[q][c] = bf16_to_f32(b4[c] >> 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < X_MI; ++mi) {
+      const int row = row_beg + wm * X_WTM + mi * 32 + fr;
+      float a[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        a[r] = gated_act<ACT>(acc[mi][0][r] * sc + bg[r / 4][r % 4], acc[mi][1][r] * sc + bu[r / 4][r % 4],
+                              p.alpha, p.limit);
+        m = fmaxf(m, fabsf(a[r]));
+      }
+      m = fmaxf(m, __shfl_xor(m, 32, MOE_WAVE));
+      if (row >= row_end) continue;
+      const int X = mx_shared_exp(m);
+      const float inv = mx_inv_scale(X);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fh;
+        *(uint32_t*)(out + (int64_t)row * p.N + oc) =
+            e4m3x4(a[4 * q] * inv, a[4 * q + 1] * inv, a[4 * q + 2] * inv, a[4 * q + 3] * inv);
+      }
+      if (fh == 0) p.out_scale[(int64_t)row * (p.N / 32) + (nb * NBO + wn * 32) / 32] = (uint8_t)(X + 127);
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < X_NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb * X_BN + wn * X_WTN + ni * 32 + 8 * q + 4 * fh;  // first of 4 columns
+        if (n >= p.N) continue;
+        float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e) {
+          const uint2 b2 = *(const uint2*)(bias_e + n);
+          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+        }
+#pragma unroll
+        for (int mi = 0; mi < X_MI; ++mi) {
+          const int row = row_beg + wm * X_WTM + mi * 32 + fr;
+          if (row >= row_end) continue;
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
+          if (OUT_BF16) {
+            uint2 w;
+            w.x = pack_bf16x2_rne(v[0], v[1]);
+            w.y = pack_bf16x2_rne(v[2], v[3]);
+            *(uint2*)((uint16_t*)p.out + (int64_t)row * p.N + n) = w;
+          } else {
+            const f32x4_t w = {v[0], v[1], v[2], v[3]};
+            *(f32x4_t*)((float*)p.out + (int64_t)row * p.N + n) = w;
+          }
+        }
+      }
+  }
+}
+
+template <typename KernelT>
+hipError_t launch_mx(KernelT kern, const MxGemmArgs& a, int max_rows, int NBO, hipStream_t st) {
+  const int prefix = (a.L + 1) * (int)sizeof(int32_t);
+  const int lds = X_LDS_PIPE > prefix ? X_LDS_PIPE : prefix;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t nonempty = (int64_t)max_rows < a.L ? max_rows : a.L;
+  const int64_t mblocks = (max_rows + X_BM - 1) / X_BM + nonempty;
+  const int64_t NB = (a.N + NBO - 1) / NBO;
+  const int64_t grid = ((mblocks * NB + 7) / 8) * 8;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  kern<<<(unsigned)grid, X_NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_mx_gate_up(const MxGemmArgs& g, int fmt, int max_rows, hipStream_t st) {
+  if (fmt == 0) return launch_mx(grouped_gemm_mx_kernel<MX_GATE_UP, ACT, 0, false>, g, max_rows, X_BN / 2, st);
+  return launch_mx(grouped_gemm_mx_kernel<MX_GATE_UP, ACT, 1, false>, g, max_rows, X_BN / 2, st);
+}
+
+}  // namespace
+
+hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {
+  hipError_t err;
+  if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
+  MxGemmArgs g{};
+  g.offsets = q.offsets;
+  g.L = q.L;
+  g.K = q.H;
+  g.N = q.D;
+  g.fmt = q.fmt;
+  g.A = q.x_perm;
+  g.A_scale = q.x_scale;
+  g.gather = q.sorted_token;
+  g.W = q.w_gate_up;
+  g.w_estride = (int64_t)2 * q.D * (q.H / 2);
+  g.W_scale = q.w_gate_up_scale;
+  g.ws_estride = (int64_t)2 * q.D * (q.H / 32);
+  g.bias = q.b_gate_up;
+  g.bias_estride = (int64_t)2 * q.D;
+  g.escale = q.gate_up_scales;
+  g.alpha = q.alpha;
+  g.limit = q.limit;
+  g.out = q.act;
+  g.out_scale = q.act_scale;
+  if (q.act_kind == ACT_SILU) err = launch_mx_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st);
+  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_mx_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st);
+  else err = launch_mx_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st);
+  if (err != hipSuccess) return err;
+  if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
+  MxGemmArgs d{};
+  d.offsets = q.offsets;
+  d.L = q.L;
+  d.K = q.D;
+  d.N = q.H;
+  d.A = q.act;
+  d.A_scale = q.act_scale;
+  d.W = q.w_down;
+  d.w_estride = (int64_t)q.H * (q.D / 2);
+  d.W_scale = q.w_down_scale;
+  d.ws_estride = (int64_t)q.H * (q.D / 32);
+  d.bias = q.b_down;
+  d.bias_estride = q.H;
+  d.escale = q.down_scales;
+  d.out = q.out;
+  if (q.out_bf16)
+    err = launch_mx(grouped_gemm_mx_kernel<MX_DOWN, ACT_SILU, 0, true>, d, q.max_rows, X_BN, st);
+  else
+    err = launch_mx(grouped_gemm_mx_kernel<MX_DOWN, ACT_SILU, 0, false>, d, q.max_rows, X_BN, st);
+  if (err == hipSuccess && q.events) err = hipEventRecord(q.events[2], st);
+  return err;
+}
+
+}  // namespace moe

@@ -12,7 +12,8 @@
 //   csr_scatter per block: stable rank of each slot among same-expert slots
 //               (wave ballots per distinct expert, LDS running counts) ->
 //               sorted_token, row_of_slot, sorted_weight
-//   permute     x_perm[p] = x[sorted_token[p]] (bf16 copy, or e4m3 + scales)
+//   permute     x_perm[p] = x[sorted_token[p]] (bf16 copy, or e4m3 + 1x128
+//               fp32 scales, or MXFP8: e4m3 + one E8M0 byte per 32 columns)
 #include "common.h"
 #include "kernels.h"
 
@@ -241,6 +242,62 @@ __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __rest
   }
 }
 
+// Per-row MXFP8 quantisation fused into the gather (OCP MX: 32 columns share
+// one E8M0 scale): one wave per row, 4 lanes own one 32-column block (8
+// elements each, block max over the quad by DPP); a wave issues the loads of
+// PQ_U passes (1 KB each) before any arithmetic.  Shared exponent
+// X = floor(log2 amax) - 8 (at least -127; 0 for an all-zero block), codes
+// e4m3(v * 2^-X) with round to nearest even and saturation, scale byte X+127.
+// With sorted_token == nullptr row p is token p (n_fixed rows).
+__global__ __launch_bounds__(256) void permute_mxfp8_kernel(const uint16_t* __restrict__ x,
+                                                            const int32_t* __restrict__ sorted_token,
+                                                            const int32_t* __restrict__ n_rows,
+                                                            int n_fixed, int H,
+                                                            uint8_t* __restrict__ xq,
+                                                            uint8_t* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int n = sorted_token ? n_rows[0] : n_fixed;
+  const int chunks = H / 8;          // 16-byte pieces of a row; 4 per block
+  for (int row = blockIdx.x * 4 + (threadIdx.x >> 6); row < n; row += gridDim.x * 4) {
+    const uint16_t* src = x + (int64_t)(sorted_token ? sorted_token[row] : row) * H;
+    uint8_t* dst = xq + (int64_t)row * H;
+    for (int c0 = 0; c0 < chunks; c0 += 64 * PQ_U) {
+      u32x4_t v[PQ_U];
+#pragma unroll
+      for (int u = 0; u < PQ_U; ++u) {
+        const int c = c0 + 64 * u + lane;
+        v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (c < chunks) v[u] = *(const u32x4_t*)(src + c * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < PQ_U; ++u) {
+        const int c = c0 + 64 * u + lane;
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_to_f32((uint16_t)(v[u][i] & 0xffffu));
+          f[2 * i + 1] = bf16_to_f32((uint16_t)(v[u][i] >> 16));
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+        amax = fmaxf(amax, __uint_as_float(dpp_u32<DPP_QP_XOR1>(__float_as_uint(amax), 0u)));
+        amax = fmaxf(amax, __uint_as_float(dpp_u32<DPP_QP_XOR2>(__float_as_uint(amax), 0u)));
+        const int ex = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+        const int X = amax == 0.0f ? 0 : max(ex - 127 - 8, -127);
+        const float inv = __uint_as_float((uint32_t)(127 - X) << 23);   // 2^-X
+        uint2 q;
+        q.x = e4m3x4(f[0] * inv, f[1] * inv, f[2] * inv, f[3] * inv);
+        q.y = e4m3x4(f[4] * inv, f[5] * inv, f[6] * inv, f[7] * inv);
+        if (c < chunks) {
+          *(uint2*)(dst + c * 8) = q;
+          if ((lane & 3) == 0) xs[(int64_t)row * (H / 32) + c / 4] = (uint8_t)(X + 127);
+        }
+      }
+    }
+  }
+}
+
 // Buckets of the shared experts: every token in each, in token order.
 __global__ __launch_bounds__(256) void shared_indices_kernel(int T, int n_shared, int32_t* __restrict__ offsets,
                                                              int32_t* __restrict__ sorted_token) {
@@ -278,13 +335,16 @@ hipError_t launch_build_indices(const int32_t* idx, const float* w, const uint8_
 }
 
 hipError_t launch_permute(const uint16_t* x, const int32_t* sorted_token, const int32_t* n_rows,
-                          int64_t max_rows, int H, int fp8, void* xp, float* xs, hipStream_t st) {
+                          int64_t max_rows, int H, int kind, void* xp, void* xs, hipStream_t st) {
   if (max_rows == 0) return hipSuccess;
   int64_t blocks = (max_rows + 3) / 4;
   if (blocks > 16384) blocks = 16384;
-  if (fp8)
+  if (kind == 1)
     permute_fp8_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, (int)max_rows, H,
-                                                    (uint8_t*)xp, xs);
+                                                    (uint8_t*)xp, (float*)xs);
+  else if (kind == 2)
+    permute_mxfp8_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, (int)max_rows, H,
+                                                      (uint8_t*)xp, (uint8_t*)xs);
   else
     permute_bf16_kernel<<<(int)blocks, 256, 0, st>>>(x, sorted_token, n_rows, H, (uint16_t*)xp);
   return hipGetLastError();

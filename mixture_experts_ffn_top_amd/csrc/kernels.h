@@ -22,8 +22,10 @@ hipError_t launch_build_indices(const int32_t* idx, const float* w, const uint8_
                                 int k, int start, int L, int32_t* offsets, int32_t* sorted_token,
                                 int32_t* row_of_slot, float* sorted_weight, int32_t* ws,
                                 hipStream_t st);
+// kind: 0 bf16 copy, 1 e4m3 with 1x128 fp32 scales, 2 MXFP8 (e4m3 with one
+// E8M0 scale byte per 32 columns)
 hipError_t launch_permute(const uint16_t* x, const int32_t* sorted_token, const int32_t* n_rows,
-                          int64_t max_rows, int H, int fp8, void* xp, float* xs, hipStream_t st);
+                          int64_t max_rows, int H, int kind, void* xp, void* xs, hipStream_t st);
 
 struct FfnBf16Params {
   const int32_t* offsets;
@@ -78,6 +80,33 @@ struct FfnFp8Params {
   hipEvent_t const* events;
 };
 hipError_t launch_ffn_fp8(const FfnFp8Params& p, hipStream_t st);
+
+// MXFP4 weights x MXFP8 activations (W4A8); every scale is an E8M0 byte per
+// 32 elements along K.
+struct FfnMxParams {
+  const int32_t* offsets;
+  int L, H, D, max_rows;
+  int fmt;                       // gate_up format
+  const uint8_t* x_perm;         // e4m3 codes [max_rows, H], or per token [T, H] with sorted_token
+  const uint8_t* x_scale;        // [max_rows, H/32] or [T, H/32]
+  const int32_t* sorted_token;   // nullptr: rows already permuted
+  const uint8_t* w_gate_up;      // packed e2m1, OUT_IN [L, 2D, H/2]
+  const uint8_t* w_gate_up_scale;  // [L, 2D, H/32]
+  const uint8_t* w_down;         // packed e2m1, OUT_IN [L, H, D/2]
+  const uint8_t* w_down_scale;   // [L, H, D/32]
+  const uint16_t* b_gate_up;     // bf16 [L, 2D] or nullptr
+  const uint16_t* b_down;        // bf16 [L, H] or nullptr
+  const float* gate_up_scales;
+  const float* down_scales;
+  int act_kind;
+  float alpha, limit;
+  uint8_t* act;                  // e4m3 codes [max_rows, D]
+  uint8_t* act_scale;            // E8M0 [max_rows, D/32]
+  void* out;                     // [max_rows, H] bf16 or fp32
+  int out_bf16;
+  hipEvent_t const* events;
+};
+hipError_t launch_ffn_mx(const FfnMxParams& p, hipStream_t st);
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,

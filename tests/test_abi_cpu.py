@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_struct_layouts_match_header_sizes():
@@ -132,6 +132,16 @@ def _ffn(**kw):
     (dict(expert_out=100), m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(act_workspace_bytes=100), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
     (dict(operand_dtype=1, hidden_dim=200), m.MOE_ERR_INVALID_ARGUMENT, "128"),
+    (dict(operand_dtype=9), m.MOE_ERR_INVALID_ARGUMENT, "operand_dtype"),
+    # MX (MXFP4 weights x MXFP8 activations)
+    (dict(operand_dtype=4, hidden_dim=224, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144),
+     m.MOE_ERR_INVALID_ARGUMENT, "128"),
+    (dict(operand_dtype=4, w_gate_up_scale=128, w_down_scale=144), m.MOE_ERR_INVALID_ARGUMENT, "x_perm_scale"),
+    (dict(operand_dtype=4, x_perm_scale=112), m.MOE_ERR_INVALID_ARGUMENT, "w_gate_up_scale"),
+    (dict(operand_dtype=4, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, b_down=170),
+     m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(operand_dtype=4, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, w_down_layout=0),
+     m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
 ])
 def test_grouped_ffn_validation(kw, status, frag):
     st, msg = _err(m.lib().moe_grouped_ffn, _ffn(**kw))
@@ -156,6 +166,9 @@ def _idx(**kw):
     (dict(x=96, hidden_dim=250, x_perm=112), m.MOE_ERR_INVALID_ARGUMENT, "hidden_dim"),
     (dict(x=96, hidden_dim=200, x_perm=112, xperm_dtype=1, x_perm_scale=128), m.MOE_ERR_INVALID_ARGUMENT, "128"),
     (dict(x=96, hidden_dim=256, x_perm=112, xperm_dtype=1), m.MOE_ERR_INVALID_ARGUMENT, "x_perm_scale"),
+    (dict(x=96, hidden_dim=240, x_perm=112, xperm_dtype=6, x_perm_scale=128), m.MOE_ERR_INVALID_ARGUMENT, "32"),
+    (dict(x=96, hidden_dim=256, x_perm=112, xperm_dtype=5), m.MOE_ERR_INVALID_ARGUMENT, "x_perm_scale"),
+    (dict(x=96, hidden_dim=256, x_perm=112, xperm_dtype=7), m.MOE_ERR_INVALID_ARGUMENT, "xperm_dtype"),
 ])
 def test_build_indices_validation(kw, status, frag):
     st, msg = _err(m.lib().moe_build_indices, _idx(**kw))
@@ -209,5 +222,7 @@ def test_workspace_queries_and_status_strings():
     assert lib.moe_ffn_workspace_bytes(8192, 14336, 0) == 8192 * 14336 * 2 + 256 * 4 + 256 * 256 * 256 * 4
     assert lib.moe_ffn_workspace_bytes(64, 512, 0) == 64 * 512 * 2 + 256 * 4 + 4 * 256 * 256 * 4
     assert lib.moe_ffn_workspace_bytes(100, 256, 1) >= 100 * 256 + 100 * 2 * 4
+    # MX: e4m3 A, then one E8M0 byte per 32 columns, each rounded up to 256 bytes
+    assert lib.moe_ffn_workspace_bytes(100, 256, 4) == 25600 + 1024
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"

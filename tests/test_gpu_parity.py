@@ -521,3 +521,106 @@ def test_fp8_layer_full_size(moe):
     _, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=5), FP8_TOL)
+
+
+# ---------------------------------------------------------------- MX: MXFP4 weights x MXFP8 activations
+
+@pytest.mark.parametrize("mode", ["mxfp8_tokens", "mxfp8"])
+def test_mx_permute(moe, mode):
+    """MXFP8 quantisation of the activations: codes and E8M0 scale bytes
+    bit-exact, including an all-zero block, bf16 subnormals and a block
+    whose largest value saturates."""
+    T, E, k, H = 3000, 16, 3, 7168
+    idx, _ = _routing(T, E, k, 12)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(6)
+    x = (torch.randn((T, H), generator=g, device=DEV) * 3).to(torch.bfloat16)
+    x[5, :32] = 0
+    x[7, 32:64] = (torch.randn(32, generator=g, device=DEV) * 1e-39).to(torch.bfloat16)
+    x[9, 64:96] = (torch.randn(32, generator=g, device=DEV) * 1e30).to(torch.bfloat16)
+    x[11, 96:128] = 511.0                 # scales into 511 > 448: saturates
+    say(f"[mx permute] {mode} T={T} H={H}")
+    out = moe.build_indices(torch.from_numpy(idx).to(DEV), E, x=x, xperm_dtype=mode)
+    ref = O.build_indices(idx, E)
+    n = int(host(out["offsets"])[-1])
+    codes, sc = O.mxfp8_quantize_rows(host(x))
+    if mode == "mxfp8_tokens":
+        assert np.array_equal(host(out["x_perm"])[:T], codes)
+        assert np.array_equal(host(out["x_perm_scale"])[:T], sc)
+    else:
+        assert np.array_equal(host(out["x_perm"])[:n], codes[ref["sorted_token"]])
+        assert np.array_equal(host(out["x_perm_scale"])[:n], sc[ref["sorted_token"]])
+
+
+def _check_mx_act(cfg, inp, res, layer):
+    """The MXFP8 re-quantised activation against the oracle's re-quantisation
+    of its own activation.  A value near a rounding boundary (or a block max
+    near a power of two, which moves the shared exponent) may land one step
+    away; dequantised, the two must agree within two steps of the coarser of
+    the two encodings."""
+    hin = synth.to_host(inp)
+    ind = res["index"]
+    off = host(ind["offsets"])
+    st = host(ind["sorted_token"])
+    R, D = layer.R, cfg.D
+    n = int(off[-1])
+    ws = host(layer.act_ws)
+    codes_gpu = ws[: R * D].reshape(R, D)[:n]
+    so = ((R * D + 255) // 256) * 256
+    scale_gpu = ws[so: so + R * (D // 32)].reshape(R, D // 32)[:n]
+    xq = O.layer_inputs_x(hin, "mxfp4")
+    same = total = 0
+    worst = 0.0
+    for e in range(cfg.E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size == 0:
+            continue
+        wgu = O.mx_dequant_fp4(hin["w_gate_up"][e], hin["w_gate_up_scale"][e]).T
+        h = xq[st[rows]] @ wgu
+        if cfg.has_bias:
+            h = h + hin["b_gate_up"][e].astype(np.float64)[None, :]
+        gg, uu = O.split_gate_up(h, cfg.gate_up_format)
+        a = O.gated_activation(gg, uu, cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
+        codes_ref, sc_ref = O.mxfp8_quantize_rows(a)
+        cg = codes_gpu[rows]
+        same += int(np.sum(cg == codes_ref))
+        total += cg.size
+        deq_g = O.mx_dequant_fp8(cg, scale_gpu[rows])
+        deq_r = O.mx_dequant_fp8(codes_ref, sc_ref)
+
+        def step(c, s):   # one e4m3 step at the value (2^-6 of the scale in the subnormal range)
+            return np.maximum(np.abs(O.e4m3_decode(c)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(O.e8m0_decode(s), 32, axis=1)
+        ratio = np.abs(deq_g - deq_r) / np.maximum(step(codes_ref, sc_ref), step(cg, scale_gpu[rows]))
+        worst = max(worst, float(ratio.max()))
+    frac = same / max(total, 1)
+    say(f"  MXFP8 activation codes identical: {frac:.5f}; worst |gpu - oracle| = {worst:.3f} e4m3 steps")
+    assert frac >= 0.99
+    assert worst <= 2.0
+
+
+@pytest.mark.parametrize("changes,nsample,gather", [
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, True),
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, False),
+    ({"T": 300, "E": 5, "k": 2, "H": 128, "D": 128}, 300, True),      # one k stage in each GEMM
+    ({"T": 777, "E": 6, "k": 4, "H": 384, "D": 640, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, 777, True),
+    ({"T": 400, "E": 4, "k": 2, "H": 256, "D": 384, "activation": "gelu_tanh", "has_bias": True}, 400, False),
+    ({"T": 2048, "E": 16, "k": 4}, 256, True),                # full hidden / moe dims of the layer
+])
+def test_mx_layer_small(moe, changes, nsample, gather):
+    cfg = synth.scaled(synth.get_config(6), **changes)
+    inp = _gen(cfg)
+    say(f"[mx layer] {changes} gather={gather}")
+    layer, res = _run_layer(moe, cfg, inp, gather=gather)
+    _check_routing(cfg, inp, res)
+    _check_mx_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=4), FP8_TOL)
+
+
+def test_mx_layer_full_size(moe):
+    cfg = synth.get_config(6)
+    inp = _gen(cfg)
+    say("[mx layer full] T=16384 H=7168 E=256 k=8 D=2048 MXFP4 W4A8")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=6), FP8_TOL)
