@@ -279,7 +279,7 @@ def main():
     gu_flops = 4.0 * R * cfg.H * cfg.D
     dn_flops = 2.0 * R * cfg.D * cfg.H
     # fp8 and the MXFP4 x MXFP8 product (which runs at the fp8 MFMA rate) take the fp8 peak
-    peak = PEAK_BF16_TFLOPS if cfg.operand_dtype == "bf16" else PEAK_FP8_TFLOPS
+    peak = PEAK_BF16_TFLOPS if cfg.operand_dtype in ("bf16", "mxfp4_a16") else PEAK_FP8_TFLOPS
     gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
     ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
     # algorithmic HBM bytes of the two bandwidth kernels
@@ -287,22 +287,36 @@ def main():
         route_bytes = 2 * cfg.T * cfg.H + 2 * cfg.H * cfg.E + 8 * cfg.T * cfg.k
     else:                         # reads the logits and the bias, writes indices and weights
         route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
-    o_bytes = 4 if cfg.operand_dtype == "bf16" else 2   # expert rows O: fp32 or bf16
+    o_bytes = 4 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else 2   # expert rows O: fp32 or bf16
     n_sh = getattr(cfg, "n_shared", 0)
     comb_bytes = o_bytes * (R + n_sh * cfg.T) * cfg.H + 8 * R + 4 * n_sh * cfg.T + 2 * cfg.T * cfg.H
+    roof = {"bound": "mfma", "achieved": round(gu_tf, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(gu_tf / peak, 4), "traffic": _traffic() if cfg.cfg_id == 2 else None,
+            "kernel": "grouped gate_up GEMM + fused activation",
+            "flops_per_launch": gu_flops, "avg_launch_ms": round(t_gu, 4)}
+    if cfg.operand_dtype == "mxfp4_a16":
+        # a decode-sized batch: the gate_up GEMM is bound by streaming the
+        # 4-bit weights (and E8M0 scales) of every expert that has a row,
+        # plus the gathered bf16 rows in and the bf16 A out
+        off = layer.last_offsets.cpu()
+        used = int(((off[1:] - off[:-1]) > 0).sum())
+        gu_bytes = used * (2 * cfg.D * cfg.H // 2 + 2 * cfg.D * cfg.H // 32) + R * cfg.H * 2 + R * cfg.D * 2
+        gbs = gu_bytes / (t_gu * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "grouped gate_up GEMM + fused activation (MXFP4 weights, bf16 activations)",
+                "bytes_per_launch": gu_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_gu, 4)}
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4_w4a8"}[cfg.operand_dtype], "data": "synthetic",
+        "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4_w4a8", "mxfp4_a16": "mxfp4_w4a16"}[cfg.operand_dtype],
+        "data": "synthetic",
         "config": {"workload": f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
                                f"top-{cfg.k} {cfg.router} router moe_dim={cfg.D} {cfg.gate_up_format} "
                                f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,
                    "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(gu_tf, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(gu_tf / peak, 4), "traffic": _traffic(),
-                     "kernel": "grouped gate_up GEMM + fused activation",
-                     "flops_per_launch": gu_flops, "avg_launch_ms": round(t_gu, 4)},
+        "roofline": roof,
         "ffn_tflops": round(ffn_tf, 2), "ffn_mfma_frac": round(ffn_tf / peak, 4),
         "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),
                          "gate_up": round(t_gu, 4), "down": round(t_dn, 4),

@@ -80,10 +80,12 @@ enum { MOE_GATE_UP_CONCATENATED = 0, MOE_GATE_UP_INTERLEAVED = 1 };
    (two per byte, element 2i in the low nibble of byte i) times MXFP8
    activations (e4m3 codes); MOE_DTYPE_MXFP8 / MOE_DTYPE_MXFP8_TOKENS are the
    moe_build_indices forms of those activations (permuted rows, or one row
-   per token in token order). */
+   per token in token order).  MOE_DTYPE_MXFP4_W4A16 is the other MXFP4
+   operand type: the same weights times bf16 activations (and a bf16
+   intermediate A). */
 enum { MOE_DTYPE_BF16 = 0, MOE_DTYPE_FP8_E4M3_BLOCK128 = 1, MOE_DTYPE_FP32 = 2,
        MOE_DTYPE_FP8_E4M3_TOKENS = 3, MOE_DTYPE_MXFP4_W4A8 = 4, MOE_DTYPE_MXFP8 = 5,
-       MOE_DTYPE_MXFP8_TOKENS = 6 };
+       MOE_DTYPE_MXFP8_TOKENS = 6, MOE_DTYPE_MXFP4_W4A16 = 7 };
 /* Weight layouts: [StackedMoE] stacked [E, in_features, out_features]
    ("Weight tensor shapes"), or its transposed view
    [E, out_features, in_features] (gate_up_proj_transposed /
@@ -243,9 +245,11 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *                  the device, no host synchronisation
  *   hidden_dim H, moe_dim D, n_local_experts L in [1, 1024]       host
  *   expert_offsets int32 [L + 1]
- *   operand_dtype  host: MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_BLOCK128 or
- *                  MOE_DTYPE_MXFP4_W4A8 (H % 128 == 0 and D % 128 == 0;
- *                  OUT_IN weights only, whose packed E2M1 rows run along K)
+ *   operand_dtype  host: MOE_DTYPE_BF16, MOE_DTYPE_FP8_E4M3_BLOCK128,
+ *                  MOE_DTYPE_MXFP4_W4A8 or MOE_DTYPE_MXFP4_W4A16 (MX: H % 128
+ *                  == 0 and D % 128 == 0; OUT_IN weights only, whose packed
+ *                  E2M1 rows run along K; W4A16 takes bf16 x_perm / x like
+ *                  the bf16 path and keeps A in bf16)
  *   x_perm         [max_rows, H] bf16 (or e4m3 codes) -- or NULL to gather
  *                  rows straight from x through sorted_token (bf16 only)
  *   x_perm_scale   fp32 [max_rows, H/128] (fp8), E8M0 bytes [max_rows, H/32] (MX)

@@ -22,10 +22,11 @@ ROUTER_SOFTMAX_TOPK, ROUTER_SIGMOID_SINK = 0, 1
 ACT = {"silu": 0, "swigluoai": 1, "gelu_tanh": 2}
 FMT = {"concatenated": 0, "interleaved": 1}
 DTYPE_BF16, DTYPE_FP8_E4M3_BLOCK128, DTYPE_FP32, DTYPE_FP8_E4M3_TOKENS = 0, 1, 2, 3
-DTYPE_MXFP4_W4A8, DTYPE_MXFP8, DTYPE_MXFP8_TOKENS = 4, 5, 6
+DTYPE_MXFP4_W4A8, DTYPE_MXFP8, DTYPE_MXFP8_TOKENS, DTYPE_MXFP4_W4A16 = 4, 5, 6, 7
 XPERM = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128, "fp8_tokens": DTYPE_FP8_E4M3_TOKENS,
          "mxfp8": DTYPE_MXFP8, "mxfp8_tokens": DTYPE_MXFP8_TOKENS}
-OPERAND = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128, "mxfp4": DTYPE_MXFP4_W4A8}
+OPERAND = {"bf16": DTYPE_BF16, "fp8": DTYPE_FP8_E4M3_BLOCK128, "mxfp4": DTYPE_MXFP4_W4A8,
+           "mxfp4_a16": DTYPE_MXFP4_W4A16}
 WEIGHT_IN_OUT, WEIGHT_OUT_IN = 0, 1
 
 _vp = ctypes.c_void_p
@@ -293,8 +294,9 @@ class ExpertWeights:
 
     layout WEIGHT_OUT_IN: w_gate_up [L, 2D, H], w_down [L, H, D] (the
     transposed views of the stacked [L, H, 2D] / [L, D, H] weights).
-    operand "mxfp4": packed E2M1 w_gate_up [L, 2D, H/2], w_down [L, H, D/2]
-    with E8M0 scales [L, 2D, H/32] / [L, H, D/32] (rows along K, OUT_IN).
+    operand "mxfp4" (W4A8) / "mxfp4_a16" (W4A16): packed E2M1 w_gate_up
+    [L, 2D, H/2], w_down [L, H, D/2] with E8M0 scales [L, 2D, H/32] /
+    [L, H, D/32] (rows along K, OUT_IN).
     """
     w_gate_up: torch.Tensor
     w_down: torch.Tensor
@@ -314,7 +316,7 @@ class ExpertWeights:
         """Take stacked [L, H, 2D] / [L, D, H] weights and lay them out once,
         at load time, in the layout the kernels read.  MXFP4 weights already
         come as rows along K ([L, 2D, H/2] / [L, H, D/2]) and are kept."""
-        if operand == "mxfp4":
+        if operand in ("mxfp4", "mxfp4_a16"):
             if layout != WEIGHT_OUT_IN:
                 raise ValueError("MXFP4 weights are rows along the reduction dimension (OUT_IN)")
             for t, name in ((w_gate_up, "w_gate_up"), (w_down, "w_down"), (w_gate_up_scale, "w_gate_up_scale"),
@@ -357,7 +359,7 @@ class MoELayer:
         R = T * k
         self.R = R
         self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev)
-        self.out_dtype = torch.float32 if cfg.operand_dtype == "bf16" else torch.bfloat16
+        self.out_dtype = torch.float32 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else torch.bfloat16
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
         # shared experts: their own weights and buckets (every token in each)
@@ -405,6 +407,7 @@ class MoELayer:
             ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,
                                 x=None if self.gather else x)
             xg = x if self.gather else None
+        self.last_offsets = ind["offsets"]
         if mark:
             mark(2)
         O = grouped_ffn(ind["offsets"], self.R, self.w, x_perm=ind.get("x_perm"),

@@ -181,6 +181,8 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t D, int32_t dtype) {
     return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 127) / 128) * 4, 256);
   if (dtype == MOE_DTYPE_MXFP4_W4A8)  // A codes, then one E8M0 byte per 32 columns
     return round_up((int64_t)max_rows * D, 256) + round_up((int64_t)max_rows * ((D + 31) / 32), 256);
+  if (dtype == MOE_DTYPE_MXFP4_W4A16)  // A in bf16
+    return round_up((int64_t)max_rows * D * 2, 256);
   // bf16: A, then the down GEMM's split-K counters and partial tiles
   return round_up((int64_t)max_rows * D * 2, 256) + moe::SPLIT_COUNTERS * 4 +
          (int64_t)moe::split_slots_for(max_rows) * moe::SPLIT_TILE_FLOATS * 4;
@@ -195,8 +197,8 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn: n_local_experts must be in [1, 1024] (got %d)", L);
   REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn: expert_offsets is required");
   REQUIRE(a->operand_dtype == MOE_DTYPE_BF16 || a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128 ||
-              a->operand_dtype == MOE_DTYPE_MXFP4_W4A8,
-          "moe_grouped_ffn: operand_dtype must be BF16, FP8_E4M3_BLOCK128 or MXFP4_W4A8");
+              a->operand_dtype == MOE_DTYPE_MXFP4_W4A8 || a->operand_dtype == MOE_DTYPE_MXFP4_W4A16,
+          "moe_grouped_ffn: operand_dtype must be BF16, FP8_E4M3_BLOCK128, MXFP4_W4A8 or MXFP4_W4A16");
   REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI ||
               a->activation == MOE_ACT_GELU_TANH,
           "moe_grouped_ffn: unknown activation %d", a->activation);
@@ -230,13 +232,16 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   if (a->act_workspace_bytes < need || (need > 0 && a->act_workspace == nullptr))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn: act_workspace needs %lld bytes (got %lld)",
                 (long long)need, (long long)a->act_workspace_bytes);
-  if (a->operand_dtype == MOE_DTYPE_MXFP4_W4A8) {
+  if (a->operand_dtype == MOE_DTYPE_MXFP4_W4A8 || a->operand_dtype == MOE_DTYPE_MXFP4_W4A16) {
+    const bool a16 = a->operand_dtype == MOE_DTYPE_MXFP4_W4A16;
     REQUIRE(H % 128 == 0 && D % 128 == 0, "moe_grouped_ffn: MX needs hidden_dim and moe_dim multiples of 128");
-    REQUIRE(a->x_perm_scale != nullptr && (a->x_perm != nullptr || a->x != nullptr),
+    REQUIRE(a16 || (a->x_perm_scale != nullptr && (a->x_perm != nullptr || a->x != nullptr)),
             "moe_grouped_ffn: MX takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
+    REQUIRE(!a16 || a->x_perm_scale == nullptr, "moe_grouped_ffn: W4A16 takes bf16 activations, no x_perm_scale");
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn: MXFP4 weights need w_gate_up_scale and w_down_scale");
-    REQUIRE((int64_t)R * H < ((int64_t)1 << 32) && (int64_t)R * D < ((int64_t)1 << 32) &&
+    const int64_t es = a16 ? 2 : 1;   // bytes per activation element
+    REQUIRE((int64_t)R * H * es < ((int64_t)1 << 32) && (int64_t)R * D * es < ((int64_t)1 << 32) &&
                 (int64_t)D * H < ((int64_t)1 << 32),
             "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
     REQUIRE(aligned16(a->b_gate_up) && aligned16(a->b_down), "moe_grouped_ffn: biases must be 16-byte aligned");
@@ -269,6 +274,7 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.out = a->expert_out;
     q.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
     q.events = (hipEvent_t const*)a->timing_events;
+    if (a16) return hip_status(moe::launch_ffn_w4a16(q, (hipStream_t)stream), "moe_grouped_ffn");
     return hip_status(moe::launch_ffn_mx(q, (hipStream_t)stream), "moe_grouped_ffn");
   }
   if (a->operand_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128) {

@@ -100,24 +100,27 @@ __device__ __forceinline__ int mx_shared_exp(float m) {
 // 2^-X for X in [-127, 120]: a normal float built from its exponent field.
 __device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
 
-template <int MODE, int ACT, int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(X_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void grouped_gemm_mx_kernel(const MxGemmArgs p) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  int32_t* s_mbp = (int32_t*)smem;  // m-block prefix, before the stage buffers are filled
+struct MxTile {
+  int e, nb, mb, row_beg, row_end;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / X_WAVES_N, wn = wave % X_WAVES_N;
-  const int L = p.L;
-
-  // ---- prefix of 256-row blocks per expert (wave 0), in LDS
+// Maps this workgroup to its tile over the experts' BM-row blocks: the
+// prefix of blocks per expert is built in LDS (wave 0), tiles are taken in
+// expert-major, n-block, m-block order (m-blocks sharing a weight tile are
+// neighbours), and each XCD (workgroups are dealt to the 8 XCDs round-robin)
+// runs one contiguous range.  Called by the whole workgroup; false when the
+// workgroup has no tile.  On return every wave has read the prefix, so the
+// LDS may be overwritten.
+template <int BM>
+__device__ __forceinline__ bool mx_map_tile(const int32_t* offsets, int L, int NB, int32_t* s_mbp, MxTile& t) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (wave == 0) {
     const int per = (L + 63) / 64;
     const int e0 = lane * per;
     int sum = 0;
     for (int i = 0; i < per; ++i) {
       const int e = e0 + i;
-      if (e < L) sum += (p.offsets[e + 1] - p.offsets[e] + X_BM - 1) / X_BM;
+      if (e < L) sum += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
     }
     int inc = sum;
 #pragma unroll
@@ -130,38 +133,62 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
       const int e = e0 + i;
       if (e < L) {
         s_mbp[e] = run;
-        run += (p.offsets[e + 1] - p.offsets[e] + X_BM - 1) / X_BM;
+        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
       }
     }
     if (lane == 63) s_mbp[L] = inc;
   }
   __syncthreads();
-
-  constexpr int NBO = (MODE == MX_GATE_UP) ? X_BN / 2 : X_BN;  // output columns per tile
-  const int NB = (p.N + NBO - 1) / NBO;
   const int total = s_mbp[L] * NB;
   const int per_xcd = (total + 7) >> 3;
   const int slot = blockIdx.x >> 3;
-  if (slot >= per_xcd) return;
+  if (slot >= per_xcd) return false;
   const int tile = (blockIdx.x & 7) * per_xcd + slot;
-  if (tile >= total) return;
+  if (tile >= total) return false;
   int lo = 0, hi = L - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (s_mbp[mid] * NB <= tile) lo = mid;
     else hi = mid - 1;
   }
-  const int e = __builtin_amdgcn_readfirstlane(lo);
-  const int nmb = s_mbp[e + 1] - s_mbp[e];
-  const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[e] * NB);
-  const int nb = local / nmb, mb = local % nmb;
-  const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * X_BM);
-  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  t.e = __builtin_amdgcn_readfirstlane(lo);
+  const int nmb = s_mbp[t.e + 1] - s_mbp[t.e];
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[t.e] * NB);
+  t.nb = local / nmb;
+  t.mb = local % nmb;
+  t.row_beg = __builtin_amdgcn_readfirstlane(offsets[t.e] + t.mb * BM);
+  t.row_end = __builtin_amdgcn_readfirstlane(offsets[t.e + 1]);
+  __syncthreads();
+  return true;
+}
+
+// Grid of a launch: enough workgroups for every tile whatever the split of
+// max_rows over the experts (each non-empty expert adds at most one partial
+// m-block), rounded to a multiple of the 8 XCDs.
+inline int64_t mx_grid(int max_rows, int L, int BM, int N, int NBO) {
+  const int64_t nonempty = (int64_t)max_rows < L ? max_rows : L;
+  const int64_t mblocks = (max_rows + BM - 1) / BM + nonempty;
+  const int64_t NB = (N + NBO - 1) / NBO;
+  return ((mblocks * NB + 7) / 8) * 8;
+}
+
+template <int MODE, int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(X_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_mx_kernel(const MxGemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int32_t* s_mbp = (int32_t*)smem;  // m-block prefix, before the stage buffers are filled
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / X_WAVES_N, wn = wave % X_WAVES_N;
+  constexpr int NBO = (MODE == MX_GATE_UP) ? X_BN / 2 : X_BN;  // output columns per tile
+  const int NB = (p.N + NBO - 1) / NBO;
+  MxTile t;
+  if (!mx_map_tile<X_BM>(p.offsets, p.L, NB, s_mbp, t)) return;
+  const int e = t.e, nb = t.nb, row_beg = t.row_beg, row_end = t.row_end;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm_s = wave_s / X_WAVES_N;
   const int KT = p.K / X_BK;        // K is a multiple of 128
   const uint32_t srow = (uint32_t)p.K / 32u;  // scale bytes per row
-  __syncthreads();  // every wave has read the prefix before the loads overwrite it
 
   // weight row of B tile row trow: wave column q owns 32 gate rows then the
   // matching 32 up rows (gate_up), or 64 consecutive rows (down)
@@ -375,16 +402,276 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
   }
 }
 
+// ------------------------------------------------------------------ W4A16
+// MXFP4 weights with bf16 activations: the weights are dequantised to bf16 in
+// registers, per MFMA fragment, by v_cvt_scalef32_pk_bf16_fp4 (two E2M1 codes
+// of a byte times an fp32 scale -> two bf16, exact for every E8M0 scale), and
+// the product runs on v_mfma_f32_32x32x16_bf16.  Tile 128 x 256 (the format
+// serves weight-bound batches first), 8 waves in 2 x 4, each 64 x 64 = 2 x 2
+// MFMA blocks; k stages of 128 triple buffered in LDS: 32 KB of bf16 rows,
+// 16 KB of packed e2m1 rows and the weight rows' 4 scale bytes.
+//
+// Inside a stage the 8 k16 steps need not walk k in order, only the same way
+// for both operands: at step s lane 32h + r takes k [64h + 8s, +8).  Its 8
+// weights then come from one MX block (2h + s/4), from dword s%4 of the
+// 16-byte chunk 2h + s/4 of its weight row, and its 8 activations are chunk
+// 8h + s of the 256-byte activation row.
+constexpr int W_BM = 128, W_BN = 256, W_BK = 128;
+constexpr int W_WTM = W_BM / X_WAVES_M, W_WTN = W_BN / X_WAVES_N;   // 64 x 64
+constexpr int W_MI = W_WTM / 32, W_NI = W_WTN / 32;                 // 2 x 2
+constexpr int W_A_ROW = W_BK * 2;                                   // bytes per bf16 stage row
+constexpr int W_A_BYTES = W_BM * W_A_ROW;                           // 32 KB
+constexpr int W_B_ROW = W_BK / 2;
+constexpr int W_B_BYTES = W_BN * W_B_ROW;                           // 16 KB
+constexpr int W_BS_OFF = W_A_BYTES + W_B_BYTES;
+constexpr int W_STAGE_BYTES = W_BS_OFF + W_BN * 4;                  // 49 KB
+constexpr int W_LPW_A = W_A_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 4
+constexpr int W_LPW_B = W_B_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 2
+constexpr int W_LOADS = W_LPW_A + W_LPW_B + 1;
+constexpr int W_LDS_PIPE = X_NSTAGE * W_STAGE_BYTES;                // 147 KB
+
+// bf16 rows: 256 bytes, 16 chunks; chunk c of row r at c ^ (r & 15).
+__device__ __forceinline__ int w4_a_off(int row, int chunk) { return row * W_A_ROW + ((chunk ^ (row & 15)) << 4); }
+
+struct W4GemmArgs {
+  const int32_t* offsets;
+  int L;
+  int K, N;
+  const uint16_t* A;         // bf16 [rows, K] (or per token, gathered)
+  const int32_t* gather;
+  const uint8_t* W;          // packed e2m1, OUT_IN per expert [w_rows, K/2]
+  int64_t w_estride;
+  const uint8_t* W_scale;    // E8M0 per expert [w_rows, K/32]
+  int64_t ws_estride;
+  const uint16_t* bias;
+  int64_t bias_estride;
+  const float* escale;
+  float alpha, limit;
+  void* out;                 // gate_up: bf16 [rows, D]; down: bf16 / fp32 [rows, H]
+};
+
+// E8M0 byte -> the fp32 2^(s-127) (s = 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_f32(uint32_t s) {
+  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+template <int MODE, int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(X_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / X_WAVES_N, wn = wave % X_WAVES_N;
+  constexpr int NBO = (MODE == MX_GATE_UP) ? W_BN / 2 : W_BN;
+  const int NB = (p.N + NBO - 1) / NBO;
+  MxTile t;
+  if (!mx_map_tile<W_BM>(p.offsets, p.L, NB, (int32_t*)smem, t)) return;
+  const int e = t.e, nb = t.nb, row_beg = t.row_beg, row_end = t.row_end;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int wm_s = wave_s / X_WAVES_N;
+  const int KT = p.K / W_BK;
+  const uint32_t srow = (uint32_t)p.K / 32u;
+
+  auto w_row = [&](int trow) {
+    if (MODE == MX_DOWN) return min(nb * W_BN + trow, p.N - 1);
+    const int q = trow / W_WTN, rr = trow % W_WTN, isup = rr / (W_WTN / 2), j = rr % (W_WTN / 2);
+    const int oc = min(nb * NBO + q * (W_WTN / 2) + j, p.N - 1);
+    return (FMT == 0) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
+  };
+
+  // ---- loader.  A: 1 KB = 4 rows x 16 chunks; B: 16 rows x 4 chunks; the
+  // weight rows' scale dwords: lanes 0..31 of wave w, rows 32w + lane.
+  const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
+  const uint8_t* WSexp = p.W_scale + (int64_t)e * p.ws_estride;
+  uint32_t a_voff[W_LPW_A], b_voff[W_LPW_B];
+#pragma unroll
+  for (int i = 0; i < W_LPW_A; ++i) {
+    const int trow = (wave * W_LPW_A + i) * 4 + (lane >> 4);
+    const int r = min(row_beg + trow, row_end - 1);
+    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+    a_voff[i] = ar * (uint32_t)p.K * 2u + (uint32_t)(((lane & 15) ^ (trow & 15)) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < W_LPW_B; ++i) {
+    const int trow = (wave * W_LPW_B + i) * 16 + (lane >> 2);
+    b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)p.K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+  }
+  const uint32_t bs_voff = (uint32_t)w_row(wave * 32 + (lane & 31)) * srow;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, X_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)WSexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
+
+  auto stage_base = [&](int kt) { return smem + (kt % X_NSTAGE) * W_STAGE_BYTES; };
+  auto issue = [&](int kt) {
+    uint8_t* st = stage_base(kt);
+#pragma unroll
+    for (int i = 0; i < W_LPW_A; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (wave_s * W_LPW_A + i) * 1024), 16, a_voff[i],
+                                               kt * W_A_ROW, 0, 0);
+#pragma unroll
+    for (int i = 0; i < W_LPW_B; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + W_A_BYTES + (wave_s * W_LPW_B + i) * 1024), 16,
+                                               b_voff[i], kt * W_B_ROW, 0, 0);
+    if (lane < 32)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + W_BS_OFF + wave_s * 128), 4, bs_voff, kt * 4, 0, 0);
+  };
+
+  const int fr = lane & 31, fh = lane >> 5;
+  f32x16_t acc[W_MI][W_NI];
+#pragma unroll
+  for (int mi = 0; mi < W_MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < W_NI; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
+  const int live_mi = min(max((row_end - (row_beg + wm_s * W_WTM) + 31) / 32, 0), W_MI);
+
+  issue(0);
+  if (KT > 1) issue(1);
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W_LOADS));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    mx_block_barrier();
+    if (kt + 2 < KT) issue(kt + 2);
+    const uint8_t* st = stage_base(kt);
+    const uint32_t* bs_l = (const uint32_t*)(st + W_BS_OFF);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {     // steps 4*half .. 4*half+3: one weight chunk, one MX block
+      u32x4_t wq[W_NI];
+      float wsc[W_NI];
+#pragma unroll
+      for (int ni = 0; ni < W_NI; ++ni) {
+        const int row = wn * W_WTN + ni * 32 + fr;
+        wq[ni] = *(const u32x4_t*)(st + W_A_BYTES + mx_b_off(row, 2 * fh + half));
+        wsc[ni] = e8m0_f32((bs_l[row] >> (8 * (2 * fh + half))) & 0xffu);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int s = 4 * half + j;
+        bf16x8_t bw[W_NI];
+#pragma unroll
+        for (int ni = 0; ni < W_NI; ++ni) {
+          const uint32_t d = wq[ni][j];
+          const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 0);
+          const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 1);
+          const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 2);
+          const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 3);
+          bw[ni] = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+#pragma unroll
+        for (int mi = 0; mi < W_MI; ++mi) {
+          if (mi < live_mi) {
+            const int row = wm * W_WTM + mi * 32 + fr;
+            const bf16x8_t af = *(const bf16x8_t*)(st + w4_a_off(row, 8 * fh + s));
+#pragma unroll
+            for (int ni = 0; ni < W_NI; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[ni], af, acc[mi][ni], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- epilogue.  acc[mi][ni][4q + c] is C[row][col] with
+  //   row = wm*64 + mi*32 + fr,  col = wn*64 + ni*32 + 8q + 4fh + c
+  const float sc = p.escale ? p.escale[e] : 1.0f;
+  const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
+  if (MODE == MX_GATE_UP) {
+    uint16_t* out = (uint16_t*)p.out;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fh;  // first of 4 outputs
+      float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (bias_e) {
+        if (FMT == 0) {
+          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
+          bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
+          bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
+          bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
+          bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
+        } else {
+          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bg[c] = bf16_to_f32(b4[c] & 0xffffu);
+            bu[c] = bf16_to_f32(b4[c] >> 16);
+          }
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < W_MI; ++mi) {
+        const int row = row_beg + wm * W_WTM + mi * 32 + fr;
+        if (row >= row_end) continue;
+        float a[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          a[c] = gated_act<ACT>(acc[mi][0][4 * q + c] * sc + bg[c], acc[mi][1][4 * q + c] * sc + bu[c], p.alpha,
+                                p.limit);
+        uint2 v;
+        v.x = pack_bf16x2_rne(a[0], a[1]);
+        v.y = pack_bf16x2_rne(a[2], a[3]);
+        *(uint2*)(out + (int64_t)row * p.N + oc) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int ni = 0; ni < W_NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = nb * W_BN + wn * W_WTN + ni * 32 + 8 * q + 4 * fh;
+        if (n >= p.N) continue;
+        float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e) {
+          const uint2 b2 = *(const uint2*)(bias_e + n);
+          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+        }
+#pragma unroll
+        for (int mi = 0; mi < W_MI; ++mi) {
+          const int row = row_beg + wm * W_WTM + mi * 32 + fr;
+          if (row >= row_end) continue;
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
+          if (OUT_BF16) {
+            uint2 w;
+            w.x = pack_bf16x2_rne(v[0], v[1]);
+            w.y = pack_bf16x2_rne(v[2], v[3]);
+            *(uint2*)((uint16_t*)p.out + (int64_t)row * p.N + n) = w;
+          } else {
+            const f32x4_t w = {v[0], v[1], v[2], v[3]};
+            *(f32x4_t*)((float*)p.out + (int64_t)row * p.N + n) = w;
+          }
+        }
+      }
+  }
+}
+
+template <typename KernelT>
+hipError_t launch_w4(KernelT kern, const W4GemmArgs& a, int max_rows, int NBO, hipStream_t st) {
+  const int prefix = (a.L + 1) * (int)sizeof(int32_t);
+  const int lds = W_LDS_PIPE > prefix ? W_LDS_PIPE : prefix;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t grid = mx_grid(max_rows, a.L, W_BM, a.N, NBO);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  kern<<<(unsigned)grid, X_NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_w4_gate_up(const W4GemmArgs& g, int fmt, int max_rows, hipStream_t st) {
+  if (fmt == 0) return launch_w4(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 0, true>, g, max_rows, W_BN / 2, st);
+  return launch_w4(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 1, true>, g, max_rows, W_BN / 2, st);
+}
+
 template <typename KernelT>
 hipError_t launch_mx(KernelT kern, const MxGemmArgs& a, int max_rows, int NBO, hipStream_t st) {
   const int prefix = (a.L + 1) * (int)sizeof(int32_t);
   const int lds = X_LDS_PIPE > prefix ? X_LDS_PIPE : prefix;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
-  const int64_t nonempty = (int64_t)max_rows < a.L ? max_rows : a.L;
-  const int64_t mblocks = (max_rows + X_BM - 1) / X_BM + nonempty;
-  const int64_t NB = (a.N + NBO - 1) / NBO;
-  const int64_t grid = ((mblocks * NB + 7) / 8) * 8;
+  const int64_t grid = mx_grid(max_rows, a.L, X_BM, a.N, NBO);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   kern<<<(unsigned)grid, X_NT, lds, st>>>(a);
@@ -398,6 +685,53 @@ hipError_t launch_mx_gate_up(const MxGemmArgs& g, int fmt, int max_rows, hipStre
 }
 
 }  // namespace
+
+hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
+  hipError_t err;
+  if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
+  W4GemmArgs g{};
+  g.offsets = q.offsets;
+  g.L = q.L;
+  g.K = q.H;
+  g.N = q.D;
+  g.A = (const uint16_t*)q.x_perm;
+  g.gather = q.sorted_token;
+  g.W = q.w_gate_up;
+  g.w_estride = (int64_t)2 * q.D * (q.H / 2);
+  g.W_scale = q.w_gate_up_scale;
+  g.ws_estride = (int64_t)2 * q.D * (q.H / 32);
+  g.bias = q.b_gate_up;
+  g.bias_estride = (int64_t)2 * q.D;
+  g.escale = q.gate_up_scales;
+  g.alpha = q.alpha;
+  g.limit = q.limit;
+  g.out = q.act;
+  if (q.act_kind == ACT_SILU) err = launch_w4_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st);
+  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_w4_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st);
+  else err = launch_w4_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st);
+  if (err != hipSuccess) return err;
+  if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
+  W4GemmArgs d{};
+  d.offsets = q.offsets;
+  d.L = q.L;
+  d.K = q.D;
+  d.N = q.H;
+  d.A = (const uint16_t*)q.act;
+  d.W = q.w_down;
+  d.w_estride = (int64_t)q.H * (q.D / 2);
+  d.W_scale = q.w_down_scale;
+  d.ws_estride = (int64_t)q.H * (q.D / 32);
+  d.bias = q.b_down;
+  d.bias_estride = q.H;
+  d.escale = q.down_scales;
+  d.out = q.out;
+  if (q.out_bf16)
+    err = launch_w4(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, true>, d, q.max_rows, W_BN, st);
+  else
+    err = launch_w4(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, false>, d, q.max_rows, W_BN, st);
+  if (err == hipSuccess && q.events) err = hipEventRecord(q.events[2], st);
+  return err;
+}
 
 hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {
   hipError_t err;

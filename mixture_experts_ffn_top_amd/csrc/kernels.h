@@ -107,6 +107,9 @@ struct FfnMxParams {
   hipEvent_t const* events;
 };
 hipError_t launch_ffn_mx(const FfnMxParams& p, hipStream_t st);
+// MXFP4 weights x bf16 activations (W4A16): x_perm / act are bf16, no
+// activation scales; the same weight fields.
+hipError_t launch_ffn_w4a16(const FfnMxParams& p, hipStream_t st);
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,

@@ -477,7 +477,7 @@ def _expert_weights_f64(inp, e, operand, suffix=""):
     W_gate_up [H, 2D] and W_down [D, H].  MXFP4 weights arrive as rows along
     the reduction dimension (the MX blocks run along it): gate_up codes
     [2D, H/2] with scales [2D, H/32], down codes [H, D/2] with [H, D/32]."""
-    if operand == "mxfp4":
+    if operand in ("mxfp4", "mxfp4_a16"):
         wgu = mx_dequant_fp4(inp["w_gate_up" + suffix][e], inp["w_gate_up" + suffix + "_scale"][e]).T
         wd = mx_dequant_fp4(inp["w_down" + suffix][e], inp["w_down" + suffix + "_scale"][e]).T
         return wgu, wd
@@ -491,7 +491,7 @@ def _expert_weights_f64(inp, e, operand, suffix=""):
 
 
 # how the layer stores the intermediate A, per operand type
-_ACT_FORMAT = {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp8"}
+_ACT_FORMAT = {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp8", "mxfp4_a16": "bf16"}
 
 
 def shared_weights(cfg, sink_weights, T):

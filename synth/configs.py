@@ -31,6 +31,7 @@ class MoEConfig:
     alpha: float = 0.0
     limit: float = 0.0
     operand_dtype: str = "bf16"  # "bf16" | "fp8" | "mxfp4" (MXFP4 weights, MXFP8 activations: W4A8)
+                                 # | "mxfp4_a16" (MXFP4 weights, bf16 activations: W4A16)
     route_scale: float = 1.0
     global_scale: float = 1.0
     logit_std: float = 2.0      # sigmoid router: logits are an input ~N(0, logit_std)
@@ -65,6 +66,11 @@ CONFIGS = {
     # MXFP4 weights with MXFP8 activations)
     6: MoEConfig(6, "mxfp4", T=16384, H=7168, E=256, k=8, D=2048,
                  router="sigmoid_sink", s=0, operand_dtype="mxfp4",
+                 route_scale=1.0, global_scale=1.0),
+    # the same experts run W4A16 on a decode-sized batch, where the layer is
+    # bound by streaming the 4-bit weights
+    7: MoEConfig(7, "mxfp4_a16", T=256, H=7168, E=256, k=8, D=2048,
+                 router="sigmoid_sink", s=0, operand_dtype="mxfp4_a16",
                  route_scale=1.0, global_scale=1.0),
 }
 

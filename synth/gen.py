@@ -95,7 +95,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
             wgu[e] = _normal((H, 2 * D), cfg.w_std, d, c, 3, e, salt).to(torch.bfloat16)
             wd[e] = _normal((D, H), cfg.w_std, d, c, 4, e, salt).to(torch.bfloat16)
         out["w_gate_up"], out["w_down"] = wgu, wd
-    elif cfg.operand_dtype == "mxfp4":
+    elif cfg.operand_dtype in ("mxfp4", "mxfp4_a16"):
         assert H % 32 == 0 and D % 32 == 0
         wgu = torch.empty((E, 2 * D, H // 2), device=d, dtype=torch.uint8)
         wgus = torch.empty((E, 2 * D, H // 32), device=d, dtype=torch.uint8)
@@ -121,7 +121,7 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
         out["b_gate_up"] = _normal((E, 2 * D), cfg.w_std, d, c, 5, 0, salt).to(torch.bfloat16)
         out["b_down"] = _normal((E, H), cfg.w_std, d, c, 6, 0, salt).to(torch.bfloat16)
     if cfg.n_shared:
-        assert cfg.operand_dtype != "mxfp4", "shared experts are bf16 or fp8"
+        assert cfg.operand_dtype in ("bf16", "fp8"), "shared experts are bf16 or fp8"
         # shared experts: the same gated MLP with moe_dim = shared_dim, in the
         # layer's operand dtype (tensor ids 7..10, one stream per shared expert)
         S, Ds = cfg.n_shared, cfg.shared_dim

@@ -624,3 +624,28 @@ def test_mx_layer_full_size(moe):
     _, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=6), FP8_TOL)
+
+
+@pytest.mark.parametrize("changes,nsample,gather", [
+    ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, True),
+    ({"T": 300, "E": 5, "k": 2, "H": 384, "D": 128}, 300, False),   # one k stage in the down GEMM
+    ({"T": 777, "E": 6, "k": 4, "H": 384, "D": 640, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, 777, True),
+    ({"T": 64, "E": 32, "k": 4, "H": 1024, "D": 512, "activation": "gelu_tanh", "has_bias": True}, 64, True),
+])
+def test_mx_w4a16_layer_small(moe, changes, nsample, gather):
+    cfg = synth.scaled(synth.get_config(7), **changes)
+    inp = _gen(cfg)
+    say(f"[mx w4a16 layer] {changes} gather={gather}")
+    _, res = _run_layer(moe, cfg, inp, gather=gather)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=7), BF16_TOL)
+
+
+def test_mx_w4a16_layer_full_size(moe):
+    cfg = synth.get_config(7)
+    inp = _gen(cfg)
+    say("[mx w4a16 layer full] T=256 H=7168 E=256 k=8 D=2048 MXFP4 W4A16")
+    _, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 8, seed=8), BF16_TOL)

@@ -510,7 +510,7 @@ def test_tokens_subset_and_mask_and_local_slice():
 
 def test_small_configs_run_end_to_end():
     import synth
-    for cid in (1, 3, 4, 6):
+    for cid in (1, 3, 4, 6, 7):
         cfg = synth.scaled(synth.get_config(cid), T=16)
         inp = synth.to_host(synth.make_inputs(synth.scaled(cfg, H=min(cfg.H, 256), D=min(cfg.D, 256), E=min(cfg.E, 16)), "cpu"))
         c2 = synth.scaled(cfg, H=min(cfg.H, 256), D=min(cfg.D, 256), E=min(cfg.E, 16))
@@ -760,4 +760,33 @@ def test_mxfp4_layer_uses_dequantised_operands():
             ac, asc = O.mxfp8_quantize_rows(a)
             aq = O.e4m3_decode(ac) * np.repeat(torch.from_numpy(asc).view(torch.float8_e8m0fnu).double().numpy(), 32, axis=1)
             acc += w[t, j] * (aq @ deq(wd[e], wds[e]).T)[0]
+        assert np.allclose(y[t], acc, rtol=1e-12, atol=1e-12)
+
+
+def test_mxfp4_w4a16_layer_uses_bf16_activations():
+    """W4A16: the same MXFP4 weights times the bf16 activations, A stored as
+    bf16 -- the plain MLP on element-wise dequantised weights."""
+    rng = np.random.default_rng(34)
+    T, H, D, E, k = 4, 64, 32, 2, 2
+    x = O.bf16_round(rng.standard_normal((T, H)))
+    wgu = rng.integers(0, 256, (E, 2 * D, H // 2), dtype=np.uint8)
+    wgus = rng.integers(118, 123, (E, 2 * D, H // 32), dtype=np.uint8)
+    wd = rng.integers(0, 256, (E, H, D // 2), dtype=np.uint8)
+    wds = rng.integers(118, 123, (E, H, D // 32), dtype=np.uint8)
+    inp = {"x": x, "w_gate_up": wgu, "w_gate_up_scale": wgus, "w_down": wd, "w_down_scale": wds}
+    cfg = _Cfg(T=T, H=H, E=E, k=k, D=D, operand_dtype="mxfp4_a16")
+    idx = np.array([[0, 1], [1, 0], [0, 1], [1, 0]], np.int32)
+    w = rng.random((T, k))
+    y = O.layer(inp, cfg, indices=idx, weights=w)
+    for t in range(T):
+        acc = np.zeros(H)
+        for j in range(k):
+            e = idx[t, j]
+            wg = np.array([[float(O.e2m1_decode(np.array([(int(wgu[e, n, kk // 2]) >> (4 * (kk % 2))) & 15]))[0])
+                            * 2.0 ** (int(wgus[e, n, kk // 32]) - 127) for kk in range(H)] for n in range(2 * D)])
+            wdd = np.array([[float(O.e2m1_decode(np.array([(int(wd[e, n, kk // 2]) >> (4 * (kk % 2))) & 15]))[0])
+                             * 2.0 ** (int(wds[e, n, kk // 32]) - 127) for kk in range(D)] for n in range(H)])
+            h = x[t:t + 1].astype(np.float64) @ wg.T
+            a = O.bf16_round(O.gated_activation(h[:, :D], h[:, D:], "silu")).astype(np.float64)
+            acc += w[t, j] * (a @ wdd.T)[0]
         assert np.allclose(y[t], acc, rtol=1e-12, atol=1e-12)
