@@ -94,9 +94,19 @@ PROFILE_CMDS = """# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp
 #       python3 $REPO/bench.py --copy-calibration        (and WRITE_SIZE into .../copy_WRITE_SIZE)
 #   python3 bench.py --summarize-profile gpurun_out/prof    (writes the files under profiles/)"""
 
+# the MX workloads' kernel traces, summarised by the same --summarize-profile call
+EXTRA_TRACES = [
+    ("trace6", 6, "mxfp4_w4a8_layer_kernel_stats.txt",
+     "MXFP4 x MXFP8 (W4A8) layer: T=16384 tokens, hidden 7168, 256 experts, top-8 sigmoid router, "
+     "moe_dim 2048, SiLU"),
+    ("trace7", 7, "mxfp4_w4a16_decode_kernel_stats.txt",
+     "MXFP4 W4A16 layer on a decode-sized batch: T=256 tokens, hidden 7168, 256 experts, top-8 sigmoid "
+     "router, moe_dim 2048, SiLU"),
+]
+
 
 def _short(name: str) -> str:
-    name = name.strip('"')
+    name = name.strip('"').replace("(anonymous namespace)::", "")
     return name.split("(")[0].replace("void ", "")
 
 
@@ -127,6 +137,30 @@ def summarize_profile(d: str):
     out += ["", "# gate_up = grouped_gemm_bf16_kernel<0,...> (SiLU, concatenated, gathered x, bf16 out)",
             "# down    = grouped_gemm_bf16_kernel<1,...> (fp32 out)"]
     open(os.path.join(prof, "mixtral_layer_kernel_stats.txt"), "w").write("\n".join(out) + "\n")
+
+    for sub, cid, name, title in EXTRA_TRACES:
+        stats = os.path.join(d, sub, "bench_kernel_stats.csv")
+        if not os.path.exists(stats):
+            continue
+        rows = [r for r in csv.DictReader(open(stats)) if "moe::" in r["Name"]]
+        bd = {}
+        for ln in open(os.path.join(d, sub + ".log")):
+            if ln.startswith('{"metric"'):
+                bd = json.loads(ln)["breakdown_ms"]
+        out = [f"# rocprofv3 kernel statistics: {title}",
+               "# command (repo root as $REPO, run from /tmp with TMPDIR=/tmp):",
+               f"#   rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/{sub} -o bench -- \\",
+               f"#       python3 $REPO/bench.py --cfg {cid} --steps 10 --warmup 3 --no-cpu-baseline "
+               f"> $REPO/gpurun_out/prof/{sub}.log",
+               "#   python3 bench.py --summarize-profile gpurun_out/prof",
+               "# calls = warmup + timed steps.  Durations in microseconds; only this library's kernels.",
+               f"# bench.py's own HIP-event timing in the same run: gate_up {bd.get('gate_up', 0) * 1e3:.1f} us, "
+               f"down {bd.get('down', 0) * 1e3:.1f} us per launch.", "",
+               f"{'kernel':58s}{'calls':>7s}{'avg_us':>10s}{'min_us':>10s}{'max_us':>10s}"]
+        for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+            out.append(f"{_short(r['Name']):58s}{int(r['Calls']):7d}{float(r['AverageNs']) / 1e3:10.1f}"
+                       f"{float(r['MinNs']) / 1e3:10.1f}{float(r['MaxNs']) / 1e3:10.1f}")
+        open(os.path.join(prof, name), "w").write("\n".join(out) + "\n")
 
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated on a plain copy of known size
     def counters(path):
