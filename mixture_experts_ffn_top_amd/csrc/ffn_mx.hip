@@ -57,6 +57,10 @@ constexpr int X_LOADS = X_LPW_A + X_LPW_B + 2;             // per wave per stage
 constexpr int X_LDS_PIPE = X_NSTAGE * X_STAGE_BYTES;       // 150 KB
 
 constexpr int X_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
+// A byte offset past every buffer's 0x7fffffff-byte range (also with a stage's
+// k offset added): such a buffer load returns zeros without touching memory,
+// and still counts as one load for the stage's vmcnt bookkeeping.
+constexpr uint32_t X_OOB = 0x80000000u;
 
 // e4m3 rows: 128 bytes, 8 chunks; chunk c of row r at c ^ fa(r).
 __device__ __forceinline__ int mx_fa(int r) { return (r ^ (r >> 3)) & 7; }
@@ -201,17 +205,22 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 
   // ---- loader.  A: 1 KB = 8 rows x 8 chunks per instruction; B: 16 rows x
   // 4 chunks.  Per-lane offsets fixed for the tile, the k offset of a stage in
-  // the scalar offset, the LDS destination in M0.  Rows past the expert's
-  // last row (or past N) repeat it; their results are never stored.
+  // the scalar offset, the LDS destination in M0.  A rows past the expert's
+  // last row read zeros; weight rows past N repeat the last one.  Neither
+  // result is ever stored.
   const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
   const uint8_t* WSexp = p.W_scale + (int64_t)e * p.ws_estride;
   uint32_t a_voff[X_LPW_A], b_voff[X_LPW_B];
 #pragma unroll
   for (int i = 0; i < X_LPW_A; ++i) {
     const int trow = (wave * X_LPW_A + i) * 8 + (lane >> 3);
-    const int r = min(row_beg + trow, row_end - 1);
-    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
-    a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
+    const int r = row_beg + trow;
+    if (r < row_end) {
+      const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+      a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
+    } else {
+      a_voff[i] = X_OOB;   // past the expert's rows: reads zeros, moves no memory
+    }
   }
 #pragma unroll
   for (int i = 0; i < X_LPW_B; ++i) {
@@ -416,19 +425,33 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 // weights then come from one MX block (2h + s/4), from dword s%4 of the
 // 16-byte chunk 2h + s/4 of its weight row, and its 8 activations are chunk
 // 8h + s of the 256-byte activation row.
-constexpr int W_BM = 128, W_BN = 256, W_BK = 128;
-constexpr int W_WTM = W_BM / X_WAVES_M, W_WTN = W_BN / X_WAVES_N;   // 64 x 64
-constexpr int W_MI = W_WTM / 32, W_NI = W_WTN / 32;                 // 2 x 2
+// Two shapes: 128-row tiles with 8 waves (2 x 4) and 3 stages, and, for
+// batches of a few rows per expert (decode), 32-row tiles with 4 waves and 6
+// stages, which keeps five 17 KB weight stages in flight per CU where the
+// larger tile could hold two: that batch is bound by streaming the weights
+// from HBM, so what counts is the bytes in flight.
+constexpr int W_BN = 256, W_BK = 128;
 constexpr int W_A_ROW = W_BK * 2;                                   // bytes per bf16 stage row
-constexpr int W_A_BYTES = W_BM * W_A_ROW;                           // 32 KB
 constexpr int W_B_ROW = W_BK / 2;
 constexpr int W_B_BYTES = W_BN * W_B_ROW;                           // 16 KB
-constexpr int W_BS_OFF = W_A_BYTES + W_B_BYTES;
-constexpr int W_STAGE_BYTES = W_BS_OFF + W_BN * 4;                  // 49 KB
-constexpr int W_LPW_A = W_A_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 4
-constexpr int W_LPW_B = W_B_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 2
-constexpr int W_LOADS = W_LPW_A + W_LPW_B + 1;
-constexpr int W_LDS_PIPE = X_NSTAGE * W_STAGE_BYTES;                // 147 KB
+
+template <int BM>
+struct W4Shape {
+  static constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = 4, NWAVES = WAVES_M * WAVES_N;
+  static constexpr int NT = 64 * NWAVES;
+  static constexpr int NS = BM >= 64 ? 3 : 6;                       // stages
+  static constexpr int WTM = BM / WAVES_M, WTN = W_BN / WAVES_N;    // wave tile, WTN = 64
+  static constexpr int MI = WTM / 32, NI = WTN / 32;
+  static constexpr int A_BYTES = BM * W_A_ROW;
+  static constexpr int BS_OFF = A_BYTES + W_B_BYTES;
+  static constexpr int STAGE = BS_OFF + W_BN * 4;
+  static constexpr int LPW_A = A_BYTES / 1024 / NWAVES, LPW_B = W_B_BYTES / 1024 / NWAVES;
+  static constexpr int BS_RPW = W_BN / NWAVES;                      // weight scale rows per wave
+  static constexpr int LOADS = LPW_A + LPW_B + 1;                   // per wave per stage
+  static constexpr int LDS = NS * STAGE;
+  static_assert(LPW_A >= 1 && LPW_B >= 1 && BS_RPW <= 64, "W4A16 tile shape");
+  static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+};
 
 // bf16 rows: 256 bytes, 16 chunks; chunk c of row r at c ^ (r & 15).
 __device__ __forceinline__ int w4_a_off(int row, int chunk) { return row * W_A_ROW + ((chunk ^ (row & 15)) << 4); }
@@ -455,19 +478,24 @@ __device__ __forceinline__ float e8m0_f32(uint32_t s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
-template <int MODE, int ACT, int FMT, bool OUT_BF16>
-__global__ __launch_bounds__(X_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int MODE, int ACT, int FMT, bool OUT_BF16, int W_BM>
+__global__ __launch_bounds__(W4Shape<W_BM>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
+  constexpr int W_WAVES_N = W4Shape<W_BM>::WAVES_N, W_WTM = W4Shape<W_BM>::WTM, W_WTN = W4Shape<W_BM>::WTN;
+  constexpr int W_MI = W4Shape<W_BM>::MI, W_NI = W4Shape<W_BM>::NI, W_NS = W4Shape<W_BM>::NS;
+  constexpr int W_A_BYTES = W4Shape<W_BM>::A_BYTES, W_BS_OFF = W4Shape<W_BM>::BS_OFF, W_STAGE = W4Shape<W_BM>::STAGE;
+  constexpr int W_LPW_A = W4Shape<W_BM>::LPW_A, W_LPW_B = W4Shape<W_BM>::LPW_B, W_LOADS = W4Shape<W_BM>::LOADS;
+  constexpr int W_BS_RPW = W4Shape<W_BM>::BS_RPW;
   extern __shared__ __align__(16) uint8_t smem[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / X_WAVES_N, wn = wave % X_WAVES_N;
+  const int wm = wave / W_WAVES_N, wn = wave % W_WAVES_N;
   constexpr int NBO = (MODE == MX_GATE_UP) ? W_BN / 2 : W_BN;
   const int NB = (p.N + NBO - 1) / NBO;
   MxTile t;
   if (!mx_map_tile<W_BM>(p.offsets, p.L, NB, (int32_t*)smem, t)) return;
   const int e = t.e, nb = t.nb, row_beg = t.row_beg, row_end = t.row_end;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int wm_s = wave_s / X_WAVES_N;
+  const int wm_s = wave_s / W_WAVES_N;
   const int KT = p.K / W_BK;
   const uint32_t srow = (uint32_t)p.K / 32u;
 
@@ -482,25 +510,33 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
   // weight rows' scale dwords: lanes 0..31 of wave w, rows 32w + lane.
   const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
   const uint8_t* WSexp = p.W_scale + (int64_t)e * p.ws_estride;
-  uint32_t a_voff[W_LPW_A], b_voff[W_LPW_B];
+  // fixed-size arrays (the lambdas below capture them; an array whose size
+  // depends on the template argument there stops clang from emitting the
+  // kernel's host stub)
+  static_assert(W_LPW_A <= 4 && W_LPW_B <= 4, "load counts");
+  uint32_t a_voff[4], b_voff[4];
 #pragma unroll
   for (int i = 0; i < W_LPW_A; ++i) {
     const int trow = (wave * W_LPW_A + i) * 4 + (lane >> 4);
-    const int r = min(row_beg + trow, row_end - 1);
-    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
-    a_voff[i] = ar * (uint32_t)p.K * 2u + (uint32_t)(((lane & 15) ^ (trow & 15)) * 16);
+    const int r = row_beg + trow;
+    if (r < row_end) {
+      const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+      a_voff[i] = ar * (uint32_t)p.K * 2u + (uint32_t)(((lane & 15) ^ (trow & 15)) * 16);
+    } else {
+      a_voff[i] = X_OOB;   // past the expert's rows: reads zeros, moves no memory
+    }
   }
 #pragma unroll
   for (int i = 0; i < W_LPW_B; ++i) {
     const int trow = (wave * W_LPW_B + i) * 16 + (lane >> 2);
     b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)p.K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
   }
-  const uint32_t bs_voff = (uint32_t)w_row(wave * 32 + (lane & 31)) * srow;
+  const uint32_t bs_voff = (uint32_t)w_row(wave * W_BS_RPW + lane % W_BS_RPW) * srow;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, X_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)WSexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
 
-  auto stage_base = [&](int kt) { return smem + (kt % X_NSTAGE) * W_STAGE_BYTES; };
+  auto stage_base = [&](int kt) { return smem + (kt % W_NS) * W_STAGE; };
   auto issue = [&](int kt) {
     uint8_t* st = stage_base(kt);
 #pragma unroll
@@ -511,8 +547,9 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
     for (int i = 0; i < W_LPW_B; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + W_A_BYTES + (wave_s * W_LPW_B + i) * 1024), 16,
                                                b_voff[i], kt * W_B_ROW, 0, 0);
-    if (lane < 32)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + W_BS_OFF + wave_s * 128), 4, bs_voff, kt * 4, 0, 0);
+    if (lane < W_BS_RPW)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + W_BS_OFF + wave_s * W_BS_RPW * 4), 4, bs_voff,
+                                               kt * 4, 0, 0);
   };
 
   const int fr = lane & 31, fh = lane >> 5;
@@ -525,13 +562,17 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
   const int live_mi = min(max((row_end - (row_beg + wm_s * W_WTM) + 31) / 32, 0), W_MI);
 
-  issue(0);
-  if (KT > 1) issue(1);
+  // stages 0 .. NS-2 in the prologue; iteration kt waits for stage kt (at
+  // most the NS-2 stages issued after it outstanding), publishes it, and
+  // issues stage kt+NS-1 into the buffer of stage kt-1
+#pragma unroll
+  for (int i = 0; i < W_NS - 1; ++i)
+    if (i < KT) issue(i);
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(W_LOADS));
+    if (kt + W_NS - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm((W_NS - 2) * W_LOADS));
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     mx_block_barrier();
-    if (kt + 2 < KT) issue(kt + 2);
+    if (kt + W_NS - 1 < KT) issue(kt + W_NS - 1);
     const uint8_t* st = stage_base(kt);
     const uint32_t* bs_l = (const uint32_t*)(st + W_BS_OFF);
 #pragma unroll
@@ -646,23 +687,24 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
   }
 }
 
-template <typename KernelT>
+template <int BM, typename KernelT>
 hipError_t launch_w4(KernelT kern, const W4GemmArgs& a, int max_rows, int NBO, hipStream_t st) {
   const int prefix = (a.L + 1) * (int)sizeof(int32_t);
-  const int lds = W_LDS_PIPE > prefix ? W_LDS_PIPE : prefix;
+  const int lds = W4Shape<BM>::LDS > prefix ? W4Shape<BM>::LDS : prefix;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
-  const int64_t grid = mx_grid(max_rows, a.L, W_BM, a.N, NBO);
+  const int64_t grid = mx_grid(max_rows, a.L, BM, a.N, NBO);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  kern<<<(unsigned)grid, X_NT, lds, st>>>(a);
+  kern<<<(unsigned)grid, W4Shape<BM>::NT, lds, st>>>(a);
   return hipGetLastError();
 }
 
-template <int ACT>
+template <int ACT, int BM>
 hipError_t launch_w4_gate_up(const W4GemmArgs& g, int fmt, int max_rows, hipStream_t st) {
-  if (fmt == 0) return launch_w4(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 0, true>, g, max_rows, W_BN / 2, st);
-  return launch_w4(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 1, true>, g, max_rows, W_BN / 2, st);
+  if (fmt == 0)
+    return launch_w4<BM>(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 0, true, BM>, g, max_rows, W_BN / 2, st);
+  return launch_w4<BM>(grouped_gemm_w4a16_kernel<MX_GATE_UP, ACT, 1, true, BM>, g, max_rows, W_BN / 2, st);
 }
 
 template <typename KernelT>
@@ -684,9 +726,8 @@ hipError_t launch_mx_gate_up(const MxGemmArgs& g, int fmt, int max_rows, hipStre
   return launch_mx(grouped_gemm_mx_kernel<MX_GATE_UP, ACT, 1, false>, g, max_rows, X_BN / 2, st);
 }
 
-}  // namespace
-
-hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
+template <int BM>
+hipError_t launch_ffn_w4a16_bm(const FfnMxParams& q, hipStream_t st) {
   hipError_t err;
   if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
   W4GemmArgs g{};
@@ -706,9 +747,9 @@ hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
   g.alpha = q.alpha;
   g.limit = q.limit;
   g.out = q.act;
-  if (q.act_kind == ACT_SILU) err = launch_w4_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st);
-  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_w4_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st);
-  else err = launch_w4_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st);
+  if (q.act_kind == ACT_SILU) err = launch_w4_gate_up<ACT_SILU, BM>(g, q.fmt, q.max_rows, st);
+  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_w4_gate_up<ACT_SWIGLUOAI, BM>(g, q.fmt, q.max_rows, st);
+  else err = launch_w4_gate_up<ACT_GELU_TANH, BM>(g, q.fmt, q.max_rows, st);
   if (err != hipSuccess) return err;
   if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
   W4GemmArgs d{};
@@ -726,11 +767,19 @@ hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
   d.escale = q.down_scales;
   d.out = q.out;
   if (q.out_bf16)
-    err = launch_w4(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, true>, d, q.max_rows, W_BN, st);
+    err = launch_w4<BM>(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, true, BM>, d, q.max_rows, W_BN, st);
   else
-    err = launch_w4(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, false>, d, q.max_rows, W_BN, st);
+    err = launch_w4<BM>(grouped_gemm_w4a16_kernel<MX_DOWN, ACT_SILU, 0, false, BM>, d, q.max_rows, W_BN, st);
   if (err == hipSuccess && q.events) err = hipEventRecord(q.events[2], st);
   return err;
+}
+
+}  // namespace
+
+// 32-row tiles when the batch averages at most 32 rows per expert
+hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
+  if ((int64_t)q.max_rows <= (int64_t)32 * q.L) return launch_ffn_w4a16_bm<32>(q, st);
+  return launch_ffn_w4a16_bm<128>(q, st);
 }
 
 hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {

@@ -632,6 +632,9 @@ def test_mx_layer_full_size(moe):
     ({"T": 777, "E": 6, "k": 4, "H": 384, "D": 640, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
       "gate_up_format": "interleaved", "has_bias": True}, 777, True),
     ({"T": 64, "E": 32, "k": 4, "H": 1024, "D": 512, "activation": "gelu_tanh", "has_bias": True}, 64, True),
+    # at most 32 rows per expert on average: the 32-row tile with the 6-stage pipeline
+    ({"T": 40, "E": 16, "k": 2, "H": 256, "D": 384, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, 40, False),
 ])
 def test_mx_w4a16_layer_small(moe, changes, nsample, gather):
     cfg = synth.scaled(synth.get_config(7), **changes)
