@@ -340,6 +340,20 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": "grouped gate_up GEMM + fused activation (MXFP4 weights, bf16 activations)",
                 "bytes_per_launch": gu_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_gu, 4)}
+    if getattr(cfg, "fused", False):
+        # the FFN is one launch (gate_up and down together) on a decode-sized
+        # batch: bound by streaming the bf16 weights of the experts that have
+        # rows, plus x rows in, A out and back in, O out
+        off = layer.last_offsets.cpu()
+        used = int(((off[1:] - off[:-1]) > 0).sum())
+        ffn_bytes = (used * (2 * cfg.D * cfg.H + cfg.H * cfg.D) * 2 + R * cfg.H * 2 + 2 * R * cfg.D * 2
+                     + R * cfg.H * 4)
+        t_ffn = t_gu + t_dn
+        gbs = ffn_bytes / (t_ffn * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "kernel": "single-launch expert FFN (gate_up + activation + down, bf16)",
+                "bytes_per_launch": ffn_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_ffn, 4)}
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),

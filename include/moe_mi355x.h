@@ -10,6 +10,7 @@
  *                      quantisation of the activations)
  *   moe_grouped_ffn    grouped gate_up GEMM with the gated activation fused
  *                      into its epilogue, then the grouped down GEMM
+ *                      (moe_grouped_ffn_fused: both legs in one launch)
  *   moe_combine        router-weighted sum of each token's expert rows
  *   moe_shared_indices buckets of the shared (sink-lane) experts: all tokens each
  *
@@ -258,7 +259,8 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
  *                  per-token scales [T, H/128] (MOE_DTYPE_FP8_E4M3_TOKENS);
  *                  for MX the MOE_DTYPE_MXFP8_TOKENS codes and scales
  *                  (x_perm / x, the activation buffer and one expert's
- *                  weights must each be under 4 GiB)
+ *                  weights must each be under 2 GiB: the GEMMs address
+ *                  them with buffer loads of a 2 GiB range)
  *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]
  *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128];
  *                  MX: packed E2M1 w_gate_up [L, 2D, H/2] with E8M0 scale
@@ -315,6 +317,34 @@ typedef struct moe_ffn_args {
 
 moe_status_t moe_grouped_ffn(const moe_ffn_args_t* args, void* stream);
 int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t operand_dtype);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_ffn_fused -- [MegaFFN] the single-launch form: the gate_up
+ * GEMM with the gated activation (L1) and the down GEMM (L2) in one launch,
+ * pipelined across workgroups with per-row-block arrival counters and no
+ * per-launch memset.  It computes exactly what moe_grouped_ffn computes
+ * (same arguments and results: A in bf16, O in fp32 or bf16), for bf16
+ * operands; it pays off where the two-launch form is bound by weight
+ * streaming and launch gaps (small batches, decode).
+ *
+ * Differences from moe_grouped_ffn:
+ *   operand_dtype  MOE_DTYPE_BF16 only; hidden_dim % 64 == 0, moe_dim % 128 == 0
+ *   act_workspace  moe_ffn_fused_workspace_bytes(max_rows, moe_dim,
+ *                  n_local_experts) bytes: the launch's control words (work
+ *                  queue, exit count, error word, one arrival counter per
+ *                  32-row block) at the start, then A.  The control words
+ *                  must be ZERO before the first call (allocate the workspace
+ *                  zero-filled); every call leaves them zero again, so one
+ *                  workspace serves calls of any smaller size.  The error
+ *                  word (the int32 at byte offset 8) becomes 1 -- and stays
+ *                  1 -- if a wait for an arrival counter ever timed out (a
+ *                  scheduling fault: the results of that call are wrong).
+ *                  Calls sharing one workspace must not overlap; the launch
+ *                  occupies one workgroup per CU.
+ *   timing_events  the first event before the launch, the other two after it
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* args, void* stream);
+int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t n_local_experts);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- [NeMoExperts] GroupedExperts.forward returns [T, dim]; the

@@ -73,8 +73,9 @@ class CombineArgs(ctypes.Structure):
                 ("shared_out", _vp), ("shared_weights", _vp)]
 
 
-ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_combine", "moe_shared_indices",
-                "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
+ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_grouped_ffn_fused", "moe_combine",
+                "moe_shared_indices", "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
+                "moe_ffn_fused_workspace_bytes",
                 "moe_status_string", "moe_last_error_message", "moe_abi_version")
 
 
@@ -83,7 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_ffn_top_amd.build`")
     lib = ctypes.CDLL(path)
     for name, argt in (("moe_route", RouteArgs), ("moe_build_indices", IndexArgs),
-                       ("moe_grouped_ffn", FfnArgs), ("moe_combine", CombineArgs)):
+                       ("moe_grouped_ffn", FfnArgs), ("moe_grouped_ffn_fused", FfnArgs),
+                       ("moe_combine", CombineArgs)):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(argt), _vp]
         f.restype = _i32
@@ -91,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_build_indices_workspace_bytes.restype = _i64
     lib.moe_ffn_workspace_bytes.argtypes = [_i32, _i32, _i32]
     lib.moe_ffn_workspace_bytes.restype = _i64
+    lib.moe_ffn_fused_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    lib.moe_ffn_fused_workspace_bytes.restype = _i64
     lib.moe_status_string.argtypes = [_i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -217,23 +221,35 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
     return out
 
 
-def ffn_workspace(max_rows: int, D: int, operand: str, device) -> torch.Tensor:
+def ffn_workspace(max_rows: int, D: int, operand: str, device, *, fused: bool = False, L: int = 0) -> torch.Tensor:
+    """The act_workspace of moe_grouped_ffn, or (fused) of moe_grouped_ffn_fused,
+    allocated zero-filled as the single-launch form needs its control words."""
+    if fused:
+        n = lib().moe_ffn_fused_workspace_bytes(max_rows, D, L)
+        return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
     n = lib().moe_ffn_workspace_bytes(max_rows, D, OPERAND[operand])
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def fused_error_word(act_workspace: torch.Tensor) -> int:
+    """The error word of a moe_grouped_ffn_fused workspace (reads the device)."""
+    return int(act_workspace[8:12].view(torch.int32).item())
 
 
 def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None, x_perm_scale=None,
                 x=None, sorted_token=None, activation="silu", alpha=0.0, limit=0.0,
                 gate_up_format="concatenated", gate_up_expert_scales=None, down_expert_scales=None,
-                out_dtype=torch.float32, act_workspace=None, out=None, timing_events=None):
-    """moe_grouped_ffn.  Returns O [max_rows, H] (rows past offsets[-1] unwritten).
+                out_dtype=torch.float32, act_workspace=None, out=None, timing_events=None, fused=False):
+    """moe_grouped_ffn (or, fused=True, moe_grouped_ffn_fused: both GEMMs in
+    one launch, bf16 only).  Returns O [max_rows, H] (rows past offsets[-1]
+    unwritten).
 
     timing_events: optional ctypes array of 3 hipEvent_t handles, recorded
     before the gate_up GEMM, between the GEMMs and after the down GEMM."""
     dev = offsets.device
     L, H, D = weights.L, weights.H, weights.D
     if act_workspace is None:
-        act_workspace = ffn_workspace(max_rows, D, weights.operand, dev)
+        act_workspace = ffn_workspace(max_rows, D, weights.operand, dev, fused=fused, L=L)
     if out is None:
         out = torch.empty((max(max_rows, 1), H), dtype=out_dtype, device=dev)
     _dt(offsets, torch.int32, "offsets")
@@ -253,7 +269,7 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
                 out_dtype=DTYPE_BF16 if out_dtype == torch.bfloat16 else DTYPE_FP32,
                 expert_out=_ptr(out),
                 timing_events=ctypes.addressof(timing_events) if timing_events is not None else None)
-    _check(lib().moe_grouped_ffn(ctypes.byref(a), _stream(dev)))
+    _check((lib().moe_grouped_ffn_fused if fused else lib().moe_grouped_ffn)(ctypes.byref(a), _stream(dev)))
     return out
 
 
@@ -342,11 +358,13 @@ class MoELayer:
     """The whole forward pass over pre-allocated buffers: route ->
     build_indices -> grouped_ffn -> combine, all on torch's current stream."""
 
-    def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True):
+    def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True, fused=None):
         self.cfg = cfg
         dev = inputs["x"].device
         self.device = dev
         self.gather = gather
+        # the single-launch FFN (bf16): on when the configuration asks for it
+        self.fused = getattr(cfg, "fused", False) if fused is None else fused
         self.w = ExpertWeights.from_stacked(
             inputs["w_gate_up"], inputs["w_down"], b_gate_up=inputs.get("b_gate_up"),
             b_down=inputs.get("b_down"), w_gate_up_scale=inputs.get("w_gate_up_scale"),
@@ -358,7 +376,7 @@ class MoELayer:
         T, k = cfg.T, cfg.k
         R = T * k
         self.R = R
-        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev)
+        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev, fused=self.fused, L=cfg.E)
         self.out_dtype = torch.float32 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else torch.bfloat16
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
@@ -415,7 +433,7 @@ class MoELayer:
                         sorted_token=ind["sorted_token"] if self.gather else None,
                         activation=c.activation, alpha=c.alpha, limit=c.limit,
                         gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
-                        act_workspace=self.act_ws, out=self.O, timing_events=ffn_events)
+                        act_workspace=self.act_ws, out=self.O, timing_events=ffn_events, fused=self.fused)
         O_sh = None
         if self.n_shared:
             xs = xg if fp8 else x
@@ -435,4 +453,5 @@ class MoELayer:
 
 
 __all__ = ["lib", "route", "build_indices", "grouped_ffn", "combine", "shared_indices", "ExpertWeights", "MoELayer",
+           "ffn_workspace", "fused_error_word",
            "MoEError", "load_library", "ENTRY_POINTS", "LIB_PATH"]

@@ -241,9 +241,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn: MXFP4 weights need w_gate_up_scale and w_down_scale");
     const int64_t es = a16 ? 2 : 1;   // bytes per activation element
-    REQUIRE((int64_t)R * H * es < ((int64_t)1 << 32) && (int64_t)R * D * es < ((int64_t)1 << 32) &&
-                (int64_t)D * H < ((int64_t)1 << 32),
-            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
+    REQUIRE((int64_t)R * H * es < ((int64_t)1 << 31) && (int64_t)R * D * es < ((int64_t)1 << 31) &&
+                (int64_t)D * H < ((int64_t)1 << 31),
+            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
     REQUIRE(aligned16(a->b_gate_up) && aligned16(a->b_down), "moe_grouped_ffn: biases must be 16-byte aligned");
     if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
       return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: MXFP4 weights must use the OUT_IN layout");
@@ -283,9 +283,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
             "moe_grouped_ffn: fp8 takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn: fp8 weights need w_gate_up_scale and w_down_scale");
-    REQUIRE((int64_t)R * H < ((int64_t)1 << 32) && (int64_t)R * D < ((int64_t)1 << 32) &&
-                (int64_t)2 * D * H < ((int64_t)1 << 32),
-            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
+    REQUIRE((int64_t)R * H < ((int64_t)1 << 31) && (int64_t)R * D < ((int64_t)1 << 31) &&
+                (int64_t)2 * D * H < ((int64_t)1 << 31),
+            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
     if (a->gate_up_format != MOE_GATE_UP_CONCATENATED)
       return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path takes the concatenated gate_up format");
     if (a->b_gate_up != nullptr || a->b_down != nullptr)
@@ -319,9 +319,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     return hip_status(moe::launch_ffn_fp8(q, (hipStream_t)stream), "moe_grouped_ffn");
   }
   // the GEMMs address rows with 32-bit byte offsets
-  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 32) && (int64_t)R * D * 2 < ((int64_t)1 << 32) &&
-              (int64_t)2 * D * H * 2 < ((int64_t)1 << 32),
-          "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 4 GiB");
+  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 31) && (int64_t)R * D * 2 < ((int64_t)1 << 31) &&
+              (int64_t)2 * D * H * 2 < ((int64_t)1 << 31),
+          "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
   if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 weights must use the OUT_IN layout for now");
   if (R == 0) return ok();
@@ -355,6 +355,82 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   p.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
   p.events = (hipEvent_t const*)a->timing_events;
   return hip_status(moe::launch_ffn_bf16(p, (hipStream_t)stream), "moe_grouped_ffn");
+}
+
+// ---------------------------------------------------------------- fused single launch
+int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t D, int32_t L) {
+  if (max_rows < 0 || D < 1 || L < 1) return 0;
+  return round_up((int64_t)max_rows * D * 2, 256) + round_up(moe::fused_ctl_words(max_rows, L) * 4, 256);
+}
+
+moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_grouped_ffn_fused: args is NULL");
+  const int R = a->max_rows, H = a->hidden_dim, D = a->moe_dim, L = a->n_local_experts;
+  REQUIRE(R >= 0, "moe_grouped_ffn_fused: max_rows must be >= 0 (got %d)", R);
+  REQUIRE(H >= 64 && H % 64 == 0, "moe_grouped_ffn_fused: hidden_dim must be a positive multiple of 64 (got %d)", H);
+  REQUIRE(D >= 128 && D % 128 == 0, "moe_grouped_ffn_fused: moe_dim must be a positive multiple of 128 (got %d)", D);
+  REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn_fused: n_local_experts must be in [1, 1024] (got %d)", L);
+  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn_fused: operand_dtype must be BF16");
+  REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn_fused: expert_offsets is required");
+  REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI || a->activation == MOE_ACT_GELU_TANH,
+          "moe_grouped_ffn_fused: unknown activation %d", a->activation);
+  REQUIRE(std::isfinite(a->alpha) && std::isfinite(a->limit), "moe_grouped_ffn_fused: alpha and limit must be finite");
+  REQUIRE(a->activation == MOE_ACT_SWIGLUOAI || a->alpha == 0.0f,
+          "moe_grouped_ffn_fused: alpha is the sigmoid scale of swigluoai and must be 0 for the other activations");
+  REQUIRE(a->activation != MOE_ACT_GELU_TANH || a->limit == 0.0f, "moe_grouped_ffn_fused: limit must be 0 for gelu_tanh");
+  REQUIRE(a->limit >= 0.0f, "moe_grouped_ffn_fused: limit must be >= 0");
+  REQUIRE(a->gate_up_format == MOE_GATE_UP_CONCATENATED || a->gate_up_format == MOE_GATE_UP_INTERLEAVED,
+          "moe_grouped_ffn_fused: unknown gate_up_format %d", a->gate_up_format);
+  REQUIRE(a->out_dtype == MOE_DTYPE_FP32 || a->out_dtype == MOE_DTYPE_BF16,
+          "moe_grouped_ffn_fused: out_dtype must be FP32 or BF16");
+  REQUIRE(a->w_gate_up && a->w_down, "moe_grouped_ffn_fused: w_gate_up and w_down are required");
+  REQUIRE(R == 0 || a->expert_out != nullptr, "moe_grouped_ffn_fused: expert_out is required");
+  const bool gather = a->x_perm == nullptr;
+  if (gather)
+    REQUIRE(R == 0 || (a->x != nullptr && a->sorted_token != nullptr),
+            "moe_grouped_ffn_fused: pass x_perm, or x and sorted_token to gather rows");
+  else
+    REQUIRE(a->x == nullptr, "moe_grouped_ffn_fused: pass either x_perm or x/sorted_token, not both");
+  REQUIRE(aligned16(a->x_perm) && aligned16(a->x) && aligned16(a->w_gate_up) && aligned16(a->w_down) &&
+              aligned16(a->act_workspace) && aligned16(a->expert_out) && aligned16(a->b_gate_up) &&
+              aligned16(a->b_down),
+          "moe_grouped_ffn_fused: tensors must be 16-byte aligned");
+  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 31) && (int64_t)R * D * 2 < ((int64_t)1 << 31) &&
+              (int64_t)2 * D * H * 2 < ((int64_t)1 << 31),
+          "moe_grouped_ffn_fused: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
+  if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_fused: weights must use the OUT_IN layout");
+  const int64_t need = moe_ffn_fused_workspace_bytes(R, D, L);
+  if (a->act_workspace_bytes < need || (need > 0 && a->act_workspace == nullptr))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn_fused: act_workspace needs %lld bytes (got %lld)",
+                (long long)need, (long long)a->act_workspace_bytes);
+  if (R == 0) return ok();
+  moe::FfnBf16Params p{};
+  p.offsets = a->expert_offsets;
+  p.L = L;
+  p.H = H;
+  p.D = D;
+  p.max_rows = R;
+  p.x_perm = (const uint16_t*)a->x_perm;
+  p.x = (const uint16_t*)a->x;
+  p.sorted_token = a->sorted_token;
+  p.w_gate_up = (const uint16_t*)a->w_gate_up;
+  p.b_gate_up = (const uint16_t*)a->b_gate_up;
+  p.w_down = (const uint16_t*)a->w_down;
+  p.b_down = (const uint16_t*)a->b_down;
+  p.gate_up_scales = a->gate_up_expert_scales;
+  p.down_scales = a->down_expert_scales;
+  p.fmt = a->gate_up_format;
+  p.act_kind = a->activation;
+  p.alpha = a->alpha;
+  p.limit = a->limit;
+  // control words first (a fixed place whatever max_rows is), then A
+  int32_t* ctl = (int32_t*)a->act_workspace;
+  p.act = (uint16_t*)((uint8_t*)a->act_workspace + round_up(moe::fused_ctl_words(R, L) * 4, 256));
+  p.out = a->expert_out;
+  p.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+  p.events = (hipEvent_t const*)a->timing_events;
+  return hip_status(moe::launch_ffn_fused(p, ctl, (hipStream_t)stream), "moe_grouped_ffn_fused");
 }
 
 // ---------------------------------------------------------------- combine

@@ -111,6 +111,13 @@ hipError_t launch_ffn_mx(const FfnMxParams& p, hipStream_t st);
 // activation scales; the same weight fields.
 hipError_t launch_ffn_w4a16(const FfnMxParams& p, hipStream_t st);
 
+// Single-launch L1+L2 FFN for small batches (bf16 operands): control words
+// (queue, exit count, error, one arrival counter per 32-row block) at the
+// start of the workspace, then A; zero when allocated, zero again after
+// every launch.
+int64_t fused_ctl_words(int64_t max_rows, int L);
+hipError_t launch_ffn_fused(const FfnBf16Params& p, int32_t* ctl, hipStream_t st);
+
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,
                           const void* O_shared, const float* w_shared, hipStream_t st);

@@ -34,6 +34,7 @@ class MoEConfig:
                                  # | "mxfp4_a16" (MXFP4 weights, bf16 activations: W4A16)
     route_scale: float = 1.0
     global_scale: float = 1.0
+    fused: bool = False         # run the FFN as one launch (moe_grouped_ffn_fused)
     logit_std: float = 2.0      # sigmoid router: logits are an input ~N(0, logit_std)
     bias_range: float = 0.1     # sigmoid router: selection bias ~U(-r, r)
     x_std: float = 1.0
@@ -72,6 +73,8 @@ CONFIGS = {
     7: MoEConfig(7, "mxfp4_a16", T=256, H=7168, E=256, k=8, D=2048,
                  router="sigmoid_sink", s=0, operand_dtype="mxfp4_a16",
                  route_scale=1.0, global_scale=1.0),
+    # the Mixtral layer on a decode-sized batch, FFN in one launch
+    8: MoEConfig(8, "mixtral_decode", T=64, H=4096, E=8, k=2, D=14336, fused=True),
 }
 
 

@@ -148,6 +148,27 @@ def test_grouped_ffn_validation(kw, status, frag):
     assert st == status and frag in msg, msg
 
 
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(hidden_dim=96), m.MOE_ERR_INVALID_ARGUMENT, "64"),
+    (dict(moe_dim=200), m.MOE_ERR_INVALID_ARGUMENT, "128"),
+    (dict(operand_dtype=1), m.MOE_ERR_INVALID_ARGUMENT, "BF16"),
+    (dict(alpha=1.0), m.MOE_ERR_INVALID_ARGUMENT, "alpha"),
+    (dict(x_perm=None), m.MOE_ERR_INVALID_ARGUMENT, "gather"),
+    (dict(w_gate_up_layout=0), m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
+    (dict(act_workspace_bytes=64 * 512 * 2), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
+])
+def test_grouped_ffn_fused_validation(kw, status, frag):
+    st, msg = _err(m.lib().moe_grouped_ffn_fused, _ffn(**kw))
+    assert st == status and frag in msg, msg
+
+
+def test_fused_workspace_bytes():
+    lib = m.lib()
+    # A in bf16, then 4 control words and one arrival counter per possible 32-row block
+    assert lib.moe_ffn_fused_workspace_bytes(64, 512, 8) == 64 * 512 * 2 + 256
+    assert lib.moe_ffn_fused_workspace_bytes(8192, 14336, 8) == 8192 * 14336 * 2 + ((4 + 256 + 8) * 4 + 255) // 256 * 256
+
+
 def _idx(**kw):
     base = dict(num_tokens=16, n_experts_per_tok=2, experts_start_idx=0, n_local_experts=8, expert_indices=16,
                 expert_offsets=32, sorted_token=48, row_of_slot=64, workspace=80, workspace_bytes=1 << 16)

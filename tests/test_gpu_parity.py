@@ -652,3 +652,67 @@ def test_mx_w4a16_layer_full_size(moe):
     _, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 8, seed=8), BF16_TOL)
+
+
+
+# ---------------------------------------------------------------- single-launch L1 + L2 (bf16)
+
+@pytest.mark.parametrize("changes", [
+    {"T": 64, "E": 8, "k": 2, "H": 512, "D": 256},
+    {"T": 37, "E": 8, "k": 2, "H": 256, "D": 384, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+     "gate_up_format": "interleaved", "has_bias": True},
+    {"T": 200, "E": 5, "k": 3, "H": 320, "D": 128, "activation": "gelu_tanh", "has_bias": True},
+    {"T": 9, "E": 64, "k": 6, "H": 1024, "D": 512},          # most experts empty, single rows
+])
+def test_fused_ffn_layer(moe, changes):
+    """The single-launch FFN against the oracle, twice in a row on the same
+    workspace (the second call reuses the control words the first left at
+    zero), with no timed-out wait, and against the two-launch FFN."""
+    cfg = synth.scaled(synth.get_config(8), **changes)
+    inp = _gen(cfg)
+    say(f"[fused] {changes}")
+    layer = moe.MoELayer(cfg, inp)
+    assert layer.fused
+    for call in range(2):
+        res = layer.forward(inp["x"])
+        torch.cuda.synchronize()
+        _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+        assert moe.fused_error_word(layer.act_ws) == 0, f"call {call}: a wait timed out"
+    ind = res["index"]
+    n = int(host(ind["offsets"])[-1])
+    o_fused = host(res["O"])[:n].astype(np.float64)
+    o_two = moe.grouped_ffn(ind["offsets"], layer.R, layer.w, x=inp["x"], sorted_token=ind["sorted_token"],
+                            activation=cfg.activation, alpha=cfg.alpha, limit=cfg.limit,
+                            gate_up_format=cfg.gate_up_format)
+    torch.cuda.synchronize()
+    err, _ = rel_rms_err(o_fused, host(o_two)[:n].astype(np.float64))
+    say(f"  fused vs two-launch O: max err / rms = {err:.2e}")
+    assert err <= BF16_TOL
+
+
+def test_fused_ffn_then_smaller_batch(moe):
+    """Two calls in a row, the second with fewer tokens and a different
+    routing: the first call's arrival counters must not leak into the second."""
+    big = synth.scaled(synth.get_config(8), T=128, H=512, D=256)
+    small = synth.scaled(big, T=17)
+    inp_b, inp_s = _gen(big), synth.make_inputs(small, DEV, salt=3)
+    say("[fused] T=128 then T=17 on one workspace")
+    lb = moe.MoELayer(big, inp_b)
+    ls = moe.MoELayer(small, inp_s)
+    ls.act_ws = lb.act_ws        # one workspace, sized for the larger call
+    rb = lb.forward(inp_b["x"])
+    rs = ls.forward(inp_s["x"])
+    torch.cuda.synchronize()
+    _check_layer(big, inp_b, rb, np.arange(big.T), BF16_TOL)
+    _check_layer(small, inp_s, rs, np.arange(small.T), BF16_TOL)
+    assert moe.fused_error_word(lb.act_ws) == 0
+
+
+def test_fused_ffn_full_size(moe):
+    cfg = synth.get_config(8)
+    inp = _gen(cfg)
+    say("[fused full] Mixtral decode T=64 H=4096 E=8 k=2 D=14336, one launch")
+    layer, res = _run_layer(moe, cfg, inp)
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 16, seed=9), BF16_TOL)
+    assert moe.fused_error_word(layer.act_ws) == 0
