@@ -425,11 +425,13 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 // weights then come from one MX block (2h + s/4), from dword s%4 of the
 // 16-byte chunk 2h + s/4 of its weight row, and its 8 activations are chunk
 // 8h + s of the 256-byte activation row.
-// Two shapes: 128-row tiles with 8 waves (2 x 4) and 3 stages, and, for
-// batches of a few rows per expert (decode), 32-row tiles with 4 waves and 6
-// stages, which keeps five 17 KB weight stages in flight per CU where the
-// larger tile could hold two: that batch is bound by streaming the weights
-// from HBM, so what counts is the bytes in flight.
+// Two shapes, both 3 stages deep: 128-row tiles with 8 waves (2 x 4), and,
+// for batches of a few rows per expert (decode), 32-row tiles with 4 waves
+// whose 75 KB of LDS let two workgroups share a CU.  Such a batch is bound by
+// streaming the weights; with one 4-wave workgroup per CU each SIMD has a
+// single wave, which serialises its LDS reads, conversions and MFMAs, and
+// the second workgroup hides them (measured: 6 stages with one workgroup per
+// CU, or 2 stages with three, were slower).
 constexpr int W_BN = 256, W_BK = 128;
 constexpr int W_A_ROW = W_BK * 2;                                   // bytes per bf16 stage row
 constexpr int W_B_ROW = W_BK / 2;
@@ -439,7 +441,7 @@ template <int BM>
 struct W4Shape {
   static constexpr int WAVES_M = BM >= 64 ? 2 : 1, WAVES_N = 4, NWAVES = WAVES_M * WAVES_N;
   static constexpr int NT = 64 * NWAVES;
-  static constexpr int NS = BM >= 64 ? 3 : 6;                       // stages
+  static constexpr int NS = 3;                                       // stages
   static constexpr int WTM = BM / WAVES_M, WTN = W_BN / WAVES_N;    // wave tile, WTN = 64
   static constexpr int MI = WTM / 32, NI = WTN / 32;
   static constexpr int A_BYTES = BM * W_A_ROW;
