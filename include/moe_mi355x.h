@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -322,29 +322,45 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t opera
  * moe_grouped_ffn_fused -- [MegaFFN] the single-launch form: the gate_up
  * GEMM with the gated activation (L1) and the down GEMM (L2) in one launch,
  * pipelined across workgroups with per-row-block arrival counters and no
- * per-launch memset.  It computes exactly what moe_grouped_ffn computes
- * (same arguments and results: A in bf16, O in fp32 or bf16), for bf16
+ * per-launch memset.  It computes what moe_grouped_ffn computes (same
+ * arguments and results: A in bf16, O in fp32 or bf16), for bf16
  * operands; it pays off where the two-launch form is bound by weight
  * streaming and launch gaps (small batches, decode).
  *
  * Differences from moe_grouped_ffn:
  *   operand_dtype  MOE_DTYPE_BF16 only; hidden_dim % 64 == 0, moe_dim % 128 == 0
- *   act_workspace  moe_ffn_fused_workspace_bytes(max_rows, moe_dim,
- *                  n_local_experts) bytes: the launch's control words (work
- *                  queue, exit count, error word, one arrival counter per
- *                  32-row block) at the start, then A.  The control words
- *                  must be ZERO before the first call (allocate the workspace
- *                  zero-filled); every call leaves them zero again, so one
- *                  workspace serves calls of any smaller size.  The error
- *                  word (the int32 at byte offset 8) becomes 1 -- and stays
- *                  1 -- if a wait for an arrival counter ever timed out (a
- *                  scheduling fault: the results of that call are wrong).
+ *   act_workspace  moe_ffn_fused_workspace_bytes(max_rows, hidden_dim,
+ *                  moe_dim, n_local_experts) bytes, holding the launch's
+ *                  control words (work queue, exit count, error word, a
+ *                  parts-done counter per split down tile, and an arrival
+ *                  counter per 32-row block, the last at the very end of the
+ *                  act_workspace_bytes the caller passes), A, and the fp32
+ *                  partial tiles of the down items split along K.  The
+ *                  control words must be ZERO before the first call
+ *                  (allocate the workspace zero-filled); every call leaves
+ *                  them zero again.  So one workspace serves any call with
+ *                  the same hidden_dim, moe_dim and n_local_experts and a
+ *                  max_rows no larger than it was sized for, PROVIDED every
+ *                  call passes the same act_workspace_bytes (the end of the
+ *                  buffer anchors the arrival counters).  The error word
+ *                  (the int32 at byte offset 8) becomes nonzero -- and
+ *                  stays so -- when a call's results are wrong: 1 if a wait
+ *                  for an arrival counter timed out (a scheduling fault), 2
+ *                  if expert_offsets[n_local_experts] exceeded max_rows
+ *                  (that call then computes nothing).
  *                  Calls sharing one workspace must not overlap; the launch
  *                  occupies one workgroup per CU.
+ *   expert_out     as for moe_grouped_ffn.  When the launch has at most 256
+ *                  down tiles (32-row blocks x ceil(hidden_dim / 256)) and
+ *                  moe_dim is at least 3 x hidden_dim, each down tile is
+ *                  summed from round(moe_dim / (2 hidden_dim)) (at most 8) fp32
+ *                  partial products over slices of K, always in the same
+ *                  order: the result is deterministic, and within rounding of
+ *                  moe_grouped_ffn's.
  *   timing_events  the first event before the launch, the other two after it
  * ---------------------------------------------------------------------- */
 moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* args, void* stream);
-int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t n_local_experts);
+int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t hidden_dim, int32_t moe_dim, int32_t n_local_experts);
 
 /* ------------------------------------------------------------------------
  * moe_combine -- [NeMoExperts] GroupedExperts.forward returns [T, dim]; the

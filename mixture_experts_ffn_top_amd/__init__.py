@@ -93,7 +93,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_build_indices_workspace_bytes.restype = _i64
     lib.moe_ffn_workspace_bytes.argtypes = [_i32, _i32, _i32]
     lib.moe_ffn_workspace_bytes.restype = _i64
-    lib.moe_ffn_fused_workspace_bytes.argtypes = [_i32, _i32, _i32]
+    lib.moe_ffn_fused_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
     lib.moe_ffn_fused_workspace_bytes.restype = _i64
     lib.moe_status_string.argtypes = [_i32]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -221,11 +221,12 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
     return out
 
 
-def ffn_workspace(max_rows: int, D: int, operand: str, device, *, fused: bool = False, L: int = 0) -> torch.Tensor:
+def ffn_workspace(max_rows: int, D: int, operand: str, device, *, fused: bool = False, L: int = 0,
+                  H: int = 0) -> torch.Tensor:
     """The act_workspace of moe_grouped_ffn, or (fused) of moe_grouped_ffn_fused,
     allocated zero-filled as the single-launch form needs its control words."""
     if fused:
-        n = lib().moe_ffn_fused_workspace_bytes(max_rows, D, L)
+        n = lib().moe_ffn_fused_workspace_bytes(max_rows, H, D, L)
         return torch.zeros(max(n, 256), dtype=torch.uint8, device=device)
     n = lib().moe_ffn_workspace_bytes(max_rows, D, OPERAND[operand])
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -249,7 +250,7 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
     dev = offsets.device
     L, H, D = weights.L, weights.H, weights.D
     if act_workspace is None:
-        act_workspace = ffn_workspace(max_rows, D, weights.operand, dev, fused=fused, L=L)
+        act_workspace = ffn_workspace(max_rows, D, weights.operand, dev, fused=fused, L=L, H=H)
     if out is None:
         out = torch.empty((max(max_rows, 1), H), dtype=out_dtype, device=dev)
     _dt(offsets, torch.int32, "offsets")
@@ -376,7 +377,7 @@ class MoELayer:
         T, k = cfg.T, cfg.k
         R = T * k
         self.R = R
-        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev, fused=self.fused, L=cfg.E)
+        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev, fused=self.fused, L=cfg.E, H=cfg.H)
         self.out_dtype = torch.float32 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else torch.bfloat16
         self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)

@@ -358,9 +358,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
 }
 
 // ---------------------------------------------------------------- fused single launch
-int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t D, int32_t L) {
-  if (max_rows < 0 || D < 1 || L < 1) return 0;
-  return round_up((int64_t)max_rows * D * 2, 256) + round_up(moe::fused_ctl_words(max_rows, L) * 4, 256);
+int64_t moe_ffn_fused_workspace_bytes(int32_t max_rows, int32_t H, int32_t D, int32_t L) {
+  if (max_rows < 0 || H < 1 || D < 1 || L < 1) return 0;
+  return moe::fused_layout(max_rows, H, D, L).bytes;
 }
 
 moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
@@ -400,7 +400,7 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
           "moe_grouped_ffn_fused: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
   if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_fused: weights must use the OUT_IN layout");
-  const int64_t need = moe_ffn_fused_workspace_bytes(R, D, L);
+  const int64_t need = moe_ffn_fused_workspace_bytes(R, H, D, L);
   if (a->act_workspace_bytes < need || (need > 0 && a->act_workspace == nullptr))
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn_fused: act_workspace needs %lld bytes (got %lld)",
                 (long long)need, (long long)a->act_workspace_bytes);
@@ -424,13 +424,11 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
   p.act_kind = a->activation;
   p.alpha = a->alpha;
   p.limit = a->limit;
-  // control words first (a fixed place whatever max_rows is), then A
-  int32_t* ctl = (int32_t*)a->act_workspace;
-  p.act = (uint16_t*)((uint8_t*)a->act_workspace + round_up(moe::fused_ctl_words(R, L) * 4, 256));
   p.out = a->expert_out;
   p.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
   p.events = (hipEvent_t const*)a->timing_events;
-  return hip_status(moe::launch_ffn_fused(p, ctl, (hipStream_t)stream), "moe_grouped_ffn_fused");
+  return hip_status(moe::launch_ffn_fused(p, a->act_workspace, a->act_workspace_bytes, (hipStream_t)stream),
+                    "moe_grouped_ffn_fused");
 }
 
 // ---------------------------------------------------------------- combine

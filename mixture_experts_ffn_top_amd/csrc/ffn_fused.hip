@@ -5,13 +5,23 @@
 //
 // A persistent grid (one workgroup per CU) takes work items from one atomic
 // queue: first every L1 item (expert, 32-row block, 128 outputs), then every
-// L2 item (expert, 32-row block, 256 outputs).  An L2 item needs the whole A
-// row block, i.e. all D/128 L1 items of its (expert, row block); it waits for
-// that block's arrival counter.  Because every L1 item leaves the queue
-// before any L2 item, the items an L2 item waits for are already held by
-// running workgroups, which never wait themselves: the wait always ends.  It
-// is bounded anyway (a few hundred ms); on timeout it sets an error word and
-// goes on, so a broken schedule gives wrong numbers, not a hang.
+// L2 item (expert, 32-row block, 256 outputs, one of S parts of K).  An L2
+// item needs the whole A row block, i.e. all D/128 L1 items of its (expert,
+// row block); it waits for that block's arrival counter.  Because every L1
+// item leaves the queue before any L2 item, the items an L2 item waits for
+// are already held by running workgroups, which never wait themselves: the
+// wait always ends.  It is bounded anyway (a few hundred ms); on timeout it
+// sets an error word and goes on, so a broken schedule gives wrong numbers,
+// not a hang.
+//
+// Balance.  An L1 item streams 256 weight rows of length H, an unsplit L2
+// item 256 rows of length D; with D several times H (Mixtral: 3.5x) the few
+// long L2 items would leave most CUs idle at the end.  So when the launch has
+// few L2 tiles, each is split into S = round(D/2H) parts along K.  Every part
+// writes its fp32 partial tile to the workspace and counts itself in; the
+// last part to arrive adds the S partials in part order (its own from
+// registers) and runs the epilogue, so the result does not depend on which
+// part came last.  No part waits for another.
 //
 // Visibility follows the HIP memory model at agent scope: an L1 item's waves
 // fence-release their A stores (write-back of the XCD's L2) before the
@@ -46,6 +56,10 @@ constexpr int F_PIPE = F_NS * F_STAGE;              // 144 KB
 constexpr int F_BUF_DWORD3 = 0x00020000;            // raw buffer resource word 3 (gfx9)
 constexpr uint32_t F_OOB = 0x80000000u;             // past every buffer range: zeros, no memory
 constexpr int F_SPIN_LIMIT = 1 << 20;               // bounded wait: ~0.2 s of s_sleep 8
+constexpr int F_MAX_TILES = 256;                    // L2 tiles a launch may split along K
+constexpr int F_MAX_PARTS = 8;
+constexpr int F_HDR_WORDS = 4 + F_MAX_TILES;        // queue, exits, error, unused, split counters
+constexpr int64_t F_PART_FLOATS = F_BM * F_BN;      // one partial tile, 32 KB
 
 // 128-byte rows, 8 chunks of 16 bytes: chunk c of row r at c ^ f(r).
 __device__ __forceinline__ int f_swz(int r) { return (r ^ (r >> 3)) & 7; }
@@ -69,7 +83,12 @@ struct FusedArgs {
   float alpha, limit;
   uint16_t* act;               // A bf16 [R, D]
   void* out;                   // O [R, H]
-  int32_t* ctl;                // [0] queue head, [1] exit count, [2] error, [4 + i] arrivals of row block i
+  int32_t* ctl;                // [0] queue head, [1] exit count, [2] error, [4 + t] parts done of L2 tile t
+  int32_t* arrive;             // [i] L1 items done of global row block i
+  float* part;                 // [tile][part] partial tiles of F_PART_FLOATS, laid out by thread
+  int S;                       // K parts of a split L2 tile
+  int row_blocks;              // arrival counters the workspace holds
+  int tiles_cap;               // split only when the launch has at most this many L2 tiles
 };
 
 template <int ACT, int FMT, bool OUT_BF16>
@@ -83,7 +102,8 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   int32_t* queue = p.ctl;
   int32_t* exits = p.ctl + 1;
   int32_t* err = p.ctl + 2;
-  int32_t* arrive = p.ctl + 4;
+  int32_t* arrive = p.arrive;
+  int32_t* tile_done = p.ctl + 4;
 
   if (wave == 0) {
     const int per = (L + 63) / 64;
@@ -110,9 +130,14 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     if (lane == 63) s_mbp[L] = inc;
   }
   __syncthreads();
-  const int total_mb = s_mbp[L];
+  // more rows than max_rows: no counter may be touched, so do nothing
+  const bool too_many = s_mbp[L] > p.row_blocks;
+  if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(p.ctl + 2, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int total_mb = too_many ? 0 : s_mbp[L];
   const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
-  const int n1 = total_mb * NB1, n_all = n1 + total_mb * NB2;
+  const int n2 = total_mb * NB2;
+  const int S = (p.S > 1 && n2 <= p.tiles_cap) ? p.S : 1;
+  const int n1 = total_mb * NB1, n_all = n1 + n2 * S;
   const int fr = lane & 31, fh = lane >> 5;
 
   for (;;) {
@@ -121,7 +146,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
     if (item >= n_all) break;
     const bool l2 = item >= n1;
-    const int NB = l2 ? NB2 : NB1;
+    const int NB = l2 ? NB2 * S : NB1;
     const int it = l2 ? item - n1 : item;
     int lo = 0, hi = L - 1;
     while (lo < hi) {
@@ -132,29 +157,36 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     const int e = __builtin_amdgcn_readfirstlane(lo);
     const int nmb = s_mbp[e + 1] - s_mbp[e];
     const int local = __builtin_amdgcn_readfirstlane(it - s_mbp[e] * NB);
-    const int nb = local / nmb, mb = local % nmb;
+    const int q_nb = local / nmb, mb = local % nmb;
+    const int nb = l2 ? q_nb / S : q_nb;
+    const int part = l2 ? q_nb % S : 0;
     const int gm = s_mbp[e] + mb;  // global row block: its arrival counter
     const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * F_BM);
     const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
 
     if (l2) {
+      // one thread spins on the counter (relaxed: no cache invalidation per
+      // poll), then acquires once; the barrier orders the other waves' loads
+      // of A after that acquire
       if (tid == 0) {
         int spins = 0;
-        while (__hip_atomic_load(arrive + gm, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < NB1) {
+        while (__hip_atomic_load(arrive + gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NB1) {
           __builtin_amdgcn_s_sleep(8);
           if (++spins > F_SPIN_LIMIT) {
             __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
 
     // ---- operands of this item
     const int K = l2 ? p.D : p.H;
-    const int KT = K / F_BK;
+    const int parts = l2 ? S : 1;
+    const int kt0 = part * (K / F_BK) / parts;
+    const int KT = (part + 1) * (K / F_BK) / parts - kt0;  // k stages of this item
     const uint16_t* a_base = l2 ? p.act : p.x;
     const uint16_t* b_base = l2 ? p.w_d + (int64_t)e * p.H * p.D : p.w_gu + (int64_t)e * 2 * p.D * p.H;
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
@@ -188,11 +220,12 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     }
     auto issue = [&](int kt) {
       uint8_t* st = smem + (kt % F_NS) * F_STAGE;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + wave_s * 1024), 16, a_voff, kt * F_ROW, 0, 0);
+      const int soff = (kt0 + kt) * F_ROW;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + wave_s * 1024), 16, a_voff, soff, 0, 0);
 #pragma unroll
       for (int i = 0; i < F_LPW_B; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + F_A_BYTES + (wave_s * F_LPW_B + i) * 1024), 16,
-                                                 b_voff[i], kt * F_ROW, 0, 0);
+                                                 b_voff[i], soff, 0, 0);
     };
 
     f32x16_t acc[2];
@@ -257,12 +290,68 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
           *(uint2*)(p.act + (int64_t)row * p.D + oc) = v;
         }
       }
-      // publish this part of the row block: every wave's A stores are
-      // written back before the counter moves
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      // publish this part of the row block.  The barrier orders every
+      // wave's A stores before thread 0's release fence, which writes them
+      // back once for the workgroup; the count then moves.
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(arrive + gm, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(arrive + gm, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     } else {
+      if (S > 1) {
+        // this part's partial tile, then count it in; acc[j/4][4(j%4) + c]
+        // goes to float 4(j*F_NT + tid) + c of the slot, the same place in
+        // every part
+        const int t2 = gm * NB2 + nb;
+        float* slots = p.part + (int64_t)t2 * S * F_PART_FLOATS;
+        float* mine = slots + (int64_t)part * F_PART_FLOATS;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4_t v = {acc[j / 4][4 * (j % 4)], acc[j / 4][4 * (j % 4) + 1], acc[j / 4][4 * (j % 4) + 2],
+                             acc[j / 4][4 * (j % 4) + 3]};
+          *(f32x4_t*)(mine + 4 * (j * F_NT + tid)) = v;
+        }
+        // release as for A; the last part acquires the others' partials
+        __syncthreads();
+        if (tid == 0) {
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+          const int done = __hip_atomic_fetch_add(tile_done + t2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          s_item[1] = done == S - 1;
+          if (done == S - 1) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // every part has counted in: reset for the next launch
+            __hip_atomic_store(tile_done + t2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+        __syncthreads();
+        if (!s_item[1]) {
+          __syncthreads();
+          continue;
+        }
+        // sum the parts in part order
+        f32x16_t sum[2];
+        for (int pp = 0; pp < S; ++pp) {
+          if (pp == part) {
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) sum[ni][r] = pp ? sum[ni][r] + acc[ni][r] : acc[ni][r];
+          } else {
+            const float* src = slots + (int64_t)pp * F_PART_FLOATS;
+            f32x4_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = *(const f32x4_t*)(src + 4 * (j * F_NT + tid));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                sum[j / 4][4 * (j % 4) + c] = pp ? sum[j / 4][4 * (j % 4) + c] + v[j][c] : v[j][c];
+          }
+        }
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) acc[ni] = sum[ni];
+      }
       const float sc = p.s_d ? p.s_d[e] : 1.0f;
       const uint16_t* bias = p.b_d ? p.b_d + (int64_t)e * p.H : nullptr;
 #pragma unroll
@@ -300,6 +389,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   __syncthreads();
   if (s_item[1]) {
     for (int i = tid; i < total_mb; i += F_NT) __hip_atomic_store(arrive + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // (the split counters were reset by their last parts)
     if (tid == 0) {
       __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(exits, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -321,7 +411,7 @@ int fused_cu_count() {
 
 template <typename KernelT>
 hipError_t launch_fused_kernel(KernelT kern, const FusedArgs& a, hipStream_t st) {
-  const int lds = F_PIPE + (a.L + 3) * (int)sizeof(int32_t);
+  const int lds = F_PIPE + (a.L + 4) * (int)sizeof(int32_t);
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int grid = fused_cu_count();
@@ -341,10 +431,30 @@ hipError_t launch_fused_act(const FusedArgs& a, int fmt, int out_bf16, hipStream
 
 }  // namespace
 
-int64_t fused_ctl_words(int64_t max_rows, int L) { return 4 + (max_rows + F_BM - 1) / F_BM + L; }
+FusedLayout fused_layout(int64_t max_rows, int H, int D, int L) {
+  FusedLayout f{};
+  auto up256 = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const int64_t R = max_rows < 0 ? 0 : max_rows;
+  // at most one partly filled 32-row block per expert that has rows
+  f.row_blocks = (R + F_BM - 1) / F_BM + (L < R ? L : R);
+  // a part of K about twice an L1 item's: each part also pays a partial tile
+  // write and its share of the reduction (measured on the Mixtral decode
+  // shape, D/H = 3.5: 2 parts 0.61 ms, 4 parts 0.63, unsplit 0.65)
+  int S = H > 0 ? (D + H) / (2 * H) : 1;
+  S = S < 1 ? 1 : (S > F_MAX_PARTS ? F_MAX_PARTS : S);
+  if (S > D / F_BK) S = D / F_BK;
+  const int64_t tiles = f.row_blocks * ((H + F_BN - 1) / F_BN);
+  f.tiles_cap = S > 1 ? (int)(tiles < F_MAX_TILES ? tiles : F_MAX_TILES) : 0;
+  f.S = f.tiles_cap > 0 ? S : 1;
+  f.act_off = up256(F_HDR_WORDS * 4);
+  f.part_off = f.act_off + up256(R * D * 2);
+  f.bytes = f.part_off + (int64_t)f.tiles_cap * f.S * F_PART_FLOATS * 4 + up256(f.row_blocks * 4);
+  return f;
+}
 
-hipError_t launch_ffn_fused(const FfnBf16Params& q, int32_t* ctl, hipStream_t st) {
+hipError_t launch_ffn_fused(const FfnBf16Params& q, void* ws, int64_t ws_bytes, hipStream_t st) {
   hipError_t err;
+  const FusedLayout f = fused_layout(q.max_rows, q.H, q.D, q.L);
   if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
   FusedArgs a{};
   a.offsets = q.offsets;
@@ -361,9 +471,14 @@ hipError_t launch_ffn_fused(const FfnBf16Params& q, int32_t* ctl, hipStream_t st
   a.s_d = q.down_scales;
   a.alpha = q.alpha;
   a.limit = q.limit;
-  a.act = q.act;
+  a.act = (uint16_t*)((uint8_t*)ws + f.act_off);
   a.out = q.out;
-  a.ctl = ctl;
+  a.ctl = (int32_t*)ws;
+  a.arrive = (int32_t*)((uint8_t*)ws + (ws_bytes & ~(int64_t)3)) - f.row_blocks;
+  a.part = (float*)((uint8_t*)ws + f.part_off);
+  a.S = f.S;
+  a.tiles_cap = f.tiles_cap;
+  a.row_blocks = (int)f.row_blocks;
   if (q.act_kind == ACT_SILU) err = launch_fused_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
   else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);
   else err = launch_fused_act<ACT_GELU_TANH>(a, q.fmt, q.out_bf16, st);

@@ -115,8 +115,23 @@ hipError_t launch_ffn_w4a16(const FfnMxParams& p, hipStream_t st);
 // (queue, exit count, error, one arrival counter per 32-row block) at the
 // start of the workspace, then A; zero when allocated, zero again after
 // every launch.
-int64_t fused_ctl_words(int64_t max_rows, int L);
-hipError_t launch_ffn_fused(const FfnBf16Params& p, int32_t* ctl, hipStream_t st);
+// Workspace of the single-launch FFN, byte offsets from its start:
+//   [0, act_off)          queue head, exit count, error word, unused, then one
+//                         parts-done counter per split L2 tile
+//   [act_off, part_off)   A, bf16 [max_rows, D]
+//   [part_off, ...)       tiles_cap * S fp32 partial tiles of 32 x 256
+//   the last row_blocks int32 of the caller's buffer: arrival counters
+// The counters are zero between launches; the layout of a smaller max_rows
+// with the same H, D, L lies inside that of a larger one.
+struct FusedLayout {
+  int64_t row_blocks;   // bound on the 32-row blocks of the launch
+  int S;                // K parts of a split L2 tile (1: no split)
+  int tiles_cap;        // L2 tiles the partial slots hold
+  int64_t act_off, part_off, bytes;
+};
+FusedLayout fused_layout(int64_t max_rows, int H, int D, int L);
+// p.act is ignored: A lives in the workspace at act_off
+hipError_t launch_ffn_fused(const FfnBf16Params& p, void* ws, int64_t ws_bytes, hipStream_t st);
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,

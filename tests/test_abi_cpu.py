@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_struct_layouts_match_header_sizes():
@@ -164,9 +164,29 @@ def test_grouped_ffn_fused_validation(kw, status, frag):
 
 def test_fused_workspace_bytes():
     lib = m.lib()
-    # A in bf16, then 4 control words and one arrival counter per possible 32-row block
-    assert lib.moe_ffn_fused_workspace_bytes(64, 512, 8) == 64 * 512 * 2 + 256
-    assert lib.moe_ffn_fused_workspace_bytes(8192, 14336, 8) == 8192 * 14336 * 2 + ((4 + 256 + 8) * 4 + 255) // 256 * 256
+    hdr = 1280    # 4 control words + 256 split counters, rounded up to 256 bytes
+
+    def rb(R, L):  # bound on the 32-row blocks: ceil(R/32) plus one partial block per expert with rows
+        return -(-R // 32) + min(L, R)
+
+    def up(b):
+        return -(-b // 256) * 256
+
+    # D < 3 H: no split, so no partial tiles
+    assert lib.moe_ffn_fused_workspace_bytes(64, 512, 256, 8) == hdr + 64 * 256 * 2 + up(4 * rb(64, 8))
+    assert lib.moe_ffn_fused_workspace_bytes(64, 512, 1408, 8) == hdr + 64 * 1408 * 2 + up(4 * rb(64, 8))
+    # Mixtral decode, 128 rows: D/H = 3.5 -> 2 parts; 12 row blocks x 16 column tiles = 192 tiles
+    assert lib.moe_ffn_fused_workspace_bytes(128, 4096, 14336, 8) == (
+        hdr + 128 * 14336 * 2 + 192 * 2 * 32 * 256 * 4 + up(4 * 12))
+    # many rows: the split tiles are capped at 256
+    assert lib.moe_ffn_fused_workspace_bytes(8192, 4096, 14336, 8) == (
+        hdr + 8192 * 14336 * 2 + 256 * 2 * 32 * 256 * 4 + up(4 * rb(8192, 8)))
+    # parts are capped at 8
+    assert lib.moe_ffn_fused_workspace_bytes(32, 256, 8192, 1) == hdr + 32 * 8192 * 2 + 2 * 8 * 32 * 256 * 4 + 256
+    # a smaller max_rows needs no more
+    assert lib.moe_ffn_fused_workspace_bytes(17, 4096, 14336, 8) <= lib.moe_ffn_fused_workspace_bytes(128, 4096, 14336, 8)
+    assert lib.moe_ffn_fused_workspace_bytes(0, 4096, 14336, 8) == hdr
+    assert lib.moe_ffn_fused_workspace_bytes(-1, 4096, 14336, 8) == 0
 
 
 def _idx(**kw):

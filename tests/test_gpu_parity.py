@@ -663,6 +663,8 @@ def test_mx_w4a16_layer_full_size(moe):
      "gate_up_format": "interleaved", "has_bias": True},
     {"T": 200, "E": 5, "k": 3, "H": 320, "D": 128, "activation": "gelu_tanh", "has_bias": True},
     {"T": 9, "E": 64, "k": 6, "H": 1024, "D": 512},          # most experts empty, single rows
+    {"T": 50, "E": 4, "k": 2, "H": 320, "D": 1664, "has_bias": True},  # down split in 3 uneven parts, N tail
+    {"T": 33, "E": 3, "k": 1, "H": 128, "D": 1152, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0},  # 5 parts
 ])
 def test_fused_ffn_layer(moe, changes):
     """The single-launch FFN against the oracle, twice in a row on the same
@@ -706,6 +708,26 @@ def test_fused_ffn_then_smaller_batch(moe):
     _check_layer(big, inp_b, rb, np.arange(big.T), BF16_TOL)
     _check_layer(small, inp_s, rs, np.arange(small.T), BF16_TOL)
     assert moe.fused_error_word(lb.act_ws) == 0
+
+
+def test_fused_ffn_big_small_big(moe):
+    """One workspace sized for 4096 rows, called with 4096, then 34, then
+    4096 rows again: a smaller call must not disturb the control words a
+    larger call needs (the arrival counters sit at the end of the buffer,
+    A and the split partials in front of them)."""
+    big = synth.scaled(synth.get_config(8), T=2048, H=256, D=1024)
+    small = synth.scaled(big, T=17)
+    inp_b, inp_s = _gen(big), synth.make_inputs(small, DEV, salt=5)
+    say("[fused] T=2048, T=17, T=2048 on one workspace (down split in 2 parts)")
+    lb = moe.MoELayer(big, inp_b)
+    ls = moe.MoELayer(small, inp_s)
+    ls.act_ws = lb.act_ws
+    for name, layer, cfg, inp in (("big", lb, big, inp_b), ("small", ls, small, inp_s), ("big again", lb, big, inp_b)):
+        res = layer.forward(inp["x"])
+        torch.cuda.synchronize()
+        say(f"  {name}")
+        _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+        assert moe.fused_error_word(lb.act_ws) == 0, name
 
 
 def test_fused_ffn_full_size(moe):
