@@ -430,17 +430,24 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
           const f32x4_t v = {acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1], acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]};
           *(f32x4_t*)(mine + ((((mi * NI + ni) * 4 + q) * NTHREADS) + tid) * 4) = v;
         }
-    __threadfence();
+    // The barrier orders every wave's partial stores before thread 0's
+    // agent-scope release (one L2 write-back for the workgroup); the last
+    // part's thread 0 acquires once, and the barrier orders the other waves'
+    // partial loads after it.
     __syncthreads();
     int32_t* s_flag = (int32_t*)smem;
     if (tid == 0) {
-      const int old = atomicAdd(&p.counters[tile - full], 1);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const int old = __hip_atomic_fetch_add(&p.counters[tile - full], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_flag[0] = (old == S - 1);
-      if (old == S - 1) p.counters[tile - full] = 0;  // ready for the next launch
+      if (old == S - 1) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // every part has counted in: ready for the next launch
+        __hip_atomic_store(&p.counters[tile - full], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __syncthreads();
     if (s_flag[0] == 0) return;
-    __threadfence();
     const float* first = p.partial + (int64_t)(tile - full) * S * (BM * BN);
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
