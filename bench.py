@@ -102,6 +102,9 @@ EXTRA_TRACES = [
     ("trace7", 7, "mxfp4_w4a16_decode_kernel_stats.txt",
      "MXFP4 W4A16 layer on a decode-sized batch: T=256 tokens, hidden 7168, 256 experts, top-8 sigmoid "
      "router, moe_dim 2048, SiLU"),
+    ("trace8", 8, "mixtral_decode_fused_ffn_kernel_stats.txt",
+     "Mixtral decode batch through the single-launch FFN: T=64 tokens, hidden 4096, 8 experts, top-2 softmax "
+     "router, moe_dim 14336, SiLU"),
 ]
 
 
