@@ -382,9 +382,9 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // buffer load
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // retire this step's fragment reads before the next step's MFMAs
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
+      // no wait here: the compiler waits for each fragment where an MFMA
+      // first uses it, so the next step's early MFMAs overlap the tail of
+      // this step's reads
     }
   };
 
