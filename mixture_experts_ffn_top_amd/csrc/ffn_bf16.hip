@@ -219,20 +219,22 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, BUF_DWORD3);
   const uint32_t a_row_bytes = (uint32_t)p.lda * 2u, b_row_bytes = (uint32_t)p.ldb * 2u;
-  uint32_t a_off[LPW_A], b_off[LPW_B];  // byte offset of this lane's row
-  int a_chunk[LPW_A], b_chunk[LPW_B];
+  // the swizzled chunk this lane fetches for load block i (recomputed where
+  // needed rather than kept in registers)
+  auto a_chunk = [&](int i) { return (lane % CPR) ^ swz_f((wave * LPW_A + i) * RPB + lrow); };
+  auto b_chunk = [&](int i) { return (lane % CPR) ^ swz_f((wave * LPW_B + i) * RPB + lrow); };
+  // byte offset of this lane's row plus its chunk, fixed for the tile
+  uint32_t a_voff[LPW_A], b_voff[LPW_B];
 #pragma unroll
   for (int i = 0; i < LPW_A; ++i) {
     const int trow = (wave * LPW_A + i) * RPB + lrow;  // tile row
-    a_chunk[i] = (lane % CPR) ^ swz_f(trow);
     const int r = min(row_beg + trow, row_end - 1);
     const uint32_t arow = GATHER ? (uint32_t)p.sorted_token[r] : (uint32_t)r;
-    a_off[i] = arow * a_row_bytes;
+    a_voff[i] = arow * a_row_bytes + (uint32_t)a_chunk(i) * 16u;
   }
 #pragma unroll
   for (int i = 0; i < LPW_B; ++i) {
     const int trow = (wave * LPW_B + i) * RPB + lrow;  // tile row
-    b_chunk[i] = (lane % CPR) ^ swz_f(trow);
     int wrow;
     if (MODE == MODE_DOWN) {
       wrow = min(nb * BN + trow, p.N - 1);
@@ -242,18 +244,13 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       const int oc = min(nb * NBO + q * (WTN / 2) + j, p.N - 1);
       wrow = (FMT == FMT_CONCAT) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
     }
-    b_off[i] = (uint32_t)wrow * b_row_bytes;
+    b_voff[i] = (uint32_t)wrow * b_row_bytes + (uint32_t)b_chunk(i) * 16u;
   }
   const int KTF = p.K / BK;              // full k stages
   const int KT_ALL = (p.K + BK - 1) / BK;  // all k stages (the last may be ragged)
   // this workgroup's k stages [KB, KT): all of them, or one part of a split tile
   const int KB = split ? part * KT_ALL / S : 0;
   const int KT = split ? (part + 1) * KT_ALL / S : KT_ALL;
-  uint32_t a_voff[LPW_A], b_voff[LPW_B];
-#pragma unroll
-  for (int i = 0; i < LPW_A; ++i) a_voff[i] = a_off[i] + (uint32_t)a_chunk[i] * 16u;
-#pragma unroll
-  for (int i = 0; i < LPW_B; ++i) b_voff[i] = b_off[i] + (uint32_t)b_chunk[i] * 16u;
 
   // A (activation rows) is double buffered, B (weight rows) triple buffered.
   // Stage kt's A goes to buffer kt % 2 and its B to buffer kt % 3.
@@ -268,8 +265,10 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       // chunks past K are zeroed in LDS before the stage is published
 #pragma unroll
       for (int i = 0; i < LPW_A; ++i) {
-        const uint32_t kb = (uint32_t)min(kt * BK + a_chunk[i] * 8, p.K - 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)((char*)dst + i * 1024), 16, a_off[i] + kb, 0, 0, 0);
+        const int c = a_chunk(i);
+        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, p.K - 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)((char*)dst + i * 1024), 16,
+                                                 a_voff[i] - (uint32_t)c * 16u + kb, 0, 0, 0);
       }
     }
   };
@@ -282,8 +281,10 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     } else {
 #pragma unroll
       for (int i = 0; i < LPW_B; ++i) {
-        const uint32_t kb = (uint32_t)min(kt * BK + b_chunk[i] * 8, p.K - 8) * 2u;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16, b_off[i] + kb, 0, 0, 0);
+        const int c = b_chunk(i);
+        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, p.K - 8) * 2u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16,
+                                                 b_voff[i] - (uint32_t)c * 16u + kb, 0, 0, 0);
       }
     }
   };
@@ -303,7 +304,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < LPW_A; ++i)
-        if (kt * BK + a_chunk[i] * 8 >= p.K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
+        if (kt * BK + a_chunk(i) * 8 >= p.K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
     }
   };
 
