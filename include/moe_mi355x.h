@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -422,6 +422,132 @@ moe_status_t moe_combine(const moe_combine_args_t* args, void* stream);
  * ---------------------------------------------------------------------- */
 moe_status_t moe_shared_indices(int32_t num_tokens, int32_t n_shared, int32_t* expert_offsets,
                                 int32_t* sorted_token, void* stream);
+
+/* ========================================================================
+ * Backward pass (routed experts, bf16 operands).  With dy = dL/dy the
+ * gradients follow the forward by the chain rule:
+ *   moe_combine_backward      dO[p] = w[t,j] dy[t],  dw[t,j] = <dy[t], O[p]>
+ *   moe_grouped_ffn_backward  dX, dW_gu, dW_d, db_gu, db_d from dO
+ *   moe_combine (weights NULL, out_dtype FP32) on dX then gives dx[t].
+ * The per-expert bias gradients are [NeMoExperts]' deterministic
+ * bias-gradient reduction (_DeterministicBiasRepeatInterleave.backward,
+ * _reduce_bias_grad_triton): one compensated fp32 sum per expert over its
+ * contiguous rows, no atomics.  Every result is deterministic.
+ * ===================================================================== */
+
+/* ------------------------------------------------------------------------
+ * moe_combine_backward -- backward of moe_combine ([NeMoExperts]
+ * GroupedExperts.forward; the down bias sits inside the weighting,
+ * _apply_bias):
+ *   d_expert_out[row_of_slot[t,j]] = expert_weights[t,j] * dy[t]   (bf16)
+ *   d_expert_weights[t,j]          = <dy[t], expert_out[row]>      (fp32)
+ * for the kept slots of valid tokens; dropped slots and masked tokens get
+ * d_expert_weights 0 and write no row.
+ *
+ *   num_tokens T, n_experts_per_tok k, hidden_dim H (multiple of 8)  host
+ *   dy              bf16 [T, H]
+ *   expert_out      O [*, H], fp32 or bf16 (out_dtype); read only when
+ *                   d_expert_weights is not NULL
+ *   row_of_slot     int32 [T, k]; expert_weights fp32 [T, k] or NULL (1)
+ *   token_mask      uint8 [T] or NULL
+ *   d_expert_out    bf16 [rows, H] out (the rows row_of_slot names)
+ *   d_expert_weights fp32 [T, k] out, or NULL
+ * ---------------------------------------------------------------------- */
+typedef struct moe_combine_backward_args {
+  int32_t num_tokens;
+  int32_t n_experts_per_tok;
+  int32_t hidden_dim;
+  const void* dy;
+  const void* expert_out;
+  int32_t out_dtype;
+  const int32_t* row_of_slot;
+  const float* expert_weights;
+  const uint8_t* token_mask;
+  void* d_expert_out;
+  float* d_expert_weights;
+} moe_combine_backward_args_t;
+
+moe_status_t moe_combine_backward(const moe_combine_backward_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_ffn_backward -- backward of moe_grouped_ffn for bf16 operands
+ * ([StackedMoE] weight shapes; [GatedAct] activations; [MegaFFN] per-leg
+ * expert scales, held constant; [NeMoExperts] bias reduction).  For each CSR
+ * row p of local expert e, with h = s_gu (x . W_gu^T) + b_gu recomputed:
+ *   dA    = s_d * dO . W_d                (bf16, in the workspace)
+ *   dH    = [dA * dact/dgate, dA * dact/dup] in W_gu's column order (bf16;
+ *           a clamp passes the gradient inside its closed range)
+ *   d_x_perm[p]     = s_gu * dH . W_gu                        fp32 [max_rows, H]
+ *   d_w_gate_up[e]  = s_gu * sum_p dH[p]^T x[p]               fp32 [L, 2D, H]
+ *   d_w_down[e]     = s_d  * sum_p dO[p]^T A[p]               fp32 [L, H, D]
+ *   d_b_gate_up[e]  = sum_p dH[p],  d_b_down[e] = sum_p dO[p] fp32, or NULL
+ * The weight gradients have the OUT_IN layout of the forward's weights;
+ * experts with no rows get zero gradients.
+ *
+ *   max_rows, hidden_dim H, moe_dim D (both multiples of 64), n_local_experts L  host
+ *   expert_offsets  int32 [L+1], as for moe_grouped_ffn
+ *   x + sorted_token (gather) or x_perm, bf16, as for moe_grouped_ffn
+ *   w_gate_up       bf16 [L, 2D, H]  the forward's OUT_IN view
+ *   w_gate_up_stacked bf16 [L, H, 2D] and w_down_stacked bf16 [L, D, H]:
+ *                   the same weights in [StackedMoE]'s stacked shapes (see
+ *                   moe_transpose_bf16); the forward's w_down is not needed
+ *   b_gate_up       bf16 [L, 2D] or NULL; gate_up_format, activation, alpha,
+ *                   limit, gate_up_expert_scales, down_expert_scales as for
+ *                   the forward
+ *   d_expert_out    dO, bf16 [max_rows, H] (moe_combine_backward's output)
+ *   workspace       moe_ffn_backward_workspace_bytes(max_rows, H, D, L)
+ *                   bytes, no initial contents: dA, the recomputed A, dH and
+ *                   transposed copies of dO, A, dH and the rows of x (every
+ *                   expert's rows padded to a multiple of 64)
+ *   timing_events   NULL or 8 caller-created hipEvent_t recorded: start,
+ *                   after dA, after the recompute, after dX, after the
+ *                   transposes, after dW_d, after dW_gu, at the end
+ * Errors as for moe_grouped_ffn; each buffer that goes through the GEMM
+ * loads (the row buffers, their transposed copies, one expert's weights)
+ * must be under 2 GiB.
+ * ---------------------------------------------------------------------- */
+typedef struct moe_ffn_backward_args {
+  int32_t max_rows;
+  int32_t hidden_dim;
+  int32_t moe_dim;
+  int32_t n_local_experts;
+  const int32_t* expert_offsets;
+  const void* x;
+  const int32_t* sorted_token;
+  const void* x_perm;
+  const void* w_gate_up;
+  const void* w_gate_up_stacked;
+  const void* w_down_stacked;
+  const void* b_gate_up;
+  int32_t gate_up_format;
+  int32_t activation;
+  float alpha;
+  float limit;
+  const float* gate_up_expert_scales;
+  const float* down_expert_scales;
+  const void* d_expert_out;
+  float* d_x_perm;
+  float* d_w_gate_up;
+  float* d_w_down;
+  float* d_b_gate_up;
+  float* d_b_down;
+  void* workspace;
+  int64_t workspace_bytes;
+  void* timing_events;
+} moe_ffn_backward_args_t;
+
+moe_status_t moe_grouped_ffn_backward(const moe_ffn_backward_args_t* args, void* stream);
+int64_t moe_ffn_backward_workspace_bytes(int32_t max_rows, int32_t hidden_dim, int32_t moe_dim,
+                                         int32_t n_local_experts);
+
+/* ------------------------------------------------------------------------
+ * moe_transpose_bf16 -- dst[b][c][r] = src[b][r][c] for a [batch, rows, cols]
+ * bf16 tensor: converts between [StackedMoE]'s stacked weight shapes and the
+ * transposed (OUT_IN) views.  rows and cols are multiples of 64; src and dst
+ * are distinct, 16-byte aligned device buffers.
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_transpose_bf16(const void* src, void* dst, int32_t batch, int32_t rows, int32_t cols,
+                                void* stream);
 
 /* Helpers. */
 const char* moe_status_string(moe_status_t status);

@@ -73,9 +73,26 @@ class CombineArgs(ctypes.Structure):
                 ("shared_out", _vp), ("shared_weights", _vp)]
 
 
+class CombineBwdArgs(ctypes.Structure):
+    _fields_ = [("num_tokens", _i32), ("n_experts_per_tok", _i32), ("hidden_dim", _i32), ("dy", _vp),
+                ("expert_out", _vp), ("out_dtype", _i32), ("row_of_slot", _vp), ("expert_weights", _vp),
+                ("token_mask", _vp), ("d_expert_out", _vp), ("d_expert_weights", _vp)]
+
+
+class FfnBwdArgs(ctypes.Structure):
+    _fields_ = [("max_rows", _i32), ("hidden_dim", _i32), ("moe_dim", _i32), ("n_local_experts", _i32),
+                ("expert_offsets", _vp), ("x", _vp), ("sorted_token", _vp), ("x_perm", _vp),
+                ("w_gate_up", _vp), ("w_gate_up_stacked", _vp), ("w_down_stacked", _vp), ("b_gate_up", _vp),
+                ("gate_up_format", _i32), ("activation", _i32), ("alpha", _f32), ("limit", _f32),
+                ("gate_up_expert_scales", _vp), ("down_expert_scales", _vp), ("d_expert_out", _vp),
+                ("d_x_perm", _vp), ("d_w_gate_up", _vp), ("d_w_down", _vp), ("d_b_gate_up", _vp),
+                ("d_b_down", _vp), ("workspace", _vp), ("workspace_bytes", _i64), ("timing_events", _vp)]
+
+
 ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_grouped_ffn_fused", "moe_combine",
                 "moe_shared_indices", "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
-                "moe_ffn_fused_workspace_bytes",
+                "moe_ffn_fused_workspace_bytes", "moe_combine_backward", "moe_grouped_ffn_backward",
+                "moe_ffn_backward_workspace_bytes", "moe_transpose_bf16",
                 "moe_status_string", "moe_last_error_message", "moe_abi_version")
 
 
@@ -85,7 +102,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     for name, argt in (("moe_route", RouteArgs), ("moe_build_indices", IndexArgs),
                        ("moe_grouped_ffn", FfnArgs), ("moe_grouped_ffn_fused", FfnArgs),
-                       ("moe_combine", CombineArgs)):
+                       ("moe_combine", CombineArgs), ("moe_combine_backward", CombineBwdArgs),
+                       ("moe_grouped_ffn_backward", FfnBwdArgs)):
         f = getattr(lib, name)
         f.argtypes = [ctypes.POINTER(argt), _vp]
         f.restype = _i32
@@ -95,6 +113,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_workspace_bytes.restype = _i64
     lib.moe_ffn_fused_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
     lib.moe_ffn_fused_workspace_bytes.restype = _i64
+    lib.moe_ffn_backward_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32]
+    lib.moe_ffn_backward_workspace_bytes.restype = _i64
+    lib.moe_transpose_bf16.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp]
+    lib.moe_transpose_bf16.restype = _i32
     lib.moe_status_string.argtypes = [_i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -294,6 +316,79 @@ def combine(expert_out, row_of_slot, T: int, k: int, *, weights=None, token_mask
     return y
 
 
+def combine_backward(dy, row_of_slot, n_rows: int, k: int, *, expert_out=None, weights=None, token_mask=None,
+                     out=None, weight_grad=True):
+    """moe_combine_backward.  Returns (dO bf16 [n_rows, H], dw fp32 [T, k] or
+    None): dO[row_of_slot[t, j]] = w[t, j] dy[t] and dw[t, j] = <dy[t], O[row]>
+    (weight_grad needs expert_out)."""
+    _dt(dy, torch.bfloat16, "dy")
+    T, H = dy.shape
+    dev = dy.device
+    dO = out if out is not None else torch.empty((max(n_rows, 1), H), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((T, k), dtype=torch.float32, device=dev) if weight_grad else None
+    o_dt = DTYPE_BF16 if expert_out is not None and expert_out.dtype == torch.bfloat16 else DTYPE_FP32
+    a = CombineBwdArgs(num_tokens=T, n_experts_per_tok=k, hidden_dim=H, dy=_ptr(dy), expert_out=_ptr(expert_out),
+                       out_dtype=o_dt, row_of_slot=_ptr(row_of_slot), expert_weights=_ptr(weights),
+                       token_mask=_ptr(token_mask), d_expert_out=_ptr(dO), d_expert_weights=_ptr(dw))
+    _check(lib().moe_combine_backward(ctypes.byref(a), _stream(dev)))
+    return dO, dw
+
+
+def ffn_backward_workspace(max_rows: int, H: int, D: int, L: int, device) -> torch.Tensor:
+    """The workspace of moe_grouped_ffn_backward (no initial contents needed)."""
+    n = lib().moe_ffn_backward_workspace_bytes(max_rows, H, D, L)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def grouped_ffn_backward(offsets, max_rows: int, weights: "ExpertWeights", d_expert_out, *, x=None,
+                         sorted_token=None, x_perm=None, activation="silu", alpha=0.0, limit=0.0,
+                         gate_up_format="concatenated", gate_up_expert_scales=None, down_expert_scales=None,
+                         workspace=None, grads=None, bias_grads=None, timing_events=None):
+    """moe_grouped_ffn_backward (bf16).  Returns a dict: d_x_perm fp32
+    [max_rows, H], d_w_gate_up fp32 [L, 2D, H], d_w_down fp32 [L, H, D], and
+    d_b_gate_up [L, 2D] / d_b_down [L, H] when bias_grads (default: when the
+    weights have biases).  `grads` may hold preallocated outputs."""
+    if weights.operand != "bf16" or weights.w_gate_up_stacked is None:
+        raise ValueError("the backward runs on bf16 weights with their stacked views")
+    dev = offsets.device
+    L, H, D = weights.L, weights.H, weights.D
+    if bias_grads is None:
+        bias_grads = weights.b_gate_up is not None
+    g = dict(grads or {})
+    g.setdefault("d_x_perm", torch.empty((max(max_rows, 1), H), dtype=torch.float32, device=dev))
+    g.setdefault("d_w_gate_up", torch.empty((L, 2 * D, H), dtype=torch.float32, device=dev))
+    g.setdefault("d_w_down", torch.empty((L, H, D), dtype=torch.float32, device=dev))
+    if bias_grads:
+        g.setdefault("d_b_gate_up", torch.empty((L, 2 * D), dtype=torch.float32, device=dev))
+        g.setdefault("d_b_down", torch.empty((L, H), dtype=torch.float32, device=dev))
+    if workspace is None:
+        workspace = ffn_backward_workspace(max_rows, H, D, L, dev)
+    _dt(offsets, torch.int32, "offsets")
+    _dt(d_expert_out, torch.bfloat16, "d_expert_out")
+    a = FfnBwdArgs(max_rows=max_rows, hidden_dim=H, moe_dim=D, n_local_experts=L, expert_offsets=_ptr(offsets),
+                   x=_ptr(x), sorted_token=_ptr(sorted_token), x_perm=_ptr(x_perm),
+                   w_gate_up=_ptr(weights.w_gate_up), w_gate_up_stacked=_ptr(weights.w_gate_up_stacked),
+                   w_down_stacked=_ptr(weights.w_down_stacked), b_gate_up=_ptr(weights.b_gate_up),
+                   gate_up_format=FMT[gate_up_format], activation=ACT[activation], alpha=alpha,
+                   limit=limit, gate_up_expert_scales=_ptr(gate_up_expert_scales),
+                   down_expert_scales=_ptr(down_expert_scales), d_expert_out=_ptr(d_expert_out),
+                   d_x_perm=_ptr(g["d_x_perm"]), d_w_gate_up=_ptr(g["d_w_gate_up"]), d_w_down=_ptr(g["d_w_down"]),
+                   d_b_gate_up=_ptr(g.get("d_b_gate_up")), d_b_down=_ptr(g.get("d_b_down")),
+                   workspace=_ptr(workspace), workspace_bytes=workspace.numel(),
+                   timing_events=ctypes.cast(timing_events, ctypes.c_void_p) if timing_events is not None else None)
+    _check(lib().moe_grouped_ffn_backward(ctypes.byref(a), _stream(dev)))
+    return g
+
+
+def transpose_bf16(src, out=None):
+    """moe_transpose_bf16: [B, R, C] -> [B, C, R] (bf16, R and C multiples of 64)."""
+    _dt(src, torch.bfloat16, "src")
+    B, R, C = src.shape
+    dst = out if out is not None else torch.empty((B, C, R), dtype=torch.bfloat16, device=src.device)
+    _check(lib().moe_transpose_bf16(_ptr(src), _ptr(dst), B, R, C, _stream(src.device)))
+    return dst
+
+
 def shared_indices(T: int, n_shared: int, device):
     """moe_shared_indices.  Returns (offsets int32 [n_shared+1], sorted_token
     int32 [n_shared*T]): the buckets of the shared experts, every token in each."""
@@ -326,6 +421,9 @@ class ExpertWeights:
     w_down_scale: torch.Tensor | None = None
     b_gate_up: torch.Tensor | None = None
     b_down: torch.Tensor | None = None
+    # bf16: the stacked [L, H, 2D] / [L, D, H] views, which the backward reads
+    w_gate_up_stacked: torch.Tensor | None = None
+    w_down_stacked: torch.Tensor | None = None
 
     @staticmethod
     def from_stacked(w_gate_up, w_down, *, b_gate_up=None, b_down=None, w_gate_up_scale=None,
@@ -345,6 +443,7 @@ class ExpertWeights:
                                  b_gate_up, b_down)
         L, H, D2 = w_gate_up.shape
         D = D2 // 2
+        stacked = (w_gate_up.contiguous(), w_down.contiguous()) if operand == "bf16" else (None, None)
         if layout == WEIGHT_OUT_IN:
             w_gate_up = w_gate_up.transpose(1, 2).contiguous()
             w_down = w_down.transpose(1, 2).contiguous()
@@ -352,7 +451,7 @@ class ExpertWeights:
                 w_gate_up_scale = w_gate_up_scale.transpose(1, 2).contiguous()
                 w_down_scale = w_down_scale.transpose(1, 2).contiguous()
         return ExpertWeights(w_gate_up, w_down, L, H, D, operand, layout, w_gate_up_scale,
-                             w_down_scale, b_gate_up, b_down)
+                             w_down_scale, b_gate_up, b_down, stacked[0], stacked[1])
 
 
 class MoELayer:
@@ -449,10 +548,38 @@ class MoELayer:
                     n_shared=self.n_shared)
         if mark:
             mark(3)
+        self.last = {"x": x, "weights": w, "index": ind, "O": O, "token_mask": token_mask, "x_gather": xg}
         return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O,
                 "O_shared": O_sh}
 
+    def backward(self, dy, *, workspace=None, timing_events=None, weight_grad=True):
+        """Backward of the routed experts of the last forward (bf16 layers,
+        routing held fixed): returns dx bf16 [T, H], the router-weight
+        gradient dw [T, k], dO, and the expert weight and bias gradients."""
+        c = self.cfg
+        if c.operand_dtype != "bf16":
+            raise ValueError("the backward is built for bf16 layers")
+        if self.n_shared:
+            raise ValueError("the backward covers the routed experts only")
+        f = self.last
+        ind = f["index"]
+        dO, dw = combine_backward(dy, ind["row_of_slot"], self.R, c.k, expert_out=f["O"], weights=f["weights"],
+                                  token_mask=f["token_mask"], weight_grad=weight_grad)
+        if workspace is None:
+            if getattr(self, "bwd_ws", None) is None:
+                self.bwd_ws = ffn_backward_workspace(self.R, c.H, c.D, c.E, self.device)
+            workspace = self.bwd_ws
+        g = grouped_ffn_backward(ind["offsets"], self.R, self.w, dO, x=f["x_gather"],
+                                 sorted_token=ind["sorted_token"] if self.gather else None,
+                                 x_perm=ind.get("x_perm"), activation=c.activation, alpha=c.alpha, limit=c.limit,
+                                 gate_up_format=c.gate_up_format, workspace=workspace,
+                                 timing_events=timing_events)
+        dx = combine(g["d_x_perm"], ind["row_of_slot"], c.T, c.k, weights=None, token_mask=f["token_mask"])
+        g.update({"dx": dx, "dw": dw, "dO": dO})
+        return g
+
 
 __all__ = ["lib", "route", "build_indices", "grouped_ffn", "combine", "shared_indices", "ExpertWeights", "MoELayer",
-           "ffn_workspace", "fused_error_word",
+           "ffn_workspace", "fused_error_word", "combine_backward", "grouped_ffn_backward", "ffn_backward_workspace",
+           "transpose_bf16",
            "MoEError", "load_library", "ENTRY_POINTS", "LIB_PATH"]

@@ -468,4 +468,126 @@ moe_status_t moe_shared_indices(int32_t T, int32_t n_shared, int32_t* expert_off
                     "moe_shared_indices");
 }
 
+// ---------------------------------------------------------------- backward
+moe_status_t moe_combine_backward(const moe_combine_backward_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_combine_backward: args is NULL");
+  const int T = a->num_tokens, k = a->n_experts_per_tok, H = a->hidden_dim;
+  REQUIRE(T >= 0, "moe_combine_backward: num_tokens must be >= 0 (got %d)", T);
+  REQUIRE(k >= 1 && k <= 1024, "moe_combine_backward: n_experts_per_tok must be in [1, 1024] (got %d)", k);
+  REQUIRE(H >= 8 && H % 8 == 0, "moe_combine_backward: hidden_dim must be a positive multiple of 8 (got %d)", H);
+  REQUIRE(a->out_dtype == MOE_DTYPE_FP32 || a->out_dtype == MOE_DTYPE_BF16,
+          "moe_combine_backward: out_dtype must be FP32 or BF16");
+  REQUIRE(T == 0 || (a->dy && a->row_of_slot && a->d_expert_out),
+          "moe_combine_backward: dy, row_of_slot and d_expert_out are required");
+  REQUIRE(T == 0 || a->d_expert_weights == nullptr || a->expert_out != nullptr,
+          "moe_combine_backward: expert_out is required for d_expert_weights");
+  REQUIRE(aligned16(a->dy) && aligned16(a->expert_out) && aligned16(a->d_expert_out),
+          "moe_combine_backward: dy, expert_out and d_expert_out must be 16-byte aligned");
+  moe::CombineBwdParams q{};
+  q.T = T;
+  q.k = k;
+  q.H = H;
+  q.dy = (const uint16_t*)a->dy;
+  q.O = a->expert_out;
+  q.o_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+  q.row_of_slot = a->row_of_slot;
+  q.w = a->expert_weights;
+  q.mask = a->token_mask;
+  q.dO = (uint16_t*)a->d_expert_out;
+  q.dw = a->d_expert_weights;
+  return hip_status(moe::launch_combine_backward(q, (hipStream_t)stream), "moe_combine_backward");
+}
+
+int64_t moe_ffn_backward_workspace_bytes(int32_t max_rows, int32_t H, int32_t D, int32_t L) {
+  if (max_rows < 0 || H < 1 || D < 1 || L < 1) return 0;
+  return moe::ffn_bwd_layout(max_rows, H, D, L).bytes;
+}
+
+moe_status_t moe_grouped_ffn_backward(const moe_ffn_backward_args_t* a, void* stream) {
+  REQUIRE(a != nullptr, "moe_grouped_ffn_backward: args is NULL");
+  const int R = a->max_rows, H = a->hidden_dim, D = a->moe_dim, L = a->n_local_experts;
+  REQUIRE(R >= 0, "moe_grouped_ffn_backward: max_rows must be >= 0 (got %d)", R);
+  REQUIRE(H >= 64 && H % 64 == 0, "moe_grouped_ffn_backward: hidden_dim must be a positive multiple of 64 (got %d)",
+          H);
+  REQUIRE(D >= 64 && D % 64 == 0, "moe_grouped_ffn_backward: moe_dim must be a positive multiple of 64 (got %d)", D);
+  REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn_backward: n_local_experts must be in [1, 1024] (got %d)", L);
+  REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI || a->activation == MOE_ACT_GELU_TANH,
+          "moe_grouped_ffn_backward: unknown activation %d", a->activation);
+  REQUIRE(std::isfinite(a->alpha) && std::isfinite(a->limit),
+          "moe_grouped_ffn_backward: alpha and limit must be finite");
+  REQUIRE(a->activation == MOE_ACT_SWIGLUOAI || a->alpha == 0.0f,
+          "moe_grouped_ffn_backward: alpha is the sigmoid scale of swigluoai and must be 0 for the other activations");
+  REQUIRE(a->activation != MOE_ACT_GELU_TANH || a->limit == 0.0f,
+          "moe_grouped_ffn_backward: limit must be 0 for gelu_tanh");
+  REQUIRE(a->limit >= 0.0f, "moe_grouped_ffn_backward: limit must be >= 0");
+  REQUIRE(a->gate_up_format == MOE_GATE_UP_CONCATENATED || a->gate_up_format == MOE_GATE_UP_INTERLEAVED,
+          "moe_grouped_ffn_backward: unknown gate_up_format %d", a->gate_up_format);
+  REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn_backward: expert_offsets is required");
+  REQUIRE(a->w_gate_up && a->w_gate_up_stacked && a->w_down_stacked,
+          "moe_grouped_ffn_backward: w_gate_up, w_gate_up_stacked and w_down_stacked are required");
+  REQUIRE(a->d_w_gate_up && a->d_w_down, "moe_grouped_ffn_backward: d_w_gate_up and d_w_down are required");
+  REQUIRE(R == 0 || (a->d_expert_out && a->d_x_perm),
+          "moe_grouped_ffn_backward: d_expert_out and d_x_perm are required");
+  const bool gather = a->x_perm == nullptr;
+  if (gather)
+    REQUIRE(R == 0 || (a->x != nullptr && a->sorted_token != nullptr),
+            "moe_grouped_ffn_backward: pass x_perm, or x and sorted_token to gather rows");
+  else
+    REQUIRE(a->x == nullptr, "moe_grouped_ffn_backward: pass either x_perm or x/sorted_token, not both");
+  REQUIRE(aligned16(a->x_perm) && aligned16(a->x) && aligned16(a->w_gate_up) && aligned16(a->w_gate_up_stacked) &&
+              aligned16(a->w_down_stacked) && aligned16(a->b_gate_up) && aligned16(a->d_expert_out) &&
+              aligned16(a->d_x_perm) && aligned16(a->d_w_gate_up) && aligned16(a->d_w_down) &&
+              aligned16(a->workspace),
+          "moe_grouped_ffn_backward: tensors must be 16-byte aligned");
+  const moe::FfnBwdLayout f = moe::ffn_bwd_layout(R, H, D, L);
+  const int64_t two_gib = (int64_t)1 << 31;
+  REQUIRE((int64_t)R * H * 4 < two_gib && (int64_t)R * 2 * D * 2 < two_gib && (int64_t)2 * D * H * 2 < two_gib &&
+              (int64_t)2 * D * f.rp * 2 < two_gib && (int64_t)H * f.rp * 2 < two_gib,
+          "moe_grouped_ffn_backward: the row buffers, their transposed copies and one expert's weights must each be "
+          "under 2 GiB");
+  if (a->workspace_bytes < f.bytes || a->workspace == nullptr)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn_backward: workspace needs %lld bytes (got %lld)",
+                (long long)f.bytes, (long long)a->workspace_bytes);
+  moe::FfnBwdParams q{};
+  q.offsets = a->expert_offsets;
+  q.L = L;
+  q.H = H;
+  q.D = D;
+  q.max_rows = R;
+  q.x = (const uint16_t*)a->x;
+  q.sorted_token = a->sorted_token;
+  q.x_perm = (const uint16_t*)a->x_perm;
+  q.w_gate_up = (const uint16_t*)a->w_gate_up;
+  q.w_gate_up_stacked = (const uint16_t*)a->w_gate_up_stacked;
+  q.w_down_stacked = (const uint16_t*)a->w_down_stacked;
+  q.b_gate_up = (const uint16_t*)a->b_gate_up;
+  q.fmt = a->gate_up_format;
+  q.act_kind = a->activation;
+  q.alpha = a->alpha;
+  q.limit = a->limit;
+  q.gate_up_scales = a->gate_up_expert_scales;
+  q.down_scales = a->down_expert_scales;
+  q.d_out = (const uint16_t*)a->d_expert_out;
+  q.d_x_perm = a->d_x_perm;
+  q.d_w_gate_up = a->d_w_gate_up;
+  q.d_w_down = a->d_w_down;
+  q.d_b_gate_up = a->d_b_gate_up;
+  q.d_b_down = a->d_b_down;
+  q.ws = a->workspace;
+  q.events = (hipEvent_t const*)a->timing_events;
+  return hip_status(moe::launch_ffn_backward(q, (hipStream_t)stream), "moe_grouped_ffn_backward");
+}
+
+moe_status_t moe_transpose_bf16(const void* src, void* dst, int32_t batch, int32_t rows, int32_t cols, void* stream) {
+  REQUIRE(batch >= 0 && rows >= 0 && cols >= 0, "moe_transpose_bf16: sizes must be >= 0");
+  REQUIRE(rows % 64 == 0 && cols % 64 == 0, "moe_transpose_bf16: rows and cols must be multiples of 64 (got %d, %d)",
+          rows, cols);
+  REQUIRE((int64_t)batch * rows * cols == 0 || (src && dst), "moe_transpose_bf16: src and dst are required");
+  REQUIRE(src != dst || (int64_t)batch * rows * cols == 0, "moe_transpose_bf16: src and dst must not be the same buffer");
+  REQUIRE(aligned16(src) && aligned16(dst), "moe_transpose_bf16: src and dst must be 16-byte aligned");
+  return hip_status(moe::launch_transpose_bf16((const uint16_t*)src, (uint16_t*)dst, batch, rows, cols,
+                                               (hipStream_t)stream),
+                    "moe_transpose_bf16");
+}
+
 }  // extern "C"

@@ -207,6 +207,39 @@ __device__ __forceinline__ float gated_act(float g, float u, float alpha, float 
   return 0.5f * g * (1.0f + t) * u;
 }
 
+// The activation (the same float steps as gated_act) and its partial
+// derivatives with respect to the unclamped gate and up.  A clamp passes the
+// gradient where its input lies inside the closed range and blocks it outside.
+template <int ACT>
+__device__ __forceinline__ void gated_act_grad(float g0, float u0, float alpha, float limit, float& a, float& dg,
+                                               float& du) {
+  float g = g0, u = u0, mg = 1.0f, mu = 1.0f;
+  if ((ACT == ACT_SILU || ACT == ACT_SWIGLUOAI) && limit > 0.0f) {
+    g = fminf(g0, limit);
+    u = fminf(fmaxf(u0, -limit), limit);
+    mg = (g0 <= limit) ? 1.0f : 0.0f;
+    mu = (u0 >= -limit && u0 <= limit) ? 1.0f : 0.0f;
+  }
+  if (ACT == ACT_SILU) {
+    const float s = sigmoid_f32(g);
+    a = g * s * u;
+    dg = mg * (s * (1.0f + g * (1.0f - s)) * u);
+    du = mu * (g * s);
+  } else if (ACT == ACT_SWIGLUOAI) {
+    const float s = sigmoid_f32(alpha * g);
+    a = g * s * (u + 1.0f);
+    dg = mg * ((s + alpha * g * s * (1.0f - s)) * (u + 1.0f));
+    du = mu * (g * s);
+  } else {
+    const float c = 0.7978845608028654f, k = 0.044715f;
+    const float t = tanhf(c * (g + k * g * g * g));
+    const float gelu = 0.5f * g * (1.0f + t);
+    a = gelu * u;
+    dg = (0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * c * (1.0f + 3.0f * k * g * g)) * u;
+    du = gelu;
+  }
+}
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]) that wait on one counter only.
 constexpr int waitcnt_vm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }

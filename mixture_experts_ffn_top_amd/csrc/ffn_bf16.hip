@@ -35,7 +35,12 @@
 
 namespace moe {
 
-enum { MODE_GATE_UP = 0, MODE_DOWN = 1 };
+// MODE_GATE_UP_BWD recomputes the gate_up product of the backward pass: its
+// epilogue stores A again and dH = dA * d act (dA read from `din`).
+// MODE_WGRAD computes per-expert weight gradients C[e] = A_e . B_e^T, where
+// A and B are [M or N rows, K] operands whose K columns are the expert's
+// padded row segment seg[e] .. seg[e+1] (a multiple of 64, zero padded).
+enum { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_GATE_UP_BWD = 2, MODE_WGRAD = 3 };
 enum { FMT_CONCAT = 0, FMT_INTERLEAVED = 1 };
 
 static constexpr int BM = 256, BN = 256, BK = 64;
@@ -79,6 +84,15 @@ struct GemmArgs {
   int G;               // workgroups resident at once (one per CU)
   int32_t* zero;       // counters this launch clears for the next one (or nullptr)
   int n_zero;
+  // MODE_GATE_UP_BWD
+  const uint16_t* din;  // dA, bf16 [rows, N]
+  int64_t ld_din;
+  void* out2;           // dH, bf16 [rows, 2N] in W_gu's column order
+  int64_t ldo2;
+  // MODE_WGRAD
+  const int32_t* seg;   // [L+1] padded K segment of each expert
+  int M;                // rows of the A operand
+  int64_t out_estride;  // elements between experts' outputs
 };
 
 // LDS layout of one operand stage: 256 rows x BK bf16, CPR 16-byte chunks
@@ -120,6 +134,37 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   if (p.zero && blockIdx.x == 0)
     for (int i = tid; i < p.n_zero; i += NTHREADS) p.zero[i] = 0;
 
+  constexpr bool GU = (MODE == MODE_GATE_UP || MODE == MODE_GATE_UP_BWD);
+  constexpr int NBO = GU ? BN / 2 : BN;  // output columns per tile
+  // the tile: expert e, column block nb, row block mb over rows [row_beg, row_end)
+  int e, nb, mb, row_beg, row_end, K;
+  int tile = 0, part = 0, S = 1, full = 0;
+  bool split = false;
+  const char* a_base;
+  const char* b_base;
+  if constexpr (MODE == MODE_WGRAD) {
+    // fixed M x N per expert: tiles expert-major, then column block, then
+    // row block, each XCD one contiguous range
+    const int nmb_w = (p.M + BM - 1) / BM, per_e = nmb_w * ((p.N + BN - 1) / BN);
+    const int total = L * per_e, per_xcd = (total + 7) >> 3, slot = blockIdx.x >> 3;
+    if (slot >= per_xcd) return;
+    const int t = (blockIdx.x & 7) * per_xcd + slot;
+    if (t >= total) return;
+    e = __builtin_amdgcn_readfirstlane(t / per_e);
+    const int local = t % per_e;
+    nb = __builtin_amdgcn_readfirstlane(local / nmb_w);
+    mb = __builtin_amdgcn_readfirstlane(local % nmb_w);
+    row_beg = mb * BM;
+    row_end = p.M;
+    // the segment, clipped to the padded width of the operands (it only
+    // exceeds it if the row offsets exceed the rows the buffers were sized for)
+    const int width = (int)p.lda;
+    const int seg0 = __builtin_amdgcn_readfirstlane(min(p.seg[e], width));
+    K = __builtin_amdgcn_readfirstlane(max(min(p.seg[e + 1], width) - seg0, 0));
+    a_base = (const char*)(p.A + seg0);
+    b_base = (const char*)(p.W + seg0);
+  } else {
+
   // ---- prefix of 256-row blocks per expert (wave 0), in LDS
   if (wave == 0) {
     const int per = (L + 63) / 64;
@@ -147,14 +192,13 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   }
   __syncthreads();
 
-  constexpr int NBO = (MODE == MODE_GATE_UP) ? BN / 2 : BN;  // output columns per tile
   const int NB = (p.N + NBO - 1) / NBO;
   const int total = s_mbp[L] * NB;
   // Tiles run in rounds of G (one workgroup per CU).  When the last round is
   // at most half full, its `rem` tiles are split along K into S parts each
   // so that it fills the chip; the last part to finish adds the S partial
   // sums in a fixed order and runs the epilogue.
-  int rem = 0, S = 1;
+  int rem = 0;
   if (p.partial && p.G > 0) {
     const int r = total % p.G;
     if (r > 0 && 2 * r <= p.G) {
@@ -164,8 +208,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       else S = 1;
     }
   }
-  const int full = total - rem;  // a multiple of G (and of 8) when splitting
-  int tile, part = 0;
+  full = total - rem;  // a multiple of G (and of 8) when splitting
   const int slot = blockIdx.x >> 3;
   if (rem == 0) {
     const int per_xcd = (total + 7) >> 3;
@@ -186,7 +229,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       part = j % S;
     }
   }
-  const bool split = tile >= full && rem > 0;
+  split = tile >= full && rem > 0;
 
   int lo = 0, hi = L - 1;
   while (lo < hi) {
@@ -196,14 +239,19 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   }
   // uniform by construction; made scalar so that every address base below
   // lives in SGPRs
-  const int e = __builtin_amdgcn_readfirstlane(lo);
+  e = __builtin_amdgcn_readfirstlane(lo);
   const int nmb = s_mbp[e + 1] - s_mbp[e];
   const int local = __builtin_amdgcn_readfirstlane(tile - s_mbp[e] * NB);
-  const int nb = local / nmb, mb = local % nmb;
-  const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * BM);
-  const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  nb = local / nmb;
+  mb = local % nmb;
+  row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * BM);
+  row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
+  K = p.K;
+  a_base = GATHER ? (const char*)p.X : (const char*)p.A;
+  b_base = (const char*)(p.W + (int64_t)e * p.w_estride);
   __syncthreads();  // every wave has read the prefix before the loads overwrite it
+  }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   // ---- loader: buffer loads straight into LDS (buffer_load_dwordx4 ... lds),
   // no VGPR staging.  One instruction moves a 1 KB block of RPB tile rows x
@@ -214,8 +262,6 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // the scalar offset and the LDS destination in M0, so a load costs no
   // vector instruction.
   const int lrow = lane / CPR;
-  const char* a_base = GATHER ? (const char*)p.X : (const char*)p.A;
-  const char* b_base = (const char*)(p.W + (int64_t)e * p.w_estride);
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, BUF_DWORD3);
   const uint32_t a_row_bytes = (uint32_t)p.lda * 2u, b_row_bytes = (uint32_t)p.ldb * 2u;
@@ -236,7 +282,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   for (int i = 0; i < LPW_B; ++i) {
     const int trow = (wave * LPW_B + i) * RPB + lrow;  // tile row
     int wrow;
-    if (MODE == MODE_DOWN) {
+    if (MODE == MODE_DOWN || MODE == MODE_WGRAD) {
       wrow = min(nb * BN + trow, p.N - 1);
     } else {
       // B rows of wave column q: WTN/2 gate rows, then the matching up rows
@@ -246,8 +292,8 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     }
     b_voff[i] = (uint32_t)wrow * b_row_bytes + (uint32_t)b_chunk(i) * 16u;
   }
-  const int KTF = p.K / BK;              // full k stages
-  const int KT_ALL = (p.K + BK - 1) / BK;  // all k stages (the last may be ragged)
+  const int KTF = K / BK;              // full k stages
+  const int KT_ALL = (K + BK - 1) / BK;  // all k stages (the last may be ragged)
   // this workgroup's k stages [KB, KT): all of them, or one part of a split tile
   const int KB = split ? part * KT_ALL / S : 0;
   const int KT = split ? (part + 1) * KT_ALL / S : KT_ALL;
@@ -266,7 +312,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < LPW_A; ++i) {
         const int c = a_chunk(i);
-        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, p.K - 8) * 2u;
+        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, K - 8) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)((char*)dst + i * 1024), 16,
                                                  a_voff[i] - (uint32_t)c * 16u + kb, 0, 0, 0);
       }
@@ -282,7 +328,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
       for (int i = 0; i < LPW_B; ++i) {
         const int c = b_chunk(i);
-        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, p.K - 8) * 2u;
+        const uint32_t kb = (uint32_t)min(kt * BK + c * 8, K - 8) * 2u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16,
                                                  b_voff[i] - (uint32_t)c * 16u + kb, 0, 0, 0);
       }
@@ -299,12 +345,12 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // chunks it fetched past K with zeros (B there holds finite weights); the
   // barrier that publishes the stage orders these writes
   auto zero_tail = [&](int kt) {
-    if (kt * BK + BK > p.K) {
+    if (kt * BK + BK > K) {
       uint16_t* as = As + (kt % NSTAGE_A) * A_ELEMS + wave_s * LPW_A * 512;
       const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < LPW_A; ++i)
-        if (kt * BK + a_chunk(i) * 8 >= p.K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
+        if (kt * BK + a_chunk(i) * 8 >= K) *(u32x4_t*)(as + i * 512 + lane * 8) = z;
     }
   };
 
@@ -389,7 +435,8 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     }
   };
 
-  const int NK = KT - KB;  // stages of this workgroup (>= 1)
+  const int NK = KT - KB;  // stages of this workgroup (0 only for an empty weight-gradient segment)
+  if (NK > 0) {
   issue_a(KB);
   issue_b(KB);
   if (NK > 1) issue_b(KB + 1);
@@ -410,6 +457,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   } else {
     for (; kt < k_steady; ++kt) iteration(kt, std::true_type{}, std::false_type{});
     for (; kt < KT; ++kt) iteration(kt, std::false_type{}, std::false_type{});
+  }
   }
 
   // ---- epilogue.  The weight fragment is the MFMA's first operand, so the
@@ -466,7 +514,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 
   const float sc = p.escale ? p.escale[e] : 1.0f;
   const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
-  if (MODE == MODE_GATE_UP) {
+  if (GU) {
     // blocks ni < NI/2 hold gate columns, ni + NI/2 the up columns of the same outputs
     uint16_t* out = (uint16_t*)p.out;
 #pragma unroll
@@ -497,20 +545,50 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
         for (int mi = 0; mi < MI; ++mi) {
           const int row = row_beg + wm * WTM + mi * 32 + fr;
           if (row >= row_end) continue;
-          float a[4];
+          float a[4], dg[4], du[4], da[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (MODE == MODE_GATE_UP_BWD) {
+            const uint2 d2 = *(const uint2*)(p.din + (int64_t)row * p.ld_din + oc);
+            da[0] = bf16_to_f32(d2.x & 0xffffu); da[1] = bf16_to_f32(d2.x >> 16);
+            da[2] = bf16_to_f32(d2.y & 0xffffu); da[3] = bf16_to_f32(d2.y >> 16);
+          }
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const float g = acc[mi][ni][4 * q + c] * sc + bg[c];
             const float u = acc[mi][ni + NI / 2][4 * q + c] * sc + bu[c];
-            a[c] = gated_act<ACT>(g, u, p.alpha, p.limit);
+            if (MODE == MODE_GATE_UP_BWD) {
+              gated_act_grad<ACT>(g, u, p.alpha, p.limit, a[c], dg[c], du[c]);
+              dg[c] *= da[c];
+              du[c] *= da[c];
+            } else {
+              a[c] = gated_act<ACT>(g, u, p.alpha, p.limit);
+            }
           }
           uint2 v;
           v.x = pack_bf16x2_rne(a[0], a[1]);
           v.y = pack_bf16x2_rne(a[2], a[3]);
           *(uint2*)(out + (int64_t)row * p.ldo + oc) = v;
+          if (MODE == MODE_GATE_UP_BWD) {
+            // dH in W_gu's column order: [gate | up], or gate/up interleaved
+            uint16_t* dh = (uint16_t*)p.out2 + (int64_t)row * p.ldo2;
+            if (FMT == FMT_CONCAT) {
+              uint2 g2, u2;
+              g2.x = pack_bf16x2_rne(dg[0], dg[1]);
+              g2.y = pack_bf16x2_rne(dg[2], dg[3]);
+              u2.x = pack_bf16x2_rne(du[0], du[1]);
+              u2.y = pack_bf16x2_rne(du[2], du[3]);
+              *(uint2*)(dh + oc) = g2;
+              *(uint2*)(dh + p.N + oc) = u2;
+            } else {
+              const u32x4_t w4 = {pack_bf16x2_rne(dg[0], du[0]), pack_bf16x2_rne(dg[1], du[1]),
+                                  pack_bf16x2_rne(dg[2], du[2]), pack_bf16x2_rne(dg[3], du[3])};
+              *(u32x4_t*)(dh + 2 * oc) = w4;
+            }
+          }
         }
       }
   } else {
+    // a weight gradient goes to its expert's block of the output
+    void* out_e = (MODE == MODE_WGRAD) ? (void*)((float*)p.out + (int64_t)e * p.out_estride) : p.out;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -534,10 +612,10 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
             uint2 w;
             w.x = pack_bf16x2_rne(v[0], v[1]);
             w.y = pack_bf16x2_rne(v[2], v[3]);
-            *(uint2*)((uint16_t*)p.out + (int64_t)row * p.ldo + n) = w;
+            *(uint2*)((uint16_t*)out_e + (int64_t)row * p.ldo + n) = w;
           } else {
             const f32x4_t w = {v[0], v[1], v[2], v[3]};
-            *(f32x4_t*)((float*)p.out + (int64_t)row * p.ldo + n) = w;
+            *(f32x4_t*)((float*)out_e + (int64_t)row * p.ldo + n) = w;
           }
         }
       }
@@ -649,6 +727,78 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
     err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, false>, d, q.max_rows, BN, st);
   if (err == hipSuccess && q.events) err = hipEventRecord(q.events[2], st);
   return err;
+}
+
+// ---------------------------------------------------------------- backward GEMMs
+
+static GemmArgs bwd_args(const BwdGemm& b) {
+  GemmArgs g{};
+  g.offsets = b.offsets;
+  g.L = b.L;
+  g.K = b.K;
+  g.N = b.N;
+  g.A = b.A;
+  g.X = b.X;
+  g.sorted_token = b.sorted_token;
+  g.W = b.W;
+  g.w_estride = b.w_estride;
+  g.lda = b.lda;
+  g.ldb = b.ldb;
+  g.bias = b.bias;
+  g.bias_estride = 2 * (int64_t)b.N;
+  g.escale = b.escale;
+  g.alpha = b.alpha;
+  g.limit = b.limit;
+  g.out = b.out;
+  g.ldo = b.ldo;
+  g.din = b.din;
+  g.ld_din = b.ld_din;
+  g.out2 = b.out2;
+  g.ldo2 = b.ldo2;
+  g.seg = b.seg;
+  g.M = b.M;
+  g.out_estride = b.out_estride;
+  return g;
+}
+
+hipError_t launch_bwd_rows_gemm(const BwdGemm& b, hipStream_t st) {
+  const GemmArgs g = bwd_args(b);
+  if (b.out_bf16)
+    return launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, true>, g, b.max_rows, BN, st);
+  return launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, false>, g, b.max_rows, BN, st);
+}
+
+template <int ACT, int FMT>
+static hipError_t gate_up_bwd_dispatch(const GemmArgs& g, bool gather, int max_rows, hipStream_t st) {
+  if (gather)
+    return launch_gemm(grouped_gemm_bf16_kernel<MODE_GATE_UP_BWD, ACT, FMT, true, true>, g, max_rows, BN / 2, st);
+  return launch_gemm(grouped_gemm_bf16_kernel<MODE_GATE_UP_BWD, ACT, FMT, false, true>, g, max_rows, BN / 2, st);
+}
+
+hipError_t launch_bwd_gate_up_gemm(const BwdGemm& b, hipStream_t st) {
+  const GemmArgs g = bwd_args(b);
+  const bool gather = b.A == nullptr;
+  if (b.fmt == FMT_CONCAT) {
+    if (b.act_kind == ACT_SILU) return gate_up_bwd_dispatch<ACT_SILU, FMT_CONCAT>(g, gather, b.max_rows, st);
+    if (b.act_kind == ACT_SWIGLUOAI) return gate_up_bwd_dispatch<ACT_SWIGLUOAI, FMT_CONCAT>(g, gather, b.max_rows, st);
+    return gate_up_bwd_dispatch<ACT_GELU_TANH, FMT_CONCAT>(g, gather, b.max_rows, st);
+  }
+  if (b.act_kind == ACT_SILU) return gate_up_bwd_dispatch<ACT_SILU, FMT_INTERLEAVED>(g, gather, b.max_rows, st);
+  if (b.act_kind == ACT_SWIGLUOAI) return gate_up_bwd_dispatch<ACT_SWIGLUOAI, FMT_INTERLEAVED>(g, gather, b.max_rows, st);
+  return gate_up_bwd_dispatch<ACT_GELU_TANH, FMT_INTERLEAVED>(g, gather, b.max_rows, st);
+}
+
+hipError_t launch_wgrad_gemm(const BwdGemm& b, hipStream_t st) {
+  const GemmArgs g = bwd_args(b);
+  auto kern = grouped_gemm_bf16_kernel<MODE_WGRAD, ACT_SILU, FMT_CONCAT, false, false>;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES_TILES);
+  if (err != hipSuccess) return err;
+  const int64_t tiles = (int64_t)b.L * ((b.M + BM - 1) / BM) * ((b.N + BN - 1) / BN);
+  const int64_t grid = (tiles + 7) / 8 * 8;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  kern<<<(unsigned)grid, NTHREADS, LDS_BYTES_TILES, st>>>(g);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -59,6 +59,85 @@ inline int split_slots_for(int64_t max_rows) {
 }
 hipError_t launch_ffn_bf16(const FfnBf16Params& p, hipStream_t st);
 
+// One GEMM of the backward pass on the bf16 grouped-GEMM kernel:
+//   rows   O[p] = escale[e] * A[p] . W[e]^T over the CSR rows (bf16 or fp32 out)
+//   gate_up recompute: A[p] = act(h), dH[p] = dA[p] * d act (h = escale * x . W^T + bias)
+//   wgrad  C[e] = escale[e] * A_e . B_e^T, K = the expert's padded segment
+struct BwdGemm {
+  const int32_t* offsets;
+  int L, K, N, max_rows;
+  const uint16_t* A;             // [rows, K] (nullptr for the gate_up recompute: gather X)
+  const uint16_t* X;
+  const int32_t* sorted_token;
+  const uint16_t* W;             // [L][N, K] (wgrad: the B operand [N, Kpad], shared)
+  int64_t w_estride, lda, ldb;
+  const uint16_t* bias;          // gate_up recompute only: [L, 2N] or nullptr
+  const float* escale;
+  int act_kind, fmt;
+  float alpha, limit;
+  void* out;
+  int64_t ldo;
+  int out_bf16;
+  const uint16_t* din;           // gate_up recompute: dA [rows, N]
+  int64_t ld_din;
+  void* out2;                    // gate_up recompute: dH [rows, 2N]
+  int64_t ldo2;
+  const int32_t* seg;            // wgrad: [L+1] padded segments
+  int M;                         // wgrad: rows of the A operand
+  int64_t out_estride;           // wgrad: elements between experts' outputs
+};
+// The backward of the routed-expert FFN (bf16 operands).
+struct FfnBwdParams {
+  const int32_t* offsets;
+  int L, H, D, max_rows;
+  const uint16_t* x;                  // bf16 [T, H] gathered through sorted_token, or
+  const int32_t* sorted_token;
+  const uint16_t* x_perm;             // bf16 [max_rows, H]
+  const uint16_t* w_gate_up;          // OUT_IN [L, 2D, H]
+  const uint16_t* w_gate_up_stacked;  // [L, H, 2D]
+  const uint16_t* w_down_stacked;     // [L, D, H]
+  const uint16_t* b_gate_up;
+  int fmt, act_kind;
+  float alpha, limit;
+  const float* gate_up_scales;
+  const float* down_scales;
+  const uint16_t* d_out;              // dO bf16 [max_rows, H]
+  float* d_x_perm;                    // [max_rows, H]
+  float* d_w_gate_up;                 // [L, 2D, H]
+  float* d_w_down;                    // [L, H, D]
+  float* d_b_gate_up;                 // [L, 2D] or nullptr
+  float* d_b_down;                    // [L, H] or nullptr
+  void* ws;
+  hipEvent_t const* events;           // optional, 8
+};
+// workspace byte offsets: segments, dA, A, dH, then the transposed operands
+// dO^T [H, rp], A^T [D, rp], dH^T [2D, rp], x^T [H, rp]
+struct FfnBwdLayout {
+  int64_t rp;  // padded row width of the transposed operands
+  int64_t seg_off, dA_off, A_off, dH_off, dOt_off, At_off, dHt_off, xt_off, bytes;
+};
+FfnBwdLayout ffn_bwd_layout(int64_t max_rows, int H, int D, int L);
+hipError_t launch_ffn_backward(const FfnBwdParams& p, hipStream_t st);
+
+struct CombineBwdParams {
+  int T, k, H;
+  const uint16_t* dy;
+  const void* O;
+  int o_bf16;
+  const int32_t* row_of_slot;
+  const float* w;
+  const uint8_t* mask;
+  uint16_t* dO;
+  float* dw;
+};
+hipError_t launch_combine_backward(const CombineBwdParams& p, hipStream_t st);
+hipError_t launch_transpose_bf16(const uint16_t* src, uint16_t* dst, int batch, int64_t rows, int64_t cols,
+                                 hipStream_t st);
+
+hipError_t launch_bwd_rows_gemm(const BwdGemm& b, hipStream_t st);
+hipError_t launch_bwd_gate_up_gemm(const BwdGemm& b, hipStream_t st);
+hipError_t launch_wgrad_gemm(const BwdGemm& b, hipStream_t st);
+
 struct FfnFp8Params {
   const int32_t* offsets;
   int L, H, D, max_rows;

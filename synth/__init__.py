@@ -6,6 +6,6 @@ layer's arithmetic: the oracle and the GPU path both receive the tensors it
 makes, and neither imports the other.
 """
 from .configs import CONFIGS, MoEConfig, get_config, scaled
-from .gen import make_inputs, to_host
+from .gen import make_grad_output, make_inputs, to_host
 
-__all__ = ["CONFIGS", "MoEConfig", "get_config", "scaled", "make_inputs", "to_host"]
+__all__ = ["CONFIGS", "MoEConfig", "get_config", "scaled", "make_inputs", "make_grad_output", "to_host"]

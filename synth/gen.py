@@ -171,3 +171,10 @@ def fp8_codes_to_float_torch(codes: torch.Tensor) -> torch.Tensor:
 
 
 __all__ = ["make_inputs", "to_host", "fp8_codes_to_float_torch"]
+
+
+def make_grad_output(cfg: MoEConfig, device="cpu", salt: int = 0) -> torch.Tensor:
+    """The upstream gradient dy = dL/dy of a backward pass: bf16 [T, H], N(0, 1)
+    (tensor id 21)."""
+    d = torch.device(device)
+    return _normal((cfg.T, cfg.H), 1.0, d, cfg.cfg_id, 21, 0, salt).to(torch.bfloat16)

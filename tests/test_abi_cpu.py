@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
 
 
 def test_struct_layouts_match_header_sizes():
@@ -35,7 +35,8 @@ def test_struct_layouts_match_header_sizes():
 
 
 STRUCTS = {"RouteArgs": "moe_route_args_t", "IndexArgs": "moe_index_args_t",
-           "FfnArgs": "moe_ffn_args_t", "CombineArgs": "moe_combine_args_t"}
+           "FfnArgs": "moe_ffn_args_t", "CombineArgs": "moe_combine_args_t",
+           "CombineBwdArgs": "moe_combine_backward_args_t", "FfnBwdArgs": "moe_ffn_backward_args_t"}
 
 
 def test_struct_layouts_match_the_c_compiler(tmp_path):
@@ -267,3 +268,77 @@ def test_workspace_queries_and_status_strings():
     assert lib.moe_ffn_workspace_bytes(100, 256, 4) == 25600 + 1024
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(3) == b"MOE_ERR_WORKSPACE_TOO_SMALL"
+
+
+# ---------------------------------------------------------------- backward entry points
+
+def _bwd(**kw):
+    base = dict(max_rows=64, hidden_dim=256, moe_dim=512, n_local_experts=8, expert_offsets=16, x_perm=32,
+                w_gate_up=48, w_gate_up_stacked=64, w_down_stacked=80, gate_up_format=0, activation=0, alpha=0.0,
+                limit=0.0, d_expert_out=96, d_x_perm=112, d_w_gate_up=128, d_w_down=144, workspace=160,
+                workspace_bytes=1 << 30)
+    base.update(kw)
+    return m.FfnBwdArgs(**base)
+
+
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(hidden_dim=96), m.MOE_ERR_INVALID_ARGUMENT, "64"),
+    (dict(moe_dim=200), m.MOE_ERR_INVALID_ARGUMENT, "64"),
+    (dict(n_local_experts=0), m.MOE_ERR_INVALID_ARGUMENT, "n_local_experts"),
+    (dict(activation=7), m.MOE_ERR_INVALID_ARGUMENT, "activation"),
+    (dict(alpha=1.0), m.MOE_ERR_INVALID_ARGUMENT, "alpha"),
+    (dict(activation=2, limit=7.0), m.MOE_ERR_INVALID_ARGUMENT, "gelu_tanh"),
+    (dict(gate_up_format=5), m.MOE_ERR_INVALID_ARGUMENT, "gate_up_format"),
+    (dict(w_down_stacked=None), m.MOE_ERR_INVALID_ARGUMENT, "w_down_stacked"),
+    (dict(d_w_down=None), m.MOE_ERR_INVALID_ARGUMENT, "d_w_down"),
+    (dict(d_expert_out=None), m.MOE_ERR_INVALID_ARGUMENT, "d_expert_out"),
+    (dict(x_perm=None), m.MOE_ERR_INVALID_ARGUMENT, "gather"),
+    (dict(x=8, sorted_token=8), m.MOE_ERR_INVALID_ARGUMENT, "not both"),
+    (dict(d_x_perm=120), m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(workspace_bytes=4096), m.MOE_ERR_WORKSPACE_TOO_SMALL, "workspace"),
+])
+def test_grouped_ffn_backward_validation(kw, status, frag):
+    st, msg = _err(m.lib().moe_grouped_ffn_backward, _bwd(**kw))
+    assert st == status and frag in msg, msg
+
+
+def test_backward_workspace_bytes():
+    lib = m.lib()
+
+    def up(b):
+        return -(-b // 256) * 256
+
+    for R, H, D, L in ((64, 256, 512, 8), (8192, 4096, 14336, 8), (7, 64, 64, 3), (0, 64, 64, 1)):
+        rp = -(-(R + 63 * min(L, R)) // 64) * 64  # every expert's rows padded to a multiple of 64
+        want = (up(4 * (L + 1)) + 2 * up(R * D * 2) + up(R * 2 * D * 2) + up(H * rp * 2) + up(D * rp * 2)
+                + up(2 * D * rp * 2) + up(H * rp * 2))
+        assert lib.moe_ffn_backward_workspace_bytes(R, H, D, L) == want, (R, H, D, L)
+    assert lib.moe_ffn_backward_workspace_bytes(-1, 64, 64, 1) == 0
+
+
+@pytest.mark.parametrize("kw,frag", [
+    (dict(hidden_dim=12), "hidden_dim"),
+    (dict(out_dtype=1), "out_dtype"),
+    (dict(d_expert_out=None), "required"),
+    (dict(expert_out=None), "expert_out is required"),
+    (dict(dy=24), "aligned"),
+])
+def test_combine_backward_validation(kw, frag):
+    base = dict(num_tokens=4, n_experts_per_tok=2, hidden_dim=64, dy=16, expert_out=32, out_dtype=2,
+                row_of_slot=48, d_expert_out=64, d_expert_weights=80)
+    base.update(kw)
+    st, msg = _err(m.lib().moe_combine_backward, m.CombineBwdArgs(**base))
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((16, 32, 1, 65, 64), "multiples of 64"),
+    ((16, 16, 1, 64, 64), "same buffer"),
+    ((0, 32, 1, 64, 64), "required"),
+    ((16, 40, 1, 64, 64), "aligned"),
+])
+def test_transpose_validation(args, frag):
+    src, dst, b, r, c = args
+    st = m.lib().moe_transpose_bf16(src or None, dst, b, r, c, None)
+    msg = m.lib().moe_last_error_message().decode()
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
