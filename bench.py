@@ -53,6 +53,9 @@ class HipEvents:
         arr = (ctypes.c_void_p * 3)(self.ev[i], self.ev[i + 1], self.ev[i + 2])
         return arr
 
+    def span(self, i: int, n: int):
+        return (ctypes.c_void_p * n)(*[self.ev[i + j] for j in range(n)])
+
     def elapsed_ms(self, a: int, b: int) -> float:
         ms = ctypes.c_float()
         assert self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self.ev[a]),
@@ -233,6 +236,70 @@ def cpu_baseline(cfg, inp, n_tokens: int):
                        f"{cfg.T} tokens") + f"; {dt:.1f} s on the host, float64 numpy"}
 
 
+def bench_backward(args, cfg, inp, moe, torch):
+    """Time the backward of the routed experts: combine backward, the grouped
+    FFN backward (its 8 phase events) and the gather of dx, on resident inputs
+    and the routing of one forward pass."""
+    import synth
+    dev = torch.device("cuda:0")
+    layer = moe.MoELayer(cfg, inp)
+    layer.forward(inp["x"])
+    dy = synth.make_grad_output(cfg, dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    K, W = args.steps, args.warmup
+    NE = 10  # 0 start, 1..8 the FFN backward's events, 9 end
+    ev = HipEvents(NE * (K + W))
+
+    def step(i):
+        b = NE * i
+        ev.record(b, stream)
+        layer.backward(dy, timing_events=ev.span(b + 1, 8))
+        ev.record(b + 9, stream)
+
+    print(f"[bench] backward: warmup {W}", file=sys.stderr, flush=True)
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    print(f"[bench] backward: timing {K} steps", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1000.0 / K
+
+    def mean_ms(a, b):
+        return sum(ev.elapsed_ms(NE * i + a, NE * i + b) for i in range(W, W + K)) / K
+
+    names = ["combine_backward", "dA", "gate_up_recompute", "dX", "transposes", "dW_down", "dW_gate_up",
+             "bias_grads", "dx_gather"]
+    t = {n: mean_ms(j, j + 1) for j, n in enumerate(names)}
+    ev.close()
+    R = cfg.T * cfg.k
+    rhd = 2.0 * R * cfg.H * cfg.D
+    flops = {"dA": rhd, "gate_up_recompute": 2 * rhd, "dX": 2 * rhd, "dW_down": rhd, "dW_gate_up": 2 * rhd}
+    peak = PEAK_BF16_TFLOPS
+    dom = max(flops, key=lambda n: t[n])
+    tf = {n: flops[n] / (t[n] * 1e-3) / 1e12 for n in flops}
+    total_tf = sum(flops.values()) / (sum(t[n] for n in flops) * 1e-3) / 1e12
+    line = {
+        "metric": "MoE layer backward tokens/s + achieved TFLOPS (% MFMA peak)",
+        "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name} MoE FFN backward (routed experts): T={cfg.T} hidden={cfg.H} "
+                               f"experts={cfg.E} top-{cfg.k} moe_dim={cfg.D} {cfg.gate_up_format} {cfg.activation}",
+                   "tokens": cfg.T, "hidden_dim": cfg.H, "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(tf[dom], 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tf[dom] / peak, 4), "traffic": None, "kernel": dom,
+                     "flops_per_launch": flops[dom], "avg_launch_ms": round(t[dom], 4)},
+        "gemm_tflops": {n: round(v, 1) for n, v in tf.items()},
+        "gemms_mfma_frac": round(total_tf / peak, 4),
+        "breakdown_ms": {n: round(v, 4) for n, v in t.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,6 +309,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens the oracle baseline runs (capped at the workload's T)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass of the routed experts (bf16 workloads) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -276,6 +345,13 @@ def main():
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload cfg {cfg.cfg_id} ({cfg.name})", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, dev)
+    if args.backward:
+        if cfg.operand_dtype != "bf16" or getattr(cfg, "n_shared", 0):
+            print("bench.py --backward: the backward is built for bf16 layers without shared experts",
+                  file=sys.stderr)
+            sys.exit(2)
+        bench_backward(args, cfg, inp, moe, torch)
+        return
     layer = moe.MoELayer(cfg, inp)
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup

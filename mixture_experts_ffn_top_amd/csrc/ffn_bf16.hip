@@ -151,9 +151,23 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     const int t = (blockIdx.x & 7) * per_xcd + slot;
     if (t >= total) return;
     e = __builtin_amdgcn_readfirstlane(t / per_e);
-    const int local = t % per_e;
-    nb = __builtin_amdgcn_readfirstlane(local / nmb_w);
-    mb = __builtin_amdgcn_readfirstlane(local % nmb_w);
+    // within an expert: bands of 8 row blocks, each walked column block by
+    // column block, so that the 32 tiles one XCD runs together are 8 row
+    // blocks x 4 column blocks and share both operands in its L2
+    const int local = t % per_e, NBW = (p.N + BN - 1) / BN;
+    const int full_rows = nmb_w / 8 * 8;
+    int nb_, mb_;
+    if (local < full_rows * NBW) {
+      const int band = local / (8 * NBW), r = local % (8 * NBW);
+      nb_ = r / 8;
+      mb_ = band * 8 + r % 8;
+    } else {
+      const int r = local - full_rows * NBW, h = nmb_w - full_rows;
+      nb_ = r / h;
+      mb_ = full_rows + r % h;
+    }
+    nb = __builtin_amdgcn_readfirstlane(nb_);
+    mb = __builtin_amdgcn_readfirstlane(mb_);
     row_beg = mb * BM;
     row_end = p.M;
     // the segment, clipped to the padded width of the operands (it only
@@ -586,9 +600,50 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
           }
         }
       }
+  } else if (!OUT_BF16) {
+    // fp32 output through LDS, one 128-row half of the tile at a time: the
+    // wave row that owns the half writes its accumulators into LDS, then
+    // every wave stores whole 1 KB output rows (one contiguous 16 bytes per
+    // lane), instead of 32-byte pieces of 32 rows per store instruction.
+    // A weight gradient goes to its expert's block of the output.
+    float* out_e = (float*)p.out + (MODE == MODE_WGRAD ? (int64_t)e * p.out_estride : 0);
+    float* stage = (float*)smem;  // [WTM][SROW]; the padding spreads the rows over the banks
+    constexpr int SROW = BN + 4;
+    static_assert(WTM * SROW * 4 <= LDS_BYTES_TILES, "staged epilogue exceeds LDS");
+#pragma unroll
+    for (int half = 0; half < WAVES_M; ++half) {
+      __syncthreads();  // the tiles (or the previous half) are no longer read
+      if (wm == half) {
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int nl = wn * WTN + ni * 32 + 8 * q + 4 * fk;  // tile column of 4
+            const int n = nb * BN + nl;
+            float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (bias_e && n < p.N) {
+              const uint2 b2 = *(const uint2*)(bias_e + n);
+              bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+              bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+              const f32x4_t v = {acc[mi][ni][4 * q] * sc + bd[0], acc[mi][ni][4 * q + 1] * sc + bd[1],
+                                 acc[mi][ni][4 * q + 2] * sc + bd[2], acc[mi][ni][4 * q + 3] * sc + bd[3]};
+              *(f32x4_t*)(stage + (mi * 32 + fr) * SROW + nl) = v;
+            }
+          }
+      }
+      __syncthreads();
+      const int n = nb * BN + lane * 4;
+      for (int rr = wave; rr < WTM; rr += WAVES_M * WAVES_N) {
+        const int row = row_beg + half * WTM + rr;
+        if (row < row_end && n < p.N)
+          *(f32x4_t*)(out_e + (int64_t)row * p.ldo + n) = *(const f32x4_t*)(stage + rr * SROW + lane * 4);
+      }
+    }
   } else {
-    // a weight gradient goes to its expert's block of the output
-    void* out_e = (MODE == MODE_WGRAD) ? (void*)((float*)p.out + (int64_t)e * p.out_estride) : p.out;
+    void* out_e = p.out;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
@@ -608,15 +663,10 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
           float v[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
-          if (OUT_BF16) {
-            uint2 w;
-            w.x = pack_bf16x2_rne(v[0], v[1]);
-            w.y = pack_bf16x2_rne(v[2], v[3]);
-            *(uint2*)((uint16_t*)out_e + (int64_t)row * p.ldo + n) = w;
-          } else {
-            const f32x4_t w = {v[0], v[1], v[2], v[3]};
-            *(f32x4_t*)((float*)out_e + (int64_t)row * p.ldo + n) = w;
-          }
+          uint2 w;
+          w.x = pack_bf16x2_rne(v[0], v[1]);
+          w.y = pack_bf16x2_rne(v[2], v[3]);
+          *(uint2*)((uint16_t*)out_e + (int64_t)row * p.ldo + n) = w;
         }
       }
   }
