@@ -528,79 +528,130 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 
   const float sc = p.escale ? p.escale[e] : 1.0f;
   const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
-  if (GU) {
-    // blocks ni < NI/2 hold gate columns, ni + NI/2 the up columns of the same outputs
-    uint16_t* out = (uint16_t*)p.out;
+  if constexpr (GU) {
+    // Blocks ni < NI/2 hold gate columns, ni + NI/2 the up columns of the
+    // same outputs.  The bf16 results go through LDS so that they leave as
+    // whole tile rows: first A (256 rows x 128 outputs), then, for the
+    // backward recompute, dH (256 rows x 256 columns in W_gu's order), its
+    // gradients recomputed from the accumulators still in registers.
+    uint16_t* stg = (uint16_t*)smem;
+    constexpr int AROW = NBO + 8, HROW = 2 * NBO + 8;  // staged row pitches (bf16), padded
+    static_assert(BM * HROW * 2 <= LDS_BYTES_TILES, "staged epilogue exceeds LDS");
+    auto bias_of = [&](int oc, float (&bg)[4], float (&bu)[4]) {
+      for (int c = 0; c < 4; ++c) bg[c] = bu[c] = 0.0f;
+      if (!bias_e) return;
+      if (FMT == FMT_CONCAT) {
+        const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
+        bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
+        bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
+        bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
+        bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
+      } else {
+        // interleaved: gate of output j at 2j, up at 2j+1
+        const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
+        for (int c = 0; c < 4; ++c) {
+          bg[c] = bf16_to_f32(b4[c] & 0xffffu);
+          bu[c] = bf16_to_f32(b4[c] >> 16);
+        }
+      }
+    };
+    // ---- A
+    __syncthreads();  // the operand tiles are no longer read
 #pragma unroll
     for (int ni = 0; ni < NI / 2; ++ni)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int oc = nb * NBO + wn * (WTN / 2) + ni * 32 + 8 * q + 4 * fk;  // first of 4 outputs
-        if (oc >= p.N) continue;  // N is a multiple of 8: all 4 are in range
-        float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias_e) {
-          if (FMT == FMT_CONCAT) {
-            const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
-            bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
-            bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
-            bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
-            bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
-          } else {
-            // interleaved: gate of output j at 2j, up at 2j+1
-            const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              bg[c] = bf16_to_f32(b4[c] & 0xffffu);
-              bu[c] = bf16_to_f32(b4[c] >> 16);
-            }
-          }
-        }
+        const int ocl = wn * (WTN / 2) + ni * 32 + 8 * q + 4 * fk;  // tile output of 4
+        const int oc = nb * NBO + ocl;
+        float bg[4], bu[4];
+        if (oc < p.N) bias_of(oc, bg, bu);  // N is a multiple of 8: all 4 are in range
+        else for (int c = 0; c < 4; ++c) bg[c] = bu[c] = 0.0f;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          const int row = row_beg + wm * WTM + mi * 32 + fr;
-          if (row >= row_end) continue;
-          float a[4], dg[4], du[4], da[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (MODE == MODE_GATE_UP_BWD) {
-            const uint2 d2 = *(const uint2*)(p.din + (int64_t)row * p.ld_din + oc);
-            da[0] = bf16_to_f32(d2.x & 0xffffu); da[1] = bf16_to_f32(d2.x >> 16);
-            da[2] = bf16_to_f32(d2.y & 0xffffu); da[3] = bf16_to_f32(d2.y >> 16);
-          }
+          float a[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float g = acc[mi][ni][4 * q + c] * sc + bg[c];
-            const float u = acc[mi][ni + NI / 2][4 * q + c] * sc + bu[c];
-            if (MODE == MODE_GATE_UP_BWD) {
-              gated_act_grad<ACT>(g, u, p.alpha, p.limit, a[c], dg[c], du[c]);
-              dg[c] *= da[c];
-              du[c] *= da[c];
-            } else {
-              a[c] = gated_act<ACT>(g, u, p.alpha, p.limit);
-            }
-          }
+          for (int c = 0; c < 4; ++c)
+            a[c] = gated_act<ACT>(acc[mi][ni][4 * q + c] * sc + bg[c], acc[mi][ni + NI / 2][4 * q + c] * sc + bu[c],
+                                  p.alpha, p.limit);
           uint2 v;
           v.x = pack_bf16x2_rne(a[0], a[1]);
           v.y = pack_bf16x2_rne(a[2], a[3]);
-          *(uint2*)(out + (int64_t)row * p.ldo + oc) = v;
-          if (MODE == MODE_GATE_UP_BWD) {
-            // dH in W_gu's column order: [gate | up], or gate/up interleaved
-            uint16_t* dh = (uint16_t*)p.out2 + (int64_t)row * p.ldo2;
+          *(uint2*)(stg + (wm * WTM + mi * 32 + fr) * AROW + ocl) = v;
+        }
+      }
+    __syncthreads();
+    {
+      uint16_t* out = (uint16_t*)p.out;
+      const int oc = nb * NBO + (lane & 15) * 8;  // 16 lanes per 256-byte row
+      for (int r = wave * 4 + (lane >> 4); r < BM; r += 4 * WAVES_M * WAVES_N) {
+        const int row = row_beg + r;
+        if (row < row_end && oc < p.N)
+          *(u32x4_t*)(out + (int64_t)row * p.ldo + oc) = *(const u32x4_t*)(stg + r * AROW + (lane & 15) * 8);
+      }
+    }
+    if (MODE == MODE_GATE_UP_BWD) {
+      // ---- dH = dA * d act, staged in W_gu's column order for this tile:
+      // concatenated [128 gate | 128 up], interleaved gate/up pairs
+      __syncthreads();
+#pragma unroll
+      for (int ni = 0; ni < NI / 2; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int ocl = wn * (WTN / 2) + ni * 32 + 8 * q + 4 * fk;
+          const int oc = nb * NBO + ocl;
+          float bg[4], bu[4];
+          if (oc < p.N) bias_of(oc, bg, bu);
+          else for (int c = 0; c < 4; ++c) bg[c] = bu[c] = 0.0f;
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) {
+            const int rl = wm * WTM + mi * 32 + fr;
+            const int row = row_beg + rl;
+            float da[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (row < row_end && oc < p.N) {
+              const uint2 d2 = *(const uint2*)(p.din + (int64_t)row * p.ld_din + oc);
+              da[0] = bf16_to_f32(d2.x & 0xffffu); da[1] = bf16_to_f32(d2.x >> 16);
+              da[2] = bf16_to_f32(d2.y & 0xffffu); da[3] = bf16_to_f32(d2.y >> 16);
+            }
+            float a, dg[4], du[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              gated_act_grad<ACT>(acc[mi][ni][4 * q + c] * sc + bg[c], acc[mi][ni + NI / 2][4 * q + c] * sc + bu[c],
+                                  p.alpha, p.limit, a, dg[c], du[c]);
+              dg[c] *= da[c];
+              du[c] *= da[c];
+            }
+            uint16_t* srow = stg + rl * HROW;
             if (FMT == FMT_CONCAT) {
               uint2 g2, u2;
               g2.x = pack_bf16x2_rne(dg[0], dg[1]);
               g2.y = pack_bf16x2_rne(dg[2], dg[3]);
               u2.x = pack_bf16x2_rne(du[0], du[1]);
               u2.y = pack_bf16x2_rne(du[2], du[3]);
-              *(uint2*)(dh + oc) = g2;
-              *(uint2*)(dh + p.N + oc) = u2;
+              *(uint2*)(srow + ocl) = g2;
+              *(uint2*)(srow + NBO + ocl) = u2;
             } else {
               const u32x4_t w4 = {pack_bf16x2_rne(dg[0], du[0]), pack_bf16x2_rne(dg[1], du[1]),
                                   pack_bf16x2_rne(dg[2], du[2]), pack_bf16x2_rne(dg[3], du[3])};
-              *(u32x4_t*)(dh + 2 * oc) = w4;
+              *(u32x4_t*)(srow + 2 * ocl) = w4;
             }
           }
         }
+      __syncthreads();
+      // 512-byte staged rows, 32 lanes each; staged column j holds
+      //   concatenated: gate (j < NBO) or up (j >= NBO) of output j mod NBO
+      //   interleaved:  column 2 * nb * NBO + j of dH
+      uint16_t* dh = (uint16_t*)p.out2;
+      const int j = (lane & 31) * 8;
+      const int oc = nb * NBO + (FMT == FMT_CONCAT ? j % NBO : j / 2);  // first output these 8 columns belong to
+      const int64_t col = (FMT == FMT_CONCAT) ? (j < NBO ? (int64_t)nb * NBO + j : (int64_t)p.N + nb * NBO + j - NBO)
+                                              : (int64_t)2 * nb * NBO + j;
+      for (int r = wave * 2 + (lane >> 5); r < BM; r += 2 * WAVES_M * WAVES_N) {
+        const int row = row_beg + r;
+        if (row < row_end && oc < p.N)
+          *(u32x4_t*)(dh + (int64_t)row * p.ldo2 + col) = *(const u32x4_t*)(stg + r * HROW + j);
       }
-  } else if (!OUT_BF16) {
+    }
+  } else if constexpr (!OUT_BF16) {
     // fp32 output through LDS, one 128-row half of the tile at a time: the
     // wave row that owns the half writes its accumulators into LDS, then
     // every wave stores whole 1 KB output rows (one contiguous 16 bytes per
