@@ -80,6 +80,33 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   return (uint32_t)w;
 }
 
+// x / s in float32, correctly rounded like __fdiv_rn, for one divisor shared
+// by many dividends: y = RN(1/s) once, then per dividend q0 = RN(x y),
+// r = x - s q0 by one fma (exact), q = RN(q0 + r y) by another.  With y the
+// correctly rounded reciprocal and no underflow on the way this correction is
+// correctly rounded (Markstein's theorem, binary floating point, round to
+// nearest); the fast form is used only for normal s >= 2^-92, which keeps r
+// normal wherever a quotient can reach an e4m3 code other than zero, and
+// x's sign is copied so that -0 stays -0.  Other divisors take __fdiv_rn.
+struct SharedDivisor {
+  float s, y;
+  bool fast;
+};
+__device__ __forceinline__ SharedDivisor shared_divisor(float s) {
+  SharedDivisor d;
+  d.s = s;
+  d.fast = s >= 0x1p-92f && s < __builtin_inff();
+  d.y = d.fast ? __fdiv_rn(1.0f, s) : 0.0f;
+  return d;
+}
+__device__ __forceinline__ float div_rn(const SharedDivisor& d, float x) {
+#pragma clang fp contract(off)
+  if (!d.fast) return __fdiv_rn(x, d.s);
+  const float q0 = x * d.y;
+  const float r = __builtin_fmaf(-q0, d.s, x);
+  return __builtin_copysignf(__builtin_fmaf(r, d.y, q0), x);
+}
+
 __device__ __forceinline__ float e4m3_to_f32(uint8_t c) {
   uint32_t s = (c & 0x80u) << 24;
   uint32_t ef = (c >> 3) & 0xfu;
@@ -120,6 +147,15 @@ __device__ __forceinline__ float wave_max(float v) {
   const uint32_t u = __float_as_uint(v);
   return fmaxf(fmaxf(__uint_as_float(row_lane(u, 0)), __uint_as_float(row_lane(u, 1))),
                fmaxf(__uint_as_float(row_lane(u, 2)), __uint_as_float(row_lane(u, 3))));
+}
+// Maximum over each row of 16 lanes (every lane of the row gets it).
+__device__ __forceinline__ float row16_max(float v) {
+  const uint32_t ninf = 0xff800000u;
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_XOR1>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_QP_XOR2>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_HALF_MIRROR>(__float_as_uint(v), ninf)));
+  v = fmaxf(v, __uint_as_float(dpp_u32<DPP_ROW_MIRROR>(__float_as_uint(v), ninf)));
+  return v;
 }
 __device__ __forceinline__ float wave_sum(float v) {
   v += __uint_as_float(dpp_u32<DPP_QP_XOR1>(__float_as_uint(v), 0u));

@@ -349,11 +349,12 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       const f32x4_t r4 = *(const f32x4_t*)(red + lrw * 4);
       const float m = fmaxf(fmaxf(r4[0], r4[1]), fmaxf(r4[2], r4[3]));
       const float s = (m > 0.0f) ? __fdiv_rn(m, 448.0f) : 1.0f;
+      const SharedDivisor ds = shared_divisor(s);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fk;
-        const uint32_t w = e4m3x4(__fdiv_rn(a[mi][4 * q + 0], s), __fdiv_rn(a[mi][4 * q + 1], s),
-                                  __fdiv_rn(a[mi][4 * q + 2], s), __fdiv_rn(a[mi][4 * q + 3], s));
+        const uint32_t w = e4m3x4(div_rn(ds, a[mi][4 * q + 0]), div_rn(ds, a[mi][4 * q + 1]),
+                                  div_rn(ds, a[mi][4 * q + 2]), div_rn(ds, a[mi][4 * q + 3]));
         *(uint32_t*)(out + (int64_t)row * p.N + oc) = w;
       }
       if (wn == 0 && fk == 0) p.out_scale[(int64_t)row * (p.N / 128) + nb] = s;

@@ -227,12 +227,12 @@ __global__ __launch_bounds__(256) void permute_fp8_kernel(const uint16_t* __rest
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, MOE_WAVE));
+        amax = row16_max(amax);  // a 128-column group is one row of 16 lanes
         const float s = (amax > 0.0f) ? __fdiv_rn(amax, 448.0f) : 1.0f;
+        const SharedDivisor ds = shared_divisor(s);
         uint2 q;
-        q.x = e4m3x4(__fdiv_rn(f[0], s), __fdiv_rn(f[1], s), __fdiv_rn(f[2], s), __fdiv_rn(f[3], s));
-        q.y = e4m3x4(__fdiv_rn(f[4], s), __fdiv_rn(f[5], s), __fdiv_rn(f[6], s), __fdiv_rn(f[7], s));
+        q.x = e4m3x4(div_rn(ds, f[0]), div_rn(ds, f[1]), div_rn(ds, f[2]), div_rn(ds, f[3]));
+        q.y = e4m3x4(div_rn(ds, f[4]), div_rn(ds, f[5]), div_rn(ds, f[6]), div_rn(ds, f[7]));
         if (g < groups) {
           *(uint2*)(dst + g * 128 + sub * 8) = q;
           if (sub == 0) xs[(int64_t)row * groups + g] = s;
