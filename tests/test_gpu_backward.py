@@ -130,6 +130,8 @@ def _compare_all(cfg, inp, res, dy, g, mask=None):
     {"T": 300, "E": 3, "k": 2, "H": 320, "D": 128},              # several 256-row blocks, ragged M and N tails
     {"T": 8, "E": 16, "k": 2, "H": 64, "D": 64},                 # most experts empty
     {"T": 1, "E": 4, "k": 1, "H": 64, "D": 128, "activation": "silu", "limit": 7.0},
+    {"T": 20, "E": 3, "k": 3, "H": 64, "D": 64},                  # k = E: every expert gets every token
+    {"T": 40, "E": 1, "k": 1, "H": 128, "D": 128, "has_bias": True},  # one expert
 ])
 def test_backward_small(moe, changes):
     cfg = synth.scaled(synth.get_config(1), **changes)

@@ -692,6 +692,19 @@ def test_fused_ffn_layer(moe, changes):
     assert err <= BF16_TOL
 
 
+def test_fused_ffn_permuted_rows(moe):
+    """The single-launch FFN on permuted rows (x_perm) instead of the gather."""
+    cfg = synth.scaled(synth.get_config(8), T=48, E=6, k=2, H=256, D=1024, has_bias=True)
+    inp = _gen(cfg)
+    say("[fused x_perm] T=48 E=6 k=2 H=256 D=1024 (down split in 2 parts)")
+    layer = moe.MoELayer(cfg, inp, gather=False)
+    assert layer.fused
+    res = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+    assert moe.fused_error_word(layer.act_ws) == 0
+
+
 def test_fused_ffn_then_smaller_batch(moe):
     """Two calls in a row, the second with fewer tokens and a different
     routing: the first call's arrival counters must not leak into the second."""
