@@ -67,6 +67,54 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
 
 
+def measure_ceilings(moe, torch) -> dict:
+    """Practical ceilings on this chip, measured with the library's probes
+    right after the timed steps (same clocks): an MFMA loop on every CU for
+    bf16 and fp8, and a 1 GiB streaming copy (bytes read + bytes written).
+    The best of five launches each."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = HipEvents(2)
+    wg = 1024
+    out = torch.empty(wg * 8, dtype=torch.float32, device=dev)
+
+    def best_rate(launch):
+        launch()
+        torch.cuda.synchronize()
+        best = 0.0
+        for _ in range(5):
+            ev.record(0, stream)
+            work = launch()
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            best = max(best, work / (ev.elapsed_ms(0, 1) * 1e-3))
+        return best
+
+    res = {}
+    for kind, name, iters in ((0, "bf16", 4000), (1, "fp8", 2000)):
+        res[f"mfma_{name}_tflops"] = round(best_rate(lambda: moe.probe_mfma(kind, wg, iters, out)) / 1e12, 1)
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+
+    def copy():
+        moe.probe_stream_copy(src, dst)
+        return 2 * n
+
+    res["stream_copy_gbs"] = round(best_rate(copy) / 1e9, 1)
+    ev.close()
+    del src, dst
+    return res
+
+
+def _with_measured(roof: dict, ceil: dict, dtype_key: str) -> dict:
+    """Adds the measured ceiling of the roofline's bound and the fraction of it."""
+    mp = ceil["stream_copy_gbs"] if roof["bound"] == "hbm" else ceil[dtype_key]
+    roof["measured_peak"] = mp
+    roof["frac_of_measured"] = round(roof["achieved"] / mp, 4)
+    return roof
+
+
 def _src_hash() -> str:
     """Hash of the sources that make the bf16 GEMM kernels."""
     h = hashlib.sha256()
@@ -274,6 +322,7 @@ def bench_backward(args, cfg, inp, moe, torch):
              "bias_grads", "dx_gather"]
     t = {n: mean_ms(j, j + 1) for j, n in enumerate(names)}
     ev.close()
+    ceil = measure_ceilings(moe, torch)
     R = cfg.T * cfg.k
     rhd = 2.0 * R * cfg.H * cfg.D
     flops = {"dA": rhd, "gate_up_recompute": 2 * rhd, "dX": 2 * rhd, "dW_down": rhd, "dW_gate_up": 2 * rhd}
@@ -290,11 +339,14 @@ def bench_backward(args, cfg, inp, moe, torch):
                                f"experts={cfg.E} top-{cfg.k} moe_dim={cfg.D} {cfg.gate_up_format} {cfg.activation}",
                    "tokens": cfg.T, "hidden_dim": cfg.H, "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D,
                    "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "achieved": round(tf[dom], 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tf[dom] / peak, 4), "traffic": None, "kernel": dom,
-                     "flops_per_launch": flops[dom], "avg_launch_ms": round(t[dom], 4)},
+        "roofline": _with_measured({"bound": "mfma", "achieved": round(tf[dom], 2), "peak": peak, "unit": "TFLOP/s",
+                                    "frac": round(tf[dom] / peak, 4), "traffic": None, "kernel": dom,
+                                    "flops_per_launch": flops[dom], "avg_launch_ms": round(t[dom], 4)},
+                                   ceil, "mfma_bf16_tflops"),
         "gemm_tflops": {n: round(v, 1) for n, v in tf.items()},
         "gemms_mfma_frac": round(total_tf / peak, 4),
+        "gemms_frac_of_measured": round(total_tf / ceil["mfma_bf16_tflops"], 4),
+        "measured_ceilings": ceil,
         "breakdown_ms": {n: round(v, 4) for n, v in t.items()},
     }
     print(json.dumps(line), flush=True)
@@ -389,6 +441,8 @@ def main():
     t_comb = (mean_ms(9, 6) if has_shared else mean_ms(5, 6))
     t_layer_dev = mean_ms(0, 6)
     ev.close()
+    print("[bench] measured ceilings (MFMA loop, streaming copy)", file=sys.stderr, flush=True)
+    ceil = measure_ceilings(moe, torch)
 
     R = cfg.T * cfg.k
     gu_flops = 4.0 * R * cfg.H * cfg.D
@@ -435,6 +489,9 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": "single-launch expert FFN (gate_up + activation + down, bf16)",
                 "bytes_per_launch": ffn_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_ffn, 4)}
+    mfma_key = "mfma_bf16_tflops" if peak == PEAK_BF16_TFLOPS else "mfma_fp8_tflops"
+    roof = _with_measured(roof, ceil, mfma_key)
+    hbm = {"route": route_bytes / (t_route * 1e-3) / 1e9, "combine": comb_bytes / (t_comb * 1e-3) / 1e9}
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
@@ -447,12 +504,15 @@ def main():
                    "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D, "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "ffn_tflops": round(ffn_tf, 2), "ffn_mfma_frac": round(ffn_tf / peak, 4),
+        "ffn_frac_of_measured": round(ffn_tf / ceil[mfma_key], 4),
         "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),
                          "gate_up": round(t_gu, 4), "down": round(t_dn, 4),
                          **({"shared_experts_ffn": round(t_shared, 4)} if has_shared else {}),
                          "combine": round(t_comb, 4), "layer_device": round(t_layer_dev, 4)},
-        "hbm_gbs": {"route": round(route_bytes / (t_route * 1e-3) / 1e9, 1),
-                    "combine": round(comb_bytes / (t_comb * 1e-3) / 1e9, 1)},
+        "hbm_gbs": {n: round(v, 1) for n, v in hbm.items()},
+        "hbm_frac": {n: round(v / PEAK_HBM_GBS, 4) for n, v in hbm.items()},
+        "hbm_frac_of_measured": {n: round(v / ceil["stream_copy_gbs"], 4) for n, v in hbm.items()},
+        "measured_ceilings": ceil,
         "weight_layout": "out_in (transposed stacked weights, laid out once at load)",
     }
     if not args.no_cpu_baseline:

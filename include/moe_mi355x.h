@@ -549,6 +549,26 @@ int64_t moe_ffn_backward_workspace_bytes(int32_t max_rows, int32_t hidden_dim, i
 moe_status_t moe_transpose_bf16(const void* src, void* dst, int32_t batch, int32_t rows, int32_t cols,
                                 void* stream);
 
+/* ------------------------------------------------------------------------
+ * Measured ceilings (diagnostics; not part of the layer).  The GEMMs and the
+ * bandwidth kernels are reported against the datasheet peaks and against
+ * what these two probes reach on the same chip under the same clocks.
+ *
+ * moe_probe_mfma -- runs workgroups x 8 waves, each issuing iters x 8
+ * independent matrix instructions on register operands: kind 0 is
+ * v_mfma_f32_32x32x16_bf16 (32768 flops each), kind 1 is
+ * v_mfma_scale_f32_32x32x64_f8f6f4 on e4m3 operands with unit scales
+ * (131072 flops each).  out (device, fp32, workgroups x 8 elements) receives
+ * one sum per wave so that the loop is kept; its values have no meaning.
+ * workgroups and iters are >= 1; kind is 0 or 1.
+ *
+ * moe_probe_stream_copy -- copies `bytes` bytes from src to dst (device,
+ * 16-byte aligned, not overlapping) with 16-byte loads and stores; bytes is a
+ * multiple of 16 (0 launches nothing).
+ * ---------------------------------------------------------------------- */
+moe_status_t moe_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, float* out, void* stream);
+moe_status_t moe_probe_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
 /* Helpers. */
 const char* moe_status_string(moe_status_t status);
 /* Message of the last failed call on this host thread ("" if none). */

@@ -92,8 +92,8 @@ class FfnBwdArgs(ctypes.Structure):
 ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_grouped_ffn_fused", "moe_combine",
                 "moe_shared_indices", "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
                 "moe_ffn_fused_workspace_bytes", "moe_combine_backward", "moe_grouped_ffn_backward",
-                "moe_ffn_backward_workspace_bytes", "moe_transpose_bf16",
-                "moe_status_string", "moe_last_error_message", "moe_abi_version")
+                "moe_ffn_backward_workspace_bytes", "moe_transpose_bf16", "moe_probe_mfma",
+                "moe_probe_stream_copy", "moe_status_string", "moe_last_error_message", "moe_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -117,6 +117,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_backward_workspace_bytes.restype = _i64
     lib.moe_transpose_bf16.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp]
     lib.moe_transpose_bf16.restype = _i32
+    lib.moe_probe_mfma.argtypes = [_i32, _i32, _i32, _vp, _vp]
+    lib.moe_probe_mfma.restype = _i32
+    lib.moe_probe_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
+    lib.moe_probe_stream_copy.restype = _i32
     lib.moe_status_string.argtypes = [_i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -386,6 +390,26 @@ def transpose_bf16(src, out=None):
     B, R, C = src.shape
     dst = out if out is not None else torch.empty((B, C, R), dtype=torch.bfloat16, device=src.device)
     _check(lib().moe_transpose_bf16(_ptr(src), _ptr(dst), B, R, C, _stream(src.device)))
+    return dst
+
+
+def probe_mfma(kind: int, workgroups: int, iters: int, out):
+    """moe_probe_mfma: the MFMA-loop ceiling probe (kind 0 bf16, 1 fp8).
+    out: fp32 device tensor of workgroups * 8 elements.  Returns the flops the
+    launch performs."""
+    _dt(out, torch.float32, "out")
+    if out.numel() < workgroups * 8:
+        raise ValueError("probe_mfma: out needs workgroups * 8 elements")
+    _check(lib().moe_probe_mfma(kind, workgroups, iters, _ptr(out), _stream(out.device)))
+    return workgroups * 8 * iters * 8 * (32768 if kind == 0 else 131072)
+
+
+def probe_stream_copy(src, dst):
+    """moe_probe_stream_copy: dst <- src (same byte size, a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("probe_stream_copy: src and dst must have the same size in bytes")
+    _check(lib().moe_probe_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
     return dst
 
 

@@ -7,6 +7,7 @@
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
+#include "probe.h"
 
 namespace {
 
@@ -588,6 +589,27 @@ moe_status_t moe_transpose_bf16(const void* src, void* dst, int32_t batch, int32
   return hip_status(moe::launch_transpose_bf16((const uint16_t*)src, (uint16_t*)dst, batch, rows, cols,
                                                (hipStream_t)stream),
                     "moe_transpose_bf16");
+}
+
+// ---------------------------------------------------------------- measured ceilings
+moe_status_t moe_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, float* out, void* stream) {
+  REQUIRE(kind == 0 || kind == 1, "moe_probe_mfma: kind must be 0 (bf16) or 1 (fp8) (got %d)", kind);
+  REQUIRE(workgroups >= 1 && workgroups <= (1 << 20), "moe_probe_mfma: workgroups must be in [1, 1048576] (got %d)",
+          workgroups);
+  REQUIRE(iters >= 1, "moe_probe_mfma: iters must be >= 1 (got %d)", iters);
+  REQUIRE(out != nullptr, "moe_probe_mfma: out is required");
+  return hip_status(moe::launch_mfma_probe(kind, workgroups, iters, out, (hipStream_t)stream), "moe_probe_mfma");
+}
+
+moe_status_t moe_probe_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  REQUIRE(bytes >= 0 && bytes % 16 == 0, "moe_probe_stream_copy: bytes must be a multiple of 16 >= 0");
+  if (bytes == 0) return ok();
+  REQUIRE(src && dst, "moe_probe_stream_copy: src and dst are required");
+  REQUIRE(aligned16(src) && aligned16(dst), "moe_probe_stream_copy: src and dst must be 16-byte aligned");
+  const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+  REQUIRE(s0 + (uintptr_t)bytes <= d0 || d0 + (uintptr_t)bytes <= s0,
+          "moe_probe_stream_copy: src and dst must not overlap");
+  return hip_status(moe::launch_stream_copy(src, dst, bytes / 16, (hipStream_t)stream), "moe_probe_stream_copy");
 }
 
 }  // extern "C"

@@ -1,0 +1,18 @@
+// Launchers of the measured-ceiling probes (MFMA loop, streaming copy).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+// waves a probe launch of `workgroups` work-groups runs
+int probe_waves(int workgroups);
+// fp8 = 0: v_mfma_f32_32x32x16_bf16; fp8 = 1: v_mfma_scale_f32_32x32x64_f8f6f4
+// (e4m3 operands, unit scales).  Each wave issues iters * 8 instructions and
+// writes one float to out[wave].
+hipError_t launch_mfma_probe(int fp8, int workgroups, int iters, float* out, hipStream_t st);
+// copies n16 16-byte units from src to dst
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t st);
+
+}  // namespace moe

@@ -342,3 +342,33 @@ def test_transpose_validation(args, frag):
     st = m.lib().moe_transpose_bf16(src or None, dst, b, r, c, None)
     msg = m.lib().moe_last_error_message().decode()
     assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((2, 1, 1, 16), "kind"),
+    ((0, 0, 1, 16), "workgroups"),
+    ((0, 1, 0, 16), "iters"),
+    ((1, 1, 1, 0), "out is required"),
+])
+def test_probe_mfma_validation(args, frag):
+    kind, wg, it, out = args
+    st = m.lib().moe_probe_mfma(kind, wg, it, out or None, None)
+    msg = m.lib().moe_last_error_message().decode()
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((16, 4096, 24), "multiple of 16"),
+    ((0, 4096, 64), "required"),
+    ((24, 4096, 64), "aligned"),
+    ((16, 48, 64), "overlap"),
+])
+def test_probe_stream_copy_validation(args, frag):
+    src, dst, n = args
+    st = m.lib().moe_probe_stream_copy(src or None, dst, n, None)
+    msg = m.lib().moe_last_error_message().decode()
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+def test_probe_stream_copy_zero_bytes_is_a_no_op():
+    assert m.lib().moe_probe_stream_copy(None, None, 0, None) == m.MOE_OK
