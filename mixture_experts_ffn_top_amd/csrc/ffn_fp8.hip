@@ -275,7 +275,10 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
     for (int ni = 0; ni < Q_NI; ++ni) {
       w[ni] = wsc[ws_blk[ni] * KT + kt];
-      if (w[ni] == 0.0f) bq[ni][0] = bq[ni][1] = i32x8_t{};
+      if (__builtin_bit_cast(uint32_t, w[ni]) << 1 == 0u) {
+        asm volatile("");
+        bq[ni][0] = bq[ni][1] = i32x8_t{};
+      }
     }
     const float* xs = (const float*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES);
 #pragma unroll
@@ -284,7 +287,10 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       if (mi + 1 < Q_MI) read_a(kt, mi + 1, aq[c ^ 1]);
       if (mi < live_mi) {
         const float x = xs[wm * Q_WTM + mi * 32 + fr];
-        if (x == 0.0f) aq[c][0] = aq[c][1] = i32x8_t{};
+        if (__builtin_amdgcn_ballot_w64(x == 0.0f) != 0) {
+          asm volatile("");
+          if (x == 0.0f) aq[c][0] = aq[c][1] = i32x8_t{};
+        }
 #pragma unroll
         for (int ni = 0; ni < Q_NI; ++ni) {
           float sc_ = x * w[ni];
