@@ -363,6 +363,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass of the routed experts (bf16 workloads) instead of the forward")
+    ap.add_argument("--scale-tokens", type=int, default=1, metavar="N",
+                    help="secondary data point: run the workload with N times its tokens, where the small "
+                         "bandwidth kernels leave the launch-latency regime (the config-size line is the reported one)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -393,6 +396,8 @@ def main():
         return
 
     cfg = synth.get_config(args.cfg)
+    if args.scale_tokens > 1:
+        cfg = synth.scaled(cfg, T=cfg.T * args.scale_tokens)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload cfg {cfg.cfg_id} ({cfg.name})", file=sys.stderr, flush=True)
@@ -456,6 +461,14 @@ def main():
         route_bytes = 2 * cfg.T * cfg.H + 2 * cfg.H * cfg.E + 8 * cfg.T * cfg.k
     else:                         # reads the logits and the bias, writes indices and weights
         route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
+    # build_indices: the CSR (histogram, scan, scatter: 20 bytes per routed row)
+    # plus, for the fp8 and W4A8 layers, the quantisation of x (each token
+    # once: bf16 read, codes and scales written; the GEMM gathers the rows)
+    idx_bytes = 20 * R + 4 * (cfg.E + 1)
+    if cfg.operand_dtype == "fp8":
+        idx_bytes += 2 * cfg.T * cfg.H + cfg.T * cfg.H + 4 * cfg.T * (cfg.H // 128)
+    elif cfg.operand_dtype == "mxfp4":
+        idx_bytes += 2 * cfg.T * cfg.H + cfg.T * cfg.H + cfg.T * (cfg.H // 32)
     o_bytes = 4 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else 2   # expert rows O: fp32 or bf16
     n_sh = getattr(cfg, "n_shared", 0)
     comb_bytes = o_bytes * (R + n_sh * cfg.T) * cfg.H + 8 * R + 4 * n_sh * cfg.T + 2 * cfg.T * cfg.H
@@ -491,14 +504,16 @@ def main():
                 "bytes_per_launch": ffn_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_ffn, 4)}
     mfma_key = "mfma_bf16_tflops" if peak == PEAK_BF16_TFLOPS else "mfma_fp8_tflops"
     roof = _with_measured(roof, ceil, mfma_key)
-    hbm = {"route": route_bytes / (t_route * 1e-3) / 1e9, "combine": comb_bytes / (t_comb * 1e-3) / 1e9}
+    hbm = {"route": route_bytes / (t_route * 1e-3) / 1e9, "build_indices": idx_bytes / (t_idx * 1e-3) / 1e9,
+           "combine": comb_bytes / (t_comb * 1e-3) / 1e9}
     line = {
         "metric": METRIC, "value": round(cfg.T / (ms_step * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4_w4a8", "mxfp4_a16": "mxfp4_w4a16"}[cfg.operand_dtype],
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
+        "config": {"workload": ("" if args.scale_tokens == 1 else f"[secondary: {args.scale_tokens}x tokens] ")
+                               + f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
                                f"top-{cfg.k} {cfg.router} router moe_dim={cfg.D} {cfg.gate_up_format} "
                                f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,
                    "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D, "parallelism": "none (1 GPU)"},
