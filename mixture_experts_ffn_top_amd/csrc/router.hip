@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void router_softmax_logits_kernel(
 // x as the B operand (16 tokens).  The hidden dimension is streamed in chunks
 // of RX_CC columns: the 16 token rows and the padded expert rows of a chunk
 // go straight from HBM/L2 into LDS with buffer loads (no VGPRs, one 1 KB
-// coalesced piece per instruction), RX_NS chunks deep, so that many loads
+// coalesced piece per instruction), NS chunks deep, so that many loads
 // are in flight per CU; the kernel is bound by reading x once.  Inside a
 // chunk wave w takes the 32-column k steps w, w+4, ...; the four partial
 // sums meet in LDS, then each wave runs the top-k of 4 tokens.
@@ -115,7 +115,10 @@ template <int ETILES>
 struct RxShape {
   static constexpr int EP = ETILES * 16;
   static constexpr int STAGE = (16 + EP) * RX_ROWB;                  // bytes per chunk
-  static constexpr int NS = ETILES == 1 ? 8 : ETILES == 2 ? 5 : ETILES == 4 ? 3 : 2;
+  // chunks in the pipeline: for E <= 32 few enough (<= 72 KB of LDS) that two
+  // workgroups share a CU, so that at large T one's ramp and top-k overlap
+  // the other's stream (at T = 32768, E = 8: 94 us against 110 with 8 chunks)
+  static constexpr int NS = ETILES == 1 ? 4 : ETILES == 2 ? 3 : ETILES == 4 ? 3 : 2;
   static constexpr int LPW = (16 + EP) * RX_ROWB / 1024 / 4;         // 1 KB loads per wave per chunk
   static constexpr int PART = 4 * 16 * (EP + 1) * 4;                 // partial-sum exchange
   static constexpr int LDS = NS * STAGE > PART ? NS * STAGE : PART;
