@@ -147,6 +147,12 @@ PROFILE_CMDS = """# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp
 
 # the MX workloads' kernel traces, summarised by the same --summarize-profile call
 EXTRA_TRACES = [
+    ("trace3", 3, "sink_router_shared_experts_layer_kernel_stats.txt",
+     "sigmoid-sink router layer with two shared experts: T=8192 tokens, hidden 2048, 128 experts, top-6 + 2 sink "
+     "lanes, moe_dim 768, SiLU, bf16"),
+    ("trace4", 4, "gptoss_shape_layer_kernel_stats.txt",
+     "gpt-oss-shape layer: T=4096 tokens, hidden 2880, 32 experts, top-4 softmax gate, moe_dim 2880, interleaved "
+     "gate_up, swigluoai (alpha 1.702, limit 7), biases, bf16"),
     ("trace5", 5, "fp8_block_scaled_layer_kernel_stats.txt",
      "fp8 block-scaled layer: T=16384 tokens, hidden 7168, 256 experts, top-8 sigmoid router, moe_dim 2048, "
      "SiLU, e4m3 operands with 128-wide fp32 block scales"),
