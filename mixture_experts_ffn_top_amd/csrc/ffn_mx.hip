@@ -27,8 +27,9 @@
 //
 // Tiling: 256 x 256 workgroup tile, 8 waves in 2 x 4 (two per SIMD), each
 // wave 128 x 64 = 4 x 2 MFMA blocks.  k stages of 128 go global -> LDS by
-// buffer loads, triple buffered: 32 KB of e4m3 rows, 16 KB of packed e2m1
-// rows and the two operands' 4 scale bytes per row.
+// buffer loads: the 32 KB of e4m3 activation rows (and their 4 scale bytes
+// per row) double buffered by waves 0-3, the 16 KB of packed e2m1 weight
+// rows (and theirs) four deep by waves 4-7.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,7 +40,6 @@ namespace {
 enum { MX_GATE_UP = 0, MX_DOWN = 1 };
 
 constexpr int X_BM = 256, X_BN = 256, X_BK = 128;         // BK in elements
-constexpr int X_NSTAGE = 3;
 constexpr int X_WAVES_M = 2, X_WAVES_N = 4;
 constexpr int X_NT = 64 * X_WAVES_M * X_WAVES_N;           // 512 threads
 constexpr int X_WTM = X_BM / X_WAVES_M, X_WTN = X_BN / X_WAVES_N;  // 128 x 64
@@ -48,13 +48,9 @@ constexpr int X_A_ROW = X_BK;                              // bytes per e4m3 sta
 constexpr int X_B_ROW = X_BK / 2;                          // bytes per packed e2m1 stage row
 constexpr int X_A_BYTES = X_BM * X_A_ROW;                  // 32 KB
 constexpr int X_B_BYTES = X_BN * X_B_ROW;                  // 16 KB
-constexpr int X_AS_OFF = X_A_BYTES + X_B_BYTES;            // 256 scale dwords of the A rows
-constexpr int X_BS_OFF = X_AS_OFF + X_BM * 4;              // 256 scale dwords of the B rows
-constexpr int X_STAGE_BYTES = X_BS_OFF + X_BN * 4;         // 50 KB
-constexpr int X_LPW_A = X_A_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 4
-constexpr int X_LPW_B = X_B_BYTES / 1024 / (X_WAVES_M * X_WAVES_N);  // 2
-constexpr int X_LOADS = X_LPW_A + X_LPW_B + 2;             // per wave per stage (+2: scale rows)
-constexpr int X_LDS_PIPE = X_NSTAGE * X_STAGE_BYTES;       // 150 KB
+// LDS: activation slots of X_A_BYTES + 256 scale dwords in a ring of 2, weight
+// slots of X_B_BYTES + 256 scale dwords in a ring of 4 (134 KB)
+constexpr int X_LDS_PIPE = 2 * (X_A_BYTES + X_BM * 4) + 4 * (X_B_BYTES + X_BN * 4);
 
 constexpr int X_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
 // A byte offset past every buffer's 0x7fffffff-byte range (also with a stage's
@@ -208,50 +204,64 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
   // the scalar offset, the LDS destination in M0.  A rows past the expert's
   // last row read zeros; weight rows past N repeat the last one.  Neither
   // result is ever stored.
+  // Loader roles: waves 0-3 fetch the activation rows (and their scales)
+  // into a ring of 2 stages, waves 4-7 the weight rows (and theirs) into a
+  // ring of 4.  A wave's vmcnt then counts one stream only, so the weight
+  // stream keeps three stages in flight while the activations, re-read from
+  // L2 by the neighbouring n-blocks, keep one.
+  constexpr int A_SLOT = X_A_BYTES + X_BM * 4, B_SLOT = X_B_BYTES + X_BN * 4;
+  constexpr int NA = 2, NB4 = 4, B_RING = NA * A_SLOT;
+  constexpr int LB = X_B_BYTES / 1024 / 4 + 1;  // loads per weight-role wave per stage
+  const bool a_role = wave_s < 4;
+  const int rw = wave_s & 3;
   const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
   const uint8_t* WSexp = p.W_scale + (int64_t)e * p.ws_estride;
-  uint32_t a_voff[X_LPW_A], b_voff[X_LPW_B];
+  uint32_t voff[8];
+  uint32_t s_voff;
+  if (a_role) {
 #pragma unroll
-  for (int i = 0; i < X_LPW_A; ++i) {
-    const int trow = (wave * X_LPW_A + i) * 8 + (lane >> 3);
-    const int r = row_beg + trow;
-    if (r < row_end) {
-      const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
-      a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
-    } else {
-      a_voff[i] = X_OOB;   // past the expert's rows: reads zeros, moves no memory
+    for (int i = 0; i < 8; ++i) {
+      const int trow = (rw * 8 + i) * 8 + (lane >> 3);
+      const int r = row_beg + trow;
+      if (r < row_end) {
+        const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+        voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
+      } else {
+        voff[i] = X_OOB;
+      }
     }
-  }
+    const int a_sr = min(row_beg + rw * 64 + lane, row_end - 1);
+    s_voff = (p.gather ? (uint32_t)p.gather[a_sr] : (uint32_t)a_sr) * srow;
+  } else {
 #pragma unroll
-  for (int i = 0; i < X_LPW_B; ++i) {
-    const int trow = (wave * X_LPW_B + i) * 16 + (lane >> 2);
-    b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)p.K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+    for (int i = 0; i < 4; ++i) {
+      const int trow = (rw * 4 + i) * 16 + (lane >> 2);
+      voff[i] = (uint32_t)w_row(trow) * ((uint32_t)p.K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+    }
+#pragma unroll
+    for (int i = 4; i < 8; ++i) voff[i] = 0;
+    s_voff = (uint32_t)w_row(rw * 64 + lane) * srow;
   }
-  // scale rows: lanes 0..31 of wave w fetch the 4 bytes of tile rows 32w + lane
-  const int sr = wave * 32 + (lane & 31);
-  const int a_sr = min(row_beg + sr, row_end - 1);
-  const uint32_t as_voff = (p.gather ? (uint32_t)p.gather[a_sr] : (uint32_t)a_sr) * srow;
-  const uint32_t bs_voff = (uint32_t)w_row(sr) * srow;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, X_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A_scale, (short)0, 0x7fffffff, X_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)WSexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
 
-  auto stage_base = [&](int kt) { return smem + (kt % X_NSTAGE) * X_STAGE_BYTES; };
-  auto issue = [&](int kt) {
-    uint8_t* st = stage_base(kt);
+  auto a_slot = [&](int kt) { return smem + (kt % NA) * A_SLOT; };
+  auto b_slot = [&](int kt) { return smem + B_RING + (kt % NB4) * B_SLOT; };
+  auto issue_a = [&](int kt) {
+    uint8_t* st = a_slot(kt);
 #pragma unroll
-    for (int i = 0; i < X_LPW_A; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (wave_s * X_LPW_A + i) * 1024), 16, a_voff[i],
-                                               kt * X_A_ROW, 0, 0);
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (rw * 8 + i) * 1024), 16, voff[i], kt * X_A_ROW, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(st + X_A_BYTES + rw * 256), 4, s_voff, kt * 4, 0, 0);
+  };
+  auto issue_b = [&](int kt) {
+    uint8_t* st = b_slot(kt);
 #pragma unroll
-    for (int i = 0; i < X_LPW_B; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + X_A_BYTES + (wave_s * X_LPW_B + i) * 1024), 16,
-                                               b_voff[i], kt * X_B_ROW, 0, 0);
-    if (lane < 32) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(st + X_AS_OFF + wave_s * 128), 4, as_voff, kt * 4, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + X_BS_OFF + wave_s * 128), 4, bs_voff, kt * 4, 0, 0);
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + (rw * 4 + i) * 1024), 16, voff[i], kt * X_B_ROW, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + X_B_BYTES + rw * 256), 4, s_voff, kt * 4, 0, 0);
   };
 
   const int fr = lane & 31, fh = lane >> 5;
@@ -270,25 +280,39 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
     return i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
   };
   auto frag_b = [&](const uint8_t* st, int row, int kk) {
-    const u32x4_t c4 = *(const u32x4_t*)(st + X_A_BYTES + mx_b_off(row, 2 * kk + fh));
+    const u32x4_t c4 = *(const u32x4_t*)(st + mx_b_off(row, 2 * kk + fh));
     return i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
   };
 
   const int live_mi = min(max((row_end - (row_beg + wm_s * X_WTM) + 31) / 32, 0), X_MI);
 
-  // ---- main loop: stage kt is waited for and published, stage kt+2 is
-  // issued into the buffer of stage kt-1 (free: every wave has passed the
-  // barrier after computing it), then the stage's 16 MFMAs per wave run
-  issue(0);
-  if (KT > 1) issue(1);
+  // ---- main loop.  Iteration kt: each role waits for its own loads of stage
+  // kt (the weight waves leave stages kt+1 and kt+2 in flight), the barrier
+  // publishes the stage, then the activation waves issue stage kt+1 into the
+  // activation slot of stage kt-1 and the weight waves stage kt+3 into the
+  // weight slot of stage kt-1 (both free: every wave has passed the barrier
+  // after computing stage kt-1), and the stage's 16 MFMAs per wave run
+  if (a_role) {
+    issue_a(0);
+  } else {
+    issue_b(0);
+    if (KT > 1) issue_b(1);
+    if (KT > 2) issue_b(2);
+  }
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(X_LOADS));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if (a_role || kt + 1 >= KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    else if (kt + 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * LB));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(LB));
     mx_block_barrier();
-    if (kt + 2 < KT) issue(kt + 2);
-    const uint8_t* st = stage_base(kt);
-    const uint32_t* as_l = (const uint32_t*)(st + X_AS_OFF);
-    const uint32_t* bs_l = (const uint32_t*)(st + X_BS_OFF);
+    if (a_role) {
+      if (kt + 1 < KT) issue_a(kt + 1);
+    } else {
+      if (kt + 3 < KT) issue_b(kt + 3);
+    }
+    const uint8_t* ast = a_slot(kt);
+    const uint8_t* bst = b_slot(kt);
+    const uint32_t* as_l = (const uint32_t*)(ast + X_A_BYTES);
+    const uint32_t* bs_l = (const uint32_t*)(bst + X_B_BYTES);
     i32x8_t bq[X_NI][2];
     int bsc[X_NI][2];
 #pragma unroll
@@ -297,7 +321,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
       const uint32_t s4 = bs_l[row];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bq[ni][kk] = frag_b(st, row, kk);
+        bq[ni][kk] = frag_b(bst, row, kk);
         bsc[ni][kk] = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
       }
     }
@@ -308,7 +332,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
         const uint32_t s4 = as_l[row];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const i32x8_t aq = frag_a(st, row, kk);
+          const i32x8_t aq = frag_a(ast, row, kk);
           const int asc = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
 #pragma unroll
           for (int ni = 0; ni < X_NI; ++ni)
