@@ -67,6 +67,33 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
 
 
+def algorithmic_work(cfg) -> dict:
+    """Algorithmic work of one layer step: the flops of the two grouped GEMMs
+    and the HBM bytes of the bandwidth kernels (each tensor read or written
+    once), the figures the roofline fractions are computed from."""
+    T, H, D, E, k = cfg.T, cfg.H, cfg.D, cfg.E, cfg.k
+    R = T * k
+    if cfg.router == "softmax":   # reads x and W_gate, writes indices and weights
+        route_bytes = 2 * T * H + 2 * H * E + 8 * T * k
+    else:                         # reads the logits and the bias, writes indices and weights (and sink weights)
+        route_bytes = 4 * T * (E + cfg.s) + 4 * E + 8 * T * k + 4 * T * cfg.s
+    # build_indices: the CSR (histogram, scan, scatter: 20 bytes per routed row)
+    # plus, for the fp8 and W4A8 layers, the quantisation of x (each token
+    # once: bf16 read, codes and scales written; the GEMM gathers the rows)
+    idx_bytes = 20 * R + 4 * (E + 1)
+    if cfg.operand_dtype == "fp8":
+        idx_bytes += 2 * T * H + T * H + 4 * T * (H // 128)
+    elif cfg.operand_dtype == "mxfp4":
+        idx_bytes += 2 * T * H + T * H + T * (H // 32)
+    o_bytes = 4 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else 2   # expert rows O: fp32 or bf16
+    n_sh = getattr(cfg, "n_shared", 0)
+    # combine: read every routed row of O (and each token's shared-expert rows),
+    # the slot rows and weights (and the sink weights), write y in bf16
+    comb_bytes = o_bytes * (R + n_sh * T) * H + 8 * R + 4 * n_sh * T + 2 * T * H
+    return {"gate_up_flops": 4.0 * R * H * D, "down_flops": 2.0 * R * D * H, "route_bytes": route_bytes,
+            "build_indices_bytes": idx_bytes, "combine_bytes": comb_bytes}
+
+
 def measure_ceilings(moe, torch) -> dict:
     """Practical ceilings on this chip, measured with the library's probes
     right after the timed steps (same clocks): an MFMA loop on every CU for
@@ -461,28 +488,13 @@ def main():
     ceil = measure_ceilings(moe, torch)
 
     R = cfg.T * cfg.k
-    gu_flops = 4.0 * R * cfg.H * cfg.D
-    dn_flops = 2.0 * R * cfg.D * cfg.H
+    work = algorithmic_work(cfg)
+    gu_flops, dn_flops = work["gate_up_flops"], work["down_flops"]
+    route_bytes, idx_bytes, comb_bytes = work["route_bytes"], work["build_indices_bytes"], work["combine_bytes"]
     # fp8 and the MXFP4 x MXFP8 product (which runs at the fp8 MFMA rate) take the fp8 peak
     peak = PEAK_BF16_TFLOPS if cfg.operand_dtype in ("bf16", "mxfp4_a16") else PEAK_FP8_TFLOPS
     gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
     ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
-    # algorithmic HBM bytes of the two bandwidth kernels
-    if cfg.router == "softmax":   # reads x and W_gate, writes indices and weights
-        route_bytes = 2 * cfg.T * cfg.H + 2 * cfg.H * cfg.E + 8 * cfg.T * cfg.k
-    else:                         # reads the logits and the bias, writes indices and weights
-        route_bytes = 4 * cfg.T * (cfg.E + cfg.s) + 4 * cfg.E + 8 * cfg.T * cfg.k + 4 * cfg.T * cfg.s
-    # build_indices: the CSR (histogram, scan, scatter: 20 bytes per routed row)
-    # plus, for the fp8 and W4A8 layers, the quantisation of x (each token
-    # once: bf16 read, codes and scales written; the GEMM gathers the rows)
-    idx_bytes = 20 * R + 4 * (cfg.E + 1)
-    if cfg.operand_dtype == "fp8":
-        idx_bytes += 2 * cfg.T * cfg.H + cfg.T * cfg.H + 4 * cfg.T * (cfg.H // 128)
-    elif cfg.operand_dtype == "mxfp4":
-        idx_bytes += 2 * cfg.T * cfg.H + cfg.T * cfg.H + cfg.T * (cfg.H // 32)
-    o_bytes = 4 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else 2   # expert rows O: fp32 or bf16
-    n_sh = getattr(cfg, "n_shared", 0)
-    comb_bytes = o_bytes * (R + n_sh * cfg.T) * cfg.H + 8 * R + 4 * n_sh * cfg.T + 2 * cfg.T * cfg.H
     roof = {"bound": "mfma", "achieved": round(gu_tf, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(gu_tf / peak, 4), "traffic": _traffic() if cfg.cfg_id == 2 else None,
             "kernel": "grouped gate_up GEMM + fused activation",
