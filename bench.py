@@ -298,28 +298,85 @@ def summarize_profile(d: str):
     print(f"[bench] wrote the profile summaries under {prof}", file=sys.stderr)
 
 
+def _cpu_model() -> str:
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, inp, n_tokens: int):
-    """The oracle as it stands, on a sample of the workload's tokens."""
+    """The oracle as it stands, on a sample of the workload's tokens, with the
+    BLAS thread pool set to every core this process may run on."""
     import numpy as np
     import synth
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    affinity = len(os.sched_getaffinity(0))
     hin = synth.to_host(inp)
     rng = np.random.default_rng(0)
     tokens = np.arange(cfg.T) if n_tokens >= cfg.T else np.sort(rng.choice(cfg.T, n_tokens, replace=False))
-    t0 = time.perf_counter()
-    r = O.route(hin, cfg)
-    y = O.layer(hin, cfg, indices=r["indices"], weights=r["weights"], tokens=tokens)
-    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=affinity, user_api="blas")
+        blas = [{"library": i.get("internal_api"), "threads": i.get("num_threads")}
+                for i in threadpool_info() if i.get("user_api") == "blas"]
+    except Exception:  # noqa: BLE001
+        limiter, blas = None, []
+    try:
+        t0 = time.perf_counter()
+        r = O.route(hin, cfg)
+        y = O.layer(hin, cfg, indices=r["indices"], weights=r["weights"], tokens=tokens)
+        dt = time.perf_counter() - t0
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
     assert np.all(np.isfinite(y))
+    threads = max([b["threads"] or 1 for b in blas] or [affinity])
     return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"the whole workload ({cfg.T} tokens)" if n_tokens >= cfg.T else
                        f"{n_tokens} of {cfg.T} tokens (seeded), all experts they route to, routing of all "
-                       f"{cfg.T} tokens") + f"; {dt:.1f} s on the host, float64 numpy"}
+                       f"{cfg.T} tokens") + f"; {dt:.1f} s on the host, float64 numpy",
+            "cpu_model": _cpu_model(), "affinity_cores": affinity, "blas_threads": blas,
+            "seconds": round(dt, 3)}
+
+
+def flushed_bandwidth(layer, moe, torch, work: dict, reps: int = 11) -> dict:
+    """route, build_indices and combine timed alone on the layer's last inputs,
+    each launch after a 512 MiB streaming copy that evicts them from L2 and
+    the Infinity Cache: median and minimum over `reps` launches, and the
+    median's rate in algorithmic HBM bytes against the 8 TB/s peak."""
+    import statistics
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    ev = HipEvents(2)
+    calls = layer.stage_calls()
+    nbytes = {"route": work["route_bytes"], "build_indices": work["build_indices_bytes"],
+              "combine": work["combine_bytes"]}
+    out = {}
+    for name, call in calls.items():
+        call()
+        ts = []
+        for _ in range(reps):
+            moe.probe_stream_copy(src, dst)
+            ev.record(0, stream)
+            call()
+            ev.record(1, stream)
+            torch.cuda.synchronize()
+            ts.append(ev.elapsed_ms(0, 1))
+        med, mn = statistics.median(ts), min(ts)
+        gbs = nbytes[name] / (med * 1e-3) / 1e9
+        out[name] = {"median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "gbs": round(gbs, 1),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes[name]}
+    ev.close()
+    del src, dst
+    return out
 
 
 def bench_backward(args, cfg, inp, moe, torch):
@@ -484,11 +541,13 @@ def main():
     t_comb = (mean_ms(9, 6) if has_shared else mean_ms(5, 6))
     t_layer_dev = mean_ms(0, 6)
     ev.close()
+    R = cfg.T * cfg.k
+    work = algorithmic_work(cfg)
+    print("[bench] bandwidth kernels alone from a flushed cache", file=sys.stderr, flush=True)
+    flushed = flushed_bandwidth(layer, moe, torch, work)
     print("[bench] measured ceilings (MFMA loop, streaming copy)", file=sys.stderr, flush=True)
     ceil = measure_ceilings(moe, torch)
 
-    R = cfg.T * cfg.k
-    work = algorithmic_work(cfg)
     gu_flops, dn_flops = work["gate_up_flops"], work["down_flops"]
     route_bytes, idx_bytes, comb_bytes = work["route_bytes"], work["build_indices_bytes"], work["combine_bytes"]
     # fp8 and the MXFP4 x MXFP8 product (which runs at the fp8 MFMA rate) take the fp8 peak
@@ -547,9 +606,16 @@ def main():
                          "gate_up": round(t_gu, 4), "down": round(t_dn, 4),
                          **({"shared_experts_ffn": round(t_shared, 4)} if has_shared else {}),
                          "combine": round(t_comb, 4), "layer_device": round(t_layer_dev, 4)},
-        "hbm_gbs": {n: round(v, 1) for n, v in hbm.items()},
-        "hbm_frac": {n: round(v / PEAK_HBM_GBS, 4) for n, v in hbm.items()},
-        "hbm_frac_of_measured": {n: round(v / ceil["stream_copy_gbs"], 4) for n, v in hbm.items()},
+        # the bandwidth kernels alone, each from a flushed cache (median of 11)
+        "hbm_gbs": {n: v["gbs"] for n, v in flushed.items()},
+        "hbm_frac": {n: v["frac"] for n, v in flushed.items()},
+        "hbm_frac_of_measured": {n: round(v["gbs"] / ceil["stream_copy_gbs"], 4) for n, v in flushed.items()},
+        "hbm_flushed": flushed,
+        # the same kernels inside the timed layer steps (mean of the steps): the
+        # combine there reads the rows O the down GEMM has just left in the
+        # Infinity Cache, so its rate is partly cache bandwidth
+        "hbm_in_layer_cache_warm": {n: {"gbs": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4)}
+                                    for n, v in hbm.items()},
         "measured_ceilings": ceil,
         "weight_layout": "out_in (transposed stacked weights, laid out once at load)",
     }

@@ -572,9 +572,43 @@ class MoELayer:
                     n_shared=self.n_shared)
         if mark:
             mark(3)
-        self.last = {"x": x, "weights": w, "index": ind, "O": O, "token_mask": token_mask, "x_gather": xg}
+        self.last = {"x": x, "weights": w, "index": ind, "O": O, "token_mask": token_mask, "x_gather": xg,
+                     "indices": idx, "O_shared": O_sh, "sink_weights": sw}
         return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O,
                 "O_shared": O_sh}
+
+    def stage_calls(self):
+        """The routing, bucketing and combine calls of the last forward, each
+        as a zero-argument callable on the same inputs and output buffers
+        (to time a bandwidth kernel alone, e.g. from a cold cache)."""
+        c = self.cfg
+        f = self.last
+        x, w, ind, tm = f["x"], f["weights"], f["index"], f["token_mask"]
+        if c.router == "softmax":
+            def rt():
+                return route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate, route_scale=c.route_scale,
+                             global_scale=self.global_scale)
+        else:
+            def rt():
+                return route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=self.logits,
+                             expert_bias=self.expert_bias, route_scale=c.route_scale,
+                             global_scale=self.global_scale)
+        idx = f["indices"]
+        if c.operand_dtype in ("fp8", "mxfp4"):
+            q = "fp8" if c.operand_dtype == "fp8" else "mxfp8"
+
+            def bi():
+                return build_indices(idx, c.E, weights=w, token_mask=tm, x=x,
+                                     xperm_dtype=q + "_tokens" if self.gather else q)
+        else:
+            def bi():
+                return build_indices(idx, c.E, weights=w, token_mask=tm, x=None if self.gather else x)
+
+        def cb():
+            return combine(f["O"], ind["row_of_slot"], c.T, c.k, weights=w, token_mask=tm, out=self.y,
+                           shared_out=f["O_shared"], shared_weights=f["sink_weights"] if c.router == "sigmoid_sink"
+                           else None, n_shared=self.n_shared)
+        return {"route": rt, "build_indices": bi, "combine": cb}
 
     def backward(self, dy, *, workspace=None, timing_events=None, weight_grad=True):
         """Backward of the routed experts of the last forward (bf16 layers,

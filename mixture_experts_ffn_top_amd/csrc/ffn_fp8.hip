@@ -1,5 +1,6 @@
 // Grouped fp8 (OCP e4m3fn) block-scaled expert GEMMs on gfx950 MFMA
-// (v_mfma_scale_f32_32x32x64_f8f6f4 with unit hardware scales).
+// (v_mfma_scale_f32_32x32x64_f8f6f4; its E8M0 operand scales carry the
+// power-of-two part of the block scales).
 //
 // Operands carry software scales (StackedMoE page: FP8 quantization with
 // block scaling; the fp8 layer's weights have one fp32 scale per 128 x 128
@@ -9,11 +10,18 @@
 // so that
 //   C[m, n] = sum over 128-wide k blocks kb of xs[m, kb] ws[n/128, kb] P_kb[m, n]
 // where P_kb is the product of the raw codes over block kb.  The two scales
-// are arbitrary fp32 values and cannot enter the MFMA; instead the running
-// sum is kept in units of the current block's scale s_kb = xs ws:
-//   acc <- acc * (s_{kb-1} / s_kb) + P_kb       and finally  C = acc * s_last
-// which needs no second set of accumulators (a zero scale keeps the previous
-// unit and zeroes the operand codes it scales, so its block adds nothing).
+// are arbitrary fp32 values.  Each is split exactly as s = 2^(e - 127) * m,
+// e its float32 exponent field clamped to [1, 253] and m = s * 2^(127 - e)
+// (in [1, 4) for a normal s, [2^-23, 1) for a subnormal one).  The exponent
+// bytes ride in the matrix instruction's E8M0 operand scales, which scale the
+// block product by 2^(ex + ew - 254) in hardware; the running sum is kept in
+// units of the current block's software factor u_kb = mx mw:
+//   acc <- acc * (u_{kb-1} / u_kb) + 2^(ex + ew - 254) P_kb,   C = acc * u_last
+// which needs no second set of accumulators.  The factors stay within
+// [2^-46, 16), so neither the reciprocal nor the rescale can overflow however
+// small the scales are, and a block whose scaled product falls below the
+// float32 range adds nothing, as it should.  A zero scale keeps the previous
+// unit and zeroes the operand codes it scales, so its block adds nothing.
 //
 // gate_up:  h = s_gu[e] * C, A = act(gate, up), then A is re-quantised per
 //           row per 128 columns (scale amax/448, 1 when amax = 0) -> codes +
@@ -70,6 +78,16 @@ __device__ __forceinline__ void f8_block_barrier() {
 }
 
 typedef const __attribute__((address_space(4))) float* scalar_f32_ptr;
+
+// s = 2^(e - 127) * m exactly: e (returned) is the exponent field clamped to
+// [1, 253], the E8M0 byte of the matrix instruction's operand scale; m =
+// s * 2^(127 - e).  Zero gives m = 0; a non-finite s gives a non-finite m.
+__device__ __forceinline__ int f8_split_scale(float s, float& m) {
+  const uint32_t ef = (__builtin_bit_cast(uint32_t, s) >> 23) & 0xffu;
+  const int e = (int)min(max(ef, 1u), 253u);
+  m = __builtin_amdgcn_ldexpf(s, 127 - e);
+  return e;
+}
 
 struct Fp8GemmArgs {
   const int32_t* offsets;
@@ -271,11 +289,13 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
   for (int kt = 0; kt < KT; ++kt) {
     // a zero scale keeps the previous unit and zeroes the codes it scales
-    float w[Q_NI];
+    float wm_[Q_NI];
+    int we[Q_NI];
 #pragma unroll
     for (int ni = 0; ni < Q_NI; ++ni) {
-      w[ni] = wsc[ws_blk[ni] * KT + kt];
-      if (__builtin_bit_cast(uint32_t, w[ni]) << 1 == 0u) {
+      const float w = wsc[ws_blk[ni] * KT + kt];
+      we[ni] = f8_split_scale(w, wm_[ni]);
+      if (__builtin_bit_cast(uint32_t, w) << 1 == 0u) {
         asm volatile("");
         bq[ni][0] = bq[ni][1] = i32x8_t{};
       }
@@ -291,20 +311,26 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
           asm volatile("");
           if (x == 0.0f) aq[c][0] = aq[c][1] = i32x8_t{};
         }
+        float xm;
+        const int xe = f8_split_scale(x, xm);
 #pragma unroll
         for (int ni = 0; ni < Q_NI; ++ni) {
-          float sc_ = x * w[ni];
-          sc_ = (sc_ != 0.0f) ? sc_ : unit[mi][ni];
-          const float ratio = unit[mi][ni] * __builtin_amdgcn_rcpf(sc_);
-          unit[mi][ni] = sc_;
+          float u = xm * wm_[ni];
+          u = (u != 0.0f) ? u : unit[mi][ni];
+          const float ratio = unit[mi][ni] * __builtin_amdgcn_rcpf(u);
+          unit[mi][ni] = u;
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mi][ni][r] *= ratio;
         }
+        // the exponent bytes: the weight operand's (first) is uniform, the
+        // activation operand's is this lane's row's (lanes r and 32 + r hold
+        // the two K halves of row r and pass the same byte)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int ni = 0; ni < Q_NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[ni][kk], aq[c][kk], acc[mi][ni], 0, 0, 0, 127, 0, 127);
+            acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[ni][kk], aq[c][kk], acc[mi][ni], 0, 0, 0,
+                                                                          we[ni], 0, xe);
       }
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));

@@ -160,6 +160,14 @@ def test_permute(moe, fp8):
     g.manual_seed(5)
     x = (torch.randn((T, H), generator=g, device=DEV) * 3).to(torch.bfloat16)
     x[5, :128] = 0                       # an all-zero group
+    if fp8:
+        # groups of bf16 subnormals, tiny and huge values: the scale amax/448
+        # is then subnormal, below 2^-92 or large, and each code still rounds
+        # the float32 quotient to nearest even
+        x[6, 128:256] = (torch.randn(128, generator=g, device=DEV) * 1e-39).to(torch.bfloat16)
+        x[7, 256:384] = (torch.randn(128, generator=g, device=DEV) * 1e-35).to(torch.bfloat16)
+        x[8, 384:512] = (torch.randn(128, generator=g, device=DEV) * 1e-30).to(torch.bfloat16)
+        x[9, 512:640] = (torch.randn(128, generator=g, device=DEV) * 1e30).to(torch.bfloat16)
     say(f"[permute] fp8={fp8} T={T} H={H}")
     mode = {False: "bf16", True: "fp8", "tokens": "fp8_tokens"}[fp8]
     out = moe.build_indices(torch.from_numpy(idx).to(DEV), E, x=x, xperm_dtype=mode)
@@ -212,6 +220,86 @@ def _check_routing(cfg, inp, res):
             assert_rel(host(res["sink_weights"]), rsw, W_RTOL, "sink weights")
 
 
+def _mblock_rows(off, seed, n_random=4, bm=256):
+    """{expert: CSR rows}: for every 256-row m-block the grouped GEMMs tile an
+    expert's rows into (the last one usually partly filled), its first and
+    last row and n_random random rows of it."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for e in range(len(off) - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = []
+        for r0 in range(lo, hi, bm):
+            r1 = min(r0 + bm, hi) - 1
+            rows += [r0, r1] + [int(v) for v in rng.integers(r0, r1 + 1, size=n_random)]
+        if rows:
+            out[e] = np.unique(np.array(rows, np.int64))
+    return out
+
+
+def _check_expert_rows(cfg, inp, res, layer, tol, seed):
+    """Expert rows O of every m-block of every expert, at full size, against
+    the oracle's expert MLP on those rows (rows are independent, so the
+    oracle's cost stays bounded); for the fp8 and W4A8 layers also the
+    re-quantised activation A of the same rows.  The error bar is
+    tol x the RMS of the oracle's rows."""
+    from concurrent.futures import ThreadPoolExecutor
+    op = cfg.operand_dtype
+    ind = res["index"]
+    off = host(ind["offsets"])
+    st = host(ind["sorted_token"])
+    rows_by_e = _mblock_rows(off, seed)
+    experts = sorted(rows_by_e)
+    all_rows = np.concatenate([rows_by_e[e] for e in experts])
+    say(f"  expert rows: {all_rows.size} rows over {len(experts)} experts, "
+        f"{sum((int(off[e + 1] - off[e]) + 255) // 256 for e in experts)} m-blocks")
+    sel = torch.from_numpy(all_rows).to(DEV)
+    o_gpu = host(res["O"].index_select(0, sel)).astype(np.float64)
+    tok = torch.from_numpy(st[all_rows].astype(np.int64)).to(DEV)
+    xq = O.layer_inputs_x({"x": host(inp["x"].index_select(0, tok))}, op)
+    kind = {"fp8": "fp8", "mxfp4": "mx"}.get(op)
+    if kind:
+        cg_all, sg_all = _gpu_act_rows(layer, kind, cfg.D, all_rows)
+    starts = np.cumsum([0] + [rows_by_e[e].size for e in experts])
+    wkeys = ["w_gate_up", "w_down"] + ([] if op == "bf16" else ["w_gate_up_scale", "w_down_scale"])
+
+    def one(i):
+        e = experts[i]
+        pos = slice(starts[i], starts[i + 1])
+        he = {kk: host(inp[kk][e:e + 1]) for kk in wkeys}
+        wgu, wd = O._expert_weights_f64(he, 0, op)
+        bgu = host(inp["b_gate_up"][e]) if cfg.has_bias else None
+        bd = host(inp["b_down"][e]) if cfg.has_bias else None
+        o_ref = O.expert_mlp(xq[pos], wgu, wd, fmt=cfg.gate_up_format, activation=cfg.activation,
+                             alpha=cfg.alpha, limit=cfg.limit, b_gate_up=bgu, b_down=bd,
+                             act_format=O._ACT_FORMAT[op])
+        stats = None
+        if kind:
+            h = xq[pos] @ wgu
+            if bgu is not None:
+                h = h + np.asarray(bgu, np.float64)[None, :]
+            gg, uu = O.split_gate_up(h, cfg.gate_up_format)
+            a = O.gated_activation(gg, uu, cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
+            stats = _act_code_stats(kind, cg_all[pos], sg_all[pos], a)
+        return o_ref, stats
+
+    with ThreadPoolExecutor(8) as ex:
+        results = list(ex.map(one, range(len(experts))))
+    o_ref = np.concatenate([r[0] for r in results])
+    rms = float(np.sqrt(np.mean(o_ref ** 2)))
+    diff = np.abs(o_gpu - o_ref)
+    err = float(diff.max()) / rms
+    worst_e = experts[int(np.searchsorted(starts, int(np.argmax(diff.max(axis=1))), side="right") - 1)]
+    say(f"  expert rows O max err / rms = {err:.3e} (worst expert {worst_e}, rms {rms:.3e})")
+    assert np.all(np.isfinite(o_gpu))
+    assert err <= tol
+    if kind:
+        same = sum(r[1][0] for r in results)
+        total = sum(r[1][1] for r in results)
+        worst = max(r[1][2] for r in results)
+        _assert_act_codes(same, total, worst, {"fp8": "fp8", "mx": "MXFP8"}[kind])
+
+
 @pytest.mark.parametrize("cid,changes,nsample", [
     (1, {}, 64),
     (3, {"T": 1024}, 1024),
@@ -235,9 +323,10 @@ def test_layer_full_size(moe, cid, nsample):
     cfg = synth.get_config(cid)
     inp = _gen(cfg)
     say(f"[layer full] cfg={cid}")
-    _, res = _run_layer(moe, cfg, inp)
+    layer, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=cid), BF16_TOL)
+    _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=cid)
 
 
 @pytest.mark.parametrize("act,alpha,limit,fmt,bias", [
@@ -432,21 +521,65 @@ def test_abi_errors_on_gpu_path(moe):
 
 # ---------------------------------------------------------------- fp8 block-scaled path
 
+def _act_code_stats(kind, cg, sg, a32):
+    """Compare the GPU's re-quantised activation rows (codes cg, scales sg)
+    with the oracle's quantisation of its own float32 activation a32.
+    Returns (identical codes, codes compared, worst distance in e4m3 steps).
+
+    The two activations differ by float32 rounding, so a code may land one
+    e4m3 step away where a value sits near a rounding boundary (for MX, a
+    block max near a power of two may also move the shared exponent); the
+    dequantised values must agree within two steps of the coarser encoding.
+    One step is 2^-3 of the value in the normal range; in the subnormal range
+    (|q| < 2^-6, absolute steps of 2^-9) values this close to zero move by a
+    few steps for float32-level differences of the activation, so there the
+    step is taken as the smallest normal 2^-6 -- all in units of the scale."""
+    if kind == "fp8":
+        codes_ref, sc_ref = O.quantize_rows_block128(a32)
+        deq_g = O.dequant_rows_block128(cg, sg)
+        deq_r = O.dequant_rows_block128(codes_ref, sc_ref)
+        step = np.maximum(np.abs(O.e4m3_decode(codes_ref)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(sc_ref, 128, axis=1)
+    else:
+        codes_ref, sc_ref = O.mxfp8_quantize_rows(a32)
+        deq_g = O.mx_dequant_fp8(cg, sg)
+        deq_r = O.mx_dequant_fp8(codes_ref, sc_ref)
+
+        def one(c, sc):
+            return np.maximum(np.abs(O.e4m3_decode(c)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(O.e8m0_decode(sc), 32, axis=1)
+        step = np.maximum(one(codes_ref, sc_ref), one(cg, sg))
+    ratio = np.abs(deq_g - deq_r) / step
+    return int(np.sum(cg == codes_ref)), cg.size, float(ratio.max()) if ratio.size else 0.0
+
+
+def _gpu_act_rows(layer, kind, D, rows):
+    """The GPU's re-quantised A for CSR rows `rows`: (codes, scales), gathered on the device."""
+    R = layer.R
+    so = ((R * D + 255) // 256) * 256
+    sel = torch.from_numpy(np.asarray(rows, np.int64)).to(DEV)
+    codes = layer.act_ws[: R * D].view(R, D).index_select(0, sel)
+    if kind == "fp8":
+        sc = layer.act_ws[so: so + R * (D // 128) * 4].view(torch.float32).view(R, D // 128).index_select(0, sel)
+    else:
+        sc = layer.act_ws[so: so + R * (D // 32)].view(R, D // 32).index_select(0, sel)
+    return host(codes), host(sc)
+
+
+def _assert_act_codes(same, total, worst, kind):
+    frac = same / max(total, 1)
+    say(f"  {kind} activation codes identical: {frac:.5f} of {total}; worst |gpu - oracle| = {worst:.3f} e4m3 steps")
+    # each side rounds to the nearest code (half a step each) and the two
+    # activations differ at float32 level: two steps bound the sum
+    assert frac >= 0.99
+    assert worst <= 2.0
+
+
 def _check_fp8_act(cfg, inp, res, layer):
-    """The re-quantised activation against the oracle's re-quantisation of its
-    own activation.  The two activations differ by float32 rounding, so a code
-    may land one e4m3 step away where a value sits near a rounding boundary;
-    the dequantised values must agree to within one step of the row scale."""
+    """The re-quantised activation against the oracle's re-quantisation of its own activation."""
     hin = synth.to_host(inp)
     ind = res["index"]
     off = host(ind["offsets"])
     st = host(ind["sorted_token"])
-    R, D = layer.R, cfg.D
-    n = int(off[-1])
-    ws = host(layer.act_ws)
-    codes_gpu = ws[: R * D].reshape(R, D)[:n]
-    so = ((R * D + 255) // 256) * 256
-    scale_gpu = ws[so: so + R * (D // 128) * 4].view(np.float32).reshape(R, D // 128)[:n]
+    D = cfg.D
     xq = O.layer_inputs_x(hin, "fp8")
     same = total = 0
     worst = 0.0
@@ -457,26 +590,10 @@ def _check_fp8_act(cfg, inp, res, layer):
         wgu = O.dequant_weight_block128(hin["w_gate_up"][e], hin["w_gate_up_scale"][e])
         h = xq[st[rows]] @ wgu
         a = O.gated_activation(h[:, :D], h[:, D:], cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
-        codes_ref, sc_ref = O.quantize_rows_block128(a)
-        cg = codes_gpu[rows]
-        same += int(np.sum(cg == codes_ref))
-        total += cg.size
-        deq_g = O.dequant_rows_block128(cg, scale_gpu[rows])
-        deq_r = O.dequant_rows_block128(codes_ref, sc_ref)
-        # one e4m3 step at the value in the normal range; in the subnormal
-        # range (|q| < 2^-6, absolute steps of 2^-9) values this close to zero
-        # move by a few steps for float32-level differences of the activation,
-        # so there the bound is the smallest normal 2^-6 -- all in units of the
-        # (oracle) row scale
-        step = np.maximum(np.abs(O.e4m3_decode(codes_ref)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(sc_ref, 128, axis=1)
-        ratio = np.abs(deq_g - deq_r) / step
-        worst = max(worst, float(ratio.max()))
-    frac = same / max(total, 1)
-    say(f"  fp8 activation codes identical: {frac:.5f}; worst |gpu - oracle| = {worst:.3f} e4m3 steps")
-    # each side rounds to the nearest code (half a step each) and the two
-    # activations differ at float32 level: two steps bound the sum
-    assert frac >= 0.99
-    assert worst <= 2.0
+        cg, sg = _gpu_act_rows(layer, "fp8", D, rows)
+        s_, t_, w_ = _act_code_stats("fp8", cg, sg, a)
+        same, total, worst = same + s_, total + t_, max(worst, w_)
+    _assert_act_codes(same, total, worst, "fp8")
 
 
 @pytest.mark.parametrize("changes,nsample,gather", [
@@ -514,13 +631,50 @@ def test_fp8_zero_scales(moe):
     _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
 
 
+def test_fp8_tiny_scales(moe):
+    """Block scales far below the usual range: a 128-group of a token at amax
+    about 1e-35, a group of bf16 subnormals, a token whose values are all
+    about 1e-36, tokens at about 1e-18 (whose activations A, about 1e-37,
+    get subnormal re-quantisation scales in the down GEMM), weight blocks of
+    amax 1e-30 and with a subnormal scale.  The products of two such scales
+    are subnormal or underflow to zero; the output must stay finite and
+    match the oracle."""
+    cfg = synth.scaled(synth.get_config(5), T=512, E=8, H=512, D=256)
+    inp = _gen(cfg)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(21)
+
+    def rnd(n, s):
+        return (torch.randn(n, generator=g, device=DEV) * s).to(torch.bfloat16)
+    x = inp["x"]
+    x[10, 128:256] = rnd(128, 1e-35)
+    x[11, 256:384] = rnd(128, 1e-39)          # bf16 subnormals
+    x[12, 0:128] = rnd(128, 1e-39)
+    x[12, 384:512] = rnd(128, 1e-37)
+    x[13, :] = rnd(512, 1e-36)
+    x[14, :] = rnd(512, 1e-18)
+    x[15, :] = rnd(512, 1e-18)
+    x[16, 0:128] = rnd(128, 2e-38)            # around the smallest normal
+    gus, ds = inp["w_gate_up_scale"], inp["w_down_scale"]   # [E, H/128, 2D/128], [E, D/128, H/128]
+    gus[:, 1, 0] = 1e-30 / 448                # a weight block of amax 1e-30 in every expert
+    gus[:, 2, 3] = 1e-40                      # a subnormal weight-block scale
+    ds[:, 0, 1] = 1e-30 / 448
+    ds[:, 1, 2] = 3e-41
+    say("[fp8 tiny scales]")
+    layer, res = _run_layer(moe, cfg, inp)
+    assert np.all(np.isfinite(host(res["O"])[: int(host(res["index"]["offsets"])[-1])]))
+    _check_fp8_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
+
+
 def test_fp8_layer_full_size(moe):
     cfg = synth.get_config(5)
     inp = _gen(cfg)
     say("[fp8 layer full] T=16384 H=7168 E=256 k=8 D=2048")
-    _, res = _run_layer(moe, cfg, inp)
+    layer, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=5), FP8_TOL)
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=5)
 
 
 # ---------------------------------------------------------------- MX: MXFP4 weights x MXFP8 activations
@@ -553,21 +707,12 @@ def test_mx_permute(moe, mode):
 
 
 def _check_mx_act(cfg, inp, res, layer):
-    """The MXFP8 re-quantised activation against the oracle's re-quantisation
-    of its own activation.  A value near a rounding boundary (or a block max
-    near a power of two, which moves the shared exponent) may land one step
-    away; dequantised, the two must agree within two steps of the coarser of
-    the two encodings."""
+    """The MXFP8 re-quantised activation against the oracle's re-quantisation of its own activation."""
     hin = synth.to_host(inp)
     ind = res["index"]
     off = host(ind["offsets"])
     st = host(ind["sorted_token"])
-    R, D = layer.R, cfg.D
-    n = int(off[-1])
-    ws = host(layer.act_ws)
-    codes_gpu = ws[: R * D].reshape(R, D)[:n]
-    so = ((R * D + 255) // 256) * 256
-    scale_gpu = ws[so: so + R * (D // 32)].reshape(R, D // 32)[:n]
+    D = cfg.D
     xq = O.layer_inputs_x(hin, "mxfp4")
     same = total = 0
     worst = 0.0
@@ -581,21 +726,10 @@ def _check_mx_act(cfg, inp, res, layer):
             h = h + hin["b_gate_up"][e].astype(np.float64)[None, :]
         gg, uu = O.split_gate_up(h, cfg.gate_up_format)
         a = O.gated_activation(gg, uu, cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
-        codes_ref, sc_ref = O.mxfp8_quantize_rows(a)
-        cg = codes_gpu[rows]
-        same += int(np.sum(cg == codes_ref))
-        total += cg.size
-        deq_g = O.mx_dequant_fp8(cg, scale_gpu[rows])
-        deq_r = O.mx_dequant_fp8(codes_ref, sc_ref)
-
-        def step(c, s):   # one e4m3 step at the value (2^-6 of the scale in the subnormal range)
-            return np.maximum(np.abs(O.e4m3_decode(c)) * 2.0 ** -3, 2.0 ** -6) * np.repeat(O.e8m0_decode(s), 32, axis=1)
-        ratio = np.abs(deq_g - deq_r) / np.maximum(step(codes_ref, sc_ref), step(cg, scale_gpu[rows]))
-        worst = max(worst, float(ratio.max()))
-    frac = same / max(total, 1)
-    say(f"  MXFP8 activation codes identical: {frac:.5f}; worst |gpu - oracle| = {worst:.3f} e4m3 steps")
-    assert frac >= 0.99
-    assert worst <= 2.0
+        cg, sg = _gpu_act_rows(layer, "mx", D, rows)
+        s_, t_, w_ = _act_code_stats("mx", cg, sg, a)
+        same, total, worst = same + s_, total + t_, max(worst, w_)
+    _assert_act_codes(same, total, worst, "MXFP8")
 
 
 @pytest.mark.parametrize("changes,nsample,gather", [
@@ -621,9 +755,10 @@ def test_mx_layer_full_size(moe):
     cfg = synth.get_config(6)
     inp = _gen(cfg)
     say("[mx layer full] T=16384 H=7168 E=256 k=8 D=2048 MXFP4 W4A8")
-    _, res = _run_layer(moe, cfg, inp)
+    layer, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 12, seed=6), FP8_TOL)
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=6)
 
 
 @pytest.mark.parametrize("changes,nsample,gather", [
@@ -649,9 +784,10 @@ def test_mx_w4a16_layer_full_size(moe):
     cfg = synth.get_config(7)
     inp = _gen(cfg)
     say("[mx w4a16 layer full] T=256 H=7168 E=256 k=8 D=2048 MXFP4 W4A16")
-    _, res = _run_layer(moe, cfg, inp)
+    layer, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 8, seed=8), BF16_TOL)
+    _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=8)
 
 
 
