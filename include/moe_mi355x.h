@@ -222,6 +222,29 @@ int64_t moe_build_indices_workspace_bytes(int32_t num_tokens, int32_t n_experts_
                                           int32_t n_local_experts);
 
 /* ------------------------------------------------------------------------
+ * moe_build_indices_noalloc -- moe_build_indices for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It computes exactly what
+ * moe_build_indices computes, with the same kernels, but its scratch (the
+ * per-block expert counts) is a static device array of the library, one
+ * copy per GPU, held until the process ends; it calls no allocating routine.
+ *
+ *   args           as for moe_build_indices, except that workspace must be
+ *                  NULL and workspace_bytes 0
+ * Errors: as moe_build_indices; MOE_ERR_WORKSPACE_TOO_SMALL when the call
+ * needs more than MOE_BUILD_INDICES_NOALLOC_MAX_SCRATCH bytes of scratch
+ * (moe_build_indices_workspace_bytes of its sizes), e.g. n_local_experts
+ * 1024 with more than 2^21 routed slots.
+ * The scratch needs no initial contents and keeps the last call's.  All
+ * calls on one GPU share it: calls that overlap on one GPU (on different
+ * streams, or from different host threads) race and give wrong results.
+ * The first call on each GPU looks up that GPU's copy of the array (with
+ * the device current); later calls reuse the address.
+ * ---------------------------------------------------------------------- */
+#define MOE_BUILD_INDICES_NOALLOC_MAX_SCRATCH (16 * 1024 * 1024)
+moe_status_t moe_build_indices_noalloc(const moe_index_args_t* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_ffn -- [StackedMoE] weight shapes, gate_up_format, has_bias,
  * quant_config (FP8 block scaling); [GatedAct] fused_activation, alpha, limit;
  * [NeMoExperts] _apply_bias; [MegaFFN] per-leg expert scales.

@@ -89,7 +89,7 @@ class FfnBwdArgs(ctypes.Structure):
                 ("d_b_down", _vp), ("workspace", _vp), ("workspace_bytes", _i64), ("timing_events", _vp)]
 
 
-ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_grouped_ffn", "moe_grouped_ffn_fused", "moe_combine",
+ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_build_indices_noalloc", "moe_grouped_ffn", "moe_grouped_ffn_fused", "moe_combine",
                 "moe_shared_indices", "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
                 "moe_ffn_fused_workspace_bytes", "moe_combine_backward", "moe_grouped_ffn_backward",
                 "moe_ffn_backward_workspace_bytes", "moe_transpose_bf16", "moe_probe_mfma",
@@ -101,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         raise ImportError(f"{path} is missing: build it with `python -m mixture_experts_ffn_top_amd.build`")
     lib = ctypes.CDLL(path)
     for name, argt in (("moe_route", RouteArgs), ("moe_build_indices", IndexArgs),
+                       ("moe_build_indices_noalloc", IndexArgs),
                        ("moe_grouped_ffn", FfnArgs), ("moe_grouped_ffn_fused", FfnArgs),
                        ("moe_combine", CombineArgs), ("moe_combine_backward", CombineBwdArgs),
                        ("moe_grouped_ffn_backward", FfnBwdArgs)):
@@ -205,20 +206,23 @@ def route(*, router: str, k: int, E: int, s: int = 0, x=None, w_gate=None, logit
 
 
 def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None, token_mask=None,
-                  x=None, xperm_dtype: str = "bf16"):
-    """moe_build_indices.  Returns a dict of device tensors: offsets, sorted_token,
-    row_of_slot, sorted_weight (if weights), x_perm / x_perm_scale (if x)."""
+                  x=None, xperm_dtype: str = "bf16", noalloc: bool = False, out: dict | None = None):
+    """moe_build_indices (noalloc=True: moe_build_indices_noalloc, whose
+    scratch is the library's static array).  Returns a dict of device
+    tensors: offsets, sorted_token, row_of_slot, sorted_weight (if weights),
+    x_perm / x_perm_scale (if x); `out` may pass those output buffers in."""
     T, k = indices.shape
     dev = indices.device
     _dt(indices, torch.int32, "indices")
     _dt(weights, torch.float32, "weights")
     _dt(token_mask, torch.uint8, "token_mask")
     R = T * k
-    out = {"offsets": torch.empty(n_local + 1, dtype=torch.int32, device=dev),
-           "sorted_token": torch.empty(max(R, 1), dtype=torch.int32, device=dev),
-           "row_of_slot": torch.empty(max(R, 1), dtype=torch.int32, device=dev)}
+    given = out or {}
+    out = {"offsets": given.get("offsets", torch.empty(n_local + 1, dtype=torch.int32, device=dev)),
+           "sorted_token": given.get("sorted_token", torch.empty(max(R, 1), dtype=torch.int32, device=dev)),
+           "row_of_slot": given.get("row_of_slot", torch.empty(max(R, 1), dtype=torch.int32, device=dev))}
     if weights is not None:
-        out["sorted_weight"] = torch.empty(max(R, 1), dtype=torch.float32, device=dev)
+        out["sorted_weight"] = given.get("sorted_weight", torch.empty(max(R, 1), dtype=torch.float32, device=dev))
     H = 0
     if xperm_dtype not in XPERM:
         raise ValueError(f"xperm_dtype must be one of {sorted(XPERM)}")
@@ -228,13 +232,19 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
     if x is not None:
         _dt(x, torch.bfloat16, "x")
         H = x.shape[1]
-        out["x_perm"] = torch.empty((max(rows, 1), H), dtype=torch.uint8 if quant else torch.bfloat16, device=dev)
+        out["x_perm"] = given.get("x_perm", torch.empty((max(rows, 1), H), dtype=torch.uint8 if quant else
+                                                        torch.bfloat16, device=dev))
         if mx:
-            out["x_perm_scale"] = torch.empty((max(rows, 1), H // 32), dtype=torch.uint8, device=dev)
+            out["x_perm_scale"] = given.get("x_perm_scale", torch.empty((max(rows, 1), H // 32), dtype=torch.uint8,
+                                                                        device=dev))
         elif quant:
-            out["x_perm_scale"] = torch.empty((max(rows, 1), H // 128), dtype=torch.float32, device=dev)
-    wsb = lib().moe_build_indices_workspace_bytes(T, k, n_local)
-    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+            out["x_perm_scale"] = given.get("x_perm_scale", torch.empty((max(rows, 1), H // 128),
+                                                                        dtype=torch.float32, device=dev))
+    if noalloc:
+        ws = None
+    else:
+        wsb = lib().moe_build_indices_workspace_bytes(T, k, n_local)
+        ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
     a = IndexArgs(num_tokens=T, n_experts_per_tok=k, experts_start_idx=expert_start,
                   n_local_experts=n_local, expert_indices=_ptr(indices), expert_weights=_ptr(weights),
                   token_mask=_ptr(token_mask), expert_offsets=_ptr(out["offsets"]),
@@ -242,8 +252,8 @@ def build_indices(indices, n_local: int, *, expert_start: int = 0, weights=None,
                   sorted_weight=_ptr(out.get("sorted_weight")), x=_ptr(x), hidden_dim=H,
                   xperm_dtype=XPERM[xperm_dtype],
                   x_perm=_ptr(out.get("x_perm")), x_perm_scale=_ptr(out.get("x_perm_scale")),
-                  workspace=_ptr(ws), workspace_bytes=ws.numel())
-    _check(lib().moe_build_indices(ctypes.byref(a), _stream(dev)))
+                  workspace=_ptr(ws), workspace_bytes=ws.numel() if ws is not None else 0)
+    _check((lib().moe_build_indices_noalloc if noalloc else lib().moe_build_indices)(ctypes.byref(a), _stream(dev)))
     return out
 
 

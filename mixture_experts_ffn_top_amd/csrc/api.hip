@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
@@ -124,45 +125,36 @@ int64_t moe_build_indices_workspace_bytes(int32_t T, int32_t k, int32_t L) {
   return round_up(nblk * L * (int64_t)sizeof(int32_t), 256);
 }
 
-moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
-  REQUIRE(a != nullptr, "moe_build_indices: args is NULL");
+}  // extern "C"
+
+namespace {
+
+// Checks every argument of moe_build_indices except the workspace, then
+// launches on `workspace` (at least moe_build_indices_workspace_bytes).
+moe_status_t build_indices_checked(const moe_index_args_t* a, int32_t* workspace, void* stream, const char* fn) {
   const int T = a->num_tokens, k = a->n_experts_per_tok, L = a->n_local_experts;
-  REQUIRE(T >= 0, "moe_build_indices: num_tokens must be >= 0 (got %d)", T);
-  REQUIRE(k >= 1 && k <= 1024, "moe_build_indices: n_experts_per_tok must be in [1, 1024] (got %d)", k);
-  REQUIRE(L >= 1 && L <= 1024, "moe_build_indices: n_local_experts must be in [1, 1024] (got %d)", L);
-  REQUIRE((int64_t)T * k < (int64_t)1 << 31, "moe_build_indices: num_tokens * n_experts_per_tok must be < 2^31");
-  REQUIRE(a->expert_offsets != nullptr, "moe_build_indices: expert_offsets is required");
-  REQUIRE(T == 0 || (a->expert_indices && a->sorted_token && a->row_of_slot),
-          "moe_build_indices: expert_indices, sorted_token and row_of_slot are required");
-  const int64_t need = moe_build_indices_workspace_bytes(T, k, L);
-  if (a->workspace_bytes < need || (need > 0 && a->workspace == nullptr))
-    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_build_indices: workspace needs %lld bytes (got %lld)",
-                (long long)need, (long long)a->workspace_bytes);
-  REQUIRE(aligned16(a->workspace), "moe_build_indices: workspace must be 16-byte aligned");
   const bool permute = a->x != nullptr;
   if (permute) {
     const int H = a->hidden_dim;
-    REQUIRE(H >= 8 && H % 8 == 0, "moe_build_indices: hidden_dim must be a positive multiple of 8 (got %d)", H);
-    REQUIRE(a->x_perm != nullptr, "moe_build_indices: x_perm is required with x");
-    REQUIRE(aligned16(a->x) && aligned16(a->x_perm), "moe_build_indices: x and x_perm must be 16-byte aligned");
+    REQUIRE(H >= 8 && H % 8 == 0, "%s: hidden_dim must be a positive multiple of 8 (got %d)", fn, H);
+    REQUIRE(a->x_perm != nullptr, "%s: x_perm is required with x", fn);
+    REQUIRE(aligned16(a->x) && aligned16(a->x_perm), "%s: x and x_perm must be 16-byte aligned", fn);
     if (a->xperm_dtype == MOE_DTYPE_FP8_E4M3_BLOCK128 || a->xperm_dtype == MOE_DTYPE_FP8_E4M3_TOKENS) {
-      REQUIRE(H % 128 == 0, "moe_build_indices: fp8 quantisation needs hidden_dim % 128 == 0 (got %d)", H);
-      REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for fp8");
+      REQUIRE(H % 128 == 0, "%s: fp8 quantisation needs hidden_dim %% 128 == 0 (got %d)", fn, H);
+      REQUIRE(a->x_perm_scale != nullptr, "%s: x_perm_scale is required for fp8", fn);
     } else if (a->xperm_dtype == MOE_DTYPE_MXFP8 || a->xperm_dtype == MOE_DTYPE_MXFP8_TOKENS) {
-      REQUIRE(H % 32 == 0, "moe_build_indices: MXFP8 quantisation needs hidden_dim % 32 == 0 (got %d)", H);
-      REQUIRE(a->x_perm_scale != nullptr, "moe_build_indices: x_perm_scale is required for MXFP8");
+      REQUIRE(H % 32 == 0, "%s: MXFP8 quantisation needs hidden_dim %% 32 == 0 (got %d)", fn, H);
+      REQUIRE(a->x_perm_scale != nullptr, "%s: x_perm_scale is required for MXFP8", fn);
     } else {
       REQUIRE(a->xperm_dtype == MOE_DTYPE_BF16,
-              "moe_build_indices: xperm_dtype must be BF16, FP8_E4M3_BLOCK128, FP8_E4M3_TOKENS, MXFP8 or "
-              "MXFP8_TOKENS");
+              "%s: xperm_dtype must be BF16, FP8_E4M3_BLOCK128, FP8_E4M3_TOKENS, MXFP8 or MXFP8_TOKENS", fn);
     }
   }
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = moe::launch_build_indices(a->expert_indices, a->expert_weights, a->token_mask, T, k,
                                            a->experts_start_idx, L, a->expert_offsets,
-                                           a->sorted_token, a->row_of_slot, a->sorted_weight,
-                                           (int32_t*)a->workspace, st);
-  if (e != hipSuccess) return hip_status(e, "moe_build_indices");
+                                           a->sorted_token, a->row_of_slot, a->sorted_weight, workspace, st);
+  if (e != hipSuccess) return hip_status(e, fn);
   if (permute) {
     const int dt = a->xperm_dtype;
     const bool tokens = dt == MOE_DTYPE_FP8_E4M3_TOKENS || dt == MOE_DTYPE_MXFP8_TOKENS;
@@ -170,9 +162,93 @@ moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
     e = moe::launch_permute((const uint16_t*)a->x, tokens ? nullptr : a->sorted_token,
                             a->expert_offsets + L, tokens ? (int64_t)T : (int64_t)T * k,
                             a->hidden_dim, kind, a->x_perm, a->x_perm_scale, st);
-    if (e != hipSuccess) return hip_status(e, "moe_build_indices (permute)");
+    if (e != hipSuccess) return hip_status(e, fn);
   }
   return ok();
+}
+
+moe_status_t build_indices_common_args(const moe_index_args_t* a, const char* fn) {
+  REQUIRE(a != nullptr, "%s: args is NULL", fn);
+  const int T = a->num_tokens, k = a->n_experts_per_tok, L = a->n_local_experts;
+  REQUIRE(T >= 0, "%s: num_tokens must be >= 0 (got %d)", fn, T);
+  REQUIRE(k >= 1 && k <= 1024, "%s: n_experts_per_tok must be in [1, 1024] (got %d)", fn, k);
+  REQUIRE(L >= 1 && L <= 1024, "%s: n_local_experts must be in [1, 1024] (got %d)", fn, L);
+  REQUIRE((int64_t)T * k < (int64_t)1 << 31, "%s: num_tokens * n_experts_per_tok must be < 2^31", fn);
+  REQUIRE(a->expert_offsets != nullptr, "%s: expert_offsets is required", fn);
+  REQUIRE(T == 0 || (a->expert_indices && a->sorted_token && a->row_of_slot),
+          "%s: expert_indices, sorted_token and row_of_slot are required", fn);
+  return MOE_OK;
+}
+
+// ---- the allocation-free form: its scratch (the per-block expert counts)
+// is a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes the array's name (a host
+// stand-in) to a kernel: the device address of each GPU's copy is looked up
+// once, with that device current, and used from then on.
+constexpr int64_t kNoallocScratchBytes = (int64_t)MOE_BUILD_INDICES_NOALLOC_MAX_SCRATCH;
+static __device__ __align__(256) int32_t scratch[kNoallocScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (NULL with the
+// message set on failure).
+int32_t* noalloc_scratch(const char* fn, moe_status_t* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = hip_status(e, fn);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the %d devices this form serves", fn, dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      *st = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, fn);
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = (int32_t*)p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_build_indices(const moe_index_args_t* a, void* stream) {
+  const char* fn = "moe_build_indices";
+  const moe_status_t c = build_indices_common_args(a, fn);
+  if (c != MOE_OK) return c;
+  const int64_t need = moe_build_indices_workspace_bytes(a->num_tokens, a->n_experts_per_tok, a->n_local_experts);
+  if (a->workspace_bytes < need || (need > 0 && a->workspace == nullptr))
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_build_indices: workspace needs %lld bytes (got %lld)",
+                (long long)need, (long long)a->workspace_bytes);
+  REQUIRE(aligned16(a->workspace), "moe_build_indices: workspace must be 16-byte aligned");
+  return build_indices_checked(a, (int32_t*)a->workspace, stream, fn);
+}
+
+moe_status_t moe_build_indices_noalloc(const moe_index_args_t* a, void* stream) {
+  const char* fn = "moe_build_indices_noalloc";
+  const moe_status_t c = build_indices_common_args(a, fn);
+  if (c != MOE_OK) return c;
+  REQUIRE(a->workspace == nullptr && a->workspace_bytes == 0,
+          "moe_build_indices_noalloc: workspace must be NULL and workspace_bytes 0 (the scratch is the library's)");
+  const int64_t need = moe_build_indices_workspace_bytes(a->num_tokens, a->n_experts_per_tok, a->n_local_experts);
+  if (need > kNoallocScratchBytes)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                "moe_build_indices_noalloc: this call needs %lld bytes of scratch; the static scratch holds %lld "
+                "(use moe_build_indices with a workspace)", (long long)need, (long long)kNoallocScratchBytes);
+  moe_status_t st = MOE_OK;
+  int32_t* ws = noalloc_scratch(fn, &st);
+  if (ws == nullptr) return st;
+  return build_indices_checked(a, ws, stream, fn);
 }
 
 // ---------------------------------------------------------------- grouped FFN

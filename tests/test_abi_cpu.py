@@ -217,6 +217,22 @@ def test_build_indices_validation(kw, status, frag):
     assert st == status and frag in msg, msg
 
 
+@pytest.mark.parametrize("kw,status,frag", [
+    (dict(), m.MOE_ERR_INVALID_ARGUMENT, "workspace must be NULL"),          # a workspace is not taken
+    (dict(workspace=None, workspace_bytes=0, n_local_experts=0), m.MOE_ERR_INVALID_ARGUMENT, "n_local_experts"),
+    # 2^20 tokens x 4 slots = 8192 blocks x 1024 experts x 4 bytes = 32 MiB > the 16 MiB static scratch
+    (dict(workspace=None, workspace_bytes=0, num_tokens=1 << 20, n_experts_per_tok=4, n_local_experts=1024),
+     m.MOE_ERR_WORKSPACE_TOO_SMALL, "static scratch"),
+])
+def test_build_indices_noalloc_validation(kw, status, frag):
+    """The allocation-free form refuses a workspace argument and any call
+    whose per-block counts exceed its static scratch, before any HIP call."""
+    st, msg = _err(m.lib().moe_build_indices_noalloc, _idx(**kw))
+    assert st == status and frag in msg, msg
+    assert m.lib().moe_build_indices_workspace_bytes(1 << 20, 4, 1024) == 32 * 1024 * 1024
+    assert m.lib().moe_build_indices_workspace_bytes(1 << 19, 4, 1024) == 16 * 1024 * 1024
+
+
 @pytest.mark.parametrize("kw,frag", [
     (dict(hidden_dim=100), "hidden_dim"),
     (dict(n_experts_per_tok=0), "n_experts_per_tok"),
