@@ -456,6 +456,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens the oracle baseline runs (capped at the workload's T)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("out_in", "in_out"), default="out_in",
+                    help="bf16 expert weights as the stacked [E, hidden, 2 moe_dim] / [E, moe_dim, hidden] tensors "
+                         "themselves (in_out) or their transposed views, laid out once at load (out_in)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass of the routed experts (bf16 workloads) instead of the forward")
     ap.add_argument("--scale-tokens", type=int, default=1, metavar="N",
@@ -504,7 +507,12 @@ def main():
             sys.exit(2)
         bench_backward(args, cfg, inp, moe, torch)
         return
-    layer = moe.MoELayer(cfg, inp)
+    layout = moe.WEIGHT_IN_OUT if args.layout == "in_out" else moe.WEIGHT_OUT_IN
+    if layout == moe.WEIGHT_IN_OUT and (cfg.operand_dtype != "bf16" or getattr(cfg, "fused", False)):
+        print("bench.py --layout in_out: the stacked layout is read by the two-launch bf16 FFN",
+              file=sys.stderr)
+        sys.exit(2)
+    layer = moe.MoELayer(cfg, inp, layout=layout)
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
     # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
@@ -617,7 +625,9 @@ def main():
         "hbm_in_layer_cache_warm": {n: {"gbs": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4)}
                                     for n, v in hbm.items()},
         "measured_ceilings": ceil,
-        "weight_layout": "out_in (transposed stacked weights, laid out once at load)",
+        "weight_layout": ("in_out (the stacked [E, hidden, 2 moe_dim] / [E, moe_dim, hidden] tensors, read "
+                          "directly)" if args.layout == "in_out" else
+                          "out_in (transposed stacked weights, laid out once at load)"),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)

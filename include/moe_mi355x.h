@@ -284,7 +284,13 @@ moe_status_t moe_build_indices_noalloc(const moe_index_args_t* args, void* strea
  *                  (x_perm / x, the activation buffer and one expert's
  *                  weights must each be under 2 GiB: the GEMMs address
  *                  them with buffer loads of a 2 GiB range)
- *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] or OUT_IN [L, 2D, H]
+ *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] (the [StackedMoE]
+ *                  "Weight tensor shapes" themselves) or OUT_IN [L, 2D, H]
+ *                  (its transposed view).  bf16 reads either layout
+ *                  (w_gate_up_layout and w_down_layout chosen independently;
+ *                  IN_OUT gate_up weights need the concatenated format, an
+ *                  interleaved IN_OUT gate_up is MOE_ERR_UNSUPPORTED); fp8
+ *                  and MX take OUT_IN only
  *   w_gate_up_scale fp32 [L, H/128, 2D/128] (IN_OUT) or [L, 2D/128, H/128];
  *                  MX: packed E2M1 w_gate_up [L, 2D, H/2] with E8M0 scale
  *                  bytes [L, 2D, H/32]

@@ -298,7 +298,7 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
                 w_gate_up=_ptr(weights.w_gate_up), w_gate_up_layout=weights.layout,
                 w_gate_up_scale=_ptr(weights.w_gate_up_scale), b_gate_up=_ptr(weights.b_gate_up),
                 gate_up_format=FMT[gate_up_format], w_down=_ptr(weights.w_down),
-                w_down_layout=weights.layout, w_down_scale=_ptr(weights.w_down_scale),
+                w_down_layout=weights.down_layout, w_down_scale=_ptr(weights.w_down_scale),
                 b_down=_ptr(weights.b_down), activation=ACT[activation], alpha=alpha, limit=limit,
                 gate_up_expert_scales=_ptr(gate_up_expert_scales),
                 down_expert_scales=_ptr(down_expert_scales),
@@ -362,8 +362,9 @@ def grouped_ffn_backward(offsets, max_rows: int, weights: "ExpertWeights", d_exp
     [max_rows, H], d_w_gate_up fp32 [L, 2D, H], d_w_down fp32 [L, H, D], and
     d_b_gate_up [L, 2D] / d_b_down [L, H] when bias_grads (default: when the
     weights have biases).  `grads` may hold preallocated outputs."""
-    if weights.operand != "bf16" or weights.w_gate_up_stacked is None:
-        raise ValueError("the backward runs on bf16 weights with their stacked views")
+    if weights.operand != "bf16":
+        raise ValueError("the backward runs on bf16 weights")
+    w_gu_oi, w_gu_st, w_d_st = weights.backward_views()
     dev = offsets.device
     L, H, D = weights.L, weights.H, weights.D
     if bias_grads is None:
@@ -381,8 +382,8 @@ def grouped_ffn_backward(offsets, max_rows: int, weights: "ExpertWeights", d_exp
     _dt(d_expert_out, torch.bfloat16, "d_expert_out")
     a = FfnBwdArgs(max_rows=max_rows, hidden_dim=H, moe_dim=D, n_local_experts=L, expert_offsets=_ptr(offsets),
                    x=_ptr(x), sorted_token=_ptr(sorted_token), x_perm=_ptr(x_perm),
-                   w_gate_up=_ptr(weights.w_gate_up), w_gate_up_stacked=_ptr(weights.w_gate_up_stacked),
-                   w_down_stacked=_ptr(weights.w_down_stacked), b_gate_up=_ptr(weights.b_gate_up),
+                   w_gate_up=_ptr(w_gu_oi), w_gate_up_stacked=_ptr(w_gu_st),
+                   w_down_stacked=_ptr(w_d_st), b_gate_up=_ptr(weights.b_gate_up),
                    gate_up_format=FMT[gate_up_format], activation=ACT[activation], alpha=alpha,
                    limit=limit, gate_up_expert_scales=_ptr(gate_up_expert_scales),
                    down_expert_scales=_ptr(down_expert_scales), d_expert_out=_ptr(d_expert_out),
@@ -438,8 +439,11 @@ def shared_indices(T: int, n_shared: int, device):
 class ExpertWeights:
     """Stacked expert weights as the library consumes them.
 
-    layout WEIGHT_OUT_IN: w_gate_up [L, 2D, H], w_down [L, H, D] (the
-    transposed views of the stacked [L, H, 2D] / [L, D, H] weights).
+    layout WEIGHT_IN_OUT: the StackedMoE page's stacked shapes themselves,
+    w_gate_up [L, H, 2D] and w_down [L, D, H] (bf16 reads them directly).
+    layout WEIGHT_OUT_IN: their transposed views, w_gate_up [L, 2D, H] and
+    w_down [L, H, D] (every operand type).  down_layout, when given, sets
+    the down GEMM's layout apart from the gate_up GEMM's.
     operand "mxfp4" (W4A8) / "mxfp4_a16" (W4A16): packed E2M1 w_gate_up
     [L, 2D, H/2], w_down [L, H, D/2] with E8M0 scales [L, 2D, H/32] /
     [L, H, D/32] (rows along K, OUT_IN).
@@ -455,16 +459,22 @@ class ExpertWeights:
     w_down_scale: torch.Tensor | None = None
     b_gate_up: torch.Tensor | None = None
     b_down: torch.Tensor | None = None
-    # bf16: the stacked [L, H, 2D] / [L, D, H] views, which the backward reads
-    w_gate_up_stacked: torch.Tensor | None = None
-    w_down_stacked: torch.Tensor | None = None
+    down_layout: int | None = None
+    # views the backward reads, made on first use: the gate_up weights in
+    # OUT_IN [L, 2D, H] and both weights in the stacked [L, H, 2D] / [L, D, H]
+    _bwd: dict | None = None
+
+    def __post_init__(self):
+        if self.down_layout is None:
+            self.down_layout = self.layout
 
     @staticmethod
     def from_stacked(w_gate_up, w_down, *, b_gate_up=None, b_down=None, w_gate_up_scale=None,
                      w_down_scale=None, operand="bf16", layout=WEIGHT_OUT_IN):
-        """Take stacked [L, H, 2D] / [L, D, H] weights and lay them out once,
-        at load time, in the layout the kernels read.  MXFP4 weights already
-        come as rows along K ([L, 2D, H/2] / [L, H, D/2]) and are kept."""
+        """Take stacked [L, H, 2D] / [L, D, H] weights.  IN_OUT keeps them as
+        they are; OUT_IN lays them out once, at load time, as their transposed
+        views (one copy: the stacked tensors are not kept).  MXFP4 weights
+        already come as rows along K ([L, 2D, H/2] / [L, H, D/2]) and are kept."""
         if operand in ("mxfp4", "mxfp4_a16"):
             if layout != WEIGHT_OUT_IN:
                 raise ValueError("MXFP4 weights are rows along the reduction dimension (OUT_IN)")
@@ -475,17 +485,40 @@ class ExpertWeights:
             return ExpertWeights(w_gate_up.contiguous(), w_down.contiguous(), L, 2 * Hh, D2 // 2, operand,
                                  layout, w_gate_up_scale.contiguous(), w_down_scale.contiguous(),
                                  b_gate_up, b_down)
+        if layout == WEIGHT_IN_OUT and operand != "bf16":
+            raise ValueError("only bf16 weights are read in the stacked (IN_OUT) layout")
         L, H, D2 = w_gate_up.shape
         D = D2 // 2
-        stacked = (w_gate_up.contiguous(), w_down.contiguous()) if operand == "bf16" else (None, None)
         if layout == WEIGHT_OUT_IN:
             w_gate_up = w_gate_up.transpose(1, 2).contiguous()
             w_down = w_down.transpose(1, 2).contiguous()
             if w_gate_up_scale is not None:
                 w_gate_up_scale = w_gate_up_scale.transpose(1, 2).contiguous()
                 w_down_scale = w_down_scale.transpose(1, 2).contiguous()
+        else:
+            w_gate_up, w_down = w_gate_up.contiguous(), w_down.contiguous()
         return ExpertWeights(w_gate_up, w_down, L, H, D, operand, layout, w_gate_up_scale,
-                             w_down_scale, b_gate_up, b_down, stacked[0], stacked[1])
+                             w_down_scale, b_gate_up, b_down)
+
+    def backward_views(self):
+        """(w_gate_up OUT_IN [L, 2D, H], w_gate_up stacked [L, H, 2D], w_down
+        stacked [L, D, H]): the weights as the backward reads them, the missing
+        ones transposed on the device on the first call and kept."""
+        if self.operand != "bf16":
+            raise ValueError("the backward runs on bf16 weights")
+        if self._bwd is None:
+            def tr(t):   # [L, R, C] -> [L, C, R]
+                if t.shape[1] % 64 == 0 and t.shape[2] % 64 == 0:
+                    return transpose_bf16(t)
+                return t.transpose(1, 2).contiguous()
+            gu_io = self.layout == WEIGHT_IN_OUT
+            d_io = self.down_layout == WEIGHT_IN_OUT
+            gu_oi = tr(self.w_gate_up) if gu_io else self.w_gate_up
+            gu_st = self.w_gate_up if gu_io else tr(self.w_gate_up)
+            d_st = self.w_down if d_io else tr(self.w_down)
+            self._bwd = {"w_gate_up": gu_oi, "w_gate_up_stacked": gu_st, "w_down_stacked": d_st}
+        b = self._bwd
+        return b["w_gate_up"], b["w_gate_up_stacked"], b["w_down_stacked"]
 
 
 class MoELayer:

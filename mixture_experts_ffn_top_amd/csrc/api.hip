@@ -399,10 +399,13 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
   REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 31) && (int64_t)R * D * 2 < ((int64_t)1 << 31) &&
               (int64_t)2 * D * H * 2 < ((int64_t)1 << 31),
           "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
-  if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: bf16 weights must use the OUT_IN layout for now");
+  if (a->w_gate_up_layout == MOE_WEIGHT_IN_OUT && a->gate_up_format != MOE_GATE_UP_CONCATENATED)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_grouped_ffn: IN_OUT gate_up weights take the concatenated format (use OUT_IN for interleaved)");
   if (R == 0) return ok();
   moe::FfnBf16Params p{};
+  p.gu_in_out = a->w_gate_up_layout == MOE_WEIGHT_IN_OUT;
+  p.d_in_out = a->w_down_layout == MOE_WEIGHT_IN_OUT;
   p.offsets = a->expert_offsets;
   p.L = L;
   p.H = H;

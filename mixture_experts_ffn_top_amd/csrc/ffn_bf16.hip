@@ -60,6 +60,10 @@ static constexpr int LDS_BYTES_TILES = (NSTAGE_A * A_ELEMS + NSTAGE_B * B_ELEMS)
 // Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
 static constexpr int BUF_DWORD3 = 0x00020000;
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16_t* lds_v4i16_ptr;
+
 struct GemmArgs {
   const int32_t* offsets;
   int L;
@@ -118,9 +122,17 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int MODE, int ACT, int FMT, bool GATHER, bool OUT_BF16>
+// B_IO: the weights in the StackedMoE page's stacked layout, each expert
+// [K, N_total] with the output columns contiguous (IN_OUT), instead of the
+// transposed [N, K] view (OUT_IN).  A weight stage is then 64 k-rows of the
+// tile's 256 columns (512 bytes each), whose 64-byte spans are XOR-swizzled
+// by (k-row & 7); the MFMA fragments (8 consecutive k of one column per lane)
+// are read with two transposing LDS reads (ds_read_b64_tr_b16) each.
+template <int MODE, int ACT, int FMT, bool GATHER, bool OUT_BF16, bool B_IO = false>
 __global__ __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void grouped_gemm_bf16_kernel(const GemmArgs p) {
+  static_assert(!B_IO || MODE == MODE_DOWN || (MODE == MODE_GATE_UP && FMT == FMT_CONCAT),
+                "stacked (IN_OUT) weights: the forward GEMMs, concatenated gate_up");
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* As = (uint16_t*)smem;
   uint16_t* Bs = As + NSTAGE_A * A_ELEMS;
@@ -294,6 +306,24 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   }
 #pragma unroll
   for (int i = 0; i < LPW_B; ++i) {
+    if constexpr (B_IO) {
+      // 1 KB = 2 k-rows of 32 chunks: lane l lands at k-row 2*blk + l/32,
+      // physical chunk l%32, and fetches the tile columns of logical chunk
+      // (l%32) ^ ((k-row & 7) << 2)
+      const int r = 2 * (wave * LPW_B + i) + (lane >> 5);
+      const int t = ((lane & 31) ^ ((r & 7) << 2)) * 8;  // first tile column of the chunk
+      int gcol;
+      if (MODE == MODE_DOWN) {
+        gcol = min(nb * BN + t, p.N - 8);
+      } else {
+        // concatenated: wave column q holds WTN/2 gate columns, then the matching up columns
+        const int q = t / WTN, rr = t % WTN, isup = rr / (WTN / 2), j = rr % (WTN / 2);
+        const int oc = min(nb * NBO + q * (WTN / 2) + j, p.N - 8);
+        gcol = isup ? p.N + oc : oc;
+      }
+      b_voff[i] = (uint32_t)r * b_row_bytes + (uint32_t)gcol * 2u;
+      continue;
+    }
     const int trow = (wave * LPW_B + i) * RPB + lrow;  // tile row
     int wrow;
     if (MODE == MODE_DOWN || MODE == MODE_WGRAD) {
@@ -334,6 +364,25 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   };
   auto issue_b = [&](int kt) {
     lptr_t dst = (lptr_t)(Bs + (kt % NSTAGE_B) * B_ELEMS + wave_s * LPW_B * 512);
+    if constexpr (B_IO) {
+      if (kt < KTF) {
+#pragma unroll
+        for (int i = 0; i < LPW_B; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16, b_voff[i],
+                                                   (uint32_t)kt * BK * b_row_bytes, 0, 0);
+      } else {
+        // the ragged last stage: k-rows past K read row K - 1 (finite weights
+        // under the zeroed A chunks)
+#pragma unroll
+        for (int i = 0; i < LPW_B; ++i) {
+          const uint32_t r = 2u * (uint32_t)(wave_s * LPW_B + i) + ((uint32_t)lane >> 5);
+          const uint32_t kr = (uint32_t)min(kt * BK + (int)r, K - 1);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)((char*)dst + i * 1024), 16,
+                                                   b_voff[i] - r * b_row_bytes + kr * b_row_bytes, 0, 0, 0);
+        }
+      }
+      return;
+    }
     if (kt < KTF) {
 #pragma unroll
       for (int i = 0; i < LPW_B; ++i)
@@ -384,8 +433,26 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     for (int mi = 0; mi < MI; ++mi)
       af[mi] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(as + swz(wm * WTM + mi * 32 + fr, kk * 2 + fk)));
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni)
-      bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(bs + swz(wn * WTN + ni * 32 + fr, kk * 2 + fk)));
+    for (int ni = 0; ni < NI; ++ni) {
+      if constexpr (B_IO) {
+        // lane l holds column l%32 of the block, k rows 8(l/32) .. +8: in
+        // each 16-lane group g, lane i addresses k-row 8(g>>1) + (i>>2) (and
+        // + 4) at columns 16(g&1) + 4(i&3) .. +4, and the transposing read
+        // hands it 4 consecutive k of column 16(g&1) + i
+        const int g = lane >> 4, i = lane & 15;
+        const int r0 = kk * 16 + 8 * (g >> 1) + (i >> 2);
+        const int col = wn * WTN + ni * 32 + 16 * (g & 1) + 4 * (i & 3);
+        auto at = [&](int r) {
+          return (lds_v4i16_ptr)(bs + r * BN + (((col >> 3) ^ ((r & 7) << 2)) << 3) + (col & 7));
+        };
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r0));
+        const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(at(r0 + 4));
+        const u32x2_t l2 = __builtin_bit_cast(u32x2_t, lo), h2 = __builtin_bit_cast(u32x2_t, hi);
+        bfr[ni] = __builtin_bit_cast(bf16x8_t, u32x4_t{l2[0], l2[1], h2[0], h2[1]});
+      } else {
+        bfr[ni] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(bs + swz(wn * WTN + ni * 32 + fr, kk * 2 + fk)));
+      }
+    }
   };
   // 32-row blocks of this wave that hold rows of the expert: the last m-block
   // of an expert is usually partly empty, and its empty blocks skip their
@@ -411,6 +478,9 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   // pipe; two waves per SIMD cover each other's barrier and wait stalls.
   // Iterations whose loads are all full stages run without branches.
   bf16x8_t fa[2][MI], fb[2][NI];
+  // LDS read instructions per k step: one per fragment, two per weight
+  // fragment read transposed
+  constexpr int NREADS = MI + (B_IO ? 2 : 1) * NI;
   auto iteration = [&](int kt, auto steady, auto full) {
     constexpr bool STEADY = decltype(steady)::value;
 #pragma unroll
@@ -422,7 +492,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < MI * NI; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-          if (j < MI + NI) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          if (j < NREADS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
         }
       } else {
         if (STEADY) {
@@ -436,7 +506,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
         if (STEADY || kt + 2 < KT) issue_a(kt + 2);
         if (STEADY || kt + 3 < KT) issue_b(kt + 3);
         mfmas(fa[c], fb[c], full);
-        __builtin_amdgcn_sched_group_barrier(0x100, MI + NI, 0);  // DS reads first
+        __builtin_amdgcn_sched_group_barrier(0x100, NREADS, 0);  // DS reads first
 #pragma unroll
         for (int j = 0; j < MI * NI; ++j) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -744,7 +814,11 @@ static hipError_t launch_gemm(KernelT kern, const GemmArgs& a, int max_rows, int
 }
 
 template <int ACT, int FMT, bool GATHER>
-static hipError_t gate_up_dispatch(const GemmArgs& a, int max_rows, hipStream_t st) {
+static hipError_t gate_up_dispatch(const GemmArgs& a, bool in_out, int max_rows, hipStream_t st) {
+  if constexpr (FMT == FMT_CONCAT) {
+    if (in_out)
+      return launch_gemm(grouped_gemm_bf16_kernel<MODE_GATE_UP, ACT, FMT, GATHER, true, true>, a, max_rows, BN / 2, st);
+  }
   return launch_gemm(grouped_gemm_bf16_kernel<MODE_GATE_UP, ACT, FMT, GATHER, true>, a, max_rows, BN / 2, st);
 }
 
@@ -779,15 +853,15 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
   g.out = q.act;
   g.ldo = q.D;
   g.lda = q.H;
-  g.ldb = q.H;
+  g.ldb = q.gu_in_out ? 2 * (int64_t)q.D : q.H;  // weight row pitch: [H, 2D] stacked or [2D, H]
   g.zero = q.split_counters;  // the down GEMM's arrival counters start at zero
   g.n_zero = q.split_counters ? SPLIT_COUNTERS : 0;
   const bool gather = (q.x_perm == nullptr);
   hipError_t err;
   if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
 #define GU(ACTV, FMTV)                                                                             \
-  err = gather ? gate_up_dispatch<ACTV, FMTV, true>(g, q.max_rows, st)                             \
-               : gate_up_dispatch<ACTV, FMTV, false>(g, q.max_rows, st)
+  err = gather ? gate_up_dispatch<ACTV, FMTV, true>(g, q.gu_in_out != 0, q.max_rows, st)          \
+               : gate_up_dispatch<ACTV, FMTV, false>(g, q.gu_in_out != 0, q.max_rows, st)
   if (q.fmt == FMT_CONCAT) {
     if (q.act_kind == ACT_SILU) GU(ACT_SILU, FMT_CONCAT);
     else if (q.act_kind == ACT_SWIGLUOAI) GU(ACT_SWIGLUOAI, FMT_CONCAT);
@@ -815,17 +889,23 @@ hipError_t launch_ffn_bf16(const FfnBf16Params& q, hipStream_t st) {
   d.out = q.out;
   d.ldo = q.H;
   d.lda = q.D;
-  d.ldb = q.D;
+  d.ldb = q.d_in_out ? q.H : q.D;  // weight row pitch: [D, H] stacked or [H, D]
   if (q.split_partial && q.split_slots > 0) {
     d.partial = q.split_partial;
     d.counters = q.split_counters;
     d.split_slots = q.split_slots < SPLIT_COUNTERS ? q.split_slots : SPLIT_COUNTERS;
     d.G = cu_count();
   }
-  if (q.out_bf16)
+  if (q.d_in_out) {
+    if (q.out_bf16)
+      err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, true, true>, d, q.max_rows, BN, st);
+    else
+      err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, false, true>, d, q.max_rows, BN, st);
+  } else if (q.out_bf16) {
     err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, true>, d, q.max_rows, BN, st);
-  else
+  } else {
     err = launch_gemm(grouped_gemm_bf16_kernel<MODE_DOWN, ACT_SILU, FMT_CONCAT, false, false>, d, q.max_rows, BN, st);
+  }
   if (err == hipSuccess && q.events) err = hipEventRecord(q.events[2], st);
   return err;
 }

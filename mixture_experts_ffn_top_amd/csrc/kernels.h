@@ -33,13 +33,14 @@ struct FfnBf16Params {
   const uint16_t* x_perm;        // or nullptr: gather from x through sorted_token
   const uint16_t* x;
   const int32_t* sorted_token;
-  const uint16_t* w_gate_up;     // OUT_IN [L, 2D, H]
+  const uint16_t* w_gate_up;     // OUT_IN [L, 2D, H], or IN_OUT [L, H, 2D] (gu_in_out)
   const uint16_t* b_gate_up;
-  const uint16_t* w_down;        // OUT_IN [L, H, D]
+  const uint16_t* w_down;        // OUT_IN [L, H, D], or IN_OUT [L, D, H] (d_in_out)
   const uint16_t* b_down;
   const float* gate_up_scales;
   const float* down_scales;
   int fmt, act_kind;
+  int gu_in_out, d_in_out;       // the stacked layouts (gate_up: concatenated format only)
   float alpha, limit;
   uint16_t* act;                 // [max_rows, D]
   void* out;                     // [max_rows, H]

@@ -143,6 +143,10 @@ def _ffn(**kw):
      m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(operand_dtype=4, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, w_down_layout=0),
      m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
+    # bf16 reads the stacked (IN_OUT) gate_up weights in the concatenated format only
+    (dict(w_gate_up_layout=0, gate_up_format=1, act_workspace_bytes=1 << 21), m.MOE_ERR_UNSUPPORTED, "concatenated"),
+    (dict(operand_dtype=1, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, w_gate_up_layout=0),
+     m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
 ])
 def test_grouped_ffn_validation(kw, status, frag):
     st, msg = _err(m.lib().moe_grouped_ffn, _ffn(**kw))

@@ -329,6 +329,68 @@ def test_layer_full_size(moe, cid, nsample):
     _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=cid)
 
 
+# ---------------------------------------------------------------- the stacked (IN_OUT) weight layout
+
+def _ffn_both_layouts(moe, cfg, inp, gather, gu_layout, d_layout):
+    """O of moe_grouped_ffn through the C ABI with the gate_up and down weights
+    in the given layouts, on the layer's own routing and bucketing."""
+    c = cfg
+    idx, w, _, _ = moe.route(router="softmax", k=c.k, E=c.E, x=inp["x"], w_gate=inp["w_gate"])
+    ind = moe.build_indices(idx, c.E, weights=w, x=None if gather else inp["x"])
+    wgu, wd = inp["w_gate_up"], inp["w_down"]     # stacked [E, H, 2D], [E, D, H]
+    ew = moe.ExpertWeights(wgu.contiguous() if gu_layout == moe.WEIGHT_IN_OUT else wgu.transpose(1, 2).contiguous(),
+                           wd.contiguous() if d_layout == moe.WEIGHT_IN_OUT else wd.transpose(1, 2).contiguous(),
+                           c.E, c.H, c.D, "bf16", gu_layout, b_gate_up=inp.get("b_gate_up"),
+                           b_down=inp.get("b_down"), down_layout=d_layout)
+    O_ = moe.grouped_ffn(ind["offsets"], c.T * c.k, ew, x_perm=ind.get("x_perm"),
+                         x=inp["x"] if gather else None, sorted_token=ind["sorted_token"] if gather else None,
+                         activation=c.activation, alpha=c.alpha, limit=c.limit, gate_up_format=c.gate_up_format)
+    y = moe.combine(O_, ind["row_of_slot"], c.T, c.k, weights=w)
+    torch.cuda.synchronize()
+    return {"O": O_, "y": y, "indices": idx, "weights": w, "index": ind}
+
+
+@pytest.mark.parametrize("cid,changes,gather", [
+    (1, {}, True),
+    (2, {"T": 256, "H": 1024, "D": 2048}, False),
+    (1, {"T": 100, "H": 1000, "D": 200}, True),        # ragged K in both GEMMs, N tails
+    (4, {"T": 300, "H": 296, "D": 72, "E": 3, "k": 2, "gate_up_format": "concatenated"}, False),  # bias, swigluoai
+    (4, {"T": 512, "E": 8, "k": 2, "gate_up_format": "concatenated"}, True),   # gpt-oss dims
+])
+def test_stacked_in_out_weights(moe, cid, changes, gather):
+    """The StackedMoE page's own weight shapes ([E, hidden, 2 moe_dim], [E,
+    moe_dim, hidden]) read directly by the bf16 GEMMs (transposing LDS
+    reads): the layer against the oracle, and the expert rows bit-identical
+    to those computed from the transposed (OUT_IN) views -- the MFMAs see
+    the same fragments in the same order -- for either GEMM's layout alone
+    and both together."""
+    cfg = synth.scaled(synth.get_config(cid), **changes)
+    inp = _gen(cfg)
+    say(f"[in_out] cfg={cid} {changes} gather={gather}")
+    IO, OI = moe.WEIGHT_IN_OUT, moe.WEIGHT_OUT_IN
+    ref = _ffn_both_layouts(moe, cfg, inp, gather, OI, OI)
+    n = int(host(ref["index"]["offsets"])[-1])
+    for gl, dl in ((IO, IO), (IO, OI), (OI, IO)):
+        res = _ffn_both_layouts(moe, cfg, inp, gather, gl, dl)
+        assert torch.equal(res["O"][:n], ref["O"][:n]), f"layouts gate_up={gl} down={dl}: O differs from OUT_IN"
+    _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+
+
+def test_stacked_in_out_weights_full_size(moe):
+    """The Mixtral-shape layer (T=4096, hidden 4096, 8 experts, top-2, moe_dim
+    14336) with IN_OUT weights: expert rows bit-identical to the OUT_IN run,
+    and sampled tokens against the oracle."""
+    cfg = synth.get_config(2)
+    inp = _gen(cfg)
+    say("[in_out full] Mixtral shape")
+    IO, OI = moe.WEIGHT_IN_OUT, moe.WEIGHT_OUT_IN
+    ref = _ffn_both_layouts(moe, cfg, inp, True, OI, OI)
+    res = _ffn_both_layouts(moe, cfg, inp, True, IO, IO)
+    n = int(host(ref["index"]["offsets"])[-1])
+    assert torch.equal(res["O"][:n], ref["O"][:n])
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 64, seed=12), BF16_TOL)
+
+
 @pytest.mark.parametrize("act,alpha,limit,fmt,bias", [
     ("silu", 0.0, 7.0, "concatenated", False),
     ("gelu_tanh", 0.0, 0.0, "concatenated", True),
