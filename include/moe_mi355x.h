@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -280,10 +280,16 @@ moe_status_t moe_build_indices_noalloc(const moe_index_args_t* args, void* strea
  *   x, sorted_token  bf16 [T, H], int32 [max_rows]   gather form; for fp8
  *                  x holds the per-token codes [T, H] and x_perm_scale the
  *                  per-token scales [T, H/128] (MOE_DTYPE_FP8_E4M3_TOKENS);
- *                  for MX the MOE_DTYPE_MXFP8_TOKENS codes and scales
- *                  (x_perm / x, the activation buffer and one expert's
- *                  weights must each be under 2 GiB: the GEMMs address
- *                  them with buffer loads of a 2 GiB range)
+ *                  for MX the MOE_DTYPE_MXFP8_TOKENS codes and scales.
+ *                  Size limits (the GEMMs address operands with buffer
+ *                  loads of a 2 GiB range): bf16 and fp8 address x_perm and
+ *                  the activation buffer from each tile's first row, so only
+ *                  x in the gather form and one expert's weights must be
+ *                  under 2 GiB; MX and moe_grouped_ffn_fused also need
+ *                  x_perm and the activation buffer under 2 GiB
+ *   num_tokens     host: rows of x in the gather form (T), used for its size
+ *                  bound; 0 = not given, then max_rows x hidden_dim is taken
+ *                  as x's size
  *   w_gate_up      bf16/e4m3: layout IN_OUT [L, H, 2D] (the [StackedMoE]
  *                  "Weight tensor shapes" themselves) or OUT_IN [L, 2D, H]
  *                  (its transposed view).  bf16 reads either layout
@@ -342,6 +348,7 @@ typedef struct moe_ffn_args {
   int32_t out_dtype;
   void* expert_out;
   void* const* timing_events;
+  int32_t num_tokens;
 } moe_ffn_args_t;
 
 moe_status_t moe_grouped_ffn(const moe_ffn_args_t* args, void* stream);

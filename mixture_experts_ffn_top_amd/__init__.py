@@ -63,7 +63,7 @@ class FfnArgs(ctypes.Structure):
                 ("activation", _i32), ("alpha", _f32), ("limit", _f32),
                 ("gate_up_expert_scales", _vp), ("down_expert_scales", _vp),
                 ("act_workspace", _vp), ("act_workspace_bytes", _i64), ("out_dtype", _i32),
-                ("expert_out", _vp), ("timing_events", _vp)]
+                ("expert_out", _vp), ("timing_events", _vp), ("num_tokens", _i32)]
 
 
 class CombineArgs(ctypes.Structure):
@@ -305,7 +305,8 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
                 act_workspace=_ptr(act_workspace), act_workspace_bytes=act_workspace.numel(),
                 out_dtype=DTYPE_BF16 if out_dtype == torch.bfloat16 else DTYPE_FP32,
                 expert_out=_ptr(out),
-                timing_events=ctypes.addressof(timing_events) if timing_events is not None else None)
+                timing_events=ctypes.addressof(timing_events) if timing_events is not None else None,
+                num_tokens=x.shape[0] if x is not None else 0)
     _check((lib().moe_grouped_ffn_fused if fused else lib().moe_grouped_ffn)(ctypes.byref(a), _stream(dev)))
     return out
 

@@ -252,6 +252,29 @@ moe_status_t moe_build_indices_noalloc(const moe_index_args_t* a, void* stream) 
 }
 
 // ---------------------------------------------------------------- grouped FFN
+}  // extern "C"
+
+namespace {
+
+// The gather form reads x [T, H] by token with 32-bit offsets from one base:
+// x must be under 2 GiB.  T is num_tokens when given; otherwise every one of
+// the max_rows rows is taken as a possible token (the bound before
+// num_tokens was part of the arguments).
+bool gather_rows_fit(const moe_ffn_args_t* a, int64_t elem_bytes) {
+  const int64_t rows = a->num_tokens > 0 ? a->num_tokens : a->max_rows;
+  return rows * a->hidden_dim * elem_bytes < ((int64_t)1 << 31);
+}
+
+const char* gather_bound_msg(const moe_ffn_args_t* a) {
+  return a->num_tokens > 0 ? "x (num_tokens x hidden_dim) must be under 2 GiB in the gather form"
+                           : "x must be under 2 GiB in the gather form; without num_tokens, max_rows x hidden_dim "
+                             "is taken as its size (pass num_tokens)";
+}
+
+}  // namespace
+
+extern "C" {
+
 int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t D, int32_t dtype) {
   if (max_rows < 0 || D < 1) return 0;
   if (dtype == MOE_DTYPE_FP8_E4M3_BLOCK128)
@@ -360,9 +383,11 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
             "moe_grouped_ffn: fp8 takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn: fp8 weights need w_gate_up_scale and w_down_scale");
-    REQUIRE((int64_t)R * H < ((int64_t)1 << 31) && (int64_t)R * D < ((int64_t)1 << 31) &&
-                (int64_t)2 * D * H < ((int64_t)1 << 31),
-            "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
+    // the GEMMs address permuted rows from each tile's first row and
+    // gathered rows from x by token: the bounds are x [T, H] (gather) and
+    // one expert's weights
+    REQUIRE(!gather || gather_rows_fit(a, 1), "moe_grouped_ffn: %s", gather_bound_msg(a));
+    REQUIRE((int64_t)2 * D * H < ((int64_t)1 << 31), "moe_grouped_ffn: one expert's weights must be under 2 GiB");
     if (a->gate_up_format != MOE_GATE_UP_CONCATENATED)
       return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path takes the concatenated gate_up format");
     if (a->b_gate_up != nullptr || a->b_down != nullptr)
@@ -395,10 +420,11 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.events = (hipEvent_t const*)a->timing_events;
     return hip_status(moe::launch_ffn_fp8(q, (hipStream_t)stream), "moe_grouped_ffn");
   }
-  // the GEMMs address rows with 32-bit byte offsets
-  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 31) && (int64_t)R * D * 2 < ((int64_t)1 << 31) &&
-              (int64_t)2 * D * H * 2 < ((int64_t)1 << 31),
-          "moe_grouped_ffn: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
+  // the GEMMs address permuted rows from each tile's first row and
+  // gathered rows from x by token: the bounds are x [T, H] (gather) and
+  // one expert's weights
+  REQUIRE(!gather || gather_rows_fit(a, 2), "moe_grouped_ffn: %s", gather_bound_msg(a));
+  REQUIRE((int64_t)2 * D * H * 2 < ((int64_t)1 << 31), "moe_grouped_ffn: one expert's weights must be under 2 GiB");
   if (a->w_gate_up_layout == MOE_WEIGHT_IN_OUT && a->gate_up_format != MOE_GATE_UP_CONCATENATED)
     return fail(MOE_ERR_UNSUPPORTED,
                 "moe_grouped_ffn: IN_OUT gate_up weights take the concatenated format (use OUT_IN for interleaved)");

@@ -273,7 +273,11 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * BM);
   row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
   K = p.K;
-  a_base = GATHER ? (const char*)p.X : (const char*)p.A;
+  // permuted rows: the buffer resource starts at the tile's first row (a
+  // 64-bit base), so the 32-bit offsets span one tile and the row buffer
+  // itself may exceed the 2 GiB a buffer resource addresses; gathered rows
+  // are addressed from x by token
+  a_base = GATHER ? (const char*)p.X : (const char*)p.A + (int64_t)row_beg * p.lda * 2;
   b_base = (const char*)(p.W + (int64_t)e * p.w_estride);
   __syncthreads();  // every wave has read the prefix before the loads overwrite it
   }
@@ -301,7 +305,9 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   for (int i = 0; i < LPW_A; ++i) {
     const int trow = (wave * LPW_A + i) * RPB + lrow;  // tile row
     const int r = min(row_beg + trow, row_end - 1);
-    const uint32_t arow = GATHER ? (uint32_t)p.sorted_token[r] : (uint32_t)r;
+    // row offset from the base: the token (gathered), the row within the
+    // tile (permuted rows, rebased), or the weight-gradient operand's row
+    const uint32_t arow = GATHER ? (uint32_t)p.sorted_token[r] : (uint32_t)(r - (MODE == MODE_WGRAD ? 0 : row_beg));
     a_voff[i] = arow * a_row_bytes + (uint32_t)a_chunk(i) * 16u;
   }
 #pragma unroll

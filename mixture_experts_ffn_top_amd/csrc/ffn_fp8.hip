@@ -181,7 +181,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   for (int i = 0; i < Q_LPW_A; ++i) {
     const int trow = (wave * Q_LPW_A + i) * 8 + lrow;
     const int r = min(row_beg + trow, row_end - 1);
-    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)r;
+    const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)(r - row_beg);
     a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16);
   }
 #pragma unroll
@@ -200,11 +200,17 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   }
   // activation scales: wave w fetches those of tile rows 32w .. 32w+31
   const int xs_r = min(row_beg + wave * 32 + (lane & 31), row_end - 1);
-  const uint32_t xs_row = p.gather ? (uint32_t)p.gather[xs_r] : (uint32_t)xs_r;
+  const uint32_t xs_row = p.gather ? (uint32_t)p.gather[xs_r] : (uint32_t)(xs_r - row_beg);
   const uint32_t xs_voff = xs_row * (uint32_t)KT * 4u;
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A, (short)0, 0x7fffffff, F8_BUF_DWORD3);
+  // permuted rows (and their scales): the buffer resources start at the
+  // tile's first row, so the row buffers may exceed 2 GiB; gathered rows are
+  // addressed from the per-token codes by token
+  const int64_t rb = p.gather ? 0 : (int64_t)row_beg;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A + rb * p.K), (short)0, 0x7fffffff, F8_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Wexp, (short)0, 0x7fffffff, F8_BUF_DWORD3);
-  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)p.A_scale, (short)0, 0x7fffffff, F8_BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t s_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.A_scale + rb * KT), (short)0, 0x7fffffff, F8_BUF_DWORD3);
 
   auto stage_base = [&](int kt) { return smem + (kt % Q_NSTAGE) * Q_STAGE_BYTES; };
   auto issue = [&](int kt) {

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
 
 
 def test_struct_layouts_match_header_sizes():
@@ -143,6 +143,12 @@ def _ffn(**kw):
      m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
     (dict(operand_dtype=4, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, w_down_layout=0),
      m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
+    # the gather form bounds x [num_tokens, hidden_dim] (or, without num_tokens, max_rows x hidden_dim)
+    (dict(x_perm=None, x=128, sorted_token=144, num_tokens=1 << 19, hidden_dim=4096, act_workspace_bytes=1 << 22),
+     m.MOE_ERR_INVALID_ARGUMENT,
+     "num_tokens x hidden_dim"),
+    (dict(x_perm=None, x=128, sorted_token=144, max_rows=1 << 19, hidden_dim=4096,
+          act_workspace_bytes=1 << 40), m.MOE_ERR_INVALID_ARGUMENT, "pass num_tokens"),
     # bf16 reads the stacked (IN_OUT) gate_up weights in the concatenated format only
     (dict(w_gate_up_layout=0, gate_up_format=1, act_workspace_bytes=1 << 21), m.MOE_ERR_UNSUPPORTED, "concatenated"),
     (dict(operand_dtype=1, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144, w_gate_up_layout=0),
