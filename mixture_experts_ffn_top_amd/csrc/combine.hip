@@ -1,8 +1,10 @@
 // Router-weighted combine: y[t] = sum_j w[t, j] * O[row_of_slot[t, j]]
 // + sum_i ws[t, i] * O_sh[i*T + t] (the shared experts, if any), fp32 sums in
-// ascending j then i, bf16 out; one wave per token, 8 columns per lane per
-// step, 16-byte loads and stores.  A gather with a fixed order, so the result
-// is deterministic.
+// ascending j then i, bf16 out.  One wave per (token, 512-column slice), 8
+// columns per lane, 16-byte loads and stores: a batch of a few thousand
+// tokens still puts tens of waves on every CU, enough loads in flight to
+// stream O from HBM.  A gather with a fixed order, so the result is
+// deterministic.
 #include "common.h"
 #include "kernels.h"
 
@@ -17,10 +19,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ O
                                                       int n_shared, const void* __restrict__ Osh,
                                                       const float* __restrict__ wsh) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int S = (H + 511) / 512;                        // column slices per token
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane((int)(gw / S));
   if (t >= T) return;
+  const int c = __builtin_amdgcn_readfirstlane((int)(gw % S)) * 512 + lane * 8;
   const bool valid = mask ? (mask[t] != 0) : true;
-  for (int c = lane * 8; c < H; c += 512) {
+  if (c < H) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
@@ -62,7 +67,9 @@ hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,
                           const void* O_shared, const float* w_shared, hipStream_t st) {
   if (T == 0) return hipSuccess;
-  dim3 grid((T + 3) / 4), block(256);
+  const int64_t waves = (int64_t)T * ((H + 511) / 512);
+  if ((waves + 3) / 4 > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((waves + 3) / 4)), block(256);
   if (o_bf16)
     combine_kernel<true><<<grid, block, 0, st>>>(O, row_of_slot, w, mask, T, k, H, y, n_shared, O_shared, w_shared);
   else
