@@ -170,6 +170,10 @@ PROFILE_CMDS = """# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp
 #   (the same with WRITE_SIZE into .../WRITE_SIZE)
 #   rocprofv3 --pmc FETCH_SIZE -f csv -d $REPO/gpurun_out/prof/copy_FETCH_SIZE -o copy -- \\
 #       python3 $REPO/bench.py --copy-calibration        (and WRITE_SIZE into .../copy_WRITE_SIZE)
+#   rocprofv3 --pmc SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS \
+#       SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --kernel-include-regex 'grouped_gemm' \
+#       -f csv -d $REPO/gpurun_out/prof/SQ2 -o bench -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline
+#   (the same with --cfg 5 into .../SQ5: the fp8 layer)
 #   python3 bench.py --summarize-profile gpurun_out/prof    (writes the files under profiles/)"""
 
 # the MX workloads' kernel traces, summarised by the same --summarize-profile call
@@ -295,7 +299,49 @@ def summarize_profile(d: str):
                    "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
                    "kernel_source_sha256_16": _src_hash(), "source": "profiles/mixtral_layer_hbm_traffic.txt"},
                   open(TRAFFIC_FILE, "w"), indent=1)
+    for sub, name, title in (
+            ("SQ2", "mixtral_gemm_pipe_counters.txt",
+             "bf16 grouped GEMMs of the Mixtral-shape layer (T=4096, hidden 4096, 8 experts, top-2, moe_dim 14336)"),
+            ("SQ5", "fp8_gemm_pipe_counters.txt",
+             "fp8 block-scaled grouped GEMMs (T=16384, hidden 7168, 256 experts, top-8, moe_dim 2048)")):
+        path = os.path.join(d, sub, "bench_counter_collection.csv")
+        if os.path.exists(path):
+            open(os.path.join(prof, name), "w").write(pipe_counter_summary(path, title, sub) + "\n")
     print(f"[bench] wrote the profile summaries under {prof}", file=sys.stderr)
+
+
+def pipe_counter_summary(path: str, title: str, sub: str) -> str:
+    """Matrix-pipe utilisation and instruction mix per GEMM kernel from one
+    rocprofv3 --pmc pass (SQ counters summed over the chip, GRBM_GUI_ACTIVE
+    summed over the 8 XCDs), averaged over the kernel's launches."""
+    import csv
+    per, dur = {}, {}
+    for r in csv.DictReader(open(path)):
+        k = _short(r["Kernel_Name"])
+        per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    n_simd = 256 * 4
+    cfg_flag = " --cfg 5" if sub == "SQ5" else ""
+    out = [f"# rocprofv3 counters: {title}",
+           "# command (repo root as $REPO, run from /tmp with TMPDIR=/tmp):",
+           "#   rocprofv3 --pmc SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_LDS \\",
+           "#       SQ_WAIT_ANY SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE --kernel-include-regex 'grouped_gemm' \\",
+           f"#       -f csv -d $REPO/gpurun_out/prof/{sub} -o bench -- python3 $REPO/bench.py{cfg_flag} --steps 3 --warmup 1 "
+           "--no-cpu-baseline",
+           "#   python3 bench.py --summarize-profile gpurun_out/prof",
+           "# clock = GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the kernel runs slower under the counters);",
+           "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (clock cycles x 1024 SIMDs); VALU counts include the MFMAs;",
+           "# waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (share of resident-wave time spent in s_waitcnt / barriers).", "",
+           f"{'kernel':50s}{'us':>8s}{'GHz':>6s}{'MFMA busy':>10s}{'VALU/MFMA':>10s}{'LDS/MFMA':>9s}"
+           f"{'waiting':>8s}{'LDS bank confl.':>16s}"]
+    for k in sorted(per):
+        c = {n: sum(v) / len(v) for n, v in per[k].items()}
+        t = sum(dur[k].values()) / len(dur[k])
+        cyc = c["GRBM_GUI_ACTIVE"] / 8
+        out.append(f"{k:50s}{t * 1e6:8.1f}{cyc / t / 1e9:6.2f}{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * n_simd):10.1%}"
+                   f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:10.2f}{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:9.2f}"
+                   f"{c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:8.1%}{c['SQ_LDS_BANK_CONFLICT']:16.3g}")
+    return "\n".join(out)
 
 
 def _cpu_model() -> str:

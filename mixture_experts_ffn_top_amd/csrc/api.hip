@@ -388,10 +388,7 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     // one expert's weights
     REQUIRE(!gather || gather_rows_fit(a, 1), "moe_grouped_ffn: %s", gather_bound_msg(a));
     REQUIRE((int64_t)2 * D * H < ((int64_t)1 << 31), "moe_grouped_ffn: one expert's weights must be under 2 GiB");
-    if (a->gate_up_format != MOE_GATE_UP_CONCATENATED)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path takes the concatenated gate_up format");
-    if (a->b_gate_up != nullptr || a->b_down != nullptr)
-      return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: the fp8 path has no bias");
+    REQUIRE(aligned16(a->b_gate_up) && aligned16(a->b_down), "moe_grouped_ffn: biases must be 16-byte aligned");
     if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
       return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn: fp8 weights must use the OUT_IN layout");
     if (R == 0) return ok();
@@ -410,6 +407,9 @@ moe_status_t moe_grouped_ffn(const moe_ffn_args_t* a, void* stream) {
     q.w_down_scale = (const float*)a->w_down_scale;
     q.gate_up_scales = a->gate_up_expert_scales;
     q.down_scales = a->down_expert_scales;
+    q.b_gate_up = (const uint16_t*)a->b_gate_up;
+    q.b_down = (const uint16_t*)a->b_down;
+    q.fmt = a->gate_up_format;
     q.act_kind = a->activation;
     q.alpha = a->alpha;
     q.limit = a->limit;

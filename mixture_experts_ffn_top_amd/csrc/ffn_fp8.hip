@@ -46,6 +46,7 @@ namespace moe {
 namespace {
 
 enum { F8_GATE_UP = 0, F8_DOWN = 1 };
+enum { F8_CONCAT = 0, F8_INTERLEAVED = 1 };  // gate_up column order (StackedMoE gate_up_format)
 
 constexpr int Q_BM = 256, Q_BN = 256, Q_BK = 128;        // BK in fp8 elements (= bytes)
 constexpr int Q_NSTAGE = 2;
@@ -104,6 +105,9 @@ struct Fp8GemmArgs {
   float alpha, limit;
   void* out;                 // gate_up: codes [rows, D]; down: bf16 / fp32 [rows, H]
   float* out_scale;          // gate_up: [rows, D/128]
+  const uint16_t* bias;      // bf16 per expert (gate_up [2D] in the column order of fmt, down [H]) or nullptr
+  int64_t bias_estride;
+  int fmt;                   // gate_up: F8_CONCAT or F8_INTERLEAVED
 };
 
 template <int MODE, int ACT, bool OUT_BF16>
@@ -194,7 +198,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       // B rows of wave column q: 32 gate rows, then the matching 32 up rows
       const int q = trow / Q_WTN, rr = trow % Q_WTN, isup = rr / (Q_WTN / 2), j = rr % (Q_WTN / 2);
       const int oc = min(nb * NBO + q * (Q_WTN / 2) + j, p.N - 1);
-      wrow = isup ? p.N + oc : oc;
+      wrow = (p.fmt == F8_CONCAT) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
     }
     b_voff[i] = (uint32_t)wrow * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16);
   }
@@ -268,7 +272,10 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
   for (int ni = 0; ni < Q_NI; ++ni) {
     if (MODE == F8_DOWN) ws_blk[ni] = min((nb * Q_BN + wn_s * Q_WTN) / 128, p.N / 128 - 1);
-    else ws_blk[ni] = (ni == 0) ? nb : (p.N / 128 + nb);
+    else if (p.fmt == F8_CONCAT) ws_blk[ni] = (ni == 0) ? nb : (p.N / 128 + nb);
+    // interleaved: output oc's gate and up rows are 2 oc and 2 oc + 1, so the
+    // tile's first 64 outputs sit in weight-row block 2 nb, the next 64 in 2 nb + 1
+    else ws_blk[ni] = 2 * nb + (wn_s >= Q_WAVES_N / 2 ? 1 : 0);
   }
   // read through the scalar cache: uniform per wave, and a vector load here
   // would make its wait drain the loads into LDS still in flight
@@ -354,10 +361,35 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   // ---- epilogue.  acc[mi][ni][4q + c] is C[row][col] in units unit[mi][ni] with
   //   row = wm*128 + mi*32 + fr,  col = wn*64 + ni*32 + 8q + 4fk + c
   const float sc = p.escale ? p.escale[e] : 1.0f;
+  const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
   if (MODE == F8_GATE_UP) {
     // block 0 holds gate columns, block 1 the up columns of the same 32
     // outputs; the 128 outputs of a row (one re-quantisation block) are spread
-    // over the four wave columns, whose row maxima meet in LDS
+    // over the four wave columns, whose row maxima meet in LDS.  The biases
+    // of this lane's 16 outputs (gate and up), in the column order of fmt:
+    float bg[16], bu[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fk;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bg[4 * q + c] = bu[4 * q + c] = 0.0f;
+      if (bias_e && oc < p.N) {
+        if (p.fmt == F8_CONCAT) {
+          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
+          bg[4 * q + 0] = bf16_to_f32(g2.x & 0xffffu); bg[4 * q + 1] = bf16_to_f32(g2.x >> 16);
+          bg[4 * q + 2] = bf16_to_f32(g2.y & 0xffffu); bg[4 * q + 3] = bf16_to_f32(g2.y >> 16);
+          bu[4 * q + 0] = bf16_to_f32(u2.x & 0xffffu); bu[4 * q + 1] = bf16_to_f32(u2.x >> 16);
+          bu[4 * q + 2] = bf16_to_f32(u2.y & 0xffffu); bu[4 * q + 3] = bf16_to_f32(u2.y >> 16);
+        } else {
+          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);   // gate, up of 4 outputs
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            bg[4 * q + c] = bf16_to_f32(b4[c] & 0xffffu);
+            bu[4 * q + c] = bf16_to_f32(b4[c] >> 16);
+          }
+        }
+      }
+    }
     float a[Q_MI][16];
     float amax[Q_MI];
 #pragma unroll
@@ -366,7 +398,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       float m = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        a[mi][r] = gated_act<ACT>(acc[mi][0][r] * ug, acc[mi][1][r] * uu, p.alpha, p.limit);
+        a[mi][r] = gated_act<ACT>(acc[mi][0][r] * ug + bg[r], acc[mi][1][r] * uu + bu[r], p.alpha, p.limit);
         m = fmaxf(m, fabsf(a[mi][r]));
       }
       amax[mi] = fmaxf(m, __shfl_xor(m, 32, MOE_WAVE));
@@ -412,6 +444,13 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
           float v[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * u;
+          if (bias_e) {
+            const uint2 b2 = *(const uint2*)(bias_e + n);
+            v[0] += bf16_to_f32(b2.x & 0xffffu);
+            v[1] += bf16_to_f32(b2.x >> 16);
+            v[2] += bf16_to_f32(b2.y & 0xffffu);
+            v[3] += bf16_to_f32(b2.y >> 16);
+          }
           if (OUT_BF16) {
             uint2 w;
             w.x = pack_bf16x2_rne(v[0], v[1]);
@@ -464,6 +503,9 @@ hipError_t launch_ffn_fp8(const FfnFp8Params& q, hipStream_t st) {
   g.limit = q.limit;
   g.out = q.act;
   g.out_scale = q.act_scale;
+  g.bias = q.b_gate_up;
+  g.bias_estride = 2 * (int64_t)q.D;
+  g.fmt = q.fmt;
   if (q.act_kind == ACT_SILU)
     err = launch_fp8(grouped_gemm_fp8_kernel<F8_GATE_UP, ACT_SILU, false>, g, q.max_rows, Q_BN / 2, st);
   else if (q.act_kind == ACT_SWIGLUOAI)
@@ -485,6 +527,8 @@ hipError_t launch_ffn_fp8(const FfnFp8Params& q, hipStream_t st) {
   d.ws_estride = (int64_t)(q.H / 128) * (q.D / 128);
   d.escale = q.down_scales;
   d.out = q.out;
+  d.bias = q.b_down;
+  d.bias_estride = q.H;
   if (q.out_bf16)
     err = launch_fp8(grouped_gemm_fp8_kernel<F8_DOWN, ACT_SILU, true>, d, q.max_rows, Q_BN, st);
   else

@@ -151,6 +151,9 @@ struct FfnFp8Params {
   const float* w_down_scale;     // [L, H/128, D/128]
   const float* gate_up_scales;
   const float* down_scales;
+  const uint16_t* b_gate_up;     // bf16 [L, 2D] (column order of fmt) or nullptr
+  const uint16_t* b_down;        // bf16 [L, H] or nullptr
+  int fmt;                       // 0 concatenated, 1 interleaved gate_up columns
   int act_kind;
   float alpha, limit;
   uint8_t* act;                  // e4m3 codes [max_rows, D]

@@ -121,11 +121,22 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
         out["b_gate_up"] = _normal((E, 2 * D), cfg.w_std, d, c, 5, 0, salt).to(torch.bfloat16)
         out["b_down"] = _normal((E, H), cfg.w_std, d, c, 6, 0, salt).to(torch.bfloat16)
     if cfg.n_shared:
-        assert cfg.operand_dtype in ("bf16", "fp8"), "shared experts are bf16 or fp8"
         # shared experts: the same gated MLP with moe_dim = shared_dim, in the
-        # layer's operand dtype (tensor ids 7..10, one stream per shared expert)
+        # layer's operand dtype (tensor ids 7..10, one stream per shared expert;
+        # MX scale streams 13 and 14)
         S, Ds = cfg.n_shared, cfg.shared_dim
-        if cfg.operand_dtype == "bf16":
+        if cfg.operand_dtype in ("mxfp4", "mxfp4_a16"):
+            assert Ds % 32 == 0
+            sgu = torch.empty((S, 2 * Ds, H // 2), device=d, dtype=torch.uint8)
+            sgus = torch.empty((S, 2 * Ds, H // 32), device=d, dtype=torch.uint8)
+            sd = torch.empty((S, H, Ds // 2), device=d, dtype=torch.uint8)
+            sds = torch.empty((S, H, Ds // 32), device=d, dtype=torch.uint8)
+            for i in range(S):
+                sgu[i], sgus[i] = _mxfp4(2 * Ds, H, d, c, 7, 13, i, salt)
+                sd[i], sds[i] = _mxfp4(H, Ds, d, c, 8, 14, i, salt)
+            out["w_gate_up_shared"], out["w_gate_up_shared_scale"] = sgu, sgus
+            out["w_down_shared"], out["w_down_shared_scale"] = sd, sds
+        elif cfg.operand_dtype == "bf16":
             sgu = torch.empty((S, H, 2 * Ds), device=d, dtype=torch.bfloat16)
             sd = torch.empty((S, Ds, H), device=d, dtype=torch.bfloat16)
             for i in range(S):

@@ -605,21 +605,29 @@ def test_shared_indices(moe):
     (1, {"T": 200, "n_shared": 3, "shared_dim": 136}, 200),                   # several, ragged dims
     (4, {"T": 300, "H": 512, "D": 384, "E": 6, "k": 2, "n_shared": 2, "shared_dim": 256}, 300),  # bias, interleaved
     (3, {"T": 700, "E": 32, "D": 256, "shared_dim": 512}, 700),               # sink-gated, two lanes
+    # MXFP4 experts: W4A8 (per-token MXFP8 activations) and W4A16, sink-gated shared experts
+    (6, {"T": 300, "E": 8, "k": 2, "s": 2, "n_shared": 2, "H": 512, "D": 256, "shared_dim": 384}, 300),
+    (7, {"T": 64, "E": 16, "k": 2, "s": 2, "n_shared": 2, "H": 1024, "D": 512, "shared_dim": 256}, 64),
+    # fp8 experts with one always-on-style sink-gated shared expert, bias, interleaved gate/up
+    (5, {"T": 256, "E": 8, "k": 3, "s": 1, "n_shared": 1, "H": 512, "D": 256, "shared_dim": 384,
+         "has_bias": True, "gate_up_format": "interleaved", "activation": "swigluoai", "alpha": 1.702,
+         "limit": 7.0}, 256),
 ])
 def test_layer_with_shared_experts(moe, cid, changes, nsample):
     cfg = synth.scaled(synth.get_config(cid), **changes)
     inp = _gen(cfg)
     say(f"[shared] cfg={cid} {changes}")
+    tol = FP8_TOL if cfg.operand_dtype in ("fp8", "mxfp4") else BF16_TOL
     _, res = _run_layer(moe, cfg, inp)
     _check_routing(cfg, inp, res)
-    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample), BF16_TOL)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample), tol)
     # masked tokens give zero rows, shared experts included
     mask = torch.ones(cfg.T, dtype=torch.uint8, device=DEV)
     mask[::7] = 0
     _, res_m = _run_layer(moe, cfg, inp, token_mask=mask)
     ym = host(res_m["y"])
     assert np.all(ym[host(mask) == 0] == 0)
-    _check_layer(cfg, inp, res_m, sample_tokens(cfg.T, nsample), BF16_TOL, token_mask=host(mask))
+    _check_layer(cfg, inp, res_m, sample_tokens(cfg.T, nsample), tol, token_mask=host(mask))
 
 
 def test_abi_errors_on_gpu_path(moe):
@@ -702,7 +710,10 @@ def _check_fp8_act(cfg, inp, res, layer):
             continue
         wgu = O.dequant_weight_block128(hin["w_gate_up"][e], hin["w_gate_up_scale"][e])
         h = xq[st[rows]] @ wgu
-        a = O.gated_activation(h[:, :D], h[:, D:], cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
+        if cfg.has_bias:
+            h = h + hin["b_gate_up"][e].astype(np.float64)[None, :]
+        gg, uu = O.split_gate_up(h, cfg.gate_up_format)
+        a = O.gated_activation(gg, uu, cfg.activation, cfg.alpha, cfg.limit).astype(np.float32)
         cg, sg = _gpu_act_rows(layer, "fp8", D, rows)
         s_, t_, w_ = _act_code_stats("fp8", cg, sg, a)
         same, total, worst = same + s_, total + t_, max(worst, w_)
@@ -722,6 +733,26 @@ def test_fp8_layer_small(moe, changes, nsample, gather):
     _check_routing(cfg, inp, res)
     _check_fp8_act(cfg, inp, res, layer)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=3), FP8_TOL)
+
+
+@pytest.mark.parametrize("changes,gather", [
+    # gpt-oss style: interleaved gate/up, swigluoai with its clamps, biases
+    ({"T": 400, "E": 6, "k": 2, "H": 512, "D": 384, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, True),
+    ({"T": 300, "E": 5, "k": 4, "H": 384, "D": 640, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True, "x_std": 4.0}, False),
+    ({"T": 256, "E": 4, "k": 2, "H": 256, "D": 256, "activation": "gelu_tanh", "has_bias": True}, True),
+    ({"T": 1024, "E": 16, "k": 4, "H": 2048, "D": 1024, "gate_up_format": "interleaved"}, True),
+])
+def test_fp8_layer_bias_and_interleaved(moe, changes, gather):
+    """The fp8 block-scaled layer with biases and with the interleaved
+    gate/up column order (the gpt-oss configuration run in fp8)."""
+    cfg = synth.scaled(synth.get_config(5), **changes)
+    inp = _gen(cfg)
+    say(f"[fp8 bias/interleaved] {changes} gather={gather}")
+    layer, res = _run_layer(moe, cfg, inp, gather=gather)
+    _check_fp8_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
 
 
 def test_fp8_zero_scales(moe):
