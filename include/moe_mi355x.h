@@ -119,7 +119,12 @@ enum { MOE_WEIGHT_IN_OUT = 0, MOE_WEIGHT_OUT_IN = 1 };
  *   hidden_dim H                       host, softmax x-form only: a multiple
  *                                      of 8 in [8, 4194304]
  *   x          bf16 [T, H]             softmax x-form (logits == NULL), E <= 128
- *   w_gate     bf16 [E, H]             gate linear layer (out, in)
+ *   w_gate     bf16 [E, H], or float32 [E, H] with router_dtype FP32: the
+ *              gate linear layer (out, in)
+ *   router_dtype host, x-form: MOE_DTYPE_BF16 (0, the default: bf16 gate) or
+ *              MOE_DTYPE_FP32 ([StackedMoE] router_dtype float32: the gate is
+ *              built in float32 and x is cast to float32, which is exact);
+ *              ignored when logits are given
  *   logits     fp32 [T, logits_ld], logits_ld >= E + s; routed experts then
  *              sink lanes; a wider row's tail is not read
  *   logits_out fp32 [T, E] or NULL     softmax x-form: the computed logits
@@ -150,6 +155,7 @@ typedef struct moe_route_args {
   int32_t* expert_indices;
   float* expert_weights;
   float* sink_weights;
+  int32_t router_dtype;
 } moe_route_args_t;
 
 moe_status_t moe_route(const moe_route_args_t* args, void* stream);

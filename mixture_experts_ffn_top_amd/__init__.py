@@ -41,7 +41,7 @@ class RouteArgs(ctypes.Structure):
                 ("x", _vp), ("w_gate", _vp), ("logits", _vp), ("logits_ld", _i64),
                 ("logits_out", _vp), ("expert_bias", _vp), ("global_scale", _vp),
                 ("route_scale", _f32), ("renormalize", _i32), ("expert_indices", _vp),
-                ("expert_weights", _vp), ("sink_weights", _vp)]
+                ("expert_weights", _vp), ("sink_weights", _vp), ("router_dtype", _i32)]
 
 
 class IndexArgs(ctypes.Structure):
@@ -189,7 +189,10 @@ def route(*, router: str, k: int, E: int, s: int = 0, x=None, w_gate=None, logit
     sw = torch.empty((T, s), dtype=torch.float32, device=dev) if s > 0 else None
     lo = torch.empty((T, E), dtype=torch.float32, device=dev) if (return_logits and logits is None) else None
     _dt(x, torch.bfloat16, "x")
-    _dt(w_gate, torch.bfloat16, "w_gate")
+    # the gate in bf16, or float32 (router_dtype float32)
+    w32 = w_gate is not None and w_gate.dtype == torch.float32
+    if not w32:
+        _dt(w_gate, torch.bfloat16, "w_gate")
     _dt(logits, torch.float32, "logits")
     _dt(expert_bias, torch.float32, "expert_bias")
     _dt(global_scale, torch.float32, "global_scale")
@@ -200,7 +203,8 @@ def route(*, router: str, k: int, E: int, s: int = 0, x=None, w_gate=None, logit
                   logits_ld=logits.stride(0) if logits is not None else 0,
                   logits_out=_ptr(lo), expert_bias=_ptr(expert_bias), global_scale=_ptr(global_scale),
                   route_scale=route_scale, renormalize=int(renormalize),
-                  expert_indices=_ptr(idx), expert_weights=_ptr(w), sink_weights=_ptr(sw))
+                  expert_indices=_ptr(idx), expert_weights=_ptr(w), sink_weights=_ptr(sw),
+                  router_dtype=DTYPE_FP32 if w32 else DTYPE_BF16)
     _check(lib().moe_route(ctypes.byref(a), _stream(dev)))
     return idx, w, sw, lo
 

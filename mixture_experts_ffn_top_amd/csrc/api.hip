@@ -86,8 +86,11 @@ moe_status_t moe_route(const moe_route_args_t* a, void* stream) {
       REQUIRE(a->hidden_dim >= 8 && a->hidden_dim % 8 == 0 && a->hidden_dim <= (1 << 22),
               "moe_route: hidden_dim must be a multiple of 8 in [8, 4194304] (got %d)", a->hidden_dim);
       REQUIRE(aligned16(a->x) && aligned16(a->w_gate), "moe_route: x and w_gate must be 16-byte aligned");
+      REQUIRE(a->router_dtype == MOE_DTYPE_BF16 || a->router_dtype == MOE_DTYPE_FP32,
+              "moe_route: router_dtype must be BF16 or FP32 (got %d)", a->router_dtype);
       return hip_status(moe::launch_router_softmax_x(
-                            (const uint16_t*)a->x, (const uint16_t*)a->w_gate, T, a->hidden_dim, E, k,
+                            (const uint16_t*)a->x, a->w_gate, a->router_dtype == MOE_DTYPE_FP32, T,
+                            a->hidden_dim, E, k,
                             a->route_scale, a->global_scale, a->renormalize, a->logits_out,
                             a->expert_indices, a->expert_weights, st),
                         "moe_route");

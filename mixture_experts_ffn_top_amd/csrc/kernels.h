@@ -10,7 +10,8 @@ namespace moe {
 hipError_t launch_router_softmax_logits(const float* logits, int64_t ld, int T, int E, int k,
                                         float scale, const float* gs, int renorm, int32_t* idx,
                                         float* w, hipStream_t st);
-hipError_t launch_router_softmax_x(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
+// wg: bf16 [E, H], or float32 [E, H] when w32 (the float32 gate)
+hipError_t launch_router_softmax_x(const uint16_t* x, const void* wg, int w32, int T, int H, int E,
                                    int k, float scale, const float* gs, int renorm,
                                    float* logits_out, int32_t* idx, float* w, hipStream_t st);
 hipError_t launch_router_sigmoid_sink(const float* logits, int64_t ld, const float* bias, int T,

@@ -97,56 +97,69 @@ __global__ __launch_bounds__(256) void router_softmax_logits_kernel(
 // A workgroup owns 16 tokens.  logits^T[e][t] = sum_h W[e][h] x[t][h] runs on
 // v_mfma_f32_16x16x32_bf16 with W as the A operand (16 experts per tile) and
 // x as the B operand (16 tokens).  The hidden dimension is streamed in chunks
-// of RX_CC columns: the 16 token rows and the padded expert rows of a chunk
-// go straight from HBM/L2 into LDS with buffer loads (no VGPRs, one 1 KB
-// coalesced piece per instruction), NS chunks deep, so that many loads
-// are in flight per CU; the kernel is bound by reading x once.  Inside a
-// chunk wave w takes the 32-column k steps w, w+4, ...; the four partial
-// sums meet in LDS, then each wave runs the top-k of 4 tokens.
+// of CC columns: the 16 token rows and the padded expert rows of a chunk go
+// straight from HBM/L2 into LDS with buffer loads (no VGPRs, one 1 KB
+// coalesced piece per instruction), NS chunks deep, so that many loads are
+// in flight per CU; the kernel is bound by reading x once.  Inside a chunk
+// wave w takes the 32-column k steps w, w+4, ...; the four partial sums meet
+// in LDS, then each wave runs the top-k of 4 tokens.
 //
-// LDS row of a chunk: 32 pieces of 16 bytes.  Piece p of row r sits at slot
+// W32: the gate in float32 (StackedMoE page, router_dtype float32: the gate
+// is built in float32 and its bf16 input cast to float32, which is exact).
+// The expert rows of a chunk are then float32, the chunk 128 columns wide,
+// and each 32-column k step runs as eight v_mfma_f32_16x16x4_f32: in MFMA m,
+// lane group g supplies column 8g + m of the step (the same permutation of k
+// for both operands), so each lane's 8 values stay contiguous in LDS.
+//
+// LDS row of a chunk: 16-byte pieces; piece p of row r sits at slot
 // p ^ (r & 15): the 16 lanes of a fragment read (16 rows, one piece) then hit
 // 16 different 16-byte bank groups.
-static constexpr int RX_CC = 256;                 // columns per chunk
-static constexpr int RX_ROWB = RX_CC * 2;         // bytes of one row of a chunk
 static constexpr int RX_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
 
-template <int ETILES>
+template <int ETILES, bool W32>
 struct RxShape {
   static constexpr int EP = ETILES * 16;
-  static constexpr int STAGE = (16 + EP) * RX_ROWB;                  // bytes per chunk
+  static constexpr int CC = W32 ? 128 : 256;                        // columns per chunk
+  static constexpr int XRB = CC * 2;                                // bytes of a token row of a chunk
+  static constexpr int WRB = CC * (W32 ? 4 : 2);                    // bytes of an expert row of a chunk
+  static constexpr int XBLK = 16 * XRB / 1024;                      // 1 KB blocks of token rows
+  static constexpr int STAGE = 16 * XRB + EP * WRB;                 // bytes per chunk
   // chunks in the pipeline: for E <= 32 few enough (<= 72 KB of LDS) that two
   // workgroups share a CU, so that at large T one's ramp and top-k overlap
   // the other's stream (at T = 32768, E = 8: 94 us against 110 with 8 chunks)
   static constexpr int NS = ETILES == 1 ? 4 : ETILES == 2 ? 3 : ETILES == 4 ? 3 : 2;
-  static constexpr int LPW = (16 + EP) * RX_ROWB / 1024 / 4;         // 1 KB loads per wave per chunk
-  static constexpr int PART = 4 * 16 * (EP + 1) * 4;                 // partial-sum exchange
+  static constexpr int LPW = STAGE / 1024 / 4;                      // 1 KB loads per wave per chunk
+  static constexpr int PART = 4 * 16 * (EP + 1) * 4;                // partial-sum exchange
   static constexpr int LDS = NS * STAGE > PART ? NS * STAGE : PART;
+  static_assert(STAGE % 4096 == 0, "a chunk is a whole number of 1 KB loads per wave");
 };
 
 // This wave's LPW loads of chunk c into the stage at `st`: 1 KB block
-// g = wave * LPW + l, x rows for g < 8, expert rows after.
-template <int LPW>
+// g = wave * LPW + l, token rows for g < XBLK, expert rows after.
+template <int ETILES, bool W32, int LPW>
 __device__ __forceinline__ void rx_issue(char* st, int c, int wave, const uint32_t (&voff)[LPW],
                                          __amdgpu_buffer_rsrc_t x_rsrc, __amdgpu_buffer_rsrc_t w_rsrc) {
+  using S = RxShape<ETILES, W32>;
 #pragma unroll
   for (int l = 0; l < LPW; ++l) {
     const int g = wave * LPW + l;
-    if (g < 8)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * RX_ROWB, 0, 0);
+    if (g < S::XBLK)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * S::XRB, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * RX_ROWB, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + g * 1024), 16, voff[l], c * S::WRB, 0, 0);
   }
 }
 
-template <int ETILES, int J>
+template <int ETILES, int J, bool W32>
 __global__ __launch_bounds__(256) void router_softmax_x_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg, int T, int H, int E, int k,
+    const uint16_t* __restrict__ x, const void* __restrict__ wg, int T, int H, int E, int k,
     float scale, const float* __restrict__ global_scale, int renorm, float* __restrict__ logits_out,
     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  constexpr int EP = RxShape<ETILES>::EP, NS = RxShape<ETILES>::NS, LPW = RxShape<ETILES>::LPW;
-  constexpr int STAGE = RxShape<ETILES>::STAGE;
-  __shared__ __attribute__((aligned(1024))) char smem[RxShape<ETILES>::LDS];
+  using S = RxShape<ETILES, W32>;
+  constexpr int EP = S::EP, NS = S::NS, LPW = S::LPW, STAGE = S::STAGE, CC = S::CC;
+  constexpr int XRB = S::XRB, WRB = S::WRB, XBLK = S::XBLK;
+  constexpr int WEB = W32 ? 4 : 2;  // bytes per gate element
+  __shared__ __attribute__((aligned(1024))) char smem[S::LDS];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t0 = blockIdx.x * 16;
@@ -155,24 +168,32 @@ __global__ __launch_bounds__(256) void router_softmax_x_kernel(
   const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(x + (int64_t)t0 * H), (short)0, nrows * H * 2, RX_BUF_DWORD3);
   const __amdgpu_buffer_rsrc_t w_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, E * H * 2, RX_BUF_DWORD3);
-  // Load l of this wave moves 1 KB block g = wave * LPW + l of a chunk: two
-  // rows (x rows for g < 8, then expert rows), lane -> (row, slot).  Rows
-  // past the token or expert count read zeros (buffer bounds).
+      __builtin_amdgcn_make_buffer_rsrc((void*)wg, (short)0, E * H * WEB, RX_BUF_DWORD3);
+  // Load l of this wave moves 1 KB block g = wave * LPW + l of a chunk: token
+  // rows for g < XBLK (XRB bytes each), then expert rows (WRB bytes each);
+  // lane -> (row, slot).  Rows past the token or expert count read zeros
+  // (buffer bounds).
   uint32_t voff[LPW];
 #pragma unroll
   for (int l = 0; l < LPW; ++l) {
     const int g = wave * LPW + l;
-    const int row = 2 * g + (lane >> 5);           // stage row: 0..15 x, then experts
-    const int piece = (lane & 31) ^ (row & 15);
-    const int r = g < 8 ? row : row - 16;
-    voff[l] = (uint32_t)r * (uint32_t)H * 2u + (uint32_t)piece * 16u;
+    if (g < XBLK) {
+      constexpr int PPR = XRB / 16;                // pieces per token row
+      const int row = g * (1024 / XRB) + lane / PPR;
+      const int piece = (lane % PPR) ^ (row & 15);
+      voff[l] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)piece * 16u;
+    } else {
+      constexpr int PPR = WRB / 16;                // pieces per expert row
+      const int row = (g - XBLK) * (1024 / WRB) + lane / PPR;
+      const int piece = (lane % PPR) ^ (row & 15);
+      voff[l] = (uint32_t)row * (uint32_t)H * (uint32_t)WEB + (uint32_t)piece * 16u;
+    }
   }
-  const int nchunk = (H + RX_CC - 1) / RX_CC;
+  const int nchunk = (H + CC - 1) / CC;
 
 #pragma unroll
   for (int c = 0; c < NS - 1; ++c)
-    if (c < nchunk) rx_issue<LPW>(smem + (c % NS) * STAGE, c, wave, voff, x_rsrc, w_rsrc);
+    if (c < nchunk) rx_issue<ETILES, W32, LPW>(smem + (c % NS) * STAGE, c, wave, voff, x_rsrc, w_rsrc);
   f32x4_t acc[ETILES];
 #pragma unroll
   for (int i = 0; i < ETILES; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -184,27 +205,50 @@ __global__ __launch_bounds__(256) void router_softmax_x_kernel(
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the buffer of chunk c-1 is free: every wave has passed the barrier
     if (c + NS - 1 < nchunk)
-      rx_issue<LPW>(smem + ((c + NS - 1) % NS) * STAGE, c + NS - 1, wave, voff, x_rsrc, w_rsrc);
+      rx_issue<ETILES, W32, LPW>(smem + ((c + NS - 1) % NS) * STAGE, c + NS - 1, wave, voff, x_rsrc, w_rsrc);
     const char* st = smem + (c % NS) * STAGE;
-    const int cols_left = H - c * RX_CC;
+    const char* sw = st + 16 * XRB;                 // the expert rows of the chunk
+    const int cols_left = H - c * CC;
 #pragma unroll
-    for (int jj = 0; jj < RX_CC / 128; ++jj) {
-      const int p = 4 * (wave + 4 * jj) + grp;     // 32-column k step wave + 4*jj                    // piece of this lane's 8 columns
-      const int slot = (p ^ col) * 16;
-      u32x4_t bv = *(const u32x4_t*)(st + col * RX_ROWB + slot);
-      u32x4_t av[ETILES];
+    for (int jj = 0; jj < CC / 128; ++jj) {
+      const int p = 4 * (wave + 4 * jj) + grp;     // this lane's 8 columns of 32-column k step wave + 4*jj
+      u32x4_t bv = *(const u32x4_t*)(st + col * XRB + (p ^ col) * 16);
+      if constexpr (!W32) {
+        u32x4_t av[ETILES];
 #pragma unroll
-      for (int et = 0; et < ETILES; ++et)
-        av[et] = *(const u32x4_t*)(st + (16 + et * 16 + col) * RX_ROWB + slot);
-      if (p * 8 >= cols_left) {                     // past the end of the rows (last chunk)
-        bv = u32x4_t{0u, 0u, 0u, 0u};
+        for (int et = 0; et < ETILES; ++et)
+          av[et] = *(const u32x4_t*)(sw + (et * 16 + col) * WRB + (p ^ col) * 16);
+        if (p * 8 >= cols_left) {                   // past the end of the rows (last chunk)
+          bv = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int et = 0; et < ETILES; ++et) av[et] = u32x4_t{0u, 0u, 0u, 0u};
+          for (int et = 0; et < ETILES; ++et) av[et] = u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int et = 0; et < ETILES; ++et)
+          acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[et]),
+                                                            __builtin_bit_cast(bf16x8_t, bv), acc[et], 0, 0, 0);
+      } else {
+        // the 8 float32 gate values of these columns are pieces 2p and 2p + 1
+        if (p * 8 >= cols_left) bv = u32x4_t{0u, 0u, 0u, 0u};
+        float xf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xf[2 * i] = bf16_to_f32((uint16_t)(bv[i] & 0xffffu));
+          xf[2 * i + 1] = bf16_to_f32((uint16_t)(bv[i] >> 16));
+        }
+#pragma unroll
+        for (int et = 0; et < ETILES; ++et) {
+          const char* wr = sw + (et * 16 + col) * WRB;
+          f32x4_t a0 = *(const f32x4_t*)(wr + ((2 * p) ^ col) * 16);
+          f32x4_t a1 = *(const f32x4_t*)(wr + ((2 * p + 1) ^ col) * 16);
+          if (p * 8 >= cols_left) a0 = a1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[m], xf[m], acc[et], 0, 0, 0);
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[et] = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[m], xf[4 + m], acc[et], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int et = 0; et < ETILES; ++et)
-        acc[et] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[et]),
-                                                          __builtin_bit_cast(bf16x8_t, bv), acc[et], 0, 0, 0);
     }
   }
   // the exchange reuses the stage buffers once every wave is done with them
@@ -313,19 +357,26 @@ hipError_t launch_router_softmax_logits(const float* logits, int64_t ld, int T, 
   return hipGetLastError();
 }
 
-hipError_t launch_router_softmax_x(const uint16_t* x, const uint16_t* wg, int T, int H, int E,
+hipError_t launch_router_softmax_x(const uint16_t* x, const void* wg, int w32, int T, int H, int E,
                                    int k, float scale, const float* gs, int renorm,
                                    float* logits_out, int32_t* idx, float* w, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((T + 15) / 16), block(256);
   const int et = (E + 15) / 16;
-#define LAUNCH(ET, JJ)                                                                             \
-  router_softmax_x_kernel<ET, JJ><<<grid, block, 0, st>>>(x, wg, T, H, E, k, scale, gs, renorm,     \
-                                                          logits_out, idx, w)
-  if (et <= 1) LAUNCH(1, 1);
-  else if (et <= 2) LAUNCH(2, 1);
-  else if (et <= 4) LAUNCH(4, 1);
-  else LAUNCH(8, 2);
+#define LAUNCH(ET, JJ, W)                                                                          \
+  router_softmax_x_kernel<ET, JJ, W><<<grid, block, 0, st>>>(x, wg, T, H, E, k, scale, gs, renorm,  \
+                                                             logits_out, idx, w)
+#define BY_E(W)                                                                                    \
+  if (et <= 1) LAUNCH(1, 1, W);                                                                    \
+  else if (et <= 2) LAUNCH(2, 1, W);                                                               \
+  else if (et <= 4) LAUNCH(4, 1, W);                                                               \
+  else LAUNCH(8, 2, W)
+  if (w32) {
+    BY_E(true);
+  } else {
+    BY_E(false);
+  }
+#undef BY_E
 #undef LAUNCH
   return hipGetLastError();
 }

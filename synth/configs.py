@@ -39,6 +39,7 @@ class MoEConfig:
     bias_range: float = 0.1     # sigmoid router: selection bias ~U(-r, r)
     x_std: float = 1.0
     w_std: float = 0.02
+    router_dtype: str = "bf16"  # softmax gate: "bf16" or "float32" (StackedMoE router_dtype)
 
     @property
     def R(self) -> int:

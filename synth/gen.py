@@ -82,7 +82,8 @@ def make_inputs(cfg: MoEConfig, device="cpu", salt: int = 0) -> dict:
     out: dict = {"cfg": cfg}
     out["x"] = (_normal((T, H), cfg.x_std, d, c, 0, 0, salt)).to(torch.bfloat16)
     if cfg.router == "softmax":
-        out["w_gate"] = _normal((E, H), cfg.w_std, d, c, 1, 0, salt).to(torch.bfloat16)
+        wg = _normal((E, H), cfg.w_std, d, c, 1, 0, salt)
+        out["w_gate"] = wg if getattr(cfg, "router_dtype", "bf16") == "float32" else wg.to(torch.bfloat16)
     else:
         out["logits"] = _normal((T, E + cfg.s), cfg.logit_std, d, c, 1, 0, salt).contiguous()
         g = _gen(d, c, 2, 0, salt)

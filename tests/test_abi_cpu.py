@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_struct_layouts_match_header_sizes():
     # pointer-size fields and natural alignment: these sizes follow from the header
-    assert ctypes.sizeof(m.RouteArgs) == 6 * 4 + 3 * 8 + 8 + 3 * 8 + 4 + 4 + 3 * 8
+    assert ctypes.sizeof(m.RouteArgs) == 6 * 4 + 3 * 8 + 8 + 3 * 8 + 4 + 4 + 3 * 8 + 8   # + router_dtype, padded
     assert ctypes.sizeof(m.CombineArgs) == 3 * 4 + 4 + 8 + 4 + 4 + 8 * 4 + 4 + 4 + 2 * 8
 
 

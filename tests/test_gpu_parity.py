@@ -41,6 +41,10 @@ def _gen(cfg):
     # below one 256-column chunk and with a ragged last chunk
     (1, 45, dict(E=64, k=6, H=1000)), (1, 33, dict(E=100, k=4, H=264)),
     (1, 16, dict(E=128, k=8, H=8)), (1, 300, dict(E=40, k=3, H=776)),
+    # the float32 gate (router_dtype float32): 128-column chunks, fp32 MFMA
+    (2, 4096, dict(router_dtype="float32")), (4, 333, dict(router_dtype="float32")),
+    (1, 45, dict(E=64, k=6, H=1000, router_dtype="float32")), (1, 33, dict(E=100, k=4, H=264, router_dtype="float32")),
+    (1, 16, dict(E=128, k=8, H=8, router_dtype="float32")), (1, 300, dict(E=40, k=3, H=776, router_dtype="float32")),
 ])
 def test_softmax_router_x_form(moe, cid, T, extra):
     cfg = synth.scaled(synth.get_config(cid), T=T, **extra)
@@ -57,6 +61,35 @@ def test_softmax_router_x_form(moe, cid, T, extra):
     ridx, rw = O.route_softmax_topk(host(lo), cfg.k)
     assert np.array_equal(host(idx), ridx)
     assert_rel(host(w), rw, W_RTOL, "softmax weights")
+
+
+def test_float32_gate_selects_on_float32_weights(moe):
+    """StackedMoE router_dtype float32: a selection that bf16 weights would
+    decide differently.  Expert 1's gate row is expert 0's (positive, and
+    ahead of the other experts for these all-positive tokens) scaled up by
+    1 + 2^-10, below half a bf16 step: in bf16 the two rows are the same (a
+    tie, won by expert 0), in float32 expert 1 wins, by a logit gap far above
+    float32 accumulation error."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(41)
+    T, E, H, k = 64, 8, 4096, 2
+    x = (torch.rand((T, H), generator=g, device=DEV) + 0.5).to(torch.bfloat16)
+    # expert 0's row positive and bf16-exact, so its logit leads the others by far
+    w0 = (torch.randn((H,), generator=g, device=DEV) * 0.02).abs().to(torch.bfloat16).float()
+    w = (torch.randn((E, H), generator=g, device=DEV) * 0.002).float()
+    w[0] = w0
+    w[1] = w0 + w0 * 2.0 ** -10          # below half a bf16 step of every entry
+    assert torch.equal(w[1].to(torch.bfloat16), w[0].to(torch.bfloat16))
+    w = w.contiguous()
+    idx32, wt32, _, lo = moe.route(router="softmax", k=k, E=E, x=x, w_gate=w, return_logits=True)
+    idx16, _, _, _ = moe.route(router="softmax", k=k, E=E, x=x, w_gate=w.to(torch.bfloat16))
+    torch.cuda.synchronize()
+    ref = O.gate_logits(host(x), host(w))
+    err, _ = rel_rms_err(host(lo), ref)
+    assert err <= 2e-5
+    ridx, _ = O.route_softmax_topk(ref.astype(np.float32), k)
+    assert np.all(ridx[:, 0] == 1) and np.array_equal(host(idx32), ridx)
+    assert np.all(host(idx16)[:, 0] == 0)          # bf16 weights: a tie, to the lower index
 
 
 @pytest.mark.parametrize("renorm,scale", [(True, 1.0), (False, 2.5)])
