@@ -220,7 +220,8 @@ def summarize_profile(d: str):
            "# workload: T=4096 tokens, hidden 4096, 8 experts, top-2 softmax gate, moe_dim 14336,",
            "#           concatenated gate_up, SiLU, bf16 operands, fp32 accumulate",
            PROFILE_CMDS,
-           f"# calls = warmup + timed steps of bench.py.  Durations in microseconds; only this library's",
+           f"# calls = warmup + timed steps of bench.py (route, csr_* and combine: + 12 launches timed alone",
+           "# after a cache flush).  Durations in microseconds; only this library's",
            "# kernels are listed (the torch kernels that generate the synthetic inputs are omitted).",
            f"# bench.py's own HIP-event timing in the same run: gate_up {bd.get('gate_up', 0) * 1e3:.1f} us, "
            f"down {bd.get('down', 0) * 1e3:.1f} us per launch.", "",
