@@ -59,6 +59,10 @@ static constexpr int LDS_BYTES_TILES = (NSTAGE_A * A_ELEMS + NSTAGE_B * B_ELEMS)
 
 // Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
 static constexpr int BUF_DWORD3 = 0x00020000;
+// A load offset beyond the 0x7fffffff-byte range of the buffer resources
+// (with room for any k offset added to or taken from it): out-of-range
+// buffer loads return zeros without touching memory.
+static constexpr uint32_t OOB_OFFSET = 0xC0000000u;
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -301,6 +305,11 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   auto b_chunk = [&](int i) { return (lane % CPR) ^ swz_f((wave * LPW_B + i) * RPB + lrow); };
   // byte offset of this lane's row plus its chunk, fixed for the tile
   uint32_t a_voff[LPW_A], b_voff[LPW_B];
+  // A wave whose activation rows (one 32-row block) all lie past the tile's
+  // last row points their loads past the end of the buffer range, where they
+  // fetch nothing: an output row depends on its own activation row only, and
+  // rows past the end are neither computed nor stored.
+  const bool a_live = row_beg + wave * LPW_A * RPB < row_end;
 #pragma unroll
   for (int i = 0; i < LPW_A; ++i) {
     const int trow = (wave * LPW_A + i) * RPB + lrow;  // tile row
@@ -308,7 +317,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     // row offset from the base: the token (gathered), the row within the
     // tile (permuted rows, rebased), or the weight-gradient operand's row
     const uint32_t arow = GATHER ? (uint32_t)p.sorted_token[r] : (uint32_t)(r - (MODE == MODE_WGRAD ? 0 : row_beg));
-    a_voff[i] = arow * a_row_bytes + (uint32_t)a_chunk(i) * 16u;
+    a_voff[i] = a_live ? arow * a_row_bytes + (uint32_t)a_chunk(i) * 16u : OOB_OFFSET;
   }
 #pragma unroll
   for (int i = 0; i < LPW_B; ++i) {

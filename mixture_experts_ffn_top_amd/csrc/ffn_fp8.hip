@@ -33,7 +33,7 @@
 // in 2 x 4 (two per SIMD), each wave 128 x 64 = 4 x 2 MFMA blocks with 128
 // fp32 accumulators per lane.  k stages of 128 fp8 (one scale block) go
 // global -> LDS by buffer loads, double buffered, with the 256 activation
-// scales of the stage; the weight scales are read through the scalar cache.
+// scales and the tile's two weight scales of the stage.
 // The weight fragment is the MFMA's first operand, so a lane's accumulators
 // are four consecutive output columns of one row per group of four.
 #include <type_traits>
@@ -57,14 +57,19 @@ constexpr int Q_MI = Q_WTM / 32, Q_NI = Q_WTN / 32;       // 4 x 2 MFMA blocks
 constexpr int Q_A_BYTES = Q_BM * Q_BK;                    // 32 KB
 constexpr int Q_B_BYTES = Q_BN * Q_BK;                    // 32 KB
 constexpr int Q_XS_BYTES = Q_BM * 4;                      // 1 KB of activation scales
-constexpr int Q_STAGE_BYTES = Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES;
+constexpr int Q_WS_BYTES = 16;                            // the tile's two weight scales (+ pad)
+constexpr int Q_STAGE_BYTES = Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES + Q_WS_BYTES;
 constexpr int Q_LPW_A = Q_A_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
 constexpr int Q_LPW_B = Q_B_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
 constexpr int Q_LOADS = Q_LPW_A + Q_LPW_B + 1;            // per wave per stage (+1: 32 row scales)
-constexpr int Q_LDS_PIPE = Q_NSTAGE * Q_STAGE_BYTES;      // 130 KB
+constexpr int Q_LDS_PIPE = Q_NSTAGE * Q_STAGE_BYTES;      // 128 KB + 2 KB of scales
 
 // Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
 constexpr int F8_BUF_DWORD3 = 0x00020000;
+// A load offset beyond the 0x7fffffff-byte range of the buffer resources
+// (with room for any k offset added to it): out-of-range buffer loads return
+// zeros without touching memory.
+constexpr uint32_t F8_OOB_OFFSET = 0xC0000000u;
 
 // 128-byte rows, 8 chunks of 16 bytes; chunk c of row r sits at c ^ f(r)
 // (fragment reads of 32 consecutive rows hit distinct banks).
@@ -77,8 +82,6 @@ __device__ __forceinline__ int f8_swz(int row, int chunk) { return row * Q_BK + 
 __device__ __forceinline__ void f8_block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
-
-typedef const __attribute__((address_space(4))) float* scalar_f32_ptr;
 
 // s = 2^(e - 127) * m exactly: e (returned) is the exponent field clamped to
 // [1, 253], the E8M0 byte of the matrix instruction's operand scale; m =
@@ -181,12 +184,17 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   const int lrow = lane >> 3;
   const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
   uint32_t a_voff[Q_LPW_A], b_voff[Q_LPW_B];
+  // A wave whose 32 activation rows all lie past the expert's last row (in
+  // its last m-block) points their loads past the end of the buffer range,
+  // where they fetch nothing: an output row depends on its own activation
+  // row only, and rows past the end are neither computed nor stored.
+  const bool a_live = row_beg + wave * 32 < row_end;
 #pragma unroll
   for (int i = 0; i < Q_LPW_A; ++i) {
     const int trow = (wave * Q_LPW_A + i) * 8 + lrow;
     const int r = min(row_beg + trow, row_end - 1);
     const uint32_t ar = p.gather ? (uint32_t)p.gather[r] : (uint32_t)(r - row_beg);
-    a_voff[i] = ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16);
+    a_voff[i] = a_live ? ar * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16) : F8_OOB_OFFSET;
   }
 #pragma unroll
   for (int i = 0; i < Q_LPW_B; ++i) {
@@ -202,10 +210,33 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     }
     b_voff[i] = (uint32_t)wrow * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16);
   }
-  // activation scales: wave w fetches those of tile rows 32w .. 32w+31
-  const int xs_r = min(row_beg + wave * 32 + (lane & 31), row_end - 1);
+  // activation scales: wave w fetches 32 of them into scale slots 32w ..
+  // 32w+31.  Slot p holds tile row (p/128)*128 + (p%4)*32 + (p%128)/4, so
+  // the four rows a lane's MFMA blocks use (wm*128 + 32 mi + fr, mi = 0..3)
+  // sit in one 16-byte piece and come in one read per stage.
+  const int xs_p = wave * 32 + (lane & 31);
+  const int xs_r = min(row_beg + (xs_p & ~127) + (xs_p & 3) * 32 + ((xs_p & 127) >> 2), row_end - 1);
   const uint32_t xs_row = p.gather ? (uint32_t)p.gather[xs_r] : (uint32_t)(xs_r - row_beg);
   const uint32_t xs_voff = xs_row * (uint32_t)KT * 4u;
+  // weight scales: a tile uses two 128 x 128 scale blocks per stage, fetched
+  // into the stage's scale slots 0 and 1 by lanes 0 and 1 of wave 0.
+  // down: the tile's 256 columns are blocks 2 nb and 2 nb + 1 (the last one
+  // clamped at an N tail); gate_up: the gate and the up block of output
+  // block nb (concatenated), or blocks 2 nb and 2 nb + 1 (interleaved:
+  // output oc's gate and up rows are 2 oc and 2 oc + 1, so the tile's first 64
+  // outputs sit in block 2 nb, the next 64 in 2 nb + 1).
+  const int ws_j = lane & 1;
+  const int ws_b = (MODE == F8_DOWN)      ? min(2 * nb + ws_j, p.N / 128 - 1)
+                   : (p.fmt == F8_CONCAT) ? (ws_j == 0 ? nb : p.N / 128 + nb)
+                                          : 2 * nb + ws_j;
+  const uint32_t ws_voff = (uint32_t)ws_b * (uint32_t)KT * 4u;
+  // slot of each of the wave's two 32-column blocks
+  int ws_slot[Q_NI];
+#pragma unroll
+  for (int ni = 0; ni < Q_NI; ++ni)
+    ws_slot[ni] = (MODE == F8_DOWN || p.fmt != F8_CONCAT) ? (wn_s >= Q_WAVES_N / 2 ? 1 : 0) : ni;
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.W_scale + (int64_t)e * p.ws_estride), (short)0, 0x7fffffff, F8_BUF_DWORD3);
   // permuted rows (and their scales): the buffer resources start at the
   // tile's first row, so the row buffers may exceed 2 GiB; gathered rows are
   // addressed from the per-token codes by token
@@ -217,17 +248,30 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.A_scale + rb * KT), (short)0, 0x7fffffff, F8_BUF_DWORD3);
 
   auto stage_base = [&](int kt) { return smem + (kt % Q_NSTAGE) * Q_STAGE_BYTES; };
-  auto issue = [&](int kt) {
+  // a wave's loads of stage kt in three parts (part 0: activation rows 0-1
+  // and weight rows 0-1, part 1: the other rows, part 2: the scales), so
+  // that they can be issued between the MFMA blocks of the stage before
+  auto issue_part = [&](int kt, int part) {
     uint8_t* st = stage_base(kt);
     const int kb = kt * Q_BK;
+    if (part < 2) {
 #pragma unroll
-    for (int i = 0; i < Q_LPW_A; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (wave_s * Q_LPW_A + i) * 1024), 16, a_voff[i], kb, 0, 0);
+      for (int i = part * Q_LPW_A / 2; i < (part + 1) * Q_LPW_A / 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (wave_s * Q_LPW_A + i) * 1024), 16, a_voff[i], kb, 0, 0);
 #pragma unroll
-    for (int i = 0; i < Q_LPW_B; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + Q_A_BYTES + (wave_s * Q_LPW_B + i) * 1024), 16, b_voff[i], kb, 0, 0);
-    if (lane < 32)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES + wave_s * 128), 4, xs_voff, kt * 4, 0, 0);
+      for (int i = part * Q_LPW_B / 2; i < (part + 1) * Q_LPW_B / 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + Q_A_BYTES + (wave_s * Q_LPW_B + i) * 1024), 16, b_voff[i], kb, 0, 0);
+    } else {
+      if (lane < 32)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES + wave_s * 128), 4, xs_voff, kt * 4, 0, 0);
+      if (wave_s == 0 && lane < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES), 4, ws_voff, kt * 4, 0, 0);
+    }
+  };
+  auto issue = [&](int kt) {
+    issue_part(kt, 0);
+    issue_part(kt, 1);
+    issue_part(kt, 2);
   };
 
   const int fr = lane & 31, fk = lane >> 5;
@@ -255,6 +299,10 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) bq[ni][kk] = frag(bs, wn * Q_WTN + ni * 32 + fr, kk);
   };
+  auto read_xs = [&](int kt) {
+    return *(const f32x4_t*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES + (wm * Q_WTM + fr * 4) * 4);
+  };
+  auto read_ws = [&](int kt) { return *(const f32x2_t*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES); };
   auto read_a = [&](int kt, int mi, i32x8_t (&aq)[2]) {
     const uint8_t* as = stage_base(kt);
 #pragma unroll
@@ -266,20 +314,6 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   const int live_mi = min(max((row_end - (row_beg + wm_s * Q_WTM) + 31) / 32, 0), Q_MI);
 
   // ---- scales.  Lane row of block mi: wm*128 + mi*32 + fr; weight-scale
-  // block rows of the wave's two 32-column blocks (down: one 128-column block;
-  // gate_up: the gate block and the up block of output block nb).
-  int ws_blk[Q_NI];
-#pragma unroll
-  for (int ni = 0; ni < Q_NI; ++ni) {
-    if (MODE == F8_DOWN) ws_blk[ni] = min((nb * Q_BN + wn_s * Q_WTN) / 128, p.N / 128 - 1);
-    else if (p.fmt == F8_CONCAT) ws_blk[ni] = (ni == 0) ? nb : (p.N / 128 + nb);
-    // interleaved: output oc's gate and up rows are 2 oc and 2 oc + 1, so the
-    // tile's first 64 outputs sit in weight-row block 2 nb, the next 64 in 2 nb + 1
-    else ws_blk[ni] = 2 * nb + (wn_s >= Q_WAVES_N / 2 ? 1 : 0);
-  }
-  // read through the scalar cache: uniform per wave, and a vector load here
-  // would make its wait drain the loads into LDS still in flight
-  const scalar_f32_ptr wsc = (scalar_f32_ptr)(p.W_scale + (int64_t)e * p.ws_estride);
   float unit[Q_MI][Q_NI];  // scale of the accumulator units
 #pragma unroll
   for (int mi = 0; mi < Q_MI; ++mi)
@@ -298,7 +332,9 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   f8_block_barrier();
   read_b(0, bq);
-  read_a(0, 0, aq[0]);
+  f32x4_t xs4 = read_xs(0);
+  f32x2_t ws2 = read_ws(0);
+  if (live_mi > 0) read_a(0, 0, aq[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
   for (int kt = 0; kt < KT; ++kt) {
     // a zero scale keeps the previous unit and zeroes the codes it scales
@@ -306,20 +342,19 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     int we[Q_NI];
 #pragma unroll
     for (int ni = 0; ni < Q_NI; ++ni) {
-      const float w = wsc[ws_blk[ni] * KT + kt];
+      const float w = ws_slot[ni] ? ws2[1] : ws2[0];
       we[ni] = f8_split_scale(w, wm_[ni]);
       if (__builtin_bit_cast(uint32_t, w) << 1 == 0u) {
         asm volatile("");
         bq[ni][0] = bq[ni][1] = i32x8_t{};
       }
     }
-    const float* xs = (const float*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES);
 #pragma unroll
     for (int mi = 0; mi < Q_MI; ++mi) {
       const int c = mi & 1;
-      if (mi + 1 < Q_MI) read_a(kt, mi + 1, aq[c ^ 1]);
+      if (mi + 1 < Q_MI && mi + 1 < live_mi) read_a(kt, mi + 1, aq[c ^ 1]);
       if (mi < live_mi) {
-        const float x = xs[wm * Q_WTM + mi * 32 + fr];
+        const float x = xs4[mi];
         if (__builtin_amdgcn_ballot_w64(x == 0.0f) != 0) {
           asm volatile("");
           if (x == 0.0f) aq[c][0] = aq[c][1] = i32x8_t{};
@@ -345,15 +380,20 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
             acc[mi][ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq[ni][kk], aq[c][kk], acc[mi][ni], 0, 0, 0,
                                                                           we[ni], 0, xe);
       }
+      // stage kt+1's loads (its buffer was freed by the barrier that began
+      // this stage), spread over the first three blocks: issued all at once
+      // they would queue behind each other and hold up the waves' next reads
+      if (mi < 3 && kt >= 1 && kt + 1 < KT) issue_part(kt + 1, mi);
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     }
     if (kt + 1 < KT) {
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       f8_block_barrier();
-      if (kt + 2 < KT) issue(kt + 2);
       read_b(kt + 1, bq);
-      read_a(kt + 1, 0, aq[0]);
+      xs4 = read_xs(kt + 1);
+      ws2 = read_ws(kt + 1);
+      if (live_mi > 0) read_a(kt + 1, 0, aq[0]);
       __builtin_amdgcn_s_waitcnt(waitcnt_lgkm(0));
     }
   }

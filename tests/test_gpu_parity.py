@@ -757,6 +757,8 @@ def _check_fp8_act(cfg, inp, res, layer):
     ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, True),
     ({"T": 512, "E": 8, "H": 512, "D": 256}, 512, False),
     ({"T": 2048, "E": 16, "k": 4}, 256, True),              # full hidden / moe dims of the fp8 layer
+    ({"T": 300, "E": 5, "k": 2, "H": 128, "D": 128}, 300, True),    # one k stage in both GEMMs
+    ({"T": 300, "E": 5, "k": 2, "H": 384, "D": 256}, 300, False),   # three and two k stages
 ])
 def test_fp8_layer_small(moe, changes, nsample, gather):
     cfg = synth.scaled(synth.get_config(5), **changes)
