@@ -97,8 +97,8 @@ def algorithmic_work(cfg) -> dict:
 def measure_ceilings(moe, torch) -> dict:
     """Practical ceilings on this chip, measured with the library's probes
     right after the timed steps (same clocks): an MFMA loop on every CU for
-    bf16 and fp8, and a 1 GiB streaming copy (bytes read + bytes written).
-    The best of five launches each."""
+    bf16 and fp8, a 1 GiB streaming copy (bytes read + bytes written) and a
+    1 GiB streaming read.  The best of five launches each."""
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = HipEvents(2)
@@ -129,8 +129,15 @@ def measure_ceilings(moe, torch) -> dict:
         return 2 * n
 
     res["stream_copy_gbs"] = round(best_rate(copy) / 1e9, 1)
+    rout = torch.empty(16384, dtype=torch.int32, device=dev)
+
+    def read():
+        moe.probe_stream_read(src, rout)
+        return n
+
+    res["stream_read_gbs"] = round(best_rate(read) / 1e9, 1)
     ev.close()
-    del src, dst
+    del src, dst, rout
     return res
 
 
@@ -393,36 +400,57 @@ def cpu_baseline(cfg, inp, n_tokens: int):
 
 def flushed_bandwidth(layer, moe, torch, work: dict, reps: int = 11) -> dict:
     """route, build_indices and combine timed alone on the layer's last inputs,
-    each launch after a 512 MiB streaming copy that evicts them from L2 and
-    the Infinity Cache: median and minimum over `reps` launches, and the
-    median's rate in algorithmic HBM bytes against the 8 TB/s peak."""
+    each launch after a 512 MiB streaming read that evicts their inputs from
+    L2 and the Infinity Cache without leaving dirty lines behind: median and
+    minimum over `reps` launches, and the median's rate in algorithmic HBM
+    bytes against the 8 TB/s peak.  Beside each, the same-size ceilings timed
+    the same way (launch and ramp included): a plain read of the same bytes
+    and a plain copy moving the same bytes (half read, half written)."""
     import statistics
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
-    n = 512 << 20
-    src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-    dst = torch.empty_like(src)
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    flush_out = torch.empty(16384, dtype=torch.int32, device=dev)
     ev = HipEvents(2)
     calls = layer.stage_calls()
     nbytes = {"route": work["route_bytes"], "build_indices": work["build_indices_bytes"],
               "combine": work["combine_bytes"]}
-    out = {}
-    for name, call in calls.items():
-        call()
+    big = max(nbytes.values()) // 16 * 16 + 16
+    src2 = torch.empty(big, dtype=torch.uint8, device=dev).fill_(2)
+    dst2 = torch.empty(big // 2 + 16, dtype=torch.uint8, device=dev)
+    out2 = torch.empty(16384, dtype=torch.int32, device=dev)
+
+    def timed(call):
         ts = []
         for _ in range(reps):
-            moe.probe_stream_copy(src, dst)
+            moe.probe_stream_read(flush_src, flush_out)
             ev.record(0, stream)
             call()
             ev.record(1, stream)
             torch.cuda.synchronize()
             ts.append(ev.elapsed_ms(0, 1))
-        med, mn = statistics.median(ts), min(ts)
+        return statistics.median(ts), min(ts)
+
+    out = {}
+    for name, call in calls.items():
+        call()
+        med, mn = timed(call)
         gbs = nbytes[name] / (med * 1e-3) / 1e9
         out[name] = {"median_us": round(med * 1e3, 2), "min_us": round(mn * 1e3, 2), "gbs": round(gbs, 1),
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes[name]}
+        n16 = nbytes[name] // 16 * 16
+        half = (nbytes[name] // 2) // 16 * 16
+        if half >= 16:
+            rs = src2[:n16]
+            rmed, _ = timed(lambda: moe.probe_stream_read(rs, out2))
+            cs, cd = src2[:half], dst2[:half]
+            cmed, _ = timed(lambda: moe.probe_stream_copy(cs, cd))
+            out[name].update({"read_same_bytes_us": round(rmed * 1e3, 2),
+                              "copy_same_bytes_us": round(cmed * 1e3, 2),
+                              "frac_of_same_size_read": round(rmed / med, 4),
+                              "frac_of_same_size_copy": round(cmed / med, 4)})
     ev.close()
-    del src, dst
+    del flush_src, flush_out, src2, dst2, out2
     return out
 
 
@@ -600,7 +628,7 @@ def main():
     work = algorithmic_work(cfg)
     print("[bench] bandwidth kernels alone from a flushed cache", file=sys.stderr, flush=True)
     flushed = flushed_bandwidth(layer, moe, torch, work)
-    print("[bench] measured ceilings (MFMA loop, streaming copy)", file=sys.stderr, flush=True)
+    print("[bench] measured ceilings (MFMA loop, streaming copy and read)", file=sys.stderr, flush=True)
     ceil = measure_ceilings(moe, torch)
 
     gu_flops, dn_flops = work["gate_up_flops"], work["down_flops"]
@@ -664,7 +692,10 @@ def main():
         # the bandwidth kernels alone, each from a flushed cache (median of 11)
         "hbm_gbs": {n: v["gbs"] for n, v in flushed.items()},
         "hbm_frac": {n: v["frac"] for n, v in flushed.items()},
-        "hbm_frac_of_measured": {n: round(v["gbs"] / ceil["stream_copy_gbs"], 4) for n, v in flushed.items()},
+        # against the measured streaming rate of the same kind: a read for the
+        # router (it reads x and writes a few bytes per token), a copy otherwise
+        "hbm_frac_of_measured": {n: round(v["gbs"] / ceil["stream_read_gbs" if n == "route" else "stream_copy_gbs"], 4)
+                                 for n, v in flushed.items()},
         "hbm_flushed": flushed,
         # the same kernels inside the timed layer steps (mean of the steps): the
         # combine there reads the rows O the down GEMM has just left in the

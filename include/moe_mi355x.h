@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -607,9 +607,19 @@ moe_status_t moe_transpose_bf16(const void* src, void* dst, int32_t batch, int32
  * moe_probe_stream_copy -- copies `bytes` bytes from src to dst (device,
  * 16-byte aligned, not overlapping) with 16-byte loads and stores; bytes is a
  * multiple of 16 (0 launches nothing).
+ *
+ * moe_probe_stream_read -- reads `bytes` bytes of src (device, 16-byte
+ * aligned; bytes a multiple of 16, 0 launches nothing) with 16-byte loads and
+ * writes nothing else: the ceiling of a read-dominated kernel, and a way to
+ * evict the caches without leaving dirty lines behind.  It launches
+ * min(ceil(bytes / 32 KiB), out_len / 4) work-groups of 4 waves; wave w
+ * writes out[w] (device, uint32) = the XOR of the 32-bit words it read, so
+ * that the XOR of the written entries is the XOR of all words of src.
+ * Entries past the launched waves are left as they are.  out_len >= 4.
  * ---------------------------------------------------------------------- */
 moe_status_t moe_probe_mfma(int32_t kind, int32_t workgroups, int32_t iters, float* out, void* stream);
 moe_status_t moe_probe_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+moe_status_t moe_probe_stream_read(const void* src, int64_t bytes, uint32_t* out, int32_t out_len, void* stream);
 
 /* Helpers. */
 const char* moe_status_string(moe_status_t status);

@@ -93,7 +93,7 @@ ENTRY_POINTS = ("moe_route", "moe_build_indices", "moe_build_indices_noalloc", "
                 "moe_shared_indices", "moe_build_indices_workspace_bytes", "moe_ffn_workspace_bytes",
                 "moe_ffn_fused_workspace_bytes", "moe_combine_backward", "moe_grouped_ffn_backward",
                 "moe_ffn_backward_workspace_bytes", "moe_transpose_bf16", "moe_probe_mfma",
-                "moe_probe_stream_copy", "moe_status_string", "moe_last_error_message", "moe_abi_version")
+                "moe_probe_stream_copy", "moe_probe_stream_read", "moe_status_string", "moe_last_error_message", "moe_abi_version")
 
 
 def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -122,6 +122,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_probe_mfma.restype = _i32
     lib.moe_probe_stream_copy.argtypes = [_vp, _vp, _i64, _vp]
     lib.moe_probe_stream_copy.restype = _i32
+    lib.moe_probe_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
+    lib.moe_probe_stream_read.restype = _i32
     lib.moe_status_string.argtypes = [_i32]
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_last_error_message.argtypes = []
@@ -427,6 +429,14 @@ def probe_stream_copy(src, dst):
         raise ValueError("probe_stream_copy: src and dst must have the same size in bytes")
     _check(lib().moe_probe_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)))
     return dst
+
+
+def probe_stream_read(src, out):
+    """moe_probe_stream_read: reads src (a multiple of 16 bytes); out (int32,
+    at least 4 entries) receives one XOR of the 32-bit words read per wave."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().moe_probe_stream_read(_ptr(src), nbytes, _ptr(out), out.numel(), _stream(src.device)))
+    return out
 
 
 def shared_indices(T: int, n_shared: int, device):

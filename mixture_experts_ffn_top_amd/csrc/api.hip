@@ -720,4 +720,14 @@ moe_status_t moe_probe_stream_copy(const void* src, void* dst, int64_t bytes, vo
   return hip_status(moe::launch_stream_copy(src, dst, bytes / 16, (hipStream_t)stream), "moe_probe_stream_copy");
 }
 
+moe_status_t moe_probe_stream_read(const void* src, int64_t bytes, uint32_t* out, int32_t out_len, void* stream) {
+  REQUIRE(bytes >= 0 && bytes % 16 == 0, "moe_probe_stream_read: bytes must be a multiple of 16 >= 0");
+  if (bytes == 0) return ok();
+  REQUIRE(src && out, "moe_probe_stream_read: src and out are required");
+  REQUIRE(aligned16(src), "moe_probe_stream_read: src must be 16-byte aligned");
+  REQUIRE(out_len >= 4, "moe_probe_stream_read: out_len must be >= 4 (got %d)", out_len);
+  return hip_status(moe::launch_stream_read(src, bytes / 16, out, out_len, (hipStream_t)stream),
+                    "moe_probe_stream_read");
+}
+
 }  // extern "C"

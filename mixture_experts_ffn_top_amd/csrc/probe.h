@@ -1,4 +1,4 @@
-// Launchers of the measured-ceiling probes (MFMA loop, streaming copy).
+// Launchers of the measured-ceiling probes (MFMA loop, streaming copy, streaming read).
 #pragma once
 #include <hip/hip_runtime.h>
 
@@ -14,5 +14,10 @@ int probe_waves(int workgroups);
 hipError_t launch_mfma_probe(int fp8, int workgroups, int iters, float* out, hipStream_t st);
 // copies n16 16-byte units from src to dst
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t st);
+// workgroups (4 waves each) a streaming read of n16 16-byte units launches
+// with out_len output entries: one per 32 KiB, at most out_len / 4
+int64_t stream_read_workgroups(int64_t n16, int32_t out_len);
+// reads n16 16-byte units of src; out[wave] = XOR of the 32-bit words the wave read
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* out, int32_t out_len, hipStream_t st);
 
 }  // namespace moe

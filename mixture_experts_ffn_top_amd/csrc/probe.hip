@@ -87,6 +87,30 @@ __global__ __launch_bounds__(COPY_NT) void stream_copy_kernel(const uint4* __res
   }
 }
 
+constexpr int READ_NT = 256;
+constexpr int READ_UNROLL = 8;
+
+// Each wave XORs the 32-bit words it reads and lane 0 writes the result, so
+// that the loads are kept and the XOR of all outputs is that of all words.
+__global__ __launch_bounds__(READ_NT) void stream_read_kernel(const uint4* __restrict__ src, int64_t n,
+                                                              uint32_t* __restrict__ out) {
+  const int64_t step = (int64_t)gridDim.x * (READ_NT * READ_UNROLL);
+  uint32_t x = 0;
+  for (int64_t base = (int64_t)blockIdx.x * (READ_NT * READ_UNROLL) + threadIdx.x; base < n; base += step) {
+    uint4 v[READ_UNROLL];
+#pragma unroll
+    for (int u = 0; u < READ_UNROLL; ++u) {
+      const int64_t i = base + (int64_t)u * READ_NT;
+      v[u] = i < n ? src[i] : uint4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < READ_UNROLL; ++u) x ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * (READ_NT / 64) + (threadIdx.x >> 6)] = x;
+}
+
 }  // namespace
 
 int probe_waves(int workgroups) { return workgroups * (PROBE_NT / 64); }
@@ -97,6 +121,22 @@ hipError_t launch_mfma_probe(int fp8, int workgroups, int iters, float* out, hip
     mfma_probe_fp8_kernel<<<workgroups, PROBE_NT, 0, st>>>(iters, 0.001f, out);
   else
     mfma_probe_bf16_kernel<<<workgroups, PROBE_NT, 0, st>>>(iters, 0.001f, out);
+  return hipGetLastError();
+}
+
+int64_t stream_read_workgroups(int64_t n16, int32_t out_len) {
+  const int64_t per_block = READ_NT * READ_UNROLL;
+  const int64_t want = (n16 + per_block - 1) / per_block;
+  const int64_t cap = out_len / (READ_NT / 64);
+  return want < cap ? want : cap;
+}
+
+hipError_t launch_stream_read(const void* src, int64_t n16, uint32_t* out, int32_t out_len, hipStream_t st) {
+  if (n16 <= 0) return hipSuccess;
+  const int64_t grid = stream_read_workgroups(n16, out_len);
+  if (grid < 1) return hipErrorInvalidValue;
+  // entries past the grid's waves stay as they are; the used ones are all written
+  stream_read_kernel<<<dim3((unsigned)grid), READ_NT, 0, st>>>((const uint4*)src, n16, out);
   return hipGetLastError();
 }
 

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
 
 
 def test_struct_layouts_match_header_sizes():
@@ -398,3 +398,21 @@ def test_probe_stream_copy_validation(args, frag):
 
 def test_probe_stream_copy_zero_bytes_is_a_no_op():
     assert m.lib().moe_probe_stream_copy(None, None, 0, None) == m.MOE_OK
+
+
+@pytest.mark.parametrize("args,frag", [
+    ((4096, 24, 64, 4), "multiple of 16"),
+    ((0, 32, 64, 4), "required"),
+    ((4096, 32, 0, 4), "required"),
+    ((24, 32, 64, 4), "aligned"),
+    ((4096, 32, 64, 3), "out_len"),
+])
+def test_probe_stream_read_validation(args, frag):
+    src, n, out, out_len = args
+    st = m.lib().moe_probe_stream_read(src or None, n, out or None, out_len, None)
+    msg = m.lib().moe_last_error_message().decode()
+    assert st == m.MOE_ERR_INVALID_ARGUMENT and frag in msg, msg
+
+
+def test_probe_stream_read_zero_bytes_is_a_no_op():
+    assert m.lib().moe_probe_stream_read(None, 0, None, 0, None) == m.MOE_OK
