@@ -63,6 +63,7 @@ constexpr int Q_LPW_A = Q_A_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
 constexpr int Q_LPW_B = Q_B_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
 constexpr int Q_LOADS = Q_LPW_A + Q_LPW_B + 1;            // per wave per stage (+1: 32 row scales)
 constexpr int Q_LDS_PIPE = Q_NSTAGE * Q_STAGE_BYTES;      // 128 KB + 2 KB of scales
+constexpr int Q_LDS_OUT = Q_BM * (Q_BN * 2 + 16);         // the down tile's bf16 outputs (132 KB)
 
 // Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
 constexpr int F8_BUF_DWORD3 = 0x00020000;
@@ -469,6 +470,48 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       }
       if (wn == 0 && fk == 0) p.out_scale[(int64_t)row * (p.N / 128) + nb] = s;
     }
+  } else if (OUT_BF16) {
+    // The tile's bf16 outputs go through LDS (row pitch 528 bytes: 4 banks of
+    // skew per row) so that each store moves whole 512-byte row pieces: a
+    // lane's own accumulators cover 8 bytes of each of 16 rows, which as
+    // direct stores would touch every output line 8 times.
+    constexpr int PITCH = Q_LDS_OUT / Q_BM;
+    __syncthreads();  // the stage buffers are free
+#pragma unroll
+    for (int ni = 0; ni < Q_NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lc = wn * Q_WTN + ni * 32 + 8 * q + 4 * fk;  // first of 4 tile columns
+        const int n = nb * Q_BN + lc;
+        float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e && n < p.N) {
+          const uint2 b2 = *(const uint2*)(bias_e + n);
+          bb[0] = bf16_to_f32(b2.x & 0xffffu);
+          bb[1] = bf16_to_f32(b2.x >> 16);
+          bb[2] = bf16_to_f32(b2.y & 0xffffu);
+          bb[3] = bf16_to_f32(b2.y >> 16);
+        }
+#pragma unroll
+        for (int mi = 0; mi < Q_MI; ++mi) {
+          const int lr = wm * Q_WTM + mi * 32 + fr;
+          const float u = unit[mi][ni] * sc;
+          uint2 w;
+          w.x = pack_bf16x2_rne(acc[mi][ni][4 * q + 0] * u + bb[0], acc[mi][ni][4 * q + 1] * u + bb[1]);
+          w.y = pack_bf16x2_rne(acc[mi][ni][4 * q + 2] * u + bb[2], acc[mi][ni][4 * q + 3] * u + bb[3]);
+          *(uint2*)(smem + lr * PITCH + lc * 2) = w;
+        }
+      }
+    __syncthreads();
+    // 64 lanes store two rows of 32 x 16 bytes; wave w takes rows 2 j + ... of its 32
+    const int cpart = lane & 31;
+    const int n = nb * Q_BN + cpart * 8;
+#pragma unroll 4
+    for (int j = 0; j < Q_BM / (2 * Q_WAVES_M * Q_WAVES_N); ++j) {
+      const int lr = wave * (Q_BM / (Q_WAVES_M * Q_WAVES_N)) + 2 * j + (lane >> 5);
+      const int row = row_beg + lr;
+      if (row < row_end && n < p.N)
+        *(u32x4_t*)((uint16_t*)p.out + (int64_t)row * p.N + n) = *(const u32x4_t*)(smem + lr * PITCH + cpart * 16);
+    }
   } else {
 #pragma unroll
     for (int ni = 0; ni < Q_NI; ++ni)
@@ -508,7 +551,8 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 template <typename KernelT>
 hipError_t launch_fp8(KernelT kern, const Fp8GemmArgs& a, int max_rows, int NBO, hipStream_t st) {
   const int prefix = (a.L + 1) * (int)sizeof(int32_t);
-  const int lds = Q_LDS_PIPE > prefix ? Q_LDS_PIPE : prefix;
+  const int pipe = Q_LDS_PIPE > Q_LDS_OUT ? Q_LDS_PIPE : Q_LDS_OUT;
+  const int lds = pipe > prefix ? pipe : prefix;
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int64_t nonempty = (int64_t)max_rows < a.L ? max_rows : a.L;
