@@ -779,32 +779,41 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
       }
     }
   } else {
-    void* out_e = p.out;
+    // bf16 output through LDS (row pitch 528 bytes: 4 banks of skew per
+    // row), so that each store moves whole 512-byte row pieces instead of 8
+    // bytes of each of 32 rows per store instruction.
+    constexpr int PITCH = BN * 2 + 16;
+    static_assert(BM * PITCH <= LDS_BYTES_TILES, "staged epilogue exceeds LDS");
+    uint8_t* stg = (uint8_t*)smem;
+    __syncthreads();  // the operand tiles are no longer read
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nb * BN + wn * WTN + ni * 32 + 8 * q + 4 * fk;  // first of 4 columns
-        if (n >= p.N) continue;
+        const int nl = wn * WTN + ni * 32 + 8 * q + 4 * fk;  // tile column of 4
+        const int n = nb * BN + nl;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias_e) {
+        if (bias_e && n < p.N) {
           const uint2 b2 = *(const uint2*)(bias_e + n);
           bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
           bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
         }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
-          const int row = row_beg + wm * WTM + mi * 32 + fr;
-          if (row >= row_end) continue;
-          float v[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
           uint2 w;
-          w.x = pack_bf16x2_rne(v[0], v[1]);
-          w.y = pack_bf16x2_rne(v[2], v[3]);
-          *(uint2*)((uint16_t*)out_e + (int64_t)row * p.ldo + n) = w;
+          w.x = pack_bf16x2_rne(acc[mi][ni][4 * q] * sc + bd[0], acc[mi][ni][4 * q + 1] * sc + bd[1]);
+          w.y = pack_bf16x2_rne(acc[mi][ni][4 * q + 2] * sc + bd[2], acc[mi][ni][4 * q + 3] * sc + bd[3]);
+          *(uint2*)(stg + (wm * WTM + mi * 32 + fr) * PITCH + nl * 2) = w;
         }
       }
+    __syncthreads();
+    uint16_t* out_e = (uint16_t*)p.out;
+    const int n = nb * BN + (lane & 31) * 8;  // 32 lanes per 512-byte row
+    for (int r = wave * 2 + (lane >> 5); r < BM; r += 2 * WAVES_M * WAVES_N) {
+      const int row = row_beg + r;
+      if (row < row_end && n < p.N)
+        *(u32x4_t*)(out_e + (int64_t)row * p.ldo + n) = *(const u32x4_t*)(stg + r * PITCH + (lane & 31) * 16);
+    }
   }
 }
 

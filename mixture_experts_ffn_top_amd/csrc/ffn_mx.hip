@@ -51,6 +51,10 @@ constexpr int X_B_BYTES = X_BN * X_B_ROW;                  // 16 KB
 // LDS: activation slots of X_A_BYTES + 256 scale dwords in a ring of 2, weight
 // slots of X_B_BYTES + 256 scale dwords in a ring of 4 (134 KB)
 constexpr int X_LDS_PIPE = 2 * (X_A_BYTES + X_BM * 4) + 4 * (X_B_BYTES + X_BN * 4);
+// the down epilogue stages its bf16 tile in LDS: rows of 512 bytes + 16 of
+// bank skew (132 KB)
+constexpr int X_LDS_OUT = X_BM * (X_BN * 2 + 16);
+static_assert(X_LDS_OUT <= X_LDS_PIPE, "the staged output tile exceeds the pipeline's LDS");
 
 constexpr int X_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
 // A byte offset past every buffer's 0x7fffffff-byte range (also with a stage's
@@ -400,6 +404,45 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
             e4m3x4(a[4 * q] * inv, a[4 * q + 1] * inv, a[4 * q + 2] * inv, a[4 * q + 3] * inv);
       }
       if (fh == 0) p.out_scale[(int64_t)row * (p.N / 32) + (nb * NBO + wn * 32) / 32] = (uint8_t)(X + 127);
+    }
+  } else if (OUT_BF16) {
+    // The tile's bf16 outputs go through LDS (row pitch 528 bytes: 4 banks of
+    // skew per row) so that each store moves whole 512-byte row pieces: a
+    // lane's own accumulators cover 8 bytes of each of 16 rows, which as
+    // direct stores would touch every output line 8 times.
+    constexpr int PITCH = X_LDS_OUT / X_BM;
+    __syncthreads();  // the stage buffers are free
+#pragma unroll
+    for (int ni = 0; ni < X_NI; ++ni)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lc = wn * X_WTN + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
+        const int n = nb * X_BN + lc;
+        float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias_e && n < p.N) {
+          const uint2 b2 = *(const uint2*)(bias_e + n);
+          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+        }
+#pragma unroll
+        for (int mi = 0; mi < X_MI; ++mi) {
+          const int lr = wm * X_WTM + mi * 32 + fr;
+          uint2 w;
+          w.x = pack_bf16x2_rne(acc[mi][ni][4 * q + 0] * sc + bd[0], acc[mi][ni][4 * q + 1] * sc + bd[1]);
+          w.y = pack_bf16x2_rne(acc[mi][ni][4 * q + 2] * sc + bd[2], acc[mi][ni][4 * q + 3] * sc + bd[3]);
+          *(uint2*)(smem + lr * PITCH + lc * 2) = w;
+        }
+      }
+    __syncthreads();
+    // 64 lanes store two rows of 32 x 16 bytes; wave w takes rows 32 w .. 32 w + 31
+    const int cpart = lane & 31;
+    const int n = nb * X_BN + cpart * 8;
+#pragma unroll 4
+    for (int j = 0; j < X_BM / (2 * X_WAVES_M * X_WAVES_N); ++j) {
+      const int lr = wave * (X_BM / (X_WAVES_M * X_WAVES_N)) + 2 * j + (lane >> 5);
+      const int row = row_beg + lr;
+      if (row < row_end && n < p.N)
+        *(u32x4_t*)((uint16_t*)p.out + (int64_t)row * p.N + n) = *(const u32x4_t*)(smem + lr * PITCH + cpart * 16);
     }
   } else {
 #pragma unroll
