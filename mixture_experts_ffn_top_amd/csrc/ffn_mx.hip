@@ -48,9 +48,14 @@ constexpr int X_A_ROW = X_BK;                              // bytes per e4m3 sta
 constexpr int X_B_ROW = X_BK / 2;                          // bytes per packed e2m1 stage row
 constexpr int X_A_BYTES = X_BM * X_A_ROW;                  // 32 KB
 constexpr int X_B_BYTES = X_BN * X_B_ROW;                  // 16 KB
-// LDS: activation slots of X_A_BYTES + 256 scale dwords in a ring of 2, weight
-// slots of X_B_BYTES + 256 scale dwords in a ring of 4 (134 KB)
-constexpr int X_LDS_PIPE = 2 * (X_A_BYTES + X_BM * 4) + 4 * (X_B_BYTES + X_BN * 4);
+// LDS: activation slots of X_A_BYTES in a ring of 2, weight slots of
+// X_B_BYTES in a ring of 4, then the scale dwords of the 256 activation rows
+// and of the 256 weight rows in rings of 2 and 4 slots, each slot holding one
+// group of up to 4 stages (16 bytes per row): 152 KB
+constexpr int X_SC_SLOT = X_BM * 16;
+constexpr int X_SC_A = 2 * X_A_BYTES + 4 * X_B_BYTES;
+constexpr int X_SC_B = X_SC_A + 2 * X_SC_SLOT;
+constexpr int X_LDS_PIPE = X_SC_B + 4 * X_SC_SLOT;
 // the down epilogue stages its bf16 tile in LDS: rows of 512 bytes + 16 of
 // bank skew (132 KB)
 constexpr int X_LDS_OUT = X_BM * (X_BN * 2 + 16);
@@ -213,9 +218,15 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
   // ring of 4.  A wave's vmcnt then counts one stream only, so the weight
   // stream keeps three stages in flight while the activations, re-read from
   // L2 by the neighbouring n-blocks, keep one.
-  constexpr int A_SLOT = X_A_BYTES + X_BM * 4, B_SLOT = X_B_BYTES + X_BN * 4;
+  constexpr int A_SLOT = X_A_BYTES, B_SLOT = X_B_BYTES;
   constexpr int NA = 2, NB4 = 4, B_RING = NA * A_SLOT;
-  constexpr int LB = X_B_BYTES / 1024 / 4 + 1;  // loads per weight-role wave per stage
+  constexpr int LB = X_B_BYTES / 1024 / 4;  // row loads per weight-role wave per stage
+  // The scale dwords of G consecutive stages (G = 4 when the stage count
+  // allows, else 1) come in one load per role wave: 16 contiguous bytes of
+  // each row instead of 4 bytes of each row per stage, a quarter of the
+  // cache lines.  Group g sits in scale slot g % 2 (activations) or g % 4
+  // (weights), rows 4 G bytes apart.
+  const int G = (KT % 4 == 0) ? 4 : 1;
   const bool a_role = wave_s < 4;
   const int rw = wave_s & 3;
   const uint8_t* Wexp = p.W + (int64_t)e * p.w_estride;
@@ -253,19 +264,29 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 
   auto a_slot = [&](int kt) { return smem + (kt % NA) * A_SLOT; };
   auto b_slot = [&](int kt) { return smem + B_RING + (kt % NB4) * B_SLOT; };
+  auto as_slot = [&](int kt) { return smem + X_SC_A + ((kt / G) % 2) * X_SC_SLOT; };
+  auto bs_slot = [&](int kt) { return smem + X_SC_B + ((kt / G) % 4) * X_SC_SLOT; };
+  // a stage's scale group first (when the stage starts one), then its rows
+  auto issue_scales = [&](const __amdgpu_buffer_rsrc_t& rsrc, uint8_t* slot, int kt) {
+    if (kt % G != 0) return;
+    if (G == 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lptr_t)(slot + rw * 64 * 16), 16, s_voff, kt * 4, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lptr_t)(slot + rw * 64 * 4), 4, s_voff, kt * 4, 0, 0);
+  };
   auto issue_a = [&](int kt) {
+    issue_scales(as_rsrc, as_slot(kt), kt);
     uint8_t* st = a_slot(kt);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + (rw * 8 + i) * 1024), 16, voff[i], kt * X_A_ROW, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(st + X_A_BYTES + rw * 256), 4, s_voff, kt * 4, 0, 0);
   };
   auto issue_b = [&](int kt) {
+    issue_scales(bs_rsrc, bs_slot(kt), kt);
     uint8_t* st = b_slot(kt);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + (rw * 4 + i) * 1024), 16, voff[i], kt * X_B_ROW, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + X_B_BYTES + rw * 256), 4, s_voff, kt * 4, 0, 0);
   };
 
   const int fr = lane & 31, fh = lane >> 5;
@@ -291,7 +312,8 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
   const int live_mi = min(max((row_end - (row_beg + wm_s * X_WTM) + 31) / 32, 0), X_MI);
 
   // ---- main loop.  Iteration kt: each role waits for its own loads of stage
-  // kt (the weight waves leave stages kt+1 and kt+2 in flight), the barrier
+  // kt (the weight waves leave stages kt+1 and kt+2 in flight: at least LB
+  // loads each, one more where a stage starts a scale group), the barrier
   // publishes the stage, then the activation waves issue stage kt+1 into the
   // activation slot of stage kt-1 and the weight waves stage kt+3 into the
   // weight slot of stage kt-1 (both free: every wave has passed the barrier
@@ -315,14 +337,15 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
     }
     const uint8_t* ast = a_slot(kt);
     const uint8_t* bst = b_slot(kt);
-    const uint32_t* as_l = (const uint32_t*)(ast + X_A_BYTES);
-    const uint32_t* bs_l = (const uint32_t*)(bst + X_B_BYTES);
+    // this stage's scale dword of row r: r * 4 G + (kt % G) * 4 in its group slot
+    const uint8_t* as_l = as_slot(kt) + (kt % G) * 4;
+    const uint8_t* bs_l = bs_slot(kt) + (kt % G) * 4;
     i32x8_t bq[X_NI][2];
     int bsc[X_NI][2];
 #pragma unroll
     for (int ni = 0; ni < X_NI; ++ni) {
       const int row = wn * X_WTN + ni * 32 + fr;
-      const uint32_t s4 = bs_l[row];
+      const uint32_t s4 = *(const uint32_t*)(bs_l + row * 4 * G);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         bq[ni][kk] = frag_b(bst, row, kk);
@@ -333,7 +356,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
     for (int mi = 0; mi < X_MI; ++mi) {
       if (mi < live_mi) {
         const int row = wm * X_WTM + mi * 32 + fr;
-        const uint32_t s4 = as_l[row];
+        const uint32_t s4 = *(const uint32_t*)(as_l + row * 4 * G);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           const i32x8_t aq = frag_a(ast, row, kk);
