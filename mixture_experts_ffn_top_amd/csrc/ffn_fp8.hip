@@ -56,13 +56,16 @@ constexpr int Q_WTM = Q_BM / Q_WAVES_M, Q_WTN = Q_BN / Q_WAVES_N;  // 128 x 64
 constexpr int Q_MI = Q_WTM / 32, Q_NI = Q_WTN / 32;       // 4 x 2 MFMA blocks
 constexpr int Q_A_BYTES = Q_BM * Q_BK;                    // 32 KB
 constexpr int Q_B_BYTES = Q_BN * Q_BK;                    // 32 KB
-constexpr int Q_XS_BYTES = Q_BM * 4;                      // 1 KB of activation scales
 constexpr int Q_WS_BYTES = 16;                            // the tile's two weight scales (+ pad)
-constexpr int Q_STAGE_BYTES = Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES + Q_WS_BYTES;
+constexpr int Q_STAGE_BYTES = Q_A_BYTES + Q_B_BYTES + Q_WS_BYTES;
 constexpr int Q_LPW_A = Q_A_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
 constexpr int Q_LPW_B = Q_B_BYTES / 1024 / (Q_WAVES_M * Q_WAVES_N);  // 4
-constexpr int Q_LOADS = Q_LPW_A + Q_LPW_B + 1;            // per wave per stage (+1: 32 row scales)
-constexpr int Q_LDS_PIPE = Q_NSTAGE * Q_STAGE_BYTES;      // 128 KB + 2 KB of scales
+constexpr int Q_ROW_LOADS = Q_LPW_A + Q_LPW_B;             // row loads per wave per stage
+// the activation scales of a group of up to 4 stages (16 bytes per row), in
+// a ring of 2 after the stage buffers
+constexpr int Q_XS_SLOT = Q_BM * 16;
+constexpr int Q_XS_OFF = Q_NSTAGE * Q_STAGE_BYTES;
+constexpr int Q_LDS_PIPE = Q_XS_OFF + 2 * Q_XS_SLOT;      // 128 KB + 8 KB of scales
 constexpr int Q_LDS_OUT = Q_BM * (Q_BN * 2 + 16);         // the down tile's bf16 outputs (132 KB)
 
 // Buffer resource word 3 for raw (unformatted) dword accesses on gfx9 parts.
@@ -211,12 +214,19 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
     }
     b_voff[i] = (uint32_t)wrow * (uint32_t)p.K + (uint32_t)(((lane & 7) ^ f8_swz_f(trow)) * 16);
   }
-  // activation scales: wave w fetches 32 of them into scale slots 32w ..
-  // 32w+31.  Slot p holds tile row (p/128)*128 + (p%4)*32 + (p%128)/4, so
-  // the four rows a lane's MFMA blocks use (wm*128 + 32 mi + fr, mi = 0..3)
-  // sit in one 16-byte piece and come in one read per stage.
+  // activation scales: wave w fetches the scales of 32 rows into scale slots
+  // 32w .. 32w+31, those of G consecutive stages at once (G = 4 when the
+  // stage count allows, else 1): 16 contiguous bytes of each row instead of
+  // 4 bytes of each row per stage, a quarter of the cache lines.  With G = 4
+  // slot p holds tile row p, and a lane reads its four rows' scales with
+  // four reads whose lanes step 16 bytes; with G = 1 slot p holds tile row
+  // (p/128)*128 + (p%4)*32 + (p%128)/4, so the four rows a lane's MFMA
+  // blocks use (wm*128 + 32 mi + fr, mi = 0..3) are the one 16-byte piece of
+  // slots wm*128 + 4 fr .. + 3.
+  const int G = (KT % 4 == 0) ? 4 : 1;
   const int xs_p = wave * 32 + (lane & 31);
-  const int xs_r = min(row_beg + (xs_p & ~127) + (xs_p & 3) * 32 + ((xs_p & 127) >> 2), row_end - 1);
+  const int xs_t = (G == 4) ? xs_p : (xs_p & ~127) + (xs_p & 3) * 32 + ((xs_p & 127) >> 2);
+  const int xs_r = min(row_beg + xs_t, row_end - 1);
   const uint32_t xs_row = p.gather ? (uint32_t)p.gather[xs_r] : (uint32_t)(xs_r - row_beg);
   const uint32_t xs_voff = xs_row * (uint32_t)KT * 4u;
   // weight scales: a tile uses two 128 x 128 scale blocks per stage, fetched
@@ -249,6 +259,15 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.A_scale + rb * KT), (short)0, 0x7fffffff, F8_BUF_DWORD3);
 
   auto stage_base = [&](int kt) { return smem + (kt % Q_NSTAGE) * Q_STAGE_BYTES; };
+  auto xs_slot = [&](int kt) { return smem + Q_XS_OFF + ((kt / G) % 2) * Q_XS_SLOT; };
+  // the group's scales, by the stage that starts it (lanes 0-31)
+  auto issue_xs = [&](int kt) {
+    if (kt % G != 0) return;
+    if (G == 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(xs_slot(kt) + wave_s * 32 * 16), 16, xs_voff, kt * 4, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(xs_slot(kt) + wave_s * 32 * 4), 4, xs_voff, kt * 4, 0, 0);
+  };
   // a wave's loads of stage kt in three parts (part 0: activation rows 0-1
   // and weight rows 0-1, part 1: the other rows, part 2: the scales), so
   // that they can be issued between the MFMA blocks of the stage before
@@ -264,9 +283,9 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + Q_A_BYTES + (wave_s * Q_LPW_B + i) * 1024), 16, b_voff[i], kb, 0, 0);
     } else {
       if (lane < 32)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES + wave_s * 128), 4, xs_voff, kt * 4, 0, 0);
+        issue_xs(kt);
       if (wave_s == 0 && lane < 2)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES), 4, ws_voff, kt * 4, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lptr_t)(st + Q_A_BYTES + Q_B_BYTES), 4, ws_voff, kt * 4, 0, 0);
     }
   };
   auto issue = [&](int kt) {
@@ -301,9 +320,14 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
       for (int kk = 0; kk < 2; ++kk) bq[ni][kk] = frag(bs, wn * Q_WTN + ni * 32 + fr, kk);
   };
   auto read_xs = [&](int kt) {
-    return *(const f32x4_t*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES + (wm * Q_WTM + fr * 4) * 4);
+    if (G == 1) return *(const f32x4_t*)(xs_slot(kt) + (wm * Q_WTM + fr * 4) * 4);
+    const uint8_t* g = xs_slot(kt) + (kt % 4) * 4 + (wm * Q_WTM + fr) * 16;
+    f32x4_t v;
+#pragma unroll
+    for (int mi = 0; mi < Q_MI; ++mi) v[mi] = *(const float*)(g + mi * 32 * 16);
+    return v;
   };
-  auto read_ws = [&](int kt) { return *(const f32x2_t*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES + Q_XS_BYTES); };
+  auto read_ws = [&](int kt) { return *(const f32x2_t*)(stage_base(kt) + Q_A_BYTES + Q_B_BYTES); };
   auto read_a = [&](int kt, int mi, i32x8_t (&aq)[2]) {
     const uint8_t* as = stage_base(kt);
 #pragma unroll
@@ -329,7 +353,8 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   i32x8_t bq[Q_NI][2], aq[2][2];
   issue(0);
   if (KT > 1) issue(1);
-  if (KT > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(Q_LOADS));
+  // stage 0 landed: stage 1 issued at least its Q_ROW_LOADS row loads after it
+  if (KT > 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(Q_ROW_LOADS));
   else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   f8_block_barrier();
   read_b(0, bq);
