@@ -507,8 +507,12 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 // of a byte times an fp32 scale -> two bf16, exact for every E8M0 scale), and
 // the product runs on v_mfma_f32_32x32x16_bf16.  Tile 128 x 256 (the format
 // serves weight-bound batches first), 8 waves in 2 x 4, each 64 x 64 = 2 x 2
-// MFMA blocks; k stages of 128 triple buffered in LDS: 32 KB of bf16 rows,
-// 16 KB of packed e2m1 rows and the weight rows' 4 scale bytes.
+// MFMA blocks; k stages of 128 triple buffered in LDS: 32 KB of bf16 rows
+// and 16 KB of packed e2m1 rows.  The weight rows' scale bytes (4 per row
+// per stage) come four stages at a time where the stage count allows: 16
+// contiguous bytes of each row instead of 4 bytes of each row per stage, a
+// quarter of the cache lines (per stage they were as many lines as the
+// weight codes).
 //
 // Inside a stage the 8 k16 steps need not walk k in order, only the same way
 // for both operands: at step s lane 32h + r takes k [64h + 8s, +8).  Its 8
@@ -535,14 +539,17 @@ struct W4Shape {
   static constexpr int WTM = BM / WAVES_M, WTN = W_BN / WAVES_N;    // wave tile, WTN = 64
   static constexpr int MI = WTM / 32, NI = WTN / 32;
   static constexpr int A_BYTES = BM * W_A_ROW;
-  static constexpr int BS_OFF = A_BYTES + W_B_BYTES;
-  static constexpr int STAGE = BS_OFF + W_BN * 4;
+  static constexpr int STAGE = A_BYTES + W_B_BYTES;
+  // scale slots after the stages: groups of 4 stages (16 bytes per row) in a
+  // ring of 2, or single stages (4 bytes per row) in a ring of 3
+  static constexpr int BS_OFF = NS * STAGE;
   static constexpr int LPW_A = A_BYTES / 1024 / NWAVES, LPW_B = W_B_BYTES / 1024 / NWAVES;
   static constexpr int BS_RPW = W_BN / NWAVES;                      // weight scale rows per wave
-  static constexpr int LOADS = LPW_A + LPW_B + 1;                   // per wave per stage
-  static constexpr int LDS = NS * STAGE;
+  static constexpr int LOADS = LPW_A + LPW_B;                       // row loads per wave per stage
+  static constexpr int LDS = BS_OFF + 2 * W_BN * 16;
   static_assert(LPW_A >= 1 && LPW_B >= 1 && BS_RPW <= 64, "W4A16 tile shape");
   static_assert((NS - 2) * LOADS < 64, "vmcnt range");
+  static_assert(BM != 32 || 2 * LDS <= 160 * 1024, "two 32-row workgroups share a CU");
 };
 
 // bf16 rows: 256 bytes, 16 chunks; chunk c of row r at c ^ (r & 15).
@@ -629,7 +636,20 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
   const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)WSexp, (short)0, 0x7fffffff, X_BUF_DWORD3);
 
   auto stage_base = [&](int kt) { return smem + (kt % W_NS) * W_STAGE; };
+  const int G = (KT % 4 == 0) ? 4 : 1;
+  auto bs_slot = [&](int kt) {
+    return smem + W_BS_OFF + (G == 4 ? ((kt / 4) % 2) * (W_BN * 16) : (kt % W_NS) * (W_BN * 4));
+  };
   auto issue = [&](int kt) {
+    // the stage's scale group first (when it starts one), then its rows
+    if (lane < W_BS_RPW && kt % G == 0) {
+      if (G == 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * W_BS_RPW * 16), 16, bs_voff,
+                                                 kt * 4, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * W_BS_RPW * 4), 4, bs_voff,
+                                                 kt * 4, 0, 0);
+    }
     uint8_t* st = stage_base(kt);
 #pragma unroll
     for (int i = 0; i < W_LPW_A; ++i)
@@ -639,9 +659,6 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
     for (int i = 0; i < W_LPW_B; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + W_A_BYTES + (wave_s * W_LPW_B + i) * 1024), 16,
                                                b_voff[i], kt * W_B_ROW, 0, 0);
-    if (lane < W_BS_RPW)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(st + W_BS_OFF + wave_s * W_BS_RPW * 4), 4, bs_voff,
-                                               kt * 4, 0, 0);
   };
 
   const int fr = lane & 31, fh = lane >> 5;
@@ -655,8 +672,9 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
   const int live_mi = min(max((row_end - (row_beg + wm_s * W_WTM) + 31) / 32, 0), W_MI);
 
   // stages 0 .. NS-2 in the prologue; iteration kt waits for stage kt (at
-  // most the NS-2 stages issued after it outstanding), publishes it, and
-  // issues stage kt+NS-1 into the buffer of stage kt-1
+  // most the NS-2 stages issued after it outstanding: at least W_LOADS row
+  // loads each), publishes it, and issues stage kt+NS-1 into the buffer of
+  // stage kt-1
 #pragma unroll
   for (int i = 0; i < W_NS - 1; ++i)
     if (i < KT) issue(i);
@@ -666,7 +684,7 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
     mx_block_barrier();
     if (kt + W_NS - 1 < KT) issue(kt + W_NS - 1);
     const uint8_t* st = stage_base(kt);
-    const uint32_t* bs_l = (const uint32_t*)(st + W_BS_OFF);
+    const uint8_t* bs_l = bs_slot(kt) + (kt % G) * 4;  // row r's scale dword at r * 4 G
 #pragma unroll
     for (int half = 0; half < 2; ++half) {     // steps 4*half .. 4*half+3: one weight chunk, one MX block
       u32x4_t wq[W_NI];
@@ -675,7 +693,7 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
       for (int ni = 0; ni < W_NI; ++ni) {
         const int row = wn * W_WTN + ni * 32 + fr;
         wq[ni] = *(const u32x4_t*)(st + W_A_BYTES + mx_b_off(row, 2 * fh + half));
-        wsc[ni] = e8m0_f32((bs_l[row] >> (8 * (2 * fh + half))) & 0xffu);
+        wsc[ni] = e8m0_f32((*(const uint32_t*)(bs_l + row * 4 * G) >> (8 * (2 * fh + half))) & 0xffu);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
