@@ -764,22 +764,29 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
       }
     }
   } else {
+    // The tile's outputs go through LDS (rows of 256 outputs plus 16 bytes
+    // of bank skew) so that each store moves whole rows: a lane's own
+    // accumulators cover 4 columns of each of its rows, which as direct
+    // stores would touch every output line 8 or 16 times.
+    constexpr int ES = OUT_BF16 ? 2 : 4;
+    constexpr int PITCH = W_BN * ES + 16;
+    static_assert(W_BM * PITCH <= W4Shape<W_BM>::LDS, "staged output tile exceeds LDS");
+    __syncthreads();  // the stage buffers are free
 #pragma unroll
     for (int ni = 0; ni < W_NI; ++ni)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = nb * W_BN + wn * W_WTN + ni * 32 + 8 * q + 4 * fh;
-        if (n >= p.N) continue;
+        const int lc = wn * W_WTN + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
+        const int n = nb * W_BN + lc;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias_e) {
+        if (bias_e && n < p.N) {
           const uint2 b2 = *(const uint2*)(bias_e + n);
           bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
           bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
         }
 #pragma unroll
         for (int mi = 0; mi < W_MI; ++mi) {
-          const int row = row_beg + wm * W_WTM + mi * 32 + fr;
-          if (row >= row_end) continue;
+          uint8_t* dst = smem + (wm * W_WTM + mi * 32 + fr) * PITCH + lc * ES;
           float v[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * sc + bd[c];
@@ -787,13 +794,23 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
             uint2 w;
             w.x = pack_bf16x2_rne(v[0], v[1]);
             w.y = pack_bf16x2_rne(v[2], v[3]);
-            *(uint2*)((uint16_t*)p.out + (int64_t)row * p.N + n) = w;
+            *(uint2*)dst = w;
           } else {
-            const f32x4_t w = {v[0], v[1], v[2], v[3]};
-            *(f32x4_t*)((float*)p.out + (int64_t)row * p.N + n) = w;
+            *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
           }
         }
       }
+    __syncthreads();
+    // a row is W_BN * ES bytes: 32 (bf16) or 64 (fp32) lanes of 16 bytes
+    constexpr int LPR = W_BN * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per store
+    constexpr int NWAVES = W4Shape<W_BM>::NWAVES;
+    const int cpart = lane % LPR;
+    const int n = nb * W_BN + cpart * (16 / ES);
+    for (int r = wave * RPI + lane / LPR; r < W_BM; r += NWAVES * RPI) {
+      const int row = row_beg + r;
+      if (row < row_end && n < p.N)
+        *(u32x4_t*)((uint8_t*)p.out + ((int64_t)row * p.N + n) * ES) = *(const u32x4_t*)(smem + r * PITCH + cpart * 16);
+    }
   }
 }
 
