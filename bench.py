@@ -94,6 +94,17 @@ def algorithmic_work(cfg) -> dict:
             "build_indices_bytes": idx_bytes, "combine_bytes": comb_bytes}
 
 
+def fused_ffn_bytes(cfg, used: int) -> int:
+    """HBM bytes of one single-launch FFN call in which `used` experts have
+    rows: their gate_up and down weights (MX: packed E2M1 plus one E8M0 byte
+    per 32), the R rows of x read, A written and read back, O written."""
+    R, H, D = cfg.T * cfg.k, cfg.H, cfg.D
+    if cfg.operand_dtype == "mxfp4":
+        w = (2 * D * H + H * D) * (1 / 2 + 1 / 32)
+        return int(used * w + R * H * (1 + 1 / 32) + 2 * R * D * (1 + 1 / 32) + R * H * 2)
+    return used * (2 * D * H + H * D) * 2 + R * H * 2 + 2 * R * D * 2 + R * H * 4
+
+
 def measure_ceilings(moe, torch) -> dict:
     """Practical ceilings on this chip, measured with the library's probes
     right after the timed steps (same clocks): an MFMA loop on every CU for
@@ -564,6 +575,8 @@ def main():
     ap.add_argument("--layout", choices=("out_in", "in_out"), default="out_in",
                     help="bf16 expert weights as the stacked [E, hidden, 2 moe_dim] / [E, moe_dim, hidden] tensors "
                          "themselves (in_out) or their transposed views, laid out once at load (out_in)")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="run a single-launch workload's FFN as the two grouped GEMM launches instead (comparison)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass of the routed experts (bf16 workloads) instead of the forward")
     ap.add_argument("--scale-tokens", type=int, default=1, metavar="N",
@@ -617,7 +630,7 @@ def main():
         print("bench.py --layout in_out: the stacked layout is read by the two-launch bf16 FFN",
               file=sys.stderr)
         sys.exit(2)
-    layer = moe.MoELayer(cfg, inp, layout=layout)
+    layer = moe.MoELayer(cfg, inp, layout=layout, fused=False if args.two_launch else None)
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
     # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
@@ -685,19 +698,19 @@ def main():
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": "grouped gate_up GEMM + fused activation (MXFP4 weights, bf16 activations)",
                 "bytes_per_launch": gu_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_gu, 4)}
-    if getattr(cfg, "fused", False):
+    if layer.fused:
         # the FFN is one launch (gate_up and down together) on a decode-sized
-        # batch: bound by streaming the bf16 weights of the experts that have
+        # batch: bound by streaming the weights of the experts that have
         # rows, plus x rows in, A out and back in, O out
         off = layer.last_offsets.cpu()
         used = int(((off[1:] - off[:-1]) > 0).sum())
-        ffn_bytes = (used * (2 * cfg.D * cfg.H + cfg.H * cfg.D) * 2 + R * cfg.H * 2 + 2 * R * cfg.D * 2
-                     + R * cfg.H * 4)
+        ffn_bytes = fused_ffn_bytes(cfg, used)
         t_ffn = t_gu + t_dn
         gbs = ffn_bytes / (t_ffn * 1e-3) / 1e9
+        kind = "MXFP4 weights, MXFP8 activations" if cfg.operand_dtype == "mxfp4" else "bf16"
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
-                "kernel": "single-launch expert FFN (gate_up + activation + down, bf16)",
+                "kernel": f"single-launch expert FFN (gate_up + activation + down, {kind})",
                 "bytes_per_launch": ffn_bytes, "experts_with_rows": used, "avg_launch_ms": round(t_ffn, 4)}
     mfma_key = "mfma_bf16_tflops" if peak == PEAK_BF16_TFLOPS else "mfma_fp8_tflops"
     roof = _with_measured(roof, ceil, mfma_key)

@@ -479,7 +479,8 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
   REQUIRE(H >= 64 && H % 64 == 0, "moe_grouped_ffn_fused: hidden_dim must be a positive multiple of 64 (got %d)", H);
   REQUIRE(D >= 128 && D % 128 == 0, "moe_grouped_ffn_fused: moe_dim must be a positive multiple of 128 (got %d)", D);
   REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn_fused: n_local_experts must be in [1, 1024] (got %d)", L);
-  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16, "moe_grouped_ffn_fused: operand_dtype must be BF16");
+  const bool mx = a->operand_dtype == MOE_DTYPE_MXFP4_W4A8;
+  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16 || mx, "moe_grouped_ffn_fused: operand_dtype must be BF16 or MXFP4_W4A8");
   REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn_fused: expert_offsets is required");
   REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI || a->activation == MOE_ACT_GELU_TANH,
           "moe_grouped_ffn_fused: unknown activation %d", a->activation);
@@ -504,9 +505,22 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
               aligned16(a->act_workspace) && aligned16(a->expert_out) && aligned16(a->b_gate_up) &&
               aligned16(a->b_down),
           "moe_grouped_ffn_fused: tensors must be 16-byte aligned");
-  REQUIRE((int64_t)R * H * 2 < ((int64_t)1 << 31) && (int64_t)R * D * 2 < ((int64_t)1 << 31) &&
-              (int64_t)2 * D * H * 2 < ((int64_t)1 << 31),
-          "moe_grouped_ffn_fused: x_perm, the activation buffer and one expert's weights must each be under 2 GiB");
+  // bytes per activation element; one expert's gate_up weights: 2D rows of H elements
+  const int64_t es = mx ? 1 : 2;
+  const int64_t wbytes = mx ? (int64_t)D * H : (int64_t)2 * D * H * 2;
+  const int64_t x_rows = gather && a->num_tokens > 0 ? a->num_tokens : R;
+  REQUIRE(x_rows * H * es < ((int64_t)1 << 31) && (int64_t)R * D * es < ((int64_t)1 << 31) &&
+              wbytes < ((int64_t)1 << 31),
+          "moe_grouped_ffn_fused: x (or x_perm), the activation buffer and one expert's weights must each be under 2 GiB");
+  if (mx) {
+    REQUIRE(H % 128 == 0, "moe_grouped_ffn_fused: MX needs hidden_dim a multiple of 128 (got %d)", H);
+    REQUIRE(a->x_perm_scale != nullptr,
+            "moe_grouped_ffn_fused: MX takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
+    REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
+            "moe_grouped_ffn_fused: MXFP4 weights need w_gate_up_scale and w_down_scale");
+    REQUIRE(aligned16(a->x_perm_scale) && aligned16(a->w_gate_up_scale) && aligned16(a->w_down_scale),
+            "moe_grouped_ffn_fused: scale tensors must be 16-byte aligned");
+  }
   if (a->w_gate_up_layout != MOE_WEIGHT_OUT_IN || a->w_down_layout != MOE_WEIGHT_OUT_IN)
     return fail(MOE_ERR_UNSUPPORTED, "moe_grouped_ffn_fused: weights must use the OUT_IN layout");
   const int64_t need = moe_ffn_fused_workspace_bytes(R, H, D, L);
@@ -514,6 +528,34 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "moe_grouped_ffn_fused: act_workspace needs %lld bytes (got %lld)",
                 (long long)need, (long long)a->act_workspace_bytes);
   if (R == 0) return ok();
+  if (mx) {
+    moe::FfnMxParams q{};
+    q.offsets = a->expert_offsets;
+    q.L = L;
+    q.H = H;
+    q.D = D;
+    q.max_rows = R;
+    q.fmt = a->gate_up_format;
+    q.x_perm = (const uint8_t*)(a->x_perm ? a->x_perm : a->x);
+    q.x_scale = (const uint8_t*)a->x_perm_scale;
+    q.sorted_token = a->x_perm ? nullptr : a->sorted_token;
+    q.w_gate_up = (const uint8_t*)a->w_gate_up;
+    q.w_gate_up_scale = (const uint8_t*)a->w_gate_up_scale;
+    q.w_down = (const uint8_t*)a->w_down;
+    q.w_down_scale = (const uint8_t*)a->w_down_scale;
+    q.b_gate_up = (const uint16_t*)a->b_gate_up;
+    q.b_down = (const uint16_t*)a->b_down;
+    q.gate_up_scales = a->gate_up_expert_scales;
+    q.down_scales = a->down_expert_scales;
+    q.act_kind = a->activation;
+    q.alpha = a->alpha;
+    q.limit = a->limit;
+    q.out = a->expert_out;
+    q.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
+    q.events = (hipEvent_t const*)a->timing_events;
+    return hip_status(moe::launch_ffn_fused_mx(q, a->act_workspace, a->act_workspace_bytes, (hipStream_t)stream),
+                      "moe_grouped_ffn_fused");
+  }
   moe::FfnBf16Params p{};
   p.offsets = a->expert_offsets;
   p.L = L;

@@ -32,10 +32,18 @@
 // caller zeroes them once, when the workspace is allocated.
 //
 // Tiles are 32 x 256 with 4 waves (32 x 64 each: the gate and up columns of
-// 32 outputs for L1), k stages of 64 bf16, 4 stages deep in LDS through
-// buffer loads: the batch is bound by streaming the weights.
+// 32 outputs for L1).  Two operand kinds share the schedule, the tile and
+// the epilogue arithmetic:
+//   bf16:  k stages of 64 bf16, 4 stages deep in LDS through buffer loads,
+//          one workgroup per CU;
+//   MX:    MXFP4 weights x MXFP8 activations (the mega_ffn page's
+//          block-scaled form), k stages of 128 on the scaled MFMA, 3 deep,
+//          two workgroups per CU; L1 re-quantises A to MXFP8 before L2
+//          reads it.
+// Either way the batch is bound by streaming the weights.
 #include "common.h"
 #include "kernels.h"
+#include "mx_common.h"
 
 namespace moe {
 
@@ -69,6 +77,176 @@ __device__ __forceinline__ void f_block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// ---------------------------------------------------------------- schedule
+// Shared by both kernels: 256 threads, 32-row blocks.
+
+// Prefix of 32-row blocks per expert into s_mbp[0 .. L] (wave 0), then a
+// barrier.
+__device__ __forceinline__ void fused_block_prefix(const int32_t* offsets, int L, int32_t* s_mbp) {
+  const int lane = threadIdx.x & 63;
+  if ((threadIdx.x >> 6) == 0) {
+    const int per = (L + 63) / 64;
+    const int e0 = lane * per;
+    int sum = 0;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < L) sum += (offsets[e + 1] - offsets[e] + F_BM - 1) / F_BM;
+    }
+    int inc = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, MOE_WAVE);
+      if (lane >= o) inc += v;
+    }
+    int run = inc - sum;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e < L) {
+        s_mbp[e] = run;
+        run += (offsets[e + 1] - offsets[e] + F_BM - 1) / F_BM;
+      }
+    }
+    if (lane == 63) s_mbp[L] = inc;
+  }
+  __syncthreads();
+}
+
+struct FusedItem {
+  bool l2;
+  int e, nb, part;
+  int gm;                // global row block: its arrival counter
+  int row_beg, row_end;
+};
+
+// Work item `item` of the queue: first the n1 L1 items (expert, row block,
+// one of NB1 blocks of 128 outputs), then the L2 items (expert, row block,
+// one of NB2 blocks of 256 outputs, one of S parts of K); within an expert,
+// output-block-major.  Every field is wave-uniform.
+__device__ __forceinline__ FusedItem fused_item(int item, int n1, int NB1, int NB2, int S, int L,
+                                                const int32_t* s_mbp, const int32_t* offsets) {
+  FusedItem t;
+  t.l2 = item >= n1;
+  const int NB = t.l2 ? NB2 * S : NB1;
+  const int it = t.l2 ? item - n1 : item;
+  int lo = 0, hi = L - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_mbp[mid] * NB <= it) lo = mid;
+    else hi = mid - 1;
+  }
+  t.e = __builtin_amdgcn_readfirstlane(lo);
+  const int nmb = s_mbp[t.e + 1] - s_mbp[t.e];
+  const int local = __builtin_amdgcn_readfirstlane(it - s_mbp[t.e] * NB);
+  const int q_nb = local / nmb, mb = local % nmb;
+  t.nb = t.l2 ? q_nb / S : q_nb;
+  t.part = t.l2 ? q_nb % S : 0;
+  t.gm = s_mbp[t.e] + mb;
+  t.row_beg = __builtin_amdgcn_readfirstlane(offsets[t.e] + mb * F_BM);
+  t.row_end = __builtin_amdgcn_readfirstlane(offsets[t.e + 1]);
+  return t;
+}
+
+// Waits until `counter` reaches `need`: one thread spins on it (relaxed: no
+// cache invalidation per poll), then acquires once; the barrier orders the
+// other waves' loads after that acquire.  The spin is bounded: on timeout it
+// sets the error word and goes on.
+__device__ __forceinline__ void fused_wait(const int32_t* counter, int need, int32_t* err) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+      __builtin_amdgcn_s_sleep(8);
+      if (++spins > F_SPIN_LIMIT) {
+        __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+}
+
+// Counts the workgroup's stores in: the barrier orders every wave's stores
+// before thread 0's release fence, which writes them back once for the
+// workgroup; the count then moves.
+__device__ __forceinline__ void fused_count_in(int32_t* counter) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// One part of a split L2 tile: writes the part's fp32 partial tile to its
+// slot (acc[j/4][4(j%4) + c] goes to float 4(j*F_NT + tid) + c, the same
+// place in every part) and counts it in at `done`.  The workgroup whose part
+// comes last resets the counter for the next launch, adds the S parts in
+// part order (its own from registers) into acc and returns true; the others
+// return false.  No part waits for another.
+__device__ __forceinline__ bool fused_split_reduce(f32x16_t (&acc)[2], float* slots, int part, int S, int32_t* done,
+                                                   int32_t* s_flag) {
+  const int tid = threadIdx.x;
+  float* mine = slots + (int64_t)part * F_PART_FLOATS;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const f32x4_t v = {acc[j / 4][4 * (j % 4)], acc[j / 4][4 * (j % 4) + 1], acc[j / 4][4 * (j % 4) + 2],
+                       acc[j / 4][4 * (j % 4) + 3]};
+    *(f32x4_t*)(mine + 4 * (j * F_NT + tid)) = v;
+  }
+  // release as for A; the last part acquires the others' partials
+  __syncthreads();
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int n = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[0] = n == S - 1;
+    if (n == S - 1) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // every part has counted in: reset for the next launch
+      __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (!s_flag[0]) return false;
+  f32x16_t sum[2];
+  for (int pp = 0; pp < S; ++pp) {
+    if (pp == part) {
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum[ni][r] = pp ? sum[ni][r] + acc[ni][r] : acc[ni][r];
+    } else {
+      const float* src = slots + (int64_t)pp * F_PART_FLOATS;
+      f32x4_t v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *(const f32x4_t*)(src + 4 * (j * F_NT + tid));
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sum[j / 4][4 * (j % 4) + c] = pp ? sum[j / 4][4 * (j % 4) + c] + v[j][c] : v[j][c];
+    }
+  }
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni) acc[ni] = sum[ni];
+  return true;
+}
+
+// The last workgroup out leaves the control words at zero for the next
+// launch (the split counters were reset by their last parts).
+__device__ __forceinline__ void fused_exit(int32_t* ctl, int32_t* arrive, int total_mb, int32_t* s_flag) {
+  const int tid = threadIdx.x;
+  if (tid == 0)
+    s_flag[0] = __hip_atomic_fetch_add(ctl + 1, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (s_flag[0]) {
+    for (int i = tid; i < total_mb; i += F_NT) __hip_atomic_store(arrive + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      __hip_atomic_store(ctl, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctl + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- bf16
 struct FusedArgs {
   const int32_t* offsets;
   int L, H, D;
@@ -100,39 +278,14 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int L = p.L;
   int32_t* queue = p.ctl;
-  int32_t* exits = p.ctl + 1;
   int32_t* err = p.ctl + 2;
   int32_t* arrive = p.arrive;
   int32_t* tile_done = p.ctl + 4;
 
-  if (wave == 0) {
-    const int per = (L + 63) / 64;
-    const int e0 = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) sum += (p.offsets[e + 1] - p.offsets[e] + F_BM - 1) / F_BM;
-    }
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, MOE_WAVE);
-      if (lane >= o) inc += v;
-    }
-    int run = inc - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) {
-        s_mbp[e] = run;
-        run += (p.offsets[e + 1] - p.offsets[e] + F_BM - 1) / F_BM;
-      }
-    }
-    if (lane == 63) s_mbp[L] = inc;
-  }
-  __syncthreads();
+  fused_block_prefix(p.offsets, L, s_mbp);
   // more rows than max_rows: no counter may be touched, so do nothing
   const bool too_many = s_mbp[L] > p.row_blocks;
-  if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(p.ctl + 2, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int total_mb = too_many ? 0 : s_mbp[L];
   const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
   const int n2 = total_mb * NB2;
@@ -145,42 +298,10 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
     if (item >= n_all) break;
-    const bool l2 = item >= n1;
-    const int NB = l2 ? NB2 * S : NB1;
-    const int it = l2 ? item - n1 : item;
-    int lo = 0, hi = L - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (s_mbp[mid] * NB <= it) lo = mid;
-      else hi = mid - 1;
-    }
-    const int e = __builtin_amdgcn_readfirstlane(lo);
-    const int nmb = s_mbp[e + 1] - s_mbp[e];
-    const int local = __builtin_amdgcn_readfirstlane(it - s_mbp[e] * NB);
-    const int q_nb = local / nmb, mb = local % nmb;
-    const int nb = l2 ? q_nb / S : q_nb;
-    const int part = l2 ? q_nb % S : 0;
-    const int gm = s_mbp[e] + mb;  // global row block: its arrival counter
-    const int row_beg = __builtin_amdgcn_readfirstlane(p.offsets[e] + mb * F_BM);
-    const int row_end = __builtin_amdgcn_readfirstlane(p.offsets[e + 1]);
-
-    if (l2) {
-      // one thread spins on the counter (relaxed: no cache invalidation per
-      // poll), then acquires once; the barrier orders the other waves' loads
-      // of A after that acquire
-      if (tid == 0) {
-        int spins = 0;
-        while (__hip_atomic_load(arrive + gm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < NB1) {
-          __builtin_amdgcn_s_sleep(8);
-          if (++spins > F_SPIN_LIMIT) {
-            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      }
-      __syncthreads();
-    }
+    const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
+    const bool l2 = t.l2;
+    const int e = t.e, nb = t.nb, part = t.part, gm = t.gm, row_beg = t.row_beg, row_end = t.row_end;
+    if (l2) fused_wait(arrive + gm, NB1, err);
 
     // ---- operands of this item
     const int K = l2 ? p.D : p.H;
@@ -290,67 +411,14 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
           *(uint2*)(p.act + (int64_t)row * p.D + oc) = v;
         }
       }
-      // publish this part of the row block.  The barrier orders every
-      // wave's A stores before thread 0's release fence, which writes them
-      // back once for the workgroup; the count then moves.
-      __syncthreads();
-      if (tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(arrive + gm, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
+      fused_count_in(arrive + gm);  // this part of the row block is published
     } else {
       if (S > 1) {
-        // this part's partial tile, then count it in; acc[j/4][4(j%4) + c]
-        // goes to float 4(j*F_NT + tid) + c of the slot, the same place in
-        // every part
         const int t2 = gm * NB2 + nb;
-        float* slots = p.part + (int64_t)t2 * S * F_PART_FLOATS;
-        float* mine = slots + (int64_t)part * F_PART_FLOATS;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const f32x4_t v = {acc[j / 4][4 * (j % 4)], acc[j / 4][4 * (j % 4) + 1], acc[j / 4][4 * (j % 4) + 2],
-                             acc[j / 4][4 * (j % 4) + 3]};
-          *(f32x4_t*)(mine + 4 * (j * F_NT + tid)) = v;
-        }
-        // release as for A; the last part acquires the others' partials
-        __syncthreads();
-        if (tid == 0) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          const int done = __hip_atomic_fetch_add(tile_done + t2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          s_item[1] = done == S - 1;
-          if (done == S - 1) {
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            // every part has counted in: reset for the next launch
-            __hip_atomic_store(tile_done + t2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
-        __syncthreads();
-        if (!s_item[1]) {
+        if (!fused_split_reduce(acc, p.part + (int64_t)t2 * S * F_PART_FLOATS, part, S, tile_done + t2, s_item + 1)) {
           __syncthreads();
           continue;
         }
-        // sum the parts in part order
-        f32x16_t sum[2];
-        for (int pp = 0; pp < S; ++pp) {
-          if (pp == part) {
-#pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-              for (int r = 0; r < 16; ++r) sum[ni][r] = pp ? sum[ni][r] + acc[ni][r] : acc[ni][r];
-          } else {
-            const float* src = slots + (int64_t)pp * F_PART_FLOATS;
-            f32x4_t v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = *(const f32x4_t*)(src + 4 * (j * F_NT + tid));
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-              for (int c = 0; c < 4; ++c)
-                sum[j / 4][4 * (j % 4) + c] = pp ? sum[j / 4][4 * (j % 4) + c] + v[j][c] : v[j][c];
-          }
-        }
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[ni] = sum[ni];
       }
       const float sc = p.s_d ? p.s_d[e] : 1.0f;
       const uint16_t* bias = p.b_d ? p.b_d + (int64_t)e * p.H : nullptr;
@@ -383,18 +451,327 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     __syncthreads();  // the stage buffers and the item word are reused by the next item
   }
 
-  // the last workgroup out leaves the control words at zero for the next launch
-  if (tid == 0)
-    s_item[1] = __hip_atomic_fetch_add(exits, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
-  __syncthreads();
-  if (s_item[1]) {
-    for (int i = tid; i < total_mb; i += F_NT) __hip_atomic_store(arrive + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    // (the split counters were reset by their last parts)
-    if (tid == 0) {
-      __hip_atomic_store(queue, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(exits, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  fused_exit(p.ctl, arrive, total_mb, s_item + 1);
+}
+
+// ---------------------------------------------------------------- MX
+// MXFP4 weights x MXFP8 activations.  A k stage of 128: 4 KB of e4m3
+// activation rows and 16 KB of packed e2m1 weight rows, 3 stages deep, plus
+// the rows' scale dwords, which come four stages per 16-byte load where the
+// item's stages allow (else one stage per 4-byte load).  With 70 KB of LDS
+// two workgroups share a CU, so each SIMD holds a second wave that covers
+// the first one's LDS reads and MFMAs while both wait on the weight stream.
+constexpr int M_NS = 3;
+constexpr int M_A_BYTES = F_BM * MX_A_ROW;              // 4 KB
+constexpr int M_B_BYTES = F_BN * MX_B_ROW;              // 16 KB
+constexpr int M_STAGE = M_A_BYTES + M_B_BYTES;
+constexpr int M_LPW_B = M_B_BYTES / 1024 / F_NW;        // 1 KB weight row loads per wave per stage: 4
+constexpr int M_LOADS = 1 + M_LPW_B;                    // row loads per wave per stage
+constexpr int M_AS_OFF = M_NS * M_STAGE;                // activation scales: 2 slots x 32 rows x 16 bytes
+constexpr int M_BS_OFF = M_AS_OFF + 2 * F_BM * 16;      // weight scales: 2 slots x 256 rows x 16 bytes
+constexpr int M_PIPE = M_BS_OFF + 2 * F_BN * 16;        // 69 KB
+constexpr int M_WG_PER_CU = 2;
+constexpr int M_CPITCH = 128 + 16;                      // staged A codes: 128 bytes per row + bank skew
+static_assert(M_NS * F_BM * 4 <= 2 * F_BM * 16 && M_NS * F_BN * 4 <= 2 * F_BN * 16, "single-stage scale slots fit");
+static_assert((M_NS - 2) * M_LOADS < 64, "vmcnt range");
+static_assert(M_WG_PER_CU * (M_PIPE + (1024 + 4) * 4) <= 160 * 1024, "two MX workgroups share a CU");
+static_assert(F_BM * M_CPITCH + F_BM * 4 <= M_NS * M_STAGE, "staged A codes and scales fit the stages");
+static_assert(F_BM * (F_BN * 4 + 16) <= M_NS * M_STAGE, "a staged fp32 output tile fits the stages");
+
+struct FusedMxArgs {
+  const int32_t* offsets;
+  int L, H, D;
+  const uint8_t* x;            // e4m3 [T, H] gathered through sorted_token, or [R, H] rows (sorted_token null)
+  const uint8_t* x_scale;      // E8M0 [T or R, H/32]
+  const int32_t* sorted_token;
+  const uint8_t* w_gu;         // packed e2m1 OUT_IN [L, 2D, H/2]
+  const uint8_t* w_gu_scale;   // E8M0 [L, 2D, H/32]
+  const uint8_t* w_d;          // packed e2m1 OUT_IN [L, H, D/2]
+  const uint8_t* w_d_scale;    // E8M0 [L, H, D/32]
+  const uint16_t* b_gu;        // [L, 2D] or null
+  const uint16_t* b_d;         // [L, H] or null
+  const float* s_gu;           // [L] or null
+  const float* s_d;
+  float alpha, limit;
+  uint8_t* act;                // A, e4m3 codes [R, D]
+  uint8_t* act_scale;          // A, E8M0 [R, D/32]
+  void* out;                   // O [R, H]
+  int32_t* ctl;                // as FusedArgs
+  int32_t* arrive;
+  float* part;
+  int S, row_blocks, tiles_cap;
+};
+
+template <int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int32_t* s_mbp = (int32_t*)(smem + M_PIPE);  // row-block prefix per expert, kept for the whole launch
+  int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-part / last-out flag
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int L = p.L;
+  int32_t* err = p.ctl + 2;
+  int32_t* tile_done = p.ctl + 4;
+
+  fused_block_prefix(p.offsets, L, s_mbp);
+  const bool too_many = s_mbp[L] > p.row_blocks;
+  if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int total_mb = too_many ? 0 : s_mbp[L];
+  const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
+  const int n2 = total_mb * NB2;
+  const int S = (p.S > 1 && n2 <= p.tiles_cap) ? p.S : 1;
+  const int n1 = total_mb * NB1, n_all = n1 + n2 * S;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  for (;;) {
+    if (tid == 0) s_item[0] = atomicAdd(p.ctl, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n_all) break;
+    const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
+    const bool l2 = t.l2;
+    const int e = t.e, nb = t.nb, part = t.part, gm = t.gm, row_beg = t.row_beg, row_end = t.row_end;
+    if (l2) fused_wait(p.arrive + gm, NB1, err);
+
+    // ---- operands of this item.  K stages ks = kt0 + kt of the whole row.
+    const int K = l2 ? p.D : p.H;
+    const int KS = K / MX_BK;
+    const int parts = l2 ? S : 1;
+    const int kt0 = part * KS / parts;
+    const int KT = (part + 1) * KS / parts - kt0;
+    // scale groups of 4 stages: 16-byte aligned rows (KS % 4 == 0) and whole
+    // groups inside this item's stages
+    const int G = (KS % 4 == 0 && kt0 % 4 == 0 && KT % 4 == 0) ? 4 : 1;
+    const uint32_t srow = (uint32_t)K / 32u;  // scale bytes per row
+    const int32_t* gather = l2 ? nullptr : p.sorted_token;
+    const uint8_t* a_base = l2 ? p.act : p.x;
+    const uint8_t* as_base = l2 ? p.act_scale : p.x_scale;
+    const uint8_t* b_base = l2 ? p.w_d + (int64_t)e * p.H * (p.D / 2) : p.w_gu + (int64_t)e * 2 * p.D * (p.H / 2);
+    const uint8_t* bs_base =
+        l2 ? p.w_d_scale + (int64_t)e * p.H * (p.D / 32) : p.w_gu_scale + (int64_t)e * 2 * p.D * (p.H / 32);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)as_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)bs_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    // weight row of tile row trow: L1 wave column q holds 32 gate rows, then
+    // the matching 32 up rows; L2 256 consecutive rows (past H: the last)
+    auto w_row = [&](int trow) -> int {
+      if (l2) return min(nb * F_BN + trow, p.H - 1);
+      const int q = trow / 64, rr = trow % 64, isup = rr / 32, j = rr % 32;
+      const int oc = nb * 128 + q * 32 + j;
+      return (FMT == 0) ? (isup ? p.D + oc : oc) : (2 * oc + isup);
+    };
+    // A: wave w loads tile rows 8w .. 8w+7 (1 KB = 8 rows x 8 chunks; rows
+    // past the expert's end read zeros) and, by lanes 0-7, their scale
+    // dwords (rows past the end repeat the last one; never used).  B: wave w
+    // loads rows 64w .. 64w+63 (16 rows x 4 chunks per 1 KB) and their scale
+    // dwords, one row per lane.
+    uint32_t a_voff, as_voff, b_voff[M_LPW_B], bs_voff;
+    {
+      const int trow = wave * 8 + (lane >> 3);
+      const int r = row_beg + trow;
+      if (r < row_end) {
+        const uint32_t ar = gather ? (uint32_t)gather[r] : (uint32_t)r;
+        a_voff = ar * (uint32_t)K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
+      } else {
+        a_voff = F_OOB;
+      }
+      const int sr = min(row_beg + wave * 8 + (lane & 7), row_end - 1);
+      as_voff = (gather ? (uint32_t)gather[sr] : (uint32_t)sr) * srow;
     }
+#pragma unroll
+    for (int i = 0; i < M_LPW_B; ++i) {
+      const int trow = (wave * M_LPW_B + i) * 16 + (lane >> 2);
+      b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+    }
+    bs_voff = (uint32_t)w_row(wave * 64 + lane) * srow;
+
+    // scale group g = kt / 4 in slot g % 2 (rows 16 bytes apart), or stage
+    // kt in slot kt % 3 (rows 4 bytes apart): row r's dword of stage kt at
+    // r * 4 G + (kt % G) * 4
+    auto as_slot = [&](int kt) {
+      return smem + M_AS_OFF + (G == 4 ? ((kt / 4) % 2) * (F_BM * 16) : (kt % M_NS) * (F_BM * 4));
+    };
+    auto bs_slot = [&](int kt) {
+      return smem + M_BS_OFF + (G == 4 ? ((kt / 4) % 2) * (F_BN * 16) : (kt % M_NS) * (F_BN * 4));
+    };
+    auto issue = [&](int kt) {
+      const int ks = kt0 + kt;
+      // the stage's scale group first (when it starts one), then its rows
+      if (kt % G == 0) {
+        if (G == 4) {
+          if (lane < 8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(as_slot(kt) + wave_s * 8 * 16), 16, as_voff,
+                                                     ks * 4, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 16), 16, bs_voff,
+                                                   ks * 4, 0, 0);
+        } else {
+          if (lane < 8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(as_slot(kt) + wave_s * 8 * 4), 4, as_voff,
+                                                     ks * 4, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 4), 4, bs_voff,
+                                                   ks * 4, 0, 0);
+        }
+      }
+      uint8_t* st = smem + (kt % M_NS) * M_STAGE;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + wave_s * 1024), 16, a_voff, ks * MX_A_ROW, 0, 0);
+#pragma unroll
+      for (int i = 0; i < M_LPW_B; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + M_A_BYTES + (wave_s * M_LPW_B + i) * 1024), 16,
+                                                 b_voff[i], ks * MX_B_ROW, 0, 0);
+    };
+
+    f32x16_t acc[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ni][r] = 0.0f;
+    // stages 0 .. NS-2 in the prologue; iteration kt waits for stage kt (the
+    // stage after it may stay in flight: at least M_LOADS loads), publishes
+    // it, and issues stage kt+2 into the buffer of stage kt-1
+#pragma unroll
+    for (int i = 0; i < M_NS - 1; ++i)
+      if (i < KT) issue(i);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + M_NS - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm((M_NS - 2) * M_LOADS));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      f_block_barrier();
+      if (kt + M_NS - 1 < KT) issue(kt + M_NS - 1);
+      const uint8_t* st = smem + (kt % M_NS) * M_STAGE;
+      const int sg = (kt % G) * 4;
+      const uint32_t as4 = *(const uint32_t*)(as_slot(kt) + sg + fr * 4 * G);
+      uint32_t bs4[2];
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) bs4[ni] = *(const uint32_t*)(bs_slot(kt) + sg + (wave * 64 + ni * 32 + fr) * 4 * G);
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        // k step kk covers MX blocks 2kk and 2kk+1; lane half fh passes block 2kk+fh's scale
+        const i32x8_t aq = mx_frag_a(st, fr, kk, fh);
+        const int asc = (int)((as4 >> (8 * (2 * kk + fh))) & 0xffu);
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const i32x8_t bq = mx_frag_b(st + M_A_BYTES, wave * 64 + ni * 32 + fr, kk, fh);
+          const int bsc = (int)((bs4[ni] >> (8 * (2 * kk + fh))) & 0xffu);
+          acc[ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq, aq, acc[ni], 4, 0, 0, bsc, 0, asc);
+        }
+      }
+    }
+
+    // ---- epilogue.  acc[ni][4q + c] is C[row][col], row = fr, col = wave*64 + ni*32 + 8q + 4fh + c
+    if (!l2) {
+      // block 0 holds the gate columns, block 1 the up columns of the wave's
+      // 32 outputs, which are one MX block of each row: the 16 values of a
+      // lane and the 16 of lane xor 32.  Re-quantised as the two-launch MX
+      // gate_up does: shared exponent floor(log2 amax) - 8, codes RNE.
+      const float sc = p.s_gu ? p.s_gu[e] : 1.0f;
+      const uint16_t* bias = p.b_gu ? p.b_gu + (int64_t)e * 2 * p.D : nullptr;
+      float a[16];
+      float m = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int oc = nb * 128 + wave * 32 + 8 * q + 4 * fh;  // first of 4 outputs
+        float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias) {
+          if (FMT == 0) {
+            const uint2 g2 = *(const uint2*)(bias + oc), u2 = *(const uint2*)(bias + p.D + oc);
+            bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
+            bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
+            bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
+            bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
+          } else {
+            const u32x4_t b4 = *(const u32x4_t*)(bias + 2 * oc);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              bg[c] = bf16_to_f32(b4[c] & 0xffffu);
+              bu[c] = bf16_to_f32(b4[c] >> 16);
+            }
+          }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a[4 * q + c] = gated_act<ACT>(acc[0][4 * q + c] * sc + bg[c], acc[1][4 * q + c] * sc + bu[c], p.alpha, p.limit);
+          m = fmaxf(m, fabsf(a[4 * q + c]));
+        }
+      }
+      m = fmaxf(m, __shfl_xor(m, 32, MOE_WAVE));
+      const int X = mx_shared_exp(m);
+      const float inv = mx_inv_scale(X);
+      // stage the codes (rows of 128 bytes) and the scale bytes (4 per row)
+      // in LDS, then store whole row pieces
+      uint8_t* s_codes = smem;
+      uint8_t* s_scales = smem + F_BM * M_CPITCH;
+      __syncthreads();  // the stage buffers are free
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(uint32_t*)(s_codes + fr * M_CPITCH + wave * 32 + 8 * q + 4 * fh) =
+            e4m3x4(a[4 * q] * inv, a[4 * q + 1] * inv, a[4 * q + 2] * inv, a[4 * q + 3] * inv);
+      if (fh == 0) s_scales[fr * 4 + wave] = (uint8_t)(X + 127);
+      __syncthreads();
+      {
+        const int r = tid >> 3, pc = tid & 7;  // 32 rows x 8 pieces of 16 bytes
+        if (row_beg + r < row_end)
+          *(u32x4_t*)(p.act + (int64_t)(row_beg + r) * p.D + nb * 128 + pc * 16) =
+              *(const u32x4_t*)(s_codes + r * M_CPITCH + pc * 16);
+        if (tid < F_BM && row_beg + tid < row_end)
+          *(uint32_t*)(p.act_scale + (int64_t)(row_beg + tid) * (p.D / 32) + nb * 4) =
+              *(const uint32_t*)(s_scales + tid * 4);
+      }
+      fused_count_in(p.arrive + gm);  // this part of the row block is published
+    } else {
+      if (S > 1) {
+        const int t2 = gm * NB2 + nb;
+        if (!fused_split_reduce(acc, p.part + (int64_t)t2 * S * F_PART_FLOATS, part, S, tile_done + t2, s_item + 1)) {
+          __syncthreads();
+          continue;
+        }
+      }
+      // the tile's outputs go through LDS (rows of 256 outputs + 16 bytes of
+      // bank skew) so that each store moves whole row pieces
+      const float sc = p.s_d ? p.s_d[e] : 1.0f;
+      const uint16_t* bias = p.b_d ? p.b_d + (int64_t)e * p.H : nullptr;
+      constexpr int ES = OUT_BF16 ? 2 : 4;
+      constexpr int PITCH = F_BN * ES + 16;
+      __syncthreads();  // the stage buffers are free
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int lc = wave * 64 + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
+          const int n = nb * F_BN + lc;
+          float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (bias && n < p.H) {
+            const uint2 b2 = *(const uint2*)(bias + n);
+            bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
+            bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+          }
+          float v[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = acc[ni][4 * q + c] * sc + bd[c];
+          uint8_t* dst = smem + fr * PITCH + lc * ES;
+          if (OUT_BF16) {
+            uint2 w;
+            w.x = pack_bf16x2_rne(v[0], v[1]);
+            w.y = pack_bf16x2_rne(v[2], v[3]);
+            *(uint2*)dst = w;
+          } else {
+            *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
+          }
+        }
+      __syncthreads();
+      // a row is F_BN * ES bytes: 32 (bf16) or 64 (fp32) lanes of 16 bytes
+      constexpr int LPR = F_BN * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per store
+      const int cpart = lane % LPR;
+      const int n = nb * F_BN + cpart * (16 / ES);
+      for (int r = wave * RPI + lane / LPR; r < F_BM; r += F_NW * RPI) {
+        const int row = row_beg + r;
+        if (row < row_end && n < p.H)
+          *(u32x4_t*)((uint8_t*)p.out + ((int64_t)row * p.H + n) * ES) = *(const u32x4_t*)(smem + r * PITCH + cpart * 16);
+      }
+    }
+    __syncthreads();  // the stage buffers and the item word are reused by the next item
   }
+
+  fused_exit(p.ctl, p.arrive, total_mb, s_item + 1);
 }
 
 int fused_cu_count() {
@@ -429,6 +806,26 @@ hipError_t launch_fused_act(const FusedArgs& a, int fmt, int out_bf16, hipStream
                   : launch_fused_kernel(fused_ffn_kernel<ACT, 1, false>, a, st);
 }
 
+template <typename KernelT>
+hipError_t launch_fused_mx_kernel(KernelT kern, const FusedMxArgs& a, hipStream_t st) {
+  const int lds = M_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int grid = M_WG_PER_CU * fused_cu_count();
+  if (grid <= 0) return hipErrorInvalidDevice;
+  kern<<<grid, F_NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_fused_mx_act(const FusedMxArgs& a, int fmt, int out_bf16, hipStream_t st) {
+  if (fmt == 0)
+    return out_bf16 ? launch_fused_mx_kernel(fused_ffn_mx_kernel<ACT, 0, true>, a, st)
+                    : launch_fused_mx_kernel(fused_ffn_mx_kernel<ACT, 0, false>, a, st);
+  return out_bf16 ? launch_fused_mx_kernel(fused_ffn_mx_kernel<ACT, 1, true>, a, st)
+                  : launch_fused_mx_kernel(fused_ffn_mx_kernel<ACT, 1, false>, a, st);
+}
+
 }  // namespace
 
 FusedLayout fused_layout(int64_t max_rows, int H, int D, int L) {
@@ -447,7 +844,11 @@ FusedLayout fused_layout(int64_t max_rows, int H, int D, int L) {
   f.tiles_cap = S > 1 ? (int)(tiles < F_MAX_TILES ? tiles : F_MAX_TILES) : 0;
   f.S = f.tiles_cap > 0 ? S : 1;
   f.act_off = up256(F_HDR_WORDS * 4);
-  f.part_off = f.act_off + up256(R * D * 2);
+  // A: bf16 [R, D], or MXFP8 codes [R, D] followed by the scale bytes [R, D/32]
+  f.act_scale_off = f.act_off + up256(R * D);
+  const int64_t act_bf16 = up256(R * D * 2), act_mx = up256(R * D) + up256(R * (D / 32));
+  const int64_t act_bytes = act_bf16 > act_mx ? act_bf16 : act_mx;
+  f.part_off = f.act_off + act_bytes;
   f.bytes = f.part_off + (int64_t)f.tiles_cap * f.S * F_PART_FLOATS * 4 + up256(f.row_blocks * 4);
   return f;
 }
@@ -484,6 +885,46 @@ hipError_t launch_ffn_fused(const FfnBf16Params& q, void* ws, int64_t ws_bytes, 
   else err = launch_fused_act<ACT_GELU_TANH>(a, q.fmt, q.out_bf16, st);
   if (err != hipSuccess) return err;
   // one launch: the middle event is recorded with the last
+  if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
+  if (q.events) err = hipEventRecord(q.events[2], st);
+  return err;
+}
+
+hipError_t launch_ffn_fused_mx(const FfnMxParams& q, void* ws, int64_t ws_bytes, hipStream_t st) {
+  hipError_t err;
+  const FusedLayout f = fused_layout(q.max_rows, q.H, q.D, q.L);
+  if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
+  FusedMxArgs a{};
+  a.offsets = q.offsets;
+  a.L = q.L;
+  a.H = q.H;
+  a.D = q.D;
+  a.x = q.x_perm;
+  a.x_scale = q.x_scale;
+  a.sorted_token = q.sorted_token;
+  a.w_gu = q.w_gate_up;
+  a.w_gu_scale = q.w_gate_up_scale;
+  a.w_d = q.w_down;
+  a.w_d_scale = q.w_down_scale;
+  a.b_gu = q.b_gate_up;
+  a.b_d = q.b_down;
+  a.s_gu = q.gate_up_scales;
+  a.s_d = q.down_scales;
+  a.alpha = q.alpha;
+  a.limit = q.limit;
+  a.act = (uint8_t*)ws + f.act_off;
+  a.act_scale = (uint8_t*)ws + f.act_scale_off;
+  a.out = q.out;
+  a.ctl = (int32_t*)ws;
+  a.arrive = (int32_t*)((uint8_t*)ws + (ws_bytes & ~(int64_t)3)) - f.row_blocks;
+  a.part = (float*)((uint8_t*)ws + f.part_off);
+  a.S = f.S;
+  a.tiles_cap = f.tiles_cap;
+  a.row_blocks = (int)f.row_blocks;
+  if (q.act_kind == ACT_SILU) err = launch_fused_mx_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
+  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_mx_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);
+  else err = launch_fused_mx_act<ACT_GELU_TANH>(a, q.fmt, q.out_bf16, st);
+  if (err != hipSuccess) return err;
   if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
   if (q.events) err = hipEventRecord(q.events[2], st);
   return err;

@@ -3,21 +3,8 @@
 // (StackedMoE page: MXFP4 weights run W4A8 with MXFP8 activations; the
 // formats are those of the OCP Microscaling specification).  The scales go
 // straight into v_mfma_scale_f32_32x32x64_f8f6f4, which applies them per 32
-// K slots, so the main loop does no scale arithmetic at all.
-//
-// Operand layout of that MFMA with the e2m1 operand first and the e4m3
-// operand second (measured with one-wave probes on gfx950): lane l = 32h + r
-// holds row r.  Its 32 e2m1 codes all fall in the first 32 K slots (h = 0) or
-// the last 32 (h = 1); of its 32 e4m3 bytes, bytes 0-15 fall in the first 32
-// slots and bytes 16-31 in the last 32.  e2m1 code p of half 0 meets e4m3
-// byte p of half 0 (p < 16) or byte p-16 of half 1; e2m1 code p of half 1
-// meets e4m3 byte 16+p of half 0 (p < 16) or byte p of half 1.  The scale of
-// the first 32 slots is lane r's, of the last 32 lane 32+r's.  So for the
-// 64-wide k step kk, whose MX blocks are 2kk and 2kk+1:
-//   e2m1 lane h: k [64kk+32h, +32)            = 16-byte chunk 2kk+h of the row
-//   e4m3 lane h: k [64kk+16h, +16), [64kk+32+16h, +16) = chunks 4kk+h, 4kk+2+h
-//   both pass the scale byte of block 2kk+h.
-// (e2m1 element 2i is the low nibble of byte i, as the MFMA reads it.)
+// K slots, so the main loop does no scale arithmetic at all.  The operand
+// layout of that MFMA and the stage row formats are in mx_common.h.
 //
 // gate_up:  h = s_gu[e] * C + b_gu[e]; A = act(gate, up), re-quantised to
 //           MXFP8 per row per 32 columns (shared exponent floor(log2 amax)-8,
@@ -32,6 +19,7 @@
 // rows (and theirs) four deep by waves 4-7.
 #include "common.h"
 #include "kernels.h"
+#include "mx_common.h"
 
 namespace moe {
 
@@ -44,8 +32,9 @@ constexpr int X_WAVES_M = 2, X_WAVES_N = 4;
 constexpr int X_NT = 64 * X_WAVES_M * X_WAVES_N;           // 512 threads
 constexpr int X_WTM = X_BM / X_WAVES_M, X_WTN = X_BN / X_WAVES_N;  // 128 x 64
 constexpr int X_MI = X_WTM / 32, X_NI = X_WTN / 32;        // 4 x 2 MFMA blocks
-constexpr int X_A_ROW = X_BK;                              // bytes per e4m3 stage row
-constexpr int X_B_ROW = X_BK / 2;                          // bytes per packed e2m1 stage row
+static_assert(X_BK == MX_BK, "stage k of the MX row formats");
+constexpr int X_A_ROW = MX_A_ROW;                          // bytes per e4m3 stage row
+constexpr int X_B_ROW = MX_B_ROW;                          // bytes per packed e2m1 stage row
 constexpr int X_A_BYTES = X_BM * X_A_ROW;                  // 32 KB
 constexpr int X_B_BYTES = X_BN * X_B_ROW;                  // 16 KB
 // LDS: activation slots of X_A_BYTES in a ring of 2, weight slots of
@@ -67,14 +56,6 @@ constexpr int X_BUF_DWORD3 = 0x00020000;  // raw buffer resource word 3 (gfx9)
 // and still counts as one load for the stage's vmcnt bookkeeping.
 constexpr uint32_t X_OOB = 0x80000000u;
 
-// e4m3 rows: 128 bytes, 8 chunks; chunk c of row r at c ^ fa(r).
-__device__ __forceinline__ int mx_fa(int r) { return (r ^ (r >> 3)) & 7; }
-__device__ __forceinline__ int mx_a_off(int row, int chunk) { return row * X_A_ROW + ((chunk ^ mx_fa(row)) << 4); }
-// e2m1 rows: 64 bytes, 4 chunks; chunk c of row r at c ^ fb(r), which puts the
-// rows r, r+4, r+8, r+12 that share banks on four different chunks (the
-// fragment reads of 32 consecutive rows are conflict-free).
-__device__ __forceinline__ int mx_fb(int r) { return (((r >> 1) ^ (r >> 3)) & 1) | (((r >> 2) & 1) << 1); }
-__device__ __forceinline__ int mx_b_off(int row, int chunk) { return row * X_B_ROW + ((chunk ^ mx_fb(row)) << 4); }
 
 __device__ __forceinline__ void mx_block_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -100,14 +81,6 @@ struct MxGemmArgs {
   uint8_t* out_scale;        // gate_up: E8M0 [rows, D/32]
 };
 
-// Shared exponent of an MXFP8 block with largest magnitude m (>= 0):
-// floor(log2 m) - 8, at least -127; 0 for m = 0.
-__device__ __forceinline__ int mx_shared_exp(float m) {
-  const int e = (int)((__float_as_uint(m) >> 23) & 0xffu);
-  return m == 0.0f ? 0 : max(e - 127 - 8, -127);
-}
-// 2^-X for X in [-127, 120]: a normal float built from its exponent field.
-__device__ __forceinline__ float mx_inv_scale(int X) { return __uint_as_float((uint32_t)(127 - X) << 23); }
 
 struct MxTile {
   int e, nb, mb, row_beg, row_end;
@@ -298,17 +271,6 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // fragments of one 64-wide k step kk (see the layout note at the top)
-  auto frag_a = [&](const uint8_t* st, int row, int kk) {
-    const u32x4_t lo4 = *(const u32x4_t*)(st + mx_a_off(row, 4 * kk + fh));
-    const u32x4_t hi4 = *(const u32x4_t*)(st + mx_a_off(row, 4 * kk + 2 + fh));
-    return i32x8_t{(int)lo4[0], (int)lo4[1], (int)lo4[2], (int)lo4[3], (int)hi4[0], (int)hi4[1], (int)hi4[2], (int)hi4[3]};
-  };
-  auto frag_b = [&](const uint8_t* st, int row, int kk) {
-    const u32x4_t c4 = *(const u32x4_t*)(st + mx_b_off(row, 2 * kk + fh));
-    return i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
-  };
-
   const int live_mi = min(max((row_end - (row_beg + wm_s * X_WTM) + 31) / 32, 0), X_MI);
 
   // ---- main loop.  Iteration kt: each role waits for its own loads of stage
@@ -348,7 +310,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
       const uint32_t s4 = *(const uint32_t*)(bs_l + row * 4 * G);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        bq[ni][kk] = frag_b(bst, row, kk);
+        bq[ni][kk] = mx_frag_b(bst, row, kk, fh);
         bsc[ni][kk] = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
       }
     }
@@ -359,7 +321,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
         const uint32_t s4 = *(const uint32_t*)(as_l + row * 4 * G);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const i32x8_t aq = frag_a(ast, row, kk);
+          const i32x8_t aq = mx_frag_a(ast, row, kk, fh);
           const int asc = (int)((s4 >> (8 * (2 * kk + fh))) & 0xffu);
 #pragma unroll
           for (int ni = 0; ni < X_NI; ++ni)
@@ -572,10 +534,6 @@ struct W4GemmArgs {
   void* out;                 // gate_up: bf16 [rows, D]; down: bf16 / fp32 [rows, H]
 };
 
-// E8M0 byte -> the fp32 2^(s-127) (s = 0 is the subnormal 2^-127).
-__device__ __forceinline__ float e8m0_f32(uint32_t s) {
-  return __uint_as_float(s ? (s << 23) : 0x00400000u);
-}
 
 template <int MODE, int ACT, int FMT, bool OUT_BF16, int W_BM>
 __global__ __launch_bounds__(W4Shape<W_BM>::NT) __attribute__((amdgpu_waves_per_eu(2, 2)))

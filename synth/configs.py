@@ -76,6 +76,12 @@ CONFIGS = {
                  route_scale=1.0, global_scale=1.0),
     # the Mixtral layer on a decode-sized batch, FFN in one launch
     8: MoEConfig(8, "mixtral_decode", T=64, H=4096, E=8, k=2, D=14336, fused=True),
+    # the MXFP4 experts run W4A8 on a decode-sized batch, FFN in one launch
+    # (mega_ffn page: the block-scaled single-launch L1 + L2 with MXFP8
+    # activations re-quantised between the legs)
+    9: MoEConfig(9, "mxfp4_decode", T=256, H=7168, E=256, k=8, D=2048,
+                 router="sigmoid_sink", s=0, operand_dtype="mxfp4",
+                 route_scale=1.0, global_scale=1.0, fused=True),
 }
 
 

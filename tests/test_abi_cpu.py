@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), f"{n} declared but not exported"
     assert set(names) == set(m.ENTRY_POINTS)
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
 
 
 def test_struct_layouts_match_header_sizes():
@@ -167,6 +167,24 @@ def test_grouped_ffn_validation(kw, status, frag):
     (dict(x_perm=None), m.MOE_ERR_INVALID_ARGUMENT, "gather"),
     (dict(w_gate_up_layout=0), m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
     (dict(act_workspace_bytes=64 * 512 * 2), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A16), m.MOE_ERR_INVALID_ARGUMENT, "MXFP4_W4A8"),
+    # MXFP4 x MXFP8: hidden_dim in whole 128-element stages, the activation and weight scales
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, hidden_dim=192, x_perm_scale=112, w_gate_up_scale=128,
+          w_down_scale=144), m.MOE_ERR_INVALID_ARGUMENT, "128"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, w_gate_up_scale=128, w_down_scale=144), m.MOE_ERR_INVALID_ARGUMENT,
+     "x_perm_scale"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, x_perm_scale=112, w_down_scale=144), m.MOE_ERR_INVALID_ARGUMENT,
+     "w_gate_up_scale"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, x_perm_scale=116, w_gate_up_scale=128, w_down_scale=144),
+     m.MOE_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144,
+          w_down_layout=0), m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
+    # gather form: x holds num_tokens rows of codes, which must stay under 2 GiB
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, x_perm=None, x=128, sorted_token=144, x_perm_scale=112,
+          w_gate_up_scale=128, w_down_scale=144, num_tokens=1 << 22, hidden_dim=1024, act_workspace_bytes=1 << 40),
+     m.MOE_ERR_INVALID_ARGUMENT, "2 GiB"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144,
+          act_workspace_bytes=64 * 512 * 2), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
 ])
 def test_grouped_ffn_fused_validation(kw, status, frag):
     st, msg = _err(m.lib().moe_grouped_ffn_fused, _ffn(**kw))
@@ -196,6 +214,9 @@ def test_fused_workspace_bytes():
     assert lib.moe_ffn_fused_workspace_bytes(32, 256, 8192, 1) == hdr + 32 * 8192 * 2 + 2 * 8 * 32 * 256 * 4 + 256
     # a smaller max_rows needs no more
     assert lib.moe_ffn_fused_workspace_bytes(17, 4096, 14336, 8) <= lib.moe_ffn_fused_workspace_bytes(128, 4096, 14336, 8)
+    # MX: A is e4m3 codes and one scale byte per 32, each region rounded to
+    # 256 bytes, which the bf16 size covers except for the tiniest rows x moe_dim
+    assert lib.moe_ffn_fused_workspace_bytes(1, 128, 128, 1) == hdr + 256 + 256 + up(4 * rb(1, 1))
     assert lib.moe_ffn_fused_workspace_bytes(0, 4096, 14336, 8) == hdr
     assert lib.moe_ffn_fused_workspace_bytes(-1, 4096, 14336, 8) == 0
 

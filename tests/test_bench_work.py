@@ -33,3 +33,17 @@ def test_combine_bytes_with_shared_experts():
     cfg = synth.get_config(3)
     extra = cfg.n_shared * cfg.T * (4 * cfg.H + 4)
     assert (bench.algorithmic_work(cfg)["combine_bytes"] - extra) / 1e6 == pytest.approx(436.6, rel=1e-3)
+
+
+def test_single_launch_ffn_bytes():
+    # Mixtral decode (T=64, top-2: 128 rows), all 8 experts with rows: per
+    # expert 2*14336*4096 + 4096*14336 bf16 weights = 352,321,536 bytes; x rows
+    # 128*4096*2, A written and read 2*128*14336*2, O 128*4096*4 (fp32)
+    cfg = synth.get_config(8)
+    assert bench.fused_ffn_bytes(cfg, 8) == 8 * 352_321_536 + 1_048_576 + 7_340_032 + 2_097_152
+    # MXFP4 decode (T=256, top-8: 2048 rows), 142 experts with rows: per
+    # expert 44,040,192 E2M1 codes at half a byte plus one scale byte per 32:
+    # 23,396,352 bytes; x rows 2048*7168 codes + scales = 15,138,816; A
+    # 2*2048*2048 codes + scales = 8,650,752; O 2048*7168*2 (bf16)
+    cfg = synth.get_config(9)
+    assert bench.fused_ffn_bytes(cfg, 142) == 142 * 23_396_352 + 15_138_816 + 8_650_752 + 29_360_128

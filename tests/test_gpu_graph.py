@@ -30,6 +30,7 @@ def moe():
     (5, {"T": 256, "E": 16, "H": 1024, "D": 512}),               # fp8 block-scaled
     (6, {"T": 256, "E": 16, "H": 1024, "D": 512}),               # MXFP4 x MXFP8
     (8, {}),                                                     # single-launch FFN (decode)
+    (9, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # single-launch FFN, MXFP4 x MXFP8
 ])
 def test_layer_replays_in_a_graph(moe, cid, changes):
     cfg = synth.scaled(synth.get_config(cid), **changes)

@@ -705,12 +705,17 @@ def _act_code_stats(kind, cg, sg, a32):
     return int(np.sum(cg == codes_ref)), cg.size, float(ratio.max()) if ratio.size else 0.0
 
 
+# byte offset of A in the single-launch FFN's workspace (after its control words)
+FUSED_ACT_OFFSET = 1280
+
+
 def _gpu_act_rows(layer, kind, D, rows):
     """The GPU's re-quantised A for CSR rows `rows`: (codes, scales), gathered on the device."""
     R = layer.R
-    so = ((R * D + 255) // 256) * 256
+    base = FUSED_ACT_OFFSET if layer.fused else 0
+    so = base + ((R * D + 255) // 256) * 256
     sel = torch.from_numpy(np.asarray(rows, np.int64)).to(DEV)
-    codes = layer.act_ws[: R * D].view(R, D).index_select(0, sel)
+    codes = layer.act_ws[base: base + R * D].view(R, D).index_select(0, sel)
     if kind == "fp8":
         sc = layer.act_ws[so: so + R * (D // 128) * 4].view(torch.float32).view(R, D // 128).index_select(0, sel)
     else:
@@ -1066,3 +1071,89 @@ def test_fused_ffn_full_size(moe):
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, 16, seed=9), BF16_TOL)
     assert moe.fused_error_word(layer.act_ws) == 0
+
+
+# ---------------------------------------------------------------- single-launch L1 + L2 (MXFP4 x MXFP8)
+
+def _fused_mx_against_two_launch(moe, cfg, inp, res, gather):
+    """The single launch against the two-launch MX FFN on the same routing:
+    bit-identical O when the down items are not split along K (the same
+    MFMA sequence per output element and the same epilogue arithmetic),
+    else within the fp8 bar."""
+    n = int(host(res["index"]["offsets"])[-1])
+    o_fused = host(res["O"])[:n]
+    two = moe.MoELayer(cfg, inp, gather=gather, fused=False)
+    r2 = two.forward(inp["x"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r2["index"]["offsets"]), host(res["index"]["offsets"]))
+    o_two = host(r2["O"])[:n]
+    split = (cfg.D + cfg.H) // (2 * cfg.H) > 1
+    if split:
+        err, _ = rel_rms_err(o_fused.astype(np.float64), o_two.astype(np.float64))
+        say(f"  fused vs two-launch O (down split along K): max err / rms = {err:.2e}")
+        assert err <= FP8_TOL
+    else:
+        same = np.array_equal(o_fused, o_two)
+        say(f"  fused vs two-launch O: bit-identical = {same}")
+        assert same
+
+
+@pytest.mark.parametrize("changes,gather", [
+    ({"T": 64, "E": 8, "k": 2, "H": 512, "D": 256}, True),
+    ({"T": 37, "E": 8, "k": 2, "H": 256, "D": 384, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, True),
+    # one k stage in L2, a half-filled last column tile (H = 1.5 x 256), permuted rows
+    ({"T": 200, "E": 5, "k": 4, "H": 384, "D": 128, "activation": "gelu_tanh", "has_bias": True}, False),
+    ({"T": 9, "E": 64, "k": 8, "H": 1024, "D": 512}, True),                 # most experts empty, single rows
+    ({"T": 50, "E": 4, "k": 2, "H": 256, "D": 1664, "has_bias": True}, True),   # down split in 3 uneven parts
+    ({"T": 40, "E": 4, "k": 2, "H": 256, "D": 2048}, True),                 # 4 parts of whole scale groups
+    ({"T": 33, "E": 3, "k": 1, "H": 128, "D": 1152, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0},
+     False),                                                                # 5 parts, one k stage in L1
+])
+def test_fused_mx_ffn_layer(moe, changes, gather):
+    """The single-launch MX FFN against the oracle, twice in a row on one
+    workspace, with no timed-out wait; its re-quantised A against the
+    oracle's; and against the two-launch MX FFN."""
+    cfg = synth.scaled(synth.get_config(9), **changes)
+    inp = _gen(cfg)
+    say(f"[fused mx] {changes} gather={gather}")
+    layer = moe.MoELayer(cfg, inp, gather=gather)
+    assert layer.fused
+    for call in range(2):
+        res = layer.forward(inp["x"])
+        torch.cuda.synchronize()
+        _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
+        assert moe.fused_error_word(layer.act_ws) == 0, f"call {call}: a wait timed out"
+    _check_mx_act(cfg, inp, res, layer)
+    _fused_mx_against_two_launch(moe, cfg, inp, res, gather)
+
+
+def test_fused_mx_ffn_then_smaller_batch(moe):
+    """One workspace, 256 then 17 tokens with another routing: the first
+    call's counters must not leak into the second."""
+    big = synth.scaled(synth.get_config(9), T=256, E=16, H=512, D=1024)
+    small = synth.scaled(big, T=17)
+    inp_b, inp_s = _gen(big), synth.make_inputs(small, DEV, salt=3)
+    say("[fused mx] T=256 then T=17 on one workspace")
+    lb = moe.MoELayer(big, inp_b)
+    ls = moe.MoELayer(small, inp_s)
+    ls.act_ws = lb.act_ws
+    rb = lb.forward(inp_b["x"])
+    rs = ls.forward(inp_s["x"])
+    torch.cuda.synchronize()
+    _check_layer(big, inp_b, rb, np.arange(big.T), FP8_TOL)
+    _check_layer(small, inp_s, rs, np.arange(small.T), FP8_TOL)
+    assert moe.fused_error_word(lb.act_ws) == 0
+
+
+def test_fused_mx_ffn_full_size(moe):
+    cfg = synth.get_config(9)
+    inp = _gen(cfg)
+    say("[fused mx full] T=256 H=7168 E=256 k=8 D=2048, MXFP4 x MXFP8 in one launch")
+    layer, res = _run_layer(moe, cfg, inp)
+    assert layer.fused
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 16, seed=10), FP8_TOL)
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=10)
+    assert moe.fused_error_word(layer.act_ws) == 0
+    _fused_mx_against_two_launch(moe, cfg, inp, res, True)
