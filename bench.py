@@ -214,6 +214,9 @@ EXTRA_TRACES = [
     ("trace8", 8, "mixtral_decode_fused_ffn_kernel_stats.txt",
      "Mixtral decode batch through the single-launch FFN: T=64 tokens, hidden 4096, 8 experts, top-2 softmax "
      "router, moe_dim 14336, SiLU"),
+    ("trace9", 9, "mxfp4_decode_fused_ffn_kernel_stats.txt",
+     "MXFP4 x MXFP8 decode batch through the single-launch FFN: T=256 tokens, hidden 7168, 256 experts, "
+     "top-8 sigmoid router, moe_dim 2048, SiLU"),
 ]
 
 
@@ -311,12 +314,22 @@ def summarize_profile(d: str):
             "# Traffic above that is weight tiles fetched again by m-blocks that missed each other in L2,",
             "# and activation rows re-read from the Infinity Cache."]
     open(os.path.join(prof, "mixtral_layer_hbm_traffic.txt"), "w").write("\n".join(out) + "\n")
+    # the counters describe the kernel source that the counter runs were built
+    # from: their bench lines carry its hash (none when they differ or are missing)
+    run_hash = set()
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        h = None
+        for ln in open(os.path.join(d, c + ".log")):
+            if ln.startswith('{"metric"'):
+                h = json.loads(ln).get("kernel_source_sha256_16")
+        run_hash.add(h)
+    src_hash = run_hash.pop() if len(run_hash) == 1 else None
     if gu:
         json.dump({"kernel": "grouped gate_up GEMM (bf16, SiLU, concatenated, gathered x)",
                    "workload": "Mixtral-shape layer, T=4096", "bytes_per_launch": round(gu[0] + gu[1]),
                    "read_bytes": round(gu[0]), "write_bytes": round(gu[1]),
                    "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
-                   "kernel_source_sha256_16": _src_hash(), "source": "profiles/mixtral_layer_hbm_traffic.txt"},
+                   "kernel_source_sha256_16": src_hash, "source": "profiles/mixtral_layer_hbm_traffic.txt"},
                   open(TRAFFIC_FILE, "w"), indent=1)
     for sub, name, title in (
             ("SQ2", "mixtral_gemm_pipe_counters.txt",
@@ -730,6 +743,8 @@ def main():
                                f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,
                    "num_experts": cfg.E, "top_k": cfg.k, "moe_dim": cfg.D, "parallelism": "none (1 GPU)"},
         "roofline": roof,
+        # the bf16 GEMM sources this run was built from (ties counter runs to the kernel they measured)
+        "kernel_source_sha256_16": _src_hash(),
         "ffn_tflops": round(ffn_tf, 2), "ffn_mfma_frac": round(ffn_tf / peak, 4),
         "ffn_frac_of_measured": round(ffn_tf / ceil[mfma_key], 4),
         "breakdown_ms": {"route": round(t_route, 4), "build_indices": round(t_idx, 4),

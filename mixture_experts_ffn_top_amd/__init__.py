@@ -284,8 +284,8 @@ def grouped_ffn(offsets, max_rows: int, weights: "ExpertWeights", *, x_perm=None
                 gate_up_format="concatenated", gate_up_expert_scales=None, down_expert_scales=None,
                 out_dtype=torch.float32, act_workspace=None, out=None, timing_events=None, fused=False):
     """moe_grouped_ffn (or, fused=True, moe_grouped_ffn_fused: both GEMMs in
-    one launch, bf16 only).  Returns O [max_rows, H] (rows past offsets[-1]
-    unwritten).
+    one launch, for bf16 or MXFP4 x MXFP8 operands).  Returns O [max_rows, H]
+    (rows past offsets[-1] unwritten).
 
     timing_events: optional ctypes array of 3 hipEvent_t handles, recorded
     before the gate_up GEMM, between the GEMMs and after the down GEMM."""
@@ -545,7 +545,7 @@ class MoELayer:
         dev = inputs["x"].device
         self.device = dev
         self.gather = gather
-        # the single-launch FFN (bf16): on when the configuration asks for it
+        # the single-launch FFN (bf16 or MXFP4 x MXFP8): on when the configuration asks for it
         self.fused = getattr(cfg, "fused", False) if fused is None else fused
         self.w = ExpertWeights.from_stacked(
             inputs["w_gate_up"], inputs["w_down"], b_gate_up=inputs.get("b_gate_up"),
