@@ -265,6 +265,7 @@ struct FusedArgs {
   int32_t* arrive;             // [i] L1 items done of global row block i
   float* part;                 // [tile][part] partial tiles of F_PART_FLOATS, laid out by thread
   int S;                       // K parts of a split L2 tile
+  int max_rows;                // rows the A and O buffers hold
   int row_blocks;              // arrival counters the workspace holds
   int tiles_cap;               // split only when the launch has at most this many L2 tiles
 };
@@ -283,8 +284,9 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   int32_t* tile_done = p.ctl + 4;
 
   fused_block_prefix(p.offsets, L, s_mbp);
-  // more rows than max_rows: no counter may be touched, so do nothing
-  const bool too_many = s_mbp[L] > p.row_blocks;
+  // more rows than max_rows: neither A, O nor a counter may be touched, so do
+  // nothing (at most max_rows rows also bound the row blocks by row_blocks)
+  const bool too_many = p.offsets[L] > p.max_rows || s_mbp[L] > p.row_blocks;
   if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int total_mb = too_many ? 0 : s_mbp[L];
   const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
@@ -499,7 +501,7 @@ struct FusedMxArgs {
   int32_t* ctl;                // as FusedArgs
   int32_t* arrive;
   float* part;
-  int S, row_blocks, tiles_cap;
+  int S, max_rows, row_blocks, tiles_cap;
 };
 
 template <int ACT, int FMT, bool OUT_BF16>
@@ -514,7 +516,8 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
   int32_t* tile_done = p.ctl + 4;
 
   fused_block_prefix(p.offsets, L, s_mbp);
-  const bool too_many = s_mbp[L] > p.row_blocks;
+  // more rows than max_rows: do nothing (as the bf16 kernel)
+  const bool too_many = p.offsets[L] > p.max_rows || s_mbp[L] > p.row_blocks;
   if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const int total_mb = too_many ? 0 : s_mbp[L];
   const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
@@ -879,6 +882,7 @@ hipError_t launch_ffn_fused(const FfnBf16Params& q, void* ws, int64_t ws_bytes, 
   a.part = (float*)((uint8_t*)ws + f.part_off);
   a.S = f.S;
   a.tiles_cap = f.tiles_cap;
+  a.max_rows = q.max_rows;
   a.row_blocks = (int)f.row_blocks;
   if (q.act_kind == ACT_SILU) err = launch_fused_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
   else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);
@@ -920,6 +924,7 @@ hipError_t launch_ffn_fused_mx(const FfnMxParams& q, void* ws, int64_t ws_bytes,
   a.part = (float*)((uint8_t*)ws + f.part_off);
   a.S = f.S;
   a.tiles_cap = f.tiles_cap;
+  a.max_rows = q.max_rows;
   a.row_blocks = (int)f.row_blocks;
   if (q.act_kind == ACT_SILU) err = launch_fused_mx_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
   else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_mx_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);

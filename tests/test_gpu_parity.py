@@ -1157,3 +1157,29 @@ def test_fused_mx_ffn_full_size(moe):
     _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=10)
     assert moe.fused_error_word(layer.act_ws) == 0
     _fused_mx_against_two_launch(moe, cfg, inp, res, True)
+
+
+@pytest.mark.parametrize("cid", [8, 9])
+def test_fused_ffn_rows_beyond_max_rows(moe, cid):
+    """expert_offsets holding more rows than max_rows (which only the device
+    sees): the single launch computes nothing, leaves expert_out as it was,
+    sets the error word to 2, and leaves the workspace's counters at zero
+    for the next call."""
+    cfg = synth.scaled(synth.get_config(cid), T=32, E=4, k=2, H=256, D=256)
+    inp = _gen(cfg)
+    say(f"[fused rows beyond max_rows] cfg={cid}")
+    layer = moe.MoELayer(cfg, inp)
+    res = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    ind = res["index"]
+    R = 16                      # the routing holds T * k = 64 rows
+    ws = moe.ffn_workspace(R, cfg.D, cfg.operand_dtype, DEV, fused=True, L=cfg.E, H=cfg.H)
+    out = torch.full((R, cfg.H), 7.0, dtype=layer.out_dtype, device=DEV)
+    moe.grouped_ffn(ind["offsets"], R, layer.w, x=layer.last["x_gather"], x_perm_scale=ind.get("x_perm_scale"),
+                    sorted_token=ind["sorted_token"], out_dtype=layer.out_dtype, act_workspace=ws, out=out,
+                    fused=True)
+    torch.cuda.synchronize()
+    assert moe.fused_error_word(ws) == 2
+    assert torch.all(out == 7.0)
+    # queue head and exit count back at zero
+    assert host(ws[:8].view(torch.int32)).tolist() == [0, 0]
