@@ -3,7 +3,7 @@
 // across workgroups (mega_ffn page: one launch that fuses the L1 and L2 legs,
 // cross-workgroup arrival counters, no per-launch memset).
 //
-// A persistent grid (one workgroup per CU) takes work items from one atomic
+// A persistent grid (one or two workgroups per CU) takes work items from one atomic
 // queue: first every L1 item (expert, 32-row block, 128 outputs), then every
 // L2 item (expert, 32-row block, 256 outputs, one of S parts of K).  An L2
 // item needs the whole A row block, i.e. all D/128 L1 items of its (expert,
@@ -23,10 +23,11 @@
 // registers) and runs the epilogue, so the result does not depend on which
 // part came last.  No part waits for another.
 //
-// Visibility follows the HIP memory model at agent scope: an L1 item's waves
-// fence-release their A stores (write-back of the XCD's L2) before the
-// counter increment; an L2 item acquires the counter and fence-acquires
-// (invalidate) before loading A, whichever XCD either ran on.  The last
+// Visibility follows the HIP memory model at agent scope: after an L1 item's
+// A stores, a workgroup barrier and one release fence (write-back of the
+// XCD's L2) precede the counter increment; an L2 item acquires the counter
+// and fence-acquires (invalidate) before loading A, whichever XCD either ran
+// on.  The last
 // workgroup to leave resets the queue, the exit count and the arrival
 // counters, so the control words start at zero on the next launch; the
 // caller zeroes them once, when the workspace is allocated.
