@@ -38,6 +38,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// ---------------------------------------------------------------- biases
+// The bf16 biases of four consecutive outputs at p (8-byte aligned), as floats.
+__device__ __forceinline__ void bias_x4(const uint16_t* p, float* b) {
+  const uint2 v = *(const uint2*)p;
+  b[0] = bf16_to_f32(v.x & 0xffffu);
+  b[1] = bf16_to_f32(v.x >> 16);
+  b[2] = bf16_to_f32(v.y & 0xffffu);
+  b[3] = bf16_to_f32(v.y >> 16);
+}
+// Gate and up biases of the outputs oc .. oc+3 of a gate_up bias row of 2N
+// values: concatenated (gate at oc, up at N + oc) or interleaved (the gate of
+// output j at 2j, its up at 2j+1; the row 16-byte aligned).
+__device__ __forceinline__ void gate_up_bias_x4(const uint16_t* row, int N, int oc, bool interleaved, float* bg,
+                                                float* bu) {
+  if (!interleaved) {
+    bias_x4(row + oc, bg);
+    bias_x4(row + N + oc, bu);
+  } else {
+    const u32x4_t b4 = *(const u32x4_t*)(row + 2 * oc);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      bg[c] = bf16_to_f32(b4[c] & 0xffffu);
+      bu[c] = bf16_to_f32(b4[c] >> 16);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- e4m3fn
 // float -> OCP e4m3fn code, round to nearest even, saturating at +-448.
 __device__ __forceinline__ uint8_t f32_to_e4m3(float f) {

@@ -625,20 +625,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
     auto bias_of = [&](int oc, float (&bg)[4], float (&bu)[4]) {
       for (int c = 0; c < 4; ++c) bg[c] = bu[c] = 0.0f;
       if (!bias_e) return;
-      if (FMT == FMT_CONCAT) {
-        const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
-        bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
-        bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
-        bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
-        bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
-      } else {
-        // interleaved: gate of output j at 2j, up at 2j+1
-        const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
-        for (int c = 0; c < 4; ++c) {
-          bg[c] = bf16_to_f32(b4[c] & 0xffffu);
-          bu[c] = bf16_to_f32(b4[c] >> 16);
-        }
-      }
+      gate_up_bias_x4(bias_e, p.N, oc, FMT != FMT_CONCAT, bg, bu);
     };
     // ---- A
     __syncthreads();  // the operand tiles are no longer read
@@ -758,9 +745,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
             const int n = nb * BN + nl;
             float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if (bias_e && n < p.N) {
-              const uint2 b2 = *(const uint2*)(bias_e + n);
-              bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-              bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+              bias_x4(bias_e + n, bd);
             }
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
@@ -794,9 +779,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
         const int n = nb * BN + nl;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias_e && n < p.N) {
-          const uint2 b2 = *(const uint2*)(bias_e + n);
-          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+          bias_x4(bias_e + n, bd);
         }
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {

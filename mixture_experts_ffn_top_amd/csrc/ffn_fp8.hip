@@ -440,20 +440,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) bg[4 * q + c] = bu[4 * q + c] = 0.0f;
       if (bias_e && oc < p.N) {
-        if (p.fmt == F8_CONCAT) {
-          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
-          bg[4 * q + 0] = bf16_to_f32(g2.x & 0xffffu); bg[4 * q + 1] = bf16_to_f32(g2.x >> 16);
-          bg[4 * q + 2] = bf16_to_f32(g2.y & 0xffffu); bg[4 * q + 3] = bf16_to_f32(g2.y >> 16);
-          bu[4 * q + 0] = bf16_to_f32(u2.x & 0xffffu); bu[4 * q + 1] = bf16_to_f32(u2.x >> 16);
-          bu[4 * q + 2] = bf16_to_f32(u2.y & 0xffffu); bu[4 * q + 3] = bf16_to_f32(u2.y >> 16);
-        } else {
-          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);   // gate, up of 4 outputs
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bg[4 * q + c] = bf16_to_f32(b4[c] & 0xffffu);
-            bu[4 * q + c] = bf16_to_f32(b4[c] >> 16);
-          }
-        }
+        gate_up_bias_x4(bias_e, p.N, oc, p.fmt != F8_CONCAT, bg + 4 * q, bu + 4 * q);
       }
     }
     float a[Q_MI][16];
@@ -510,11 +497,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
         const int n = nb * Q_BN + lc;
         float bb[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias_e && n < p.N) {
-          const uint2 b2 = *(const uint2*)(bias_e + n);
-          bb[0] = bf16_to_f32(b2.x & 0xffffu);
-          bb[1] = bf16_to_f32(b2.x >> 16);
-          bb[2] = bf16_to_f32(b2.y & 0xffffu);
-          bb[3] = bf16_to_f32(b2.y >> 16);
+          bias_x4(bias_e + n, bb);
         }
 #pragma unroll
         for (int mi = 0; mi < Q_MI; ++mi) {
@@ -553,11 +536,10 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) v[c] = acc[mi][ni][4 * q + c] * u;
           if (bias_e) {
-            const uint2 b2 = *(const uint2*)(bias_e + n);
-            v[0] += bf16_to_f32(b2.x & 0xffffu);
-            v[1] += bf16_to_f32(b2.x >> 16);
-            v[2] += bf16_to_f32(b2.y & 0xffffu);
-            v[3] += bf16_to_f32(b2.y >> 16);
+            float bb[4];
+            bias_x4(bias_e + n, bb);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] += bb[c];
           }
           if (OUT_BF16) {
             uint2 w;

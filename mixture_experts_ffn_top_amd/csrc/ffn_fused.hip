@@ -388,20 +388,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
         const int oc = nb * 128 + wave * 32 + 8 * q + 4 * fh;  // first of 4 outputs
         float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias) {
-          if (FMT == 0) {
-            const uint2 g2 = *(const uint2*)(bias + oc), u2 = *(const uint2*)(bias + p.D + oc);
-            bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
-            bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
-            bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
-            bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
-          } else {
-            const u32x4_t b4 = *(const u32x4_t*)(bias + 2 * oc);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              bg[c] = bf16_to_f32(b4[c] & 0xffffu);
-              bu[c] = bf16_to_f32(b4[c] >> 16);
-            }
-          }
+          gate_up_bias_x4(bias, p.D, oc, FMT != 0, bg, bu);
         }
         if (row < row_end) {
           float a[4];
@@ -433,9 +420,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
           if (n >= p.H || row >= row_end) continue;
           float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if (bias) {
-            const uint2 b2 = *(const uint2*)(bias + n);
-            bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-            bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+            bias_x4(bias + n, bd);
           }
           float v[4];
 #pragma unroll
@@ -676,20 +661,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
         const int oc = nb * 128 + wave * 32 + 8 * q + 4 * fh;  // first of 4 outputs
         float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias) {
-          if (FMT == 0) {
-            const uint2 g2 = *(const uint2*)(bias + oc), u2 = *(const uint2*)(bias + p.D + oc);
-            bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
-            bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
-            bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
-            bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
-          } else {
-            const u32x4_t b4 = *(const u32x4_t*)(bias + 2 * oc);
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              bg[c] = bf16_to_f32(b4[c] & 0xffffu);
-              bu[c] = bf16_to_f32(b4[c] >> 16);
-            }
-          }
+          gate_up_bias_x4(bias, p.D, oc, FMT != 0, bg, bu);
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -744,9 +716,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
           const int n = nb * F_BN + lc;
           float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
           if (bias && n < p.H) {
-            const uint2 b2 = *(const uint2*)(bias + n);
-            bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-            bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+            bias_x4(bias + n, bd);
           }
           float v[4];
 #pragma unroll

@@ -351,20 +351,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
         bu[q][c] = 0.0f;
       }
       if (bias_e) {
-        if (FMT == 0) {
-          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
-          bg[q][0] = bf16_to_f32(g2.x & 0xffffu); bg[q][1] = bf16_to_f32(g2.x >> 16);
-          bg[q][2] = bf16_to_f32(g2.y & 0xffffu); bg[q][3] = bf16_to_f32(g2.y >> 16);
-          bu[q][0] = bf16_to_f32(u2.x & 0xffffu); bu[q][1] = bf16_to_f32(u2.x >> 16);
-          bu[q][2] = bf16_to_f32(u2.y & 0xffffu); bu[q][3] = bf16_to_f32(u2.y >> 16);
-        } else {
-          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bg[q][c] = bf16_to_f32(b4[c] & 0xffffu);
-            bu[q][c] = bf16_to_f32(b4[c] >> 16);
-          }
-        }
+        gate_up_bias_x4(bias_e, p.N, oc, FMT != 0, bg[q], bu[q]);
       }
     }
 #pragma unroll
@@ -405,9 +392,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
         const int n = nb * X_BN + lc;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias_e && n < p.N) {
-          const uint2 b2 = *(const uint2*)(bias_e + n);
-          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+          bias_x4(bias_e + n, bd);
         }
 #pragma unroll
         for (int mi = 0; mi < X_MI; ++mi) {
@@ -438,9 +423,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
         if (n >= p.N) continue;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias_e) {
-          const uint2 b2 = *(const uint2*)(bias_e + n);
-          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+          bias_x4(bias_e + n, bd);
         }
 #pragma unroll
         for (int mi = 0; mi < X_MI; ++mi) {
@@ -691,20 +674,7 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
       const int oc = nb * NBO + wn * 32 + 8 * q + 4 * fh;  // first of 4 outputs
       float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       if (bias_e) {
-        if (FMT == 0) {
-          const uint2 g2 = *(const uint2*)(bias_e + oc), u2 = *(const uint2*)(bias_e + p.N + oc);
-          bg[0] = bf16_to_f32(g2.x & 0xffffu); bg[1] = bf16_to_f32(g2.x >> 16);
-          bg[2] = bf16_to_f32(g2.y & 0xffffu); bg[3] = bf16_to_f32(g2.y >> 16);
-          bu[0] = bf16_to_f32(u2.x & 0xffffu); bu[1] = bf16_to_f32(u2.x >> 16);
-          bu[2] = bf16_to_f32(u2.y & 0xffffu); bu[3] = bf16_to_f32(u2.y >> 16);
-        } else {
-          const u32x4_t b4 = *(const u32x4_t*)(bias_e + 2 * oc);
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            bg[c] = bf16_to_f32(b4[c] & 0xffffu);
-            bu[c] = bf16_to_f32(b4[c] >> 16);
-          }
-        }
+        gate_up_bias_x4(bias_e, p.N, oc, FMT != 0, bg, bu);
       }
 #pragma unroll
       for (int mi = 0; mi < W_MI; ++mi) {
@@ -738,9 +708,7 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
         const int n = nb * W_BN + lc;
         float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (bias_e && n < p.N) {
-          const uint2 b2 = *(const uint2*)(bias_e + n);
-          bd[0] = bf16_to_f32(b2.x & 0xffffu); bd[1] = bf16_to_f32(b2.x >> 16);
-          bd[2] = bf16_to_f32(b2.y & 0xffffu); bd[3] = bf16_to_f32(b2.y >> 16);
+          bias_x4(bias_e + n, bd);
         }
 #pragma unroll
         for (int mi = 0; mi < W_MI; ++mi) {
