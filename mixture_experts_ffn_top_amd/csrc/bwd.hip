@@ -30,29 +30,7 @@ constexpr int TT = 64;  // transpose tile
 // seg[e] = sum over e' < e of round_up(rows of e', 64); seg[L] = the total
 __global__ __launch_bounds__(64) void seg_offsets_kernel(const int32_t* __restrict__ offsets, int L,
                                                          int32_t* __restrict__ seg) {
-  const int lane = threadIdx.x;
-  const int per = (L + 63) / 64;
-  const int e0 = lane * per;
-  int sum = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = e0 + i;
-    if (e < L) sum += (offsets[e + 1] - offsets[e] + TT - 1) / TT * TT;
-  }
-  int inc = sum;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(inc, o, MOE_WAVE);
-    if (lane >= o) inc += v;
-  }
-  int run = inc - sum;
-  for (int i = 0; i < per; ++i) {
-    const int e = e0 + i;
-    if (e < L) {
-      seg[e] = run;
-      run += (offsets[e + 1] - offsets[e] + TT - 1) / TT * TT;
-    }
-  }
-  if (lane == 63) seg[L] = inc;
+  wave_expert_prefix(offsets, L, seg, [](int rows) { return (rows + TT - 1) / TT * TT; });
 }
 
 // dst[c, q] for the padded row q of column block blockIdx.x, q block

@@ -38,6 +38,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// ---------------------------------------------------------------- experts
+// Exclusive prefix over the L experts of blocks(rows of e), rows = offsets[e+1]
+// - offsets[e]: out[e] for e < L and the total in out[L].  Run by one whole
+// wave; lane i takes ceil(L/64) consecutive experts.
+template <typename Blocks>
+__device__ __forceinline__ void wave_expert_prefix(const int32_t* offsets, int L, int32_t* out, Blocks blocks) {
+  const int lane = threadIdx.x & 63;
+  const int per = (L + 63) / 64;
+  const int e0 = lane * per;
+  int sum = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < L) sum += blocks(offsets[e + 1] - offsets[e]);
+  }
+  int inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(inc, o, MOE_WAVE);
+    if (lane >= o) inc += v;
+  }
+  int run = inc - sum;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < L) {
+      out[e] = run;
+      run += blocks(offsets[e + 1] - offsets[e]);
+    }
+  }
+  if (lane == 63) out[L] = inc;
+}
+
 // ---------------------------------------------------------------- biases
 // The bf16 biases of four consecutive outputs at p (8-byte aligned), as floats.
 __device__ __forceinline__ void bias_x4(const uint16_t* p, float* b) {

@@ -196,30 +196,7 @@ void grouped_gemm_bf16_kernel(const GemmArgs p) {
   } else {
 
   // ---- prefix of 256-row blocks per expert (wave 0), in LDS
-  if (wave == 0) {
-    const int per = (L + 63) / 64;
-    const int e0 = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) sum += (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
-    }
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, MOE_WAVE);
-      if (lane >= o) inc += v;
-    }
-    int run = inc - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) {
-        s_mbp[e] = run;
-        run += (p.offsets[e + 1] - p.offsets[e] + BM - 1) / BM;
-      }
-    }
-    if (lane == 63) s_mbp[L] = inc;
-  }
+  if (wave == 0) wave_expert_prefix(p.offsets, L, s_mbp, [](int rows) { return (rows + BM - 1) / BM; });
   __syncthreads();
 
   const int NB = (p.N + NBO - 1) / NBO;

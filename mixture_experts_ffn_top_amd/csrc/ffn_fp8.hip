@@ -130,30 +130,7 @@ void grouped_gemm_fp8_kernel(const Fp8GemmArgs p) {
   const int L = p.L;
 
   // ---- prefix of 256-row blocks per expert (wave 0), in LDS
-  if (wave == 0) {
-    const int per = (L + 63) / 64;
-    const int e0 = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) sum += (p.offsets[e + 1] - p.offsets[e] + Q_BM - 1) / Q_BM;
-    }
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, MOE_WAVE);
-      if (lane >= o) inc += v;
-    }
-    int run = inc - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) {
-        s_mbp[e] = run;
-        run += (p.offsets[e + 1] - p.offsets[e] + Q_BM - 1) / Q_BM;
-      }
-    }
-    if (lane == 63) s_mbp[L] = inc;
-  }
+  if (wave == 0) wave_expert_prefix(p.offsets, L, s_mbp, [](int rows) { return (rows + Q_BM - 1) / Q_BM; });
   __syncthreads();
 
   constexpr int NBO = (MODE == F8_GATE_UP) ? Q_BN / 2 : Q_BN;  // output columns per tile

@@ -84,31 +84,7 @@ __device__ __forceinline__ void f_block_barrier() {
 // Prefix of 32-row blocks per expert into s_mbp[0 .. L] (wave 0), then a
 // barrier.
 __device__ __forceinline__ void fused_block_prefix(const int32_t* offsets, int L, int32_t* s_mbp) {
-  const int lane = threadIdx.x & 63;
-  if ((threadIdx.x >> 6) == 0) {
-    const int per = (L + 63) / 64;
-    const int e0 = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) sum += (offsets[e + 1] - offsets[e] + F_BM - 1) / F_BM;
-    }
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, MOE_WAVE);
-      if (lane >= o) inc += v;
-    }
-    int run = inc - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) {
-        s_mbp[e] = run;
-        run += (offsets[e + 1] - offsets[e] + F_BM - 1) / F_BM;
-      }
-    }
-    if (lane == 63) s_mbp[L] = inc;
-  }
+  if ((threadIdx.x >> 6) == 0) wave_expert_prefix(offsets, L, s_mbp, [](int rows) { return (rows + F_BM - 1) / F_BM; });
   __syncthreads();
 }
 

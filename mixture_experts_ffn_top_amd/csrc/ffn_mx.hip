@@ -95,31 +95,8 @@ struct MxTile {
 // LDS may be overwritten.
 template <int BM>
 __device__ __forceinline__ bool mx_map_tile(const int32_t* offsets, int L, int NB, int32_t* s_mbp, MxTile& t) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave == 0) {
-    const int per = (L + 63) / 64;
-    const int e0 = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) sum += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-    }
-    int inc = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, MOE_WAVE);
-      if (lane >= o) inc += v;
-    }
-    int run = inc - sum;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e < L) {
-        s_mbp[e] = run;
-        run += (offsets[e + 1] - offsets[e] + BM - 1) / BM;
-      }
-    }
-    if (lane == 63) s_mbp[L] = inc;
-  }
+  const int wave = threadIdx.x >> 6;
+  if (wave == 0) wave_expert_prefix(offsets, L, s_mbp, [](int rows) { return (rows + BM - 1) / BM; });
   __syncthreads();
   const int total = s_mbp[L] * NB;
   const int per_xcd = (total + 7) >> 3;
