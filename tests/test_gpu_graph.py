@@ -25,10 +25,12 @@ def moe():
 
 @pytest.mark.parametrize("cid,changes", [
     (1, {}),                                                     # softmax gate, bf16
+    (2, {"T": 512}),                                             # Mixtral dims, split-K down tail round
     (3, {"T": 512}),                                             # sink router, shared experts
     (4, {"T": 300}),                                             # interleaved swigluoai with biases
     (5, {"T": 256, "E": 16, "H": 1024, "D": 512}),               # fp8 block-scaled
     (6, {"T": 256, "E": 16, "H": 1024, "D": 512}),               # MXFP4 x MXFP8
+    (7, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # MXFP4 weights x bf16 activations (W4A16)
     (8, {}),                                                     # single-launch FFN (decode)
     (9, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # single-launch FFN, MXFP4 x MXFP8
 ])
