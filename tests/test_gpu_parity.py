@@ -168,6 +168,13 @@ def _routing(T, E, k, seed, mode="random"):
     (1000, 64, 4, 0, 64, "half_empty", True),
     (1, 8, 2, 0, 8, "random", False),
     (5000, 1024, 3, 0, 1024, "random", False),
+    # the one-workgroup form (at most 4096 slots) at its limit and one token past it, with a
+    # masked expert slice, with all 1024 experts, and with a single expert
+    (512, 64, 8, 0, 64, "random", False),
+    (513, 64, 8, 0, 64, "random", False),
+    (1000, 256, 4, 64, 64, "random", True),
+    (1365, 1024, 3, 0, 1024, "random", False),
+    (700, 1, 1, 0, 1, "random", False),
 ])
 def test_build_indices(moe, T, E, k, start, L, mode, masked):
     idx, w = _routing(T, E, k, 7 + T, mode)
