@@ -102,6 +102,9 @@ def fused_ffn_bytes(cfg, used: int) -> int:
     if cfg.operand_dtype == "mxfp4":
         w = (2 * D * H + H * D) * (1 / 2 + 1 / 32)
         return int(used * w + R * H * (1 + 1 / 32) + 2 * R * D * (1 + 1 / 32) + R * H * 2)
+    if cfg.operand_dtype == "mxfp4_a16":   # MX weights, bf16 rows and A, fp32 O
+        w = (2 * D * H + H * D) * (1 / 2 + 1 / 32)
+        return int(used * w + R * H * 2 + 2 * R * D * 2 + R * H * 4)
     return used * (2 * D * H + H * D) * 2 + R * H * 2 + 2 * R * D * 2 + R * H * 4
 
 
@@ -217,6 +220,9 @@ EXTRA_TRACES = [
     ("trace9", 9, "mxfp4_decode_fused_ffn_kernel_stats.txt",
      "MXFP4 x MXFP8 decode batch through the single-launch FFN: T=256 tokens, hidden 7168, 256 experts, "
      "top-8 sigmoid router, moe_dim 2048, SiLU"),
+    ("trace10", 10, "mxfp4_a16_decode_fused_ffn_kernel_stats.txt",
+     "MXFP4 x bf16 (W4A16) decode batch through the single-launch FFN: T=256 tokens, hidden 7168, 256 "
+     "experts, top-8 sigmoid router, moe_dim 2048, SiLU"),
 ]
 
 
@@ -720,7 +726,8 @@ def main():
         ffn_bytes = fused_ffn_bytes(cfg, used)
         t_ffn = t_gu + t_dn
         gbs = ffn_bytes / (t_ffn * 1e-3) / 1e9
-        kind = "MXFP4 weights, MXFP8 activations" if cfg.operand_dtype == "mxfp4" else "bf16"
+        kind = {"mxfp4": "MXFP4 weights, MXFP8 activations", "mxfp4_a16": "MXFP4 weights, bf16 activations"}.get(
+            cfg.operand_dtype, "bf16")
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
                 "kernel": f"single-launch expert FFN (gate_up + activation + down, {kind})",

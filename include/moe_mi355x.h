@@ -365,19 +365,20 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t opera
  * GEMM with the gated activation (L1) and the down GEMM (L2) in one launch,
  * pipelined across workgroups with per-row-block arrival counters and no
  * per-launch memset.  It computes what moe_grouped_ffn computes (same
- * arguments and results: A in bf16, or MXFP8 for MX operands; O in fp32 or
- * bf16), for bf16 operands and for MXFP4 weights with MXFP8 activations
- * (the page's block-scaled form, whose L1 re-quantises A); it pays off where
- * the two-launch form is bound by weight streaming and launch gaps (small
- * batches, decode).
+ * arguments and results: A in bf16, or MXFP8 for W4A8; O in fp32 or bf16),
+ * for bf16 operands and for MXFP4 weights with MXFP8 activations (the page's
+ * block-scaled form, whose L1 re-quantises A) or with bf16 activations; it
+ * pays off where the two-launch form is bound by weight streaming and launch
+ * gaps (small batches, decode).
  *
  * Differences from moe_grouped_ffn:
- *   operand_dtype  MOE_DTYPE_BF16 or MOE_DTYPE_MXFP4_W4A8; hidden_dim % 64
- *                  == 0 (MX: % 128), moe_dim % 128 == 0.  MX takes x_perm
- *                  (or the per-token x) with x_perm_scale as moe_grouped_ffn
- *                  does, and computes bit for bit what moe_grouped_ffn's MX
- *                  path computes unless the down items are split along K
- *                  (below)
+ *   operand_dtype  MOE_DTYPE_BF16, MOE_DTYPE_MXFP4_W4A8 or
+ *                  MOE_DTYPE_MXFP4_W4A16; hidden_dim % 64 == 0 (MX: % 128),
+ *                  moe_dim % 128 == 0.  W4A8 takes x_perm (or the per-token
+ *                  x) with x_perm_scale, W4A16 bf16 x_perm or x without it,
+ *                  as moe_grouped_ffn does; both compute bit for bit what
+ *                  moe_grouped_ffn's MX paths compute unless the down items
+ *                  are split along K (below)
  *   act_workspace  moe_ffn_fused_workspace_bytes(max_rows, hidden_dim,
  *                  moe_dim, n_local_experts) bytes (the same for both
  *                  operand types), holding the launch's control words (work
@@ -385,7 +386,7 @@ int64_t moe_ffn_workspace_bytes(int32_t max_rows, int32_t moe_dim, int32_t opera
  *                  split down tile, and an arrival counter per 32-row block,
  *                  the last at the very end of the act_workspace_bytes the
  *                  caller passes), A from byte offset 1280 (bf16 [max_rows,
- *                  D]; MX: e4m3 codes [max_rows, D], then from byte offset
+ *                  D]; W4A8: e4m3 codes [max_rows, D], then from byte offset
  *                  1280 + round_up(max_rows * D, 256) the E8M0 scale bytes
  *                  [max_rows, D/32]), and the fp32 partial tiles of the down
  *                  items split along K.  The

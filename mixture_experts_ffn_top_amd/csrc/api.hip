@@ -479,8 +479,10 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
   REQUIRE(H >= 64 && H % 64 == 0, "moe_grouped_ffn_fused: hidden_dim must be a positive multiple of 64 (got %d)", H);
   REQUIRE(D >= 128 && D % 128 == 0, "moe_grouped_ffn_fused: moe_dim must be a positive multiple of 128 (got %d)", D);
   REQUIRE(L >= 1 && L <= 1024, "moe_grouped_ffn_fused: n_local_experts must be in [1, 1024] (got %d)", L);
-  const bool mx = a->operand_dtype == MOE_DTYPE_MXFP4_W4A8;
-  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16 || mx, "moe_grouped_ffn_fused: operand_dtype must be BF16 or MXFP4_W4A8");
+  const bool a16 = a->operand_dtype == MOE_DTYPE_MXFP4_W4A16;
+  const bool mx = a->operand_dtype == MOE_DTYPE_MXFP4_W4A8 || a16;
+  REQUIRE(a->operand_dtype == MOE_DTYPE_BF16 || mx,
+          "moe_grouped_ffn_fused: operand_dtype must be BF16, MXFP4_W4A8 or MXFP4_W4A16");
   REQUIRE(a->expert_offsets != nullptr, "moe_grouped_ffn_fused: expert_offsets is required");
   REQUIRE(a->activation == MOE_ACT_SILU || a->activation == MOE_ACT_SWIGLUOAI || a->activation == MOE_ACT_GELU_TANH,
           "moe_grouped_ffn_fused: unknown activation %d", a->activation);
@@ -506,7 +508,7 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
               aligned16(a->b_down),
           "moe_grouped_ffn_fused: tensors must be 16-byte aligned");
   // bytes per activation element; one expert's gate_up weights: 2D rows of H elements
-  const int64_t es = mx ? 1 : 2;
+  const int64_t es = (mx && !a16) ? 1 : 2;
   const int64_t wbytes = mx ? (int64_t)D * H : (int64_t)2 * D * H * 2;
   const int64_t x_rows = gather && a->num_tokens > 0 ? a->num_tokens : R;
   REQUIRE(x_rows * H * es < ((int64_t)1 << 31) && (int64_t)R * D * es < ((int64_t)1 << 31) &&
@@ -514,8 +516,12 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
           "moe_grouped_ffn_fused: x (or x_perm), the activation buffer and one expert's weights must each be under 2 GiB");
   if (mx) {
     REQUIRE(H % 128 == 0, "moe_grouped_ffn_fused: MX needs hidden_dim a multiple of 128 (got %d)", H);
-    REQUIRE(a->x_perm_scale != nullptr,
-            "moe_grouped_ffn_fused: MX takes x_perm (or per-token x) and x_perm_scale, quantised by moe_build_indices");
+    if (a16)
+      REQUIRE(a->x_perm_scale == nullptr, "moe_grouped_ffn_fused: W4A16 takes bf16 activations, no x_perm_scale");
+    else
+      REQUIRE(a->x_perm_scale != nullptr,
+              "moe_grouped_ffn_fused: W4A8 takes x_perm (or per-token x) and x_perm_scale, quantised by "
+              "moe_build_indices");
     REQUIRE(a->w_gate_up_scale != nullptr && a->w_down_scale != nullptr,
             "moe_grouped_ffn_fused: MXFP4 weights need w_gate_up_scale and w_down_scale");
     REQUIRE(aligned16(a->x_perm_scale) && aligned16(a->w_gate_up_scale) && aligned16(a->w_down_scale),
@@ -553,6 +559,9 @@ moe_status_t moe_grouped_ffn_fused(const moe_ffn_args_t* a, void* stream) {
     q.out = a->expert_out;
     q.out_bf16 = a->out_dtype == MOE_DTYPE_BF16;
     q.events = (hipEvent_t const*)a->timing_events;
+    if (a16)
+      return hip_status(moe::launch_ffn_fused_w4a16(q, a->act_workspace, a->act_workspace_bytes, (hipStream_t)stream),
+                        "moe_grouped_ffn_fused");
     return hip_status(moe::launch_ffn_fused_mx(q, a->act_workspace, a->act_workspace_bytes, (hipStream_t)stream),
                       "moe_grouped_ffn_fused");
   }

@@ -418,6 +418,50 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   fused_exit(p.ctl, arrive, total_mb, s_item + 1);
 }
 
+// L2 epilogue of the MX kernels: O = sc * C + bias for the 32 x 256 tile,
+// staged in LDS (rows of 256 outputs + 16 bytes of bank skew) so that each
+// store moves whole row pieces.  acc[ni][4q + c] is C[fr][wave*64 + ni*32 +
+// 8q + 4fh + c].  Called by the whole workgroup; smem must be free.
+template <bool OUT_BF16>
+__device__ __forceinline__ void fused_store_o_tile(const f32x16_t (&acc)[2], float sc, const uint16_t* bias, int H,
+                                                   int nb, int row_beg, int row_end, void* out, uint8_t* smem) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, fr = lane & 31, fh = lane >> 5;
+  constexpr int ES = OUT_BF16 ? 2 : 4;
+  constexpr int PITCH = F_BN * ES + 16;
+  __syncthreads();
+#pragma unroll
+  for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int lc = wave * 64 + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
+      const int n = nb * F_BN + lc;
+      float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (bias && n < H) bias_x4(bias + n, bd);
+      float v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = acc[ni][4 * q + c] * sc + bd[c];
+      uint8_t* dst = smem + fr * PITCH + lc * ES;
+      if (OUT_BF16) {
+        uint2 w;
+        w.x = pack_bf16x2_rne(v[0], v[1]);
+        w.y = pack_bf16x2_rne(v[2], v[3]);
+        *(uint2*)dst = w;
+      } else {
+        *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
+      }
+    }
+  __syncthreads();
+  // a row is F_BN * ES bytes: 32 (bf16) or 64 (fp32) lanes of 16 bytes
+  constexpr int LPR = F_BN * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per store
+  const int cpart = lane % LPR;
+  const int n = nb * F_BN + cpart * (16 / ES);
+  for (int r = wave * RPI + lane / LPR; r < F_BM; r += F_NW * RPI) {
+    const int row = row_beg + r;
+    if (row < row_end && n < H)
+      *(u32x4_t*)((uint8_t*)out + ((int64_t)row * H + n) * ES) = *(const u32x4_t*)(smem + r * PITCH + cpart * 16);
+  }
+}
+
 // ---------------------------------------------------------------- MX
 // MXFP4 weights x MXFP8 activations.  A k stage of 128: 4 KB of e4m3
 // activation rows and 16 KB of packed e2m1 weight rows, 3 stages deep, plus
@@ -677,46 +721,260 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
           continue;
         }
       }
-      // the tile's outputs go through LDS (rows of 256 outputs + 16 bytes of
-      // bank skew) so that each store moves whole row pieces
-      const float sc = p.s_d ? p.s_d[e] : 1.0f;
-      const uint16_t* bias = p.b_d ? p.b_d + (int64_t)e * p.H : nullptr;
-      constexpr int ES = OUT_BF16 ? 2 : 4;
-      constexpr int PITCH = F_BN * ES + 16;
-      __syncthreads();  // the stage buffers are free
+      fused_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
+                                   row_beg, row_end, p.out, smem);
+    }
+    __syncthreads();  // the stage buffers and the item word are reused by the next item
+  }
+
+  fused_exit(p.ctl, p.arrive, total_mb, s_item + 1);
+}
+
+// ---------------------------------------------------------------- W4A16
+// MXFP4 weights x bf16 activations: the weights are dequantised to bf16 in
+// registers per fragment (v_cvt_scalef32_pk_bf16_fp4, exact for every E8M0
+// scale) and multiplied on v_mfma_f32_32x32x16_bf16, in the k order of the
+// two-launch W4A16 GEMMs (mx_common.h); A stays bf16.  A k stage of 128:
+// 8 KB of bf16 activation rows and 16 KB of packed e2m1 weight rows.  Two
+// workgroups share a CU with two activation slots beside three weight slots
+// (64 KB, plus the weight rows' scale dwords): each iteration issues the
+// next stage's activations and then the weight stage after that, so the
+// wait for a stage (loads retire in order per wave) leaves the next weight
+// stage in flight.
+constexpr int V_A_BYTES = F_BM * MX_A16_ROW;             // 8 KB
+constexpr int V_B_BYTES = F_BN * MX_B_ROW;               // 16 KB
+constexpr int V_NA = 2, V_NB = 3;                        // activation and weight slots
+constexpr int V_LPW_A = V_A_BYTES / 1024 / F_NW;         // 1 KB loads per wave per stage: 2
+constexpr int V_LPW_B = V_B_BYTES / 1024 / F_NW;         // 4
+constexpr int V_B_OFF = V_NA * V_A_BYTES;
+constexpr int V_BS_OFF = V_B_OFF + V_NB * V_B_BYTES;     // weight scales: 2 slots x 256 rows x 16 bytes
+constexpr int V_PIPE = V_BS_OFF + 2 * F_BN * 16;         // 72 KB
+constexpr int V_APITCH = 128 * 2 + 16;                   // staged A rows: 128 bf16 + bank skew
+static_assert(V_NB * F_BN * 4 <= 2 * F_BN * 16, "single-stage scale slots fit");
+static_assert(V_LPW_B < 64, "vmcnt range");
+static_assert(M_WG_PER_CU * (V_PIPE + (1024 + 4) * 4) <= 160 * 1024, "two W4A16 workgroups share a CU");
+static_assert(F_BM * V_APITCH <= V_BS_OFF, "staged A rows fit the stages");
+static_assert(F_BM * (F_BN * 4 + 16) <= V_BS_OFF, "a staged fp32 output tile fits the stages");
+
+struct FusedW4Args {
+  const int32_t* offsets;
+  int L, H, D;
+  const uint16_t* x;           // bf16 [T, H] gathered through sorted_token, or [R, H] rows (sorted_token null)
+  const int32_t* sorted_token;
+  const uint8_t* w_gu;         // packed e2m1 OUT_IN [L, 2D, H/2]
+  const uint8_t* w_gu_scale;   // E8M0 [L, 2D, H/32]
+  const uint8_t* w_d;          // packed e2m1 OUT_IN [L, H, D/2]
+  const uint8_t* w_d_scale;    // E8M0 [L, H, D/32]
+  const uint16_t* b_gu;        // [L, 2D] or null
+  const uint16_t* b_d;         // [L, H] or null
+  const float* s_gu;           // [L] or null
+  const float* s_d;
+  float alpha, limit;
+  uint16_t* act;               // A bf16 [R, D]
+  void* out;                   // O [R, H]
+  int32_t* ctl;                // as FusedArgs
+  int32_t* arrive;
+  float* part;
+  int S, max_rows, row_blocks, tiles_cap;
+};
+
+template <int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(F_NT) void fused_ffn_w4a16_kernel(const FusedW4Args p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int32_t* s_mbp = (int32_t*)(smem + V_PIPE);  // row-block prefix per expert, kept for the whole launch
+  int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-part / last-out flag
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int L = p.L;
+  int32_t* err = p.ctl + 2;
+  int32_t* tile_done = p.ctl + 4;
+
+  fused_block_prefix(p.offsets, L, s_mbp);
+  // more rows than max_rows: do nothing (as the bf16 kernel)
+  const bool too_many = p.offsets[L] > p.max_rows || s_mbp[L] > p.row_blocks;
+  if (too_many && tid == 0 && blockIdx.x == 0) __hip_atomic_store(err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int total_mb = too_many ? 0 : s_mbp[L];
+  const int NB1 = p.D / 128, NB2 = (p.H + F_BN - 1) / F_BN;
+  const int n2 = total_mb * NB2;
+  const int S = (p.S > 1 && n2 <= p.tiles_cap) ? p.S : 1;
+  const int n1 = total_mb * NB1, n_all = n1 + n2 * S;
+  const int fr = lane & 31, fh = lane >> 5;
+
+  for (;;) {
+    if (tid == 0) s_item[0] = atomicAdd(p.ctl, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n_all) break;
+    const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
+    const bool l2 = t.l2;
+    const int e = t.e, nb = t.nb, part = t.part, gm = t.gm, row_beg = t.row_beg, row_end = t.row_end;
+    if (l2) fused_wait(p.arrive + gm, NB1, err);
+
+    // ---- operands of this item.  K stages ks = kt0 + kt of the whole row.
+    const int K = l2 ? p.D : p.H;
+    const int KS = K / MX_BK;
+    const int parts = l2 ? S : 1;
+    const int kt0 = part * KS / parts;
+    const int KT = (part + 1) * KS / parts - kt0;
+    const int G = (KS % 4 == 0 && kt0 % 4 == 0 && KT % 4 == 0) ? 4 : 1;
+    const uint32_t srow = (uint32_t)K / 32u;
+    const int32_t* gather = l2 ? nullptr : p.sorted_token;
+    const uint16_t* a_base = l2 ? p.act : p.x;
+    const uint8_t* b_base = l2 ? p.w_d + (int64_t)e * p.H * (p.D / 2) : p.w_gu + (int64_t)e * 2 * p.D * (p.H / 2);
+    const uint8_t* bs_base =
+        l2 ? p.w_d_scale + (int64_t)e * p.H * (p.D / 32) : p.w_gu_scale + (int64_t)e * 2 * p.D * (p.H / 32);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)bs_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    auto w_row = [&](int trow) -> int {
+      if (l2) return min(nb * F_BN + trow, p.H - 1);
+      const int q = trow / 64, rr = trow % 64, isup = rr / 32, j = rr % 32;
+      const int oc = nb * 128 + q * 32 + j;
+      return (FMT == 0) ? (isup ? p.D + oc : oc) : (2 * oc + isup);
+    };
+    // A: wave w loads tile rows 8w .. 8w+7 as two 1 KB loads of 4 rows x 16
+    // chunks (rows past the expert's end read zeros).  B: rows 64w .. 64w+63
+    // (16 rows x 4 chunks per 1 KB) and their scale dwords, one row per lane.
+    uint32_t a_voff[V_LPW_A], b_voff[V_LPW_B], bs_voff;
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+    for (int i = 0; i < V_LPW_A; ++i) {
+      const int trow = (wave * V_LPW_A + i) * 4 + (lane >> 4);
+      const int r = row_beg + trow;
+      if (r < row_end) {
+        const uint32_t ar = gather ? (uint32_t)gather[r] : (uint32_t)r;
+        a_voff[i] = ar * (uint32_t)K * 2u + (uint32_t)(((lane & 15) ^ (trow & 15)) * 16);
+      } else {
+        a_voff[i] = F_OOB;
+      }
+    }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int lc = wave * 64 + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
-          const int n = nb * F_BN + lc;
-          float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (bias && n < p.H) {
-            bias_x4(bias + n, bd);
-          }
-          float v[4];
+    for (int i = 0; i < V_LPW_B; ++i) {
+      const int trow = (wave * V_LPW_B + i) * 16 + (lane >> 2);
+      b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
+    }
+    bs_voff = (uint32_t)w_row(wave * 64 + lane) * srow;
+
+    auto a_slot = [&](int kt) { return smem + (kt % V_NA) * V_A_BYTES; };
+    auto b_slot = [&](int kt) { return smem + V_B_OFF + (kt % V_NB) * V_B_BYTES; };
+    // scale group g = kt / 4 in slot g % 2 (rows 16 bytes apart), or stage
+    // kt in slot kt % 3 (rows 4 bytes apart)
+    auto bs_slot = [&](int kt) {
+      return smem + V_BS_OFF + (G == 4 ? ((kt / 4) % 2) * (F_BN * 16) : (kt % V_NB) * (F_BN * 4));
+    };
+    auto issue_a = [&](int kt) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) v[c] = acc[ni][4 * q + c] * sc + bd[c];
-          uint8_t* dst = smem + fr * PITCH + lc * ES;
-          if (OUT_BF16) {
-            uint2 w;
-            w.x = pack_bf16x2_rne(v[0], v[1]);
-            w.y = pack_bf16x2_rne(v[2], v[3]);
-            *(uint2*)dst = w;
-          } else {
-            *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
+      for (int i = 0; i < V_LPW_A; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(a_slot(kt) + (wave_s * V_LPW_A + i) * 1024), 16,
+                                                 a_voff[i], (kt0 + kt) * MX_A16_ROW, 0, 0);
+    };
+    auto issue_b = [&](int kt) {
+      const int ks = kt0 + kt;
+      // the stage's scale group first (when it starts one), then its rows
+      if (kt % G == 0) {
+        if (G == 4)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 16), 16, bs_voff,
+                                                   ks * 4, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 4), 4, bs_voff,
+                                                   ks * 4, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < V_LPW_B; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(b_slot(kt) + (wave_s * V_LPW_B + i) * 1024), 16,
+                                                 b_voff[i], ks * MX_B_ROW, 0, 0);
+    };
+
+    f32x16_t acc[2];
+#pragma unroll
+    for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[ni][r] = 0.0f;
+    // Load order per wave: B(0), A(0), B(1), then per iteration kt: A(kt+1),
+    // B(kt+2).  Iteration kt needs A(kt) and B(kt); only B(kt+1), issued
+    // after A(kt), may still be in flight (its V_LPW_B row loads last).
+    // A(kt+1) goes into the activation slot of stage kt-1 and B(kt+2) into
+    // its weight slot, both free once every wave has passed iteration kt's
+    // barrier.
+    issue_b(0);
+    issue_a(0);
+    if (KT > 1) issue_b(1);
+    for (int kt = 0; kt < KT; ++kt) {
+      if (kt + 1 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm(V_LPW_B));
+      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      f_block_barrier();
+      if (kt + 1 < KT) issue_a(kt + 1);
+      if (kt + 2 < KT) issue_b(kt + 2);
+      const uint8_t* ast = a_slot(kt);
+      const uint8_t* bst = b_slot(kt);
+      const uint8_t* bs_l = bs_slot(kt) + (kt % G) * 4;  // row r's scale dword at r * 4 G
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {  // steps 4*half .. 4*half+3: one weight chunk, one MX block
+        u32x4_t wq[2];
+        float wsc[2];
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni) {
+          const int row = wave * 64 + ni * 32 + fr;
+          wq[ni] = *(const u32x4_t*)(bst + mx_b_off(row, 2 * fh + half));
+          wsc[ni] = e8m0_f32((*(const uint32_t*)(bs_l + row * 4 * G) >> (8 * (2 * fh + half))) & 0xffu);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int st = 4 * half + j;
+          const bf16x8_t af = *(const bf16x8_t*)(ast + mx_a16_off(fr, 8 * fh + st));
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni) {
+            const uint32_t d = wq[ni][j];
+            const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 0);
+            const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 1);
+            const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 2);
+            const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, wsc[ni], 3);
+            const bf16x8_t bw = bf16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            acc[ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw, af, acc[ni], 0, 0, 0);
           }
         }
-      __syncthreads();
-      // a row is F_BN * ES bytes: 32 (bf16) or 64 (fp32) lanes of 16 bytes
-      constexpr int LPR = F_BN * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per store
-      const int cpart = lane % LPR;
-      const int n = nb * F_BN + cpart * (16 / ES);
-      for (int r = wave * RPI + lane / LPR; r < F_BM; r += F_NW * RPI) {
-        const int row = row_beg + r;
-        if (row < row_end && n < p.H)
-          *(u32x4_t*)((uint8_t*)p.out + ((int64_t)row * p.H + n) * ES) = *(const u32x4_t*)(smem + r * PITCH + cpart * 16);
       }
+    }
+
+    // ---- epilogue.  acc[ni][4q + c] is C[row][col], row = fr, col = wave*64 + ni*32 + 8q + 4fh + c
+    if (!l2) {
+      // block 0 holds the gate columns, block 1 the up columns of the wave's
+      // 32 outputs; A in bf16, staged in LDS and stored as whole row pieces
+      const float sc = p.s_gu ? p.s_gu[e] : 1.0f;
+      const uint16_t* bias = p.b_gu ? p.b_gu + (int64_t)e * 2 * p.D : nullptr;
+      __syncthreads();  // the stage buffers are free
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int lc = wave * 32 + 8 * q + 4 * fh;  // first of 4 of the tile's 128 outputs
+        float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (bias) gate_up_bias_x4(bias, p.D, nb * 128 + lc, FMT != 0, bg, bu);
+        float a[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          a[c] = gated_act<ACT>(acc[0][4 * q + c] * sc + bg[c], acc[1][4 * q + c] * sc + bu[c], p.alpha, p.limit);
+        uint2 v;
+        v.x = pack_bf16x2_rne(a[0], a[1]);
+        v.y = pack_bf16x2_rne(a[2], a[3]);
+        *(uint2*)(smem + fr * V_APITCH + lc * 2) = v;
+      }
+      __syncthreads();
+      // 32 rows x 16 pieces of 16 bytes
+      for (int i = tid; i < F_BM * 16; i += F_NT) {
+        const int r = i >> 4, pc = i & 15;
+        if (row_beg + r < row_end)
+          *(u32x4_t*)(p.act + (int64_t)(row_beg + r) * p.D + nb * 128 + pc * 8) =
+              *(const u32x4_t*)(smem + r * V_APITCH + pc * 16);
+      }
+      fused_count_in(p.arrive + gm);  // this part of the row block is published
+    } else {
+      if (S > 1) {
+        const int t2 = gm * NB2 + nb;
+        if (!fused_split_reduce(acc, p.part + (int64_t)t2 * S * F_PART_FLOATS, part, S, tile_done + t2, s_item + 1)) {
+          __syncthreads();
+          continue;
+        }
+      }
+      fused_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
+                                   row_beg, row_end, p.out, smem);
     }
     __syncthreads();  // the stage buffers and the item word are reused by the next item
   }
@@ -765,6 +1023,26 @@ hipError_t launch_fused_mx_kernel(KernelT kern, const FusedMxArgs& a, hipStream_
   if (grid <= 0) return hipErrorInvalidDevice;
   kern<<<grid, F_NT, lds, st>>>(a);
   return hipGetLastError();
+}
+
+template <typename KernelT>
+hipError_t launch_fused_w4_kernel(KernelT kern, const FusedW4Args& a, hipStream_t st) {
+  const int lds = V_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int grid = M_WG_PER_CU * fused_cu_count();
+  if (grid <= 0) return hipErrorInvalidDevice;
+  kern<<<grid, F_NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_fused_w4_act(const FusedW4Args& a, int fmt, int out_bf16, hipStream_t st) {
+  if (fmt == 0)
+    return out_bf16 ? launch_fused_w4_kernel(fused_ffn_w4a16_kernel<ACT, 0, true>, a, st)
+                    : launch_fused_w4_kernel(fused_ffn_w4a16_kernel<ACT, 0, false>, a, st);
+  return out_bf16 ? launch_fused_w4_kernel(fused_ffn_w4a16_kernel<ACT, 1, true>, a, st)
+                  : launch_fused_w4_kernel(fused_ffn_w4a16_kernel<ACT, 1, false>, a, st);
 }
 
 template <int ACT>
@@ -876,6 +1154,45 @@ hipError_t launch_ffn_fused_mx(const FfnMxParams& q, void* ws, int64_t ws_bytes,
   if (q.act_kind == ACT_SILU) err = launch_fused_mx_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
   else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_mx_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);
   else err = launch_fused_mx_act<ACT_GELU_TANH>(a, q.fmt, q.out_bf16, st);
+  if (err != hipSuccess) return err;
+  if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
+  if (q.events) err = hipEventRecord(q.events[2], st);
+  return err;
+}
+
+hipError_t launch_ffn_fused_w4a16(const FfnMxParams& q, void* ws, int64_t ws_bytes, hipStream_t st) {
+  hipError_t err;
+  const FusedLayout f = fused_layout(q.max_rows, q.H, q.D, q.L);
+  if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
+  FusedW4Args a{};
+  a.offsets = q.offsets;
+  a.L = q.L;
+  a.H = q.H;
+  a.D = q.D;
+  a.x = (const uint16_t*)q.x_perm;
+  a.sorted_token = q.sorted_token;
+  a.w_gu = q.w_gate_up;
+  a.w_gu_scale = q.w_gate_up_scale;
+  a.w_d = q.w_down;
+  a.w_d_scale = q.w_down_scale;
+  a.b_gu = q.b_gate_up;
+  a.b_d = q.b_down;
+  a.s_gu = q.gate_up_scales;
+  a.s_d = q.down_scales;
+  a.alpha = q.alpha;
+  a.limit = q.limit;
+  a.act = (uint16_t*)((uint8_t*)ws + f.act_off);
+  a.out = q.out;
+  a.ctl = (int32_t*)ws;
+  a.arrive = (int32_t*)((uint8_t*)ws + (ws_bytes & ~(int64_t)3)) - f.row_blocks;
+  a.part = (float*)((uint8_t*)ws + f.part_off);
+  a.S = f.S;
+  a.tiles_cap = f.tiles_cap;
+  a.max_rows = q.max_rows;
+  a.row_blocks = (int)f.row_blocks;
+  if (q.act_kind == ACT_SILU) err = launch_fused_w4_act<ACT_SILU>(a, q.fmt, q.out_bf16, st);
+  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_fused_w4_act<ACT_SWIGLUOAI>(a, q.fmt, q.out_bf16, st);
+  else err = launch_fused_w4_act<ACT_GELU_TANH>(a, q.fmt, q.out_bf16, st);
   if (err != hipSuccess) return err;
   if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
   if (q.events) err = hipEventRecord(q.events[2], st);

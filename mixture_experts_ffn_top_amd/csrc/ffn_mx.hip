@@ -436,11 +436,7 @@ void grouped_gemm_mx_kernel(const MxGemmArgs p) {
 // quarter of the cache lines (per stage they were as many lines as the
 // weight codes).
 //
-// Inside a stage the 8 k16 steps need not walk k in order, only the same way
-// for both operands: at step s lane 32h + r takes k [64h + 8s, +8).  Its 8
-// weights then come from one MX block (2h + s/4), from dword s%4 of the
-// 16-byte chunk 2h + s/4 of its weight row, and its 8 activations are chunk
-// 8h + s of the 256-byte activation row.
+// The k16 steps of a stage take k in the order mx_common.h gives for W4A16.
 // Two shapes, both 3 stages deep: 128-row tiles with 8 waves (2 x 4), and,
 // for batches of a few rows per expert (decode), 32-row tiles with 4 waves
 // whose 75 KB of LDS let two workgroups share a CU.  Such a batch is bound by
@@ -474,8 +470,7 @@ struct W4Shape {
   static_assert(BM != 32 || 2 * LDS <= 160 * 1024, "two 32-row workgroups share a CU");
 };
 
-// bf16 rows: 256 bytes, 16 chunks; chunk c of row r at c ^ (r & 15).
-__device__ __forceinline__ int w4_a_off(int row, int chunk) { return row * W_A_ROW + ((chunk ^ (row & 15)) << 4); }
+static_assert(W_A_ROW == MX_A16_ROW, "the bf16 activation rows of mx_common.h");
 
 struct W4GemmArgs {
   const int32_t* offsets;
@@ -630,7 +625,7 @@ void grouped_gemm_w4a16_kernel(const W4GemmArgs p) {
         for (int mi = 0; mi < W_MI; ++mi) {
           if (mi < live_mi) {
             const int row = wm * W_WTM + mi * 32 + fr;
-            const bf16x8_t af = *(const bf16x8_t*)(st + w4_a_off(row, 8 * fh + s));
+            const bf16x8_t af = *(const bf16x8_t*)(st + mx_a16_off(row, 8 * fh + s));
 #pragma unroll
             for (int ni = 0; ni < W_NI; ++ni)
               acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[ni], af, acc[mi][ni], 0, 0, 0);

@@ -195,7 +195,7 @@ hipError_t launch_ffn_mx(const FfnMxParams& p, hipStream_t st);
 // activation scales; the same weight fields.
 hipError_t launch_ffn_w4a16(const FfnMxParams& p, hipStream_t st);
 
-// Single-launch L1+L2 FFN for small batches (bf16 or MX operands): control words
+// Single-launch L1+L2 FFN for small batches (bf16, W4A8 or W4A16 operands): control words
 // (queue, exit count, error, one arrival counter per 32-row block) at the
 // start of the workspace, then A; zero when allocated, zero again after
 // every launch.
@@ -221,6 +221,9 @@ hipError_t launch_ffn_fused(const FfnBf16Params& p, void* ws, int64_t ws_bytes, 
 // The same schedule for MXFP4 weights x MXFP8 activations (p.act and
 // p.act_scale are ignored: A lives in the workspace).
 hipError_t launch_ffn_fused_mx(const FfnMxParams& p, void* ws, int64_t ws_bytes, hipStream_t st);
+// ... and for MXFP4 weights x bf16 activations (p.x_perm: bf16 rows or, with
+// sorted_token, bf16 tokens; A bf16 in the workspace).
+hipError_t launch_ffn_fused_w4a16(const FfnMxParams& p, void* ws, int64_t ws_bytes, hipStream_t st);
 
 hipError_t launch_combine(const void* O, int o_bf16, const int32_t* row_of_slot, const float* w,
                           const uint8_t* mask, int T, int k, int H, uint16_t* y, int n_shared,

@@ -51,6 +51,17 @@ __device__ __forceinline__ i32x8_t mx_frag_b(const uint8_t* st, int row, int kk,
   return i32x8_t{(int)c4[0], (int)c4[1], (int)c4[2], (int)c4[3], 0, 0, 0, 0};
 }
 
+// W4A16 (MXFP4 weights, bf16 activations on v_mfma_f32_32x32x16_bf16): a k
+// stage of 128 holds bf16 activation rows of 256 bytes (16 chunks) beside
+// the same packed e2m1 weight rows.  Inside a stage the 8 k16 steps need not
+// walk k in order, only the same way for both operands: at step s lane
+// 32h + r takes k [64h + 8s, +8).  Its 8 weights then come from one MX block
+// (2h + s/4), from dword s%4 of the 16-byte chunk 2h + s/4 of its weight
+// row, and its 8 activations are chunk 8h + s of the activation row.
+constexpr int MX_A16_ROW = MX_BK * 2;  // bytes per bf16 stage row
+// bf16 rows: chunk c of row r at c ^ (r & 15).
+__device__ __forceinline__ int mx_a16_off(int row, int chunk) { return row * MX_A16_ROW + ((chunk ^ (row & 15)) << 4); }
+
 // Shared exponent of an MXFP8 block with largest magnitude m (>= 0):
 // floor(log2 m) - 8, at least -127; 0 for m = 0.
 __device__ __forceinline__ int mx_shared_exp(float m) {

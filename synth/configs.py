@@ -82,6 +82,10 @@ CONFIGS = {
     9: MoEConfig(9, "mxfp4_decode", T=256, H=7168, E=256, k=8, D=2048,
                  router="sigmoid_sink", s=0, operand_dtype="mxfp4",
                  route_scale=1.0, global_scale=1.0, fused=True),
+    # config 7's batch (MXFP4 experts, bf16 activations) with the FFN in one launch
+    10: MoEConfig(10, "mxfp4_a16_decode", T=256, H=7168, E=256, k=8, D=2048,
+                  router="sigmoid_sink", s=0, operand_dtype="mxfp4_a16",
+                  route_scale=1.0, global_scale=1.0, fused=True),
 }
 
 

@@ -167,7 +167,13 @@ def test_grouped_ffn_validation(kw, status, frag):
     (dict(x_perm=None), m.MOE_ERR_INVALID_ARGUMENT, "gather"),
     (dict(w_gate_up_layout=0), m.MOE_ERR_UNSUPPORTED, "OUT_IN"),
     (dict(act_workspace_bytes=64 * 512 * 2), m.MOE_ERR_WORKSPACE_TOO_SMALL, "act_workspace"),
-    (dict(operand_dtype=m.DTYPE_MXFP4_W4A16), m.MOE_ERR_INVALID_ARGUMENT, "MXFP4_W4A8"),
+    (dict(operand_dtype=m.DTYPE_FP8_E4M3_TOKENS), m.MOE_ERR_INVALID_ARGUMENT, "MXFP4_W4A16"),
+    # W4A16: bf16 activations (no x_perm_scale), MXFP4 weight scales
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A16, x_perm_scale=112, w_gate_up_scale=128, w_down_scale=144),
+     m.MOE_ERR_INVALID_ARGUMENT, "no x_perm_scale"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A16, w_gate_up_scale=128), m.MOE_ERR_INVALID_ARGUMENT, "w_down_scale"),
+    (dict(operand_dtype=m.DTYPE_MXFP4_W4A16, w_gate_up_scale=128, w_down_scale=144, hidden_dim=192),
+     m.MOE_ERR_INVALID_ARGUMENT, "128"),
     # MXFP4 x MXFP8: hidden_dim in whole 128-element stages, the activation and weight scales
     (dict(operand_dtype=m.DTYPE_MXFP4_W4A8, hidden_dim=192, x_perm_scale=112, w_gate_up_scale=128,
           w_down_scale=144), m.MOE_ERR_INVALID_ARGUMENT, "128"),

@@ -47,3 +47,6 @@ def test_single_launch_ffn_bytes():
     # 2*2048*2048 codes + scales = 8,650,752; O 2048*7168*2 (bf16)
     cfg = synth.get_config(9)
     assert bench.fused_ffn_bytes(cfg, 142) == 142 * 23_396_352 + 15_138_816 + 8_650_752 + 29_360_128
+    # the same experts with bf16 rows (W4A16): x 2048*7168*2, A 2*2048*2048*2, O fp32 2048*7168*4
+    cfg = synth.get_config(10)
+    assert bench.fused_ffn_bytes(cfg, 142) == 142 * 23_396_352 + 29_360_128 + 16_777_216 + 58_720_256

@@ -33,6 +33,7 @@ def moe():
     (7, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # MXFP4 weights x bf16 activations (W4A16)
     (8, {}),                                                     # single-launch FFN (decode)
     (9, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # single-launch FFN, MXFP4 x MXFP8
+    (10, {"T": 64, "E": 16, "H": 1024, "D": 512}),               # single-launch FFN, MXFP4 x bf16
 ])
 def test_layer_replays_in_a_graph(moe, cid, changes):
     cfg = synth.scaled(synth.get_config(cid), **changes)

@@ -1082,11 +1082,11 @@ def test_fused_ffn_full_size(moe):
 
 # ---------------------------------------------------------------- single-launch L1 + L2 (MXFP4 x MXFP8)
 
-def _fused_mx_against_two_launch(moe, cfg, inp, res, gather):
+def _fused_mx_against_two_launch(moe, cfg, inp, res, gather, tol=FP8_TOL):
     """The single launch against the two-launch MX FFN on the same routing:
     bit-identical O when the down items are not split along K (the same
     MFMA sequence per output element and the same epilogue arithmetic),
-    else within the fp8 bar."""
+    else within the format's bar."""
     n = int(host(res["index"]["offsets"])[-1])
     o_fused = host(res["O"])[:n]
     two = moe.MoELayer(cfg, inp, gather=gather, fused=False)
@@ -1098,7 +1098,7 @@ def _fused_mx_against_two_launch(moe, cfg, inp, res, gather):
     if split:
         err, _ = rel_rms_err(o_fused.astype(np.float64), o_two.astype(np.float64))
         say(f"  fused vs two-launch O (down split along K): max err / rms = {err:.2e}")
-        assert err <= FP8_TOL
+        assert err <= tol
     else:
         same = np.array_equal(o_fused, o_two)
         say(f"  fused vs two-launch O: bit-identical = {same}")
@@ -1166,7 +1166,7 @@ def test_fused_mx_ffn_full_size(moe):
     _fused_mx_against_two_launch(moe, cfg, inp, res, True)
 
 
-@pytest.mark.parametrize("cid", [8, 9])
+@pytest.mark.parametrize("cid", [8, 9, 10])
 def test_fused_ffn_rows_beyond_max_rows(moe, cid):
     """expert_offsets holding more rows than max_rows (which only the device
     sees): the single launch computes nothing, leaves expert_out as it was,
@@ -1190,3 +1190,46 @@ def test_fused_ffn_rows_beyond_max_rows(moe, cid):
     assert torch.all(out == 7.0)
     # queue head and exit count back at zero
     assert host(ws[:8].view(torch.int32)).tolist() == [0, 0]
+
+
+# ---------------------------------------------------------------- single-launch L1 + L2 (MXFP4 x bf16)
+
+@pytest.mark.parametrize("changes,gather", [
+    ({"T": 64, "E": 8, "k": 2, "H": 512, "D": 256}, True),
+    ({"T": 37, "E": 8, "k": 2, "H": 256, "D": 384, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, True),
+    # one k stage in L2, a half-filled last column tile (H = 1.5 x 256), permuted rows
+    ({"T": 200, "E": 5, "k": 4, "H": 384, "D": 128, "activation": "gelu_tanh", "has_bias": True}, False),
+    ({"T": 9, "E": 64, "k": 8, "H": 1024, "D": 512}, True),                 # most experts empty, single rows
+    ({"T": 50, "E": 4, "k": 2, "H": 256, "D": 1664, "has_bias": True}, True),   # down split in 3 uneven parts
+    ({"T": 40, "E": 4, "k": 2, "H": 256, "D": 2048}, True),                 # 4 parts of whole scale groups
+    ({"T": 33, "E": 3, "k": 1, "H": 128, "D": 1152, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0},
+     False),                                                                # 5 parts, one k stage in L1
+])
+def test_fused_w4a16_ffn_layer(moe, changes, gather):
+    """The single-launch W4A16 FFN against the oracle, twice in a row on one
+    workspace, with no timed-out wait, and against the two-launch W4A16 FFN."""
+    cfg = synth.scaled(synth.get_config(10), **changes)
+    inp = _gen(cfg)
+    say(f"[fused w4a16] {changes} gather={gather}")
+    layer = moe.MoELayer(cfg, inp, gather=gather)
+    assert layer.fused
+    for call in range(2):
+        res = layer.forward(inp["x"])
+        torch.cuda.synchronize()
+        _check_layer(cfg, inp, res, np.arange(cfg.T), BF16_TOL)
+        assert moe.fused_error_word(layer.act_ws) == 0, f"call {call}: a wait timed out"
+    _fused_mx_against_two_launch(moe, cfg, inp, res, gather, BF16_TOL)
+
+
+def test_fused_w4a16_ffn_full_size(moe):
+    cfg = synth.get_config(10)
+    inp = _gen(cfg)
+    say("[fused w4a16 full] T=256 H=7168 E=256 k=8 D=2048, MXFP4 x bf16 in one launch")
+    layer, res = _run_layer(moe, cfg, inp)
+    assert layer.fused
+    _check_routing(cfg, inp, res)
+    _check_layer(cfg, inp, res, sample_tokens(cfg.T, 16, seed=11), BF16_TOL)
+    _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=11)
+    assert moe.fused_error_word(layer.act_ws) == 0
+    _fused_mx_against_two_launch(moe, cfg, inp, res, True, BF16_TOL)
