@@ -33,15 +33,17 @@
 // caller zeroes them once, when the workspace is allocated.
 //
 // Tiles are 32 x 256 with 4 waves (32 x 64 each: the gate and up columns of
-// 32 outputs for L1).  Two operand kinds share the schedule, the tile and
+// 32 outputs for L1).  Three operand kinds share the schedule, the tile and
 // the epilogue arithmetic:
-//   bf16:  k stages of 64 bf16, 4 stages deep in LDS through buffer loads,
-//          one workgroup per CU;
-//   MX:    MXFP4 weights x MXFP8 activations (the mega_ffn page's
-//          block-scaled form), k stages of 128 on the scaled MFMA, 3 deep,
-//          two workgroups per CU; L1 re-quantises A to MXFP8 before L2
-//          reads it.
-// Either way the batch is bound by streaming the weights.
+//   bf16:   k stages of 64 bf16, 4 stages deep in LDS through buffer loads,
+//           one workgroup per CU;
+//   W4A8:   MXFP4 weights x MXFP8 activations (the mega_ffn page's
+//           block-scaled form), k stages of 128 on the scaled MFMA, 3 deep,
+//           two workgroups per CU; L1 re-quantises A to MXFP8 before L2
+//           reads it;
+//   W4A16:  MXFP4 weights dequantised in registers x bf16 activations,
+//           k stages of 128 on the bf16 MFMA, two workgroups per CU.
+// Every kind is bound by streaming the weights.
 #include "common.h"
 #include "kernels.h"
 #include "mx_common.h"
@@ -462,7 +464,7 @@ __device__ __forceinline__ void fused_store_o_tile(const f32x16_t (&acc)[2], flo
   }
 }
 
-// ---------------------------------------------------------------- MX
+// ---------------------------------------------------------------- W4A8
 // MXFP4 weights x MXFP8 activations.  A k stage of 128: 4 KB of e4m3
 // activation rows and 16 KB of packed e2m1 weight rows, 3 stages deep, plus
 // the rows' scale dwords, which come four stages per 16-byte load where the
