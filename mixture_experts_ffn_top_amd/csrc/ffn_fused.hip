@@ -47,6 +47,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx_common.h"
+#include "mx_tile32.h"
 
 namespace moe {
 
@@ -420,73 +421,12 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   fused_exit(p.ctl, arrive, total_mb, s_item + 1);
 }
 
-// L2 epilogue of the MX kernels: O = sc * C + bias for the 32 x 256 tile,
-// staged in LDS (rows of 256 outputs + 16 bytes of bank skew) so that each
-// store moves whole row pieces.  acc[ni][4q + c] is C[fr][wave*64 + ni*32 +
-// 8q + 4fh + c].  Called by the whole workgroup; smem must be free.
-template <bool OUT_BF16>
-__device__ __forceinline__ void fused_store_o_tile(const f32x16_t (&acc)[2], float sc, const uint16_t* bias, int H,
-                                                   int nb, int row_beg, int row_end, void* out, uint8_t* smem) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, fr = lane & 31, fh = lane >> 5;
-  constexpr int ES = OUT_BF16 ? 2 : 4;
-  constexpr int PITCH = F_BN * ES + 16;
-  __syncthreads();
-#pragma unroll
-  for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int lc = wave * 64 + ni * 32 + 8 * q + 4 * fh;  // first of 4 tile columns
-      const int n = nb * F_BN + lc;
-      float bd[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (bias && n < H) bias_x4(bias + n, bd);
-      float v[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = acc[ni][4 * q + c] * sc + bd[c];
-      uint8_t* dst = smem + fr * PITCH + lc * ES;
-      if (OUT_BF16) {
-        uint2 w;
-        w.x = pack_bf16x2_rne(v[0], v[1]);
-        w.y = pack_bf16x2_rne(v[2], v[3]);
-        *(uint2*)dst = w;
-      } else {
-        *(f32x4_t*)dst = f32x4_t{v[0], v[1], v[2], v[3]};
-      }
-    }
-  __syncthreads();
-  // a row is F_BN * ES bytes: 32 (bf16) or 64 (fp32) lanes of 16 bytes
-  constexpr int LPR = F_BN * ES / 16, RPI = 64 / LPR;  // lanes per row, rows per store
-  const int cpart = lane % LPR;
-  const int n = nb * F_BN + cpart * (16 / ES);
-  for (int r = wave * RPI + lane / LPR; r < F_BM; r += F_NW * RPI) {
-    const int row = row_beg + r;
-    if (row < row_end && n < H)
-      *(u32x4_t*)((uint8_t*)out + ((int64_t)row * H + n) * ES) = *(const u32x4_t*)(smem + r * PITCH + cpart * 16);
-  }
-}
-
 // ---------------------------------------------------------------- W4A8
-// MXFP4 weights x MXFP8 activations.  A k stage of 128: 4 KB of e4m3
-// activation rows and 16 KB of packed e2m1 weight rows, 3 stages deep, plus
-// the rows' scale dwords, which come four stages per 16-byte load where the
-// item's stages allow (else one stage per 4-byte load).  With 70 KB of LDS
-// two workgroups share a CU, so each SIMD holds a second wave that covers
-// the first one's LDS reads and MFMAs while both wait on the weight stream.
-constexpr int M_NS = 3;
-constexpr int M_A_BYTES = F_BM * MX_A_ROW;              // 4 KB
-constexpr int M_B_BYTES = F_BN * MX_B_ROW;              // 16 KB
-constexpr int M_STAGE = M_A_BYTES + M_B_BYTES;
-constexpr int M_LPW_B = M_B_BYTES / 1024 / F_NW;        // 1 KB weight row loads per wave per stage: 4
-constexpr int M_LOADS = 1 + M_LPW_B;                    // row loads per wave per stage
-constexpr int M_AS_OFF = M_NS * M_STAGE;                // activation scales: 2 slots x 32 rows x 16 bytes
-constexpr int M_BS_OFF = M_AS_OFF + 2 * F_BM * 16;      // weight scales: 2 slots x 256 rows x 16 bytes
-constexpr int M_PIPE = M_BS_OFF + 2 * F_BN * 16;        // 69 KB
+// MXFP4 weights x MXFP8 activations on the 32 x 256 tile of mx_tile32.h, two
+// workgroups per CU.
 constexpr int M_WG_PER_CU = 2;
-constexpr int M_CPITCH = 128 + 16;                      // staged A codes: 128 bytes per row + bank skew
-static_assert(M_NS * F_BM * 4 <= 2 * F_BM * 16 && M_NS * F_BN * 4 <= 2 * F_BN * 16, "single-stage scale slots fit");
-static_assert((M_NS - 2) * M_LOADS < 64, "vmcnt range");
-static_assert(M_WG_PER_CU * (M_PIPE + (1024 + 4) * 4) <= 160 * 1024, "two MX workgroups share a CU");
-static_assert(F_BM * M_CPITCH + F_BM * 4 <= M_NS * M_STAGE, "staged A codes and scales fit the stages");
-static_assert(F_BM * (F_BN * 4 + 16) <= M_NS * M_STAGE, "a staged fp32 output tile fits the stages");
+static_assert(T32_BM == F_BM && T32_BN == F_BN && T32_NT == F_NT, "the W4A8 tile is the schedule's tile");
+static_assert(M_WG_PER_CU * (T32_PIPE + (1024 + 4) * 4) <= 160 * 1024, "two W4A8 workgroups share a CU");
 
 struct FusedMxArgs {
   const int32_t* offsets;
@@ -515,10 +455,9 @@ struct FusedMxArgs {
 template <int ACT, int FMT, bool OUT_BF16>
 __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int32_t* s_mbp = (int32_t*)(smem + M_PIPE);  // row-block prefix per expert, kept for the whole launch
+  int32_t* s_mbp = (int32_t*)(smem + T32_PIPE);  // row-block prefix per expert, kept for the whole launch
   int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-part / last-out flag
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int tid = threadIdx.x;
   const int L = p.L;
   int32_t* err = p.ctl + 2;
   int32_t* tile_done = p.ctl + 4;
@@ -532,7 +471,6 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
   const int n2 = total_mb * NB2;
   const int S = (p.S > 1 && n2 <= p.tiles_cap) ? p.S : 1;
   const int n1 = total_mb * NB1, n_all = n1 + n2 * S;
-  const int fr = lane & 31, fh = lane >> 5;
 
   for (;;) {
     if (tid == 0) s_item[0] = atomicAdd(p.ctl, 1);
@@ -544,26 +482,23 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
     const int e = t.e, nb = t.nb, part = t.part, gm = t.gm, row_beg = t.row_beg, row_end = t.row_end;
     if (l2) fused_wait(p.arrive + gm, NB1, err);
 
-    // ---- operands of this item.  K stages ks = kt0 + kt of the whole row.
+    // ---- operands of this item: k stages kt0 .. kt0+KT-1 of the whole row
     const int K = l2 ? p.D : p.H;
     const int KS = K / MX_BK;
     const int parts = l2 ? S : 1;
     const int kt0 = part * KS / parts;
     const int KT = (part + 1) * KS / parts - kt0;
-    // scale groups of 4 stages: 16-byte aligned rows (KS % 4 == 0) and whole
-    // groups inside this item's stages
-    const int G = (KS % 4 == 0 && kt0 % 4 == 0 && KT % 4 == 0) ? 4 : 1;
-    const uint32_t srow = (uint32_t)K / 32u;  // scale bytes per row
-    const int32_t* gather = l2 ? nullptr : p.sorted_token;
-    const uint8_t* a_base = l2 ? p.act : p.x;
-    const uint8_t* as_base = l2 ? p.act_scale : p.x_scale;
-    const uint8_t* b_base = l2 ? p.w_d + (int64_t)e * p.H * (p.D / 2) : p.w_gu + (int64_t)e * 2 * p.D * (p.H / 2);
-    const uint8_t* bs_base =
-        l2 ? p.w_d_scale + (int64_t)e * p.H * (p.D / 32) : p.w_gu_scale + (int64_t)e * 2 * p.D * (p.H / 32);
-    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
-    const __amdgpu_buffer_rsrc_t as_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)as_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
-    const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
-    const __amdgpu_buffer_rsrc_t bs_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)bs_base, (short)0, 0x7fffffff, F_BUF_DWORD3);
+    Mx32Operands o;
+    o.a = l2 ? p.act : p.x;
+    o.a_scale = l2 ? p.act_scale : p.x_scale;
+    o.gather = l2 ? nullptr : p.sorted_token;
+    o.w = l2 ? p.w_d + (int64_t)e * p.H * (p.D / 2) : p.w_gu + (int64_t)e * 2 * p.D * (p.H / 2);
+    o.w_scale = l2 ? p.w_d_scale + (int64_t)e * p.H * (p.D / 32) : p.w_gu_scale + (int64_t)e * 2 * p.D * (p.H / 32);
+    o.K = K;
+    o.row_beg = row_beg;
+    o.row_end = row_end;
+    o.kt0 = kt0;
+    o.KT = KT;
     // weight row of tile row trow: L1 wave column q holds 32 gate rows, then
     // the matching 32 up rows; L2 256 consecutive rows (past H: the last)
     auto w_row = [&](int trow) -> int {
@@ -572,148 +507,13 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
       const int oc = nb * 128 + q * 32 + j;
       return (FMT == 0) ? (isup ? p.D + oc : oc) : (2 * oc + isup);
     };
-    // A: wave w loads tile rows 8w .. 8w+7 (1 KB = 8 rows x 8 chunks; rows
-    // past the expert's end read zeros) and, by lanes 0-7, their scale
-    // dwords (rows past the end repeat the last one; never used).  B: wave w
-    // loads rows 64w .. 64w+63 (16 rows x 4 chunks per 1 KB) and their scale
-    // dwords, one row per lane.
-    uint32_t a_voff, as_voff, b_voff[M_LPW_B], bs_voff;
-    {
-      const int trow = wave * 8 + (lane >> 3);
-      const int r = row_beg + trow;
-      if (r < row_end) {
-        const uint32_t ar = gather ? (uint32_t)gather[r] : (uint32_t)r;
-        a_voff = ar * (uint32_t)K + (uint32_t)(((lane & 7) ^ mx_fa(trow)) * 16);
-      } else {
-        a_voff = F_OOB;
-      }
-      const int sr = min(row_beg + wave * 8 + (lane & 7), row_end - 1);
-      as_voff = (gather ? (uint32_t)gather[sr] : (uint32_t)sr) * srow;
-    }
-#pragma unroll
-    for (int i = 0; i < M_LPW_B; ++i) {
-      const int trow = (wave * M_LPW_B + i) * 16 + (lane >> 2);
-      b_voff[i] = (uint32_t)w_row(trow) * ((uint32_t)K / 2u) + (uint32_t)(((lane & 3) ^ mx_fb(trow)) * 16);
-    }
-    bs_voff = (uint32_t)w_row(wave * 64 + lane) * srow;
-
-    // scale group g = kt / 4 in slot g % 2 (rows 16 bytes apart), or stage
-    // kt in slot kt % 3 (rows 4 bytes apart): row r's dword of stage kt at
-    // r * 4 G + (kt % G) * 4
-    auto as_slot = [&](int kt) {
-      return smem + M_AS_OFF + (G == 4 ? ((kt / 4) % 2) * (F_BM * 16) : (kt % M_NS) * (F_BM * 4));
-    };
-    auto bs_slot = [&](int kt) {
-      return smem + M_BS_OFF + (G == 4 ? ((kt / 4) % 2) * (F_BN * 16) : (kt % M_NS) * (F_BN * 4));
-    };
-    auto issue = [&](int kt) {
-      const int ks = kt0 + kt;
-      // the stage's scale group first (when it starts one), then its rows
-      if (kt % G == 0) {
-        if (G == 4) {
-          if (lane < 8)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(as_slot(kt) + wave_s * 8 * 16), 16, as_voff,
-                                                     ks * 4, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 16), 16, bs_voff,
-                                                   ks * 4, 0, 0);
-        } else {
-          if (lane < 8)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(as_rsrc, (lptr_t)(as_slot(kt) + wave_s * 8 * 4), 4, as_voff,
-                                                     ks * 4, 0, 0);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(bs_rsrc, (lptr_t)(bs_slot(kt) + wave_s * 64 * 4), 4, bs_voff,
-                                                   ks * 4, 0, 0);
-        }
-      }
-      uint8_t* st = smem + (kt % M_NS) * M_STAGE;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lptr_t)(st + wave_s * 1024), 16, a_voff, ks * MX_A_ROW, 0, 0);
-#pragma unroll
-      for (int i = 0; i < M_LPW_B; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(b_rsrc, (lptr_t)(st + M_A_BYTES + (wave_s * M_LPW_B + i) * 1024), 16,
-                                                 b_voff[i], ks * MX_B_ROW, 0, 0);
-    };
-
     f32x16_t acc[2];
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[ni][r] = 0.0f;
-    // stages 0 .. NS-2 in the prologue; iteration kt waits for stage kt (the
-    // stage after it may stay in flight: at least M_LOADS loads), publishes
-    // it, and issues stage kt+2 into the buffer of stage kt-1
-#pragma unroll
-    for (int i = 0; i < M_NS - 1; ++i)
-      if (i < KT) issue(i);
-    for (int kt = 0; kt < KT; ++kt) {
-      if (kt + M_NS - 2 < KT) __builtin_amdgcn_s_waitcnt(waitcnt_vm((M_NS - 2) * M_LOADS));
-      else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-      f_block_barrier();
-      if (kt + M_NS - 1 < KT) issue(kt + M_NS - 1);
-      const uint8_t* st = smem + (kt % M_NS) * M_STAGE;
-      const int sg = (kt % G) * 4;
-      const uint32_t as4 = *(const uint32_t*)(as_slot(kt) + sg + fr * 4 * G);
-      uint32_t bs4[2];
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) bs4[ni] = *(const uint32_t*)(bs_slot(kt) + sg + (wave * 64 + ni * 32 + fr) * 4 * G);
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // k step kk covers MX blocks 2kk and 2kk+1; lane half fh passes block 2kk+fh's scale
-        const i32x8_t aq = mx_frag_a(st, fr, kk, fh);
-        const int asc = (int)((as4 >> (8 * (2 * kk + fh))) & 0xffu);
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-          const i32x8_t bq = mx_frag_b(st + M_A_BYTES, wave * 64 + ni * 32 + fr, kk, fh);
-          const int bsc = (int)((bs4[ni] >> (8 * (2 * kk + fh))) & 0xffu);
-          acc[ni] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bq, aq, acc[ni], 4, 0, 0, bsc, 0, asc);
-        }
-      }
-    }
+    mx32_tile_loop(o, w_row, smem, acc);
 
-    // ---- epilogue.  acc[ni][4q + c] is C[row][col], row = fr, col = wave*64 + ni*32 + 8q + 4fh + c
+    // ---- epilogue
     if (!l2) {
-      // block 0 holds the gate columns, block 1 the up columns of the wave's
-      // 32 outputs, which are one MX block of each row: the 16 values of a
-      // lane and the 16 of lane xor 32.  Re-quantised as the two-launch MX
-      // gate_up does: shared exponent floor(log2 amax) - 8, codes RNE.
-      const float sc = p.s_gu ? p.s_gu[e] : 1.0f;
-      const uint16_t* bias = p.b_gu ? p.b_gu + (int64_t)e * 2 * p.D : nullptr;
-      float a[16];
-      float m = 0.0f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int oc = nb * 128 + wave * 32 + 8 * q + 4 * fh;  // first of 4 outputs
-        float bg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, bu[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (bias) {
-          gate_up_bias_x4(bias, p.D, oc, FMT != 0, bg, bu);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          a[4 * q + c] = gated_act<ACT>(acc[0][4 * q + c] * sc + bg[c], acc[1][4 * q + c] * sc + bu[c], p.alpha, p.limit);
-          m = fmaxf(m, fabsf(a[4 * q + c]));
-        }
-      }
-      m = fmaxf(m, __shfl_xor(m, 32, MOE_WAVE));
-      const int X = mx_shared_exp(m);
-      const float inv = mx_inv_scale(X);
-      // stage the codes (rows of 128 bytes) and the scale bytes (4 per row)
-      // in LDS, then store whole row pieces
-      uint8_t* s_codes = smem;
-      uint8_t* s_scales = smem + F_BM * M_CPITCH;
-      __syncthreads();  // the stage buffers are free
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(uint32_t*)(s_codes + fr * M_CPITCH + wave * 32 + 8 * q + 4 * fh) =
-            e4m3x4(a[4 * q] * inv, a[4 * q + 1] * inv, a[4 * q + 2] * inv, a[4 * q + 3] * inv);
-      if (fh == 0) s_scales[fr * 4 + wave] = (uint8_t)(X + 127);
-      __syncthreads();
-      {
-        const int r = tid >> 3, pc = tid & 7;  // 32 rows x 8 pieces of 16 bytes
-        if (row_beg + r < row_end)
-          *(u32x4_t*)(p.act + (int64_t)(row_beg + r) * p.D + nb * 128 + pc * 16) =
-              *(const u32x4_t*)(s_codes + r * M_CPITCH + pc * 16);
-        if (tid < F_BM && row_beg + tid < row_end)
-          *(uint32_t*)(p.act_scale + (int64_t)(row_beg + tid) * (p.D / 32) + nb * 4) =
-              *(const uint32_t*)(s_scales + tid * 4);
-      }
+      mx32_store_a_mxfp8<ACT>(acc, p.s_gu ? p.s_gu[e] : 1.0f, p.b_gu ? p.b_gu + (int64_t)e * 2 * p.D : nullptr, p.D,
+                              FMT != 0, p.alpha, p.limit, nb, row_beg, row_end, p.act, p.act_scale, smem);
       fused_count_in(p.arrive + gm);  // this part of the row block is published
     } else {
       if (S > 1) {
@@ -723,8 +523,8 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
           continue;
         }
       }
-      fused_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
-                                   row_beg, row_end, p.out, smem);
+      mx32_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
+                                  row_beg, row_end, p.out, smem);
     }
     __syncthreads();  // the stage buffers and the item word are reused by the next item
   }
@@ -975,8 +775,8 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_w4a16_kernel(const FusedW4Args
           continue;
         }
       }
-      fused_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
-                                   row_beg, row_end, p.out, smem);
+      mx32_store_o_tile<OUT_BF16>(acc, p.s_d ? p.s_d[e] : 1.0f, p.b_d ? p.b_d + (int64_t)e * p.H : nullptr, p.H, nb,
+                                  row_beg, row_end, p.out, smem);
     }
     __syncthreads();  // the stage buffers and the item word are reused by the next item
   }
@@ -1018,7 +818,7 @@ hipError_t launch_fused_act(const FusedArgs& a, int fmt, int out_bf16, hipStream
 
 template <typename KernelT>
 hipError_t launch_fused_mx_kernel(KernelT kern, const FusedMxArgs& a, hipStream_t st) {
-  const int lds = M_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  const int lds = T32_PIPE + (a.L + 4) * (int)sizeof(int32_t);
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int grid = M_WG_PER_CU * fused_cu_count();

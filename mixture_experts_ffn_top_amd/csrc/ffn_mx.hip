@@ -12,7 +12,9 @@
 //           down GEMM's operand.
 // down:     O = s_d[e] * C + b_d[e]  (bf16 or fp32 out)
 //
-// Tiling: 256 x 256 workgroup tile, 8 waves in 2 x 4 (two per SIMD), each
+// Tiling (batches of more than 32 rows per expert on average; smaller ones
+// take the 32-row tiles further down): 256 x 256 workgroup tile, 8 waves in
+// 2 x 4 (two per SIMD), each
 // wave 128 x 64 = 4 x 2 MFMA blocks.  k stages of 128 go global -> LDS by
 // buffer loads: the 32 KB of e4m3 activation rows (and their 4 scale bytes
 // per row) double buffered by waves 0-3, the 16 KB of packed e2m1 weight
@@ -20,6 +22,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mx_common.h"
+#include "mx_tile32.h"
 
 namespace moe {
 
@@ -751,6 +754,70 @@ hipError_t launch_mx_gate_up(const MxGemmArgs& g, int fmt, int max_rows, hipStre
   return launch_mx(grouped_gemm_mx_kernel<MX_GATE_UP, ACT, 1, false>, g, max_rows, X_BN / 2, st);
 }
 
+// ------------------------------------------------------------------ W4A8, 32-row tiles
+// For batches of a few rows per expert (decode) the 256-row tiles above are
+// mostly empty.  These GEMMs run the 32 x 256 tile of mx_tile32.h instead
+// (4 waves, 69 KB of LDS, two workgroups per CU), with the same MFMA
+// sequence per output element and the same epilogue arithmetic as the
+// 256-row kernels, so their results are bit-identical.
+template <int MODE, int ACT, int FMT, bool OUT_BF16>
+__global__ __launch_bounds__(T32_NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void grouped_gemm_mx32_kernel(const MxGemmArgs p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int NBO = (MODE == MX_GATE_UP) ? T32_BN / 2 : T32_BN;  // output columns per tile
+  const int NB = (p.N + NBO - 1) / NBO;
+  MxTile t;
+  if (!mx_map_tile<T32_BM>(p.offsets, p.L, NB, (int32_t*)smem, t)) return;
+  const int e = t.e, nb = t.nb;
+  Mx32Operands o;
+  o.a = p.A;
+  o.a_scale = p.A_scale;
+  o.gather = p.gather;
+  o.w = p.W + (int64_t)e * p.w_estride;
+  o.w_scale = p.W_scale + (int64_t)e * p.ws_estride;
+  o.K = p.K;
+  o.row_beg = t.row_beg;
+  o.row_end = t.row_end;
+  o.kt0 = 0;
+  o.KT = p.K / MX_BK;
+  // weight row of tile row trow: wave column q owns 32 gate rows then the
+  // matching 32 up rows (gate_up), or 64 consecutive rows (down)
+  auto w_row = [&](int trow) -> int {
+    if (MODE == MX_DOWN) return min(nb * T32_BN + trow, p.N - 1);
+    const int q = trow / 64, rr = trow % 64, isup = rr / 32, j = rr % 32;
+    const int oc = min(nb * NBO + q * 32 + j, p.N - 1);
+    return (FMT == 0) ? (isup ? p.N + oc : oc) : (2 * oc + isup);
+  };
+  f32x16_t acc[2];
+  mx32_tile_loop(o, w_row, smem, acc);
+  const float sc = p.escale ? p.escale[e] : 1.0f;
+  const uint16_t* bias_e = p.bias ? p.bias + (int64_t)e * p.bias_estride : nullptr;
+  if (MODE == MX_GATE_UP)
+    mx32_store_a_mxfp8<ACT>(acc, sc, bias_e, p.N, FMT != 0, p.alpha, p.limit, nb, t.row_beg, t.row_end,
+                            (uint8_t*)p.out, p.out_scale, smem);
+  else
+    mx32_store_o_tile<OUT_BF16>(acc, sc, bias_e, p.N, nb, t.row_beg, t.row_end, p.out, smem);
+}
+
+template <typename KernelT>
+hipError_t launch_mx32(KernelT kern, const MxGemmArgs& a, int max_rows, int NBO, hipStream_t st) {
+  const int prefix = (a.L + 1) * (int)sizeof(int32_t);
+  const int lds = T32_PIPE > prefix ? T32_PIPE : prefix;
+  hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (err != hipSuccess) return err;
+  const int64_t grid = mx_grid(max_rows, a.L, T32_BM, a.N, NBO);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  kern<<<(unsigned)grid, T32_NT, lds, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int ACT>
+hipError_t launch_mx32_gate_up(const MxGemmArgs& g, int fmt, int max_rows, hipStream_t st) {
+  if (fmt == 0) return launch_mx32(grouped_gemm_mx32_kernel<MX_GATE_UP, ACT, 0, false>, g, max_rows, T32_BN / 2, st);
+  return launch_mx32(grouped_gemm_mx32_kernel<MX_GATE_UP, ACT, 1, false>, g, max_rows, T32_BN / 2, st);
+}
+
 template <int BM>
 hipError_t launch_ffn_w4a16_bm(const FfnMxParams& q, hipStream_t st) {
   hipError_t err;
@@ -807,8 +874,10 @@ hipError_t launch_ffn_w4a16(const FfnMxParams& q, hipStream_t st) {
   return launch_ffn_w4a16_bm<128>(q, st);
 }
 
+// 32-row tiles when the batch averages at most 32 rows per expert
 hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {
   hipError_t err;
+  const bool small = (int64_t)q.max_rows <= (int64_t)32 * q.L;
   if (q.events && (err = hipEventRecord(q.events[0], st)) != hipSuccess) return err;
   MxGemmArgs g{};
   g.offsets = q.offsets;
@@ -830,9 +899,15 @@ hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {
   g.limit = q.limit;
   g.out = q.act;
   g.out_scale = q.act_scale;
-  if (q.act_kind == ACT_SILU) err = launch_mx_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st);
-  else if (q.act_kind == ACT_SWIGLUOAI) err = launch_mx_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st);
-  else err = launch_mx_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st);
+  if (q.act_kind == ACT_SILU)
+    err = small ? launch_mx32_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st)
+                : launch_mx_gate_up<ACT_SILU>(g, q.fmt, q.max_rows, st);
+  else if (q.act_kind == ACT_SWIGLUOAI)
+    err = small ? launch_mx32_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st)
+                : launch_mx_gate_up<ACT_SWIGLUOAI>(g, q.fmt, q.max_rows, st);
+  else
+    err = small ? launch_mx32_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st)
+                : launch_mx_gate_up<ACT_GELU_TANH>(g, q.fmt, q.max_rows, st);
   if (err != hipSuccess) return err;
   if (q.events && (err = hipEventRecord(q.events[1], st)) != hipSuccess) return err;
   MxGemmArgs d{};
@@ -850,7 +925,10 @@ hipError_t launch_ffn_mx(const FfnMxParams& q, hipStream_t st) {
   d.bias_estride = q.H;
   d.escale = q.down_scales;
   d.out = q.out;
-  if (q.out_bf16)
+  if (small)
+    err = q.out_bf16 ? launch_mx32(grouped_gemm_mx32_kernel<MX_DOWN, ACT_SILU, 0, true>, d, q.max_rows, T32_BN, st)
+                     : launch_mx32(grouped_gemm_mx32_kernel<MX_DOWN, ACT_SILU, 0, false>, d, q.max_rows, T32_BN, st);
+  else if (q.out_bf16)
     err = launch_mx(grouped_gemm_mx_kernel<MX_DOWN, ACT_SILU, 0, true>, d, q.max_rows, X_BN, st);
   else
     err = launch_mx(grouped_gemm_mx_kernel<MX_DOWN, ACT_SILU, 0, false>, d, q.max_rows, X_BN, st);

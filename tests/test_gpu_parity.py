@@ -942,6 +942,38 @@ def test_mx_layer_small(moe, changes, nsample, gather):
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=4), FP8_TOL)
 
 
+@pytest.mark.parametrize("changes,gather", [
+    ({"T": 64, "E": 16, "k": 8, "H": 512, "D": 256}, True),                # exactly 32 rows per expert on average
+    ({"T": 40, "E": 16, "k": 4, "H": 384, "D": 640, "activation": "swigluoai", "alpha": 1.702, "limit": 7.0,
+      "gate_up_format": "interleaved", "has_bias": True}, False),
+    ({"T": 30, "E": 8, "k": 8, "H": 1024, "D": 384, "activation": "gelu_tanh", "has_bias": True}, True),
+    ({"T": 5, "E": 64, "k": 8, "H": 256, "D": 128}, True),                 # single rows, one k stage in down
+])
+def test_mx_small_batch_tiles(moe, changes, gather):
+    """W4A8 on a batch of at most 32 rows per expert on average runs the
+    32-row tiles: against the oracle, and bit for bit against the 256-row
+    tiles (the same call with max_rows above 32 per expert)."""
+    cfg = synth.scaled(synth.get_config(6), **changes)
+    assert cfg.T * cfg.k <= 32 * cfg.E
+    inp = _gen(cfg)
+    say(f"[mx 32-row tiles] {changes} gather={gather}")
+    layer, res = _run_layer(moe, cfg, inp, gather=gather)
+    _check_routing(cfg, inp, res)
+    _check_mx_act(cfg, inp, res, layer)
+    _check_layer(cfg, inp, res, np.arange(cfg.T), FP8_TOL)
+    ind = res["index"]
+    n = int(host(ind["offsets"])[-1])
+    big = 32 * cfg.E + 1
+    o_big = moe.grouped_ffn(ind["offsets"], big, layer.w, x_perm=ind.get("x_perm"), x_perm_scale=ind["x_perm_scale"],
+                            x=layer.last["x_gather"], sorted_token=ind["sorted_token"] if gather else None,
+                            activation=cfg.activation, alpha=cfg.alpha, limit=cfg.limit,
+                            gate_up_format=cfg.gate_up_format, out_dtype=layer.out_dtype)
+    torch.cuda.synchronize()
+    same = np.array_equal(host(o_big)[:n], host(res["O"])[:n])
+    say(f"  32-row vs 256-row tiles: O bit-identical = {same}")
+    assert same
+
+
 def test_mx_layer_full_size(moe):
     cfg = synth.get_config(6)
     inp = _gen(cfg)
