@@ -24,10 +24,11 @@
 // part came last.  No part waits for another.
 //
 // Visibility follows the HIP memory model at agent scope: after an L1 item's
-// A stores, a workgroup barrier and one release fence (write-back of the
-// XCD's L2) precede the counter increment; an L2 item acquires the counter
-// and fence-acquires (invalidate) before loading A, whichever XCD either ran
-// on.  The last
+// A stores, a workgroup barrier and a release fence (write-back of the XCD's
+// L2) precede the counter increment; an L2 item acquires the counter and
+// fence-acquires (invalidate) before loading A, whichever XCD either ran on.
+// One fence publishes up to F_PUB L1 items of a workgroup at once; a
+// workgroup publishes what it holds before it waits or leaves.  The last
 // workgroup to leave resets the queue, the exit count and the arrival
 // counters, so the control words start at zero on the next launch; the
 // caller zeroes them once, when the workspace is allocated.
@@ -68,6 +69,7 @@ constexpr int F_PIPE = F_NS * F_STAGE;              // 144 KB
 constexpr int F_BUF_DWORD3 = 0x00020000;            // raw buffer resource word 3 (gfx9)
 constexpr uint32_t F_OOB = 0x80000000u;             // past every buffer range: zeros, no memory
 constexpr int F_SPIN_LIMIT = 1 << 20;               // bounded wait: ~0.2 s of s_sleep 8
+constexpr int F_PUB = 4;                            // L1 items published per release fence
 constexpr int F_MAX_TILES = 256;                    // L2 tiles a launch may split along K
 constexpr int F_MAX_PARTS = 8;
 constexpr int F_HDR_WORDS = 4 + F_MAX_TILES;        // queue, exits, error, unused, split counters
@@ -145,14 +147,39 @@ __device__ __forceinline__ void fused_wait(const int32_t* counter, int need, int
   __syncthreads();
 }
 
-// Counts the workgroup's stores in: the barrier orders every wave's stores
-// before thread 0's release fence, which writes them back once for the
-// workgroup; the count then moves.
-__device__ __forceinline__ void fused_count_in(int32_t* counter) {
+// L1 publication.  One release fence covers the A stores of up to F_PUB
+// L1 items of a workgroup: thread 0 keeps their row blocks in s_pend
+// ([0] the count, then the blocks) and counts them in together when the list
+// is full, and before the workgroup takes an L2 item or leaves.  So a
+// workgroup that waits holds nothing unpublished: every L1 item is published
+// by a workgroup that does not wait, and each wait still ends.  (The fence
+// writes back the XCD's whole L2; one per item cost up to 0.1 ms per launch.)
+//
+// Publishes the list (thread 0 only: no other thread reads it).
+__device__ __forceinline__ void fused_flush0(int32_t* arrive, int32_t* s_pend) {
+  if (s_pend[0] > 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int i = 1; i <= s_pend[0]; ++i)
+      __hip_atomic_fetch_add(arrive + s_pend[i], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_pend[0] = 0;
+  }
+}
+
+// Called by every thread after a barrier that follows the stores (each
+// wave's barrier waits for its own stores first).
+__device__ __forceinline__ void fused_flush(int32_t* arrive, int32_t* s_pend) {
+  if (threadIdx.x == 0) fused_flush0(arrive, s_pend);
+}
+
+// An L1 item's A stores are done: its row block joins the list, and a full
+// list is published.
+__device__ __forceinline__ void fused_count_in(int32_t* arrive, int gm, int32_t* s_pend) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int n = s_pend[0] + 1;
+    s_pend[n] = gm;
+    s_pend[0] = n;
+    if (n == F_PUB) fused_flush0(arrive, s_pend);
   }
 }
 
@@ -255,6 +282,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   extern __shared__ __align__(16) uint8_t smem[];
   int32_t* s_mbp = (int32_t*)(smem + F_PIPE);  // row-block prefix per expert, kept for the whole launch
   int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-out flag
+  int32_t* s_pend = s_item + 2;                 // L1 row blocks not yet published
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int L = p.L;
@@ -263,6 +291,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
   int32_t* arrive = p.arrive;
   int32_t* tile_done = p.ctl + 4;
 
+  if (tid == 0) s_pend[0] = 0;
   fused_block_prefix(p.offsets, L, s_mbp);
   // more rows than max_rows: neither A, O nor a counter may be touched, so do
   // nothing (at most max_rows rows also bound the row blocks by row_blocks)
@@ -279,6 +308,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
     if (tid == 0) s_item[0] = atomicAdd(queue, 1);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n1) fused_flush(p.arrive, s_pend);  // before any wait, and before leaving
     if (item >= n_all) break;
     const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
     const bool l2 = t.l2;
@@ -380,7 +410,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_kernel(const FusedArgs p) {
           *(uint2*)(p.act + (int64_t)row * p.D + oc) = v;
         }
       }
-      fused_count_in(arrive + gm);  // this part of the row block is published
+      fused_count_in(arrive, gm, s_pend);  // this part of the row block is done
     } else {
       if (S > 1) {
         const int t2 = gm * NB2 + nb;
@@ -457,11 +487,13 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
   extern __shared__ __align__(16) uint8_t smem[];
   int32_t* s_mbp = (int32_t*)(smem + T32_PIPE);  // row-block prefix per expert, kept for the whole launch
   int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-part / last-out flag
+  int32_t* s_pend = s_item + 2;                 // L1 row blocks not yet published
   const int tid = threadIdx.x;
   const int L = p.L;
   int32_t* err = p.ctl + 2;
   int32_t* tile_done = p.ctl + 4;
 
+  if (tid == 0) s_pend[0] = 0;
   fused_block_prefix(p.offsets, L, s_mbp);
   // more rows than max_rows: do nothing (as the bf16 kernel)
   const bool too_many = p.offsets[L] > p.max_rows || s_mbp[L] > p.row_blocks;
@@ -476,6 +508,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
     if (tid == 0) s_item[0] = atomicAdd(p.ctl, 1);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n1) fused_flush(p.arrive, s_pend);  // before any wait, and before leaving
     if (item >= n_all) break;
     const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
     const bool l2 = t.l2;
@@ -514,7 +547,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_mx_kernel(const FusedMxArgs p)
     if (!l2) {
       mx32_store_a_mxfp8<ACT>(acc, p.s_gu ? p.s_gu[e] : 1.0f, p.b_gu ? p.b_gu + (int64_t)e * 2 * p.D : nullptr, p.D,
                               FMT != 0, p.alpha, p.limit, nb, row_beg, row_end, p.act, p.act_scale, smem);
-      fused_count_in(p.arrive + gm);  // this part of the row block is published
+      fused_count_in(p.arrive, gm, s_pend);  // this part of the row block is done
     } else {
       if (S > 1) {
         const int t2 = gm * NB2 + nb;
@@ -585,12 +618,14 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_w4a16_kernel(const FusedW4Args
   extern __shared__ __align__(16) uint8_t smem[];
   int32_t* s_mbp = (int32_t*)(smem + V_PIPE);  // row-block prefix per expert, kept for the whole launch
   int32_t* s_item = s_mbp + p.L + 1;            // the current item, then the last-part / last-out flag
+  int32_t* s_pend = s_item + 2;                 // L1 row blocks not yet published
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int L = p.L;
   int32_t* err = p.ctl + 2;
   int32_t* tile_done = p.ctl + 4;
 
+  if (tid == 0) s_pend[0] = 0;
   fused_block_prefix(p.offsets, L, s_mbp);
   // more rows than max_rows: do nothing (as the bf16 kernel)
   const bool too_many = p.offsets[L] > p.max_rows || s_mbp[L] > p.row_blocks;
@@ -606,6 +641,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_w4a16_kernel(const FusedW4Args
     if (tid == 0) s_item[0] = atomicAdd(p.ctl, 1);
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item[0]);
+    if (item >= n1) fused_flush(p.arrive, s_pend);  // before any wait, and before leaving
     if (item >= n_all) break;
     const FusedItem t = fused_item(item, n1, NB1, NB2, S, L, s_mbp, p.offsets);
     const bool l2 = t.l2;
@@ -766,7 +802,7 @@ __global__ __launch_bounds__(F_NT) void fused_ffn_w4a16_kernel(const FusedW4Args
           *(u32x4_t*)(p.act + (int64_t)(row_beg + r) * p.D + nb * 128 + pc * 8) =
               *(const u32x4_t*)(smem + r * V_APITCH + pc * 16);
       }
-      fused_count_in(p.arrive + gm);  // this part of the row block is published
+      fused_count_in(p.arrive, gm, s_pend);  // this part of the row block is done
     } else {
       if (S > 1) {
         const int t2 = gm * NB2 + nb;
@@ -798,7 +834,7 @@ int fused_cu_count() {
 
 template <typename KernelT>
 hipError_t launch_fused_kernel(KernelT kern, const FusedArgs& a, hipStream_t st) {
-  const int lds = F_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  const int lds = F_PIPE + (a.L + 4 + F_PUB) * (int)sizeof(int32_t);
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int grid = fused_cu_count();
@@ -818,7 +854,7 @@ hipError_t launch_fused_act(const FusedArgs& a, int fmt, int out_bf16, hipStream
 
 template <typename KernelT>
 hipError_t launch_fused_mx_kernel(KernelT kern, const FusedMxArgs& a, hipStream_t st) {
-  const int lds = T32_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  const int lds = T32_PIPE + (a.L + 4 + F_PUB) * (int)sizeof(int32_t);
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int grid = M_WG_PER_CU * fused_cu_count();
@@ -829,7 +865,7 @@ hipError_t launch_fused_mx_kernel(KernelT kern, const FusedMxArgs& a, hipStream_
 
 template <typename KernelT>
 hipError_t launch_fused_w4_kernel(KernelT kern, const FusedW4Args& a, hipStream_t st) {
-  const int lds = V_PIPE + (a.L + 4) * (int)sizeof(int32_t);
+  const int lds = V_PIPE + (a.L + 4 + F_PUB) * (int)sizeof(int32_t);
   hipError_t err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (err != hipSuccess) return err;
   const int grid = M_WG_PER_CU * fused_cu_count();
