@@ -67,12 +67,13 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(self.ev[i]))
 
 
-def algorithmic_work(cfg) -> dict:
+def algorithmic_work(cfg, rows=None) -> dict:
     """Algorithmic work of one layer step: the flops of the two grouped GEMMs
     and the HBM bytes of the bandwidth kernels (each tensor read or written
-    once), the figures the roofline fractions are computed from."""
+    once), the figures the roofline fractions are computed from.  rows: the
+    expert rows the local experts received (default every slot, T*k)."""
     T, H, D, E, k = cfg.T, cfg.H, cfg.D, cfg.E, cfg.k
-    R = T * k
+    R = T * k if rows is None else rows
     if cfg.router == "softmax":   # reads x and W_gate, writes indices and weights
         route_bytes = 2 * T * H + 2 * H * E + 8 * T * k
     else:                         # reads the logits and the bias, writes indices and weights (and sink weights)
@@ -80,7 +81,7 @@ def algorithmic_work(cfg) -> dict:
     # build_indices: the CSR (histogram, scan, scatter: 20 bytes per routed row)
     # plus, for the fp8 and W4A8 layers, the quantisation of x (each token
     # once: bf16 read, codes and scales written; the GEMM gathers the rows)
-    idx_bytes = 20 * R + 4 * (E + 1)
+    idx_bytes = 20 * T * k + 4 * (E + 1)
     if cfg.operand_dtype == "fp8":
         idx_bytes += 2 * T * H + T * H + 4 * T * (H // 128)
     elif cfg.operand_dtype == "mxfp4":
@@ -89,7 +90,7 @@ def algorithmic_work(cfg) -> dict:
     n_sh = getattr(cfg, "n_shared", 0)
     # combine: read every routed row of O (and each token's shared-expert rows),
     # the slot rows and weights (and the sink weights), write y in bf16
-    comb_bytes = o_bytes * (R + n_sh * T) * H + 8 * R + 4 * n_sh * T + 2 * T * H
+    comb_bytes = o_bytes * (R + n_sh * T) * H + 8 * T * k + 4 * n_sh * T + 2 * T * H
     return {"gate_up_flops": 4.0 * R * H * D, "down_flops": 2.0 * R * D * H, "route_bytes": route_bytes,
             "build_indices_bytes": idx_bytes, "combine_bytes": comb_bytes}
 
@@ -601,6 +602,10 @@ def main():
     ap.add_argument("--scale-tokens", type=int, default=1, metavar="N",
                     help="secondary data point: run the workload with N times its tokens, where the small "
                          "bandwidth kernels leave the launch-latency regime (the config-size line is the reported one)")
+    ap.add_argument("--ep-share", type=int, default=1, metavar="G",
+                    help="secondary data point: one rank's share of an expert-parallel layer over G GPUs "
+                         "(G times the tokens routed over every expert, the first E/G experts local, row "
+                         "buffers sized to the rows they receive); the exchanges between ranks are left out")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     ap.add_argument("--summarize-profile", metavar="DIR",
@@ -633,6 +638,14 @@ def main():
     cfg = synth.get_config(args.cfg)
     if args.scale_tokens > 1:
         cfg = synth.scaled(cfg, T=cfg.T * args.scale_tokens)
+    ep = args.ep_share
+    if ep > 1:
+        if (cfg.E % ep or getattr(cfg, "n_shared", 0) or cfg.fused or args.backward or args.scale_tokens > 1
+                or args.layout != "out_in"):
+            print("bench.py --ep-share: the two-launch forward of a layer without shared experts whose "
+                  "expert count G divides, alone", file=sys.stderr)
+            sys.exit(2)
+        cfg = synth.scaled(cfg, T=cfg.T * ep)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print(f"[bench] generating workload cfg {cfg.cfg_id} ({cfg.name})", file=sys.stderr, flush=True)
@@ -649,7 +662,15 @@ def main():
         print("bench.py --layout in_out: the stacked layout is read by the two-launch bf16 FFN",
               file=sys.stderr)
         sys.exit(2)
-    layer = moe.MoELayer(cfg, inp, layout=layout, fused=False if args.two_launch else None)
+    if ep > 1:
+        layer = moe.MoELayer(cfg, inp, layout=layout, fused=False, expert_slice=(0, cfg.E // ep), max_rows=0)
+        local_rows = layer.local_rows(inp["x"])
+        layer.reserve_rows(local_rows)
+        print(f"[bench] rank share of EP={ep}: {cfg.E // ep} local experts receive {local_rows} rows",
+              file=sys.stderr, flush=True)
+    else:
+        local_rows = None
+        layer = moe.MoELayer(cfg, inp, layout=layout, fused=False if args.two_launch else None)
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
     # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
@@ -686,8 +707,10 @@ def main():
     t_comb = (mean_ms(9, 6) if has_shared else mean_ms(5, 6))
     t_layer_dev = mean_ms(0, 6)
     ev.close()
-    R = cfg.T * cfg.k
-    work = algorithmic_work(cfg)
+    R = cfg.T * cfg.k if local_rows is None else local_rows
+    work = algorithmic_work(cfg, rows=local_rows)
+    if ep > 1 and int(layer.last_offsets[-1].item()) != local_rows:
+        raise RuntimeError("the routed row count changed between steps")
     print("[bench] bandwidth kernels alone from a flushed cache", file=sys.stderr, flush=True)
     flushed = flushed_bandwidth(layer, moe, torch, work)
     print("[bench] measured ceilings (MFMA loop, streaming copy and read)", file=sys.stderr, flush=True)
@@ -695,6 +718,9 @@ def main():
     print("[bench] the same step replayed from a HIP graph", file=sys.stderr, flush=True)
     graph_ms = graph_replay_ms(layer, inp["x"], torch, K, W)
 
+    # the committed HBM counters were taken on the default workload only
+    default_workload = (cfg.cfg_id == 2 and args.scale_tokens == 1 and ep == 1 and args.layout == "out_in"
+                        and not args.two_launch)
     gu_flops, dn_flops = work["gate_up_flops"], work["down_flops"]
     route_bytes, idx_bytes, comb_bytes = work["route_bytes"], work["build_indices_bytes"], work["combine_bytes"]
     # fp8 and the MXFP4 x MXFP8 product (which runs at the fp8 MFMA rate) take the fp8 peak
@@ -702,7 +728,7 @@ def main():
     gu_tf = gu_flops / (t_gu * 1e-3) / 1e12
     ffn_tf = (gu_flops + dn_flops) / ((t_gu + t_dn) * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": round(gu_tf, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(gu_tf / peak, 4), "traffic": _traffic() if cfg.cfg_id == 2 else None,
+            "frac": round(gu_tf / peak, 4), "traffic": _traffic() if default_workload else None,
             "kernel": "grouped gate_up GEMM + fused activation",
             "flops_per_launch": gu_flops, "avg_launch_ms": round(t_gu, 4)}
     if cfg.operand_dtype == "mxfp4_a16":
@@ -745,6 +771,10 @@ def main():
         "dtype": {"bf16": "bf16", "fp8": "fp8", "mxfp4": "mxfp4_w4a8", "mxfp4_a16": "mxfp4_w4a16"}[cfg.operand_dtype],
         "data": "synthetic",
         "config": {"workload": ("" if args.scale_tokens == 1 else f"[secondary: {args.scale_tokens}x tokens] ")
+                               + ("" if ep == 1 else f"[secondary: one rank's share of expert parallelism over "
+                                                     f"{ep} GPUs: experts 0..{cfg.E // ep - 1} local, "
+                                                     f"{local_rows} rows received; route and combine over all "
+                                                     f"tokens, no exchange] ")
                                + f"{cfg.name} MoE FFN forward: T={cfg.T} hidden={cfg.H} experts={cfg.E} "
                                f"top-{cfg.k} {cfg.router} router moe_dim={cfg.D} {cfg.gate_up_format} "
                                f"{cfg.activation}", "tokens": cfg.T, "hidden_dim": cfg.H,
@@ -776,7 +806,7 @@ def main():
                           "directly)" if args.layout == "in_out" else
                           "out_in (transposed stacked weights, laid out once at load)"),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and ep == 1:
         print("[bench] cpu baseline (oracle on a token sample)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, inp, min(args.cpu_sample, cfg.T))
     else:

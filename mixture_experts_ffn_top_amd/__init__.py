@@ -538,29 +538,47 @@ class ExpertWeights:
 
 class MoELayer:
     """The whole forward pass over pre-allocated buffers: route ->
-    build_indices -> grouped_ffn -> combine, all on torch's current stream."""
+    build_indices -> grouped_ffn -> combine, all on torch's current stream.
 
-    def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True, fused=None):
+    expert_slice=(start, n) keeps only the routed experts [start, start + n):
+    one expert-parallel rank's share (moe.experts page, GroupedExperts:
+    experts_start_idx / n_local_experts).  Its weights are those experts'
+    slices of the stacked tensors, assignments to other experts are dropped
+    by the bucketing, and the combine sums the local slots only (in an
+    expert-parallel layer the other ranks' slots arrive by the exchange
+    that one GPU leaves out).  max_rows bounds the rows the local experts
+    receive (default T*k, every slot); a smaller bound, such as the row count
+    an expert-parallel rank learns from its exchange, sizes the row buffers
+    and the GEMM grids, and every call must stay within it."""
+
+    def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True, fused=None, expert_slice=None,
+                 max_rows=None):
         self.cfg = cfg
         dev = inputs["x"].device
         self.device = dev
         self.gather = gather
         # the single-launch FFN (bf16 or MXFP4 x MXFP8): on when the configuration asks for it
         self.fused = getattr(cfg, "fused", False) if fused is None else fused
+        e0, L = expert_slice if expert_slice is not None else (0, cfg.E)
+        if not (0 <= e0 and L >= 1 and e0 + L <= cfg.E):
+            raise ValueError(f"expert_slice {expert_slice} is not a slice of the {cfg.E} routed experts")
+        if expert_slice is not None and getattr(cfg, "n_shared", 0):
+            raise ValueError("expert_slice covers the routed experts of layers without shared experts")
+        self.expert_start, self.n_local = e0, L
+
+        def local(t):
+            return t if t is None or (e0, L) == (0, cfg.E) else t[e0:e0 + L]
         self.w = ExpertWeights.from_stacked(
-            inputs["w_gate_up"], inputs["w_down"], b_gate_up=inputs.get("b_gate_up"),
-            b_down=inputs.get("b_down"), w_gate_up_scale=inputs.get("w_gate_up_scale"),
-            w_down_scale=inputs.get("w_down_scale"), operand=cfg.operand_dtype, layout=layout)
+            local(inputs["w_gate_up"]), local(inputs["w_down"]), b_gate_up=local(inputs.get("b_gate_up")),
+            b_down=local(inputs.get("b_down")), w_gate_up_scale=local(inputs.get("w_gate_up_scale")),
+            w_down_scale=local(inputs.get("w_down_scale")), operand=cfg.operand_dtype, layout=layout)
         self.w_gate = inputs.get("w_gate")
         self.logits = inputs.get("logits")
         self.expert_bias = inputs.get("expert_bias")
         self.global_scale = torch.tensor([cfg.global_scale], dtype=torch.float32, device=dev)
         T, k = cfg.T, cfg.k
-        R = T * k
-        self.R = R
-        self.act_ws = ffn_workspace(R, cfg.D, cfg.operand_dtype, dev, fused=self.fused, L=cfg.E, H=cfg.H)
         self.out_dtype = torch.float32 if cfg.operand_dtype in ("bf16", "mxfp4_a16") else torch.bfloat16
-        self.O = torch.empty((max(R, 1), cfg.H), dtype=self.out_dtype, device=dev)
+        self.reserve_rows(T * k if max_rows is None else max_rows)
         self.y = torch.empty((T, cfg.H), dtype=torch.bfloat16, device=dev)
         # shared experts: their own weights and buckets (every token in each)
         self.n_shared = getattr(cfg, "n_shared", 0)
@@ -579,6 +597,32 @@ class MoELayer:
             self.act_ws_shared = ffn_workspace(Rs, cfg.shared_dim, cfg.operand_dtype, dev)
             self.O_shared = torch.empty((max(Rs, 1), cfg.H), dtype=self.out_dtype, device=dev)
 
+    def reserve_rows(self, max_rows: int):
+        """(Re)size the row buffers (activation workspace, expert rows O) and
+        the bound the GEMM grids are sized for to max_rows rows."""
+        c = self.cfg
+        R = int(max_rows)
+        if not 0 <= R <= c.T * c.k:
+            raise ValueError(f"max_rows must be in [0, T*k = {c.T * c.k}] (got {max_rows})")
+        self.R = R
+        self.act_ws = ffn_workspace(R, c.D, c.operand_dtype, self.device, fused=self.fused, L=self.n_local, H=c.H)
+        self.O = torch.empty((max(R, 1), c.H), dtype=self.out_dtype, device=self.device)
+
+    def _route(self, x):
+        c = self.cfg
+        if c.router == "softmax":
+            return route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate,
+                         route_scale=c.route_scale, global_scale=self.global_scale)
+        return route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=self.logits,
+                     expert_bias=self.expert_bias, route_scale=c.route_scale, global_scale=self.global_scale)
+
+    def local_rows(self, x, token_mask=None) -> int:
+        """Rows the local experts receive for x: the routing and bucketing
+        alone, then a synchronising read of the count (set-up, not the step)."""
+        idx, w, _, _ = self._route(x)
+        ind = build_indices(idx, self.n_local, expert_start=self.expert_start, weights=w, token_mask=token_mask)
+        return int(ind["offsets"][-1].item())
+
     def forward(self, x, token_mask=None, mark=None, ffn_events=None, shared_events=None):
         """One layer pass.  mark(i), if given, is called on the host after
         each of the routing (i=1) and bucketing (i=2) calls and after the
@@ -586,13 +630,7 @@ class MoELayer:
         grouped FFN call (before gate_up, between the GEMMs, after down), and
         shared_events the same for the shared experts' FFN call."""
         c = self.cfg
-        if c.router == "softmax":
-            idx, w, sw, _ = route(router="softmax", k=c.k, E=c.E, x=x, w_gate=self.w_gate,
-                                  route_scale=c.route_scale, global_scale=self.global_scale)
-        else:
-            idx, w, sw, _ = route(router="sigmoid", k=c.k, E=c.E, s=c.s, logits=self.logits,
-                                  expert_bias=self.expert_bias, route_scale=c.route_scale,
-                                  global_scale=self.global_scale)
+        idx, w, sw, _ = self._route(x)
         if mark:
             mark(1)
         fp8 = c.operand_dtype in ("fp8", "mxfp4")
@@ -600,12 +638,12 @@ class MoELayer:
             # the fp8 / MXFP8 operand: every token quantised once; gathered by
             # the GEMM (gather=True) or quantised per permuted row here
             q = "fp8" if c.operand_dtype == "fp8" else "mxfp8"
-            ind = build_indices(idx, c.E, weights=w, token_mask=token_mask, x=x,
-                                xperm_dtype=q + "_tokens" if self.gather else q)
+            ind = build_indices(idx, self.n_local, expert_start=self.expert_start, weights=w,
+                                token_mask=token_mask, x=x, xperm_dtype=q + "_tokens" if self.gather else q)
             xg = ind.pop("x_perm") if self.gather else None
         else:
-            ind = build_indices(idx, c.E, weights=w, token_mask=token_mask,
-                                x=None if self.gather else x)
+            ind = build_indices(idx, self.n_local, expert_start=self.expert_start, weights=w,
+                                token_mask=token_mask, x=None if self.gather else x)
             xg = x if self.gather else None
         self.last_offsets = ind["offsets"]
         if mark:
@@ -656,11 +694,12 @@ class MoELayer:
             q = "fp8" if c.operand_dtype == "fp8" else "mxfp8"
 
             def bi():
-                return build_indices(idx, c.E, weights=w, token_mask=tm, x=x,
-                                     xperm_dtype=q + "_tokens" if self.gather else q)
+                return build_indices(idx, self.n_local, expert_start=self.expert_start, weights=w,
+                                     token_mask=tm, x=x, xperm_dtype=q + "_tokens" if self.gather else q)
         else:
             def bi():
-                return build_indices(idx, c.E, weights=w, token_mask=tm, x=None if self.gather else x)
+                return build_indices(idx, self.n_local, expert_start=self.expert_start, weights=w,
+                                     token_mask=tm, x=None if self.gather else x)
 
         def cb():
             return combine(f["O"], ind["row_of_slot"], c.T, c.k, weights=w, token_mask=tm, out=self.y,
@@ -683,7 +722,7 @@ class MoELayer:
                                   token_mask=f["token_mask"], weight_grad=weight_grad)
         if workspace is None:
             if getattr(self, "bwd_ws", None) is None:
-                self.bwd_ws = ffn_backward_workspace(self.R, c.H, c.D, c.E, self.device)
+                self.bwd_ws = ffn_backward_workspace(self.R, c.H, c.D, self.n_local, self.device)
             workspace = self.bwd_ws
         g = grouped_ffn_backward(ind["offsets"], self.R, self.w, dO, x=f["x_gather"],
                                  sorted_token=ind["sorted_token"] if self.gather else None,

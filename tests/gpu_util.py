@@ -46,6 +46,24 @@ def bf16_floor(y_ref) -> float:
     return rel_rms_err(O.bf16_round(y_ref), y_ref)[0]
 
 
+def err_beyond_bf16_output(got, want) -> float:
+    """max over elements of (|got - want| - half a bf16 ulp of got) / rms(want),
+    floored at 0: the error of a bf16 output beyond its own final rounding.
+    A bf16 value y = bf16_RNE(s) of an exact-arithmetic-free sum s satisfies
+    |y - s| <= 2^(floor(log2 |y|) - 8), so this bounds |s - want| / rms, the
+    arithmetic error before the output is rounded."""
+    g = np.asarray(got, np.float64)
+    w = np.asarray(want, np.float64)
+    rms = float(np.sqrt(np.mean(w * w))) if w.size else 0.0
+    a = np.abs(g)
+    half = np.where(a >= 2.0 ** -126, np.exp2(np.floor(np.log2(np.maximum(a, 2.0 ** -126))) - 8), 2.0 ** -134)
+    half = np.where(a == 0, 0.0, half)
+    beyond = np.maximum(np.abs(g - w) - half, 0.0)
+    if not g.size:
+        return 0.0
+    return float(beyond.max() / rms) if rms > 0 else float(beyond.max())
+
+
 def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
     if n >= T:
         return np.arange(T)

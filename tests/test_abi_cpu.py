@@ -443,3 +443,22 @@ def test_probe_stream_read_validation(args, frag):
 
 def test_probe_stream_read_zero_bytes_is_a_no_op():
     assert m.lib().moe_probe_stream_read(None, 0, None, 0, None) == m.MOE_OK
+
+
+@pytest.mark.parametrize("sl,frag", [((7, 2), "not a slice"), ((-1, 2), "not a slice"), ((0, 0), "not a slice")])
+def test_layer_expert_slice_validation(sl, frag):
+    """MoELayer refuses an expert slice outside the routed experts before it
+    touches any tensor."""
+    import torch
+    import synth
+    cfg = synth.get_config(1)
+    with pytest.raises(ValueError, match=frag):
+        m.MoELayer(cfg, {"x": torch.zeros(1)}, expert_slice=sl)
+
+
+def test_layer_expert_slice_refuses_shared_experts():
+    import torch
+    import synth
+    cfg = synth.get_config(3)
+    with pytest.raises(ValueError, match="without shared experts"):
+        m.MoELayer(cfg, {"x": torch.zeros(1)}, expert_slice=(0, 16))

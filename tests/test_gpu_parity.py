@@ -10,7 +10,7 @@ import torch
 
 import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_rel, bf16_floor, host, rel_rms_err, sample_tokens, say
+from tests.gpu_util import assert_rel, bf16_floor, err_beyond_bf16_output, host, rel_rms_err, sample_tokens, say
 
 pytestmark = pytest.mark.gpu
 
@@ -277,7 +277,7 @@ def _mblock_rows(off, seed, n_random=4, bm=256):
     return out
 
 
-def _check_expert_rows(cfg, inp, res, layer, tol, seed):
+def _check_expert_rows(cfg, inp, res, layer, tol, seed, expert_start=0):
     """Expert rows O of every m-block of every expert, at full size (rows are
     independent, so the oracle's cost stays bounded).
 
@@ -316,10 +316,11 @@ def _check_expert_rows(cfg, inp, res, layer, tol, seed):
     def one(i):
         e = experts[i]
         pos = slice(starts[i], starts[i + 1])
-        he = {kk: host(inp[kk][e:e + 1]) for kk in wkeys}
+        g = expert_start + e   # the expert's index among all routed experts
+        he = {kk: host(inp[kk][g:g + 1]) for kk in wkeys}
         wgu, wd = O._expert_weights_f64(he, 0, op)
-        bgu = host(inp["b_gate_up"][e]) if cfg.has_bias else None
-        bd = host(inp["b_down"][e]) if cfg.has_bias else None
+        bgu = host(inp["b_gate_up"][g]) if cfg.has_bias else None
+        bd = host(inp["b_down"][g]) if cfg.has_bias else None
         if kind:
             # the oracle's down projection on the GPU's own re-quantised A
             a_gpu = (O.dequant_rows_block128(cg_all[pos], sg_all[pos]) if kind == "fp8"
@@ -387,6 +388,77 @@ def test_layer_full_size(moe, cid, nsample):
     _check_routing(cfg, inp, res)
     _check_layer(cfg, inp, res, sample_tokens(cfg.T, nsample, seed=cid), BF16_TOL)
     _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=cid)
+
+
+# ---------------------------------------------------------------- one expert-parallel rank's share
+
+def _run_layer_slice(moe, cfg, inp, start, n, gather=True):
+    """MoELayer over the routed experts [start, start + n) only, its row
+    buffers sized to the rows those experts receive."""
+    layer = moe.MoELayer(cfg, inp, gather=gather, expert_slice=(start, n), max_rows=0)
+    rows = layer.local_rows(inp["x"])
+    layer.reserve_rows(rows)
+    res = layer.forward(inp["x"])
+    torch.cuda.synchronize()
+    assert int(host(res["index"]["offsets"])[-1]) == rows
+    return layer, res, rows
+
+
+def _check_layer_slice(cfg, inp, res, tokens, tol, start, n):
+    """y of the sampled tokens against the oracle layer restricted to the
+    local experts: the sum over each token's local slots, a zero row for a
+    token with none.  The bar is on the error beyond y's own final bf16
+    rounding (half an ulp of each output): with a few hundred tokens the
+    largest outputs reach several times the RMS, where that rounding alone
+    comes to 2e-2 x RMS, so a bar on the raw difference would fail an
+    exactly computed sum."""
+    hin = synth.to_host(inp)
+    idx = host(res["indices"])
+    y_ref = O.layer(hin, cfg, indices=idx, weights=host(res["weights"]).astype(np.float64), tokens=tokens,
+                    expert_start=start, num_local=n)
+    y = host(res["y"])[tokens]
+    live = np.any((idx[tokens] >= start) & (idx[tokens] < start + n), axis=1)
+    assert np.all(y[~live] == 0)
+    err, rms = rel_rms_err(y[live], y_ref[live])
+    beyond = err_beyond_bf16_output(y[live], y_ref[live])
+    say(f"  local slice y max err / rms = {err:.3e} ({beyond:.3e} beyond the output's bf16 rounding) over "
+        f"{int(live.sum())} tokens with a local slot (bf16 floor {bf16_floor(y_ref[live]):.3e})")
+    assert np.all(np.isfinite(y))
+    assert beyond <= tol
+
+
+@pytest.mark.parametrize("cid,changes,start,n,gather", [
+    (1, {}, 3, 4, True),
+    (2, {"T": 384, "H": 1024, "D": 2048}, 2, 3, False),
+    (4, {"T": 256, "E": 16, "k": 4}, 5, 6, True),                              # bias, interleaved, swigluoai
+    (5, {"T": 256, "H": 1024, "D": 512, "E": 32, "k": 8}, 8, 8, True),         # fp8 block-scaled
+    (6, {"T": 256, "H": 1024, "D": 512, "E": 32, "k": 8}, 24, 8, True),        # MXFP4 x MXFP8
+])
+def test_layer_expert_slice(moe, cid, changes, start, n, gather):
+    """One expert-parallel rank's share: the layer over a slice of the
+    routed experts, row buffers sized to the rows it receives."""
+    cfg = synth.scaled(synth.get_config(cid), **changes)
+    inp = _gen(cfg)
+    say(f"[layer slice] cfg={cid} {changes} experts {start}..{start + n - 1}")
+    layer, res, rows = _run_layer_slice(moe, cfg, inp, start, n, gather=gather)
+    say(f"  {rows} of {cfg.T * cfg.k} slots local")
+    tol = BF16_TOL if cfg.operand_dtype == "bf16" else FP8_TOL
+    _check_layer_slice(cfg, inp, res, np.arange(cfg.T), tol, start, n)
+    _check_expert_rows(cfg, inp, res, layer, tol, seed=cid, expert_start=start)
+
+
+def test_layer_expert_slice_mixtral_ep8_share(moe):
+    """The Mixtral-shape layer's share on one of 8 expert-parallel GPUs at
+    its real shape: 8 x 4096 tokens routed over the 8 experts, expert 0
+    local with the ~8192 rows it receives."""
+    base = synth.get_config(2)
+    cfg = synth.scaled(base, T=base.T * 8)
+    inp = _gen(cfg)
+    say("[layer slice full] Mixtral dims, T=32768, expert 0 of 8")
+    layer, res, rows = _run_layer_slice(moe, cfg, inp, 0, 1)
+    say(f"  {rows} rows local")
+    _check_layer_slice(cfg, inp, res, sample_tokens(cfg.T, 64, seed=12), BF16_TOL, 0, 1)
+    _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=12)
 
 
 # ---------------------------------------------------------------- the stacked (IN_OUT) weight layout
