@@ -200,30 +200,38 @@ PROFILE_CMDS = """# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp
 
 # the MX workloads' kernel traces, summarised by the same --summarize-profile call
 EXTRA_TRACES = [
-    ("trace3", 3, "sink_router_shared_experts_layer_kernel_stats.txt",
+    ("trace3", "--cfg 3", "sink_router_shared_experts_layer_kernel_stats.txt",
      "sigmoid-sink router layer with two shared experts: T=8192 tokens, hidden 2048, 128 experts, top-6 + 2 sink "
      "lanes, moe_dim 768, SiLU, bf16"),
-    ("trace4", 4, "gptoss_shape_layer_kernel_stats.txt",
+    ("trace4", "--cfg 4", "gptoss_shape_layer_kernel_stats.txt",
      "gpt-oss-shape layer: T=4096 tokens, hidden 2880, 32 experts, top-4 softmax gate, moe_dim 2880, interleaved "
      "gate_up, swigluoai (alpha 1.702, limit 7), biases, bf16"),
-    ("trace5", 5, "fp8_block_scaled_layer_kernel_stats.txt",
+    ("trace5", "--cfg 5", "fp8_block_scaled_layer_kernel_stats.txt",
      "fp8 block-scaled layer: T=16384 tokens, hidden 7168, 256 experts, top-8 sigmoid router, moe_dim 2048, "
      "SiLU, e4m3 operands with 128-wide fp32 block scales"),
-    ("trace6", 6, "mxfp4_w4a8_layer_kernel_stats.txt",
+    ("trace6", "--cfg 6", "mxfp4_w4a8_layer_kernel_stats.txt",
      "MXFP4 x MXFP8 (W4A8) layer: T=16384 tokens, hidden 7168, 256 experts, top-8 sigmoid router, "
      "moe_dim 2048, SiLU"),
-    ("trace7", 7, "mxfp4_w4a16_decode_kernel_stats.txt",
+    ("trace7", "--cfg 7", "mxfp4_w4a16_decode_kernel_stats.txt",
      "MXFP4 W4A16 layer on a decode-sized batch: T=256 tokens, hidden 7168, 256 experts, top-8 sigmoid "
      "router, moe_dim 2048, SiLU"),
-    ("trace8", 8, "mixtral_decode_fused_ffn_kernel_stats.txt",
+    ("trace8", "--cfg 8", "mixtral_decode_fused_ffn_kernel_stats.txt",
      "Mixtral decode batch through the single-launch FFN: T=64 tokens, hidden 4096, 8 experts, top-2 softmax "
      "router, moe_dim 14336, SiLU"),
-    ("trace9", 9, "mxfp4_decode_fused_ffn_kernel_stats.txt",
+    ("trace9", "--cfg 9", "mxfp4_decode_fused_ffn_kernel_stats.txt",
      "MXFP4 x MXFP8 decode batch through the single-launch FFN: T=256 tokens, hidden 7168, 256 experts, "
      "top-8 sigmoid router, moe_dim 2048, SiLU"),
-    ("trace10", 10, "mxfp4_a16_decode_fused_ffn_kernel_stats.txt",
+    ("trace10", "--cfg 10", "mxfp4_a16_decode_fused_ffn_kernel_stats.txt",
      "MXFP4 x bf16 (W4A16) decode batch through the single-launch FFN: T=256 tokens, hidden 7168, 256 "
      "experts, top-8 sigmoid router, moe_dim 2048, SiLU"),
+    ("trace2ep", "--cfg 2 --ep-share 8", "mixtral_ep8_share_kernel_stats.txt",
+     "one rank's share of the Mixtral-shape layer at expert parallelism 8: T=32768 tokens routed over the 8 "
+     "experts (top-2 softmax gate, hidden 4096, moe_dim 14336, SiLU, bf16), expert 0 local with the rows it "
+     "receives; route, bucketing and combine run over all 32768 tokens"),
+    ("trace5ep", "--cfg 5 --ep-share 8", "fp8_ep8_share_kernel_stats.txt",
+     "one rank's share of the fp8 block-scaled layer at expert parallelism 8: T=131072 tokens routed over the "
+     "256 experts (top-8 sigmoid router, hidden 7168, moe_dim 2048, SiLU, e4m3 with 128-wide fp32 block "
+     "scales), experts 0-31 local with the rows they receive; route, bucketing and combine over all tokens"),
 ]
 
 
@@ -236,8 +244,15 @@ def summarize_profile(d: str):
     """Turn the rocprofv3 outputs of PROFILE_CMDS into the committed summaries."""
     import csv
     prof = os.path.join(ROOT, "profiles")
-    # kernel statistics of the bench run
-    rows = list(csv.DictReader(open(os.path.join(d, "trace", "bench_kernel_stats.csv"))))
+    # kernel statistics of the bench run (each summary only from the outputs present in d)
+    main_stats = os.path.join(d, "trace", "bench_kernel_stats.csv")
+    if os.path.exists(main_stats):
+        _summarize_main_trace(d, csv, main_stats, prof)
+    _summarize_extra_and_counters(d, csv, prof)
+
+
+def _summarize_main_trace(d, csv, main_stats, prof):
+    rows = list(csv.DictReader(open(main_stats)))
     mine = [r for r in rows if "moe::" in r["Name"]]
     line = None
     for ln in open(os.path.join(d, "trace.log")):
@@ -263,7 +278,9 @@ def summarize_profile(d: str):
             "# the timed steps (6 launches each), not part of the layer"]
     open(os.path.join(prof, "mixtral_layer_kernel_stats.txt"), "w").write("\n".join(out) + "\n")
 
-    for sub, cid, name, title in EXTRA_TRACES:
+
+def _summarize_extra_and_counters(d, csv, prof):
+    for sub, bargs, name, title in EXTRA_TRACES:
         stats = os.path.join(d, sub, "bench_kernel_stats.csv")
         if not os.path.exists(stats):
             continue
@@ -275,7 +292,7 @@ def summarize_profile(d: str):
         out = [f"# rocprofv3 kernel statistics: {title}",
                "# command (repo root as $REPO, run from /tmp with TMPDIR=/tmp):",
                f"#   rocprofv3 --kernel-trace --stats -f csv -d $REPO/gpurun_out/prof/{sub} -o bench -- \\",
-               f"#       python3 $REPO/bench.py --cfg {cid} --steps 10 --warmup 3 --no-cpu-baseline "
+               f"#       python3 $REPO/bench.py {bargs} --steps 10 --warmup 3 --no-cpu-baseline "
                f"> $REPO/gpurun_out/prof/{sub}.log",
                "#   python3 bench.py --summarize-profile gpurun_out/prof",
                "# calls = warmup + timed steps.  Durations in microseconds; only this library's kernels.",
@@ -294,6 +311,9 @@ def summarize_profile(d: str):
             per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         return per
     n_copy = 1 << 30
+    if not os.path.exists(os.path.join(d, "FETCH_SIZE", "bench_counter_collection.csv")):
+        _summarize_pipe_counters(d, prof)
+        return
     cf = counters(os.path.join(d, "copy_FETCH_SIZE", "copy_counter_collection.csv"))
     cw = counters(os.path.join(d, "copy_WRITE_SIZE", "copy_counter_collection.csv"))
     copy_f = [v for k, vs in cf.items() if "copyBuffer" in k for v in vs]
@@ -338,6 +358,10 @@ def summarize_profile(d: str):
                    "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
                    "kernel_source_sha256_16": src_hash, "source": "profiles/mixtral_layer_hbm_traffic.txt"},
                   open(TRAFFIC_FILE, "w"), indent=1)
+    _summarize_pipe_counters(d, prof)
+
+
+def _summarize_pipe_counters(d, prof):
     for sub, name, title in (
             ("SQ2", "mixtral_gemm_pipe_counters.txt",
              "bf16 grouped GEMMs of the Mixtral-shape layer (T=4096, hidden 4096, 8 experts, top-2, moe_dim 14336)"),
