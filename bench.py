@@ -698,14 +698,15 @@ def main():
     stream = torch.cuda.current_stream(dev).cuda_stream
     K, W = args.steps, args.warmup
     # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
-    # 6 after combine, 7..9 the shared experts' ffn (if any)
-    NE = 10
+    # 6 after combine, 7..9 the shared experts' ffn (if any; on their own stream, beside
+    # the routing and the routed ffn), 10 before the combine
+    NE = 11
     ev = HipEvents(NE * (K + W))
     has_shared = getattr(cfg, "n_shared", 0) > 0
 
     def step(i):
         base = NE * i
-        slots = {1: base + 1, 2: base + 2, 3: base + 6}
+        slots = {1: base + 1, 2: base + 2, 3: base + 6, 4: base + 10}
         ev.record(base + 0, stream)
         layer.forward(inp["x"], mark=lambda j: ev.record(slots[j], stream), ffn_events=ev.triple(base + 3),
                       shared_events=ev.triple(base + 7) if has_shared else None)
@@ -728,7 +729,7 @@ def main():
     t_route, t_idx = mean_ms(0, 1), mean_ms(1, 2)
     t_gu, t_dn = mean_ms(3, 4), mean_ms(4, 5)
     t_shared = mean_ms(7, 9) if has_shared else 0.0
-    t_comb = (mean_ms(9, 6) if has_shared else mean_ms(5, 6))
+    t_comb = mean_ms(10, 6)
     t_layer_dev = mean_ms(0, 6)
     ev.close()
     R = cfg.T * cfg.k if local_rows is None else local_rows

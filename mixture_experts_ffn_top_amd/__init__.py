@@ -552,7 +552,7 @@ class MoELayer:
     and the GEMM grids, and every call must stay within it."""
 
     def __init__(self, cfg, inputs: dict, *, layout=WEIGHT_OUT_IN, gather=True, fused=None, expert_slice=None,
-                 max_rows=None):
+                 max_rows=None, overlap_shared=True):
         self.cfg = cfg
         dev = inputs["x"].device
         self.device = dev
@@ -596,6 +596,12 @@ class MoELayer:
             self.shared_offsets, self.shared_token = shared_indices(T, self.n_shared, dev)
             self.act_ws_shared = ffn_workspace(Rs, cfg.shared_dim, cfg.operand_dtype, dev)
             self.O_shared = torch.empty((max(Rs, 1), cfg.H), dtype=self.out_dtype, device=dev)
+            # the shared experts' FFN depends on x alone (and, for the fp8 and
+            # MXFP8 operands, on its per-token codes), not on the routing: it
+            # runs on a second stream (default priority) beside the routing,
+            # the bucketing and the routed FFN, so that its tiles fill the
+            # CUs the routed GEMMs leave idle in their last rounds
+            self.side = torch.cuda.Stream(device=dev) if overlap_shared and dev.type == "cuda" else None
 
     def reserve_rows(self, max_rows: int):
         """(Re)size the row buffers (activation workspace, expert rows O) and
@@ -625,15 +631,24 @@ class MoELayer:
 
     def forward(self, x, token_mask=None, mark=None, ffn_events=None, shared_events=None):
         """One layer pass.  mark(i), if given, is called on the host after
-        each of the routing (i=1) and bucketing (i=2) calls and after the
-        combine (i=3); ffn_events are hipEvent_t handles recorded inside the
+        each of the routing (i=1) and bucketing (i=2) calls, just before the
+        combine (i=4, once the shared experts' stream has joined) and after
+        it (i=3); ffn_events are hipEvent_t handles recorded inside the
         grouped FFN call (before gate_up, between the GEMMs, after down), and
-        shared_events the same for the shared experts' FFN call."""
+        shared_events the same for the shared experts' FFN call (on their
+        stream)."""
         c = self.cfg
+        fp8 = c.operand_dtype in ("fp8", "mxfp4")
+        side = self.side if self.n_shared else None
+        main = torch.cuda.current_stream(self.device) if side is not None else None
+        O_sh = None
+        if side is not None and not fp8:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                O_sh = self._shared_ffn(x, None, shared_events)
         idx, w, sw, _ = self._route(x)
         if mark:
             mark(1)
-        fp8 = c.operand_dtype in ("fp8", "mxfp4")
         if fp8:
             # the fp8 / MXFP8 operand: every token quantised once; gathered by
             # the GEMM (gather=True) or quantised per permuted row here
@@ -648,21 +663,22 @@ class MoELayer:
         self.last_offsets = ind["offsets"]
         if mark:
             mark(2)
+        if side is not None and fp8:
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                O_sh = self._shared_ffn(xg, ind.get("x_perm_scale"), shared_events)
         O = grouped_ffn(ind["offsets"], self.R, self.w, x_perm=ind.get("x_perm"),
                         x_perm_scale=ind.get("x_perm_scale"), x=xg,
                         sorted_token=ind["sorted_token"] if self.gather else None,
                         activation=c.activation, alpha=c.alpha, limit=c.limit,
                         gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
                         act_workspace=self.act_ws, out=self.O, timing_events=ffn_events, fused=self.fused)
-        O_sh = None
-        if self.n_shared:
-            xs = xg if fp8 else x
-            O_sh = grouped_ffn(self.shared_offsets, self.R_shared, self.w_shared,
-                               x_perm_scale=ind.get("x_perm_scale") if fp8 else None, x=xs,
-                               sorted_token=self.shared_token, activation=c.activation, alpha=c.alpha,
-                               limit=c.limit, gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
-                               act_workspace=self.act_ws_shared, out=self.O_shared,
-                               timing_events=shared_events)
+        if side is not None:
+            main.wait_stream(side)
+        elif self.n_shared:
+            O_sh = self._shared_ffn(xg if fp8 else x, ind.get("x_perm_scale") if fp8 else None, shared_events)
+        if mark:
+            mark(4)
         y = combine(O, ind["row_of_slot"], c.T, c.k, weights=w, token_mask=token_mask, out=self.y,
                     shared_out=O_sh, shared_weights=sw if c.router == "sigmoid_sink" else None,
                     n_shared=self.n_shared)
@@ -672,6 +688,15 @@ class MoELayer:
                      "indices": idx, "O_shared": O_sh, "sink_weights": sw}
         return {"y": y, "indices": idx, "weights": w, "sink_weights": sw, "index": ind, "O": O,
                 "O_shared": O_sh}
+
+    def _shared_ffn(self, xs, xs_scale, timing_events):
+        """The shared experts' FFN on every token (their buckets hold all T
+        tokens), on the current stream."""
+        c = self.cfg
+        return grouped_ffn(self.shared_offsets, self.R_shared, self.w_shared, x_perm_scale=xs_scale, x=xs,
+                           sorted_token=self.shared_token, activation=c.activation, alpha=c.alpha,
+                           limit=c.limit, gate_up_format=c.gate_up_format, out_dtype=self.out_dtype,
+                           act_workspace=self.act_ws_shared, out=self.O_shared, timing_events=timing_events)
 
     def stage_calls(self):
         """The routing, bucketing and combine calls of the last forward, each

@@ -742,6 +742,30 @@ def test_layer_with_shared_experts(moe, cid, changes, nsample):
     _check_layer(cfg, inp, res_m, sample_tokens(cfg.T, nsample), tol, token_mask=host(mask))
 
 
+@pytest.mark.parametrize("cid,changes", [
+    (3, {"T": 700, "E": 32, "D": 256, "shared_dim": 512}),                                   # bf16, sink-gated
+    (5, {"T": 256, "E": 8, "k": 3, "s": 1, "n_shared": 1, "H": 512, "D": 256, "shared_dim": 384}),  # fp8
+    (6, {"T": 300, "E": 8, "k": 2, "s": 2, "n_shared": 2, "H": 512, "D": 256, "shared_dim": 384}),  # W4A8
+])
+def test_shared_experts_on_their_own_stream(moe, cid, changes):
+    """The shared experts' FFN on a second stream beside the routed path
+    gives the same bytes as the same calls in one stream, call after call."""
+    cfg = synth.scaled(synth.get_config(cid), **changes)
+    inp = _gen(cfg)
+    say(f"[shared stream] cfg={cid} {changes}")
+    seq = moe.MoELayer(cfg, inp, overlap_shared=False)
+    ovl = moe.MoELayer(cfg, inp)
+    assert ovl.side is not None
+    want = seq.forward(inp["x"])
+    ys = host(want["y"]).copy()
+    osh = host(want["O_shared"]).copy()
+    for _ in range(3):
+        got = ovl.forward(inp["x"])
+        torch.cuda.synchronize()
+        assert np.array_equal(host(got["O_shared"]), osh)
+        assert np.array_equal(host(got["y"]), ys)
+
+
 def test_abi_errors_on_gpu_path(moe):
     """Invalid arguments are refused before any launch, also from the binding."""
     x = torch.zeros((4, 24), dtype=torch.bfloat16, device=DEV)
