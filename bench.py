@@ -699,13 +699,20 @@ def main():
     K, W = args.steps, args.warmup
     # per step: 0 start, 1 after route, 2 after indices, 3..5 ffn (gate_up start, mid, end),
     # 6 after combine, 7..9 the shared experts' ffn (if any; on their own stream, beside
-    # the routing and the routed ffn), 10 before the combine
+    # the routing and the routed ffn), 10 before the combine.  The timed steps record
+    # only the three events inside the FFN call (the GEMMs' own durations); every
+    # event between the kernels costs the step a few microseconds (0.8 % of the
+    # Mixtral step, a third of the tiny one), so the per-stage breakdown comes from
+    # K more steps after the timed region, with all of them.
     NE = 11
-    ev = HipEvents(NE * (K + W))
+    ev = HipEvents(NE * (W + 2 * K))
     has_shared = getattr(cfg, "n_shared", 0) > 0
 
-    def step(i):
+    def step(i, instrumented):
         base = NE * i
+        if not instrumented:
+            layer.forward(inp["x"], ffn_events=ev.triple(base + 3))
+            return
         slots = {1: base + 1, 2: base + 2, 3: base + 6, 4: base + 10}
         ev.record(base + 0, stream)
         layer.forward(inp["x"], mark=lambda j: ev.record(slots[j], stream), ffn_events=ev.triple(base + 3),
@@ -713,21 +720,28 @@ def main():
 
     print(f"[bench] warmup {W}", file=sys.stderr, flush=True)
     for i in range(W):
-        step(i)
+        step(i, False)
     torch.cuda.synchronize()
     print(f"[bench] timing {K} steps", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(W, W + K):
-        step(i)
+        step(i, False)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     ms_step = dt * 1000.0 / K
+    print(f"[bench] {K} more steps with events between the kernels (per-stage breakdown)", file=sys.stderr,
+          flush=True)
+    for i in range(W + K, W + 2 * K):
+        step(i, True)
+    torch.cuda.synchronize()
 
-    def mean_ms(a, b):
-        return sum(ev.elapsed_ms(NE * i + a, NE * i + b) for i in range(W, W + K)) / K
+    def mean_ms(a, b, timed=False):
+        steps = range(W, W + K) if timed else range(W + K, W + 2 * K)
+        return sum(ev.elapsed_ms(NE * i + a, NE * i + b) for i in steps) / K
 
     t_route, t_idx = mean_ms(0, 1), mean_ms(1, 2)
-    t_gu, t_dn = mean_ms(3, 4), mean_ms(4, 5)
+    # the GEMMs from the timed steps themselves
+    t_gu, t_dn = mean_ms(3, 4, timed=True), mean_ms(4, 5, timed=True)
     t_shared = mean_ms(7, 9) if has_shared else 0.0
     t_comb = mean_ms(10, 6)
     t_layer_dev = mean_ms(0, 6)
