@@ -433,6 +433,8 @@ def _check_layer_slice(cfg, inp, res, tokens, tol, start, n):
     (4, {"T": 256, "E": 16, "k": 4}, 5, 6, True),                              # bias, interleaved, swigluoai
     (5, {"T": 256, "H": 1024, "D": 512, "E": 32, "k": 8}, 8, 8, True),         # fp8 block-scaled
     (6, {"T": 256, "H": 1024, "D": 512, "E": 32, "k": 8}, 24, 8, True),        # MXFP4 x MXFP8
+    (8, {"H": 1024, "D": 2048}, 2, 4, True),                                   # single-launch FFN, bf16
+    (9, {"H": 1024, "D": 512}, 64, 32, True),                                 # single-launch FFN, W4A8
 ])
 def test_layer_expert_slice(moe, cid, changes, start, n, gather):
     """One expert-parallel rank's share: the layer over a slice of the
