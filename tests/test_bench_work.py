@@ -3,10 +3,14 @@ worked out by hand from the workloads' tensor shapes: the FLOP of the grouped
 FFN (6 R H D, R = T k), the bytes of the softmax router (x and W_gate read
 once, indices and weights written) and of the combine (O read once, the slot
 rows and weights read, y written in bf16)."""
+import os
+
 import pytest
 
 import bench
 import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 @pytest.mark.parametrize("cid,ffn_flop", [(1, 1.007e8), (2, 2.886e12), (3, 4.639e11), (4, 8.154e11),
@@ -50,3 +54,29 @@ def test_single_launch_ffn_bytes():
     # the same experts with bf16 rows (W4A16): x 2048*7168*2, A 2*2048*2048*2, O fp32 2048*7168*4
     cfg = synth.get_config(10)
     assert bench.fused_ffn_bytes(cfg, 142) == 142 * 23_396_352 + 29_360_128 + 16_777_216 + 58_720_256
+
+
+def test_algorithmic_work_with_local_rows():
+    """An expert-parallel share: the GEMM flops and the combine's O bytes
+    follow the rows the local experts received; the bucketing still reads
+    every slot."""
+    import synth
+    cfg = synth.scaled(synth.get_config(2), T=32768)
+    full = bench.algorithmic_work(cfg)
+    part = bench.algorithmic_work(cfg, rows=8318)
+    assert part["gate_up_flops"] == 4.0 * 8318 * 4096 * 14336
+    assert part["down_flops"] == 2.0 * 8318 * 14336 * 4096
+    assert part["build_indices_bytes"] == full["build_indices_bytes"]
+    assert full["combine_bytes"] - part["combine_bytes"] == 4 * (32768 * 2 - 8318) * 4096
+
+
+@pytest.mark.parametrize("argv", [["--cfg", "2", "--ep-share", "3"], ["--cfg", "3", "--ep-share", "8"],
+                                  ["--cfg", "8", "--ep-share", "2"], ["--gpus", "2"]])
+def test_bench_refuses_unsupported_runs(argv):
+    """Runs the bench cannot make exit with status 2 and a message, before any GPU use."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *argv], capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 2, r.stderr
+    assert "bench.py" in r.stderr
