@@ -305,21 +305,12 @@ def _summarize_extra_and_counters(d, csv, prof):
         open(os.path.join(prof, name), "w").write("\n".join(out) + "\n")
 
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated on a plain copy of known size
-    def counters(path):
-        per = {}
-        for r in csv.DictReader(open(path)):
-            per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
-        return per
-    n_copy = 1 << 30
+    counters = _pmc_counters
+    _summarize_ep_traffic(d, prof)
     if not os.path.exists(os.path.join(d, "FETCH_SIZE", "bench_counter_collection.csv")):
         _summarize_pipe_counters(d, prof)
         return
-    cf = counters(os.path.join(d, "copy_FETCH_SIZE", "copy_counter_collection.csv"))
-    cw = counters(os.path.join(d, "copy_WRITE_SIZE", "copy_counter_collection.csv"))
-    copy_f = [v for k, vs in cf.items() if "copyBuffer" in k for v in vs]
-    copy_w = [v for k, vs in cw.items() if "copyBuffer" in k for v in vs]
-    f_factor = n_copy / (sum(copy_f) / len(copy_f) * 1024)
-    w_factor = n_copy / (sum(copy_w) / len(copy_w) * 1024)
+    copy_f, copy_w, f_factor, w_factor = _copy_calibration(d)
     fe = counters(os.path.join(d, "FETCH_SIZE", "bench_counter_collection.csv"))
     wr = counters(os.path.join(d, "WRITE_SIZE", "bench_counter_collection.csv"))
     out = ["# HBM traffic per launch from rocprofv3 counters: Mixtral-shape MoE FFN layer (bench.py workload)",
@@ -359,6 +350,68 @@ def _summarize_extra_and_counters(d, csv, prof):
                    "kernel_source_sha256_16": src_hash, "source": "profiles/mixtral_layer_hbm_traffic.txt"},
                   open(TRAFFIC_FILE, "w"), indent=1)
     _summarize_pipe_counters(d, prof)
+
+
+def _pmc_counters(path):
+    """{kernel: [counter value per dispatch]} of one rocprofv3 --pmc pass."""
+    import csv
+    per = {}
+    for r in csv.DictReader(open(path)):
+        per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def _copy_calibration(d):
+    """FETCH_SIZE / WRITE_SIZE of a plain 1 GiB device copy: the factors that
+    turn the counters (KiB per dispatch) into bytes."""
+    n_copy = 1 << 30
+    cf = _pmc_counters(os.path.join(d, "copy_FETCH_SIZE", "copy_counter_collection.csv"))
+    cw = _pmc_counters(os.path.join(d, "copy_WRITE_SIZE", "copy_counter_collection.csv"))
+    copy_f = [v for k, vs in cf.items() if "copyBuffer" in k for v in vs]
+    copy_w = [v for k, vs in cw.items() if "copyBuffer" in k for v in vs]
+    return (copy_f, copy_w, n_copy / (sum(copy_f) / len(copy_f) * 1024),
+            n_copy / (sum(copy_w) / len(copy_w) * 1024))
+
+
+def _summarize_ep_traffic(d, prof):
+    """HBM traffic of the GEMMs of one expert-parallel rank's share of the
+    Mixtral-shape layer (bench.py --cfg 2 --ep-share 8), if its counter
+    passes are in d."""
+    fe_p = os.path.join(d, "FETCH_SIZE_ep8", "bench_counter_collection.csv")
+    wr_p = os.path.join(d, "WRITE_SIZE_ep8", "bench_counter_collection.csv")
+    if not (os.path.exists(fe_p) and os.path.exists(wr_p)):
+        return
+    copy_f, copy_w, f_factor, w_factor = _copy_calibration(d)
+    fe, wr = _pmc_counters(fe_p), _pmc_counters(wr_p)
+    rows = None
+    for ln in open(os.path.join(d, "FETCH_SIZE_ep8.log")):
+        if ln.startswith('{"metric"'):
+            rows = json.loads(ln)["roofline"]["flops_per_launch"] / (4.0 * 4096 * 14336)
+    out = ["# HBM traffic per launch from rocprofv3 counters: one rank's share of the Mixtral-shape layer at",
+           "# expert parallelism 8 (32768 tokens routed over the 8 experts, expert 0 local)",
+           "# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp):",
+           "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'grouped_gemm' -f csv -d $REPO/gpurun_out/prof/"
+           "FETCH_SIZE_ep8 -o bench -- \\",
+           "#       python3 $REPO/bench.py --cfg 2 --ep-share 8 --steps 3 --warmup 1 --no-cpu-baseline "
+           "> $REPO/gpurun_out/prof/FETCH_SIZE_ep8.log",
+           "#   (the same with WRITE_SIZE into .../WRITE_SIZE_ep8; the copy calibration as for the layer's",
+           "#   traffic file)",
+           "#   python3 bench.py --summarize-profile gpurun_out/prof",
+           f"# calibration, a plain 1 GiB device copy: read factor {f_factor:.3f}, write factor {w_factor:.3f}",
+           "# bytes = counter KiB x 1024 x factor, averaged over the launches of each kernel.", "",
+           f"{'kernel':58s}{'read_MB':>10s}{'write_MB':>10s}{'total_MB':>10s}"]
+    for k in fe:
+        rd = sum(fe[k]) / len(fe[k]) * 1024 * f_factor
+        wb = sum(wr.get(k, [0.0])) / max(len(wr.get(k, [])), 1) * 1024 * w_factor
+        out.append(f"{k:58s}{rd / 1e6:10.1f}{wb / 1e6:10.1f}{(rd + wb) / 1e6:10.1f}")
+    if rows:
+        r = int(round(rows))
+        out += ["", f"# algorithmic bytes per launch for comparison ({r} rows on the local expert): gate_up reads",
+                f"# the expert's gate_up weights ({4096 * 28672 * 2 / 1e6:.1f} MB) and its rows of x "
+                f"({r * 4096 * 2 / 1e6:.1f} MB) and writes A ({r * 14336 * 2 / 1e6:.1f} MB);",
+                f"# down reads the down weights ({14336 * 4096 * 2 / 1e6:.1f} MB) and A and writes O fp32 "
+                f"({r * 4096 * 4 / 1e6:.1f} MB)."]
+    open(os.path.join(prof, "mixtral_ep8_share_hbm_traffic.txt"), "w").write("\n".join(out) + "\n")
 
 
 def _summarize_pipe_counters(d, prof):
