@@ -390,6 +390,82 @@ def test_layer_full_size(moe, cid, nsample):
     _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=cid)
 
 
+# ---------------------------------------------------------------- seeded random shapes
+
+def _random_layer_cfg(seed):
+    """A small layer drawn from the parameter space the pages allow: operand
+    type, router (softmax, or sigmoid with sink lanes so that k + s is a power
+    of two), expert count and top-k, hidden and moe dims (any multiple of 8
+    for bf16, of 128 for the block-scaled operands), gate/up format, bias,
+    activation and its clamps; plus gathered or permuted activation rows."""
+    rng = np.random.default_rng(7000 + seed)
+    op = ["bf16", "bf16", "fp8", "mxfp4", "mxfp4_a16"][seed % 5]
+    base = {"bf16": 1, "fp8": 5, "mxfp4": 6, "mxfp4_a16": 7}[op]
+    E = int(rng.integers(1, 40))
+    if rng.random() < 0.5:
+        router, k, s_ = "softmax", int(rng.integers(1, min(E, 8) + 1)), 0
+    else:
+        p2 = int(rng.choice([2, 4, 8, 16]))
+        k = int(rng.integers(1, min(E, p2) + 1))
+        router, s_ = "sigmoid_sink", p2 - k
+    if op == "bf16":
+        H, D = 8 * int(rng.integers(1, 97)), int(rng.integers(1, 65)) * 8
+    else:
+        H, D = 128 * int(rng.integers(1, 5)), 128 * int(rng.integers(1, 4))
+    act = str(rng.choice(["silu", "swigluoai", "gelu_tanh"]))
+    alpha = 1.702 if act == "swigluoai" else 0.0
+    limit = 0.0 if act == "gelu_tanh" else float(rng.choice([0.0, 7.0]))
+    cfg = synth.scaled(synth.get_config(base), T=int(rng.integers(1, 300)), H=H, E=E, k=k, D=D, router=router,
+                       s=s_, n_shared=0, shared_dim=0, activation=act, alpha=alpha, limit=limit,
+                       gate_up_format=str(rng.choice(["concatenated", "interleaved"])),
+                       has_bias=bool(rng.random() < 0.5), route_scale=float(rng.choice([1.0, 2.5])),
+                       fused=False)
+    return cfg, bool(rng.random() < 0.7)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_layer_random_shapes(moe, seed):
+    """The whole layer on a seeded random small shape against the oracle,
+    routing exact.  bf16 and W4A16 (A kept in bf16): y of every token within
+    the bar beyond y's own bf16 rounding (half an ulp per output, as for the
+    expert-slice tests).  fp8 and W4A8, whose gate_up leg re-quantises A: the
+    two legs apart, as the full-size tests check them (`_check_expert_rows`:
+    A's codes against the oracle's quantisation of its own activation, O of
+    every expert row against the oracle's down projection of the GPU's A),
+    and y against the oracle's combine of the GPU's O.  A code at a rounding
+    boundary may come out one step apart from two float32 evaluations of the
+    same activation; in a batch of a few dozen tokens with one expert each, a
+    single such step at a large element moves y by several percent of its
+    RMS, which the end-to-end fp8 bar on the larger fp8 cases does not see."""
+    cfg, gather = _random_layer_cfg(seed)
+    say(f"[random layer] seed={seed} op={cfg.operand_dtype} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} s={cfg.s} "
+        f"D={cfg.D} {cfg.router} {cfg.gate_up_format} bias={cfg.has_bias} {cfg.activation} limit={cfg.limit} "
+        f"gather={gather}")
+    inp = _gen(cfg)
+    layer, res = _run_layer(moe, cfg, inp, gather=gather)
+    _check_routing(cfg, inp, res)
+    y = host(res["y"])
+    assert np.all(np.isfinite(y))
+    if cfg.operand_dtype in ("bf16", "mxfp4_a16"):
+        hin = synth.to_host(inp)
+        sw = host(res["sink_weights"]).astype(np.float64) if res.get("sink_weights") is not None else None
+        y_ref = O.layer(hin, cfg, indices=host(res["indices"]), weights=host(res["weights"]).astype(np.float64),
+                        sink_weights=sw)
+        err, _ = rel_rms_err(y, y_ref)
+        beyond = err_beyond_bf16_output(y, y_ref)
+        say(f"  y max err / rms = {err:.3e} ({beyond:.3e} beyond the output's bf16 rounding)")
+        assert beyond <= BF16_TOL
+        return
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=seed)
+    ind = res["index"]
+    R = int(host(ind["offsets"])[-1])
+    y_c = O.combine(host(res["O"])[:R].astype(np.float64), host(ind["row_of_slot"]).reshape(cfg.T, cfg.k),
+                    host(res["weights"]).astype(np.float64))
+    beyond = err_beyond_bf16_output(y, y_c)
+    say(f"  y against the oracle's combine of the GPU's O: {beyond:.3e} beyond the output's bf16 rounding")
+    assert beyond <= 1e-3
+
+
 # ---------------------------------------------------------------- one expert-parallel rank's share
 
 def _run_layer_slice(moe, cfg, inp, start, n, gather=True):
