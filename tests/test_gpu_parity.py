@@ -466,6 +466,67 @@ def test_layer_random_shapes(moe, seed):
     assert beyond <= 1e-3
 
 
+@pytest.mark.parametrize("seed", range(20))
+def test_layer_random_masks_slices_shared(moe, seed):
+    """Seeded random small layers as above, with masked tokens, an expert
+    slice (one expert-parallel rank's share, row buffers sized to the rows it
+    receives) or shared experts (bf16 and W4A16 layers: always on after a
+    softmax gate, gated one to one by the sink lanes after a sigmoid one)."""
+    cfg, gather = _random_layer_cfg(100 + seed)
+    rng = np.random.default_rng(9100 + seed)
+    mx_or_fp8 = cfg.operand_dtype in ("fp8", "mxfp4")
+    what = rng.choice(["slice", "shared"] if not mx_or_fp8 else ["slice"])
+    if what == "shared" and (cfg.router == "softmax" or 1 <= cfg.s <= 3):
+        n_sh = int(rng.integers(1, 3)) if cfg.router == "softmax" else cfg.s
+        sdim = 128 * int(rng.integers(1, 4)) if cfg.operand_dtype == "mxfp4_a16" else 8 * int(rng.integers(1, 48))
+        cfg = synth.scaled(cfg, n_shared=n_sh, shared_dim=sdim)
+    else:
+        what = "slice"
+    inp = _gen(cfg)
+    mask = None
+    if rng.random() < 0.6:
+        mask = (torch.rand((cfg.T,), generator=torch.Generator(device=DEV).manual_seed(seed), device=DEV)
+                > 0.2).to(torch.uint8)
+    start, n = 0, cfg.E
+    if what == "slice":
+        n = int(rng.integers(1, cfg.E + 1))
+        start = int(rng.integers(0, cfg.E - n + 1))
+    say(f"[random layer+] seed={seed} op={cfg.operand_dtype} T={cfg.T} H={cfg.H} E={cfg.E} k={cfg.k} s={cfg.s} "
+        f"D={cfg.D} {cfg.router} {cfg.gate_up_format} bias={cfg.has_bias} {cfg.activation} gather={gather} "
+        f"masked={mask is not None} experts {start}..{start + n - 1} shared={cfg.n_shared}")
+    if what == "slice":
+        layer = moe.MoELayer(cfg, inp, gather=gather, expert_slice=(start, n), max_rows=0)
+        layer.reserve_rows(layer.local_rows(inp["x"], token_mask=mask))
+    else:
+        layer = moe.MoELayer(cfg, inp, gather=gather)
+    res = layer.forward(inp["x"], token_mask=mask)
+    torch.cuda.synchronize()
+    _check_routing(cfg, inp, res)
+    y = host(res["y"])
+    assert np.all(np.isfinite(y))
+    hm = None if mask is None else host(mask)
+    if hm is not None:
+        assert np.all(y[hm == 0] == 0)
+    valid = np.ones(cfg.T, bool) if hm is None else hm != 0
+    if not mx_or_fp8:
+        hin = synth.to_host(inp)
+        sw = host(res["sink_weights"]).astype(np.float64) if res.get("sink_weights") is not None else None
+        y_ref = O.layer(hin, cfg, indices=host(res["indices"]), weights=host(res["weights"]).astype(np.float64),
+                        token_mask=hm, expert_start=start, num_local=n, sink_weights=sw)
+        beyond = err_beyond_bf16_output(y[valid], y_ref[valid])
+        say(f"  y: {beyond:.3e} beyond the output's bf16 rounding over {int(valid.sum())} valid tokens")
+        assert beyond <= BF16_TOL
+        return
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=seed, expert_start=start)
+    ind = res["index"]
+    R = int(host(ind["offsets"])[-1])
+    y_c = O.combine(host(res["O"])[:R].astype(np.float64), host(ind["row_of_slot"]).reshape(cfg.T, cfg.k),
+                    host(res["weights"]).astype(np.float64), token_mask=hm)
+    beyond = err_beyond_bf16_output(y[valid], y_c[valid])
+    say(f"  y against the oracle's combine of the GPU's O: {beyond:.3e} beyond the output's bf16 rounding")
+    assert beyond <= 1e-3
+
+
 # ---------------------------------------------------------------- one expert-parallel rank's share
 
 def _run_layer_slice(moe, cfg, inp, start, n, gather=True):
