@@ -263,8 +263,8 @@ def _summarize_main_trace(d, csv, main_stats, prof):
            "# workload: T=4096 tokens, hidden 4096, 8 experts, top-2 softmax gate, moe_dim 14336,",
            "#           concatenated gate_up, SiLU, bf16 operands, fp32 accumulate",
            PROFILE_CMDS,
-           f"# calls = warmup + timed steps of bench.py (route, csr_* and combine: + 12 launches timed alone",
-           "# after a cache flush).  Durations in microseconds; only this library's",
+           "# calls = the warmup, timed and instrumented steps of bench.py and its graph replays (route, csr_*",
+           "# and combine: + 12 launches timed alone after a cache flush).  Durations in microseconds; only this library's",
            "# kernels are listed (the torch kernels that generate the synthetic inputs are omitted).",
            f"# bench.py's own HIP-event timing in the same run: gate_up {bd.get('gate_up', 0) * 1e3:.1f} us, "
            f"down {bd.get('down', 0) * 1e3:.1f} us per launch.", "",
@@ -295,7 +295,8 @@ def _summarize_extra_and_counters(d, csv, prof):
                f"#       python3 $REPO/bench.py {bargs} --steps 10 --warmup 3 --no-cpu-baseline "
                f"> $REPO/gpurun_out/prof/{sub}.log",
                "#   python3 bench.py --summarize-profile gpurun_out/prof",
-               "# calls = warmup + timed steps.  Durations in microseconds; only this library's kernels.",
+               "# calls = the warmup, timed and instrumented steps and the graph replays.  Durations in microseconds;",
+               "# only this library's kernels.",
                f"# bench.py's own HIP-event timing in the same run: gate_up {bd.get('gate_up', 0) * 1e3:.1f} us, "
                f"down {bd.get('down', 0) * 1e3:.1f} us per launch.", "",
                f"{'kernel':58s}{'calls':>7s}{'avg_us':>10s}{'min_us':>10s}{'max_us':>10s}"]
