@@ -34,14 +34,25 @@ def moe():
     (8, {}),                                                     # single-launch FFN (decode)
     (9, {"T": 64, "E": 16, "H": 1024, "D": 512}),                # single-launch FFN, MXFP4 x MXFP8
     (10, {"T": 64, "E": 16, "H": 1024, "D": 512}),               # single-launch FFN, MXFP4 x bf16
+    # one expert-parallel rank's share, row buffers sized to the rows it receives
+    (2, {"T": 512, "expert_slice": (2, 3)}),
+    # shared experts on their own stream, forked after the per-token quantise (fp8, W4A8)
+    (5, {"T": 256, "E": 8, "k": 3, "s": 1, "n_shared": 1, "H": 512, "D": 256, "shared_dim": 384}),
+    (6, {"T": 256, "E": 8, "k": 2, "s": 2, "n_shared": 2, "H": 512, "D": 256, "shared_dim": 384}),
 ])
 def test_layer_replays_in_a_graph(moe, cid, changes):
+    changes = dict(changes)
+    sl = changes.pop("expert_slice", None)
     cfg = synth.scaled(synth.get_config(cid), **changes)
-    say(f"[graph] cfg={cid} {changes}")
+    say(f"[graph] cfg={cid} {changes} slice={sl}")
     inp = synth.make_inputs(cfg, DEV)
-    layer = moe.MoELayer(cfg, inp)
     x = inp["x"]
     x_other = (inp["x"].float() * -0.5 + 0.25).to(inp["x"].dtype)
+    if sl is None:
+        layer = moe.MoELayer(cfg, inp)
+    else:
+        layer = moe.MoELayer(cfg, inp, expert_slice=sl, max_rows=0)
+        layer.reserve_rows(max(layer.local_rows(x), layer.local_rows(x_other)))
     want = layer.forward(x)["y"].clone()
     other = layer.forward(x_other)["y"].clone()
     torch.cuda.synchronize()
