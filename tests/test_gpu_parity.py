@@ -603,6 +603,21 @@ def test_layer_expert_slice_mixtral_ep8_share(moe):
     _check_expert_rows(cfg, inp, res, layer, BF16_TOL, seed=12)
 
 
+def test_layer_expert_slice_fp8_ep8_share(moe):
+    """The fp8 block-scaled layer's share on one of 8 expert-parallel GPUs at
+    its real shape: 8 x 16384 tokens routed over the 256 experts, experts
+    0..31 local with the rows they receive (thousands per expert, so most of
+    their m-blocks are full)."""
+    base = synth.get_config(5)
+    cfg = synth.scaled(base, T=base.T * 8)
+    inp = _gen(cfg)
+    say("[layer slice full] fp8 dims, T=131072, experts 0..31 of 256")
+    layer, res, rows = _run_layer_slice(moe, cfg, inp, 0, 32)
+    say(f"  {rows} rows local")
+    _check_expert_rows(cfg, inp, res, layer, FP8_TOL, seed=13)
+    _check_layer_slice(cfg, inp, res, sample_tokens(cfg.T, 12, seed=13), FP8_TOL, 0, 32)
+
+
 # ---------------------------------------------------------------- the stacked (IN_OUT) weight layout
 
 def _ffn_both_layouts(moe, cfg, inp, gather, gu_layout, d_layout):
