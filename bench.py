@@ -890,7 +890,7 @@ def main():
         "hbm_frac_of_measured": {n: round(v["gbs"] / ceil["stream_read_gbs" if n == "route" else "stream_copy_gbs"], 4)
                                  for n, v in flushed.items()},
         "hbm_flushed": flushed,
-        # the same kernels inside the timed layer steps (mean of the steps): the
+        # the same kernels inside the instrumented layer steps (mean of the steps): the
         # combine there reads the rows O the down GEMM has just left in the
         # Infinity Cache, so its rate is partly cache bandwidth
         "hbm_in_layer_cache_warm": {n: {"gbs": round(v, 1), "frac": round(v / PEAK_HBM_GBS, 4)}
