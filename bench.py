@@ -308,6 +308,7 @@ def _summarize_extra_and_counters(d, csv, prof):
     # HBM traffic from FETCH_SIZE / WRITE_SIZE, calibrated on a plain copy of known size
     counters = _pmc_counters
     _summarize_ep_traffic(d, prof)
+    _summarize_fabric_reads(d, prof)
     if not os.path.exists(os.path.join(d, "FETCH_SIZE", "bench_counter_collection.csv")):
         _summarize_pipe_counters(d, prof)
         return
@@ -459,6 +460,43 @@ def pipe_counter_summary(path: str, title: str, sub: str) -> str:
                    f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:10.2f}{c['SQ_INSTS_LDS'] / c['SQ_INSTS_MFMA']:9.2f}"
                    f"{c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:8.1%}{c['SQ_LDS_BANK_CONFLICT']:16.3g}")
     return "\n".join(out)
+
+
+EA_COUNTERS = "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_LEVEL_sum TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum GRBM_GUI_ACTIVE"
+
+
+def _summarize_fabric_reads(d, prof):
+    """The GEMMs' L2 miss reads through the fabric: requests, their average
+    time in flight (TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, in L2 clock cycles)
+    and the cycles stalled for want of DRAM credits, for the Mixtral-shape
+    layer and its expert-parallel share, if their counter passes are in d."""
+    import csv
+    runs = [("EA2", "", "Mixtral-shape layer (8 experts, ~1024 rows each)"),
+            ("EA2ep", " --ep-share 8", "its expert-parallel share at EP 8 (one expert, ~8300 rows)")]
+    if not all(os.path.exists(os.path.join(d, sub, "bench_counter_collection.csv")) for sub, _, _ in runs):
+        return
+    out = ["# rocprofv3 counters: fabric reads of the bf16 grouped GEMMs (L2 misses), two workloads",
+           "# commands (repo root as $REPO, run from /tmp with TMPDIR=/tmp), one pass each:",
+           f"#   rocprofv3 --pmc {EA_COUNTERS} --kernel-include-regex 'grouped_gemm' -f csv \\",
+           "#       -d $REPO/gpurun_out/prof/EA2 -o bench -- python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+           "#   (the same with --cfg 2 --ep-share 8 into .../EA2ep)",
+           "#   python3 bench.py --summarize-profile gpurun_out/prof",
+           "# reads = TCC_EA0_RDREQ (32- or 64-byte requests, all channels); latency = TCC_EA0_RDREQ_LEVEL /",
+           "# TCC_EA0_RDREQ (average L2 clock cycles a read is in flight); credit stall = TCC_EA0_RDREQ_DRAM_CREDIT_STALL",
+           "# summed over the channels, per GRBM_GUI_ACTIVE cycle summed over the 8 XCDs.  Averages over the launches.", ""]
+    for sub, flag, title in runs:
+        per = {}
+        for r in csv.DictReader(open(os.path.join(d, sub, "bench_counter_collection.csv"))):
+            per.setdefault(_short(r["Kernel_Name"]), {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        out += [f"# {title}", f"{'kernel':58s}{'reads':>12s}{'latency':>9s}{'stall/cyc':>10s}"]
+        for k in sorted(per):
+            c = {n: sum(v) / len(v) for n, v in per[k].items()}
+            rd = c["TCC_EA0_RDREQ_sum"]
+            out.append(f"{k:58s}{rd:12.4g}{c['TCC_EA0_RDREQ_LEVEL_sum'] / max(rd, 1):9.0f}"
+                       f"{c['TCC_EA0_RDREQ_DRAM_CREDIT_STALL_sum'] / max(c['GRBM_GUI_ACTIVE'], 1):10.3f}")
+        out.append("")
+    open(os.path.join(prof, "mixtral_gemm_fabric_reads.txt"), "w").write("\n".join(out))
 
 
 def _cpu_model() -> str:
